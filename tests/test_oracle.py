@@ -1,0 +1,236 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The pages print no numerical example for the recurrence, so the oracle is
+pinned by hand-worked cases derived from the printed equations
+(tests/golden/), by special cases with closed forms or textbook equivalents,
+by an independent brute-force product form, and by structural invariants the
+pages state (erase-then-write; KDA generalises Gated DeltaNet).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import models
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+rng0 = np.random.default_rng(1234)
+
+
+def _rand_case(T, dk, dv, H=1, B=1, per_channel=False, seed=0, unit_keys=True, s0=True):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, T, H, dk))
+    k = r.standard_normal((B, T, H, dk))
+    if unit_keys:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, T, H, dv))
+    beta = 1.0 / (1.0 + np.exp(-r.standard_normal((B, T, H))))
+    shape = (B, T, H, dk) if per_channel else (B, T, H)
+    log_alpha = -np.log1p(np.exp(r.standard_normal(shape)))
+    S0 = 0.5 * r.standard_normal((B, H, dv, dk)) if s0 else None
+    return q, k, v, beta, log_alpha, S0
+
+
+# ---------------------------------------------------------------- golden ----
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "hand_worked_2x2.json")))["cases"],
+                         ids=lambda c: c["name"])
+def test_hand_worked_examples(case):
+    k = np.array(case["k"])[None, :, None, :]
+    q = np.array(case["q"])[None, :, None, :]
+    v = np.array(case["v"])[None, :, None, :]
+    beta = np.array(case["beta"])[None, :, None]
+    la = np.log(np.array(case["alpha"]))[None, :, None, :]
+    S0 = np.array(case["S0"])[None, None]
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    np.testing.assert_allclose(out[0, :, 0], np.array(case["out"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(fin[0, 0], np.array(case["final_state"]), rtol=0, atol=1e-14)
+    # the same case through the per-head gate form when all channels share alpha
+    alpha = np.array(case["alpha"])
+    if np.all(alpha[:, :1] == alpha):
+        out2, fin2 = oracle.recurrence(q, k, v, beta, la[..., 0], initial_state=S0)
+        np.testing.assert_allclose(out2[0, :, 0], np.array(case["out"]), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(fin2[0, 0], np.array(case["final_state"]), rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------ special cases ----
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_p1_no_write_no_decay_keeps_state(per_channel):
+    q, k, v, beta, la, S0 = _rand_case(9, 8, 6, H=2, per_channel=per_channel, seed=1)
+    beta[:] = 0.0
+    la[:] = 0.0
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    assert np.array_equal(fin, S0)
+    expect = np.einsum("hij,bthj->bthi", S0[0], q)
+    np.testing.assert_allclose(out, expect, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_p2_erase_then_write_recalls_value(per_channel):
+    """Unit-norm key and beta = 1: the written key recalls exactly its value
+    (the erase factor removes the old association first)."""
+    q, k, v, beta, la, S0 = _rand_case(12, 16, 8, H=3, per_channel=per_channel, seed=2)
+    beta[:] = 1.0
+    state = S0
+    for t in range(k.shape[1]):
+        _, state = oracle.recurrence(q[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1], beta[:, t:t + 1],
+                                     la[:, t:t + 1], initial_state=state)
+        recalled = np.einsum("hij,hj->hi", state[0], k[0, t])
+        np.testing.assert_allclose(recalled, v[0, t], rtol=0, atol=1e-13)
+
+
+def test_p3_equal_channel_kda_is_gdn_equation():
+    q, k, v, beta, la, S0 = _rand_case(10, 8, 5, H=2, per_channel=False, seed=3)
+    la_kda = np.repeat(la[..., None], 8, axis=-1)
+    out_kda, fin_kda = oracle.recurrence(q, k, v, beta, la_kda, initial_state=S0)
+    out_gdn, fin_gdn = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    for h in range(2):
+        O, S = models.gdn_equation(q[0, :, h], k[0, :, h], v[0, :, h], beta[0, :, h], la[0, :, h], S0[0, h])
+        np.testing.assert_allclose(out_kda[0, :, h], O, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(fin_kda[0, h], S, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(out_gdn[0, :, h], O, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(fin_gdn[0, h], S, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+def test_p4_brute_force_product_form(per_channel, T):
+    q, k, v, beta, la, S0 = _rand_case(T, 6, 4, H=2, per_channel=per_channel, seed=10 + T,
+                                       unit_keys=False)
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    for h in range(2):
+        O, S = models.product_form(q[0, :, h], k[0, :, h], v[0, :, h], beta[0, :, h], la[0, :, h], S0[0, h])
+        np.testing.assert_allclose(out[0, :, h], O, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(fin[0, h], S, rtol=0, atol=1e-12)
+
+
+def test_p5_reduces_to_causal_linear_attention():
+    """alpha = 1, beta = 1, orthonormal keys, zero state: each key is written
+    once and never disturbed, so o_t = sum_{i<=t} (q_t . k_i) v_i and
+    S_T = V^T K -- plain (additive) causal linear attention."""
+    T, dk, dv = 7, 12, 5
+    r = np.random.default_rng(5)
+    Kq, _ = np.linalg.qr(r.standard_normal((dk, T)))
+    K = Kq.T                      # T orthonormal rows
+    Q = r.standard_normal((T, dk))
+    V = r.standard_normal((T, dv))
+    out, fin = oracle.recurrence(Q[None, :, None], K[None, :, None], V[None, :, None],
+                                 np.ones((1, T, 1)), np.zeros((1, T, 1)))
+    np.testing.assert_allclose(out[0, :, 0], np.tril(Q @ K.T) @ V, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(fin[0, 0], V.T @ K, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_p6_pure_decay_closed_form(per_channel):
+    q, k, v, beta, la, S0 = _rand_case(11, 8, 4, H=2, per_channel=per_channel, seed=6)
+    beta[:] = 0.0
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    g = np.cumsum(la, axis=1)  # [1, T, H(, dk)]
+    for h in range(2):
+        for t in range(11):
+            dec = np.exp(g[0, t, h]) * np.ones(8)
+            np.testing.assert_allclose(out[0, t, h], S0[0, h] @ (dec * q[0, t, h]), rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(fin[0, h], S0[0, h] * (np.exp(g[0, -1, h]) * np.ones(8))[None, :],
+                                   rtol=1e-14, atol=1e-16)
+
+
+def test_p7_structure_linear_affine_row_independent():
+    q, k, v, beta, la, S0 = _rand_case(9, 8, 6, H=2, per_channel=True, seed=7)
+    # linear in V when S0 = 0
+    o1, s1 = oracle.recurrence(q, k, v, beta, la)
+    o2, s2 = oracle.recurrence(q, k, 2.5 * v, beta, la)
+    np.testing.assert_allclose(o2, 2.5 * o1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(s2, 2.5 * s1, rtol=1e-13, atol=1e-14)
+    # affine in S0: f(S0) = f(0) + (f(S0, v=0))
+    oa, sa = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    ob, sb = oracle.recurrence(q, k, np.zeros_like(v), beta, la, initial_state=S0)
+    np.testing.assert_allclose(oa, o1 + ob, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sa, s1 + sb, rtol=0, atol=1e-13)
+    # value channels (rows of S) evolve independently: permuting v permutes rows
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    op, sp = oracle.recurrence(q, k, v[..., perm], beta, la, initial_state=S0[:, :, perm])
+    np.testing.assert_allclose(op, oa[..., perm], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(sp, sa[:, :, perm], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("chunk", [1, 2, 3, 5, 16, 64])
+def test_p8_chunked_algebra_matches_oracle(per_channel, chunk):
+    T = 37 if chunk <= 16 else 150
+    q, k, v, beta, la, S0 = _rand_case(T, 16, 12, H=1, per_channel=per_channel, seed=8 + chunk)
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    O, S = models.chunked(q[0, :, 0], k[0, :, 0], v[0, :, 0], beta[0, :, 0], la[0, :, 0], S0[0, 0], chunk=chunk)
+    np.testing.assert_allclose(O, out[0, :, 0], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(S, fin[0, 0], rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_p9_continuation(per_channel):
+    q, k, v, beta, la, S0 = _rand_case(23, 8, 8, H=2, per_channel=per_channel, seed=9)
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    T1 = 10
+    o_a, s_a = oracle.recurrence(q[:, :T1], k[:, :T1], v[:, :T1], beta[:, :T1], la[:, :T1], initial_state=S0)
+    o_b, s_b = oracle.recurrence(q[:, T1:], k[:, T1:], v[:, T1:], beta[:, T1:], la[:, T1:], initial_state=s_a)
+    np.testing.assert_allclose(np.concatenate([o_a, o_b], axis=1), out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(s_b, fin, rtol=0, atol=1e-13)
+    # token-by-token decode equals the prefill
+    state = S0
+    for t in range(23):
+        o_t, state = oracle.decode(q[:, t], k[:, t], v[:, t], beta[:, t], la[:, t], state)
+        np.testing.assert_allclose(o_t, out[:, t], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(state, fin, rtol=0, atol=1e-13)
+
+
+def test_p10_packed_equals_separate_runs():
+    lens = [5, 0, 13, 1, 9]
+    T = sum(lens)
+    q, k, v, beta, la, _ = _rand_case(T, 8, 4, H=3, per_channel=True, seed=10)
+    r = np.random.default_rng(11)
+    S0 = r.standard_normal((len(lens), 3, 4, 8))
+    bounds = np.concatenate([[0], np.cumsum(lens)])
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0, seq_bounds=bounds)
+    for n, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        o_n, s_n = oracle.recurrence(q[:, a:b], k[:, a:b], v[:, a:b], beta[:, a:b], la[:, a:b],
+                                     initial_state=S0[n:n + 1])
+        assert np.array_equal(out[:, a:b], o_n)
+        assert np.array_equal(fin[n:n + 1], s_n)
+    assert np.array_equal(fin[1], S0[1])  # empty sequence: final = initial
+
+
+def test_p12_bounded_growth():
+    """||k|| = 1, beta in [0, 2], alpha in (0, 1]: the transition is
+    non-expansive, so ||S_t||_F <= ||S_{t-1}||_F + |beta_t| ||v_t||."""
+    q, k, v, beta, la, S0 = _rand_case(200, 16, 8, per_channel=True, seed=12)
+    beta = 2.0 * np.random.default_rng(13).random(beta.shape)
+    state = S0
+    for t in range(200):
+        prev = np.linalg.norm(state)
+        _, state = oracle.recurrence(q[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1], beta[:, t:t + 1],
+                                     la[:, t:t + 1], initial_state=state)
+        assert np.linalg.norm(state) <= prev + beta[0, t, 0] * np.linalg.norm(v[0, t, 0]) + 1e-12
+
+
+def test_scale_multiplies_readout_only():
+    q, k, v, beta, la, S0 = _rand_case(9, 8, 8, per_channel=False, seed=14)
+    o1, s1 = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    o2, s2 = oracle.recurrence(q, k, v, beta, la, initial_state=S0, scale=0.125)
+    np.testing.assert_allclose(o2, 0.125 * o1, rtol=1e-15, atol=0)
+    assert np.array_equal(s1, s2)
+
+
+def test_planted_mistake_is_caught():
+    """Sanity check of the pins themselves: a copy of the recurrence with the
+    decay applied after the erase (a plausible mistake) fails the
+    erase-then-write pin for per-channel decay, while the oracle passes it."""
+    q, k, v, beta, la, S0 = _rand_case(6, 8, 4, per_channel=True, seed=15)
+    beta[:] = 1.0
+    S = S0[0, 0].copy()
+    worst = 0.0
+    for t in range(6):
+        a = np.exp(la[0, t, 0])
+        kt = k[0, t, 0]
+        S = (S - np.outer(S @ kt, kt)) * a[None, :] + np.outer(v[0, t, 0], kt)  # wrong order
+        worst = max(worst, np.abs(S @ kt - v[0, t, 0]).max())
+    assert worst > 1e-3

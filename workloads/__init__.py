@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the gated delta-rule recurrence.
+
+This module only draws random numbers; it holds none of the recurrence's
+arithmetic.  Both the oracle-side tests and the GPU path take their inputs
+from here, so the two see bit-identical stored values.
+
+The pages publish no dataset for this layer, so every input is synthetic with
+the shapes the pages' models use (head dimension 128: page "How the New Flash
+Models Work: Inside GLM-5.3-Flash and Qwen3.8-Flash-Next", section "The two
+stacks, layer by layer"; page "Qwen3.8-Flash-Next and GLM-5.3-Flash share a
+3:1 long-context pattern", sections "Gated DeltaNet carries most of the
+sequence" and "Kimi Delta Attention extends recurrent memory control").
+
+Recipe (per workload, one seed):
+  q, k ~ N(0, 1), L2-normalised over the key dimension per (token, head),
+  v ~ N(0, 1), beta = sigmoid(N(0, 1)), log_alpha = -softplus(N(0, 1))
+  (one value per (token, head) for per-head decay, one per key channel for
+  per-channel decay), initial state ~ N(0, 0.02^2) where asked for.
+  Draw order: q, k, v, beta logits, alpha logits, initial state.
+  Draws are fp32 from torch's seeded generator on the target device; q/k/v are
+  then rounded to the storage dtype (bf16 round-to-nearest-even), gates and
+  states stay fp32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str                 # "prefill" or "decode"
+    heads: int
+    dk: int
+    dv: int
+    qkv_dtype: torch.dtype
+    gate: str = "head"        # "head" (Gated DeltaNet) or "channel" (Kimi Delta Attention)
+    batch: int = 1            # prefill: dense batch; decode: number of sequences
+    seqlen: int = 0           # prefill: tokens per sequence (dense) or total (packed)
+    chunk: int = 64
+    init_state: bool = False
+    packed: dict = field(default_factory=dict)   # {"num_seqs", "min_len", "max_len"}
+    seed: int = 0
+
+
+WORKLOADS = {
+    "tiny_gdn": Workload("tiny_gdn", "prefill", heads=2, dk=16, dv=16, qkv_dtype=torch.float32,
+                         gate="head", batch=1, seqlen=64, chunk=16, init_state=False, seed=0),
+    "gdn_prefill_8k": Workload("gdn_prefill_8k", "prefill", heads=16, dk=128, dv=128,
+                               qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=8192,
+                               chunk=64, init_state=False, seed=1),
+    "kda_prefill_32k": Workload("kda_prefill_32k", "prefill", heads=32, dk=128, dv=128,
+                                qkv_dtype=torch.bfloat16, gate="channel", batch=2, seqlen=32768,
+                                chunk=64, init_state=True, seed=2),
+    "decode_256x32": Workload("decode_256x32", "decode", heads=32, dk=128, dv=128,
+                              qkv_dtype=torch.bfloat16, gate="both", batch=256, init_state=True,
+                              seed=3),
+    "packed_gdn_256k": Workload("packed_gdn_256k", "prefill", heads=16, dk=128, dv=128,
+                                qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=262144,
+                                chunk=64, init_state=True,
+                                packed={"num_seqs": 8, "min_len": 4096, "max_len": 61440}, seed=4),
+}
+
+
+def packed_lengths(total: int, num_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Lengths uniform in [lo, hi] summing to ``total``: draw the first
+    num_seqs-1 uniformly, give the rest to the last one, and redraw until the
+    last one also lies in [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for _ in range(100000):
+        head = rng.integers(lo, hi + 1, size=num_seqs - 1)
+        last = total - int(head.sum())
+        if lo <= last <= hi:
+            return np.concatenate([head, [last]]).astype(np.int64)
+    raise RuntimeError("length sampler did not converge")
+
+
+def _unit_norm(x: torch.Tensor) -> torch.Tensor:
+    return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def prefill_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batch: int | None = None,
+                   heads: int | None = None, lengths=None, gate: str | None = None, seed: int | None = None,
+                   init_state: bool | None = None):
+    """Inputs of a prefill workload (optionally resized for tests).
+
+    Returns a dict with q, k, v [B, T, H, d], beta [B, T, H], log_alpha
+    [B, T, H] or [B, T, H, dk], initial_state [N, H, dv, dk] or None and
+    cu_seqlens (int32 [N+1], packed workloads only).
+    """
+    B = w.batch if batch is None else batch
+    T = w.seqlen if seqlen is None else seqlen
+    H = w.heads if heads is None else heads
+    gate = w.gate if gate is None else gate
+    seed = w.seed if seed is None else seed
+    init_state = w.init_state if init_state is None else init_state
+    dk, dv = w.dk, w.dv
+    cu = None
+    if lengths is not None or w.packed:
+        if lengths is None:
+            p = w.packed
+            lengths = packed_lengths(T, p["num_seqs"], p["min_len"], p["max_len"], seed)
+        lengths = np.asarray(lengths, dtype=np.int64)
+        T = int(lengths.sum())
+        B = 1
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=device)
+        N = len(lengths)
+    else:
+        N = B
+    g = _gen(device, seed)
+    f32 = torch.float32
+    q = _unit_norm(torch.randn(B, T, H, dk, generator=g, device=device, dtype=f32)).to(w.qkv_dtype)
+    k = _unit_norm(torch.randn(B, T, H, dk, generator=g, device=device, dtype=f32)).to(w.qkv_dtype)
+    v = torch.randn(B, T, H, dv, generator=g, device=device, dtype=f32).to(w.qkv_dtype)
+    beta = torch.sigmoid(torch.randn(B, T, H, generator=g, device=device, dtype=f32))
+    ashape = (B, T, H) if gate == "head" else (B, T, H, dk)
+    log_alpha = -torch.nn.functional.softplus(torch.randn(*ashape, generator=g, device=device, dtype=f32))
+    s0 = None
+    if init_state:
+        s0 = 0.02 * torch.randn(N, H, dv, dk, generator=g, device=device, dtype=f32)
+    return {"q": q, "k": k, "v": v, "beta": beta, "log_alpha": log_alpha,
+            "initial_state": s0, "cu_seqlens": cu}
+
+
+def decode_inputs(w: Workload, device="cpu", *, gate: str = "head", num_seqs: int | None = None,
+                  heads: int | None = None, dk: int | None = None, dv: int | None = None,
+                  seed: int | None = None, qkv_dtype=None):
+    """One token per sequence: q, k [N, H, dk], v [N, H, dv], beta [N, H],
+    log_alpha [N, H] or [N, H, dk], state [N, H, dv, dk] (fp32)."""
+    N = w.batch if num_seqs is None else num_seqs
+    H = w.heads if heads is None else heads
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    dt = w.qkv_dtype if qkv_dtype is None else qkv_dtype
+    g = _gen(device, w.seed if seed is None else seed)
+    f32 = torch.float32
+    q = _unit_norm(torch.randn(N, H, dk, generator=g, device=device, dtype=f32)).to(dt)
+    k = _unit_norm(torch.randn(N, H, dk, generator=g, device=device, dtype=f32)).to(dt)
+    v = torch.randn(N, H, dv, generator=g, device=device, dtype=f32).to(dt)
+    beta = torch.sigmoid(torch.randn(N, H, generator=g, device=device, dtype=f32))
+    ashape = (N, H) if gate == "head" else (N, H, dk)
+    log_alpha = -torch.nn.functional.softplus(torch.randn(*ashape, generator=g, device=device, dtype=f32))
+    state = 0.02 * torch.randn(N, H, dv, dk, generator=g, device=device, dtype=f32)
+    return {"q": q, "k": k, "v": v, "beta": beta, "log_alpha": log_alpha, "state": state}
