@@ -1,0 +1,173 @@
+"""Gated delta-rule recurrence (Gated DeltaNet / Kimi Delta Attention) on MI355X.
+
+Thin Python binding of ``libgdr.so`` (C ABI in ``include/gdr.h``).  This module
+only marshals arguments: it checks tensor placement, takes the current HIP
+stream from torch and calls the library; every step of the computation runs
+in the library's gfx950 kernels.  There is no fallback: if the library is
+missing, the calls raise.
+
+    o, S = gdr_prefill_chunked(q, k, v, beta, log_alpha, initial_state=S0, cu_seqlens=cu)
+    o    = gdr_decode_step(q, k, v, beta, log_alpha, state)   # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "prefill_chunked", "decode_step",
+           "gdr_state_bytes", "GdrError", "load_library", "library_path"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libgdr.so")
+
+GDR_SUCCESS, GDR_ERROR_INVALID_VALUE, GDR_ERROR_NOT_SUPPORTED = 0, 1, 2
+GDR_ERROR_INSUFFICIENT_WORKSPACE, GDR_ERROR_LAUNCH_FAILED = 3, 4
+GDR_F32, GDR_BF16 = 0, 1
+GDR_GATE_HEAD, GDR_GATE_CHANNEL = 0, 1
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gdr status {status}: {message}")
+        self.status = status
+
+
+class PrefillShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libgdr.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with `python -m gated_delta_rule_73_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        lib.gdr_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), i32]
+        lib.gdr_prefill_workspace_bytes.restype = sz
+        lib.gdr_prefill_chunked.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, p, p, p, p, p, p, p, i32, i32, ctypes.c_float, p, p, p,
+                                            sz, p]
+        lib.gdr_prefill_chunked.restype = ctypes.c_int
+        lib.gdr_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        p, p, p, p, p, p, ctypes.c_float, p, p]
+        lib.gdr_decode_step.restype = ctypes.c_int
+        lib.gdr_state_bytes.argtypes = [ctypes.c_int64] * 4
+        lib.gdr_state_bytes.restype = ctypes.c_uint64
+        lib.gdr_status_string.argtypes = [ctypes.c_int]
+        lib.gdr_status_string.restype = ctypes.c_char_p
+        lib.gdr_last_error.restype = ctypes.c_char_p
+        lib.gdr_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != GDR_SUCCESS:
+        raise GdrError(status, load_library().gdr_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def gdr_state_bytes(num_seqs: int, num_heads: int, head_dim_k: int, head_dim_v: int) -> int:
+    return int(load_library().gdr_state_bytes(num_seqs, num_heads, head_dim_k, head_dim_v))
+
+
+def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seqlens=None, chunk_size: int = 0,
+                        dv_slice: int = 0, scale: float = 1.0, out=None, out_dtype=torch.float32,
+                        final_state=None, output_final_state: bool = True):
+    """Chunked prefill.  q, k [B, T, H, dk]; v [B, T, H, dv] (bf16 or fp32);
+    beta [B, T, H] fp32; log_alpha [B, T, H] (per-head decay) or [B, T, H, dk]
+    (per-key-channel decay) fp32; initial_state [N, H, dv, dk] fp32 or None;
+    cu_seqlens int32 [N+1] (packed, B == 1) or None.
+    out_dtype (fp32 or bf16) applies when ``out`` is not given.
+    Returns (out [B, T, H, dv], final_state [N, H, dv, dk] or None)."""
+    lib = load_library()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if log_alpha.dim() == 3:
+        gate = GDR_GATE_HEAD
+    elif log_alpha.dim() == 4:
+        gate = GDR_GATE_CHANNEL
+    else:
+        raise ValueError("log_alpha must be [B, T, H] or [B, T, H, dk]")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, q.dtype, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(initial_state, "initial_state", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    if out is None:
+        out = torch.empty(B, T, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", None, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty(N, H, dv, dk, dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev)
+    shape = PrefillShape(B, T, H, dk, dv, N)
+    ws_bytes = lib.gdr_prefill_workspace_bytes(ctypes.byref(shape), int(cu_seqlens is not None))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    _check(lib.gdr_prefill_chunked(
+        ctypes.byref(shape), gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+        _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(dv_slice), float(scale), _ptr(out),
+        _ptr(final_state), _ptr(ws), int(ws_bytes), _stream(dev)))
+    return out, final_state
+
+
+def gdr_decode_step(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, out=None, out_dtype=torch.float32):
+    """Decode step, one token per sequence: q, k [N, H, dk]; v [N, H, dv];
+    beta [N, H]; log_alpha [N, H] or [N, H, dk]; state [N, H, dv, dk] fp32
+    (updated in place).  Returns out [N, H, dv]."""
+    lib = load_library()
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    gate = GDR_GATE_HEAD if log_alpha.dim() == 2 else GDR_GATE_CHANNEL
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, q.dtype, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    if out is None:
+        out = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", None, dev)
+    _check(lib.gdr_decode_step(N, H, dk, dv, gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                               _ptr(log_alpha), _ptr(state), float(scale), _ptr(out), _stream(dev)))
+    return out
+
+
+prefill_chunked = gdr_prefill_chunked
+decode_step = gdr_decode_step

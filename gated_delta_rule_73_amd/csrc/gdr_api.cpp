@@ -1,0 +1,258 @@
+// gdr_api.cpp -- the C ABI of libgdr (declared in include/gdr.h): argument
+// validation on the host, launch-shape selection, error reporting.  Every
+// check runs before the first HIP call, so a rejected call enqueues nothing
+// and needs no GPU.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gdr.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdr_status fail(gdr_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+gdr_status ok() {
+    g_last_error[0] = '\0';
+    return GDR_SUCCESS;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi), empty when lo == hi
+};
+
+Range range(const char *name, const void *p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+bool overlaps(const Range &a, const Range &b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+size_t dsize(gdr_dtype t) { return t == GDR_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == GDR_F32 || t == GDR_BF16; }
+bool valid_gate(int g) { return g == GDR_GATE_HEAD || g == GDR_GATE_CHANNEL; }
+
+gdr_status launch_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(GDR_ERROR_LAUNCH_FAILED, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+size_t order_bytes(int32_t num_seqs) {
+    const size_t b = sizeof(int32_t) * (size_t)(num_seqs > 0 ? num_seqs : 0);
+    return (b + 255) & ~size_t(255);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdr_status_string(gdr_status s) {
+    switch (s) {
+        case GDR_SUCCESS: return "success";
+        case GDR_ERROR_INVALID_VALUE: return "invalid value";
+        case GDR_ERROR_NOT_SUPPORTED: return "not supported";
+        case GDR_ERROR_INSUFFICIENT_WORKSPACE: return "insufficient workspace";
+        case GDR_ERROR_LAUNCH_FAILED: return "launch failed";
+    }
+    return "unknown status";
+}
+
+const char *gdr_last_error(void) { return g_last_error; }
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+uint64_t gdr_state_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim_k, int64_t head_dim_v) {
+    if (num_seqs < 0 || num_heads < 0 || head_dim_k < 0 || head_dim_v < 0) return 0;
+    return (uint64_t)num_seqs * (uint64_t)num_heads * (uint64_t)head_dim_k * (uint64_t)head_dim_v * sizeof(float);
+}
+
+size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, int32_t packed) {
+    if (!shape || !packed) return 0;
+    return order_bytes(shape->num_seqs);
+}
+
+gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
+                               gdr_dtype gate_dtype, gdr_dtype out_dtype, const void *q, const void *k, const void *v,
+                               const void *beta, const void *log_alpha, const float *initial_state,
+                               const int32_t *cu_seqlens, int32_t chunk_size, int32_t dv_slice, float scale,
+                               void *out, float *final_state, void *workspace, size_t workspace_bytes,
+                               void *hip_stream) {
+    if (!shape) return fail(GDR_ERROR_INVALID_VALUE, "shape is NULL");
+    const gdr_prefill_shape s = *shape;
+    if (s.batch < 1 || s.seqlen < 0 || s.num_heads < 1 || s.head_dim_k < 1 || s.head_dim_v < 1 || s.num_seqs < 0)
+        return fail(GDR_ERROR_INVALID_VALUE,
+                    "bad shape (batch=%d seqlen=%d heads=%d dk=%d dv=%d num_seqs=%d)", s.batch, s.seqlen,
+                    s.num_heads, s.head_dim_k, s.head_dim_v, s.num_seqs);
+    if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
+    if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
+        return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d out=%d)", (int)qkv_dtype,
+                    (int)gate_dtype, (int)out_dtype);
+    if (gate_dtype != GDR_F32) return fail(GDR_ERROR_NOT_SUPPORTED, "gates must be fp32");
+    const bool packed = cu_seqlens != nullptr;
+    if (packed && s.batch != 1) return fail(GDR_ERROR_INVALID_VALUE, "cu_seqlens requires batch == 1");
+    if (!packed && s.num_seqs != s.batch)
+        return fail(GDR_ERROR_INVALID_VALUE, "dense batch needs num_seqs == batch (%d != %d)", s.num_seqs, s.batch);
+    const int64_t tokens = (int64_t)s.batch * s.seqlen;
+    if (tokens > INT32_MAX) return fail(GDR_ERROR_INVALID_VALUE, "more than 2^31-1 tokens");
+    if ((int64_t)s.num_seqs * s.num_heads > INT32_MAX / 8)
+        return fail(GDR_ERROR_INVALID_VALUE, "too many (sequence, head) units");
+    const int dk = s.head_dim_k, dv = s.head_dim_v;
+    const bool bf16 = qkv_dtype == GDR_BF16;
+    const bool kda = gate == GDR_GATE_CHANNEL;
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_k %d not in {16, 32, 64, 128}", dk);
+    if (dv % 16 != 0 || dv > 256) return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_v %d not a multiple of 16 <= 256", dv);
+    if (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+        return fail(GDR_ERROR_INVALID_VALUE, "chunk_size %d not in {0, 16, 32, 64}", chunk_size);
+    if (dv_slice != 0 && dv_slice != 16 && dv_slice != 32 && dv_slice != 64)
+        return fail(GDR_ERROR_INVALID_VALUE, "dv_slice %d not in {0, 16, 32, 64}", dv_slice);
+    if (dv_slice != 0 && dv % dv_slice != 0)
+        return fail(GDR_ERROR_INVALID_VALUE, "dv_slice %d does not divide head_dim_v %d", dv_slice, dv);
+    // automatic choices: 64-token chunks for bf16 per-head decay, 32 for
+    // per-channel decay (its split Gram operands) and for fp32 operands;
+    // value slices of 32 channels while that still gives >= 1 workgroup per CU
+    int C = chunk_size ? chunk_size : ((bf16 && !kda) ? 64 : 32);
+    int DVS = dv_slice;
+    if (!DVS) {
+        const int64_t units = (int64_t)s.num_seqs * s.num_heads;
+        DVS = (!bf16 || dv % 32 != 0 || units * (dv / 32) < 256) ? 16 : 32;
+    }
+    if (!gdr::prefill_supported(bf16, kda, dk, DVS, C))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "no prefill kernel for %s dk=%d dv_slice=%d chunk=%d",
+                    bf16 ? "bf16" : "fp32", dk, DVS, C);
+
+    const size_t es = dsize(qkv_dtype);
+    const size_t nq = (size_t)tokens * s.num_heads * dk, nv = (size_t)tokens * s.num_heads * dv;
+    const size_t ng = (size_t)tokens * s.num_heads;
+    const size_t nla = kda ? ng * dk : ng;
+    const size_t nstate = (size_t)s.num_seqs * s.num_heads * dv * dk;
+    if (tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !out))
+        return fail(GDR_ERROR_INVALID_VALUE, "q, k, v, beta, log_alpha and out must be non-NULL");
+    const void *aligned16[] = {q, k, v, out, initial_state, final_state};
+    const char *names16[] = {"q", "k", "v", "out", "initial_state", "final_state"};
+    for (int i = 0; i < 6; ++i)
+        if (!aligned(aligned16[i], 16)) return fail(GDR_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", names16[i]);
+    if (!aligned(beta, 4) || !aligned(log_alpha, 4) || !aligned(cu_seqlens, 4))
+        return fail(GDR_ERROR_INVALID_VALUE, "beta, log_alpha and cu_seqlens must be 4-byte aligned");
+
+    const size_t need_ws = packed ? order_bytes(s.num_seqs) : 0;
+    if (workspace_bytes < need_ws)
+        return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need_ws);
+    if (need_ws && !workspace) return fail(GDR_ERROR_INVALID_VALUE, "workspace is NULL");
+    if (need_ws && !aligned(workspace, 256)) return fail(GDR_ERROR_INVALID_VALUE, "workspace is not 256-byte aligned");
+
+    const Range in[] = {range("q", q, nq * es), range("k", k, nq * es), range("v", v, nv * es),
+                        range("beta", beta, ng * 4), range("log_alpha", log_alpha, nla * 4),
+                        range("initial_state", initial_state, nstate * 4),
+                        range("cu_seqlens", cu_seqlens, packed ? 4 * ((size_t)s.num_seqs + 1) : 0)};
+    const Range ro = range("out", out, nv * dsize(out_dtype));
+    const Range rf = range("final_state", final_state, final_state ? nstate * 4 : 0);
+    const Range rw = range("workspace", workspace, need_ws);
+    for (const Range &r : in) {
+        if (overlaps(ro, r)) return fail(GDR_ERROR_INVALID_VALUE, "out overlaps %s", r.name);
+        if (overlaps(rw, r)) return fail(GDR_ERROR_INVALID_VALUE, "workspace overlaps %s", r.name);
+        if (overlaps(rf, r) && !(r.lo == reinterpret_cast<uintptr_t>(initial_state) && final_state == initial_state))
+            return fail(GDR_ERROR_INVALID_VALUE, "final_state overlaps %s", r.name);
+    }
+    if (overlaps(ro, rf) || overlaps(ro, rw) || overlaps(rf, rw))
+        return fail(GDR_ERROR_INVALID_VALUE, "out, final_state and workspace must not overlap");
+
+    if (tokens == 0 && !final_state) return ok();
+    gdr::PrefillArgs a{};
+    a.batch = s.batch;
+    a.seqlen = s.seqlen;
+    a.num_heads = s.num_heads;
+    a.dk = dk;
+    a.dv = dv;
+    a.num_seqs = s.num_seqs;
+    a.kda = kda;
+    a.bf16 = bf16;
+    a.out_bf16 = out_dtype == GDR_BF16;
+    a.chunk = C;
+    a.dv_slice = DVS;
+    a.q = q; a.k = k; a.v = v;
+    a.beta = static_cast<const float *>(beta);
+    a.log_alpha = static_cast<const float *>(log_alpha);
+    a.initial_state = initial_state;
+    a.cu_seqlens = cu_seqlens;
+    a.scale = scale;
+    a.out = out;
+    a.final_state = final_state;
+    a.order = static_cast<int32_t *>(workspace);
+    return launch_status(gdr::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_chunked");
+}
+
+gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                           gdr_gate gate, gdr_dtype qkv_dtype, gdr_dtype gate_dtype, gdr_dtype out_dtype,
+                           const void *q, const void *k, const void *v, const void *beta, const void *log_alpha, float *state, float scale,
+                           void *out, void *hip_stream) {
+    if (num_seqs < 0 || num_heads < 1 || head_dim_k < 1 || head_dim_v < 1)
+        return fail(GDR_ERROR_INVALID_VALUE, "bad shape (num_seqs=%d heads=%d dk=%d dv=%d)", num_seqs, num_heads,
+                    head_dim_k, head_dim_v);
+    if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
+    if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
+        return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d out=%d)", (int)qkv_dtype,
+                    (int)gate_dtype, (int)out_dtype);
+    if (gate_dtype != GDR_F32) return fail(GDR_ERROR_NOT_SUPPORTED, "gates must be fp32");
+    const int dk = head_dim_k, dv = head_dim_v;
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_k %d not in {16, 32, 64, 128}", dk);
+    if (dv % 4 != 0 || dv > 256) return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_v %d not a multiple of 4 <= 256", dv);
+    if ((int64_t)num_seqs * num_heads > INT32_MAX) return fail(GDR_ERROR_INVALID_VALUE, "too many heads");
+    if (num_seqs == 0) return ok();
+    if (!q || !k || !v || !beta || !log_alpha || !state || !out)
+        return fail(GDR_ERROR_INVALID_VALUE, "q, k, v, beta, log_alpha, state and out must be non-NULL");
+    const bool kda = gate == GDR_GATE_CHANNEL;
+    const bool bf16 = qkv_dtype == GDR_BF16;
+    const size_t es = dsize(qkv_dtype);
+    const size_t units = (size_t)num_seqs * num_heads;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(log_alpha, kda ? 16 : 4) ||
+        !aligned(v, es) || !aligned(out, dsize(out_dtype)) || !aligned(beta, 4))
+        return fail(GDR_ERROR_INVALID_VALUE, "misaligned pointer (q/k/state need 16 bytes)");
+    const Range in[] = {range("q", q, units * dk * es), range("k", k, units * dk * es),
+                        range("v", v, units * dv * es), range("beta", beta, units * 4),
+                        range("log_alpha", log_alpha, units * (kda ? dk : 1) * 4)};
+    const Range rs = range("state", state, units * dv * dk * 4);
+    const Range ro = range("out", out, units * dv * dsize(out_dtype));
+    for (const Range &r : in) {
+        if (overlaps(rs, r)) return fail(GDR_ERROR_INVALID_VALUE, "state overlaps %s", r.name);
+        if (overlaps(ro, r)) return fail(GDR_ERROR_INVALID_VALUE, "out overlaps %s", r.name);
+    }
+    if (overlaps(rs, ro)) return fail(GDR_ERROR_INVALID_VALUE, "out overlaps state");
+    gdr::DecodeArgs a{};
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.dk = dk;
+    a.dv = dv;
+    a.kda = kda;
+    a.bf16 = bf16;
+    a.out_bf16 = out_dtype == GDR_BF16;
+    a.q = q; a.k = k; a.v = v;
+    a.beta = static_cast<const float *>(beta);
+    a.log_alpha = static_cast<const float *>(log_alpha);
+    a.state = state;
+    a.scale = scale;
+    a.out = out;
+    return launch_status(gdr::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "gdr_decode_step");
+}
+
+}  // extern "C"

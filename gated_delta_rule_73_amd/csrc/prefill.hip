@@ -1,0 +1,57 @@
+// prefill.hip -- prefill dispatch and the packed-batch schedule.
+//
+// Packed batches (cu_seqlens) can hold sequences of very different lengths;
+// each (sequence, head, value slice) is one workgroup that walks its chunks
+// in order, so the longest sequence sets the critical path.  A tiny kernel
+// ranks the sequences longest first (ties by index, so the schedule is
+// deterministic) and the prefill kernel maps its workgroups in that order,
+// letting the long chains start first.
+#include "launch.h"
+#include "prefill_shapes.h"
+
+namespace gdr {
+
+hipError_t launch_prefill_bf16_gdn(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_prefill_bf16_kda(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_prefill_f32_gdn(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_prefill_f32_kda(const PrefillArgs &a, hipStream_t st);
+
+__global__ __launch_bounds__(256) void longest_first_kernel(const int32_t *__restrict__ cu, int n,
+                                                            int32_t *__restrict__ order) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int li = cu[i + 1] - cu[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+        const int lj = cu[j + 1] - cu[j];
+        rank += (lj > li) || (lj == li && j < i);
+    }
+    order[rank] = i;
+}
+
+bool prefill_supported(bool bf16, bool kda, int dk, int dv_slice, int chunk) {
+#define GDR_CASE(DK_, DVS_, C_) if (dk == DK_ && dv_slice == DVS_ && chunk == C_) return true;
+    if (bf16 && kda) {
+        GDR_PREFILL_BF16_KDA_SHAPES(GDR_CASE)
+    } else if (bf16) {
+        GDR_PREFILL_BF16_GDN_SHAPES(GDR_CASE)
+    } else {
+        GDR_PREFILL_F32_SHAPES(GDR_CASE)
+    }
+#undef GDR_CASE
+    return false;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
+    if (a.num_seqs == 0 || a.num_heads == 0) return hipSuccess;
+    if (a.cu_seqlens) {
+        hipLaunchKernelGGL(longest_first_kernel, dim3((unsigned)((a.num_seqs + 255) / 256)), dim3(256), 0, st,
+                           a.cu_seqlens, a.num_seqs, a.order);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.bf16) return a.kda ? launch_prefill_bf16_kda(a, st) : launch_prefill_bf16_gdn(a, st);
+    return a.kda ? launch_prefill_f32_kda(a, st) : launch_prefill_f32_gdn(a, st);
+}
+
+}  // namespace gdr

@@ -1,0 +1,16 @@
+// prefill_bf16_kda.hip -- instances of the chunked prefill kernel
+// (operand type __bf16, per-channel decay = true).
+#include "prefill_impl.h"
+#include "prefill_shapes.h"
+
+namespace gdr {
+
+hipError_t launch_prefill_bf16_kda(const PrefillArgs &a, hipStream_t st) {
+#define GDR_CASE(DK_, DVS_, C_) \
+    if (a.dk == DK_ && a.dv_slice == DVS_ && a.chunk == C_) return launch_prefill_t<DK_, DVS_, C_, true, __bf16>(a, st);
+    GDR_PREFILL_BF16_KDA_SHAPES(GDR_CASE)
+#undef GDR_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

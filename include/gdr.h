@@ -1,0 +1,190 @@
+/*
+ * gdr.h -- C ABI of libgdr, the gated delta-rule recurrence on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (page "How the New Flash Models Work: Inside GLM-5.3-Flash and
+ * Qwen3.8-Flash-Next", section "Linear attention: a fixed-size memory in place
+ * of the cache"): per head, a d_v x d_k state S is carried over the tokens of a
+ * sequence and updated once per token,
+ *
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = scale * S_t q_t,
+ *
+ * where alpha_t = exp(log_alpha_t) is one value per (token, head) for Gated
+ * DeltaNet (the section's first equation, decay "per head") and one value per
+ * key channel for Kimi Delta Attention (the section's second equation; page
+ * "GLM-5.3-Flash vs Qwen3.8-Flash-Next: Two Labs, One Architecture", section
+ * "The four shared design choices": KDA gates per channel, GDN per head).
+ * The state is held in FP32 (same first section: recurrent state is often
+ * held in FP32).  The pages print no query scale; `scale` multiplies the
+ * readout only and is 1 for the equations as printed.
+ *
+ * Two phases, as the pages' serving discussion separates them (page "How the
+ * New Flash Models Work...", section "Serving: prefill and decode are
+ * different problems"): a chunked prefill over whole prompts, and a decode
+ * step of one token per sequence that reads and writes the state in place.
+ * The prefill's final state has exactly the layout the decode step takes.
+ *
+ * Conventions for every call:
+ *  - Pointers named as device pointers must be device memory (or memory the
+ *    device can access); host pointers are read before the call returns.
+ *  - The caller owns and allocates every buffer (the recurrent state's
+ *    lifecycle -- retain, reuse, zero, evict -- is the caller's: page
+ *    "Qwen3.8-Flash-Next and GLM-5.3-Flash share a 3:1 long-context pattern",
+ *    section "Recurrent state and sparse caches need lifecycle controls").
+ *    The library allocates no device memory and keeps no pointer after a call
+ *    returns.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
+ *    and the call returns without synchronising.  Buffers must stay valid
+ *    until the stream has executed the work.
+ *  - Every argument is validated on the host before anything is enqueued; a
+ *    call that returns an error has enqueued nothing.  No call aborts or
+ *    throws.  gdr_last_error() gives a message for the last failure on the
+ *    calling thread.
+ *  - Results are bitwise deterministic run to run (no floating-point atomics).
+ *  - Inputs must be finite; log_alpha must be finite (a hard reset with
+ *    log_alpha = -inf is not supported).  These preconditions are not checked
+ *    (checking would need device reads).
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum gdr_status {
+    GDR_SUCCESS = 0,
+    GDR_ERROR_INVALID_VALUE = 1,        /* null pointer, bad size, misalignment, overlap */
+    GDR_ERROR_NOT_SUPPORTED = 2,        /* valid request outside the compiled kernel set */
+    GDR_ERROR_INSUFFICIENT_WORKSPACE = 3,
+    GDR_ERROR_LAUNCH_FAILED = 4         /* the HIP runtime refused a launch */
+} gdr_status;
+
+typedef enum gdr_dtype {
+    GDR_F32 = 0,
+    GDR_BF16 = 1
+} gdr_dtype;
+
+typedef enum gdr_gate {
+    GDR_GATE_HEAD = 0,      /* Gated DeltaNet: log_alpha has one value per (token, head)        */
+    GDR_GATE_CHANNEL = 1    /* Kimi Delta Attention: one value per (token, head, key channel)   */
+} gdr_gate;
+
+/*
+ * Problem shape of a prefill call.
+ *  Dense batch:  batch = B sequences of seqlen tokens each, num_seqs = B,
+ *                cu_seqlens = NULL.
+ *  Packed batch: batch = 1, seqlen = total tokens, num_seqs = N and
+ *                cu_seqlens[N+1] gives each sequence's token range.
+ */
+typedef struct gdr_prefill_shape {
+    int32_t batch;
+    int32_t seqlen;
+    int32_t num_heads;
+    int32_t head_dim_k;
+    int32_t head_dim_v;
+    int32_t num_seqs;
+} gdr_prefill_shape;
+
+/*
+ * Bytes of device workspace gdr_prefill_chunked needs for this shape: the
+ * per-call sequence schedule of a packed batch (packed != 0, i.e. cu_seqlens
+ * will be passed); 0 for a dense batch.  Returns 0 for a NULL shape.
+ */
+size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, int32_t packed);
+
+/*
+ * Chunked prefill: runs the recurrence over every token of every sequence and
+ * writes all outputs and each sequence's final state.
+ *
+ * Arguments (device pointers unless noted; row-major, contiguous):
+ *  shape          host pointer, see gdr_prefill_shape.
+ *  gate           GDR_GATE_HEAD or GDR_GATE_CHANNEL.
+ *  qkv_dtype      dtype of q, k and v: GDR_BF16 or GDR_F32.
+ *  gate_dtype     dtype of beta and log_alpha: GDR_F32.
+ *  out_dtype      dtype of out: GDR_F32 or GDR_BF16 (independent of q/k/v;
+ *                 bf16 outputs are rounded to nearest even from fp32).
+ *  q, k           [batch, seqlen, num_heads, head_dim_k]
+ *  v              [batch, seqlen, num_heads, head_dim_v]
+ *  beta           [batch, seqlen, num_heads]           write strengths (any finite value)
+ *  log_alpha      [batch, seqlen, num_heads]           (GDR_GATE_HEAD)
+ *                 [batch, seqlen, num_heads, head_dim_k] (GDR_GATE_CHANNEL)
+ *  initial_state  [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, or NULL
+ *                 for zeros.
+ *  cu_seqlens     NULL (dense) or int32 [num_seqs+1]: 0 = cu[0] <= cu[1] <=
+ *                 ... <= cu[N] = seqlen (not checked: device memory).  Empty
+ *                 sequences are allowed (their final state = initial state).
+ *  chunk_size     tokens per chunk: 0 = automatic, else 16, 32 or 64.
+ *  dv_slice       value channels one workgroup owns: 0 = automatic, else
+ *                 16, 32 or 64 (a divisor of head_dim_v).
+ *  scale          readout factor (1 for the printed equations).
+ *  out            [batch, seqlen, num_heads, head_dim_v], dtype out_dtype.
+ *                 Must not overlap any input.
+ *  final_state    [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, or NULL
+ *                 (not written).  May equal initial_state (updated in place)
+ *                 but must not partially overlap it or any other buffer.
+ *  workspace      device buffer of at least gdr_prefill_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0), 256-byte aligned.
+ *  hip_stream     hipStream_t to enqueue on.
+ * Limits: head_dim_k in {16, 32, 64, 128} (bf16: {32, 64, 128}); head_dim_v
+ * a multiple of 16 up to 256; the q/k/v/out/state base pointers 16-byte
+ * aligned; gate pointers 4-byte aligned.
+ * Returns GDR_SUCCESS or an error status (nothing enqueued on error).
+ */
+gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate,
+                               gdr_dtype qkv_dtype, gdr_dtype gate_dtype, gdr_dtype out_dtype,
+                               const void *q, const void *k, const void *v,
+                               const void *beta, const void *log_alpha,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t chunk_size, int32_t dv_slice, float scale,
+                               void *out, float *final_state,
+                               void *workspace, size_t workspace_bytes,
+                               void *hip_stream);
+
+/*
+ * Decode step: one new token for each of num_seqs sequences.  Reads each
+ * (sequence, head) state once, applies the decay, the erase-then-write update
+ * and the readout, and writes the state back in place.
+ *
+ *  q, k       [num_seqs, num_heads, head_dim_k]   dtype qkv_dtype
+ *  v          [num_seqs, num_heads, head_dim_v]   dtype qkv_dtype
+ *  beta       [num_seqs, num_heads]               fp32
+ *  log_alpha  [num_seqs, num_heads] (GDR_GATE_HEAD) or
+ *             [num_seqs, num_heads, head_dim_k] (GDR_GATE_CHANNEL), fp32
+ *  state      [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, read and
+ *             written in place (must not overlap any other argument)
+ *  out        [num_seqs, num_heads, head_dim_v]   dtype out_dtype (GDR_F32 or
+ *             GDR_BF16, rounded to nearest even)
+ * Limits: head_dim_k in {16, 32, 64, 128}; head_dim_v a multiple of 4 up to
+ * 256; base pointers 16-byte aligned (gates 4-byte).
+ */
+gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k,
+                           int32_t head_dim_v, gdr_gate gate, gdr_dtype qkv_dtype,
+                           gdr_dtype gate_dtype, gdr_dtype out_dtype, const void *q, const void *k,
+                           const void *v, const void *beta, const void *log_alpha,
+                           float *state, float scale, void *out, void *hip_stream);
+
+/* Bytes of fp32 recurrent state for num_seqs x num_heads heads of d_v x d_k
+ * (the per-layer state the pages size in their state-size table). */
+uint64_t gdr_state_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim_k, int64_t head_dim_v);
+
+/* Static description of a status code. */
+const char *gdr_status_string(gdr_status status);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char *gdr_last_error(void);
+
+/* GDR_ABI_VERSION of the built library. */
+int gdr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

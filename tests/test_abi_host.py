@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/gdr.h declares, and rejects bad arguments with the
+documented status before touching the device."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_73_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gdr.library_path), reason="libgdr.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gdr.load_library()
+    names = declared_functions()
+    assert "gdr_prefill_chunked" in names and "gdr_decode_step" in names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    lib = gdr.load_library()
+    assert lib.gdr_abi_version() == 1
+    assert lib.gdr_status_string(0) == b"success"
+    assert lib.gdr_status_string(2) == b"not supported"
+
+
+def test_state_bytes_match_printed_table():
+    rows = json.load(open(os.path.join(GOLDEN, "state_sizes.json")))["rows"]
+    for r in rows:
+        per_layer = gdr.gdr_state_bytes(1, r["heads"], r["dk"], r["dv"])  # fp32 bytes
+        values = per_layer // 4
+        assert round(values / 1e6, 2) == r["per_layer_values_millions"]
+        assert round(values * r["layers"] / 1e6, 1) == r["all_layers_values_millions"]
+        assert round(values * r["layers"] * 2 / 1e6) == r["all_layers_bf16_MB"]   # bf16: 2 bytes
+        assert per_layer == 2 * values * 2                                          # fp32 doubles bf16
+
+
+# ---- validation: every call below must fail on the host ---------------------
+A = 0x10000000  # fake, suitably aligned "device" addresses; never dereferenced
+MB = 1 << 20
+
+
+def _prefill(shape=(1, 64, 2, 64, 64, 1), gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + 8 * MB, v=A + 16 * MB, beta=A + 24 * MB,
+             la=A + 25 * MB, s0=None, cu=None, chunk=0, dvs=0, out=A + 32 * MB, fin=None, ws=None, wsb=0):
+    lib = gdr.load_library()
+    sh = gdr.PrefillShape(*shape)
+    v_ = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_prefill_chunked(ctypes.byref(sh), gate, qkv, gdt, odt, v_(q), v_(k), v_(v), v_(beta), v_(la), v_(s0),
+                                 v_(cu), chunk, dvs, 1.0, v_(out), v_(fin), v_(ws), wsb, None)
+    return st, lib.gdr_last_error().decode()
+
+
+def _decode(N=4, H=2, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + MB, v=A + 2 * MB, beta=A + 3 * MB,
+            la=A + 4 * MB, state=A + 8 * MB, out=A + 64 * MB):
+    lib = gdr.load_library()
+    v_ = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_decode_step(N, H, dk, dv, gate, qkv, gdt, odt, v_(q), v_(k), v_(v), v_(beta), v_(la), v_(state), 1.0,
+                             v_(out), None)
+    return st, lib.gdr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(shape=(0, 64, 2, 64, 64, 0)), 1, "bad shape"),
+    (dict(shape=(1, 64, 0, 64, 64, 1)), 1, "bad shape"),
+    (dict(gate=7), 1, "gate"),
+    (dict(qkv=5), 1, "dtype"),
+    (dict(odt=9), 1, "dtype"),
+    (dict(gdt=1), 2, "fp32"),
+    (dict(shape=(1, 64, 2, 48, 64, 1)), 2, "head_dim_k"),
+    (dict(shape=(1, 64, 2, 64, 40, 1)), 2, "head_dim_v"),
+    (dict(shape=(1, 64, 2, 16, 64, 1)), 2, "no prefill kernel"),        # bf16 needs dk >= 32
+    (dict(chunk=48), 1, "chunk_size"),
+    (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 needs chunks of 32 or 64
+    (dict(dvs=48), 1, "dv_slice"),
+    (dict(shape=(1, 64, 2, 64, 48, 1), dvs=32), 1, "does not divide"),
+    (dict(shape=(2, 64, 2, 64, 64, 1)), 1, "num_seqs == batch"),
+    (dict(shape=(2, 64, 2, 64, 64, 2), cu=A + 40 * MB), 1, "batch == 1"),
+    (dict(q=None), 1, "non-NULL"),
+    (dict(q=A + 2), 1, "16-byte aligned"),
+    (dict(out=A + 8 * MB + 64), 1, "out overlaps k"),
+    (dict(out=A - 32 * 1024 + 16, odt=0), 1, "out overlaps q"),     # fp32 out is 32 KiB here
+    (dict(out=A - 32 * 1024 + 16, odt=1), 0, None),                 # bf16 out (16 KiB) stops short of q
+    (dict(fin=A + 8 * MB), 1, "final_state overlaps k"),
+    (dict(s0=A + 40 * MB, fin=A + 40 * MB + 16), 1, "final_state overlaps initial_state"),
+    (dict(cu=A + 40 * MB, ws=None, wsb=0), 3, "workspace"),
+    (dict(cu=A + 40 * MB, ws=None, wsb=4096), 1, "workspace is NULL"),
+    (dict(cu=A + 40 * MB, ws=A + 48 * MB + 4, wsb=4096), 1, "256-byte"),
+])
+def test_prefill_rejects(kw, status, msg):
+    if status == 0:
+        # passes validation; stop before the launch by making it unsupported instead
+        kw = dict(kw, chunk=16)
+        st, err = _prefill(**kw)
+        assert st == 2 and "no prefill kernel" in err
+        return
+    st, err = _prefill(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_prefill_workspace_size():
+    lib = gdr.load_library()
+    sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9)
+    assert lib.gdr_prefill_workspace_bytes(ctypes.byref(sh), 0) == 0
+    ws = lib.gdr_prefill_workspace_bytes(ctypes.byref(sh), 1)
+    assert ws >= 9 * 4 and ws % 256 == 0
+    assert lib.gdr_prefill_workspace_bytes(None, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(N=-1), 1, "bad shape"),
+    (dict(gate=3), 1, "gate"),
+    (dict(gdt=1), 2, "fp32"),
+    (dict(dk=96), 2, "head_dim_k"),
+    (dict(dv=66), 2, "head_dim_v"),
+    (dict(state=None), 1, "non-NULL"),
+    (dict(q=A + 8), 1, "misaligned"),
+    (dict(state=A + MB), 1, "state overlaps k"),
+    (dict(out=A + 8 * MB), 1, "out overlaps state"),
+])
+def test_decode_rejects(kw, status, msg):
+    st, err = _decode(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_decode_zero_sequences_is_a_noop():
+    st, _ = _decode(N=0, q=None, k=None, v=None, beta=None, la=None, state=None, out=None)
+    assert st == 0
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(Exception):
+        gdr.gdr_prefill_chunked(q, q, q, torch.zeros(1, 4, 1, dtype=torch.float32),
+                                torch.zeros(1, 4, 1, 3, 3))

@@ -1,0 +1,220 @@
+"""Chunked prefill on the GPU vs the fp64 oracle (sequential recurrence)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_73_amd as gdr
+import oracle
+from parity import TOL, assert_close, assert_close_rounded, gpu_available, say, to_np
+from workloads import WORKLOADS, Workload, packed_lengths, prefill_inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
+DEV = "cuda"
+
+
+def _gpu(inp, **kw):
+    out, fin = gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                       initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def _oracle(inp):
+    cu = inp["cu_seqlens"]
+    return oracle.recurrence(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                             initial_state=inp["initial_state"],
+                             seq_bounds=None if cu is None else cu.cpu().numpy())
+
+
+def _check_all(inp, label, **kw):
+    say(f"prefill {label} {kw}")
+    out, fin = _gpu(inp, **kw)
+    ref_o, ref_s = _oracle(inp)
+    tol = TOL[inp["q"].dtype]
+    assert_close("out", out, ref_o, tol)
+    assert_close("final_state", fin, ref_s, tol)
+    return out, fin
+
+
+def _small(dk, dv, H, T, gate, dtype, init, seed, B=1, lengths=None):
+    w = Workload("small", "prefill", heads=H, dk=dk, dv=dv, qkv_dtype=dtype, gate=gate, batch=B, seqlen=T,
+                 init_state=init, seed=seed)
+    return prefill_inputs(w, DEV, lengths=lengths)
+
+
+# ------------------------------------------------------------ workloads ----
+def test_tiny_gdn_workload():
+    """B=1, H=2, T=64, d=16, fp32, chunk 16, zero initial state."""
+    w = WORKLOADS["tiny_gdn"]
+    _check_all(prefill_inputs(w, DEV), "tiny_gdn", chunk_size=w.chunk)
+
+
+def test_gdn_prefill_8k_workload():
+    """B=1, H=16, T=8192, d=128, bf16 q/k/v, per-head decay, chunk 64."""
+    w = WORKLOADS["gdn_prefill_8k"]
+    _check_all(prefill_inputs(w, DEV), "gdn_prefill_8k", chunk_size=w.chunk)
+
+
+def _check_sampled(inp, units, label, **kw):
+    """Full-size GPU run; oracle on sampled (sequence, head) units."""
+    say(f"prefill {label} (sampled units {units}) {kw}")
+    out, fin = _gpu(inp, **kw)
+    cu = inp["cu_seqlens"]
+    tol = TOL[inp["q"].dtype]
+    for (n, h) in units:
+        if cu is None:
+            sl = (slice(n, n + 1), slice(None), slice(h, h + 1))
+            lo, hi = None, None
+        else:
+            bounds = cu.cpu().numpy()
+            lo, hi = int(bounds[n]), int(bounds[n + 1])
+            sl = (slice(0, 1), slice(lo, hi), slice(h, h + 1))
+        sub = {key: inp[key][sl].contiguous() for key in ("q", "k", "v", "beta", "log_alpha")}
+        s0 = inp["initial_state"]
+        s0 = None if s0 is None else s0[n:n + 1, h:h + 1].contiguous()
+        ref_o, ref_s = oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["beta"], sub["log_alpha"],
+                                         initial_state=s0)
+        assert_close(f"out[{n},{h}]", out[sl], ref_o, tol)
+        assert_close(f"final_state[{n},{h}]", fin[n:n + 1, h:h + 1], ref_s, tol)
+    return out, fin
+
+
+@pytest.mark.slow
+def test_kda_prefill_32k_workload():
+    """B=2, H=32, T=32768, d=128, bf16, per-channel decay, S0 ~ N(0, 0.02^2);
+    every output is produced by the GPU, four (sequence, head) units are
+    checked against the oracle, and the whole output is checked for finiteness."""
+    w = WORKLOADS["kda_prefill_32k"]
+    inp = prefill_inputs(w, DEV)
+    out, fin = _check_sampled(inp, [(0, 0), (0, 17), (1, 5), (1, 31)], "kda_prefill_32k")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(fin).all()
+
+
+@pytest.mark.slow
+def test_packed_gdn_256k_workload():
+    """262144 tokens as 8 packed sequences (4096..61440 each), H=16, d=128."""
+    w = WORKLOADS["packed_gdn_256k"]
+    inp = prefill_inputs(w, DEV)
+    lens = np.diff(inp["cu_seqlens"].cpu().numpy())
+    longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
+    out, fin = _check_sampled(inp, [(longest, 0), (shortest, 15), (3, 7)], "packed_gdn_256k")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(fin).all()
+
+
+# -------------------------------------------------------- shape sweeps ----
+BF16_CASES = [
+    # dk, dv, H, T, gate, init, chunk, dv_slice
+    (128, 128, 2, 1, "head", False, 64, 32),
+    (128, 128, 2, 63, "channel", True, 32, 32),
+    (128, 128, 1, 64, "head", True, 64, 16),
+    (128, 128, 3, 65, "channel", False, 32, 16),
+    (128, 128, 2, 197, "head", True, 32, 32),
+    (128, 128, 2, 197, "channel", True, 32, 16),
+    (128, 64, 1, 300, "channel", True, 32, 32),
+    (64, 64, 3, 130, "head", True, 64, 32),
+    (64, 32, 2, 129, "channel", True, 32, 16),
+    (32, 32, 1, 95, "head", False, 32, 32),
+    (32, 48, 2, 100, "channel", True, 32, 16),
+    (32, 48, 2, 100, "head", True, 64, 16),
+]
+
+
+@pytest.mark.parametrize("dk,dv,H,T,gate,init,chunk,dvs", BF16_CASES)
+def test_prefill_bf16_shapes(dk, dv, H, T, gate, init, chunk, dvs):
+    inp = _small(dk, dv, H, T, gate, torch.bfloat16, init, seed=dk + dv + T + H)
+    _check_all(inp, f"bf16 dk={dk} dv={dv} H={H} T={T} {gate} init={init}", chunk_size=chunk, dv_slice=dvs)
+
+
+F32_CASES = [
+    (16, 16, 2, 1, "head", False, 16),
+    (16, 16, 2, 17, "channel", True, 16),
+    (32, 16, 1, 15, "head", True, 16),
+    (32, 32, 2, 70, "channel", True, 32),
+    (64, 48, 1, 33, "head", True, 32),
+    (128, 64, 2, 100, "channel", True, 32),
+    (128, 32, 1, 16, "head", False, 16),
+]
+
+
+@pytest.mark.parametrize("dk,dv,H,T,gate,init,chunk", F32_CASES)
+def test_prefill_f32_shapes(dk, dv, H, T, gate, init, chunk):
+    inp = _small(dk, dv, H, T, gate, torch.float32, init, seed=7 * dk + T)
+    _check_all(inp, f"fp32 dk={dk} dv={dv} H={H} T={T} {gate}", chunk_size=chunk)
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_dense_batch(gate):
+    inp = _small(128, 128, 3, 150, gate, torch.bfloat16, True, seed=31, B=3)
+    _check_all(inp, f"dense B=3 {gate}")
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_packed_with_empty_and_ragged(gate):
+    lens = [70, 0, 1, 129, 64, 0, 200]
+    inp = _small(128, 64, 2, 0, gate, torch.bfloat16, True, seed=41, lengths=lens)
+    _, fin = _check_all(inp, f"packed {lens} {gate}")
+    assert torch.equal(fin[1], inp["initial_state"][1]) and torch.equal(fin[5], inp["initial_state"][5])
+
+
+# ------------------------------------------------------- GPU properties ----
+def test_prefill_deterministic():
+    inp = _small(128, 128, 2, 333, "channel", torch.bfloat16, True, seed=51)
+    o1, s1 = _gpu(inp)
+    o2, s2 = _gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("gate,chunks", [("head", (32, 64)), ("channel", (32,))])
+def test_prefill_chunk_and_slice_invariance(gate, chunks):
+    inp = _small(128, 128, 2, 256, gate, torch.bfloat16, True, seed=52)
+    ref_o, ref_s = _oracle(inp)
+    for chunk in chunks:
+        for dvs in (16, 32):
+            say(f"chunk {chunk} dv_slice {dvs}")
+            o, s = _gpu(inp, chunk_size=chunk, dv_slice=dvs)
+            assert_close("out", o, ref_o, TOL[torch.bfloat16])
+            assert_close("final_state", s, ref_s, TOL[torch.bfloat16])
+
+
+def test_prefill_in_place_state_and_poisoned_output():
+    inp = _small(128, 128, 2, 100, "head", torch.bfloat16, True, seed=53)
+    ref_o, ref_s = _oracle(inp)
+    state = inp["initial_state"].clone()
+    out = torch.full(inp["v"].shape, float("nan"), dtype=torch.float32, device=DEV)
+    gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], initial_state=state,
+                            out=out, final_state=state)
+    torch.cuda.synchronize()
+    assert_close("out", out, ref_o, TOL[torch.bfloat16])
+    assert_close("final_state (in place)", state, ref_s, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_bf16_output(gate):
+    inp = _small(128, 128, 2, 190, gate, torch.bfloat16, True, seed=55)
+    ref_o, ref_s = _oracle(inp)
+    out, fin = _gpu(inp, out_dtype=torch.bfloat16)
+    assert out.dtype == torch.bfloat16
+    assert_close_rounded("out (bf16)", out, ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", fin, ref_s, TOL[torch.bfloat16])
+
+
+def test_prefill_continuation_then_decode():
+    """prefill(x[:T1]) -> prefill(x[T1:T2], S) -> decode steps: every piece
+    matches the oracle's single pass over the whole sequence (the prefill's
+    final state is the decode step's input, unchanged in layout)."""
+    T, T1, T2 = 200, 77, 190
+    inp = _small(128, 128, 2, T, "channel", torch.bfloat16, True, seed=54)
+    ref_o, ref_s = _oracle(inp)
+    part = lambda a, b: {**{k_: inp[k_][:, a:b].contiguous() for k_ in ("q", "k", "v", "beta", "log_alpha")},
+                         "cu_seqlens": None}
+    o1, s1 = _gpu({**part(0, T1), "initial_state": inp["initial_state"]})
+    o2, s2 = _gpu({**part(T1, T2), "initial_state": s1})
+    outs = [o1, o2]
+    state = s2
+    for t in range(T2, T):
+        o = gdr.gdr_decode_step(inp["q"][:, t].contiguous(), inp["k"][:, t].contiguous(), inp["v"][:, t].contiguous(),
+                                inp["beta"][:, t].contiguous(), inp["log_alpha"][:, t].contiguous(), state)
+        outs.append(o[:, None])
+    torch.cuda.synchronize()
+    assert_close("out", torch.cat(outs, dim=1), ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", state, ref_s, TOL[torch.bfloat16])
