@@ -1,0 +1,228 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+One step = one chunked prefill of the Kimi-Delta-Attention workload
+(B=2, T=32768, H=32, d=128, bf16 q/k/v, fp32 gates and state) followed by one
+decode step of 256 sequences x 32 heads (128x128 fp32 states, in place) with
+per-head decay and one with per-channel decay.  Prints one JSON line.
+
+value = prefill throughput (B*T tokens, all heads) in Mtok/s.  Per-kernel
+times come from HIP events on the stream the kernels are launched on, over
+the timed steps.  The roofline object reports the prefill kernel against HBM
+bandwidth (its algorithmic intensity, ~73 flop/byte, is far below the bf16
+MFMA ridge of ~310 flop/byte); the MFMA fraction of the same kernel is
+reported beside it.  cpu_baseline times the fp64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PROFILE_PMC = os.path.join(ROOT, "profiles", "prefill_kda_32k_traffic.json")
+KERNEL_SOURCES = ["prefill_impl.h", "prefill_shapes.h", "prefill_bf16_kda.hip", "gdr_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_73_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_alg_bytes(B, T, H, dk, dv, kda, out_bytes, init_state=True, final_state=True):
+    tok = B * T * H
+    b = tok * (2 * dk + dv) * 2                  # q, k, v (bf16)
+    b += tok * 4                                 # beta
+    b += tok * (dk if kda else 1) * 4            # log alpha (fp32)
+    b += tok * dv * out_bytes                    # out
+    b += (int(init_state) + int(final_state)) * B * H * dv * dk * 4
+    return b
+
+
+def prefill_alg_flops(B, T, H, dk, dv, C):
+    # dense chunk products of the chunked form, full C x C tiles
+    return B * T * H * (4 * C * (dk + dv) + 6 * dk * dv)
+
+
+def decode_alg_bytes(N, H, dk, dv, kda, out_bytes):
+    u = N * H
+    return u * (2 * dv * dk * 4 + (2 * dk + dv) * 2 + 4 + (dk if kda else 1) * 4 + dv * out_bytes)
+
+
+def cpu_baseline(inp, H, target_s):
+    """fp64 oracle on the first tokens of every (sequence, head) unit of the
+    prefill workload, timed on the host cores; the token count is sized from
+    a short calibration run so the measured run takes about target_s."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    B, T = inp["q"].shape[:2]
+    threads = min(cores, B * H)
+    s0 = inp["initial_state"].cpu()
+
+    def run(n):
+        sub = {k: inp[k][:, :n].contiguous().cpu() for k in ("q", "k", "v", "beta", "log_alpha")}
+        t0 = time.perf_counter()
+        oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["beta"], sub["log_alpha"], initial_state=s0,
+                          num_threads=threads)
+        return time.perf_counter() - t0
+
+    probe = 128
+    dt = run(probe)
+    sample_tokens = int(min(T, max(probe, probe * target_s / max(dt, 1e-3))))
+    dt = run(sample_tokens)
+    tokens = B * sample_tokens  # every head of these tokens
+    return {"value": tokens / dt / 1e6, "unit": "Mtok/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_tokens} of {inp['q'].shape[1]} tokens of all {B}x{H} (sequence, head) "
+                      f"units of the prefill workload, fp64, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--dv-slice", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="also run one 1 GiB device copy (a known-size kernel for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_73_amd as gdr
+    from workloads import WORKLOADS, decode_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp = WORKLOADS["kda_prefill_32k"]
+    wd = WORKLOADS["decode_256x32"]
+    print(f"[bench] generating inputs ({wp.name}, {wd.name})", file=sys.stderr, flush=True)
+    inp = prefill_inputs(wp, dev)
+    dec = {g: decode_inputs(wd, dev, gate=g) for g in ("head", "channel")}
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[-1]
+    out = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+    fin = torch.empty_like(inp["initial_state"])
+    dout = {g: torch.empty(wd.batch, wd.heads, wd.dv, dtype=torch.float32, device=dev) for g in dec}
+
+    def prefill():
+        gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                initial_state=inp["initial_state"], chunk_size=args.chunk,
+                                dv_slice=args.dv_slice, out=out, final_state=fin)
+
+    def decode(g):
+        d = dec[g]
+        gdr.gdr_decode_step(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["state"], out=dout[g])
+
+    if args.copy_reference:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        prefill()
+        decode("head")
+        decode("channel")
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record()
+        prefill()
+        e[1].record()
+        decode("head")
+        e[2].record()
+        decode("channel")
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    t_pre = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps / 1e3   # s per launch
+    t_dg = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps / 1e3
+    t_dk = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps / 1e3
+
+    chunk = args.chunk or 32
+    tokens = B * T
+    pre_bytes = prefill_alg_bytes(B, T, H, dk, dv, True, 4)
+    pre_flops = prefill_alg_flops(B, T, H, dk, dv, chunk)
+    dg_bytes = decode_alg_bytes(wd.batch, wd.heads, wd.dk, wd.dv, False, 4)
+    dk_bytes = decode_alg_bytes(wd.batch, wd.heads, wd.dk, wd.dv, True, 4)
+    pre_gbs = pre_bytes / t_pre / 1e9
+
+    traffic = None
+    if os.path.exists(PROFILE_PMC):
+        rec = json.load(open(PROFILE_PMC))
+        if rec.get("kernel_source_hash") == kernel_source_hash() and rec.get("chunk") == chunk:
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": "delta-rule prefill Mtok/s at T=32K (MFMA %) + decode step HBM GB/s (% peak)",
+        "value": round(tokens / t_pre / 1e6, 3),
+        "unit": "Mtok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "kda_prefill_32k + decode_256x32 (per-head and per-channel decay)",
+            "prefill": {"batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv, "gate": "per-channel",
+                        "chunk": chunk, "dv_slice": args.dv_slice or "auto", "initial_state": True,
+                        "out_dtype": "fp32"},
+            "decode": {"num_seqs": wd.batch, "heads": wd.heads, "d_k": wd.dk, "d_v": wd.dv,
+                       "state": "fp32 in place", "out_dtype": "fp32"},
+            "precision": "bf16 q/k/v, fp32 gates and states; fp16/bf16 MFMA operands (hi/lo split on the "
+                         "value-carrying ones), fp32 accumulation",
+        },
+        "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "prefill_kernel<128,32,32,KDA,bf16>",
+                     "alg_bytes_per_launch": pre_bytes, "avg_launch_us": round(t_pre * 1e6, 2)},
+        "prefill": {"us_per_launch": round(t_pre * 1e6, 2), "Mtok_s": round(tokens / t_pre / 1e6, 3),
+                    "mfma_frac": round(pre_flops / t_pre / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
+                    "alg_flops": pre_flops, "hbm_GBps": round(pre_gbs, 1)},
+        "decode": {
+            "per_head_decay": {"us_per_step": round(t_dg * 1e6, 2), "GBps": round(dg_bytes / t_dg / 1e9, 1),
+                               "frac_of_hbm_peak": round(dg_bytes / t_dg / 1e9 / HBM_PEAK_GBS, 4),
+                               "Mtok_s": round(wd.batch / t_dg / 1e6, 4), "alg_bytes": dg_bytes},
+            "per_channel_decay": {"us_per_step": round(t_dk * 1e6, 2), "GBps": round(dk_bytes / t_dk / 1e9, 1),
+                                  "frac_of_hbm_peak": round(dk_bytes / t_dk / 1e9 / HBM_PEAK_GBS, 4),
+                                  "Mtok_s": round(wd.batch / t_dk / 1e6, 4), "alg_bytes": dk_bytes},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inp, H, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
