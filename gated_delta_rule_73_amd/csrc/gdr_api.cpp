@@ -127,15 +127,15 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
         return fail(GDR_ERROR_INVALID_VALUE, "dv_slice %d not in {0, 16, 32, 64}", dv_slice);
     if (dv_slice != 0 && dv % dv_slice != 0)
         return fail(GDR_ERROR_INVALID_VALUE, "dv_slice %d does not divide head_dim_v %d", dv_slice, dv);
-    // automatic choices: 64-token chunks for bf16 per-head decay, 32 for
-    // per-channel decay (its split Gram operands) and for fp32 operands;
+    // automatic choices: 32-token chunks (16 where 32 is not compiled);
     // value slices of 32 channels while that still gives >= 1 workgroup per CU
-    int C = chunk_size ? chunk_size : ((bf16 && !kda) ? 64 : 32);
+    int C = chunk_size;
     int DVS = dv_slice;
     if (!DVS) {
         const int64_t units = (int64_t)s.num_seqs * s.num_heads;
         DVS = (!bf16 || dv % 32 != 0 || units * (dv / 32) < 256) ? 16 : 32;
     }
+    if (!C) C = gdr::prefill_supported(bf16, kda, dk, DVS, 32) ? 32 : 16;
     if (!gdr::prefill_supported(bf16, kda, dk, DVS, C))
         return fail(GDR_ERROR_NOT_SUPPORTED, "no prefill kernel for %s dk=%d dv_slice=%d chunk=%d",
                     bf16 ? "bf16" : "fp32", dk, DVS, C);

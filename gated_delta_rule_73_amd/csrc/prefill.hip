@@ -35,8 +35,10 @@ bool prefill_supported(bool bf16, bool kda, int dk, int dv_slice, int chunk) {
         GDR_PREFILL_BF16_KDA_SHAPES(GDR_CASE)
     } else if (bf16) {
         GDR_PREFILL_BF16_GDN_SHAPES(GDR_CASE)
+    } else if (kda) {
+        GDR_PREFILL_F32_KDA_SHAPES(GDR_CASE)
     } else {
-        GDR_PREFILL_F32_SHAPES(GDR_CASE)
+        GDR_PREFILL_F32_GDN_SHAPES(GDR_CASE)
     }
 #undef GDR_CASE
     return false;

@@ -8,7 +8,7 @@ namespace gdr {
 hipError_t launch_prefill_f32_gdn(const PrefillArgs &a, hipStream_t st) {
 #define GDR_CASE(DK_, DVS_, C_) \
     if (a.dk == DK_ && a.dv_slice == DVS_ && a.chunk == C_) return launch_prefill_t<DK_, DVS_, C_, false, float>(a, st);
-    GDR_PREFILL_F32_SHAPES(GDR_CASE)
+    GDR_PREFILL_F32_GDN_SHAPES(GDR_CASE)
 #undef GDR_CASE
     return hipErrorInvalidValue;
 }

@@ -14,19 +14,29 @@
 //     X   = (K e^g) S0^T,   W = diag(b)(V - X),   U = T W
 //     O   = (Q e^g) S0^T + M U,   M = tril((Q e^g)(K e^-g)^T)
 //     S_C = S0 Diag(e^{g_C}) + U^T (K e^{g_C - g}).
-// Rows of S (value channels) evolve independently, so a workgroup owns a
-// slice of DVS value channels of one (sequence, head) and walks its chunks in
-// order; the key-side work (Gram, T) is recomputed by each slice.
+//
+// Work split.  One workgroup owns a slice of DVS value channels of one
+// (sequence, head): rows of S evolve independently, so slices never talk.
+// Inside the workgroup, four "prologue" waves build everything a chunk needs
+// that does not depend on the state (gate prefix sums, decayed operands,
+// Gram matrices, T), one chunk ahead, into a double buffer; one "chain" wave
+// per 16 value channels walks the chunks in order, holding its part of the
+// state transposed (S^T: key rows x value columns) as fp32 MFMA accumulators.
+// In that layout the state, W and U feed the next product straight from
+// registers (each lane's accumulator rows are exactly the k-indices its
+// MFMA operand fragment needs), so the sequential chain X -> W -> U -> (O, S)
+// touches LDS only to read the prologue's shared operands.  Global inputs of
+// chunk j+1 are prefetched into registers while chunk j is built.
 //
 // Precision (bf16 q/k/v).  Outputs reach ~15x their RMS, so an error bound of
 // 2e-2 x RMS on the largest element needs ~1e-3 relative accuracy on the
 // terms that carry v; one bf16 rounding (2^-8) of those terms is too coarse.
-// The products therefore run on fp16 MFMA (11-bit operands) with the value-
-// carrying operands W and U split into an fp16 hi + lo pair (two MFMAs each),
-// and the per-channel decay Gram M of Kimi Delta Attention from bf16 hi + lo
-// pairs (three MFMAs: hi.hi + hi.lo + lo.hi).  The Gram A that feeds T keeps
-// single bf16 operands: the delta rule's erase step corrects what an error in
-// T leaves behind.  fp32 q/k/v use fp32 MFMA throughout.
+// The products run on fp16 MFMA (11-bit operands) with the value-carrying
+// operands W and U split into an fp16 hi + lo pair (two MFMAs each), and the
+// per-channel-decay Gram M from bf16 hi + lo pairs (three MFMAs: hi.hi +
+// hi.lo + lo.hi).  The Gram A that feeds T keeps single bf16 operands: the
+// delta rule's erase step corrects what an error in T leaves behind.  fp32
+// q/k/v use fp32 MFMA throughout.
 //
 // Exponent range.  Gated DeltaNet: the decay is a per-row scalar; raw k/q
 // (exact in fp16) feed the products and e^{g_r - g_i} <= 1 scales the fp32
@@ -43,6 +53,7 @@
 namespace gdr {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // ---- MFMA traits: 16x16 fp32 tile, K advanced KSTEP per instruction -------
 // Lane l holds row (l & 15) of each 16-row operand and KPL consecutive
@@ -75,17 +86,106 @@ template <> struct Mfma<float> {
     }
 };
 
-// acc += A[16 rows] * B[16 rows]^T over k in [k0, k1); both row-major in LDS
+// acc += A[16 rows] * B[16 rows]^T over k in [0, K); both row-major in LDS
 // with k contiguous (leading dimensions lda, ldb, in elements).
-template <typename OT>
-__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const OT *A, int lda, const OT *B, int ldb, int k0, int k1,
-                                          int lane) {
+template <typename OT, int K>
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const OT *A, int lda, const OT *B, int ldb, int lane) {
     using M = Mfma<OT>;
     const OT *pa = A + (lane & 15) * lda + (lane >> 4) * M::KPL;
     const OT *pb = B + (lane & 15) * ldb + (lane >> 4) * M::KPL;
-    for (int k = k0; k < k1; k += M::KSTEP) acc = M::mma(M::load(pa + k), M::load(pb + k), acc);
+#pragma unroll
+    for (int k = 0; k < K; k += M::KSTEP) acc = M::mma(M::load(pa + k), M::load(pb + k), acc);
     return acc;
 }
+
+// ---- operands held in registers in the accumulator layout ------------------
+// A k-dimension of NBLK 16-blocks held as fp32 accumulator tiles v[blk]
+// (lane: k-indices 16*blk + 4*lg + i).  As an MFMA B operand it is consumed
+// with the A operand read from LDS at the same k-indices.
+template <typename ST, int NBLK> struct RegB;
+template <int NBLK> struct RegB<_Float16, NBLK> {
+    static_assert(NBLK % 2 == 0, "fp16 k-steps span two 16-blocks");
+    f16x8 f[NBLK / 2];
+    __device__ __forceinline__ void set(const f32x4 *v) {
+#pragma unroll
+        for (int s = 0; s < NBLK / 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[s][i] = (_Float16)v[2 * s][i];
+                f[s][4 + i] = (_Float16)v[2 * s + 1][i];
+            }
+    }
+    // split v = hi + lo: this object takes hi, `lo` takes the remainder
+    __device__ __forceinline__ void set_split(const f32x4 *v, RegB &lo) {
+#pragma unroll
+        for (int s = 0; s < NBLK / 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const _Float16 h0 = (_Float16)v[2 * s][i], h1 = (_Float16)v[2 * s + 1][i];
+                f[s][i] = h0;
+                f[s][4 + i] = h1;
+                lo.f[s][i] = (_Float16)(v[2 * s][i] - (float)h0);
+                lo.f[s][4 + i] = (_Float16)(v[2 * s + 1][i] - (float)h1);
+            }
+    }
+    // acc += A * B, A given as preloaded fragments (RowA) of the same k-range
+    template <class RA>
+    __device__ __forceinline__ f32x4 mma(f32x4 acc, const RA &a, int nsteps = 1 << 20) const {
+#pragma unroll
+        for (int s = 0; s < NBLK / 2; ++s)
+            if (s < nsteps) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.f[s], f[s], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+template <int NBLK> struct RegB<float, NBLK> {
+    f32x4 f[NBLK];
+    __device__ __forceinline__ void set(const f32x4 *v) {
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) f[b] = v[b];
+    }
+    __device__ __forceinline__ void set_split(const f32x4 *v, RegB &lo) {
+        set(v);
+        (void)lo;
+    }
+    // nsteps counts 32-wide k-steps (two 16-blocks), as for fp16 operands
+    template <class RA>
+    __device__ __forceinline__ f32x4 mma(f32x4 acc, const RA &a, int nsteps = 1 << 20) const {
+        const int nblk = nsteps < NBLK ? 2 * nsteps : NBLK;
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b)
+            if (b < nblk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[b][i], f[b][i], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+// A-operand fragments of one 16-row tile read from LDS at the k-indices a
+// RegB of the same NBLK supplies (lane row = lr, k = 16*blk + 4*lg + i).
+template <typename ST, int NBLK> struct RowA;
+template <int NBLK> struct RowA<_Float16, NBLK> {
+    f16x8 f[NBLK / 2];
+    __device__ __forceinline__ void load(const _Float16 *arow, int lg, int nsteps = 1 << 20) {
+#pragma unroll
+        for (int s = 0; s < NBLK / 2; ++s) {
+            if (s < nsteps) {
+                const f16x4 a0 = *reinterpret_cast<const f16x4 *>(arow + 32 * s + 4 * lg);
+                const f16x4 a1 = *reinterpret_cast<const f16x4 *>(arow + 32 * s + 16 + 4 * lg);
+                f[s] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    }
+};
+template <int NBLK> struct RowA<float, NBLK> {
+    f32x4 f[NBLK];
+    __device__ __forceinline__ void load(const float *arow, int lg, int nsteps = 1 << 20) {
+        const int nblk = nsteps < NBLK ? 2 * nsteps : NBLK;
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b)
+            if (b < nblk) f[b] = *reinterpret_cast<const f32x4 *>(arow + 16 * b + 4 * lg);
+    }
+};
 
 // ---- precision policy per input type --------------------------------------
 template <typename IT> struct Prec;
@@ -102,7 +202,7 @@ template <> struct Prec<float> {
 
 template <typename T, int N> struct VecT { typedef T type __attribute__((ext_vector_type(N))); };
 
-// ---- shared-memory layout ---------------------------------------------------
+// ---- shared memory ----------------------------------------------------------
 template <int DK, int DVS, int C, bool KDA, typename IT>
 struct PrefillSmem {
     using ST = typename Prec<IT>::ST;
@@ -111,42 +211,41 @@ struct PrefillSmem {
     static constexpr int PAD = 16 / sizeof(ST);   // 16-byte row padding spreads LDS banks
     static constexpr int LDK = DK + PAD;          // [*][DK] operand rows (ST and GT have equal size)
     static constexpr int LDC = C + PAD;           // [*][C] operand rows
+    static constexpr int LDV = DVS + PAD;         // value-slice rows
     static constexpr int LDA = C + 4;             // fp32 [C][C]
     static constexpr int NB = C / 16;
-    static constexpr int KG = KDA ? C : 1;        // rows of per-channel Gram operands
+    static constexpr int KG = KDA ? C : 1;
     static constexpr int KGS = (KDA && SPLIT) ? C : 1;
-    static constexpr int SP = SPLIT ? DVS : 1;
 
-    ST Kt[C][LDK];          // GDN: k            KDA: k e^g
-    ST Qt[C][LDK];          // GDN: q            KDA: q e^g
-    ST KeT[DK][LDC];        // (k e^{g_C - g})^T
-    GT Lk[KG][LDK];         // KDA: k e^{g-m}
-    GT Lq[KG][LDK];         // KDA: q e^{g-m} (hi)
-    GT Lql[KGS][LDK];       //                (lo)
-    GT Rh[KG][LDK];         // KDA: k e^{m-g} (hi)
-    GT Rl[KGS][LDK];        //                (lo)
-    union {
-        float G[KDA ? C : 1][DK];   // KDA: log-decay, then its in-chunk prefix sum
+    // per-chunk operands, double-buffered (prologue writes chunk j+1 while
+    // the chain reads chunk j)
+    struct alignas(16) Buf {
+        float dec[KDA ? DK : 4];  // decay over the chunk: e^{g_C} (per key channel for KDA)
+        ST Kt[C][LDK];          // GDN: k              KDA: k e^g
+        ST Qt[C][LDK];          // GDN: q              KDA: q e^g
+        ST KeT[DK][LDC];        // (k e^{g_C - g})^T
+        ST Tm[C][LDC];          // T = (I + A)^-1 (zero above the diagonal)
+        ST Mm[C][LDC];          // M (zero above the diagonal)
+        IT V[C][LDV];           // value slice
+        float beta[C];
+        float eg[KDA ? 1 : C];  // GDN: e^{g_r}
+    } buf[2];
+    // prologue scratch
+    union alignas(16) {
+        float G[KDA ? C : 1][DK];   // KDA: log-decay, then e^{g - m}
         struct {
             float A[C][LDA];        // strict_tril(diag(b) Gram)
-            float Tf[C][LDA];       // (I + A)^-1
+            float Tf[C][LDA];       // (I + A)^-1, fp32
         } at;
-        float O[C][DVS + 4];        // output slice, staged for the store
     } u;
-    float P[(NB > 1 ? NB - 1 : 1) * 256];  // inverse scratch
-    ST M[C][LDC];           // tril(Q K^T) with decay
-    ST T[C][LDC];           // (I + A)^-1
-    ST S[DVS][LDK];         // state slice operand
-    ST Wh[DVS][LDC];        // diag(b)(V - X), transposed [value][token]  (hi)
-    ST Wl[SP][LDC];         //                                              (lo)
-    ST Uh[DVS][LDC];        // U, transposed (hi)
-    ST Ul[SP][LDC];         //               (lo)
-    IT V[C][DVS];           // value slice
-    float beta[C];
-    float g[C], eg[C], egc[C];                      // GDN: g, e^g, e^{g_C - g}
-    float m[KDA ? DK : 1], em[KDA ? DK : 1];        // KDA: reference m, e^m
-    float egcm[KDA ? DK : 1], egC[KDA ? DK : 1];    // KDA: e^{g_C - m}, e^{g_C}
-    float egCs;                                     // GDN: e^{g_C}
+    float P[256];                   // T_10 intermediate (two 16-blocks)
+    alignas(16) GT Lk[KG][LDK];     // KDA: k e^{g-m}
+    GT Lq[KG][LDK];                 // KDA: q e^{g-m} (hi)
+    GT Lql[KGS][LDK];               //                (lo)
+    GT Rh[KG][LDK];                 // KDA: k e^{m-g} (hi)
+    GT Rl[KGS][LDK];                //                (lo)
+    float em[KDA ? DK : 1], egcm[KDA ? DK : 1];   // KDA: e^m, e^{g_C - m}
+    float g[KDA ? 1 : C], egc[KDA ? 1 : C];       // GDN: g, e^{g_C - g}
 };
 
 struct PrefillKArgs {
@@ -160,40 +259,54 @@ struct PrefillKArgs {
     bool out_bf16;
 };
 
-// hi/lo split of x in ST: hi = ST(x), lo = ST(x - hi) (lo unused without SPLIT)
 template <typename ST>
 __device__ __forceinline__ void split2(float x, ST &hi, ST &lo) {
     hi = (ST)x;
     lo = (ST)(x - (float)hi);
 }
 
+constexpr int kPrologueWaves = 4;
+
+// Barriers per pipeline iteration.  Per-head decay: (1) inputs to LDS,
+// (2) Gram + T + K_end^T, chain alongside.  Per-channel decay: (1) prefix sums
+// and e^{g-m}, (2) decayed operands, chain alongside, (3) Gram + T + K_end^T.
+template <bool KDA>
+constexpr int pipeline_barriers() { return KDA ? 3 : 2; }
+
 template <int DK, int DVS, int C, bool KDA, typename IT>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillKArgs p) {
+__global__ __launch_bounds__(64 * (kPrologueWaves + DVS / 16)) void prefill_kernel(PrefillKArgs p) {
     using SM = PrefillSmem<DK, DVS, C, KDA, IT>;
+    using Buf = typename SM::Buf;
     using ST = typename SM::ST;
     using GT = typename SM::GT;
     constexpr bool SPLIT = SM::SPLIT;
+    constexpr int NPW = kPrologueWaves;
     constexpr int EPV = 16 / sizeof(IT);           // elements per 16-byte input vector
     using IV = typename VecT<IT, EPV>::type;
     using SV = typename VecT<ST, EPV>::type;
     using GV = typename VecT<GT, EPV>::type;
-    using MS = Mfma<ST>;
-    constexpr int LDK = SM::LDK, LDC = SM::LDC;
-    constexpr int NB = C / 16;                     // 16-token blocks
-    constexpr int NCB = DVS / 16;                  // 16-channel value blocks
+    constexpr int LDK = SM::LDK;
+    constexpr int NB = C / 16;                     // 16-token blocks per chunk
     constexpr int NKB = DK / 16;                   // 16-channel key blocks
-    constexpr int NST = NCB * NKB;                 // state tiles
-    constexpr int STPW = (NST + 3) / 4;            // state tiles per wave
-    constexpr int NOT = NB * NCB;                  // output tiles per chunk
-    constexpr int OTPW = (NOT + 3) / 4;
     constexpr int KV = C * (DK / EPV);             // 16-byte k (or q) vectors per chunk
-    constexpr int KVPT = (KV + 255) / 256;         // ... per thread
+    constexpr int KVPT = (KV + 255) / 256;
+    constexpr int VV = C * (DVS / EPV);            // 16-byte value vectors per chunk
+    constexpr int NSEG = 256 / DK;                 // KDA prefix sum: lanes per key channel
+    constexpr int SEGL = C / NSEG;                 //   tokens per lane
+    constexpr int NBAR = pipeline_barriers<KDA>();
+    constexpr int CHAIN_STAGE = 1;                 // barriers the chain waits for before its work
+    static_assert(NB <= 2, "the inverse below handles at most two 16-token blocks");
+    static_assert(NB * (NB + 1) / 2 <= kPrologueWaves - 1, "one M tile per prologue wave");
     static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
-    static_assert(C % MS::KSTEP == 0 && DK % MS::KSTEP == 0, "tile sizes");
+    static_assert(C % Mfma<ST>::KSTEP == 0 && DK % Mfma<ST>::KSTEP == 0, "tile sizes");
+    static_assert(VV <= 256 && C <= 64 && SEGL >= 1, "prologue thread mapping");
     static_assert(sizeof(ST) == sizeof(IT) && sizeof(GT) == sizeof(IT), "operand sizes");
 
     __shared__ SM sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index in a scalar register: the chain / prologue split below is a
+    // uniform branch, so each wave executes only its own path's barriers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int H = p.H, DV = p.DV;
 
@@ -209,338 +322,415 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillKArgs p) {
     if (p.cu) { bos = p.cu[n]; eos = p.cu[n + 1]; }
     else { bos = n * p.T; eos = bos + p.T; }
     const int v0 = slice * DVS;
+    const int nchunks = (eos - bos + C - 1) / C;
 
+    if (wave >= NPW) {
+        // =================== chain wave: 16 value channels ===================
+        const int cb = wave - NPW;
+        // S^T of this wave's value block (lane: value column v0 + 16 cb + lr,
+        // key rows 16 kb + 4 lg + i)
+        f32x4 St[NKB];
+        const size_t srow = ((size_t)n * H + h) * DV * DK + (size_t)(v0 + 16 * cb + lr) * DK + 4 * lg;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            St[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (p.initial_state) St[kb] = *reinterpret_cast<const f32x4 *>(p.initial_state + srow + 16 * kb);
+        }
+        float *gof = static_cast<float *>(p.out);
+        __bf16 *gob = static_cast<__bf16 *>(p.out);
+
+        for (int it = 0; it <= nchunks; ++it) {
+#pragma unroll
+            for (int b = 0; b < CHAIN_STAGE; ++b) __syncthreads();
+            if (it >= 1) {
+                const Buf &bc = sm.buf[(it + 1) & 1];
+                const int jc = it - 1;
+                const int t0 = bos + jc * C;
+                const int nv = min(C, eos - t0);
+                // every LDS operand of the chunk, read up front
+                RowA<ST, NKB> ka[NB], qa[NB];
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    ka[rb].load(&bc.Kt[16 * rb + lr][0], lg);
+                    qa[rb].load(&bc.Qt[16 * rb + lr][0], lg);
+                }
+                float vv[NB][4], bt[NB][4], eg[NB][4];
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * rb + 4 * lg + i;
+                        vv[rb][i] = (float)bc.V[t][16 * cb + lr];
+                        bt[rb][i] = bc.beta[t];
+                        eg[rb][i] = KDA ? 1.f : bc.eg[KDA ? 0 : t];
+                    }
+                RegB<ST, NKB> sop;
+                sop.set(St);
+                f32x4 X[NB], Y[NB], W[NB];
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    X[rb] = sop.mma(f32x4{0.f, 0.f, 0.f, 0.f}, ka[rb]);
+                    Y[rb] = sop.mma(f32x4{0.f, 0.f, 0.f, 0.f}, qa[rb]);
+                }
+                RowA<ST, NB> ta[NB], ma[NB];
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    const int ns = (16 * rb + 16 + 31) / 32;   // T and M are lower triangular
+                    ta[rb].load(&bc.Tm[16 * rb + lr][0], lg, ns);
+                    ma[rb].load(&bc.Mm[16 * rb + lr][0], lg, ns);
+                }
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        Y[rb][i] *= eg[rb][i];
+                        W[rb][i] = bt[rb][i] * (vv[rb][i] - X[rb][i] * eg[rb][i]);
+                    }
+                RegB<ST, NB> wh, wl;
+                wh.set_split(W, wl);
+                f32x4 U[NB];
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    const int ns = (16 * rb + 16 + 31) / 32;
+                    U[rb] = wh.mma(f32x4{0.f, 0.f, 0.f, 0.f}, ta[rb], ns);
+                    if constexpr (SPLIT) U[rb] = wl.mma(U[rb], ta[rb], ns);
+                }
+                RowA<ST, NB> kea[NKB];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) kea[kb].load(&bc.KeT[16 * kb + lr][0], lg);
+                RegB<ST, NB> uh, ul;
+                uh.set_split(U, ul);
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    const int ns = (16 * rb + 16 + 31) / 32;
+                    f32x4 o = uh.mma(Y[rb], ma[rb], ns);
+                    if constexpr (SPLIT) o = ul.mma(o, ma[rb], ns);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * rb + 4 * lg + i;
+                        if (t < nv) {
+                            const size_t off = ((size_t)(t0 + t) * H + h) * DV + v0 + 16 * cb + lr;
+                            if (p.out_bf16) gob[off] = (__bf16)(p.scale * o[i]);
+                            else gof[off] = p.scale * o[i];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    f32x4 acc = St[kb];
+                    if constexpr (KDA) {
+                        const f32x4 d = *reinterpret_cast<const f32x4 *>(&bc.dec[16 * kb + 4 * lg]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] *= d[i];
+                    } else {
+                        const float d = bc.dec[0];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] *= d;
+                    }
+                    acc = uh.mma(acc, kea[kb]);
+                    if constexpr (SPLIT) acc = ul.mma(acc, kea[kb]);
+                    St[kb] = acc;
+                }
+            }
+#pragma unroll
+            for (int b = CHAIN_STAGE; b < NBAR; ++b) __syncthreads();
+        }
+        if (p.final_state) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                *reinterpret_cast<f32x4 *>(p.final_state + srow + 16 * kb) = St[kb];
+        }
+        return;
+    }
+
+    // ======================= prologue waves (256 threads) ====================
     const IT *gq = static_cast<const IT *>(p.q);
     const IT *gk = static_cast<const IT *>(p.k);
     const IT *gv = static_cast<const IT *>(p.v);
-    float *gof = static_cast<float *>(p.out);
-    __bf16 *gob = static_cast<__bf16 *>(p.out);
-
-    // ---- state slice in registers (fp32, MFMA accumulator layout)
-    f32x4 Sreg[STPW];
-    const size_t sbase = ((size_t)n * H + h) * DV * DK;
+    IV kreg[KVPT], qreg[KVPT], vreg;
+    float greg[KDA ? SEGL : 1];                    // KDA: this lane's (channel, token segment) of log-decay
+    float gsc = 0.f, breg = 0.f;
+    const int gc = tid / NSEG, gseg = tid % NSEG;  // KDA prefix-sum lane: key channel, token segment
+    // raw inputs of chunk j into registers (zeros past the sequence end)
+    auto prefetch = [&](int j) {
+        const int t0 = bos + j * C;
+        const int nv = j < nchunks ? min(C, eos - t0) : 0;
 #pragma unroll
-    for (int j = 0; j < STPW; ++j) {
-        const int tile = wave + 4 * j;
-        Sreg[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tile < NST && p.initial_state) {
-            const int cb = tile / NKB, kb = tile % NKB;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                Sreg[j][i] = p.initial_state[sbase + (size_t)(v0 + 16 * cb + 4 * lg + i) * DK + 16 * kb + lr];
-        }
-    }
-
-    for (int t0 = bos; t0 < eos; t0 += C) {
-        const int nv = min(C, eos - t0);
-
-        // ================= L: loads, gates, prefix sums, operands ===========
-        IV kreg[KVPT], qreg[KVPT];
-#pragma unroll
-        for (int j = 0; j < KVPT; ++j) {
-            const int e = tid + 256 * j;
+        for (int x = 0; x < KVPT; ++x) {
+            const int e = tid + 256 * x;
             const int t = e / (DK / EPV), c = (e % (DK / EPV)) * EPV;
-            kreg[j] = IV{};
-            qreg[j] = IV{};
+            kreg[x] = IV{};
+            qreg[x] = IV{};
             if (e < KV && t < nv) {
                 const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                kreg[j] = *reinterpret_cast<const IV *>(gk + off);
-                qreg[j] = *reinterpret_cast<const IV *>(gq + off);
+                kreg[x] = *reinterpret_cast<const IV *>(gk + off);
+                qreg[x] = *reinterpret_cast<const IV *>(gq + off);
             }
         }
-        if (tid < C) sm.beta[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
-        for (int e = tid; e < C * (DVS / EPV); e += 256) {
-            const int t = e / (DVS / EPV), c = (e % (DVS / EPV)) * EPV;
-            IV vv{};
-            if (t < nv) vv = *reinterpret_cast<const IV *>(gv + ((size_t)(t0 + t) * H + h) * DV + v0 + c);
-            *reinterpret_cast<IV *>(&sm.V[t][c]) = vv;
-        }
-        if constexpr (!KDA) {
-            if (wave == 0) {
-                float x = (lane < nv) ? p.log_alpha[(size_t)(t0 + lane) * H + h] : 0.f;
+        if constexpr (KDA) {
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(x, off);
-                    if (lane >= off) x += y;
-                }
-                const float gC = __shfl(x, C - 1);
-                if (lane < C) {
-                    sm.g[lane] = x;
-                    sm.eg[lane] = __expf(x);
-                    sm.egc[lane] = __expf(gC - x);
-                }
-                if (lane == 0) sm.egCs = __expf(gC);
+            for (int x = 0; x < SEGL; ++x) {
+                const int t = gseg * SEGL + x;
+                greg[x] = t < nv ? p.log_alpha[((size_t)(t0 + t) * H + h) * DK + gc] : 0.f;
             }
         } else {
-            for (int e = tid; e < C * (DK / 4); e += 256) {
-                const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
-                f32x4 a{0.f, 0.f, 0.f, 0.f};
-                if (t < nv) a = *reinterpret_cast<const f32x4 *>(p.log_alpha + ((size_t)(t0 + t) * H + h) * DK + c);
-                *reinterpret_cast<f32x4 *>(&sm.u.G[t][c]) = a;
-            }
-            __syncthreads();
-            for (int c = tid; c < DK; c += 256) {
-                float run = 0.f;
-                for (int t = 0; t < C; ++t) {
-                    run += sm.u.G[t][c];
-                    sm.u.G[t][c] = run;
-                }
-                const float m = 0.5f * (sm.u.G[0][c] + run);
-                sm.m[c] = m;
-                sm.em[c] = __expf(m);
-                sm.egcm[c] = __expf(run - m);
-                sm.egC[c] = __expf(run);
-            }
+            gsc = tid < nv ? p.log_alpha[(size_t)(t0 + tid) * H + h] : 0.f;
         }
-        // state operand of this chunk
-#pragma unroll
-        for (int j = 0; j < STPW; ++j) {
-            const int tile = wave + 4 * j;
-            if (tile < NST) {
-                const int cb = tile / NKB, kb = tile % NKB;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.S[16 * cb + 4 * lg + i][16 * kb + lr] = (ST)Sreg[j][i];
-            }
+        vreg = IV{};
+        if (tid < VV) {
+            const int t = tid / (DVS / EPV), c = (tid % (DVS / EPV)) * EPV;
+            if (t < nv) vreg = *reinterpret_cast<const IV *>(gv + ((size_t)(t0 + t) * H + h) * DV + v0 + c);
         }
-        __syncthreads();
+        breg = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    };
 
-        // operands from the registers holding k and q
-#pragma unroll
-        for (int j = 0; j < KVPT; ++j) {
-            const int e = tid + 256 * j;
-            if (e >= KV) break;
-            const int t = e / (DK / EPV), c = (e % (DK / EPV)) * EPV;
-            SV kt, qt;
-            if constexpr (!KDA) {
-                const float ec = sm.egc[t];
-#pragma unroll
-                for (int x = 0; x < EPV; ++x) {
-                    const float kf = (float)kreg[j][x];
-                    kt[x] = (ST)kf;
-                    qt[x] = (ST)(float)qreg[j][x];
-                    sm.KeT[c + x][t] = (ST)(kf * ec);
+    // Gram tiles of the lower block triangle.  M (operand, zero above the
+    // diagonal) goes to waves 0..NLT-1, one tile each; the last prologue wave
+    // computes the A tiles and then T = (I + A)^-1 by itself, so the A -> T
+    // dependency needs no barrier (a wave's LDS accesses complete in order).
+    auto gram_inverse = [&](Buf &bp) {
+        constexpr int NLT = NB * (NB + 1) / 2;     // lower tiles
+        const int I0[3] = {0, 1, 1}, J0[3] = {0, 0, 1};
+        if (wave < NLT) {
+            const int I = I0[wave], J = J0[wave];
+            f32x4 a0{0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+            if constexpr (KDA) {
+                a0 = tile_mma<GT, DK>(a0, &sm.Lq[16 * I][0], LDK, &sm.Rh[16 * J][0], LDK, lane);
+                if constexpr (SPLIT) {
+                    a1 = tile_mma<GT, DK>(a1, &sm.Lq[16 * I][0], LDK, &sm.Rl[16 * J][0], LDK, lane);
+                    a2 = tile_mma<GT, DK>(a2, &sm.Lql[16 * I][0], LDK, &sm.Rh[16 * J][0], LDK, lane);
                 }
             } else {
-                GV lk, lq, lql, rh, rl;
-#pragma unroll
-                for (int x = 0; x < EPV; ++x) {
-                    const float kf = (float)kreg[j][x], qf = (float)qreg[j][x];
-                    const float d = sm.u.G[t][c + x] - sm.m[c + x];
-                    const float e1 = __expf(d), e2 = __expf(-d);
-                    lk[x] = (GT)(kf * e1);
-                    GT hi, lo;
-                    split2<GT>(qf * e1, hi, lo);
-                    lq[x] = hi;
-                    lql[x] = lo;
-                    split2<GT>(kf * e2, hi, lo);
-                    rh[x] = hi;
-                    rl[x] = lo;
-                    const float eg = e1 * sm.em[c + x];
-                    kt[x] = (ST)(kf * eg);
-                    qt[x] = (ST)(qf * eg);
-                    sm.KeT[c + x][t] = (ST)(kf * e2 * sm.egcm[c + x]);
-                }
-                *reinterpret_cast<GV *>(&sm.Lk[t][c]) = lk;
-                *reinterpret_cast<GV *>(&sm.Lq[t][c]) = lq;
-                *reinterpret_cast<GV *>(&sm.Rh[t][c]) = rh;
-                if constexpr (SPLIT) {
-                    *reinterpret_cast<GV *>(&sm.Lql[t][c]) = lql;
-                    *reinterpret_cast<GV *>(&sm.Rl[t][c]) = rl;
-                }
+                a0 = tile_mma<ST, DK>(a0, &bp.Qt[16 * I][0], LDK, &bp.Kt[16 * J][0], LDK, lane);
             }
-            *reinterpret_cast<SV *>(&sm.Kt[t][c]) = kt;
-            *reinterpret_cast<SV *>(&sm.Qt[t][c]) = qt;
-        }
-        __syncthreads();
-
-        // ================= G: Gram matrices A (fp32) and M (operand) ========
-        for (int job = wave; job < 2 * NB * NB; job += 4) {
-            const bool isM = job >= NB * NB;
-            const int I = (job % (NB * NB)) / NB, J = job % NB;
-            f32x4 acc{0.f, 0.f, 0.f, 0.f};
-            if (J <= I) {
-                if constexpr (!KDA) {
-                    acc = tile_mma(acc, isM ? &sm.Qt[16 * I][0] : &sm.Kt[16 * I][0], LDK, &sm.Kt[16 * J][0], LDK, 0,
-                                   DK, lane);
-                } else if (!isM) {
-                    acc = tile_mma(acc, &sm.Lk[16 * I][0], LDK, &sm.Rh[16 * J][0], LDK, 0, DK, lane);
-                } else {
-                    acc = tile_mma(acc, &sm.Lq[16 * I][0], LDK, &sm.Rh[16 * J][0], LDK, 0, DK, lane);
-                    if constexpr (SPLIT) {
-                        acc = tile_mma(acc, &sm.Lq[16 * I][0], LDK, &sm.Rl[16 * J][0], LDK, 0, DK, lane);
-                        acc = tile_mma(acc, &sm.Lql[16 * I][0], LDK, &sm.Rh[16 * J][0], LDK, 0, DK, lane);
-                    }
-                }
-            }
+            const f32x4 acc = a0 + a1 + a2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * I + 4 * lg + i, c = 16 * J + lr;
                 float val = 0.f;
-                if (isM ? (c <= r) : (c < r)) {
+                if (c <= r) {
                     val = acc[i];
                     if constexpr (!KDA) val *= __expf(sm.g[r] - sm.g[c]);
-                    if (!isM) val *= sm.beta[r];
                 }
-                if (isM) sm.M[r][c] = (ST)val;
-                else sm.u.at.A[r][c] = val;
+                bp.Mm[r][c] = (ST)val;
+                if (NB == 2 && I == 0) bp.Mm[r][16 + lr] = (ST)0.f;
             }
         }
-        __syncthreads();
-
-        // ================= I: T = (I + A)^-1 =================================
-        // diagonal 16x16 blocks by forward substitution, one column per thread
-        if (tid < C) {
-            const int I = tid / 16, jc = tid % 16;
-            float tcol[16];
+        if (wave == NPW - 1) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == jc) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc -= sm.u.at.A[16 * I + i][16 * I + m] * tcol[m];
-                tcol[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sm.u.at.Tf[16 * I + i][16 * I + jc] = tcol[i];
-        }
-        __syncthreads();
-        // off-diagonal blocks by distance d = I - J:  T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
-        for (int d = 1; d < NB; ++d) {
-            const int nblk = NB - d;
-            for (int e = tid; e < nblk * 256; e += 256) {
-                const int J = e / 256, I = J + d, r = (e % 256) / 16, c = e % 16;
-                float acc = 0.f;
-                for (int K = J; K < I; ++K)
-#pragma unroll
-                    for (int m = 0; m < 16; ++m) acc += sm.u.at.A[16 * I + r][16 * K + m] * sm.u.at.Tf[16 * K + m][16 * J + c];
-                sm.P[e] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < nblk * 256; e += 256) {
-                const int J = e / 256, I = J + d, r = (e % 256) / 16, c = e % 16;
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) acc += sm.u.at.Tf[16 * I + r][16 * I + m] * sm.P[J * 256 + m * 16 + c];
-                sm.u.at.Tf[16 * I + r][16 * J + c] = -acc;
-            }
-            __syncthreads();
-        }
-        for (int e = tid; e < C * C; e += 256) {
-            const int r = e / C, c = e % C;
-            sm.T[r][c] = (ST)(c <= r ? sm.u.at.Tf[r][c] : 0.f);
-        }
-        __syncthreads();
-
-        // ================= X, Y; W = diag(b)(V - X) ==========================
-        f32x4 Y[OTPW];
-#pragma unroll
-        for (int j = 0; j < OTPW; ++j) {
-            const int tile = wave + 4 * j;
-            Y[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tile < NOT) {
-                const int rb = tile / NCB, cb = tile % NCB;
-                f32x4 X = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, &sm.Kt[16 * rb][0], LDK, &sm.S[16 * cb][0], LDK, 0, DK,
-                                   lane);
-                Y[j] = tile_mma(Y[j], &sm.Qt[16 * rb][0], LDK, &sm.S[16 * cb][0], LDK, 0, DK, lane);
-                const int dv = 16 * cb + lr;
+            for (int x = 0; x < NLT; ++x) {
+                const int I = I0[x], J = J0[x];
+                f32x4 a{0.f, 0.f, 0.f, 0.f};
+                if constexpr (KDA) a = tile_mma<GT, DK>(a, &sm.Lk[16 * I][0], LDK, &sm.Rh[16 * J][0], LDK, lane);
+                else a = tile_mma<ST, DK>(a, &bp.Kt[16 * I][0], LDK, &bp.Kt[16 * J][0], LDK, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * lg + i;
-                    float x = X[i];
-                    if constexpr (!KDA) { x *= sm.eg[r]; Y[j][i] *= sm.eg[r]; }
-                    const float w = sm.beta[r] * ((float)sm.V[r][dv] - x);
-                    ST hi, lo;
-                    split2<ST>(w, hi, lo);
-                    sm.Wh[dv][r] = hi;
-                    if constexpr (SPLIT) sm.Wl[dv][r] = lo;
+                    const int r = 16 * I + 4 * lg + i, c = 16 * J + lr;
+                    float val = 0.f;
+                    if (c < r) {
+                        val = a[i] * bp.beta[r];
+                        if constexpr (!KDA) val *= __expf(sm.g[r] - sm.g[c]);
+                    }
+                    sm.u.at.A[r][c] = val;
+                }
+            }
+            // diagonal 16x16 blocks by forward substitution, one column per
+            // lane: t_i = delta_ij - sum_{m<i} A_im t_m, row i of A read from LDS
+            if (lane < C) {
+                const int I = lane / 16, jc = lane % 16;
+                float tcol[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float acc0 = (i == jc) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+                    for (int m4 = 0; m4 < i; m4 += 4) {
+                        const f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.u.at.A[16 * I + i][16 * I + m4]);
+#pragma unroll
+                        for (int y = 0; y < 4; ++y)
+                            if (m4 + y < i) {
+                                if (y & 1) acc1 -= v[y] * tcol[m4 + y];
+                                else acc0 -= v[y] * tcol[m4 + y];
+                            }
+                    }
+                    tcol[i] = acc0 + acc1;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    sm.u.at.Tf[16 * I + i][16 * I + jc] = tcol[i];
+                    bp.Tm[16 * I + i][16 * I + jc] = (ST)tcol[i];
+                }
+            }
+            if constexpr (NB == 2) {
+                // T_10 = -T_11 (A_10 T_00); four entries per lane
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const int e = lane + 64 * y, r = e / 16, c = e % 16;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 16; ++m) acc += sm.u.at.A[16 + r][m] * sm.u.at.Tf[m][c];
+                    sm.P[e] = acc;
+                }
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const int e = lane + 64 * y, r = e / 16, c = e % 16;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 16; ++m) acc += sm.u.at.Tf[16 + r][16 + m] * sm.P[m * 16 + c];
+                    bp.Tm[16 + r][c] = (ST)(-acc);
+                    bp.Tm[r][16 + c] = (ST)0.f;
                 }
             }
         }
-        __syncthreads();
-
-        // ================= U = T W (lower-triangular in tokens) ==============
+    };
+    // K_end^T (key rows, token columns) via column reads of row-major data
+    auto transpose_kend = [&](Buf &bp) {
+        if (wave == NPW - 1) return;
+        for (int e = tid; e < DK * (C / EPV); e += 64 * (NPW - 1)) {
+            const int c = e % DK, t0 = (e / DK) * EPV;
+            SV o;
 #pragma unroll
-        for (int j = 0; j < OTPW; ++j) {
-            const int tile = wave + 4 * j;
-            if (tile < NOT) {
-                const int rb = tile / NCB, cb = tile % NCB;
-                const int kend = min(C, ((16 * rb + 16 + MS::KSTEP - 1) / MS::KSTEP) * MS::KSTEP);
-                f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, &sm.T[16 * rb][0], LDC, &sm.Wh[16 * cb][0], LDC, 0,
-                                     kend, lane);
-                if constexpr (SPLIT) acc = tile_mma(acc, &sm.T[16 * rb][0], LDC, &sm.Wl[16 * cb][0], LDC, 0, kend, lane);
-                const int dv = 16 * cb + lr;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * lg + i;
-                    ST hi, lo;
-                    split2<ST>(acc[i], hi, lo);
-                    sm.Uh[dv][r] = hi;
-                    if constexpr (SPLIT) sm.Ul[dv][r] = lo;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ================= O = Y + M U;  S <- S Diag(e^{g_C}) + U^T K_end =====
-#pragma unroll
-        for (int j = 0; j < OTPW; ++j) {
-            const int tile = wave + 4 * j;
-            if (tile < NOT) {
-                const int rb = tile / NCB, cb = tile % NCB;
-                const int kend = min(C, ((16 * rb + 16 + MS::KSTEP - 1) / MS::KSTEP) * MS::KSTEP);
-                f32x4 acc = tile_mma(Y[j], &sm.M[16 * rb][0], LDC, &sm.Uh[16 * cb][0], LDC, 0, kend, lane);
-                if constexpr (SPLIT) acc = tile_mma(acc, &sm.M[16 * rb][0], LDC, &sm.Ul[16 * cb][0], LDC, 0, kend, lane);
-                const int dv = 16 * cb + lr;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.u.O[16 * rb + 4 * lg + i][dv] = p.scale * acc[i];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < STPW; ++j) {
-            const int tile = wave + 4 * j;
-            if (tile < NST) {
-                const int cb = tile / NKB, kb = tile % NKB;
-                float dec;
-                if constexpr (KDA) dec = sm.egC[16 * kb + lr];
-                else dec = sm.egCs;
-                f32x4 acc = Sreg[j];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= dec;
-                acc = tile_mma(acc, &sm.Uh[16 * cb][0], LDC, &sm.KeT[16 * kb][0], LDC, 0, C, lane);
-                if constexpr (SPLIT) acc = tile_mma(acc, &sm.Ul[16 * cb][0], LDC, &sm.KeT[16 * kb][0], LDC, 0, C, lane);
-                Sreg[j] = acc;
-            }
-        }
-        __syncthreads();
-
-        // ================= write the output slice ============================
-        for (int e = tid; e < C * (DVS / 4); e += 256) {
-            const int t = e / (DVS / 4), c = (e % (DVS / 4)) * 4;
-            if (t < nv) {
-                const f32x4 o = *reinterpret_cast<const f32x4 *>(&sm.u.O[t][c]);
-                const size_t off = ((size_t)(t0 + t) * H + h) * DV + v0 + c;
-                if (p.out_bf16) {
-                    bf16x4 b;
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) b[x] = (__bf16)o[x];
-                    *reinterpret_cast<bf16x4 *>(gob + off) = b;
+            for (int x = 0; x < EPV; ++x) {
+                float val;
+                if constexpr (KDA) {
+                    val = (float)sm.Rh[t0 + x][c];
+                    if constexpr (SPLIT) val += (float)sm.Rl[t0 + x][c];
+                    val *= sm.egcm[c];
                 } else {
-                    *reinterpret_cast<f32x4 *>(gof + off) = o;
+                    val = (float)bp.Kt[t0 + x][c] * sm.egc[t0 + x];
+                }
+                o[x] = (ST)val;
+            }
+            *reinterpret_cast<SV *>(&bp.KeT[c][t0]) = o;
+        }
+    };
+
+    prefetch(0);
+    // iteration `it` builds chunk it; the chain waves consume chunk it-1
+    for (int it = 0; it <= nchunks; ++it) {
+        const bool pro = it < nchunks;
+        Buf &bp = sm.buf[it & 1];
+        if (pro) {
+            if (tid < VV) {
+                const int t = tid / (DVS / EPV), c = (tid % (DVS / EPV)) * EPV;
+                *reinterpret_cast<IV *>(&bp.V[t][c]) = vreg;
+            }
+            if (tid < C) bp.beta[tid] = breg;
+        }
+        if constexpr (!KDA) {
+            // ---- stage 1: inputs to LDS, per-head decay prefix sums
+            if (pro) {
+                if (wave == 0) {
+                    float x = gsc;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float y = __shfl_up(x, off);
+                        if (lane >= off) x += y;
+                    }
+                    const float gC = __shfl(x, C - 1);
+                    if (lane < C) {
+                        sm.g[lane] = x;
+                        bp.eg[lane] = __expf(x);
+                        sm.egc[lane] = __expf(gC - x);
+                    }
+                    if (lane == 0) bp.dec[0] = __expf(gC);
+                }
+#pragma unroll
+                for (int x = 0; x < KVPT; ++x) {
+                    const int e = tid + 256 * x;
+                    if (e < KV) {
+                        const int t = e / (DK / EPV), c = (e % (DK / EPV)) * EPV;
+                        SV kt, qt;
+#pragma unroll
+                        for (int y = 0; y < EPV; ++y) {
+                            kt[y] = (ST)(float)kreg[x][y];
+                            qt[y] = (ST)(float)qreg[x][y];
+                        }
+                        *reinterpret_cast<SV *>(&bp.Kt[t][c]) = kt;
+                        *reinterpret_cast<SV *>(&bp.Qt[t][c]) = qt;
+                    }
                 }
             }
-        }
-        __syncthreads();
-    }
-
-    if (p.final_state) {
-#pragma unroll
-        for (int j = 0; j < STPW; ++j) {
-            const int tile = wave + 4 * j;
-            if (tile < NST) {
-                const int cb = tile / NKB, kb = tile % NKB;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    p.final_state[sbase + (size_t)(v0 + 16 * cb + 4 * lg + i) * DK + 16 * kb + lr] = Sreg[j][i];
+            __syncthreads();
+            // ---- stage 2: Gram, T, K_end^T; next chunk's inputs requested
+            if (pro) {
+                gram_inverse(bp);
+                transpose_kend(bp);
+                prefetch(it + 1);
             }
+            __syncthreads();
+        } else {
+            // ---- stage 1: per-channel prefix sums and e^{g-m}
+            if (pro) {
+                float gv_[SEGL];
+#pragma unroll
+                for (int s2 = 0; s2 < SEGL; ++s2) gv_[s2] = greg[s2];
+#pragma unroll
+                for (int s2 = 1; s2 < SEGL; ++s2) gv_[s2] += gv_[s2 - 1];
+                float incl = gv_[SEGL - 1];
+#pragma unroll
+                for (int off = 1; off < NSEG; off <<= 1) {
+                    const float y = __shfl_up(incl, off, NSEG);
+                    if (gseg >= off) incl += y;
+                }
+                const float carry = incl - gv_[SEGL - 1];
+                const float gC = __shfl(incl, NSEG - 1, NSEG);
+                const float g0 = __shfl(gv_[0], 0, NSEG);
+                const float m = 0.5f * (g0 + gC);
+#pragma unroll
+                for (int s2 = 0; s2 < SEGL; ++s2) sm.u.G[gseg * SEGL + s2][gc] = __expf(gv_[s2] + carry - m);
+                if (gseg == 0) {
+                    sm.em[gc] = __expf(m);
+                    sm.egcm[gc] = __expf(gC - m);
+                    bp.dec[gc] = __expf(gC);
+                }
+            }
+            __syncthreads();
+            // ---- stage 2: decayed operands; next chunk's inputs requested
+            if (pro) {
+#pragma unroll
+                for (int x = 0; x < KVPT; ++x) {
+                    const int e = tid + 256 * x;
+                    if (e < KV) {
+                        const int t = e / (DK / EPV), c = (e % (DK / EPV)) * EPV;
+                        SV kt, qt;
+                        GV lk, lq, lql, rh, rl;
+#pragma unroll
+                        for (int y = 0; y < EPV; ++y) {
+                            const float kf = (float)kreg[x][y], qf = (float)qreg[x][y];
+                            const float e1 = sm.u.G[t][c + y];
+                            const float e2 = __builtin_amdgcn_rcpf(e1);
+                            lk[y] = (GT)(kf * e1);
+                            GT hi, lo;
+                            split2<GT>(qf * e1, hi, lo);
+                            lq[y] = hi;
+                            lql[y] = lo;
+                            split2<GT>(kf * e2, hi, lo);
+                            rh[y] = hi;
+                            rl[y] = lo;
+                            const float eg = e1 * sm.em[c + y];
+                            kt[y] = (ST)(kf * eg);
+                            qt[y] = (ST)(qf * eg);
+                        }
+                        *reinterpret_cast<GV *>(&sm.Lk[t][c]) = lk;
+                        *reinterpret_cast<GV *>(&sm.Lq[t][c]) = lq;
+                        *reinterpret_cast<GV *>(&sm.Rh[t][c]) = rh;
+                        if constexpr (SPLIT) {
+                            *reinterpret_cast<GV *>(&sm.Lql[t][c]) = lql;
+                            *reinterpret_cast<GV *>(&sm.Rl[t][c]) = rl;
+                        }
+                        *reinterpret_cast<SV *>(&bp.Kt[t][c]) = kt;
+                        *reinterpret_cast<SV *>(&bp.Qt[t][c]) = qt;
+                    }
+                }
+                prefetch(it + 1);
+            }
+            __syncthreads();
+            // ---- stage 3: Gram, T, K_end^T
+            if (pro) {
+                gram_inverse(bp);
+                transpose_kend(bp);
+            }
+            __syncthreads();
         }
     }
 }
@@ -561,7 +751,8 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
     p.out_bf16 = a.out_bf16;
     const long units = (long)a.num_seqs * a.num_heads;
     const long grid = ((units + 7) / 8) * 8 * (a.dv / DVS);
-    hipLaunchKernelGGL((prefill_kernel<DK, DVS, C, KDA, IT>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<DK, DVS, C, KDA, IT>), dim3((unsigned)grid),
+                       dim3(64 * (kPrologueWaves + DVS / 16)), 0, st, p);
     return hipGetLastError();
 }
 

@@ -84,7 +84,8 @@ def _decode(N=4, H=2, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + MB, 
     (dict(shape=(1, 64, 2, 64, 40, 1)), 2, "head_dim_v"),
     (dict(shape=(1, 64, 2, 16, 64, 1)), 2, "no prefill kernel"),        # bf16 needs dk >= 32
     (dict(chunk=48), 1, "chunk_size"),
-    (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 needs chunks of 32 or 64
+    (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 runs 32-token chunks
+    (dict(chunk=64), 2, "no prefill kernel"),
     (dict(dvs=48), 1, "dv_slice"),
     (dict(shape=(1, 64, 2, 64, 48, 1), dvs=32), 1, "does not divide"),
     (dict(shape=(2, 64, 2, 64, 64, 1)), 1, "num_seqs == batch"),

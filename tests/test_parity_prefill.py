@@ -50,9 +50,10 @@ def test_tiny_gdn_workload():
 
 
 def test_gdn_prefill_8k_workload():
-    """B=1, H=16, T=8192, d=128, bf16 q/k/v, per-head decay, chunk 64."""
+    """B=1, H=16, T=8192, d=128, bf16 q/k/v, per-head decay (the kernel's own
+    32-token chunking; the function does not depend on the chunk size)."""
     w = WORKLOADS["gdn_prefill_8k"]
-    _check_all(prefill_inputs(w, DEV), "gdn_prefill_8k", chunk_size=w.chunk)
+    _check_all(prefill_inputs(w, DEV), "gdn_prefill_8k")
 
 
 def _check_sampled(inp, units, label, **kw):
@@ -104,18 +105,18 @@ def test_packed_gdn_256k_workload():
 # -------------------------------------------------------- shape sweeps ----
 BF16_CASES = [
     # dk, dv, H, T, gate, init, chunk, dv_slice
-    (128, 128, 2, 1, "head", False, 64, 32),
-    (128, 128, 2, 63, "channel", True, 32, 32),
-    (128, 128, 1, 64, "head", True, 64, 16),
-    (128, 128, 3, 65, "channel", False, 32, 16),
+    (128, 128, 2, 1, "head", False, 32, 32),
+    (128, 128, 2, 31, "channel", True, 32, 32),
+    (128, 128, 1, 32, "head", True, 32, 16),
+    (128, 128, 3, 33, "channel", False, 32, 16),
     (128, 128, 2, 197, "head", True, 32, 32),
     (128, 128, 2, 197, "channel", True, 32, 16),
     (128, 64, 1, 300, "channel", True, 32, 32),
-    (64, 64, 3, 130, "head", True, 64, 32),
+    (64, 64, 3, 130, "head", True, 32, 32),
     (64, 32, 2, 129, "channel", True, 32, 16),
     (32, 32, 1, 95, "head", False, 32, 32),
     (32, 48, 2, 100, "channel", True, 32, 16),
-    (32, 48, 2, 100, "head", True, 64, 16),
+    (32, 48, 2, 100, "head", True, 32, 16),
 ]
 
 
@@ -131,8 +132,10 @@ F32_CASES = [
     (32, 16, 1, 15, "head", True, 16),
     (32, 32, 2, 70, "channel", True, 32),
     (64, 48, 1, 33, "head", True, 32),
-    (128, 64, 2, 100, "channel", True, 32),
+    (128, 64, 2, 100, "channel", True, 16),
     (128, 32, 1, 16, "head", False, 16),
+    (128, 32, 1, 77, "head", True, 32),
+    (64, 16, 2, 64, "channel", True, 32),
 ]
 
 
@@ -164,16 +167,26 @@ def test_prefill_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
-@pytest.mark.parametrize("gate,chunks", [("head", (32, 64)), ("channel", (32,))])
-def test_prefill_chunk_and_slice_invariance(gate, chunks):
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_slice_invariance(gate):
     inp = _small(128, 128, 2, 256, gate, torch.bfloat16, True, seed=52)
     ref_o, ref_s = _oracle(inp)
-    for chunk in chunks:
-        for dvs in (16, 32):
-            say(f"chunk {chunk} dv_slice {dvs}")
-            o, s = _gpu(inp, chunk_size=chunk, dv_slice=dvs)
-            assert_close("out", o, ref_o, TOL[torch.bfloat16])
-            assert_close("final_state", s, ref_s, TOL[torch.bfloat16])
+    for dvs in (16, 32):
+        say(f"dv_slice {dvs}")
+        o, s = _gpu(inp, dv_slice=dvs)
+        assert_close("out", o, ref_o, TOL[torch.bfloat16])
+        assert_close("final_state", s, ref_s, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_chunk_invariance_fp32(gate):
+    inp = _small(64, 32, 2, 150, gate, torch.float32, True, seed=56)
+    ref_o, ref_s = _oracle(inp)
+    for chunk in (16, 32):
+        say(f"chunk {chunk}")
+        o, s = _gpu(inp, chunk_size=chunk)
+        assert_close("out", o, ref_o, TOL[torch.float32])
+        assert_close("final_state", s, ref_s, TOL[torch.float32])
 
 
 def test_prefill_in_place_state_and_poisoned_output():
