@@ -59,31 +59,38 @@ def decode_alg_bytes(N, H, dk, dv, kda, out_bytes):
 
 
 def cpu_baseline(inp, H, target_s):
-    """fp64 oracle on the first tokens of every (sequence, head) unit of the
-    prefill workload, timed on the host cores; the token count is sized from
-    a short calibration run so the measured run takes about target_s."""
+    """fp64 oracle over the first tokens of every (sequence, head) unit of the
+    prefill workload, timed on the host cores.  The token count grows from a
+    short probe until one run takes at least target_s/4 (or covers the whole
+    sequence); that run is repeated until target_s of wall time has passed."""
     import oracle
 
     cores = len(os.sched_getaffinity(0))
     B, T = inp["q"].shape[:2]
     threads = min(cores, B * H)
     s0 = inp["initial_state"].cpu()
+    host = {k: inp[k].cpu() for k in ("q", "k", "v", "beta", "log_alpha")}
 
     def run(n):
-        sub = {k: inp[k][:, :n].contiguous().cpu() for k in ("q", "k", "v", "beta", "log_alpha")}
+        sub = {k: host[k][:, :n].contiguous() for k in host}
         t0 = time.perf_counter()
         oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["beta"], sub["log_alpha"], initial_state=s0,
                           num_threads=threads)
         return time.perf_counter() - t0
 
-    probe = 128
-    dt = run(probe)
-    sample_tokens = int(min(T, max(probe, probe * target_s / max(dt, 1e-3))))
-    dt = run(sample_tokens)
-    tokens = B * sample_tokens  # every head of these tokens
-    return {"value": tokens / dt / 1e6, "unit": "Mtok/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {sample_tokens} of {inp['q'].shape[1]} tokens of all {B}x{H} (sequence, head) "
-                      f"units of the prefill workload, fp64, {dt:.1f} s wall"}
+    n = 128
+    dt = run(n)
+    while dt < target_s / 4 and n < T:
+        n = int(min(T, max(2 * n, n * (target_s / 3) / max(dt, 1e-3))))
+        dt = run(n)
+    reps, total = 1, dt
+    while total < target_s:
+        total += run(n)
+        reps += 1
+    tokens = B * n * reps  # every head of these tokens
+    return {"value": tokens / total / 1e6, "unit": "Mtok/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {T} tokens of all {B}x{H} (sequence, head) units of the prefill "
+                      f"workload, fp64, {reps} run(s), {total:.1f} s wall"}
 
 
 def main():
