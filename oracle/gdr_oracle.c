@@ -18,8 +18,8 @@
  *   KDA equation:  S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T)
  *                        + beta_t v_t k_t^T.
  *
- *   S_t is d_v x d_k per head (same section: "a d_v x d_k state matrix per
- *   head"); the decay multiplies key columns.  Expanding either equation row by
+ *   The same section gives each head one state of d_v rows by d_k columns;
+ *   the decay multiplies key columns.  Expanding either equation row by
  *   row gives the order used below:
  *       S'   = S_{t-1} Diag(alpha_t)                 (decay)
  *       x    = S' k_t                                (what S' recalls for k_t)
