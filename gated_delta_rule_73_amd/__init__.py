@@ -50,7 +50,7 @@ def load_library():
             raise RuntimeError(f"{library_path} is missing: build it with `python -m gated_delta_rule_73_amd.build`")
         lib = ctypes.CDLL(library_path)
         p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-        lib.gdr_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), i32]
+        lib.gdr_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), i32, i32, i32, i32]
         lib.gdr_prefill_workspace_bytes.restype = sz
         lib.gdr_prefill_chunked.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, p, p, p, p, p, p, p, i32, i32, ctypes.c_float, p, p, p,
@@ -138,7 +138,8 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
         final_state = torch.empty(N, H, dv, dk, dtype=torch.float32, device=dev)
     _need(final_state, "final_state", torch.float32, dev)
     shape = PrefillShape(B, T, H, dk, dv, N)
-    ws_bytes = lib.gdr_prefill_workspace_bytes(ctypes.byref(shape), int(cu_seqlens is not None))
+    ws_bytes = lib.gdr_prefill_workspace_bytes(ctypes.byref(shape), gate, _dtype_code(q), int(chunk_size),
+                                               int(cu_seqlens is not None))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
     _check(lib.gdr_prefill_chunked(
         ctypes.byref(shape), gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),

@@ -56,10 +56,35 @@ gdr_status launch_status(hipError_t e, const char *what) {
     return fail(GDR_ERROR_LAUNCH_FAILED, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
-size_t order_bytes(int32_t num_seqs) {
-    const size_t b = sizeof(int32_t) * (size_t)(num_seqs > 0 ? num_seqs : 0);
-    return (b + 255) & ~size_t(255);
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Workspace of one prefill call: [order][chunk offsets] (packed batches only),
+// then one record per (chunk slot, head).
+struct PrefillWorkspace {
+    size_t order_off = 0, choff_off = 0, rec_off = 0, total = 0;
+    long record_chunks = 0;
+};
+
+PrefillWorkspace prefill_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, int chunk, bool packed) {
+    PrefillWorkspace w;
+    size_t off = 0;
+    if (packed) {
+        w.order_off = 0;
+        off = round256(sizeof(int32_t) * (size_t)s.num_seqs);
+        w.choff_off = off;
+        off += round256(sizeof(int32_t) * ((size_t)s.num_seqs + 1));
+    }
+    w.rec_off = off;
+    const long ncps = ((long)s.seqlen + chunk - 1) / chunk;
+    w.record_chunks = packed ? ncps + s.num_seqs : (long)s.batch * ncps;
+    off += (size_t)w.record_chunks * (size_t)s.num_heads *
+           gdr::chunk_record_stride(s.head_dim_k, chunk, kda, bf16 ? 2 : 4);
+    w.total = off;
+    return w;
 }
+
+// automatic chunk size: 32 tokens where compiled, else 16
+int auto_chunk(bool bf16, bool kda, int dk) { return gdr::prefill_supported(bf16, kda, dk, 16, 32) ? 32 : 16; }
 
 }  // namespace
 
@@ -85,9 +110,15 @@ uint64_t gdr_state_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim_k
     return (uint64_t)num_seqs * (uint64_t)num_heads * (uint64_t)head_dim_k * (uint64_t)head_dim_v * sizeof(float);
 }
 
-size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, int32_t packed) {
-    if (!shape || !packed) return 0;
-    return order_bytes(shape->num_seqs);
+size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
+                                   int32_t chunk_size, int32_t packed) {
+    if (!shape || !valid_gate(gate) || !valid_dtype(qkv_dtype)) return 0;
+    const gdr_prefill_shape &s = *shape;
+    if (s.batch < 1 || s.seqlen < 0 || s.num_heads < 1 || s.head_dim_k < 1 || s.num_seqs < 0) return 0;
+    if (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
+    const bool bf16 = qkv_dtype == GDR_BF16, kda = gate == GDR_GATE_CHANNEL;
+    const int C = chunk_size ? chunk_size : auto_chunk(bf16, kda, s.head_dim_k);
+    return prefill_workspace(s, kda, bf16, C, packed != 0).total;
 }
 
 gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
@@ -135,7 +166,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
         const int64_t units = (int64_t)s.num_seqs * s.num_heads;
         DVS = (!bf16 || dv % 32 != 0 || units * (dv / 32) < 256) ? 16 : 32;
     }
-    if (!C) C = gdr::prefill_supported(bf16, kda, dk, DVS, 32) ? 32 : 16;
+    if (!C) C = auto_chunk(bf16, kda, dk);
     if (!gdr::prefill_supported(bf16, kda, dk, DVS, C))
         return fail(GDR_ERROR_NOT_SUPPORTED, "no prefill kernel for %s dk=%d dv_slice=%d chunk=%d",
                     bf16 ? "bf16" : "fp32", dk, DVS, C);
@@ -151,10 +182,12 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     const char *names16[] = {"q", "k", "v", "out", "initial_state", "final_state"};
     for (int i = 0; i < 6; ++i)
         if (!aligned(aligned16[i], 16)) return fail(GDR_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", names16[i]);
-    if (!aligned(beta, 4) || !aligned(log_alpha, 4) || !aligned(cu_seqlens, 4))
-        return fail(GDR_ERROR_INVALID_VALUE, "beta, log_alpha and cu_seqlens must be 4-byte aligned");
+    if (!aligned(beta, 4) || !aligned(log_alpha, kda ? 16 : 4) || !aligned(cu_seqlens, 4))
+        return fail(GDR_ERROR_INVALID_VALUE, "beta and cu_seqlens must be 4-byte aligned, log_alpha %d-byte aligned",
+                    kda ? 16 : 4);
 
-    const size_t need_ws = packed ? order_bytes(s.num_seqs) : 0;
+    const PrefillWorkspace ws = prefill_workspace(s, kda, bf16, C, packed);
+    const size_t need_ws = ws.total;
     if (workspace_bytes < need_ws)
         return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need_ws);
     if (need_ws && !workspace) return fail(GDR_ERROR_INVALID_VALUE, "workspace is NULL");
@@ -197,7 +230,11 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     a.scale = scale;
     a.out = out;
     a.final_state = final_state;
-    a.order = static_cast<int32_t *>(workspace);
+    char *wsb = static_cast<char *>(workspace);
+    a.order = packed ? reinterpret_cast<int32_t *>(wsb + ws.order_off) : nullptr;
+    a.chunk_offset = packed ? reinterpret_cast<int32_t *>(wsb + ws.choff_off) : nullptr;
+    a.records = wsb ? wsb + ws.rec_off : nullptr;
+    a.record_chunks = ws.record_chunks;
     return launch_status(gdr::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_chunked");
 }
 

@@ -1,11 +1,13 @@
 // prefill.hip -- prefill dispatch and the packed-batch schedule.
 //
 // Packed batches (cu_seqlens) can hold sequences of very different lengths;
-// each (sequence, head, value slice) is one workgroup that walks its chunks
-// in order, so the longest sequence sets the critical path.  A tiny kernel
-// ranks the sequences longest first (ties by index, so the schedule is
-// deterministic) and the prefill kernel maps its workgroups in that order,
-// letting the long chains start first.
+// each (sequence, head, value slice) is one chain workgroup that walks its
+// chunks in order, so the longest sequence sets the critical path.  A tiny
+// kernel ranks the sequences longest first (ties by index, so the schedule is
+// deterministic) and the chain kernel maps its workgroups in that order,
+// letting the long chains start first.  The same kernel gives each sequence
+// its first slot in the per-chunk record array (prefix sum of its chunk
+// counts; quadratic in the number of sequences, which is small).
 #include "launch.h"
 #include "prefill_shapes.h"
 
@@ -16,17 +18,20 @@ hipError_t launch_prefill_bf16_kda(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_f32_gdn(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_f32_kda(const PrefillArgs &a, hipStream_t st);
 
-__global__ __launch_bounds__(256) void longest_first_kernel(const int32_t *__restrict__ cu, int n,
-                                                            int32_t *__restrict__ order) {
+__global__ __launch_bounds__(256) void schedule_kernel(const int32_t *__restrict__ cu, int n, int chunk,
+                                                       int32_t *__restrict__ order, int32_t *__restrict__ choff) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const int li = cu[i + 1] - cu[i];
-    int rank = 0;
+    int rank = 0, off = 0;
     for (int j = 0; j < n; ++j) {
         const int lj = cu[j + 1] - cu[j];
         rank += (lj > li) || (lj == li && j < i);
+        if (j < i) off += (lj + chunk - 1) / chunk;
     }
     order[rank] = i;
+    choff[i] = off;
+    if (i == n - 1) choff[n] = off + (li + chunk - 1) / chunk;
 }
 
 bool prefill_supported(bool bf16, bool kda, int dk, int dv_slice, int chunk) {
@@ -47,8 +52,8 @@ bool prefill_supported(bool bf16, bool kda, int dk, int dv_slice, int chunk) {
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     if (a.num_seqs == 0 || a.num_heads == 0) return hipSuccess;
     if (a.cu_seqlens) {
-        hipLaunchKernelGGL(longest_first_kernel, dim3((unsigned)((a.num_seqs + 255) / 256)), dim3(256), 0, st,
-                           a.cu_seqlens, a.num_seqs, a.order);
+        hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)((a.num_seqs + 255) / 256)), dim3(256), 0, st,
+                           a.cu_seqlens, a.num_seqs, a.chunk, a.order, a.chunk_offset);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -9,11 +9,10 @@
 #define GDR_PREFILL_BF16_KDA_SHAPES(X) \
     X(32, 16, 32) X(32, 32, 32) X(64, 16, 32) X(64, 32, 32) X(128, 16, 32) X(128, 32, 32)
 
-// fp32 q/k/v: fp32 MFMA 16x16x4, chunks of 16 or 32 tokens (16 only for
-// per-channel decay at d_k = 128, where 32 would overflow LDS).
+// fp32 q/k/v: fp32 MFMA 16x16x4, chunks of 16 or 32 tokens.
 #define GDR_PREFILL_F32_GDN_SHAPES(X) \
     X(16, 16, 16) X(16, 16, 32) X(32, 16, 16) X(32, 16, 32) \
     X(64, 16, 16) X(64, 16, 32) X(128, 16, 16) X(128, 16, 32)
 #define GDR_PREFILL_F32_KDA_SHAPES(X) \
     X(16, 16, 16) X(16, 16, 32) X(32, 16, 16) X(32, 16, 32) \
-    X(64, 16, 16) X(64, 16, 32) X(128, 16, 16)
+    X(64, 16, 16) X(64, 16, 32) X(128, 16, 16) X(128, 16, 32)

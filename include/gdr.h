@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum gdr_status {
     GDR_SUCCESS = 0,
@@ -93,11 +93,21 @@ typedef struct gdr_prefill_shape {
 } gdr_prefill_shape;
 
 /*
- * Bytes of device workspace gdr_prefill_chunked needs for this shape: the
- * per-call sequence schedule of a packed batch (packed != 0, i.e. cu_seqlens
- * will be passed); 0 for a dense batch.  Returns 0 for a NULL shape.
+ * Bytes of device workspace gdr_prefill_chunked needs for this problem:
+ *  - packed batches (packed != 0, i.e. cu_seqlens will be passed): the
+ *    per-call sequence schedule, 2 x 4 x (num_seqs + 1) bytes, rounded up;
+ *  - one record per chunk slot and head holding that chunk's state-independent
+ *    operands (decayed keys and queries, the transposed end-of-chunk keys, the
+ *    UT-transform inverse and the intra-chunk query-key matrix):
+ *    (num_heads x chunk slots) x R bytes, where the chunk slots are
+ *    batch x ceil(seqlen / C) (dense) or ceil(seqlen / C) + num_seqs (packed)
+ *    and R is about (3 C d_k + 2 C^2) x (2 for bf16 q/k/v, 4 for fp32) bytes.
+ * gate, qkv_dtype and chunk_size are the values that will be passed to
+ * gdr_prefill_chunked (chunk_size 0 = automatic).  Returns 0 for a NULL shape
+ * or an invalid argument.
  */
-size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, int32_t packed);
+size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
+                                   int32_t chunk_size, int32_t packed);
 
 /*
  * Chunked prefill: runs the recurrence over every token of every sequence and
@@ -134,7 +144,12 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, int32_t packe
  *  hip_stream     hipStream_t to enqueue on.
  * Limits: head_dim_k in {16, 32, 64, 128} (bf16: {32, 64, 128}); head_dim_v
  * a multiple of 16 up to 256; the q/k/v/out/state base pointers 16-byte
- * aligned; gate pointers 4-byte aligned.
+ * aligned; beta 4-byte aligned; log_alpha 16-byte aligned for
+ * GDR_GATE_CHANNEL, else 4-byte aligned.  Per-channel decay: the log-decay
+ * summed over one chunk must stay above about -170 in every channel (the
+ * chunk's operands are scaled around its midpoint in fp32 range).
+ * Work: one kernel computes every chunk's record into the workspace, a second
+ * walks each sequence's chunks in order; both are enqueued on hip_stream.
  * Returns GDR_SUCCESS or an error status (nothing enqueued on error).
  */
 gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = gdr.load_library()
-    assert lib.gdr_abi_version() == 1
+    assert lib.gdr_abi_version() == 2
     assert lib.gdr_status_string(0) == b"success"
     assert lib.gdr_status_string(2) == b"not supported"
 
@@ -55,7 +55,7 @@ MB = 1 << 20
 
 
 def _prefill(shape=(1, 64, 2, 64, 64, 1), gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + 8 * MB, v=A + 16 * MB, beta=A + 24 * MB,
-             la=A + 25 * MB, s0=None, cu=None, chunk=0, dvs=0, out=A + 32 * MB, fin=None, ws=None, wsb=0):
+             la=A + 25 * MB, s0=None, cu=None, chunk=0, dvs=0, out=A + 32 * MB, fin=None, ws=A + 48 * MB, wsb=16 * MB):
     lib = gdr.load_library()
     sh = gdr.PrefillShape(*shape)
     v_ = lambda x: None if x is None else ctypes.c_void_p(x)
@@ -97,9 +97,12 @@ def _decode(N=4, H=2, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + MB, 
     (dict(out=A - 32 * 1024 + 16, odt=1), 0, None),                 # bf16 out (16 KiB) stops short of q
     (dict(fin=A + 8 * MB), 1, "final_state overlaps k"),
     (dict(s0=A + 40 * MB, fin=A + 40 * MB + 16), 1, "final_state overlaps initial_state"),
-    (dict(cu=A + 40 * MB, ws=None, wsb=0), 3, "workspace"),
-    (dict(cu=A + 40 * MB, ws=None, wsb=4096), 1, "workspace is NULL"),
-    (dict(cu=A + 40 * MB, ws=A + 48 * MB + 4, wsb=4096), 1, "256-byte"),
+    (dict(wsb=0), 3, "workspace"),
+    (dict(cu=A + 40 * MB, wsb=60000), 3, "workspace"),          # packed: schedule + more chunk slots
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(ws=A + 48 * MB + 4), 1, "256-byte"),
+    (dict(ws=A + 24 * MB), 1, "workspace overlaps beta"),
+    (dict(shape=(1, 64, 2, 64, 64, 1), gate=1, la=A + 25 * MB + 4), 1, "log_alpha 16-byte"),
 ])
 def test_prefill_rejects(kw, status, msg):
     if status == 0:
@@ -114,12 +117,21 @@ def test_prefill_rejects(kw, status, msg):
 
 
 def test_prefill_workspace_size():
+    """Records: one per (chunk slot, head) of (3 C dk + 2 C^2) operands plus
+    the decay rows, 256-byte aligned; packed batches add the schedule and one
+    spare chunk slot per sequence."""
     lib = gdr.load_library()
+    f = lib.gdr_prefill_workspace_bytes
     sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9)
-    assert lib.gdr_prefill_workspace_bytes(ctypes.byref(sh), 0) == 0
-    ws = lib.gdr_prefill_workspace_bytes(ctypes.byref(sh), 1)
-    assert ws >= 9 * 4 and ws % 256 == 0
-    assert lib.gdr_prefill_workspace_bytes(None, 1) == 0
+    rec_gdn_bf16 = -(-(4 * 4 + 32 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
+    rec_kda_f32 = -(-(64 * 4 + 4 * 4 + (3 * 16 * 64 + 2 * 16 * 16) * 4) // 256) * 256
+    assert f(ctypes.byref(sh), 0, 1, 32, 0) == 32 * 4 * rec_gdn_bf16
+    assert f(ctypes.byref(sh), 0, 1, 0, 0) == 32 * 4 * rec_gdn_bf16          # automatic chunk = 32
+    assert f(ctypes.byref(sh), 0, 1, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_bf16
+    assert f(ctypes.byref(sh), 1, 0, 16, 0) == 63 * 4 * rec_kda_f32
+    assert f(None, 0, 1, 0, 1) == 0
+    assert f(ctypes.byref(sh), 5, 1, 0, 0) == 0
+    assert f(ctypes.byref(sh), 0, 1, 48, 0) == 0
 
 
 @pytest.mark.parametrize("kw,status,msg", [
