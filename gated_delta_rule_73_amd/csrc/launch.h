@@ -36,11 +36,10 @@ struct PrefillArgs {
 };
 
 // Size of one per-chunk record of the prefill (see ChunkRec in
-// prefill_impl.h): decay row, GDN e^{g_r}, K e^g, Q e^g, K_end^T, T diag(b), M.
+// prefill_impl.h): decay row, K e^g, Q e^g, K_end^T, T diag(b), M.
 // es = bytes per operand element (2 for fp16 operands, 4 for fp32).
 constexpr size_t chunk_record_bytes(int dk, int chunk, bool kda, int es) {
-    return (size_t)(kda ? dk : 4) * 4 + (size_t)(kda ? 4 : chunk) * 4 +
-           ((size_t)3 * chunk * dk + (size_t)2 * chunk * chunk) * (size_t)es;
+    return (size_t)(kda ? dk : 4) * 4 + ((size_t)3 * chunk * dk + (size_t)2 * chunk * chunk) * (size_t)es;
 }
 constexpr size_t chunk_record_stride(int dk, int chunk, bool kda, int es) {
     return (chunk_record_bytes(dk, chunk, kda, es) + 255) & ~size_t(255);

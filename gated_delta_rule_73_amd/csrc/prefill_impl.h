@@ -84,17 +84,21 @@ template <int NBLK> struct RegB<_Float16, NBLK> {
                 f[s][4 + i] = (_Float16)v[2 * s + 1][i];
             }
     }
-    // split v = hi + lo: this object takes hi, `lo` takes the remainder
+    // split v = hi + lo: this object takes hi, `lo` takes the remainder.
+    // hi keeps the top 11 significant bits (exact in fp16 over its normal
+    // range), so lo = v - hi is exact in fp32 and |lo| < 2^-10 |v|.
     __device__ __forceinline__ void set_split(const f32x4 *v, RegB &lo) {
 #pragma unroll
         for (int s = 0; s < NBLK / 2; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const _Float16 h0 = (_Float16)v[2 * s][i], h1 = (_Float16)v[2 * s + 1][i];
-                f[s][i] = h0;
-                f[s][4 + i] = h1;
-                lo.f[s][i] = (_Float16)(v[2 * s][i] - (float)h0);
-                lo.f[s][4 + i] = (_Float16)(v[2 * s + 1][i] - (float)h1);
+                const float x0 = v[2 * s][i], x1 = v[2 * s + 1][i];
+                const float h0 = __uint_as_float(__float_as_uint(x0) & 0xffffe000u);
+                const float h1 = __uint_as_float(__float_as_uint(x1) & 0xffffe000u);
+                f[s][i] = (_Float16)h0;
+                f[s][4 + i] = (_Float16)h1;
+                lo.f[s][i] = (_Float16)(x0 - h0);
+                lo.f[s][4 + i] = (_Float16)(x1 - h1);
             }
     }
     // acc += A * B, A given as preloaded fragments (RowA) of the same k-range
@@ -201,9 +205,8 @@ template <int DK, int C, bool KDA, typename IT>
 struct ChunkRec {
     using ST = typename Prec<IT>::ST;
     float dec[KDA ? DK : 4];   // e^{g_C}: per key channel (KDA) or dec[0] (GDN)
-    float eg[KDA ? 4 : C];     // GDN: e^{g_r}
-    ST Kt[C][DK];              // KDA: k e^g     GDN: k
-    ST Qt[C][DK];              // KDA: q e^g     GDN: q
+    ST Kt[C][DK];              // k e^g
+    ST Qt[C][DK];              // q e^g
     ST KeT[DK][C];             // (k e^{g_C - g})^T
     ST Tm[C][C];               // T diag(b), zero above the diagonal
     ST Mm[C][C];               // M, zero above the diagonal
@@ -225,7 +228,7 @@ struct PrepSmem {
         float Pt[4][2 * NT][16][20];     // per-wave partial Gram tiles: A tiles, then M tiles
     } u;
     alignas(16) float em[KDA ? DK : 4];  // KDA: e^m
-    float g[C], egc[C], beta[C];         // GDN: g, e^{g_C - g};  beta
+    float g[C], egc[C], egt[C], beta[C]; // GDN: g, e^{g_C - g}, e^g;  beta
     alignas(16) float Af[C][LDA];        // strict_tril(diag(b) Gram)
     alignas(16) float Tf[C][LDA];        // (I + A)^-1
     float P[256];                        // A_10 T_00
@@ -233,6 +236,7 @@ struct PrepSmem {
 
 struct PrepKArgs {
     int T, H, num_seqs, ncps;
+    float scale;                 // readout factor, folded into Q e^g and M
     const void *q, *k;
     const float *beta, *log_alpha;
     const int32_t *cu, *choff;
@@ -311,7 +315,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
             if (t < nv) gv = *reinterpret_cast<const f32x4 *>(p.log_alpha + ((size_t)(t0 + t) * H + h) * DK + c);
             *reinterpret_cast<f32x4 *>(&sm.u.in.G[t][c]) = gv;
         }
-        if (tid < 4) rec.eg[tid] = 0.f;
     } else if (wave == 0) {
         float g = lane < nv && lane < C ? p.log_alpha[(size_t)(t0 + lane) * H + h] : 0.f;
 #pragma unroll
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
         if (lane < C) {
             sm.g[lane] = g;
             sm.egc[lane] = __expf(gC - g);
-            rec.eg[lane] = __expf(g);
+            sm.egt[lane] = __expf(g);
         }
         if (lane < 4) rec.dec[lane] = lane == 0 ? __expf(gC) : 0.f;
     }
@@ -419,15 +422,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                         fql[rb][4 * hh + i] = (FT)(lq - (float)qh);
                         frl[rb][4 * hh + i] = (FT)(rk - (float)rh);
                         kt[i] = (ST)(lk * emv[i]);
-                        qt[i] = (ST)(lq * emv[i]);
+                        qt[i] = (ST)(lq * emv[i] * p.scale);
                     }
                 } else {
+                    // raw k, q for the Gram (the decay scales its fp32 result);
+                    // k e^g, q e^g for the state-side products
+                    const float e = sm.egt[t];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        kt[i] = (ST)kf[i];
-                        qt[i] = (ST)qf[i];
-                        fk[rb][4 * hh + i] = kt[i];
-                        fq[rb][4 * hh + i] = qt[i];
+                        fk[rb][4 * hh + i] = (ST)kf[i];
+                        fq[rb][4 * hh + i] = (ST)qf[i];
+                        kt[i] = (ST)(kf[i] * e);
+                        qt[i] = (ST)(qf[i] * e * p.scale);
                     }
                 }
                 if (valid) {
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                 fm *= d;
             }
             sm.Af[R][c] = fa;
-            mv[i] = (ST)fm;
+            mv[i] = (ST)(fm * p.scale);
         }
         store_vec<ST, 4>(&rec.Mm[R][c0], mv);
     }
@@ -557,15 +563,14 @@ struct alignas(16) ChainSlot {
     static constexpr int PAD = 16 / sizeof(ST);   // 16-byte row padding spreads LDS banks
     static constexpr int LDK = DK + PAD;
     static constexpr int LDC = C + PAD;
-    static constexpr int LDV = DVS + 16 / sizeof(IT);
+    static constexpr int LDVT = C + 16 / sizeof(IT);
     float dec[KDA ? DK : 4];
-    float eg[KDA ? 4 : C];
     ST Kt[C][LDK];
     ST Qt[C][LDK];
     ST KeT[DK][LDC];
     ST Tm[C][LDC];
     ST Mm[C][LDC];
-    IT V[C][LDV];
+    IT Vt[DVS][LDVT];             // value slice, transposed (token columns)
 };
 
 // Byte offset in a ChainSlot of the 16-byte piece p of a ChunkRec: the
@@ -574,13 +579,11 @@ template <int DK, int DVS, int C, bool KDA, typename IT>
 __device__ __forceinline__ int slot_offset(int p) {
     using Slot = ChainSlot<DK, DVS, C, KDA, IT>;
     using ST = typename Prec<IT>::ST;
-    constexpr int PD = (KDA ? DK : 4) * 4 / 16, PE = (KDA ? 4 : C) * 4 / 16;
+    constexpr int PD = (KDA ? DK : 4) * 4 / 16;
     constexpr int RK = DK * (int)sizeof(ST) / 16, RC = C * (int)sizeof(ST) / 16;
     constexpr int BK = Slot::LDK * (int)sizeof(ST), BC = Slot::LDC * (int)sizeof(ST);
     if (p < PD) return (int)__builtin_offsetof(Slot, dec) + 16 * p;
     p -= PD;
-    if (p < PE) return (int)__builtin_offsetof(Slot, eg) + 16 * p;
-    p -= PE;
     if (p < C * RK) return (int)__builtin_offsetof(Slot, Kt) + (p / RK) * BK + (p % RK) * 16;
     p -= C * RK;
     if (p < C * RK) return (int)__builtin_offsetof(Slot, Qt) + (p / RK) * BK + (p % RK) * 16;
@@ -598,15 +601,13 @@ struct ChainKArgs {
     const float *initial_state;
     const int32_t *cu, *order, *choff;
     const char *rec;
-    float scale;
     void *out;
     float *final_state;
-    bool out_bf16;
 };
 
 constexpr int kLoaderWaves = 4;
 
-template <int DK, int DVS, int C, bool KDA, typename IT>
+template <int DK, int DVS, int C, bool KDA, typename IT, bool OUTB>
 __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(ChainKArgs p) {
     using Slot = ChainSlot<DK, DVS, C, KDA, IT>;
     using Rec = ChunkRec<DK, C, KDA, IT>;
@@ -663,13 +664,16 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             St[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (p.initial_state) St[kb] = *reinterpret_cast<const f32x4 *>(p.initial_state + srow + 16 * kb);
         }
-        float *gof = static_cast<float *>(p.out);
-        __bf16 *gob = static_cast<__bf16 *>(p.out);
+        using OT = typename std::conditional<OUTB, __bf16, float>::type;
+        // outputs of chunk jc: a uniform row base plus 32-bit lane offsets
+        const int HDV = H * DV;
+        const int oofs = 4 * lg * HDV + lr;
         __syncthreads();
         for (int jc = 0; jc < nchunks; ++jc) {
             const Slot &bc = slot[jc & 1];
             const int t0 = bos + jc * C;
             const int nv = min(C, eos - t0);
+            OT *ob = static_cast<OT *>(p.out) + ((size_t)t0 * H + h) * DV + v0 + 16 * cb;
             // every LDS operand of the chunk, read up front
             RowA<ST, NKB> ka[NB], qa[NB];
 #pragma unroll
@@ -677,15 +681,14 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
                 ka[rb].load(&bc.Kt[16 * rb + lr][0], lg);
                 qa[rb].load(&bc.Qt[16 * rb + lr][0], lg);
             }
-            float vv[NB][4], eg[NB][4];
+            float vv[NB][4];
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb)
+            for (int rb = 0; rb < NB; ++rb) {
+                using IV4 = typename VecT<IT, 4>::type;
+                const IV4 x = *reinterpret_cast<const IV4 *>(&bc.Vt[16 * cb + lr][16 * rb + 4 * lg]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * rb + 4 * lg + i;
-                    vv[rb][i] = (float)bc.V[t][16 * cb + lr];
-                    eg[rb][i] = KDA ? 1.f : bc.eg[KDA ? 0 : t];
-                }
+                for (int i = 0; i < 4; ++i) vv[rb][i] = (float)x[i];
+            }
             RegB<ST, NKB> sop;
             sop.set(St);
             f32x4 X[NB], Y[NB], W[NB];
@@ -704,10 +707,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Y[rb][i] *= eg[rb][i];
-                    W[rb][i] = vv[rb][i] - X[rb][i] * eg[rb][i];
-                }
+                for (int i = 0; i < 4; ++i) W[rb][i] = vv[rb][i] - X[rb][i];
             RegB<ST, NB> wh, wl;
             wh.set_split(W, wl);
             f32x4 U[NB];
@@ -727,14 +727,13 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
                 const int ns = (16 * rb + 16 + 31) / 32;
                 f32x4 o = uh.mma(Y[rb], ma[rb], ns);
                 if constexpr (SPLIT) o = ul.mma(o, ma[rb], ns);
+                if (nv == C) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * rb + 4 * lg + i;
-                    if (t < nv) {
-                        const size_t off = ((size_t)(t0 + t) * H + h) * DV + v0 + 16 * cb + lr;
-                        if (p.out_bf16) gob[off] = (__bf16)(p.scale * o[i]);
-                        else gof[off] = p.scale * o[i];
-                    }
+                    for (int i = 0; i < 4; ++i) ob[oofs + (16 * rb + i) * HDV] = (OT)o[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * rb + 4 * lg + i < nv) ob[oofs + (16 * rb + i) * HDV] = (OT)o[i];
                 }
             }
 #pragma unroll
@@ -794,7 +793,10 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
 #pragma unroll
         for (int x = 0; x < PPT; ++x)
             if (lofs[x] >= 0) *reinterpret_cast<i32x4 *>(base + lofs[x]) = r[x];
-        if (tid < VV) *reinterpret_cast<IV *>(&s.V[vt][vc]) = v;
+        if (tid < VV) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) s.Vt[vc + e][vt] = v[e];
+        }
     };
 #pragma unroll
     for (int c = 0; c < DEPTH; ++c) issue(rg[c], vr[c], c);
@@ -817,6 +819,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
 
 template <int DK, int DVS, int C, bool KDA, typename IT>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
+    constexpr int threads = 64 * (kLoaderWaves + DVS / 16);
     const int ncps = (a.seqlen + C - 1) / C;
     if (a.record_chunks > 0) {
         PrepKArgs pk;
@@ -824,6 +827,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
         pk.H = a.num_heads;
         pk.num_seqs = a.num_seqs;
         pk.ncps = ncps;
+        pk.scale = a.scale;
         pk.q = a.q; pk.k = a.k;
         pk.beta = a.beta; pk.log_alpha = a.log_alpha;
         pk.cu = a.cu_seqlens;
@@ -846,14 +850,14 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
     p.order = a.cu_seqlens ? a.order : nullptr;
     p.choff = a.chunk_offset;
     p.rec = a.records;
-    p.scale = a.scale;
     p.out = a.out;
     p.final_state = a.final_state;
-    p.out_bf16 = a.out_bf16;
     const long units = (long)a.num_seqs * a.num_heads;
     const long grid = ((units + 7) / 8) * 8 * (a.dv / DVS);
-    hipLaunchKernelGGL((chain_kernel<DK, DVS, C, KDA, IT>), dim3((unsigned)grid),
-                       dim3(64 * (kLoaderWaves + DVS / 16)), 0, st, p);
+    if (a.out_bf16)
+        hipLaunchKernelGGL((chain_kernel<DK, DVS, C, KDA, IT, true>), dim3((unsigned)grid), dim3(threads), 0, st, p);
+    else
+        hipLaunchKernelGGL((chain_kernel<DK, DVS, C, KDA, IT, false>), dim3((unsigned)grid), dim3(threads), 0, st, p);
     return hipGetLastError();
 }
 

@@ -101,7 +101,8 @@ typedef struct gdr_prefill_shape {
  *    UT-transform inverse and the intra-chunk query-key matrix):
  *    (num_heads x chunk slots) x R bytes, where the chunk slots are
  *    batch x ceil(seqlen / C) (dense) or ceil(seqlen / C) + num_seqs (packed)
- *    and R is about (3 C d_k + 2 C^2) x (2 for bf16 q/k/v, 4 for fp32) bytes.
+ *    and R is (3 C d_k + 2 C^2) x (2 for bf16 q/k/v, 4 for fp32) bytes plus
+ *    the chunk's decay (4 d_k or 16 bytes), rounded up to 256.
  * gate, qkv_dtype and chunk_size are the values that will be passed to
  * gdr_prefill_chunked (chunk_size 0 = automatic).  Returns 0 for a NULL shape
  * or an invalid argument.

@@ -123,8 +123,8 @@ def test_prefill_workspace_size():
     lib = gdr.load_library()
     f = lib.gdr_prefill_workspace_bytes
     sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9)
-    rec_gdn_bf16 = -(-(4 * 4 + 32 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
-    rec_kda_f32 = -(-(64 * 4 + 4 * 4 + (3 * 16 * 64 + 2 * 16 * 16) * 4) // 256) * 256
+    rec_gdn_bf16 = -(-(4 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
+    rec_kda_f32 = -(-(64 * 4 + (3 * 16 * 64 + 2 * 16 * 16) * 4) // 256) * 256
     assert f(ctypes.byref(sh), 0, 1, 32, 0) == 32 * 4 * rec_gdn_bf16
     assert f(ctypes.byref(sh), 0, 1, 0, 0) == 32 * 4 * rec_gdn_bf16          # automatic chunk = 32
     assert f(ctypes.byref(sh), 0, 1, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_bf16
