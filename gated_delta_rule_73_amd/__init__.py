@@ -107,12 +107,15 @@ def gdr_state_bytes(num_seqs: int, num_heads: int, head_dim_k: int, head_dim_v: 
 
 def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seqlens=None, chunk_size: int = 0,
                         dv_slice: int = 0, scale: float = 1.0, out=None, out_dtype=torch.float32,
-                        final_state=None, output_final_state: bool = True):
+                        final_state=None, output_final_state: bool = True, workspace=None):
     """Chunked prefill.  q, k [B, T, H, dk]; v [B, T, H, dv] (bf16 or fp32);
     beta [B, T, H] fp32; log_alpha [B, T, H] (per-head decay) or [B, T, H, dk]
     (per-key-channel decay) fp32; initial_state [N, H, dv, dk] fp32 or None;
     cu_seqlens int32 [N+1] (packed, B == 1) or None.
     out_dtype (fp32 or bf16) applies when ``out`` is not given.
+    workspace: uint8 device tensor, or None to allocate the size
+    ``gdr_prefill_workspace_bytes`` reports (a smaller one makes a dense batch
+    run in segments).
     Returns (out [B, T, H, dv], final_state [N, H, dv, dk] or None)."""
     lib = load_library()
     dev = q.device
@@ -140,7 +143,11 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
     shape = PrefillShape(B, T, H, dk, dv, N)
     ws_bytes = lib.gdr_prefill_workspace_bytes(ctypes.byref(shape), gate, _dtype_code(q), int(chunk_size),
                                                int(cu_seqlens is not None))
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    if workspace is None:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+        ws, ws_bytes = workspace, workspace.numel()
     _check(lib.gdr_prefill_chunked(
         ctypes.byref(shape), gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
         _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(dv_slice), float(scale), _ptr(out),

@@ -4,13 +4,14 @@
 // and needs no GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/gdr.h"
+#include "gdr.h"
 #include "launch.h"
 
 namespace {
@@ -59,13 +60,20 @@ gdr_status launch_status(hipError_t e, const char *what) {
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Workspace of one prefill call: [order][chunk offsets] (packed batches only),
-// then one record per (chunk slot, head).
+// the per-chunk records, and (segmented runs) the state carried between
+// segments.  seg = 0: one record per chunk of every sequence (the size
+// gdr_prefill_workspace_bytes reports); seg > 0 (dense batches): records of
+// one segment of seg chunks at a time.
 struct PrefillWorkspace {
-    size_t order_off = 0, choff_off = 0, rec_off = 0, total = 0;
+    size_t order_off = 0, choff_off = 0, rec_off = 0, carry_off = 0, total = 0;
     long record_chunks = 0;
+    int num_segments = 1, segment_chunks = 0;
 };
 
-PrefillWorkspace prefill_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, int chunk, bool packed) {
+constexpr int kMinSegmentChunks = 16;
+
+PrefillWorkspace prefill_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, int chunk, bool packed,
+                                   long seg = 0) {
     PrefillWorkspace w;
     size_t off = 0;
     if (packed) {
@@ -74,13 +82,38 @@ PrefillWorkspace prefill_workspace(const gdr_prefill_shape &s, bool kda, bool bf
         w.choff_off = off;
         off += round256(sizeof(int32_t) * ((size_t)s.num_seqs + 1));
     }
-    w.rec_off = off;
     const long ncps = ((long)s.seqlen + chunk - 1) / chunk;
-    w.record_chunks = packed ? ncps + s.num_seqs : (long)s.batch * ncps;
-    off += (size_t)w.record_chunks * (size_t)s.num_heads *
-           gdr::chunk_record_stride(s.head_dim_k, chunk, kda, bf16 ? 2 : 4);
+    w.segment_chunks = (int)ncps;
+    if (!packed && seg > 0 && seg < ncps) {
+        w.segment_chunks = (int)seg;
+        w.num_segments = (int)((ncps + seg - 1) / seg);
+    }
+    w.rec_off = off;
+    w.record_chunks = packed ? ncps + s.num_seqs : (long)s.batch * w.segment_chunks;
+    off += round256((size_t)w.record_chunks * (size_t)s.num_heads *
+                    gdr::chunk_record_stride(s.head_dim_k, chunk, kda, bf16 ? 2 : 4));
+    w.carry_off = off;
+    if (w.num_segments > 1)
+        off += round256((size_t)s.num_seqs * s.num_heads * s.head_dim_k * s.head_dim_v * sizeof(float));
     w.total = off;
     return w;
+}
+
+// The layout for a workspace of `bytes`: unsegmented if it fits, else (dense
+// batches) the longest segment that fits; total > bytes if none does.
+PrefillWorkspace fit_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, int chunk, bool packed, size_t bytes) {
+    PrefillWorkspace w = prefill_workspace(s, kda, bf16, chunk, packed);
+    if (w.total <= bytes || packed) return w;
+    long lo = kMinSegmentChunks, hi = w.segment_chunks - 1;
+    PrefillWorkspace best = prefill_workspace(s, kda, bf16, chunk, packed, lo);
+    if (best.total > bytes) return w;
+    while (lo < hi) {   // largest segment whose layout fits
+        const long mid = (lo + hi + 1) / 2;
+        const PrefillWorkspace m = prefill_workspace(s, kda, bf16, chunk, packed, mid);
+        if (m.total <= bytes) { lo = mid; best = m; }
+        else hi = mid - 1;
+    }
+    return best;
 }
 
 // automatic chunk size: 32 tokens where compiled, else 16
@@ -186,7 +219,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
         return fail(GDR_ERROR_INVALID_VALUE, "beta and cu_seqlens must be 4-byte aligned, log_alpha %d-byte aligned",
                     kda ? 16 : 4);
 
-    const PrefillWorkspace ws = prefill_workspace(s, kda, bf16, C, packed);
+    const PrefillWorkspace ws = fit_workspace(s, kda, bf16, C, packed, workspace_bytes);
     const size_t need_ws = ws.total;
     if (workspace_bytes < need_ws)
         return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need_ws);
@@ -235,6 +268,9 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     a.chunk_offset = packed ? reinterpret_cast<int32_t *>(wsb + ws.choff_off) : nullptr;
     a.records = wsb ? wsb + ws.rec_off : nullptr;
     a.record_chunks = ws.record_chunks;
+    a.num_segments = ws.num_segments;
+    a.segment_chunks = ws.segment_chunks;
+    a.carry = wsb ? reinterpret_cast<float *>(wsb + ws.carry_off) : nullptr;
     return launch_status(gdr::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_chunked");
 }
 

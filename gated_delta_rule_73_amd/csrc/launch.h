@@ -32,7 +32,10 @@ struct PrefillArgs {
     int32_t *order;                 // packed only: longest-first sequence order [num_seqs]
     int32_t *chunk_offset;          // packed only: first record chunk of each sequence [num_seqs + 1]
     char *records;                  // per-chunk records, record_chunks * num_heads of them
-    long record_chunks;             // chunk slots per head (dense: batch * ceil(seqlen / chunk))
+    long record_chunks;             // chunk slots per head (one segment: all chunks)
+    int num_segments;               // dense batches in a bounded workspace: chunk segments
+    int segment_chunks;             //   chunks per segment (records of one segment resident)
+    float *carry;                   //   state between segments [num_seqs, H, dv, dk]
 };
 
 // Size of one per-chunk record of the prefill (see ChunkRec in

@@ -235,7 +235,8 @@ struct PrepSmem {
 };
 
 struct PrepKArgs {
-    int T, H, num_seqs, ncps;
+    int T, H, num_seqs;
+    int j0, seg_chunks;          // dense: chunks [j0, j0 + seg_chunks) of every sequence
     float scale;                 // readout factor, folded into Q e^g and M
     const void *q, *k;
     const float *beta, *log_alpha;
@@ -285,8 +286,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
         n = lo;
         j = x - p.choff[n];
     } else {
-        n = x / p.ncps;
-        j = x % p.ncps;
+        n = x / p.seg_chunks;
+        j = p.j0 + x % p.seg_chunks;
     }
     const int bos = p.cu ? p.cu[n] : n * p.T;
     const int eos = p.cu ? p.cu[n + 1] : bos + p.T;
@@ -596,13 +597,14 @@ __device__ __forceinline__ int slot_offset(int p) {
 }
 
 struct ChainKArgs {
-    int T, H, DV, num_seqs, ncps;
+    int T, H, DV, num_seqs;
+    int j0, seg_chunks;          // dense: chunks [j0, j0 + seg_chunks) of every sequence
     const void *v;
-    const float *initial_state;
+    const float *state_in;       // state entering chunk j0 (NULL: zeros)
     const int32_t *cu, *order, *choff;
     const char *rec;
     void *out;
-    float *final_state;
+    float *state_out;            // state after the last chunk processed (NULL: not written)
 };
 
 constexpr int kLoaderWaves = 4;
@@ -645,16 +647,21 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     if (urank >= p.num_seqs * H) return;
     const int srank = urank / H, h = urank % H;
     const int n = p.order ? p.order[srank] : srank;
-    int bos, eos, x0;
-    if (p.cu) { bos = p.cu[n]; eos = p.cu[n + 1]; x0 = p.choff[n]; }
-    else { bos = n * p.T; eos = bos + p.T; x0 = n * p.ncps; }
+    int bos, eos, rbase;
+    if (p.cu) { bos = p.cu[n]; eos = p.cu[n + 1]; rbase = p.choff[n]; }
+    else { bos = n * p.T; eos = bos + p.T; rbase = n * p.seg_chunks; }
     const int v0 = slice * DVS;
-    const int nchunks = (eos - bos + C - 1) / C;
-    const char *rec0 = p.rec + ((size_t)x0 * H + h) * RS;   // chunk j at rec0 + j * H * RS
+    const int nall = (eos - bos + C - 1) / C;
+    const int nchunks = p.cu ? nall : max(0, min(nall - p.j0, p.seg_chunks));
+    bos += p.j0 * C;                                         // first token of this launch's chunks
+    const char *rec0 = p.rec + ((size_t)rbase * H + h) * RS;   // its chunk i at rec0 + i * H * RS
 
     if (wave >= NLW) {
         // =================== chain wave: 16 value channels ===================
         const int cb = wave - NLW;
+        // the chain is the serial critical path: let it win issue arbitration
+        // against loader waves and co-resident prep workgroups
+        __builtin_amdgcn_s_setprio(2);
         // S^T of this wave's value block (lane: value column v0 + 16 cb + lr,
         // key rows 16 kb + 4 lg + i)
         f32x4 St[NKB];
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             St[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (p.initial_state) St[kb] = *reinterpret_cast<const f32x4 *>(p.initial_state + srow + 16 * kb);
+            if (p.state_in) St[kb] = *reinterpret_cast<const f32x4 *>(p.state_in + srow + 16 * kb);
         }
         using OT = typename std::conditional<OUTB, __bf16, float>::type;
         // outputs of chunk jc: a uniform row base plus 32-bit lane offsets
@@ -754,10 +761,10 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             }
             __syncthreads();
         }
-        if (p.final_state) {
+        if (p.state_out) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
-                *reinterpret_cast<f32x4 *>(p.final_state + srow + 16 * kb) = St[kb];
+                *reinterpret_cast<f32x4 *>(p.state_out + srow + 16 * kb) = St[kb];
         }
         return;
     }
@@ -817,41 +824,45 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     }
 }
 
+template <int DK, int C, bool KDA, typename IT>
+hipError_t launch_prep(const PrefillArgs &a, int j0, int seg_chunks, char *rec, long record_chunks, hipStream_t st) {
+    if (record_chunks <= 0) return hipSuccess;
+    PrepKArgs pk;
+    pk.T = a.seqlen;
+    pk.H = a.num_heads;
+    pk.num_seqs = a.num_seqs;
+    pk.j0 = j0;
+    pk.seg_chunks = seg_chunks;
+    pk.scale = a.scale;
+    pk.q = a.q; pk.k = a.k;
+    pk.beta = a.beta; pk.log_alpha = a.log_alpha;
+    pk.cu = a.cu_seqlens;
+    pk.choff = a.chunk_offset;
+    pk.rec = rec;
+    hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT>), dim3((unsigned)(record_chunks * a.num_heads)), dim3(256), 0, st,
+                       pk);
+    return hipGetLastError();
+}
+
 template <int DK, int DVS, int C, bool KDA, typename IT>
-hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
+hipError_t launch_chain(const PrefillArgs &a, int j0, int seg_chunks, const char *rec, const float *state_in,
+                        float *state_out, hipStream_t st) {
     constexpr int threads = 64 * (kLoaderWaves + DVS / 16);
-    const int ncps = (a.seqlen + C - 1) / C;
-    if (a.record_chunks > 0) {
-        PrepKArgs pk;
-        pk.T = a.seqlen;
-        pk.H = a.num_heads;
-        pk.num_seqs = a.num_seqs;
-        pk.ncps = ncps;
-        pk.scale = a.scale;
-        pk.q = a.q; pk.k = a.k;
-        pk.beta = a.beta; pk.log_alpha = a.log_alpha;
-        pk.cu = a.cu_seqlens;
-        pk.choff = a.chunk_offset;
-        pk.rec = a.records;
-        const long grid = a.record_chunks * a.num_heads;
-        hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT>), dim3((unsigned)grid), dim3(256), 0, st, pk);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     ChainKArgs p;
     p.T = a.seqlen;
     p.H = a.num_heads;
     p.DV = a.dv;
     p.num_seqs = a.num_seqs;
-    p.ncps = ncps;
+    p.j0 = j0;
+    p.seg_chunks = seg_chunks;
     p.v = a.v;
-    p.initial_state = a.initial_state;
+    p.state_in = state_in;
     p.cu = a.cu_seqlens;
     p.order = a.cu_seqlens ? a.order : nullptr;
     p.choff = a.chunk_offset;
-    p.rec = a.records;
+    p.rec = rec;
     p.out = a.out;
-    p.final_state = a.final_state;
+    p.state_out = state_out;
     const long units = (long)a.num_seqs * a.num_heads;
     const long grid = ((units + 7) / 8) * 8 * (a.dv / DVS);
     if (a.out_bf16)
@@ -859,6 +870,33 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
     else
         hipLaunchKernelGGL((chain_kernel<DK, DVS, C, KDA, IT, false>), dim3((unsigned)grid), dim3(threads), 0, st, p);
     return hipGetLastError();
+}
+
+// One segment (the default): every record, then every chain.  When the
+// caller's workspace holds fewer records, dense batches run in segments of
+// chunks: records of one segment at a time, the state carried between
+// segments in the workspace.  (Running a segment's records on a second stream
+// beside the previous segment's chains was measured slower: the two kernels
+// then compete for HBM and evict each other's records from L2.)
+template <int DK, int DVS, int C, bool KDA, typename IT>
+hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
+    const int ncps = (a.seqlen + C - 1) / C;
+    if (a.num_segments <= 1) {
+        hipError_t e = launch_prep<DK, C, KDA, IT>(a, 0, ncps, a.records, a.record_chunks, st);
+        if (e != hipSuccess) return e;
+        return launch_chain<DK, DVS, C, KDA, IT>(a, 0, ncps, a.records, a.initial_state, a.final_state, st);
+    }
+    const int S = a.segment_chunks;
+    for (int sgi = 0; sgi < a.num_segments; ++sgi) {
+        const int j0 = sgi * S, cnt = min(S, ncps - j0);
+        hipError_t e = launch_prep<DK, C, KDA, IT>(a, j0, cnt, a.records, (long)a.batch * cnt, st);
+        if (e != hipSuccess) return e;
+        const bool last = sgi == a.num_segments - 1;
+        e = launch_chain<DK, DVS, C, KDA, IT>(a, j0, cnt, a.records, sgi == 0 ? a.initial_state : a.carry,
+                                             last ? a.final_state : a.carry, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gdr

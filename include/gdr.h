@@ -98,11 +98,16 @@ typedef struct gdr_prefill_shape {
  *    per-call sequence schedule, 2 x 4 x (num_seqs + 1) bytes, rounded up;
  *  - one record per chunk slot and head holding that chunk's state-independent
  *    operands (decayed keys and queries, the transposed end-of-chunk keys, the
- *    UT-transform inverse and the intra-chunk query-key matrix):
- *    (num_heads x chunk slots) x R bytes, where the chunk slots are
- *    batch x ceil(seqlen / C) (dense) or ceil(seqlen / C) + num_seqs (packed)
- *    and R is (3 C d_k + 2 C^2) x (2 for bf16 q/k/v, 4 for fp32) bytes plus
- *    the chunk's decay (4 d_k or 16 bytes), rounded up to 256.
+ *    UT-transform inverse and the intra-chunk query-key matrix), R bytes each:
+ *    (3 C d_k + 2 C^2) x (2 for bf16 q/k/v, 4 for fp32) plus the chunk's decay
+ *    (4 d_k or 16 bytes), rounded up to 256.  Chunk slots: ceil(seqlen / C) +
+ *    num_seqs (packed) or batch x ceil(seqlen / C) (dense).
+ * This is the size for one pass over all chunks, the fastest schedule.  A
+ * dense batch also accepts a smaller workspace: the prefill then runs in
+ * segments of S >= 16 chunks (the largest S that fits), needing
+ * batch x S x num_heads x R bytes of records plus the state carried between
+ * segments (num_seqs x num_heads x head_dim_v x head_dim_k x 4 bytes), each
+ * part rounded up to 256 bytes.
  * gate, qkv_dtype and chunk_size are the values that will be passed to
  * gdr_prefill_chunked (chunk_size 0 = automatic).  Returns 0 for a NULL shape
  * or an invalid argument.
@@ -150,7 +155,8 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  * summed over one chunk must stay above about -170 in every channel (the
  * chunk's operands are scaled around its midpoint in fp32 range).
  * Work: one kernel computes every chunk's record into the workspace, a second
- * walks each sequence's chunks in order; both are enqueued on hip_stream.
+ * walks each sequence's chunks in order (per segment, when the workspace is
+ * smaller than gdr_prefill_workspace_bytes reports); all on hip_stream.
  * Returns GDR_SUCCESS or an error status (nothing enqueued on error).
  */
 gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate,

@@ -129,6 +129,10 @@ def test_prefill_workspace_size():
     assert f(ctypes.byref(sh), 0, 1, 0, 0) == 32 * 4 * rec_gdn_bf16          # automatic chunk = 32
     assert f(ctypes.byref(sh), 0, 1, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_bf16
     assert f(ctypes.byref(sh), 1, 0, 16, 0) == 63 * 4 * rec_kda_f32
+    # one pass over every chunk, whatever the length
+    sh = gdr.PrefillShape(2, 32768, 4, 128, 64, 2)
+    rec_kda_bf16 = -(-(128 * 4 + (3 * 32 * 128 + 2 * 32 * 32) * 2) // 256) * 256
+    assert f(ctypes.byref(sh), 1, 1, 32, 0) == 2 * 1024 * 4 * rec_kda_bf16
     assert f(None, 0, 1, 0, 1) == 0
     assert f(ctypes.byref(sh), 5, 1, 0, 0) == 0
     assert f(ctypes.byref(sh), 0, 1, 48, 0) == 0

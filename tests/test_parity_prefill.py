@@ -159,6 +159,34 @@ def test_prefill_packed_with_empty_and_ragged(gate):
     assert torch.equal(fin[1], inp["initial_state"][1]) and torch.equal(fin[5], inp["initial_state"][5])
 
 
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_segments(gate):
+    """A workspace smaller than the one-pass size: the dense batch runs in
+    segments (here 64 chunks, the last one partial) with the state carried
+    between them; outputs and states match the one-pass run bit for bit."""
+    T = 64 * 32 * 2 + 77                                   # 131 chunks -> segments 64, 64, 3
+    inp = _small(64, 64, 2, T, gate, torch.bfloat16, True, seed=61, B=2)
+    out, fin = _check_all(inp, f"one pass {gate}")
+    rec = -(-((64 * 4 if gate == "channel" else 16) + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
+    ws_bytes = 2 * 64 * 2 * rec + 2 * 2 * 64 * 64 * 4   # records of one 64-chunk segment + carried state
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    say("segments of 64 chunks; then in place; then without the final state")
+    o1, f1 = _gpu(inp, workspace=ws)
+    state = inp["initial_state"].clone()
+    o2, _ = gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                    initial_state=state, final_state=state, workspace=ws)
+    o3, f3 = gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                     initial_state=inp["initial_state"], output_final_state=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert f3 is None
+    for o in (o1, o2, o3):
+        assert torch.equal(o, out)
+    assert torch.equal(f1, fin) and torch.equal(state, fin)
+    with pytest.raises(gdr.GdrError, match="workspace"):
+        gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                workspace=ws[: 2 * 15 * 2 * rec])
+
+
 # ------------------------------------------------------- GPU properties ----
 def test_prefill_deterministic():
     inp = _small(128, 128, 2, 333, "channel", torch.bfloat16, True, seed=51)
