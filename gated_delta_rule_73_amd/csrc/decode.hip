@@ -21,16 +21,20 @@
 // instruction).  The two row dot products are finished with cross-lane sums
 // inside the row's lane group.  Rows are independent, so a thread keeps RB
 // rows in flight at once to cover HBM latency.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace gdr {
 
-template <int DK, bool KDA, typename QT, int RB>
+// EXACT: d_v is a multiple of the rows one pass covers, so no row index
+// needs a bounds check (measured ~5% faster at d = 128); OUTB: bf16 outputs.
+template <int DK, bool KDA, typename QT, int RB, bool EXACT, bool OUTB>
 __global__ __launch_bounds__(256) void decode_kernel(
     int H, int DV, const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ v,
     const float *__restrict__ beta, const float *__restrict__ log_alpha, float *__restrict__ state,
-    float scale, void *__restrict__ out, bool out_bf16) {
+    float scale, void *__restrict__ out) {
     constexpr int LPR = DK / 4;          // lanes per state row
     constexpr int RPP = 256 / LPR;       // rows covered by the workgroup per pass
     const int unit = blockIdx.x;         // n * H + h
@@ -53,8 +57,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
 
     float *S = state + (size_t)unit * DV * DK;
     const QT *vu = v + (size_t)unit * DV;
-    float *of = static_cast<float *>(out) + (size_t)unit * DV;
-    __bf16 *ob = static_cast<__bf16 *>(out) + (size_t)unit * DV;
+    using OT = typename std::conditional<OUTB, __bf16, float>::type;
+    OT *ou = static_cast<OT *>(out) + (size_t)unit * DV;
 
     for (int base = 0; base < DV; base += RPP * RB) {
         f32x4 s[RB];
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int i = base + r * RPP + rsub;
-            if (i < DV) {
+            if (EXACT || i < DV) {
                 s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)i * DK + c0));
                 vi[r] = to_f32(vu[i]);
             }
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
             const int i = base + r * RPP + rsub;
             // the group-sum below needs every lane of the row group; i < DV is
             // uniform over the group (all its lanes share rsub), so skipping is safe
-            if (i < DV) {
+            if (EXACT || i < DV) {
                 f32x4 t = s[r];
                 t[0] *= a.x; t[1] *= a.y; t[2] *= a.z; t[3] *= a.w;
                 float x = t[0] * kv.x + t[1] * kv.y + t[2] * kv.z + t[3] * kv.w;
@@ -82,11 +86,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
                 const float u = b * (vi[r] - x);
                 t[0] += u * kv.x; t[1] += u * kv.y; t[2] += u * kv.z; t[3] += u * kv.w;
                 __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(S + (size_t)i * DK + c0));
-                if (lane == 0) {
-                    const float o = scale * (y + u * kq);
-                    if (out_bf16) ob[i] = (__bf16)o;
-                    else of[i] = o;
-                }
+                if (lane == 0) ou[i] = (OT)(scale * (y + u * kq));
             }
         }
     }
@@ -98,9 +98,19 @@ static hipError_t launch_decode_t(const DecodeArgs &p, hipStream_t st) {
     constexpr int RPP = 256 / LPR;
     constexpr int RB = (RPP >= 64) ? 2 : (RPP >= 32 ? 4 : 8);
     const unsigned grid = (unsigned)((size_t)p.num_seqs * p.num_heads);
-    hipLaunchKernelGGL((decode_kernel<DK, KDA, QT, RB>), dim3(grid), dim3(256), 0, st, p.num_heads,
-                       p.dv, (const QT *)p.q, (const QT *)p.k, (const QT *)p.v, p.beta, p.log_alpha,
-                       p.state, p.scale, p.out, p.out_bf16);
+    const bool exact = p.dv % (RPP * RB) == 0;
+#define GDR_DECODE_LAUNCH(E, O)                                                                        \
+    hipLaunchKernelGGL((decode_kernel<DK, KDA, QT, RB, E, O>), dim3(grid), dim3(256), 0, st, p.num_heads, \
+                       p.dv, (const QT *)p.q, (const QT *)p.k, (const QT *)p.v, p.beta, p.log_alpha,     \
+                       p.state, p.scale, p.out)
+    if (exact) {
+        if (p.out_bf16) GDR_DECODE_LAUNCH(true, true);
+        else GDR_DECODE_LAUNCH(true, false);
+    } else {
+        if (p.out_bf16) GDR_DECODE_LAUNCH(false, true);
+        else GDR_DECODE_LAUNCH(false, false);
+    }
+#undef GDR_DECODE_LAUNCH
     return hipGetLastError();
 }
 
