@@ -48,6 +48,7 @@
 // state-side operands k e^g, q e^g, k e^{g_C-g} are all <= 1 in magnitude.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -236,6 +237,7 @@ struct PrepSmem {
 
 struct PrepKArgs {
     int T, H, num_seqs;
+    long num_records;            // chunk slots x heads in this launch
     int j0, seg_chunks;          // dense: chunks [j0, j0 + seg_chunks) of every sequence
     float scale;                 // readout factor, folded into Q e^g and M
     const void *q, *k;
@@ -244,9 +246,10 @@ struct PrepKArgs {
     char *rec;
 };
 
-// One workgroup (four waves) per (chunk, head): every chunk of every
-// sequence at once, so this kernel is bound by its HBM traffic, not by the
-// latency of its serial steps.
+// Every (chunk, head) record is independent, so this kernel is bound by its
+// HBM traffic, not by the latency of its serial steps: a few persistent
+// workgroups (four waves each) per CU walk the records, each holding the next
+// record's inputs in flight while it computes the current one.
 template <int DK, int C, bool KDA, typename IT>
 __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
     using SM = PrepSmem<DK, C, KDA, IT>;
@@ -267,57 +270,115 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
     static_assert(sizeof(Rec) == chunk_record_bytes(DK, C, KDA, sizeof(ST)), "record layout");
     static_assert(sizeof(SM) <= 64 * 1024, "LDS budget (several workgroups per CU)");
 
+    constexpr int KVPT = (C * DK / EPV + 255) / 256;        // 16-byte k (and q) vectors per thread
+    constexpr int GVPT = KDA ? (C * DK / 4 + 255) / 256 : 1;  // 16-byte log-decay vectors per thread
+
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int H = p.H;
-    const int h = blockIdx.x % H;
-    const int x = blockIdx.x / H;            // record chunk index
-    int n, j;
-    if (p.cu) {
-        if (x >= p.choff[p.num_seqs]) return;
-        int lo = 0, hi = p.num_seqs - 1;     // last n with choff[n] <= x
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.choff[mid] <= x) lo = mid;
-            else hi = mid - 1;
-        }
-        n = lo;
-        j = x - p.choff[n];
-    } else {
-        n = x / p.seg_chunks;
-        j = p.j0 + x % p.seg_chunks;
-    }
-    const int bos = p.cu ? p.cu[n] : n * p.T;
-    const int eos = p.cu ? p.cu[n + 1] : bos + p.T;
-    const int t0 = bos + j * C;
-    const int nv = min(C, eos - t0);
-    Rec &rec = *reinterpret_cast<Rec *>(p.rec + ((size_t)x * H + h) * chunk_record_stride(DK, C, KDA, sizeof(ST)));
     const IT *gq = static_cast<const IT *>(p.q);
     const IT *gk = static_cast<const IT *>(p.k);
+    constexpr size_t RS = chunk_record_stride(DK, C, KDA, sizeof(ST));
 
-    // ---- A: inputs to LDS (zeros past the sequence end)
-    for (int e = tid; e < C * DK / EPV; e += 256) {
-        const int t = e / (DK / EPV), c = (e % (DK / EPV)) * EPV;
-        IV kv{}, qv{};
-        if (t < nv) {
-            const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-            kv = *reinterpret_cast<const IV *>(gk + off);
-            qv = *reinterpret_cast<const IV *>(gq + off);
+    // record r = (chunk slot x, head h), r = x * H + h: its first token and
+    // its token count (0: no such chunk)
+    auto locate = [&](long r, int &h, int &t0, int &nv) {
+        h = (int)(r % H);
+        const int x = (int)(r / H);
+        nv = 0;
+        t0 = 0;
+        if (r >= p.num_records) return;
+        int n, j;
+        if (p.cu) {
+            if (x >= p.choff[p.num_seqs]) return;
+            int lo = 0, hi = p.num_seqs - 1;     // last n with choff[n] <= x
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (p.choff[mid] <= x) lo = mid;
+                else hi = mid - 1;
+            }
+            n = lo;
+            j = x - p.choff[n];
+        } else {
+            n = x / p.seg_chunks;
+            j = p.j0 + x % p.seg_chunks;
         }
-        *reinterpret_cast<IV *>(&sm.u.in.Ks[t][c]) = kv;
-        *reinterpret_cast<IV *>(&sm.u.in.Qs[t][c]) = qv;
+        const int bos = p.cu ? p.cu[n] : n * p.T;
+        const int eos = p.cu ? p.cu[n + 1] : bos + p.T;
+        t0 = bos + j * C;
+        nv = min(C, eos - t0);
+    };
+    // the raw inputs of one record, held in registers while the previous
+    // record is processed (zeros past the sequence end)
+    IV kr[KVPT], qr[KVPT];
+    f32x4 gr[GVPT];
+    float br = 0.f, gs = 0.f;
+    auto fetch = [&](long r) {
+        int h, t0, nv;
+        locate(r, h, t0, nv);
+#pragma unroll
+        for (int x = 0; x < KVPT; ++x) {
+            const int e = tid + 256 * x;
+            const int t = e / (DK / EPV), c = (e % (DK / EPV)) * EPV;
+            kr[x] = IV{};
+            qr[x] = IV{};
+            if (e < C * DK / EPV && t < nv) {
+                const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
+                kr[x] = *reinterpret_cast<const IV *>(gk + off);
+                qr[x] = *reinterpret_cast<const IV *>(gq + off);
+            }
+        }
+        if constexpr (KDA) {
+#pragma unroll
+            for (int x = 0; x < GVPT; ++x) {
+                const int e = tid + 256 * x;
+                const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
+                gr[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (e < C * DK / 4 && t < nv)
+                    gr[x] = *reinterpret_cast<const f32x4 *>(p.log_alpha + ((size_t)(t0 + t) * H + h) * DK + c);
+            }
+        } else {
+            gs = tid < nv ? p.log_alpha[(size_t)(t0 + tid) * H + h] : 0.f;
+        }
+        br = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    };
+
+    // persistent workgroups: records blockIdx.x, + gridDim.x, ...; the next
+    // record's inputs are requested as soon as this one's reach LDS
+    long r = blockIdx.x;
+    fetch(r);
+    for (; r < p.num_records; r += gridDim.x) {
+    int h, t0, nv;
+    locate(r, h, t0, nv);
+    if (nv == 0) {                           // uniform: a chunk slot past the last sequence's end
+        fetch(r + gridDim.x);
+        continue;
+    }
+    Rec &rec = *reinterpret_cast<Rec *>(p.rec + (size_t)r * RS);
+
+    // ---- A: inputs to LDS
+#pragma unroll
+    for (int x = 0; x < KVPT; ++x) {
+        const int e = tid + 256 * x;
+        if (e < C * DK / EPV) {
+            const int t = e / (DK / EPV), c = (e % (DK / EPV)) * EPV;
+            *reinterpret_cast<IV *>(&sm.u.in.Ks[t][c]) = kr[x];
+            *reinterpret_cast<IV *>(&sm.u.in.Qs[t][c]) = qr[x];
+        }
     }
     if constexpr (KDA) {
-        for (int e = tid; e < C * DK / 4; e += 256) {
-            const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
-            f32x4 gv{0.f, 0.f, 0.f, 0.f};
-            if (t < nv) gv = *reinterpret_cast<const f32x4 *>(p.log_alpha + ((size_t)(t0 + t) * H + h) * DK + c);
-            *reinterpret_cast<f32x4 *>(&sm.u.in.G[t][c]) = gv;
+#pragma unroll
+        for (int x = 0; x < GVPT; ++x) {
+            const int e = tid + 256 * x;
+            if (e < C * DK / 4) {
+                const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
+                *reinterpret_cast<f32x4 *>(&sm.u.in.G[t][c]) = gr[x];
+            }
         }
     } else if (wave == 0) {
-        float g = lane < nv && lane < C ? p.log_alpha[(size_t)(t0 + lane) * H + h] : 0.f;
+        float g = gs;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(g, off);
@@ -331,7 +392,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
         }
         if (lane < 4) rec.dec[lane] = lane == 0 ? __expf(gC) : 0.f;
     }
-    if (tid < C) sm.beta[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    if (tid < C) sm.beta[tid] = br;
+    fetch(r + gridDim.x);
     __syncthreads();
 
     // ---- B: per-channel prefix sums (KDA) and K_end^T, one key channel per
@@ -555,6 +617,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
         }
         store_vec<ST, 4>(&rec.Tm[R][c0], tv);
     }
+    __syncthreads();   // the next record's inputs overwrite this one's scratch
+    }
 }
 
 // ============================ chain kernel ===================================
@@ -672,7 +736,9 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             if (p.state_in) St[kb] = *reinterpret_cast<const f32x4 *>(p.state_in + srow + 16 * kb);
         }
         using OT = typename std::conditional<OUTB, __bf16, float>::type;
-        // outputs of chunk jc: a uniform row base plus 32-bit lane offsets
+        // outputs of chunk jc: a uniform row base plus 32-bit lane offsets;
+        // streamed with non-temporal stores so they do not push the records
+        // the value slices share out of L2
         const int HDV = H * DV;
         const int oofs = 4 * lg * HDV + lr;
         __syncthreads();
@@ -736,11 +802,12 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
                 if constexpr (SPLIT) o = ul.mma(o, ma[rb], ns);
                 if (nv == C) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ob[oofs + (16 * rb + i) * HDV] = (OT)o[i];
+                    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store((OT)o[i], &ob[oofs + (16 * rb + i) * HDV]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (16 * rb + 4 * lg + i < nv) ob[oofs + (16 * rb + i) * HDV] = (OT)o[i];
+                        if (16 * rb + 4 * lg + i < nv)
+                            __builtin_nontemporal_store((OT)o[i], &ob[oofs + (16 * rb + i) * HDV]);
                 }
             }
 #pragma unroll
@@ -839,8 +906,18 @@ hipError_t launch_prep(const PrefillArgs &a, int j0, int seg_chunks, char *rec, 
     pk.cu = a.cu_seqlens;
     pk.choff = a.chunk_offset;
     pk.rec = rec;
-    hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT>), dim3((unsigned)(record_chunks * a.num_heads)), dim3(256), 0, st,
-                       pk);
+    pk.num_records = record_chunks * a.num_heads;
+    static int resident = 0;   // workgroups of this kernel that fit on the device at once
+    if (!resident) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep_kernel<DK, C, KDA, IT>, 256, 0);
+        if (e != hipSuccess) return e;
+        resident = std::max(1, cus * per_cu);
+    }
+    const long grid = std::min<long>(pk.num_records, resident);
+    hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT>), dim3((unsigned)grid), dim3(256), 0, st, pk);
     return hipGetLastError();
 }
 
