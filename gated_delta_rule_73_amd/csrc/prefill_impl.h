@@ -850,32 +850,39 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     const int vt = tid / (DVS / EPV), vc = (tid % (DVS / EPV)) * EPV;
     i32x4 rg[DEPTH][PPT];
     IV vr[DEPTH];
-    auto issue = [&](i32x4 (&r)[PPT], IV &v, int c) {
-        if (c >= nchunks) return;
-        const char *src = rec0 + (size_t)c * H * RS;
+    // Every chunk issues the same loads, unconditionally (chunks past the end
+    // reload the last one, pieces past the record reload its last piece, value
+    // rows past the sequence are zeroed after the load): with no branch around
+    // a load the compiler counts outstanding loads exactly and waits only for
+    // the set it needs, keeping DEPTH chunks in flight.
+    const int vrow = tid < VV ? vt : 0;
+    bool vok[DEPTH];   // value row inside the sequence (applied when written to LDS)
+    auto issue = [&](i32x4 (&r)[PPT], IV &v, bool &ok, int c) {
+        const int cc = min(c, nchunks - 1);
+        const char *src = rec0 + (size_t)cc * H * RS;
 #pragma unroll
         for (int x = 0; x < PPT; ++x)
-            if (lofs[x] >= 0) r[x] = *reinterpret_cast<const i32x4 *>(src + 16 * (tid + 64 * NLW * x));
-        v = IV{};
-        if (tid < VV) {
-            const int t = c * C + vt;
-            if (bos + t < eos) v = *reinterpret_cast<const IV *>(gv + ((size_t)(bos + t) * H + h) * DV + v0 + vc);
-        }
+            r[x] = *reinterpret_cast<const i32x4 *>(src + 16 * min(tid + 64 * NLW * x, NPIECE - 1));
+        const int t = bos + cc * C + vrow;
+        v = *reinterpret_cast<const IV *>(gv + ((size_t)min(t, eos - 1) * H + h) * DV + v0 + vc);
+        ok = t < eos;
     };
-    auto commit = [&](const i32x4 (&r)[PPT], const IV &v, Slot &s) {
+    auto commit = [&](const i32x4 (&r)[PPT], const IV &v, bool ok, Slot &s) {
         char *base = reinterpret_cast<char *>(&s);
 #pragma unroll
         for (int x = 0; x < PPT; ++x)
             if (lofs[x] >= 0) *reinterpret_cast<i32x4 *>(base + lofs[x]) = r[x];
         if (tid < VV) {
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) s.Vt[vc + e][vt] = v[e];
+            for (int e = 0; e < EPV; ++e) s.Vt[vc + e][vt] = ok ? v[e] : IT(0.f);
         }
     };
+    if (nchunks > 0) {
 #pragma unroll
-    for (int c = 0; c < DEPTH; ++c) issue(rg[c], vr[c], c);
-    if (nchunks > 0) commit(rg[0], vr[0], slot[0]);
-    issue(rg[0], vr[0], DEPTH);
+        for (int c = 0; c < DEPTH; ++c) issue(rg[c], vr[c], vok[c], c);
+        commit(rg[0], vr[0], vok[0], slot[0]);
+        issue(rg[0], vr[0], vok[0], DEPTH);
+    }
     __syncthreads();
     for (int jb = 0; jb < nchunks; jb += DEPTH) {
 #pragma unroll
@@ -883,8 +890,8 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             const int jc = jb + u;
             if (jc < nchunks) {
                 const int s = (u + 1) % DEPTH;   // holds chunk jc + 1
-                if (jc + 1 < nchunks) commit(rg[s], vr[s], slot[(jc + 1) & 1]);
-                issue(rg[s], vr[s], jc + 1 + DEPTH);
+                if (jc + 1 < nchunks) commit(rg[s], vr[s], vok[s], slot[(jc + 1) & 1]);
+                issue(rg[s], vr[s], vok[s], jc + 1 + DEPTH);
                 __syncthreads();
             }
         }
