@@ -102,12 +102,18 @@ template <int NBLK> struct RegB<_Float16, NBLK> {
                 lo.f[s][4 + i] = (_Float16)(x1 - h1);
             }
     }
+    static constexpr int STEPS = NBLK / 2;   // 32-wide k-steps
+    // acc += A * B over k-step s only
+    template <class RA>
+    __device__ __forceinline__ f32x4 step(f32x4 acc, const RA &a, int s) const {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.f[s], f[s], acc, 0, 0, 0);
+    }
     // acc += A * B, A given as preloaded fragments (RowA) of the same k-range
     template <class RA>
     __device__ __forceinline__ f32x4 mma(f32x4 acc, const RA &a, int nsteps = 1 << 20) const {
 #pragma unroll
-        for (int s = 0; s < NBLK / 2; ++s)
-            if (s < nsteps) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.f[s], f[s], acc, 0, 0, 0);
+        for (int s = 0; s < STEPS; ++s)
+            if (s < nsteps) acc = step(acc, a, s);
         return acc;
     }
 };
@@ -122,33 +128,47 @@ template <int NBLK> struct RegB<float, NBLK> {
         set(v);
         (void)lo;
     }
-    // nsteps counts 32-wide k-steps (two 16-blocks), as for fp16 operands
+    // k-steps are 32 wide (two 16-blocks), as for fp16 operands; a 16-row
+    // chunk (NBLK = 1) has one half step
+    static constexpr int STEPS = (NBLK + 1) / 2;
+    template <class RA>
+    __device__ __forceinline__ f32x4 step(f32x4 acc, const RA &a, int s) const {
+#pragma unroll
+        for (int b = 2 * s; b < 2 * s + 2 && b < NBLK; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[b][i], f[b][i], acc, 0, 0, 0);
+        return acc;
+    }
     template <class RA>
     __device__ __forceinline__ f32x4 mma(f32x4 acc, const RA &a, int nsteps = 1 << 20) const {
-        const int nblk = nsteps < NBLK ? 2 * nsteps : NBLK;
 #pragma unroll
-        for (int b = 0; b < NBLK; ++b)
-            if (b < nblk)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[b][i], f[b][i], acc, 0, 0, 0);
+        for (int s = 0; s < STEPS; ++s)
+            if (s < nsteps) acc = step(acc, a, s);
         return acc;
     }
 };
 
+// Stored k-order of the A operands.  An fp16 k-step gives lane group lg the
+// k-indices {4lg+i, 16+4lg+i} (i < 4) of its 32; the record stores each
+// 32-wide k-block with those eight adjacent (position 8lg + 4h + i holds
+// k = 16h + 4lg + i), so one 16-byte LDS read fetches a lane's operand.  The
+// map keeps aligned groups of four together.  fp32 steps (16 wide, four
+// adjacent k per lane) are stored in plain order.
+template <typename ST> __host__ __device__ constexpr int kpos(int k) {
+    if constexpr (sizeof(ST) == 2) return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+    else return k;
+}
+
 // A-operand fragments of one 16-row tile read from LDS at the k-indices a
-// RegB of the same NBLK supplies (lane row = lr, k = 16*blk + 4*lg + i).
+// RegB of the same NBLK supplies (lane row = lr, k = 16*blk + 4*lg + i), the
+// row stored in kpos order.
 template <typename ST, int NBLK> struct RowA;
 template <int NBLK> struct RowA<_Float16, NBLK> {
     f16x8 f[NBLK / 2];
     __device__ __forceinline__ void load(const _Float16 *arow, int lg, int nsteps = 1 << 20) {
 #pragma unroll
-        for (int s = 0; s < NBLK / 2; ++s) {
-            if (s < nsteps) {
-                const f16x4 a0 = *reinterpret_cast<const f16x4 *>(arow + 32 * s + 4 * lg);
-                const f16x4 a1 = *reinterpret_cast<const f16x4 *>(arow + 32 * s + 16 + 4 * lg);
-                f[s] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-        }
+        for (int s = 0; s < NBLK / 2; ++s)
+            if (s < nsteps) f[s] = *reinterpret_cast<const f16x8 *>(arow + 32 * s + 8 * lg);
     }
 };
 template <int NBLK> struct RowA<float, NBLK> {
@@ -201,7 +221,8 @@ __device__ __forceinline__ void store_vec(ST *dst, const ST (&v)[N]) {
     *reinterpret_cast<typename VecT<ST, N>::type *>(dst) = x;
 }
 
-// ---- per-chunk record (workspace, unpadded rows) ---------------------------
+// ---- per-chunk record (workspace, unpadded rows; the k-index of the A
+// operands Kt, Qt (key channel), KeT, Tm, Mm (token) stored in kpos order) ----
 template <int DK, int C, bool KDA, typename IT>
 struct ChunkRec {
     using ST = typename Prec<IT>::ST;
@@ -269,6 +290,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
     static_assert(SEGL >= 1 && C <= 64, "prefix-sum thread mapping");
     static_assert(sizeof(Rec) == chunk_record_bytes(DK, C, KDA, sizeof(ST)), "record layout");
     static_assert(sizeof(SM) <= 64 * 1024, "LDS budget (several workgroups per CU)");
+    static_assert(sizeof(ST) == 4 || (C % 32 == 0 && DK % 32 == 0), "fp16 operands are stored in 32-wide k-blocks");
 
     constexpr int KVPT = (C * DK / EPV + 255) / 256;        // 16-byte k (and q) vectors per thread
     constexpr int GVPT = KDA ? (C * DK / 4 + 255) / 256 : 1;  // 16-byte log-decay vectors per thread
@@ -439,11 +461,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
 #pragma unroll
             for (int s = 0; s < SEGL; s += 4) {
                 const ST v4[4] = {(ST)ke[s], (ST)ke[s + 1], (ST)ke[s + 2], (ST)ke[s + 3]};
-                store_vec<ST, 4>(&rec.KeT[gc][gseg * SEGL + s], v4);
+                store_vec<ST, 4>(&rec.KeT[gc][kpos<ST>(gseg * SEGL + s)], v4);
             }
         } else {
 #pragma unroll
-            for (int s = 0; s < SEGL; ++s) rec.KeT[gc][gseg * SEGL + s] = (ST)ke[s];
+            for (int s = 0; s < SEGL; ++s) rec.KeT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)ke[s];
         }
     }
     __syncthreads();
@@ -500,8 +522,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                     }
                 }
                 if (valid) {
-                    store_vec<ST, 4>(&rec.Kt[t][ch], kt);
-                    store_vec<ST, 4>(&rec.Qt[t][ch], qt);
+                    store_vec<ST, 4>(&rec.Kt[t][kpos<ST>(ch)], kt);
+                    store_vec<ST, 4>(&rec.Qt[t][kpos<ST>(ch)], qt);
                 }
             }
         }
@@ -560,7 +582,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
             sm.Af[R][c] = fa;
             mv[i] = (ST)(fm * p.scale);
         }
-        store_vec<ST, 4>(&rec.Mm[R][c0], mv);
+        store_vec<ST, 4>(&rec.Mm[R][kpos<ST>(c0)], mv);
     }
     __syncthreads();
     // diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution, one
@@ -615,7 +637,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
             const int c = c0 + i;
             tv[i] = (ST)(c <= R ? sm.Tf[R][c] * sm.beta[c] : 0.f);
         }
-        store_vec<ST, 4>(&rec.Tm[R][c0], tv);
+        store_vec<ST, 4>(&rec.Tm[R][kpos<ST>(c0)], tv);
     }
     __syncthreads();   // the next record's inputs overwrite this one's scratch
     }
@@ -693,6 +715,8 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     static_assert(VV <= 64 * NLW, "one value vector per loader lane");
     static_assert(2 * sizeof(Slot) <= 160 * 1024, "LDS budget");
     static_assert(NB <= 2, "T and M rows span at most one 32-wide k-step");
+    // 32-wide k-steps of the lower-triangular T and M rows of row block rb
+    auto tri_steps = [](int rb) { return (16 * rb + 16 + 31) / 32; };
 
     __shared__ Slot slot[2];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -747,7 +771,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             const int t0 = bos + jc * C;
             const int nv = min(C, eos - t0);
             OT *ob = static_cast<OT *>(p.out) + ((size_t)t0 * H + h) * DV + v0 + 16 * cb;
-            // every LDS operand of the chunk, read up front
+            // every LDS operand of the chunk, issued up front in the order of use
             RowA<ST, NKB> ka[NB], qa[NB];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
@@ -762,69 +786,102 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
 #pragma unroll
                 for (int i = 0; i < 4; ++i) vv[rb][i] = (float)x[i];
             }
+            f32x4 dk[KDA ? NKB : 1];
+            if constexpr (KDA) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) dk[kb] = *reinterpret_cast<const f32x4 *>(&bc.dec[16 * kb + 4 * lg]);
+            } else {
+                const float d = bc.dec[0];
+                dk[0] = f32x4{d, d, d, d};
+            }
+            RowA<ST, NB> ta[NB], ma[NB], kea[NKB];
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                ta[rb].load(&bc.Tm[16 * rb + lr][0], lg, tri_steps(rb));
+                ma[rb].load(&bc.Mm[16 * rb + lr][0], lg, tri_steps(rb));
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kea[kb].load(&bc.KeT[16 * kb + lr][0], lg);
+
             RegB<ST, NKB> sop;
             sop.set(St);
+            // the decayed state S0 Diag(e^{g_C}), formed while the products run
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) St[kb][i] *= dk[KDA ? kb : 0][i];
+            // X = (K e^g) S0^T and Y = (Q e^g) S0^T: 2 NB independent
+            // accumulations, interleaved k-step by k-step
             f32x4 X[NB], Y[NB], W[NB];
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                X[rb] = sop.mma(f32x4{0.f, 0.f, 0.f, 0.f}, ka[rb]);
-                Y[rb] = sop.mma(f32x4{0.f, 0.f, 0.f, 0.f}, qa[rb]);
-            }
-            RowA<ST, NB> ta[NB], ma[NB];
+            for (int rb = 0; rb < NB; ++rb) X[rb] = Y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                const int ns = (16 * rb + 16 + 31) / 32;   // T and M are lower triangular
-                ta[rb].load(&bc.Tm[16 * rb + lr][0], lg, ns);
-                ma[rb].load(&bc.Mm[16 * rb + lr][0], lg, ns);
-            }
+            for (int st = 0; st < RegB<ST, NKB>::STEPS; ++st)
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    X[rb] = sop.step(X[rb], ka[rb], st);
+                    Y[rb] = sop.step(Y[rb], qa[rb], st);
+                }
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) W[rb][i] = vv[rb][i] - X[rb][i];
             RegB<ST, NB> wh, wl;
             wh.set_split(W, wl);
+            // U = T diag(b) (V - X): hi products of every row block, then lo
             f32x4 U[NB];
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                const int ns = (16 * rb + 16 + 31) / 32;
-                U[rb] = wh.mma(f32x4{0.f, 0.f, 0.f, 0.f}, ta[rb], ns);
-                if constexpr (SPLIT) U[rb] = wl.mma(U[rb], ta[rb], ns);
-            }
-            RowA<ST, NB> kea[NKB];
+            for (int rb = 0; rb < NB; ++rb) U[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kea[kb].load(&bc.KeT[16 * kb + lr][0], lg);
+            for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb)
+                    if (st < tri_steps(rb)) U[rb] = wh.step(U[rb], ta[rb], st);
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb)
+                        if (st < tri_steps(rb)) U[rb] = wl.step(U[rb], ta[rb], st);
+            }
             RegB<ST, NB> uh, ul;
             uh.set_split(U, ul);
+            // S^T <- Diag(e^{g_C}) S0^T + K_end^T U: hi products of every key
+            // block, then lo
+#pragma unroll
+            for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) St[kb] = uh.step(St[kb], kea[kb], st);
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) St[kb] = ul.step(St[kb], kea[kb], st);
+            }
+            // O = Y + M U
+#pragma unroll
+            for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb)
+                    if (st < tri_steps(rb)) Y[rb] = uh.step(Y[rb], ma[rb], st);
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb)
+                        if (st < tri_steps(rb)) Y[rb] = ul.step(Y[rb], ma[rb], st);
+            }
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                const int ns = (16 * rb + 16 + 31) / 32;
-                f32x4 o = uh.mma(Y[rb], ma[rb], ns);
-                if constexpr (SPLIT) o = ul.mma(o, ma[rb], ns);
                 if (nv == C) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store((OT)o[i], &ob[oofs + (16 * rb + i) * HDV]);
+                    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store((OT)Y[rb][i], &ob[oofs + (16 * rb + i) * HDV]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (16 * rb + 4 * lg + i < nv)
-                            __builtin_nontemporal_store((OT)o[i], &ob[oofs + (16 * rb + i) * HDV]);
+                            __builtin_nontemporal_store((OT)Y[rb][i], &ob[oofs + (16 * rb + i) * HDV]);
                 }
-            }
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                f32x4 acc = St[kb];
-                if constexpr (KDA) {
-                    const f32x4 d = *reinterpret_cast<const f32x4 *>(&bc.dec[16 * kb + 4 * lg]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] *= d[i];
-                } else {
-                    const float d = bc.dec[0];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] *= d;
-                }
-                acc = uh.mma(acc, kea[kb]);
-                if constexpr (SPLIT) acc = ul.mma(acc, kea[kb]);
-                St[kb] = acc;
             }
             __syncthreads();
         }
