@@ -221,13 +221,24 @@ __device__ __forceinline__ void store_vec(ST *dst, const ST (&v)[N]) {
     *reinterpret_cast<typename VecT<ST, N>::type *>(dst) = x;
 }
 
+// ---- buffer stores ----------------------------------------------------------
+// Fourth descriptor word of a raw (unstructured) buffer on CDNA.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCachePolicyNT = 2;   // non-temporal
+__device__ __forceinline__ void buffer_store_nt(__amdgpu_buffer_rsrc_t r, int byte_ofs, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_ofs, 0, kCachePolicyNT);
+}
+__device__ __forceinline__ void buffer_store_nt(__amdgpu_buffer_rsrc_t r, int byte_ofs, __bf16 v) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, byte_ofs, 0, kCachePolicyNT);
+}
+
 // ---- per-chunk record (workspace, unpadded rows; the k-index of the A
-// operands Kt, Qt (key channel), KeT, Tm, Mm (token) stored in kpos order) ----
+// operands Kn, Qt (key channel), KeT, Tm, Mm (token) stored in kpos order) ----
 template <int DK, int C, bool KDA, typename IT>
 struct ChunkRec {
     using ST = typename Prec<IT>::ST;
     float dec[KDA ? DK : 4];   // e^{g_C}: per key channel (KDA) or dec[0] (GDN)
-    ST Kt[C][DK];              // k e^g
+    ST Kn[C][DK];              // -k e^g (negated: V - X accumulates from V)
     ST Qt[C][DK];              // q e^g
     ST KeT[DK][C];             // (k e^{g_C - g})^T
     ST Tm[C][C];               // T diag(b), zero above the diagonal
@@ -506,7 +517,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                         fr[rb][4 * hh + i] = rh;
                         fql[rb][4 * hh + i] = (FT)(lq - (float)qh);
                         frl[rb][4 * hh + i] = (FT)(rk - (float)rh);
-                        kt[i] = (ST)(lk * emv[i]);
+                        kt[i] = (ST)(-lk * emv[i]);
                         qt[i] = (ST)(lq * emv[i] * p.scale);
                     }
                 } else {
@@ -517,12 +528,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                     for (int i = 0; i < 4; ++i) {
                         fk[rb][4 * hh + i] = (ST)kf[i];
                         fq[rb][4 * hh + i] = (ST)qf[i];
-                        kt[i] = (ST)(kf[i] * e);
+                        kt[i] = (ST)(-kf[i] * e);
                         qt[i] = (ST)(qf[i] * e * p.scale);
                     }
                 }
                 if (valid) {
-                    store_vec<ST, 4>(&rec.Kt[t][kpos<ST>(ch)], kt);
+                    store_vec<ST, 4>(&rec.Kn[t][kpos<ST>(ch)], kt);
                     store_vec<ST, 4>(&rec.Qt[t][kpos<ST>(ch)], qt);
                 }
             }
@@ -644,15 +655,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
 }
 
 // ============================ chain kernel ===================================
+// LDS row pitch for rows read as MFMA A fragments (lane: row l & 15, 16
+// bytes at column group l >> 4).  A wave's 16-byte reads are served 32 lanes
+// at a time from 128 four-byte banks, i.e. 16 rows x 32 contiguous bytes per
+// half wave; those meet every bank once exactly when the pitch is an odd
+// multiple of 32 bytes (measured with the LDS bank-conflict counter on gfx950).
+constexpr int lds_pitch(int bytes) { return bytes + ((32 - bytes % 64) + 64) % 64; }
+
 template <int DK, int DVS, int C, bool KDA, typename IT>
 struct alignas(16) ChainSlot {
     using ST = typename Prec<IT>::ST;
-    static constexpr int PAD = 16 / sizeof(ST);   // 16-byte row padding spreads LDS banks
-    static constexpr int LDK = DK + PAD;
-    static constexpr int LDC = C + PAD;
-    static constexpr int LDVT = C + 16 / sizeof(IT);
+    static constexpr int LDK = lds_pitch(DK * (int)sizeof(ST)) / (int)sizeof(ST);
+    static constexpr int LDC = lds_pitch(C * (int)sizeof(ST)) / (int)sizeof(ST);
+    static constexpr int LDVT = lds_pitch(C * (int)sizeof(IT)) / (int)sizeof(IT);
     float dec[KDA ? DK : 4];
-    ST Kt[C][LDK];
+    ST Kn[C][LDK];
     ST Qt[C][LDK];
     ST KeT[DK][LDC];
     ST Tm[C][LDC];
@@ -671,7 +688,7 @@ __device__ __forceinline__ int slot_offset(int p) {
     constexpr int BK = Slot::LDK * (int)sizeof(ST), BC = Slot::LDC * (int)sizeof(ST);
     if (p < PD) return (int)__builtin_offsetof(Slot, dec) + 16 * p;
     p -= PD;
-    if (p < C * RK) return (int)__builtin_offsetof(Slot, Kt) + (p / RK) * BK + (p % RK) * 16;
+    if (p < C * RK) return (int)__builtin_offsetof(Slot, Kn) + (p / RK) * BK + (p % RK) * 16;
     p -= C * RK;
     if (p < C * RK) return (int)__builtin_offsetof(Slot, Qt) + (p / RK) * BK + (p % RK) * 16;
     p -= C * RK;
@@ -760,22 +777,31 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             if (p.state_in) St[kb] = *reinterpret_cast<const f32x4 *>(p.state_in + srow + 16 * kb);
         }
         using OT = typename std::conditional<OUTB, __bf16, float>::type;
-        // outputs of chunk jc: a uniform row base plus 32-bit lane offsets;
-        // streamed with non-temporal stores so they do not push the records
-        // the value slices share out of L2
+        // outputs of a chunk: buffer stores from the chunk's first output
+        // element (a uniform base) at fixed per-lane byte offsets (row
+        // 16 rb + 4 lg + i, column lr); the buffer's size ends after the
+        // chunk's last token, so rows past the sequence are dropped by the
+        // range check.  Non-temporal, so they do not push the records the
+        // value slices share out of L2.
         const int HDV = H * DV;
-        const int oofs = 4 * lg * HDV + lr;
+        int oofs[NB][4];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oofs[rb][i] = ((16 * rb + 4 * lg + i) * HDV + lr) * (int)sizeof(OT);
         __syncthreads();
         for (int jc = 0; jc < nchunks; ++jc) {
             const Slot &bc = slot[jc & 1];
             const int t0 = bos + jc * C;
             const int nv = min(C, eos - t0);
             OT *ob = static_cast<OT *>(p.out) + ((size_t)t0 * H + h) * DV + v0 + 16 * cb;
+            const __amdgpu_buffer_rsrc_t orsrc =
+                __builtin_amdgcn_make_buffer_rsrc(ob, 0, ((nv - 1) * HDV + 16) * (int)sizeof(OT), kBufferWord3);
             // every LDS operand of the chunk, issued up front in the order of use
             RowA<ST, NKB> ka[NB], qa[NB];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                ka[rb].load(&bc.Kt[16 * rb + lr][0], lg);
+                ka[rb].load(&bc.Kn[16 * rb + lr][0], lg);
                 qa[rb].load(&bc.Qt[16 * rb + lr][0], lg);
             }
             float vv[NB][4];
@@ -810,22 +836,22 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) St[kb][i] *= dk[KDA ? kb : 0][i];
-            // X = (K e^g) S0^T and Y = (Q e^g) S0^T: 2 NB independent
-            // accumulations, interleaved k-step by k-step
-            f32x4 X[NB], Y[NB], W[NB];
+            // W = V - (K e^g) S0^T (from the negated record operand) and
+            // Y = (Q e^g) S0^T: 2 NB independent accumulations, interleaved
+            // k-step by k-step
+            f32x4 W[NB], Y[NB];
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) X[rb] = Y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rb = 0; rb < NB; ++rb) {
+                W[rb] = f32x4{vv[rb][0], vv[rb][1], vv[rb][2], vv[rb][3]};
+                Y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int st = 0; st < RegB<ST, NKB>::STEPS; ++st)
 #pragma unroll
                 for (int rb = 0; rb < NB; ++rb) {
-                    X[rb] = sop.step(X[rb], ka[rb], st);
+                    W[rb] = sop.step(W[rb], ka[rb], st);
                     Y[rb] = sop.step(Y[rb], qa[rb], st);
                 }
-#pragma unroll
-            for (int rb = 0; rb < NB; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) W[rb][i] = vv[rb][i] - X[rb][i];
             RegB<ST, NB> wh, wl;
             wh.set_split(W, wl);
             // U = T diag(b) (V - X): hi products of every row block, then lo
@@ -872,17 +898,9 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
                         if (st < tri_steps(rb)) Y[rb] = ul.step(Y[rb], ma[rb], st);
             }
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                if (nv == C) {
+            for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store((OT)Y[rb][i], &ob[oofs + (16 * rb + i) * HDV]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (16 * rb + 4 * lg + i < nv)
-                            __builtin_nontemporal_store((OT)Y[rb][i], &ob[oofs + (16 * rb + i) * HDV]);
-                }
-            }
+                for (int i = 0; i < 4; ++i) buffer_store_nt(orsrc, oofs[rb][i], (OT)Y[rb][i]);
             __syncthreads();
         }
         if (p.state_out) {
