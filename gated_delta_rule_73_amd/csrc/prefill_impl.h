@@ -163,23 +163,86 @@ template <typename ST> __host__ __device__ constexpr int kpos(int k) {
 // RegB of the same NBLK supplies (lane row = lr, k = 16*blk + 4*lg + i), the
 // row stored in kpos order.
 template <typename ST, int NBLK> struct RowA;
+// The lane reads 16-byte group 4s + lg (s: k-step) of its row; `sw` XORs
+// the group index for rows stored swizzled (row_swizzle).
 template <int NBLK> struct RowA<_Float16, NBLK> {
     f16x8 f[NBLK / 2];
-    __device__ __forceinline__ void load(const _Float16 *arow, int lg, int nsteps = 1 << 20) {
+    __device__ __forceinline__ void load(const _Float16 *arow, int lg, int nsteps = 1 << 20, int sw = 0) {
 #pragma unroll
         for (int s = 0; s < NBLK / 2; ++s)
-            if (s < nsteps) f[s] = *reinterpret_cast<const f16x8 *>(arow + 32 * s + 8 * lg);
+            if (s < nsteps) f[s] = *reinterpret_cast<const f16x8 *>(arow + 8 * ((4 * s + lg) ^ sw));
+    }
+    // the inverse of load (plain rows, kpos order)
+    __device__ __forceinline__ void store(_Float16 *arow, int lg) const {
+#pragma unroll
+        for (int s = 0; s < NBLK / 2; ++s) *reinterpret_cast<f16x8 *>(arow + 32 * s + 8 * lg) = f[s];
     }
 };
 template <int NBLK> struct RowA<float, NBLK> {
     f32x4 f[NBLK];
-    __device__ __forceinline__ void load(const float *arow, int lg, int nsteps = 1 << 20) {
+    __device__ __forceinline__ void load(const float *arow, int lg, int nsteps = 1 << 20, int sw = 0) {
         const int nblk = nsteps < NBLK ? 2 * nsteps : NBLK;
 #pragma unroll
         for (int b = 0; b < NBLK; ++b)
-            if (b < nblk) f[b] = *reinterpret_cast<const f32x4 *>(arow + 16 * b + 4 * lg);
+            if (b < nblk) f[b] = *reinterpret_cast<const f32x4 *>(arow + 4 * ((4 * b + lg) ^ sw));
+    }
+    __device__ __forceinline__ void store(float *arow, int lg) const {
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) *reinterpret_cast<f32x4 *>(arow + 16 * b + 4 * lg) = f[b];
     }
 };
+
+// A lane's fragment of row `row` of T diag(b) (k = column), from the fp32 T
+// row and b: T_row,s b_s for s <= row, else 0, rounded to ST.
+template <typename ST, int NBLK>
+__device__ __forceinline__ RowA<ST, NBLK> tbeta_fragment(const float *trow, const float *beta, int row, int lg);
+template <>
+__device__ __forceinline__ RowA<_Float16, 2> tbeta_fragment<_Float16, 2>(const float *trow, const float *beta, int row, int lg) {
+    RowA<_Float16, 2> r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int s0 = 16 * h + 4 * lg;
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(trow + s0), b = *reinterpret_cast<const f32x4 *>(beta + s0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.f[0][4 * h + i] = (_Float16)(s0 + i <= row ? t[i] * b[i] : 0.f);
+    }
+    return r;
+}
+template <int NBLK>
+__device__ __forceinline__ RowA<float, NBLK> tbeta_fragment_f32(const float *trow, const float *beta, int row, int lg) {
+    RowA<float, NBLK> r;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+        const int s0 = 16 * blk + 4 * lg;
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(trow + s0), b = *reinterpret_cast<const f32x4 *>(beta + s0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.f[blk][i] = s0 + i <= row ? t[i] * b[i] : 0.f;
+    }
+    return r;
+}
+template <>
+__device__ __forceinline__ RowA<float, 1> tbeta_fragment<float, 1>(const float *trow, const float *beta, int row, int lg) {
+    return tbeta_fragment_f32<1>(trow, beta, row, lg);
+}
+template <>
+__device__ __forceinline__ RowA<float, 2> tbeta_fragment<float, 2>(const float *trow, const float *beta, int row, int lg) {
+    return tbeta_fragment_f32<2>(trow, beta, row, lg);
+}
+
+// acc += A * B over k-step s, both operands read from LDS as RowA fragments
+// (A rows and B columns at lane l & 15)
+template <int NBLK>
+__device__ __forceinline__ f32x4 rowa_mma(f32x4 acc, const RowA<_Float16, NBLK> &a, const RowA<_Float16, NBLK> &b, int s) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.f[s], b.f[s], acc, 0, 0, 0);
+}
+template <int NBLK>
+__device__ __forceinline__ f32x4 rowa_mma(f32x4 acc, const RowA<float, NBLK> &a, const RowA<float, NBLK> &b, int s) {
+#pragma unroll
+    for (int blk = 2 * s; blk < 2 * s + 2 && blk < NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[blk][i], b.f[blk][i], acc, 0, 0, 0);
+    return acc;
+}
 
 // ---- Gram products of the prep kernel: one 32-wide k-step -------------------
 // Each lane supplies 8 operand values for the k-indices {4lg+i, 16+4lg+i}
@@ -221,6 +284,13 @@ __device__ __forceinline__ void store_vec(ST *dst, const ST (&v)[N]) {
     *reinterpret_cast<typename VecT<ST, N>::type *>(dst) = x;
 }
 
+// LDS row pitch for rows read as MFMA A fragments (lane: row l & 15, 16
+// bytes at column group l >> 4).  A wave's 16-byte reads are served 32 lanes
+// at a time from 128 four-byte banks, i.e. 16 rows x 32 contiguous bytes per
+// half wave; those meet every bank once exactly when the pitch is an odd
+// multiple of 32 bytes (measured with the LDS bank-conflict counter on gfx950).
+constexpr int lds_pitch(int bytes) { return bytes + ((32 - bytes % 64) + 64) % 64; }
+
 // ---- buffer stores ----------------------------------------------------------
 // Fourth descriptor word of a raw (unstructured) buffer on CDNA.
 constexpr int kBufferWord3 = 0x00020000;
@@ -233,12 +303,12 @@ __device__ __forceinline__ void buffer_store_nt(__amdgpu_buffer_rsrc_t r, int by
 }
 
 // ---- per-chunk record (workspace, unpadded rows; the k-index of the A
-// operands Kn, Qt (key channel), KeT, Tm, Mm (token) stored in kpos order) ----
+// operands Wn, Qt (key channel), KeT, Tm, Mm (token) stored in kpos order) ----
 template <int DK, int C, bool KDA, typename IT>
 struct ChunkRec {
     using ST = typename Prec<IT>::ST;
     float dec[KDA ? DK : 4];   // e^{g_C}: per key channel (KDA) or dec[0] (GDN)
-    ST Kn[C][DK];              // -k e^g (negated: V - X accumulates from V)
+    ST Wn[C][DK];              // -T diag(b) (k e^g) (negated: U accumulates from T diag(b) V)
     ST Qt[C][DK];              // q e^g
     ST KeT[DK][C];             // (k e^{g_C - g})^T
     ST Tm[C][C];               // T diag(b), zero above the diagonal
@@ -261,10 +331,19 @@ struct PrepSmem {
         float Pt[4][2 * NT][16][20];     // per-wave partial Gram tiles: A tiles, then M tiles
     } u;
     alignas(16) float em[KDA ? DK : 4];  // KDA: e^m
-    float g[C], egc[C], egt[C], beta[C]; // GDN: g, e^{g_C - g}, e^g;  beta
-    alignas(16) float Af[C][LDA];        // strict_tril(diag(b) Gram)
-    alignas(16) float Tf[C][LDA];        // (I + A)^-1
-    float P[256];                        // A_10 T_00
+    float g[C], egc[C], egt[C];          // GDN: g, e^{g_C - g}, e^g
+    alignas(16) float beta[C];
+    // Once the partial tiles are summed, their space holds the lower tiles
+    // of A (in place of wave 0's partials: each thread overwrites only what
+    // it has read), T = (I + A)^-1 and T's diagonal blocks transposed.
+    __device__ float *a_tile(int tt) { return &u.Pt[0][tt][0][0]; }   // rows of 20
+    __device__ float (*tf())[LDA] { return reinterpret_cast<float (*)[LDA]>(&u.Pt[1][0][0][0]); }
+    __device__ float (*tft())[LDA] { return reinterpret_cast<float (*)[LDA]>(&u.Pt[2][0][0][0]); }
+    static_assert(C * LDA <= 2 * NT * 16 * 20, "T fits in one wave's partial tiles");
+    // operands of W = T diag(b) (K e^g), token index in kpos order
+    using ST = typename Prec<IT>::ST;
+    static constexpr int LDT = lds_pitch(C * (int)sizeof(ST)) / (int)sizeof(ST);
+    alignas(16) ST KtT[DK][LDT];         // (K e^g)^T
 };
 
 struct PrepKArgs {
@@ -283,7 +362,7 @@ struct PrepKArgs {
 // workgroups (four waves each) per CU walk the records, each holding the next
 // record's inputs in flight while it computes the current one.
 template <int DK, int C, bool KDA, typename IT>
-__global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
+__global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     using SM = PrepSmem<DK, C, KDA, IT>;
     using Rec = ChunkRec<DK, C, KDA, IT>;
     using ST = typename Prec<IT>::ST;
@@ -300,7 +379,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
     static_assert(NB <= 2, "the inverse below handles at most two 16-token blocks");
     static_assert(SEGL >= 1 && C <= 64, "prefix-sum thread mapping");
     static_assert(sizeof(Rec) == chunk_record_bytes(DK, C, KDA, sizeof(ST)), "record layout");
-    static_assert(sizeof(SM) <= 64 * 1024, "LDS budget (several workgroups per CU)");
+    static_assert(sizeof(SM) <= (sizeof(ST) == 2 ? 64 : 160) * 1024, "LDS budget (fp16: two workgroups per CU)");
     static_assert(sizeof(ST) == 4 || (C % 32 == 0 && DK % 32 == 0), "fp16 operands are stored in 32-wide k-blocks");
 
     constexpr int KVPT = (C * DK / EPV + 255) / 256;        // 16-byte k (and q) vectors per thread
@@ -429,11 +508,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
     fetch(r + gridDim.x);
     __syncthreads();
 
-    // ---- B: per-channel prefix sums (KDA) and K_end^T, one key channel per
-    // NSEG lanes, SEGL tokens each
+    // ---- B: per-channel prefix sums (KDA), K_end^T to the record and
+    // (K e^g)^T to LDS, one key channel per NSEG lanes, SEGL tokens each
     {
         const int gc = tid / NSEG, gseg = tid % NSEG;
-        float ke[SEGL];
+        float ke[SEGL], kt[SEGL];
         if constexpr (KDA) {
             float gv[SEGL];
 #pragma unroll
@@ -455,7 +534,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                 const int t = gseg * SEGL + s;
                 const float g = gv[s] + carry;
                 sm.u.in.G[t][gc] = g - m;
-                ke[s] = (float)sm.u.in.Ks[t][gc] * __expf(gC - g);
+                const float kv = (float)sm.u.in.Ks[t][gc];
+                ke[s] = kv * __expf(gC - g);
+                kt[s] = kv * __expf(g);
             }
             if (gseg == 0) {
                 sm.em[gc] = __expf(m);
@@ -465,7 +546,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
 #pragma unroll
             for (int s = 0; s < SEGL; ++s) {
                 const int t = gseg * SEGL + s;
-                ke[s] = (float)sm.u.in.Ks[t][gc] * sm.egc[t];
+                const float kv = (float)sm.u.in.Ks[t][gc];
+                ke[s] = kv * sm.egc[t];
+                kt[s] = kv * sm.egt[t];
             }
         }
         if constexpr (SEGL % 4 == 0) {
@@ -473,10 +556,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
             for (int s = 0; s < SEGL; s += 4) {
                 const ST v4[4] = {(ST)ke[s], (ST)ke[s + 1], (ST)ke[s + 2], (ST)ke[s + 3]};
                 store_vec<ST, 4>(&rec.KeT[gc][kpos<ST>(gseg * SEGL + s)], v4);
+                const ST w4[4] = {(ST)kt[s], (ST)kt[s + 1], (ST)kt[s + 2], (ST)kt[s + 3]};
+                store_vec<ST, 4>(&sm.KtT[gc][kpos<ST>(gseg * SEGL + s)], w4);
             }
         } else {
 #pragma unroll
-            for (int s = 0; s < SEGL; ++s) rec.KeT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)ke[s];
+            for (int s = 0; s < SEGL; ++s) {
+                rec.KeT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)ke[s];
+                sm.KtT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)kt[s];
+            }
         }
     }
     __syncthreads();
@@ -500,7 +588,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                     kf[i] = valid ? (float)sm.u.in.Ks[t][ch + i] : 0.f;
                     qf[i] = valid ? (float)sm.u.in.Qs[t][ch + i] : 0.f;
                 }
-                ST kt[4], qt[4];
+                ST qt[4];
                 if constexpr (KDA) {
                     f32x4 xv{0.f, 0.f, 0.f, 0.f}, emv{0.f, 0.f, 0.f, 0.f};
                     if (valid) {
@@ -517,7 +605,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                         fr[rb][4 * hh + i] = rh;
                         fql[rb][4 * hh + i] = (FT)(lq - (float)qh);
                         frl[rb][4 * hh + i] = (FT)(rk - (float)rh);
-                        kt[i] = (ST)(-lk * emv[i]);
                         qt[i] = (ST)(lq * emv[i] * p.scale);
                     }
                 } else {
@@ -528,14 +615,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                     for (int i = 0; i < 4; ++i) {
                         fk[rb][4 * hh + i] = (ST)kf[i];
                         fq[rb][4 * hh + i] = (ST)qf[i];
-                        kt[i] = (ST)(-kf[i] * e);
                         qt[i] = (ST)(qf[i] * e * p.scale);
                     }
                 }
-                if (valid) {
-                    store_vec<ST, 4>(&rec.Kn[t][kpos<ST>(ch)], kt);
-                    store_vec<ST, 4>(&rec.Qt[t][kpos<ST>(ch)], qt);
-                }
+                if (valid) store_vec<ST, 4>(&rec.Qt[t][kpos<ST>(ch)], qt);
             }
         }
 #pragma unroll
@@ -590,114 +673,170 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKArgs p) {
                 fa *= d;
                 fm *= d;
             }
-            sm.Af[R][c] = fa;
+            if (J <= I) sm.a_tile(I * (I + 1) / 2 + J)[r * 20 + cc + i] = fa;
             mv[i] = (ST)(fm * p.scale);
         }
         store_vec<ST, 4>(&rec.Mm[R][kpos<ST>(c0)], mv);
     }
     __syncthreads();
-    // diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution, one
-    // column per lane: t_i = delta_ij - sum_{m<i} A_im t_m
-    if (wave == 0 && lane < C) {
-        const int I = lane / 16, jc = lane % 16;
+    // T = (I + A)^-1 on wave 0.  Diagonal 16x16 blocks by forward
+    // substitution, one column per lane (lanes 0-15 block 0, 16-31 block 1,
+    // the upper half wave repeating them): t_i = delta_ij - sum_{m<i} A_im t_m,
+    // with the block's strictly lower triangle read into registers first
+    // (all lanes of a block read the same rows).  Then, for two blocks,
+    // T_10 = -T_11 (A_10 T_00) as two fp32 MFMA products on the same wave:
+    // A_10 T_00 lands in the accumulator layout that the second product
+    // takes as its B operand.
+    float (*const Tf)[SM::LDA] = sm.tf();
+    float (*const TfT)[SM::LDA] = sm.tft();
+    if (wave == 0) {
+        const int I = NB == 2 ? (lane >> 4) & 1 : 0, jc = lane & 15;
+        f32x4 arow[16][4];
+        const float *adiag = sm.a_tile(I * (I + 1) / 2 + I);
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+#pragma unroll
+            for (int m4 = 0; m4 < i; m4 += 4) arow[i][m4 / 4] = *reinterpret_cast<const f32x4 *>(&adiag[i * 20 + m4]);
         float tcol[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float acc0 = (i == jc) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-            for (int m4 = 0; m4 < i; m4 += 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.Af[16 * I + i][16 * I + m4]);
-#pragma unroll
-                for (int y = 0; y < 4; ++y)
-                    if (m4 + y < i) {
-                        if (y & 1) acc1 -= v[y] * tcol[m4 + y];
-                        else acc0 -= v[y] * tcol[m4 + y];
-                    }
+            for (int m = 0; m < i; ++m) {
+                if (m & 1) acc1 -= arow[i][m / 4][m % 4] * tcol[m];
+                else acc0 -= arow[i][m / 4][m % 4] * tcol[m];
             }
             tcol[i] = acc0 + acc1;
         }
+        if (lane < 16 * NB) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.Tf[16 * I + i][16 * I + jc] = tcol[i];
+            for (int i = 0; i < 16; ++i) Tf[16 * I + i][16 * I + jc] = tcol[i];
+#pragma unroll
+            for (int i4 = 0; i4 < 16; i4 += 4)
+                *reinterpret_cast<f32x4 *>(&TfT[16 * I + jc][16 * I + i4]) =
+                    f32x4{tcol[i4], tcol[i4 + 1], tcol[i4 + 2], tcol[i4 + 3]};
+        }
+        if constexpr (NB == 2) {
+            // (this wave's LDS writes above are visible to its reads below:
+            // one wave's LDS operations execute in order)
+            RowA<float, 1> a10, t00c, t11;
+            a10.load(sm.a_tile(1) + lr * 20, lg);  // A_10 rows
+            t00c.load(&TfT[lr][0], lg);            // T_00 columns
+            const f32x4 P = rowa_mma(f32x4{0.f, 0.f, 0.f, 0.f}, a10, t00c, 0);
+            RegB<float, 1> pb;
+            pb.set(&P);
+            t11.load(&Tf[16 + lr][16], lg);        // T_11 rows
+            const f32x4 t10 = pb.mma(f32x4{0.f, 0.f, 0.f, 0.f}, t11);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Tf[16 + 4 * lg + i][lr] = -t10[i];
+        }
     }
     __syncthreads();
-    if constexpr (NB == 2) {
-        // T_10 = -T_11 (A_10 T_00)
-        {
-            const int r = tid >> 4, c = tid & 15;
-            float acc = 0.f;
+    // ---- E: T diag(b) and W = T diag(b) (K e^g), both to the record.  The
+    // B operand of the W product is T diag(b) itself (rows: output token,
+    // k: token), built per lane from T and b as the rounded values the
+    // record stores; those lane fragments are 16-byte pieces of the record's
+    // T diag(b) rows.  Each W tile is W^T for (16 keys, 16 tokens), so a
+    // lane's four results are adjacent keys of one token.
+    {
+        RowA<ST, NB> tbf[NB];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc += sm.Af[16 + r][m] * sm.Tf[m][c];
-            sm.P[tid] = acc;
+        for (int tb = 0; tb < NB; ++tb) {
+            const int row = 16 * tb + lr;
+            tbf[tb] = tbeta_fragment<ST, NB>(&Tf[row][0], sm.beta, row, lg);
+            if (wave == tb) tbf[tb].store(&rec.Tm[row][0], lg);
         }
-        __syncthreads();
-        {
-            const int r = tid >> 4, c = tid & 15;
-            float acc = 0.f;
+        // key blocks kb = wave, wave + 4, ... of every token block
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc += sm.Tf[16 + r][16 + m] * sm.P[m * 16 + c];
-            sm.Tf[16 + r][c] = -acc;
-        }
-        __syncthreads();
-    }
-    // T diag(b)
-    for (int e = tid; e < C * C / 4; e += 256) {
-        const int R = e / (C / 4), c0 = (e % (C / 4)) * 4;
-        ST tv[4];
+        for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = c0 + i;
-            tv[i] = (ST)(c <= R ? sm.Tf[R][c] * sm.beta[c] : 0.f);
+        for (int j = 0; j < (DK / 16 + 3) / 4; ++j) {
+            const int kb = wave + 4 * j;
+            if (kb < DK / 16) {
+                RowA<ST, NB> a;
+                a.load(&sm.KtT[16 * kb + lr][0], lg);
+                f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st) acc = rowa_mma(acc, a, tbf[tb], st);
+                ST w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = (ST)(-acc[i]);
+                store_vec<ST, 4>(&rec.Wn[16 * tb + lr][kpos<ST>(16 * kb + 4 * lg)], w);
+            }
         }
-        store_vec<ST, 4>(&rec.Tm[R][kpos<ST>(c0)], tv);
     }
     __syncthreads();   // the next record's inputs overwrite this one's scratch
     }
 }
 
 // ============================ chain kernel ===================================
-// LDS row pitch for rows read as MFMA A fragments (lane: row l & 15, 16
-// bytes at column group l >> 4).  A wave's 16-byte reads are served 32 lanes
-// at a time from 128 four-byte banks, i.e. 16 rows x 32 contiguous bytes per
-// half wave; those meet every bank once exactly when the pitch is an odd
-// multiple of 32 bytes (measured with the LDS bank-conflict counter on gfx950).
-constexpr int lds_pitch(int bytes) { return bytes + ((32 - bytes % 64) + 64) % 64; }
+// Swizzle of an unpadded LDS row of G 16-byte groups: row r stores logical
+// group c at position c ^ row_swizzle(G, r).  Rows r and r + 32/G fall on the
+// same banks; the XOR moves the two groups a lane pair reads onto distinct
+// banks for 16 consecutive rows (the same rule as lds_pitch, for rows that
+// cannot be padded because they are filled by whole-wave LDS-direct loads).
+// Periodic in r with period 16.
+__host__ __device__ constexpr int row_swizzle(int G, int r) { return G >= 4 ? 2 * ((r / (32 / G)) % (G / 2)) : 0; }
+
+// Loader waves of the chain kernel: kRecordWaves copy records into LDS with
+// LDS-direct loads, one more wave carries the value slice through registers.
+constexpr int kRecordWaves = 3;
+constexpr int kLoaderWaves = kRecordWaves + 1;
 
 template <int DK, int DVS, int C, bool KDA, typename IT>
 struct alignas(16) ChainSlot {
     using ST = typename Prec<IT>::ST;
-    static constexpr int LDK = lds_pitch(DK * (int)sizeof(ST)) / (int)sizeof(ST);
-    static constexpr int LDC = lds_pitch(C * (int)sizeof(ST)) / (int)sizeof(ST);
-    static constexpr int LDVT = lds_pitch(C * (int)sizeof(IT)) / (int)sizeof(IT);
-    float dec[KDA ? DK : 4];
-    ST Kn[C][LDK];
-    ST Qt[C][LDK];
-    ST KeT[DK][LDC];
-    ST Tm[C][LDC];
-    ST Mm[C][LDC];
-    IT Vt[DVS][LDVT];             // value slice, transposed (token columns)
+    using Rec = ChunkRec<DK, C, KDA, IT>;
+    static constexpr int NPIECE = (int)sizeof(Rec) / 16;
+    // record bytes rounded up to whole rounds of the record waves' 1 KB loads
+    static constexpr int RPIECES = (NPIECE + 64 * kRecordWaves - 1) / (64 * kRecordWaves) * (64 * kRecordWaves);
+    static constexpr int LDVT = lds_pitch(C * (int)sizeof(ST)) / (int)sizeof(ST);
+    union {
+        Rec r;                          // the record, each row swizzled (row_swizzle)
+        char raw[16 * RPIECES];
+    } rec;
+    ST Vt[DVS][LDVT];                   // value slice as an MFMA operand: value rows, tokens in kpos order
 };
 
-// Byte offset in a ChainSlot of the 16-byte piece p of a ChunkRec: the
-// record's rows are unpadded, the slot's are padded.
-template <int DK, int DVS, int C, bool KDA, typename IT>
-__device__ __forceinline__ int slot_offset(int p) {
-    using Slot = ChainSlot<DK, DVS, C, KDA, IT>;
+// The record piece held by 16-byte position q of a slot's record area (past
+// the record: any valid piece).  The decay row is stored plainly; the rows of
+// Wn, Qt (G = DK groups) and KeT, Tm, Mm (G = C groups) are swizzled.
+template <int DK, int C, bool KDA, typename IT>
+__device__ __forceinline__ int rec_piece_at(int q) {
     using ST = typename Prec<IT>::ST;
     constexpr int PD = (KDA ? DK : 4) * 4 / 16;
-    constexpr int RK = DK * (int)sizeof(ST) / 16, RC = C * (int)sizeof(ST) / 16;
-    constexpr int BK = Slot::LDK * (int)sizeof(ST), BC = Slot::LDC * (int)sizeof(ST);
-    if (p < PD) return (int)__builtin_offsetof(Slot, dec) + 16 * p;
-    p -= PD;
-    if (p < C * RK) return (int)__builtin_offsetof(Slot, Kn) + (p / RK) * BK + (p % RK) * 16;
-    p -= C * RK;
-    if (p < C * RK) return (int)__builtin_offsetof(Slot, Qt) + (p / RK) * BK + (p % RK) * 16;
-    p -= C * RK;
-    if (p < DK * RC) return (int)__builtin_offsetof(Slot, KeT) + (p / RC) * BC + (p % RC) * 16;
-    p -= DK * RC;
-    if (p < C * RC) return (int)__builtin_offsetof(Slot, Tm) + (p / RC) * BC + (p % RC) * 16;
-    p -= C * RC;
-    return (int)__builtin_offsetof(Slot, Mm) + (p / RC) * BC + (p % RC) * 16;
+    constexpr int GK = DK * (int)sizeof(ST) / 16, GC = C * (int)sizeof(ST) / 16;
+    constexpr int NP = (int)sizeof(ChunkRec<DK, C, KDA, IT>) / 16;
+    if (q >= NP) return NP - 1;
+    if (q < PD) return q;
+    q -= PD;
+    if (q < 2 * C * GK) {
+        const int r = q / GK, g = q % GK;
+        return PD + r * GK + (g ^ row_swizzle(GK, r));
+    }
+    q -= 2 * C * GK;
+    const int r = q / GC, g = q % GC;
+    return PD + 2 * C * GK + r * GC + (g ^ row_swizzle(GC, r));
 }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (lds uniform across the wave).  Completion is counted by
+// vmcnt like any load.  (The builtin exists only in the device pass; the host
+// pass, which compiles just the kernel's launch stub, never runs it.)
+__device__ __forceinline__ void lds_direct_load16(const void *src, void *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#else
+    (void)src;
+    (void)lds;
+#endif
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations: loads
+// in flight to registers or to LDS keep going across it (the compiler's own
+// barrier would drain them).  Waves that fill LDS with LDS-direct loads wait
+// for them explicitly before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct ChainKArgs {
     int T, H, DV, num_seqs;
@@ -710,8 +849,6 @@ struct ChainKArgs {
     float *state_out;            // state after the last chunk processed (NULL: not written)
 };
 
-constexpr int kLoaderWaves = 4;
-
 template <int DK, int DVS, int C, bool KDA, typename IT, bool OUTB>
 __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(ChainKArgs p) {
     using Slot = ChainSlot<DK, DVS, C, KDA, IT>;
@@ -723,19 +860,27 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     constexpr int NKB = DK / 16;                   // 16-channel key blocks
     constexpr int EPV = 16 / sizeof(IT);
     using IV = typename VecT<IT, EPV>::type;
-    constexpr int NPIECE = (int)sizeof(Rec) / 16;  // 16-byte pieces of a record
-    constexpr int PPT = (NPIECE + 64 * NLW - 1) / (64 * NLW);
+    constexpr int NRW = kRecordWaves;
+    constexpr int RX = Slot::RPIECES / (64 * NRW);  // LDS-direct loads per record-wave lane per chunk
     constexpr int VV = C * (DVS / EPV);            // 16-byte value vectors per chunk
-    constexpr int DEPTH = PPT > 8 ? 2 : 4;         // chunks in flight in the loaders' registers
+    // LDS slots: the chain reads one while the loaders fill the next NSLOT - 1
+    constexpr int NSLOT = std::min<int>(4, (int)((160 * 1024) / sizeof(Slot)));
+    constexpr int GK = DK * (int)sizeof(ST) / 16, GC = C * (int)sizeof(ST) / 16;
     constexpr size_t RS = chunk_record_stride(DK, C, KDA, sizeof(ST));
     static_assert(sizeof(Rec) % 16 == 0, "record pieces");
-    static_assert(VV <= 64 * NLW, "one value vector per loader lane");
-    static_assert(2 * sizeof(Slot) <= 160 * 1024, "LDS budget");
+    static_assert(GK <= 32 && GC <= 32, "row swizzle covers rows of up to 32 groups");
+    static_assert(VV % 64 == 0, "whole value vectors per lane of the value wave");
+    static_assert(NSLOT >= 2, "LDS budget");
     static_assert(NB <= 2, "T and M rows span at most one 32-wide k-step");
     // 32-wide k-steps of the lower-triangular T and M rows of row block rb
     auto tri_steps = [](int rb) { return (16 * rb + 16 + 31) / 32; };
 
-    __shared__ Slot slot[2];
+    __shared__ Slot slot0, slot1, slot2, slot3;
+    auto slot = [&](int i) -> Slot & {
+        if constexpr (NSLOT > 3) if (i == 3) return slot3;
+        if constexpr (NSLOT > 2) if (i == 2) return slot2;
+        return i == 1 ? slot1 : slot0;
+    };
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: the chain / loader split below is a
     // uniform branch, so each wave executes only its own path's barriers
@@ -789,29 +934,27 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
         for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) oofs[rb][i] = ((16 * rb + 4 * lg + i) * HDV + lr) * (int)sizeof(OT);
-        __syncthreads();
+        const int swK = row_swizzle(GK, lr), swC = row_swizzle(GC, lr);
+        lds_barrier();
         for (int jc = 0; jc < nchunks; ++jc) {
-            const Slot &bc = slot[jc & 1];
+            const Slot &bs = slot(jc % NSLOT);
+            const Rec &bc = bs.rec.r;
             const int t0 = bos + jc * C;
             const int nv = min(C, eos - t0);
             OT *ob = static_cast<OT *>(p.out) + ((size_t)t0 * H + h) * DV + v0 + 16 * cb;
             const __amdgpu_buffer_rsrc_t orsrc =
                 __builtin_amdgcn_make_buffer_rsrc(ob, 0, ((nv - 1) * HDV + 16) * (int)sizeof(OT), kBufferWord3);
             // every LDS operand of the chunk, issued up front in the order of use
-            RowA<ST, NKB> ka[NB], qa[NB];
+            RowA<ST, NKB> wa[NB], qa[NB];
+            RowA<ST, NB> ta[NB], vb;
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                ka[rb].load(&bc.Kn[16 * rb + lr][0], lg);
-                qa[rb].load(&bc.Qt[16 * rb + lr][0], lg);
+                ta[rb].load(&bc.Tm[16 * rb + lr][0], lg, tri_steps(rb), swC);
+                wa[rb].load(&bc.Wn[16 * rb + lr][0], lg, 1 << 20, swK);
             }
-            float vv[NB][4];
+            vb.load(&bs.Vt[16 * cb + lr][0], lg);
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                using IV4 = typename VecT<IT, 4>::type;
-                const IV4 x = *reinterpret_cast<const IV4 *>(&bc.Vt[16 * cb + lr][16 * rb + 4 * lg]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vv[rb][i] = (float)x[i];
-            }
+            for (int rb = 0; rb < NB; ++rb) qa[rb].load(&bc.Qt[16 * rb + lr][0], lg, 1 << 20, swK);
             f32x4 dk[KDA ? NKB : 1];
             if constexpr (KDA) {
 #pragma unroll
@@ -820,15 +963,21 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
                 const float d = bc.dec[0];
                 dk[0] = f32x4{d, d, d, d};
             }
-            RowA<ST, NB> ta[NB], ma[NB], kea[NKB];
+            RowA<ST, NB> ma[NB], kea[NKB];
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) ma[rb].load(&bc.Mm[16 * rb + lr][0], lg, tri_steps(rb), swC);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kea[kb].load(&bc.KeT[16 * kb + lr][0], lg, 1 << 20, swC);
+
+            // U = T diag(b) V + W_neg S0^T: the state-independent part first
+            f32x4 U[NB], Y[NB];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                ta[rb].load(&bc.Tm[16 * rb + lr][0], lg, tri_steps(rb));
-                ma[rb].load(&bc.Mm[16 * rb + lr][0], lg, tri_steps(rb));
-            }
+                U[rb] = Y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kea[kb].load(&bc.KeT[16 * kb + lr][0], lg);
-
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+                    if (st < tri_steps(rb)) U[rb] = rowa_mma(U[rb], ta[rb], vb, st);
+            }
             RegB<ST, NKB> sop;
             sop.set(St);
             // the decayed state S0 Diag(e^{g_C}), formed while the products run
@@ -836,40 +985,16 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) St[kb][i] *= dk[KDA ? kb : 0][i];
-            // W = V - (K e^g) S0^T (from the negated record operand) and
-            // Y = (Q e^g) S0^T: 2 NB independent accumulations, interleaved
-            // k-step by k-step
-            f32x4 W[NB], Y[NB];
-#pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                W[rb] = f32x4{vv[rb][0], vv[rb][1], vv[rb][2], vv[rb][3]};
-                Y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            // the state-dependent part of U, then Y = (Q e^g) S0^T; NB
+            // independent accumulations each, interleaved k-step by k-step
 #pragma unroll
             for (int st = 0; st < RegB<ST, NKB>::STEPS; ++st)
 #pragma unroll
-                for (int rb = 0; rb < NB; ++rb) {
-                    W[rb] = sop.step(W[rb], ka[rb], st);
-                    Y[rb] = sop.step(Y[rb], qa[rb], st);
-                }
-            RegB<ST, NB> wh, wl;
-            wh.set_split(W, wl);
-            // U = T diag(b) (V - X): hi products of every row block, then lo
-            f32x4 U[NB];
+                for (int rb = 0; rb < NB; ++rb) U[rb] = sop.step(U[rb], wa[rb], st);
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) U[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < RegB<ST, NKB>::STEPS; ++st)
 #pragma unroll
-            for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
-#pragma unroll
-                for (int rb = 0; rb < NB; ++rb)
-                    if (st < tri_steps(rb)) U[rb] = wh.step(U[rb], ta[rb], st);
-            if constexpr (SPLIT) {
-#pragma unroll
-                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
-#pragma unroll
-                    for (int rb = 0; rb < NB; ++rb)
-                        if (st < tri_steps(rb)) U[rb] = wl.step(U[rb], ta[rb], st);
-            }
+                for (int rb = 0; rb < NB; ++rb) Y[rb] = sop.step(Y[rb], qa[rb], st);
             RegB<ST, NB> uh, ul;
             uh.set_split(U, ul);
             // S^T <- Diag(e^{g_C}) S0^T + K_end^T U: hi products of every key
@@ -901,7 +1026,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) buffer_store_nt(orsrc, oofs[rb][i], (OT)Y[rb][i]);
-            __syncthreads();
+            lds_barrier();
         }
         if (p.state_out) {
 #pragma unroll
@@ -911,65 +1036,99 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
         return;
     }
 
-    // ======================= loader waves (256 threads) ======================
-    // Chunk c's record sits in register set c % DEPTH from the moment its
-    // loads are issued until it is copied into LDS slot c & 1, the iteration
-    // before the chain waves read it.
-    int lofs[PPT];
+    // ============================ loader waves ================================
+    // Chunk c uses slot c % NSLOT; its loads are issued NSLOT - 1 chunks
+    // ahead.  Every chunk issues the same loads, unconditionally (chunks past
+    // the end reload the last one into a slot nobody reads; value rows past
+    // the sequence are zeroed when written), so a wave's count of loads in
+    // flight is fixed.  The two kinds of loader run on separate waves: a wave
+    // whose code both writes LDS and has LDS-direct loads in flight would be
+    // made to wait for all of them before each write.
+    if (nchunks > 0 && wave < NRW) {
+        // ---- record waves: global -> LDS directly, no registers.  Load x of
+        // wave w fills the slot's record bytes [1 KB (x NRW + w), +1 KB), lane
+        // l the 16-byte position q = 64 (x NRW + w) + l, which holds the
+        // record piece rec_piece_at(q).
+        int goff[RX];
 #pragma unroll
-    for (int x = 0; x < PPT; ++x) {
-        const int pc = tid + 64 * NLW * x;
-        lofs[x] = pc < NPIECE ? slot_offset<DK, DVS, C, KDA, IT>(pc) : -1;
-    }
-    const IT *gv = static_cast<const IT *>(p.v);
-    const int vt = tid / (DVS / EPV), vc = (tid % (DVS / EPV)) * EPV;
-    i32x4 rg[DEPTH][PPT];
-    IV vr[DEPTH];
-    // Every chunk issues the same loads, unconditionally (chunks past the end
-    // reload the last one, pieces past the record reload its last piece, value
-    // rows past the sequence are zeroed after the load): with no branch around
-    // a load the compiler counts outstanding loads exactly and waits only for
-    // the set it needs, keeping DEPTH chunks in flight.
-    const int vrow = tid < VV ? vt : 0;
-    bool vok[DEPTH];   // value row inside the sequence (applied when written to LDS)
-    auto issue = [&](i32x4 (&r)[PPT], IV &v, bool &ok, int c) {
-        const int cc = min(c, nchunks - 1);
-        const char *src = rec0 + (size_t)cc * H * RS;
+        for (int x = 0; x < RX; ++x) goff[x] = 16 * rec_piece_at<DK, C, KDA, IT>(64 * (x * NRW + wave) + lane);
+        auto issue = [&](int c, int sl) {
+            const char *src = rec0 + (size_t)min(c, nchunks - 1) * H * RS;
+            char *dst = slot(sl).rec.raw + 1024 * wave;
 #pragma unroll
-        for (int x = 0; x < PPT; ++x)
-            r[x] = *reinterpret_cast<const i32x4 *>(src + 16 * min(tid + 64 * NLW * x, NPIECE - 1));
-        const int t = bos + cc * C + vrow;
-        v = *reinterpret_cast<const IV *>(gv + ((size_t)min(t, eos - 1) * H + h) * DV + v0 + vc);
-        ok = t < eos;
-    };
-    auto commit = [&](const i32x4 (&r)[PPT], const IV &v, bool ok, Slot &s) {
-        char *base = reinterpret_cast<char *>(&s);
+            for (int x = 0; x < RX; ++x) lds_direct_load16(src + goff[x], dst + 1024 * NRW * x);
+        };
+        // chunk c + 1 has landed while the NSLOT - 2 chunks after it stay in
+        // flight (loads complete in issue order)
+        constexpr int AFTER = (NSLOT - 2) * RX;
+        static_assert(AFTER < 64, "vmcnt range");
+        auto wait_next = [&]() { __builtin_amdgcn_s_waitcnt((AFTER & 15) | ((AFTER >> 4) << 14) | (7 << 4) | (15 << 8)); };
 #pragma unroll
-        for (int x = 0; x < PPT; ++x)
-            if (lofs[x] >= 0) *reinterpret_cast<i32x4 *>(base + lofs[x]) = r[x];
-        if (tid < VV) {
+        for (int c = 0; c < NSLOT - 1; ++c) issue(c, c);
+        wait_next();   // chunk 0
+        lds_barrier();
+        for (int jb = 0; jb < nchunks; jb += NSLOT) {
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) s.Vt[vc + e][vt] = ok ? v[e] : IT(0.f);
-        }
-    };
-    if (nchunks > 0) {
-#pragma unroll
-        for (int c = 0; c < DEPTH; ++c) issue(rg[c], vr[c], vok[c], c);
-        commit(rg[0], vr[0], vok[0], slot[0]);
-        issue(rg[0], vr[0], vok[0], DEPTH);
-    }
-    __syncthreads();
-    for (int jb = 0; jb < nchunks; jb += DEPTH) {
-#pragma unroll
-        for (int u = 0; u < DEPTH; ++u) {
-            const int jc = jb + u;
-            if (jc < nchunks) {
-                const int s = (u + 1) % DEPTH;   // holds chunk jc + 1
-                if (jc + 1 < nchunks) commit(rg[s], vr[s], vok[s], slot[(jc + 1) & 1]);
-                issue(rg[s], vr[s], vok[s], jc + 1 + DEPTH);
-                __syncthreads();
+            for (int u = 0; u < NSLOT; ++u) {
+                if (jb + u < nchunks) {
+                    issue(jb + u + NSLOT - 1, (u + NSLOT - 1) % NSLOT);   // the slot chunk jb + u - 1 used
+                    wait_next();                                        // chunk jb + u + 1
+                    lds_barrier();
+                }
             }
         }
+        // no LDS-direct write may land after the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(0);
+    } else if (nchunks > 0) {
+        // ---- value wave: the value slice through registers, written
+        // transposed (value rows, tokens in kpos order) as the fp16 operand
+        constexpr int VPL = VV / 64;
+        const IT *gv = static_cast<const IT *>(p.v);
+        IV vr[NSLOT][VPL];
+        bool vok[NSLOT][VPL];
+        auto issue = [&](int c, int sl) {
+            const int cc = min(c, nchunks - 1);
+#pragma unroll
+            for (int y = 0; y < VPL; ++y) {
+                const int e = lane + 64 * y, vt = e / (DVS / EPV), vc = (e % (DVS / EPV)) * EPV;
+                const int t = bos + cc * C + vt;
+                vr[sl][y] = *reinterpret_cast<const IV *>(gv + ((size_t)min(t, eos - 1) * H + h) * DV + v0 + vc);
+                vok[sl][y] = t < eos;
+            }
+        };
+        using UT = typename std::conditional<sizeof(IT) == 2, unsigned short, unsigned>::type;
+        auto commit = [&](int sl) {
+#pragma unroll
+            for (int y = 0; y < VPL; ++y) {
+                const int e = lane + 64 * y, vt = e / (DVS / EPV), vc = (e % (DVS / EPV)) * EPV;
+                const UT keep = vok[sl][y] ? UT(~UT(0)) : UT(0);   // rows past the sequence become +0
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) {
+                    // (element copied out first: a bit cast of a vector element
+                    // in place reads element 0 with this compiler)
+                    const IT el = vr[sl][y][i];
+                    const IT x = __builtin_bit_cast(IT, UT(__builtin_bit_cast(UT, el) & keep));
+                    slot(sl).Vt[vc + i][kpos<ST>(vt)] = (ST)(float)x;
+                }
+            }
+        };
+#pragma unroll
+        for (int c = 0; c < NSLOT - 1; ++c) issue(c, c);
+        commit(0);
+        lds_barrier();
+        for (int jb = 0; jb < nchunks; jb += NSLOT) {
+#pragma unroll
+            for (int u = 0; u < NSLOT; ++u) {
+                const int jc = jb + u;
+                if (jc < nchunks) {
+                    issue(jc + NSLOT - 1, (u + NSLOT - 1) % NSLOT);
+                    if (jc + 1 < nchunks) commit((u + 1) % NSLOT);
+                    lds_barrier();
+                }
+            }
+        }
+    } else {
+        lds_barrier();   // the chain waves' first barrier
     }
 }
 
