@@ -8,6 +8,11 @@ missing, the calls raise.
 
     o, S = gdr_prefill_chunked(q, k, v, beta, log_alpha, initial_state=S0, cu_seqlens=cu)
     o    = gdr_decode_step(q, k, v, beta, log_alpha, state)   # state updated in place
+    o    = gdr_decode_tokens(q, k, v, beta, log_alpha, pool, num_commit=c, state_slots=s)
+
+Value heads may share query-key heads: q and k carry Hk heads, v, the gates,
+the states and the outputs H (a multiple of Hk); value head h reads q/k head
+h // (H // Hk).
 """
 from __future__ import annotations
 
@@ -16,7 +21,8 @@ import os
 
 import torch
 
-__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "prefill_chunked", "decode_step",
+__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "gdr_decode_tokens", "prefill_chunked", "decode_step",
+           "decode_tokens",
            "gdr_state_bytes", "GdrError", "load_library", "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +42,10 @@ class GdrError(RuntimeError):
 
 class PrefillShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("num_heads", ctypes.c_int32),
-                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32)]
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("num_qk_heads", ctypes.c_int32)]
+
+ABI_VERSION = 3
 
 
 _lib = None
@@ -56,15 +65,20 @@ def load_library():
                                             ctypes.c_int, p, p, p, p, p, p, p, i32, i32, ctypes.c_float, p, p, p,
                                             sz, p]
         lib.gdr_prefill_chunked.restype = ctypes.c_int
-        lib.gdr_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        p, p, p, p, p, p, ctypes.c_float, p, p]
+        lib.gdr_decode_step.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, p, p, p, p, p, p, ctypes.c_float, p, p]
         lib.gdr_decode_step.restype = ctypes.c_int
+        lib.gdr_decode_tokens.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, p, p, p, p, p, p, p, p, p, i32, ctypes.c_float, p, p]
+        lib.gdr_decode_tokens.restype = ctypes.c_int
         lib.gdr_state_bytes.argtypes = [ctypes.c_int64] * 4
         lib.gdr_state_bytes.restype = ctypes.c_uint64
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_status_string.restype = ctypes.c_char_p
         lib.gdr_last_error.restype = ctypes.c_char_p
         lib.gdr_abi_version.restype = ctypes.c_int
+        if lib.gdr_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{library_path} has ABI {lib.gdr_abi_version()}, this binding needs {ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 
@@ -108,7 +122,7 @@ def gdr_state_bytes(num_seqs: int, num_heads: int, head_dim_k: int, head_dim_v: 
 def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seqlens=None, chunk_size: int = 0,
                         dv_slice: int = 0, scale: float = 1.0, out=None, out_dtype=torch.float32,
                         final_state=None, output_final_state: bool = True, workspace=None):
-    """Chunked prefill.  q, k [B, T, H, dk]; v [B, T, H, dv] (bf16 or fp32);
+    """Chunked prefill.  q, k [B, T, Hk, dk]; v [B, T, H, dv] (bf16 or fp32; Hk divides H);
     beta [B, T, H] fp32; log_alpha [B, T, H] (per-head decay) or [B, T, H, dk]
     (per-key-channel decay) fp32; initial_state [N, H, dv, dk] fp32 or None;
     cu_seqlens int32 [N+1] (packed, B == 1) or None.
@@ -119,8 +133,10 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
     Returns (out [B, T, H, dv], final_state [N, H, dv, dk] or None)."""
     lib = load_library()
     dev = q.device
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or beta.shape != (B, T, H):
+        raise ValueError("shapes: q, k [B, T, Hk, dk], v [B, T, H, dv], beta [B, T, H]")
     if log_alpha.dim() == 3:
         gate = GDR_GATE_HEAD
     elif log_alpha.dim() == 4:
@@ -140,7 +156,7 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
     if final_state is None and output_final_state:
         final_state = torch.empty(N, H, dv, dk, dtype=torch.float32, device=dev)
     _need(final_state, "final_state", torch.float32, dev)
-    shape = PrefillShape(B, T, H, dk, dv, N)
+    shape = PrefillShape(B, T, H, dk, dv, N, Hk)
     ws_bytes = lib.gdr_prefill_workspace_bytes(ctypes.byref(shape), gate, _dtype_code(q), int(chunk_size),
                                                int(cu_seqlens is not None))
     if workspace is None:
@@ -156,13 +172,15 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
 
 
 def gdr_decode_step(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, out=None, out_dtype=torch.float32):
-    """Decode step, one token per sequence: q, k [N, H, dk]; v [N, H, dv];
+    """Decode step, one token per sequence: q, k [N, Hk, dk]; v [N, H, dv];
     beta [N, H]; log_alpha [N, H] or [N, H, dk]; state [N, H, dv, dk] fp32
     (updated in place).  Returns out [N, H, dv]."""
     lib = load_library()
     dev = q.device
-    N, H, dk = q.shape
-    dv = v.shape[-1]
+    N, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N or beta.shape != (N, H):
+        raise ValueError("shapes: q, k [N, Hk, dk], v [N, H, dv], beta [N, H]")
     gate = GDR_GATE_HEAD if log_alpha.dim() == 2 else GDR_GATE_CHANNEL
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, q.dtype, dev)
@@ -172,10 +190,48 @@ def gdr_decode_step(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, out=
     if out is None:
         out = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
     _need(out, "out", None, dev)
-    _check(lib.gdr_decode_step(N, H, dk, dv, gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+    _check(lib.gdr_decode_step(N, H, Hk, dk, dv, gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                _ptr(log_alpha), _ptr(state), float(scale), _ptr(out), _stream(dev)))
+    return out
+
+
+def gdr_decode_tokens(q, k, v, beta, log_alpha, state_pool, *, num_tokens=None, num_commit=None,
+                      state_slots=None, scale: float = 1.0, out=None, out_dtype=torch.float32):
+    """Up to K tokens per sequence from a pool of states: q, k [N, K, Hk, dk];
+    v [N, K, H, dv]; beta [N, K, H]; log_alpha [N, K, H] or [N, K, H, dk];
+    state_pool [P, H, dv, dk] fp32; num_tokens, num_commit, state_slots int32
+    [N] device tensors or None (K tokens, all committed, slot n).  Runs each
+    sequence's tokens from its slot, writes out [N, K, H, dv] for its tokens
+    and keeps in the slot the state after its first num_commit tokens (0: the
+    slot is left as it was).  Returns out."""
+    lib = load_library()
+    dev = q.device
+    N, K, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (N, K) or beta.shape != (N, K, H):
+        raise ValueError("shapes: q, k [N, K, Hk, dk], v [N, K, H, dv], beta [N, K, H]")
+    gate = GDR_GATE_HEAD if log_alpha.dim() == 3 else GDR_GATE_CHANNEL
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, q.dtype, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(state_pool, "state_pool", torch.float32, dev)
+    for t, nm in ((num_tokens, "num_tokens"), (num_commit, "num_commit"), (state_slots, "state_slots")):
+        _need(t, nm, torch.int32, dev)
+        if t is not None and t.shape != (N,):
+            raise ValueError(f"{nm} must have shape [{N}]")
+    if state_pool.dim() != 4 or state_pool.shape[1:] != (H, dv, dk):
+        raise ValueError(f"state_pool must be [P, {H}, {dv}, {dk}]")
+    if out is None:
+        out = torch.empty(N, K, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", None, dev)
+    _check(lib.gdr_decode_tokens(N, K, H, Hk, dk, dv, gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(num_tokens), _ptr(num_commit),
+                                 _ptr(state_slots), _ptr(state_pool), int(state_pool.shape[0]), float(scale),
+                                 _ptr(out), _stream(dev)))
     return out
 
 
 prefill_chunked = gdr_prefill_chunked
 decode_step = gdr_decode_step
+decode_tokens = gdr_decode_tokens

@@ -33,6 +33,6 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ int div_up(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int div_up(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace gdr

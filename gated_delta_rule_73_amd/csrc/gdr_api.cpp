@@ -119,6 +119,84 @@ PrefillWorkspace fit_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, 
 // automatic chunk size: 32 tokens where compiled, else 16
 int auto_chunk(bool bf16, bool kda, int dk) { return gdr::prefill_supported(bf16, kda, dk, 16, 32) ? 32 : 16; }
 
+
+constexpr int kMaxDecodeTokens = 64;
+
+// num_qk_heads: 0 means num_heads; else it must divide num_heads.
+gdr_status resolve_qk_heads(int32_t num_heads, int32_t num_qk_heads, int &hk) {
+    hk = num_qk_heads ? num_qk_heads : num_heads;
+    if (hk < 1 || hk > num_heads || num_heads % hk != 0)
+        return fail(GDR_ERROR_INVALID_VALUE, "num_qk_heads %d does not divide num_heads %d", num_qk_heads, num_heads);
+    return GDR_SUCCESS;
+}
+
+// Validation shared by the one-token and the multi-token decode: K tokens
+// per sequence, `state` holding num_slots (sequence or slot) states.  Fills
+// `a` on success.
+gdr_status check_decode(int32_t num_seqs, int32_t K, int32_t num_heads, int32_t num_qk_heads, int32_t dk, int32_t dv,
+                        gdr_gate gate, gdr_dtype qkv_dtype, gdr_dtype gate_dtype, gdr_dtype out_dtype, const void *q,
+                        const void *k, const void *v, const void *beta, const void *log_alpha,
+                        const int32_t *num_tokens, const int32_t *num_commit, const int32_t *slots, float *state,
+                        int32_t num_slots, float scale, void *out, gdr::DecodeArgs &a) {
+    if (num_seqs < 0 || num_heads < 1 || dk < 1 || dv < 1)
+        return fail(GDR_ERROR_INVALID_VALUE, "bad shape (num_seqs=%d heads=%d dk=%d dv=%d)", num_seqs, num_heads, dk,
+                    dv);
+    int hk = 0;
+    if (resolve_qk_heads(num_heads, num_qk_heads, hk) != GDR_SUCCESS) return GDR_ERROR_INVALID_VALUE;
+    if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
+    if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
+        return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d out=%d)", (int)qkv_dtype,
+                    (int)gate_dtype, (int)out_dtype);
+    if (gate_dtype != GDR_F32) return fail(GDR_ERROR_NOT_SUPPORTED, "gates must be fp32");
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_k %d not in {16, 32, 64, 128}", dk);
+    if (dv % 4 != 0 || dv > 256) return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_v %d not a multiple of 4 <= 256", dv);
+    if ((int64_t)num_seqs * K * num_heads > INT32_MAX || (int64_t)num_slots * num_heads > INT32_MAX)
+        return fail(GDR_ERROR_INVALID_VALUE, "too many heads");
+    if (num_seqs == 0) return ok();
+    if (!q || !k || !v || !beta || !log_alpha || !state || !out)
+        return fail(GDR_ERROR_INVALID_VALUE, "q, k, v, beta, log_alpha, state and out must be non-NULL");
+    const bool kda = gate == GDR_GATE_CHANNEL;
+    const size_t es = dsize(qkv_dtype);
+    const size_t rows = (size_t)num_seqs * K;   // token rows
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(log_alpha, kda ? 16 : 4) ||
+        !aligned(v, es) || !aligned(out, dsize(out_dtype)) || !aligned(beta, 4) || !aligned(num_tokens, 4) ||
+        !aligned(num_commit, 4) || !aligned(slots, 4))
+        return fail(GDR_ERROR_INVALID_VALUE, "misaligned pointer (q/k/state need 16 bytes)");
+    const Range in[] = {range("q", q, rows * hk * dk * es), range("k", k, rows * hk * dk * es),
+                        range("v", v, rows * num_heads * dv * es), range("beta", beta, rows * num_heads * 4),
+                        range("log_alpha", log_alpha, rows * num_heads * (kda ? dk : 1) * 4),
+                        range("num_tokens", num_tokens, num_tokens ? 4 * (size_t)num_seqs : 0),
+                        range("num_commit", num_commit, num_commit ? 4 * (size_t)num_seqs : 0),
+                        range("state_slots", slots, slots ? 4 * (size_t)num_seqs : 0)};
+    const Range rs = range("state", state, (size_t)num_slots * num_heads * dv * dk * 4);
+    const Range ro = range("out", out, rows * num_heads * dv * dsize(out_dtype));
+    for (const Range &r : in) {
+        if (overlaps(rs, r)) return fail(GDR_ERROR_INVALID_VALUE, "state overlaps %s", r.name);
+        if (overlaps(ro, r)) return fail(GDR_ERROR_INVALID_VALUE, "out overlaps %s", r.name);
+    }
+    if (overlaps(rs, ro)) return fail(GDR_ERROR_INVALID_VALUE, "out overlaps state");
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_qk_heads = hk;
+    a.dk = dk;
+    a.dv = dv;
+    a.kda = kda;
+    a.bf16 = qkv_dtype == GDR_BF16;
+    a.out_bf16 = out_dtype == GDR_BF16;
+    a.q = q; a.k = k; a.v = v;
+    a.beta = static_cast<const float *>(beta);
+    a.log_alpha = static_cast<const float *>(log_alpha);
+    a.state = state;
+    a.scale = scale;
+    a.out = out;
+    a.max_tokens = K;
+    a.num_slots = num_slots;
+    a.num_tokens = num_tokens;
+    a.num_commit = num_commit;
+    a.slots = slots;
+    return ok();
+}
 }  // namespace
 
 extern "C" {
@@ -166,6 +244,8 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
         return fail(GDR_ERROR_INVALID_VALUE,
                     "bad shape (batch=%d seqlen=%d heads=%d dk=%d dv=%d num_seqs=%d)", s.batch, s.seqlen,
                     s.num_heads, s.head_dim_k, s.head_dim_v, s.num_seqs);
+    int hk = 0;
+    if (resolve_qk_heads(s.num_heads, s.num_qk_heads, hk) != GDR_SUCCESS) return GDR_ERROR_INVALID_VALUE;
     if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
     if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
         return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d out=%d)", (int)qkv_dtype,
@@ -205,7 +285,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
                     bf16 ? "bf16" : "fp32", dk, DVS, C);
 
     const size_t es = dsize(qkv_dtype);
-    const size_t nq = (size_t)tokens * s.num_heads * dk, nv = (size_t)tokens * s.num_heads * dv;
+    const size_t nq = (size_t)tokens * hk * dk, nv = (size_t)tokens * s.num_heads * dv;
     const size_t ng = (size_t)tokens * s.num_heads;
     const size_t nla = kda ? ng * dk : ng;
     const size_t nstate = (size_t)s.num_seqs * s.num_heads * dv * dk;
@@ -247,6 +327,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     a.batch = s.batch;
     a.seqlen = s.seqlen;
     a.num_heads = s.num_heads;
+    a.num_qk_heads = hk;
     a.dk = dk;
     a.dv = dv;
     a.num_seqs = s.num_seqs;
@@ -274,58 +355,36 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     return launch_status(gdr::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_chunked");
 }
 
-gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
-                           gdr_gate gate, gdr_dtype qkv_dtype, gdr_dtype gate_dtype, gdr_dtype out_dtype,
-                           const void *q, const void *k, const void *v, const void *beta, const void *log_alpha, float *state, float scale,
-                           void *out, void *hip_stream) {
-    if (num_seqs < 0 || num_heads < 1 || head_dim_k < 1 || head_dim_v < 1)
-        return fail(GDR_ERROR_INVALID_VALUE, "bad shape (num_seqs=%d heads=%d dk=%d dv=%d)", num_seqs, num_heads,
-                    head_dim_k, head_dim_v);
-    if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
-    if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
-        return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d out=%d)", (int)qkv_dtype,
-                    (int)gate_dtype, (int)out_dtype);
-    if (gate_dtype != GDR_F32) return fail(GDR_ERROR_NOT_SUPPORTED, "gates must be fp32");
-    const int dk = head_dim_k, dv = head_dim_v;
-    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128))
-        return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_k %d not in {16, 32, 64, 128}", dk);
-    if (dv % 4 != 0 || dv > 256) return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_v %d not a multiple of 4 <= 256", dv);
-    if ((int64_t)num_seqs * num_heads > INT32_MAX) return fail(GDR_ERROR_INVALID_VALUE, "too many heads");
-    if (num_seqs == 0) return ok();
-    if (!q || !k || !v || !beta || !log_alpha || !state || !out)
-        return fail(GDR_ERROR_INVALID_VALUE, "q, k, v, beta, log_alpha, state and out must be non-NULL");
-    const bool kda = gate == GDR_GATE_CHANNEL;
-    const bool bf16 = qkv_dtype == GDR_BF16;
-    const size_t es = dsize(qkv_dtype);
-    const size_t units = (size_t)num_seqs * num_heads;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(log_alpha, kda ? 16 : 4) ||
-        !aligned(v, es) || !aligned(out, dsize(out_dtype)) || !aligned(beta, 4))
-        return fail(GDR_ERROR_INVALID_VALUE, "misaligned pointer (q/k/state need 16 bytes)");
-    const Range in[] = {range("q", q, units * dk * es), range("k", k, units * dk * es),
-                        range("v", v, units * dv * es), range("beta", beta, units * 4),
-                        range("log_alpha", log_alpha, units * (kda ? dk : 1) * 4)};
-    const Range rs = range("state", state, units * dv * dk * 4);
-    const Range ro = range("out", out, units * dv * dsize(out_dtype));
-    for (const Range &r : in) {
-        if (overlaps(rs, r)) return fail(GDR_ERROR_INVALID_VALUE, "state overlaps %s", r.name);
-        if (overlaps(ro, r)) return fail(GDR_ERROR_INVALID_VALUE, "out overlaps %s", r.name);
-    }
-    if (overlaps(rs, ro)) return fail(GDR_ERROR_INVALID_VALUE, "out overlaps state");
+gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t num_qk_heads, int32_t head_dim_k,
+                           int32_t head_dim_v, gdr_gate gate, gdr_dtype qkv_dtype, gdr_dtype gate_dtype,
+                           gdr_dtype out_dtype, const void *q, const void *k, const void *v, const void *beta,
+                           const void *log_alpha, float *state, float scale, void *out, void *hip_stream) {
     gdr::DecodeArgs a{};
-    a.num_seqs = num_seqs;
-    a.num_heads = num_heads;
-    a.dk = dk;
-    a.dv = dv;
-    a.kda = kda;
-    a.bf16 = bf16;
-    a.out_bf16 = out_dtype == GDR_BF16;
-    a.q = q; a.k = k; a.v = v;
-    a.beta = static_cast<const float *>(beta);
-    a.log_alpha = static_cast<const float *>(log_alpha);
-    a.state = state;
-    a.scale = scale;
-    a.out = out;
+    const gdr_status st = check_decode(num_seqs, 1, num_heads, num_qk_heads, head_dim_k, head_dim_v, gate, qkv_dtype,
+                                       gate_dtype, out_dtype, q, k, v, beta, log_alpha, nullptr, nullptr, nullptr,
+                                       state, num_seqs, scale, out, a);
+    if (st != GDR_SUCCESS || num_seqs == 0) return st;
     return launch_status(gdr::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "gdr_decode_step");
+}
+
+gdr_status gdr_decode_tokens(int32_t num_seqs, int32_t max_tokens, int32_t num_heads, int32_t num_qk_heads,
+                             int32_t head_dim_k, int32_t head_dim_v, gdr_gate gate, gdr_dtype qkv_dtype,
+                             gdr_dtype gate_dtype, gdr_dtype out_dtype, const void *q, const void *k,
+                             const void *v, const void *beta, const void *log_alpha, const int32_t *num_tokens,
+                             const int32_t *num_commit, const int32_t *state_slots, float *state_pool,
+                             int32_t num_slots, float scale, void *out, void *hip_stream) {
+    if (max_tokens < 1 || max_tokens > kMaxDecodeTokens)
+        return fail(GDR_ERROR_INVALID_VALUE, "max_tokens %d not in [1, %d]", max_tokens, kMaxDecodeTokens);
+    if (num_slots < 0) return fail(GDR_ERROR_INVALID_VALUE, "num_slots %d < 0", num_slots);
+    if (!state_slots && num_slots < num_seqs)
+        return fail(GDR_ERROR_INVALID_VALUE, "without state_slots the pool needs num_seqs slots (%d < %d)", num_slots,
+                    num_seqs);
+    gdr::DecodeArgs a{};
+    const gdr_status st = check_decode(num_seqs, max_tokens, num_heads, num_qk_heads, head_dim_k, head_dim_v, gate,
+                                       qkv_dtype, gate_dtype, out_dtype, q, k, v, beta, log_alpha, num_tokens,
+                                       num_commit, state_slots, state_pool, num_slots, scale, out, a);
+    if (st != GDR_SUCCESS || num_seqs == 0) return st;
+    return launch_status(gdr::launch_decode_tokens(a, static_cast<hipStream_t>(hip_stream)), "gdr_decode_tokens");
 }
 
 }  // extern "C"

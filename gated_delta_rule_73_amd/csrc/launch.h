@@ -8,18 +8,22 @@
 
 namespace gdr {
 
+// num_heads value heads; value head h reads q/k head h / (num_heads / num_qk_heads)
 struct DecodeArgs {
-    int num_seqs, num_heads, dk, dv;
+    int num_seqs, num_heads, num_qk_heads, dk, dv;
     bool kda, bf16, out_bf16;
     const void *q, *k, *v;
     const float *beta, *log_alpha;
-    float *state;
+    float *state;                   // decode step: [num_seqs, H, dv, dk]; multi-token: the slot pool
     float scale;
     void *out;
+    // multi-token decode only
+    int max_tokens, num_slots;
+    const int32_t *num_tokens, *num_commit, *slots;   // [num_seqs] each, or NULL
 };
 
 struct PrefillArgs {
-    int batch, seqlen, num_heads, dk, dv, num_seqs;
+    int batch, seqlen, num_heads, num_qk_heads, dk, dv, num_seqs;
     bool kda, bf16, out_bf16;
     int chunk, dv_slice;            // resolved (non-zero) values
     const void *q, *k, *v;
@@ -49,6 +53,7 @@ constexpr size_t chunk_record_stride(int dk, int chunk, bool kda, int es) {
 }
 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t st);
+hipError_t launch_decode_tokens(const DecodeArgs &p, hipStream_t st);
 
 // True when a prefill kernel is compiled for this combination.
 bool prefill_supported(bool bf16, bool kda, int dk, int dv_slice, int chunk);

@@ -348,6 +348,7 @@ struct PrepSmem {
 
 struct PrepKArgs {
     int T, H, num_seqs;
+    int HK, G;                   // q/k heads; value head h reads q/k head h / G
     long num_records;            // chunk slots x heads in this launch
     int j0, seg_chunks;          // dense: chunks [j0, j0 + seg_chunks) of every sequence
     float scale;                 // readout factor, folded into Q e^g and M
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
             kr[x] = IV{};
             qr[x] = IV{};
             if (e < C * DK / EPV && t < nv) {
-                const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
+                const size_t off = ((size_t)(t0 + t) * p.HK + h / p.G) * DK + c;
                 kr[x] = *reinterpret_cast<const IV *>(gk + off);
                 qr[x] = *reinterpret_cast<const IV *>(gq + off);
             }
@@ -1138,6 +1139,8 @@ hipError_t launch_prep(const PrefillArgs &a, int j0, int seg_chunks, char *rec, 
     PrepKArgs pk;
     pk.T = a.seqlen;
     pk.H = a.num_heads;
+    pk.HK = a.num_qk_heads;
+    pk.G = a.num_heads / a.num_qk_heads;
     pk.num_seqs = a.num_seqs;
     pk.j0 = j0;
     pk.seg_chunks = seg_chunks;

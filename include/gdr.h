@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 typedef enum gdr_status {
     GDR_SUCCESS = 0,
@@ -82,6 +82,13 @@ typedef enum gdr_gate {
  *                cu_seqlens = NULL.
  *  Packed batch: batch = 1, seqlen = total tokens, num_seqs = N and
  *                cu_seqlens[N+1] gives each sequence's token range.
+ *  num_heads is the number of value heads: one state, one write strength and
+ *  one decay per value head.  num_qk_heads query-key heads are shared by
+ *  groups of G = num_heads / num_qk_heads consecutive value heads: value head
+ *  h reads q and k of head h / G (page "How the New Flash Models Work...",
+ *  section "The two stacks, layer by layer": the Gated DeltaNet layers have
+ *  16 key heads and 48 value heads; the state-size table counts one state per
+ *  value head).  num_qk_heads = 0 means num_heads (no grouping).
  */
 typedef struct gdr_prefill_shape {
     int32_t batch;
@@ -90,6 +97,7 @@ typedef struct gdr_prefill_shape {
     int32_t head_dim_k;
     int32_t head_dim_v;
     int32_t num_seqs;
+    int32_t num_qk_heads;
 } gdr_prefill_shape;
 
 /*
@@ -126,7 +134,7 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  *  gate_dtype     dtype of beta and log_alpha: GDR_F32.
  *  out_dtype      dtype of out: GDR_F32 or GDR_BF16 (independent of q/k/v;
  *                 bf16 outputs are rounded to nearest even from fp32).
- *  q, k           [batch, seqlen, num_heads, head_dim_k]
+ *  q, k           [batch, seqlen, num_qk_heads, head_dim_k]
  *  v              [batch, seqlen, num_heads, head_dim_v]
  *  beta           [batch, seqlen, num_heads]           write strengths (any finite value)
  *  log_alpha      [batch, seqlen, num_heads]           (GDR_GATE_HEAD)
@@ -149,7 +157,8 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  *                 bytes (may be NULL when that is 0), 256-byte aligned.
  *  hip_stream     hipStream_t to enqueue on.
  * Limits: head_dim_k in {16, 32, 64, 128} (bf16: {32, 64, 128}); head_dim_v
- * a multiple of 16 up to 256; the q/k/v/out/state base pointers 16-byte
+ * a multiple of 16 up to 256; num_heads a multiple of num_qk_heads (when
+ * that is not 0); the q/k/v/out/state base pointers 16-byte
  * aligned; beta 4-byte aligned; log_alpha 16-byte aligned for
  * GDR_GATE_CHANNEL, else 4-byte aligned.  Per-channel decay: the log-decay
  * summed over one chunk must stay above about -170 in every channel (the
@@ -174,7 +183,10 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate,
  * (sequence, head) state once, applies the decay, the erase-then-write update
  * and the readout, and writes the state back in place.
  *
- *  q, k       [num_seqs, num_heads, head_dim_k]   dtype qkv_dtype
+ *  num_heads     value heads (states, gates, v, out); num_qk_heads query-key
+ *                heads shared by groups of value heads as in gdr_prefill_shape
+ *                (0 = num_heads)
+ *  q, k       [num_seqs, num_qk_heads, head_dim_k] dtype qkv_dtype
  *  v          [num_seqs, num_heads, head_dim_v]   dtype qkv_dtype
  *  beta       [num_seqs, num_heads]               fp32
  *  log_alpha  [num_seqs, num_heads] (GDR_GATE_HEAD) or
@@ -186,11 +198,57 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate,
  * Limits: head_dim_k in {16, 32, 64, 128}; head_dim_v a multiple of 4 up to
  * 256; base pointers 16-byte aligned (gates 4-byte).
  */
-gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k,
+gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t num_qk_heads, int32_t head_dim_k,
                            int32_t head_dim_v, gdr_gate gate, gdr_dtype qkv_dtype,
                            gdr_dtype gate_dtype, gdr_dtype out_dtype, const void *q, const void *k,
                            const void *v, const void *beta, const void *log_alpha,
                            float *state, float scale, void *out, void *hip_stream);
+
+/*
+ * Multi-token decode: up to max_tokens new tokens for each of num_seqs
+ * sequences whose states live in a pool of slots.  For the speculative
+ * decoding both models serve with (page "How the New Flash Models Work...",
+ * section "Decoding several tokens per pass": a draft of several tokens is
+ * verified in one pass of the main model) and the replay of accepted tokens
+ * that the GLM serving stack names (page "Qwen3.8-Flash-Next and GLM-5.3-Flash
+ * share a 3:1 long-context pattern", section "GLM's serving design is
+ * explicitly disaggregated": ReplaySSM).
+ *
+ * For sequence n with slot s = state_slots[n] (n when state_slots is NULL),
+ * T_n = num_tokens[n] (max_tokens when NULL) and C_n = num_commit[n] (T_n
+ * when NULL), the call runs the recurrence over tokens 0 .. T_n - 1 starting
+ * from state_pool[s], writes out[n, t] for every t < T_n, and stores back
+ * into state_pool[s] the state after the first C_n tokens only:
+ *   C_n = T_n        plain multi-token decode;
+ *   C_n = 0          verify a draft: outputs only, the slot is not written;
+ *   0 < C_n < T_n    replay the C_n tokens accepted in the previous step, then
+ *                    verify a new draft, with one read and one write of the
+ *                    state (the caller ignores the replayed tokens' outputs).
+ * Device values out of range are clamped, not rejected (they cannot be read
+ * on the host): T_n to [0, max_tokens], C_n to [0, T_n]; a sequence whose slot
+ * is negative or >= num_slots is skipped (nothing read or written, its outputs
+ * left as they were), which is how padding entries of a batch are marked.
+ * Two sequences of one call must not share a slot (their updates would race).
+ *
+ *  q, k         [num_seqs, max_tokens, num_qk_heads, head_dim_k]  qkv_dtype
+ *  v            [num_seqs, max_tokens, num_heads, head_dim_v]     qkv_dtype
+ *  beta         [num_seqs, max_tokens, num_heads]                 fp32
+ *  log_alpha    [num_seqs, max_tokens, num_heads] (GDR_GATE_HEAD) or
+ *               [num_seqs, max_tokens, num_heads, head_dim_k]     fp32
+ *  num_tokens, num_commit, state_slots   int32 [num_seqs] device arrays or NULL
+ *  state_pool   [num_slots, num_heads, head_dim_v, head_dim_k] fp32, read and
+ *               written in place (must not overlap any other argument)
+ *  out          [num_seqs, max_tokens, num_heads, head_dim_v]  out_dtype;
+ *               rows t >= T_n are not written
+ * Limits: as gdr_decode_step; 1 <= max_tokens <= 64.
+ */
+gdr_status gdr_decode_tokens(int32_t num_seqs, int32_t max_tokens, int32_t num_heads, int32_t num_qk_heads,
+                             int32_t head_dim_k, int32_t head_dim_v, gdr_gate gate, gdr_dtype qkv_dtype,
+                             gdr_dtype gate_dtype, gdr_dtype out_dtype, const void *q, const void *k,
+                             const void *v, const void *beta, const void *log_alpha,
+                             const int32_t *num_tokens, const int32_t *num_commit,
+                             const int32_t *state_slots, float *state_pool, int32_t num_slots,
+                             float scale, void *out, void *hip_stream);
 
 /* Bytes of fp32 recurrent state for num_seqs x num_heads heads of d_v x d_k
  * (the per-layer state the pages size in their state-size table). */

@@ -11,6 +11,14 @@ equations); see the C file's header for the step order.
 
 Every input is converted to fp64 exactly (bf16 and fp32 values are exactly
 representable), so the oracle sees the same numbers as the GPU path.
+
+Grouped value heads (page "How the New Flash Models Work...", section "The two
+stacks, layer by layer": 16 key heads and 48 value heads in the Gated DeltaNet
+layers; the state-size table of section "Linear attention..." counts one state
+per value head): q and k may carry Hk heads while v, the gates and the states
+carry H, a multiple of Hk.  Value head h uses q/k head h // (H // Hk), i.e.
+each q/k head is repeated for its group of consecutive value heads before the
+recurrence runs -- which is all that grouping means.
 """
 from __future__ import annotations
 
@@ -76,12 +84,24 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _expand_groups(q, k, H):
+    """q/k with Hk heads on axis -2 -> H heads, value head h taking q/k head
+    h // (H // Hk)."""
+    Hk = q.shape[-2]
+    if Hk == H:
+        return q, k
+    if Hk < 1 or H % Hk:
+        raise ValueError(f"{Hk} q/k heads do not divide {H} value heads")
+    return np.repeat(q, H // Hk, axis=-2), np.repeat(k, H // Hk, axis=-2)
+
+
 def recurrence(q, k, v, beta, log_alpha, *, initial_state=None, seq_bounds=None,
                scale: float = 1.0, num_threads: int = 0):
     """Run the sequential fp64 recurrence.
 
-    Dense form:  q, k [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
-                 log_alpha [B, T, H] (per-head decay) or [B, T, H, dk] (per-channel).
+    Dense form:  q, k [B, T, Hk, dk]; v [B, T, H, dv]; beta [B, T, H];
+                 log_alpha [B, T, H] (per-head decay) or [B, T, H, dk] (per-channel);
+                 Hk divides H (Hk < H: grouped value heads, see the module text).
     Packed form: same with B == 1 and ``seq_bounds`` = the N+1 token offsets.
     initial_state [N, H, dv, dk] or None (zeros).
 
@@ -89,6 +109,9 @@ def recurrence(q, k, v, beta, log_alpha, *, initial_state=None, seq_bounds=None,
     """
     q, k, v, beta, log_alpha = (_f64(x) for x in (q, k, v, beta, log_alpha))
     initial_state = _f64(initial_state)
+    if k.shape != q.shape or q.ndim != 4 or v.ndim != 4:
+        raise ValueError("q and k must be [B, T, Hk, dk], v [B, T, H, dv]")
+    q, k = _expand_groups(q, k, v.shape[2])
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
@@ -123,7 +146,7 @@ def recurrence(q, k, v, beta, log_alpha, *, initial_state=None, seq_bounds=None,
 
 
 def decode(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, num_threads: int = 0):
-    """One token per sequence: q, k [N, H, dk]; v [N, H, dv]; beta [N, H];
+    """One token per sequence: q, k [N, Hk, dk]; v [N, H, dv]; beta [N, H];
     log_alpha [N, H] or [N, H, dk]; state [N, H, dv, dk].
     Returns (out [N, H, dv], new_state) -- the oracle recurrence with T = 1."""
     q, k, v, beta, log_alpha = (_f64(x) for x in (q, k, v, beta, log_alpha))
@@ -135,3 +158,62 @@ def decode(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, num_threads: 
         scale=scale, num_threads=num_threads,
     )
     return out[:, 0], final
+
+
+def decode_tokens(q, k, v, beta, log_alpha, state_pool, *, num_tokens=None, num_commit=None,
+                  state_slots=None, scale: float = 1.0, num_threads: int = 0):
+    """Several tokens per sequence from a pool of state slots (speculative
+    verify with replay of the accepted tokens: page "How the New Flash Models
+    Work...", section "Decoding several tokens per pass"; page "Qwen3.8-Flash-
+    Next and GLM-5.3-Flash share a 3:1 long-context pattern", section "GLM's
+    serving design is explicitly disaggregated", which names ReplaySSM).
+
+    q, k [N, K, Hk, dk]; v [N, K, H, dv]; beta [N, K, H]; log_alpha [N, K, H]
+    or [N, K, H, dk]; state_pool [P, H, dv, dk]; num_tokens, num_commit,
+    state_slots: length-N integer arrays or None (K; T_n; n).
+
+    For each sequence n whose slot s = state_slots[n] lies in [0, P): with
+    T = clamp(num_tokens[n], 0, K) and C = clamp(num_commit[n], 0, T), run the
+    recurrence over its tokens 0..C-1 from state_pool[s], then over tokens
+    C..T-1 from the state so reached; the outputs of all T tokens are written
+    and state_pool[s] becomes the state after token C-1 (unchanged if C = 0).
+    Sequences with a slot outside [0, P) are skipped.
+
+    Returns (out [N, K, H, dv], written [N, K] bool, new_pool [P, H, dv, dk]);
+    rows that are not written hold 0 in ``out``.
+    """
+    q, k, v, beta, log_alpha, pool = (_f64(x) for x in (q, k, v, beta, log_alpha, state_pool))
+    N, K = q.shape[:2]
+    H, dv = v.shape[2], v.shape[3]
+    P = pool.shape[0]
+
+    def ints(a, default):
+        if a is None:
+            return np.asarray(default, dtype=np.int64)
+        if hasattr(a, "detach"):
+            a = a.detach().cpu().numpy()
+        return np.asarray(a, dtype=np.int64)
+
+    slots = ints(state_slots, np.arange(N))
+    T = np.clip(ints(num_tokens, np.full(N, K)), 0, K)
+    C = np.clip(ints(num_commit, T), 0, T)
+    out = np.zeros((N, K, H, dv))
+    written = np.zeros((N, K), dtype=bool)
+    new_pool = pool.copy()
+    for n in range(N):
+        s = int(slots[n])
+        if s < 0 or s >= P or T[n] == 0:
+            continue
+        c, t = int(C[n]), int(T[n])
+        tok = lambda a, lo, hi: a[n:n + 1, lo:hi]
+        args = lambda lo, hi: [tok(a, lo, hi) for a in (q, k, v, beta, log_alpha)]
+        S = pool[s:s + 1]
+        if c > 0:
+            o1, S = recurrence(*args(0, c), initial_state=S, scale=scale, num_threads=num_threads)
+            out[n, :c] = o1[0]
+            new_pool[s] = S[0]
+        if t > c:
+            o2, _ = recurrence(*args(c, t), initial_state=S, scale=scale, num_threads=num_threads)
+            out[n, c:t] = o2[0]
+        written[n, :t] = True
+    return out, written, new_pool

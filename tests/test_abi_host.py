@@ -26,14 +26,14 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = gdr.load_library()
     names = declared_functions()
-    assert "gdr_prefill_chunked" in names and "gdr_decode_step" in names
+    assert {"gdr_prefill_chunked", "gdr_decode_step", "gdr_decode_tokens"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_abi_version_and_status_strings():
     lib = gdr.load_library()
-    assert lib.gdr_abi_version() == 2
+    assert lib.gdr_abi_version() == 3 == gdr.ABI_VERSION
     assert lib.gdr_status_string(0) == b"success"
     assert lib.gdr_status_string(2) == b"not supported"
 
@@ -54,7 +54,7 @@ A = 0x10000000  # fake, suitably aligned "device" addresses; never dereferenced
 MB = 1 << 20
 
 
-def _prefill(shape=(1, 64, 2, 64, 64, 1), gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + 8 * MB, v=A + 16 * MB, beta=A + 24 * MB,
+def _prefill(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + 8 * MB, v=A + 16 * MB, beta=A + 24 * MB,
              la=A + 25 * MB, s0=None, cu=None, chunk=0, dvs=0, out=A + 32 * MB, fin=None, ws=A + 48 * MB, wsb=16 * MB):
     lib = gdr.load_library()
     sh = gdr.PrefillShape(*shape)
@@ -64,32 +64,48 @@ def _prefill(shape=(1, 64, 2, 64, 64, 1), gate=0, qkv=1, gdt=0, odt=0, q=A, k=A 
     return st, lib.gdr_last_error().decode()
 
 
-def _decode(N=4, H=2, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + MB, v=A + 2 * MB, beta=A + 3 * MB,
+def _decode(N=4, H=2, Hk=0, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + MB, v=A + 2 * MB, beta=A + 3 * MB,
             la=A + 4 * MB, state=A + 8 * MB, out=A + 64 * MB):
     lib = gdr.load_library()
     v_ = lambda x: None if x is None else ctypes.c_void_p(x)
-    st = lib.gdr_decode_step(N, H, dk, dv, gate, qkv, gdt, odt, v_(q), v_(k), v_(v), v_(beta), v_(la), v_(state), 1.0,
-                             v_(out), None)
+    st = lib.gdr_decode_step(N, H, Hk, dk, dv, gate, qkv, gdt, odt, v_(q), v_(k), v_(v), v_(beta), v_(la), v_(state),
+                             1.0, v_(out), None)
+    return st, lib.gdr_last_error().decode()
+
+
+def _decode_tokens(N=4, K=4, H=2, Hk=0, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + MB, v=A + 2 * MB,
+                   beta=A + 3 * MB, la=A + 4 * MB, ntok=None, ncom=None, slots=None, pool=A + 8 * MB, P=4,
+                   out=A + 64 * MB):
+    lib = gdr.load_library()
+    v_ = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_decode_tokens(N, K, H, Hk, dk, dv, gate, qkv, gdt, odt, v_(q), v_(k), v_(v), v_(beta), v_(la),
+                               v_(ntok), v_(ncom), v_(slots), v_(pool), P, 1.0, v_(out), None)
     return st, lib.gdr_last_error().decode()
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(shape=(0, 64, 2, 64, 64, 0)), 1, "bad shape"),
-    (dict(shape=(1, 64, 0, 64, 64, 1)), 1, "bad shape"),
+    (dict(shape=(0, 64, 2, 64, 64, 0, 0)), 1, "bad shape"),
+    (dict(shape=(1, 64, 0, 64, 64, 1, 0)), 1, "bad shape"),
+    (dict(shape=(1, 64, 6, 64, 64, 1, 4)), 1, "num_qk_heads 4 does not divide"),
+    (dict(shape=(1, 64, 2, 64, 64, 1, 3)), 1, "does not divide"),
+    (dict(shape=(1, 64, 2, 64, 64, 1, -1)), 1, "does not divide"),
+    # q, k hold 2 heads (16 KiB each) when 6 value heads share them, 6 (48 KiB) otherwise
+    (dict(shape=(1, 64, 6, 64, 64, 1, 2), k=A + 16 * 1024, out=A + 32 * 1024), 0, None),
+    (dict(shape=(1, 64, 6, 64, 64, 1, 0), k=A + 48 * 1024, out=A + 32 * 1024), 1, "out overlaps q"),
     (dict(gate=7), 1, "gate"),
     (dict(qkv=5), 1, "dtype"),
     (dict(odt=9), 1, "dtype"),
     (dict(gdt=1), 2, "fp32"),
-    (dict(shape=(1, 64, 2, 48, 64, 1)), 2, "head_dim_k"),
-    (dict(shape=(1, 64, 2, 64, 40, 1)), 2, "head_dim_v"),
-    (dict(shape=(1, 64, 2, 16, 64, 1)), 2, "no prefill kernel"),        # bf16 needs dk >= 32
+    (dict(shape=(1, 64, 2, 48, 64, 1, 0)), 2, "head_dim_k"),
+    (dict(shape=(1, 64, 2, 64, 40, 1, 0)), 2, "head_dim_v"),
+    (dict(shape=(1, 64, 2, 16, 64, 1, 0)), 2, "no prefill kernel"),        # bf16 needs dk >= 32
     (dict(chunk=48), 1, "chunk_size"),
     (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 runs 32-token chunks
     (dict(chunk=64), 2, "no prefill kernel"),
     (dict(dvs=48), 1, "dv_slice"),
-    (dict(shape=(1, 64, 2, 64, 48, 1), dvs=32), 1, "does not divide"),
-    (dict(shape=(2, 64, 2, 64, 64, 1)), 1, "num_seqs == batch"),
-    (dict(shape=(2, 64, 2, 64, 64, 2), cu=A + 40 * MB), 1, "batch == 1"),
+    (dict(shape=(1, 64, 2, 64, 48, 1, 0), dvs=32), 1, "does not divide"),
+    (dict(shape=(2, 64, 2, 64, 64, 1, 0)), 1, "num_seqs == batch"),
+    (dict(shape=(2, 64, 2, 64, 64, 2, 0), cu=A + 40 * MB), 1, "batch == 1"),
     (dict(q=None), 1, "non-NULL"),
     (dict(q=A + 2), 1, "16-byte aligned"),
     (dict(out=A + 8 * MB + 64), 1, "out overlaps k"),
@@ -102,7 +118,7 @@ def _decode(N=4, H=2, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=0, q=A, k=A + MB, 
     (dict(ws=None), 1, "workspace is NULL"),
     (dict(ws=A + 48 * MB + 4), 1, "256-byte"),
     (dict(ws=A + 24 * MB), 1, "workspace overlaps beta"),
-    (dict(shape=(1, 64, 2, 64, 64, 1), gate=1, la=A + 25 * MB + 4), 1, "log_alpha 16-byte"),
+    (dict(shape=(1, 64, 2, 64, 64, 1, 0), gate=1, la=A + 25 * MB + 4), 1, "log_alpha 16-byte"),
 ])
 def test_prefill_rejects(kw, status, msg):
     if status == 0:
@@ -122,7 +138,7 @@ def test_prefill_workspace_size():
     spare chunk slot per sequence."""
     lib = gdr.load_library()
     f = lib.gdr_prefill_workspace_bytes
-    sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9)
+    sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9, 0)
     rec_gdn_bf16 = -(-(4 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
     rec_kda_f32 = -(-(64 * 4 + (3 * 16 * 64 + 2 * 16 * 16) * 4) // 256) * 256
     assert f(ctypes.byref(sh), 0, 1, 32, 0) == 32 * 4 * rec_gdn_bf16
@@ -130,7 +146,7 @@ def test_prefill_workspace_size():
     assert f(ctypes.byref(sh), 0, 1, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_bf16
     assert f(ctypes.byref(sh), 1, 0, 16, 0) == 63 * 4 * rec_kda_f32
     # one pass over every chunk, whatever the length
-    sh = gdr.PrefillShape(2, 32768, 4, 128, 64, 2)
+    sh = gdr.PrefillShape(2, 32768, 4, 128, 64, 2, 0)
     rec_kda_bf16 = -(-(128 * 4 + (3 * 32 * 128 + 2 * 32 * 32) * 2) // 256) * 256
     assert f(ctypes.byref(sh), 1, 1, 32, 0) == 2 * 1024 * 4 * rec_kda_bf16
     assert f(None, 0, 1, 0, 1) == 0
@@ -153,6 +169,39 @@ def test_decode_rejects(kw, status, msg):
     st, err = _decode(**kw)
     assert st == status, err
     assert msg in err
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=0), 1, "max_tokens"),
+    (dict(K=65), 1, "max_tokens"),
+    (dict(P=-1), 1, "num_slots"),
+    (dict(P=3), 1, "without state_slots"),
+    (dict(P=3, slots=A + 5 * MB), 0, None),                     # slots given: any pool size
+    (dict(H=6, Hk=4), 1, "does not divide"),
+    (dict(gate=2), 1, "gate"),
+    (dict(dk=48), 2, "head_dim_k"),
+    (dict(q=A + 4), 1, "misaligned"),
+    (dict(ntok=A + 5 * MB + 2), 1, "misaligned"),
+    (dict(pool=A + 3 * MB), 1, "state overlaps beta"),
+    (dict(out=A + MB), 1, "out overlaps k"),
+    (dict(slots=A + 8 * MB + 16), 1, "state overlaps state_slots"),
+])
+def test_decode_tokens_rejects(kw, status, msg):
+    if status == 0:
+        st, err = _decode_tokens(**dict(kw, dk=48))    # valid so far: stop at the unsupported head size
+        assert st == 2 and "head_dim_k" in err
+        return
+    st, err = _decode_tokens(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_decode_grouped_heads_validation():
+    st, err = _decode(H=6, Hk=4)
+    assert st == 1 and "does not divide" in err
+    # q/k hold Hk heads: with Hk = 1 the 4 x 1 x 64 bf16 q ends 512 bytes after A
+    st, err = _decode(H=2, Hk=1, dk=48, k=A + 512)
+    assert st == 2 and "head_dim_k" in err
 
 
 def test_decode_zero_sequences_is_a_noop():

@@ -234,3 +234,113 @@ def test_planted_mistake_is_caught():
         S = (S - np.outer(S @ kt, kt)) * a[None, :] + np.outer(v[0, t, 0], kt)  # wrong order
         worst = max(worst, np.abs(S @ kt - v[0, t, 0]).max())
     assert worst > 1e-3
+
+
+# ------------------------------------------------- grouped value heads ----
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_grouped_value_heads_against_product_form(per_channel):
+    """Hk = 2 q/k heads shared by H = 6 value heads (groups of 3 consecutive
+    value heads): every value head equals the brute-force product form run
+    with its own v, gates and state and the q/k of head h // 3.  Distinct q/k
+    per head, so a wrong head map (h % Hk, say) fails."""
+    T, dk, dv, Hk, H = 6, 5, 3, 2, 6
+    r = np.random.default_rng(40)
+    q = r.standard_normal((1, T, Hk, dk))
+    k = r.standard_normal((1, T, Hk, dk)) / np.sqrt(dk)
+    v = r.standard_normal((1, T, H, dv))
+    beta = r.random((1, T, H))
+    la = -r.random((1, T, H, dk) if per_channel else (1, T, H))
+    S0 = r.standard_normal((1, H, dv, dk))
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0)
+    for h in range(H):
+        O, S = models.product_form(q[0, :, h // 3], k[0, :, h // 3], v[0, :, h], beta[0, :, h], la[0, :, h], S0[0, h])
+        np.testing.assert_allclose(out[0, :, h], O, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(fin[0, h], S, rtol=0, atol=1e-12)
+    # decode takes the same grouping
+    o1, s1 = oracle.decode(q[:, 0], k[:, 0], v[:, 0], beta[:, 0], la[:, 0], S0)
+    for h in range(H):
+        O, S = models.product_form(q[0, :1, h // 3], k[0, :1, h // 3], v[0, :1, h], beta[0, :1, h], la[0, :1, h],
+                                   S0[0, h])
+        np.testing.assert_allclose(o1[0, h], O[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(s1[0, h], S, rtol=0, atol=1e-12)
+
+
+def test_grouped_heads_reject_non_divisor():
+    q = np.zeros((1, 2, 4, 8))
+    v = np.zeros((1, 2, 6, 8))
+    with pytest.raises(ValueError):
+        oracle.recurrence(q, q, v, np.zeros((1, 2, 6)), np.zeros((1, 2, 6)))
+
+
+# ------------------------------------------------- multi-token decode ----
+def _tokens_case(N, K, Hk, H, dk, dv, P, per_channel, seed):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((N, K, Hk, dk))
+    k = r.standard_normal((N, K, Hk, dk)) / np.sqrt(dk)
+    v = r.standard_normal((N, K, H, dv))
+    beta = r.random((N, K, H))
+    la = -r.random((N, K, H, dk) if per_channel else (N, K, H))
+    pool = r.standard_normal((P, H, dv, dk))
+    return q, k, v, beta, la, pool
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_decode_tokens_against_product_form(per_channel):
+    """Each sequence's outputs are the brute-force product form's readouts of
+    its first T tokens from its slot; its slot ends at the product form's
+    state after C tokens; other slots, padding entries (slot -1 or >= P) and
+    rows past T are untouched.  Values past the limits are clamped."""
+    N, K, Hk, H, dk, dv, P = 6, 5, 1, 2, 4, 3, 9
+    q, k, v, beta, la, pool = _tokens_case(N, K, Hk, H, dk, dv, P, per_channel, 41)
+    slots = np.array([7, 2, -1, 0, 9, 4])
+    ntok = np.array([5, 3, 5, 0, 2, 9])       # 9 > K: clamped to 5
+    ncom = np.array([5, 0, 2, 0, 1, 2])
+    out, written, new_pool = oracle.decode_tokens(q, k, v, beta, la, pool, num_tokens=ntok, num_commit=ncom,
+                                                  state_slots=slots)
+    touched = set()
+    for n in range(N):
+        s, T = slots[n], min(ntok[n], K)
+        C = min(ncom[n], T)
+        if s < 0 or s >= P or T == 0:
+            assert not written[n].any() and not out[n].any()
+            continue
+        assert written[n, :T].all() and not written[n, T:].any() and not out[n, T:].any()
+        for h in range(H):
+            O, _ = models.product_form(q[n, :T, h // (H // Hk)], k[n, :T, h // (H // Hk)], v[n, :T, h],
+                                       beta[n, :T, h], la[n, :T, h], pool[s, h])
+            np.testing.assert_allclose(out[n, :T, h], O, rtol=0, atol=1e-12)
+            _, Sc = models.product_form(q[n, :C, 0], k[n, :C, 0], v[n, :C, h], beta[n, :C, h], la[n, :C, h],
+                                        pool[s, h])
+            np.testing.assert_allclose(new_pool[s, h], Sc, rtol=0, atol=1e-12)
+        if C > 0:
+            touched.add(s)
+    for s in range(P):
+        if s not in touched:
+            assert np.array_equal(new_pool[s], pool[s])
+    assert touched == {7, 4}
+
+
+def test_decode_tokens_verify_then_replay_equals_decoding_the_accepted_tokens():
+    """The speculative flow: verify a K-token draft without committing, then
+    replay the j accepted tokens (committing them) fused with the next draft;
+    the slot then holds the state after the accepted tokens, the draft's
+    outputs equal a plain K-token decode's, and one-token decode steps give
+    the same numbers."""
+    N, K, H, dk, dv = 3, 4, 2, 6, 5
+    q, k, v, beta, la, pool = _tokens_case(N, K, H, H, dk, dv, N, True, 42)
+    o_verify, _, p1 = oracle.decode_tokens(q, k, v, beta, la, pool, num_commit=np.zeros(N))
+    assert np.array_equal(p1, pool)
+    o_plain, _, p_all = oracle.decode_tokens(q, k, v, beta, la, pool)
+    np.testing.assert_array_equal(o_verify, o_plain)
+    state = pool.copy()
+    for t in range(K):
+        o_t, state = oracle.decode(q[:, t], k[:, t], v[:, t], beta[:, t], la[:, t], state)
+        np.testing.assert_allclose(o_plain[:, t], o_t, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(p_all, state, rtol=0, atol=1e-13)
+    acc = np.array([1, 3, 0])
+    _, _, p2 = oracle.decode_tokens(q, k, v, beta, la, pool, num_tokens=np.full(N, K), num_commit=acc)
+    for n in range(N):
+        j = acc[n]
+        _, s_j = oracle.recurrence(q[n:n + 1, :j], k[n:n + 1, :j], v[n:n + 1, :j], beta[n:n + 1, :j],
+                                   la[n:n + 1, :j], initial_state=pool[n:n + 1])
+        np.testing.assert_allclose(p2[n], s_j[0], rtol=0, atol=1e-13)

@@ -1,11 +1,13 @@
-"""Decode step on the GPU vs the fp64 oracle (the recurrence with T = 1)."""
+"""Decode on the GPU vs the fp64 oracle: the one-token step (the recurrence
+with T = 1) and the multi-token decode over a pool of state slots."""
+import numpy as np
 import pytest
 import torch
 
 import gated_delta_rule_73_amd as gdr
 import oracle
-from parity import TOL, assert_close, assert_close_rounded, gpu_available, say
-from workloads import WORKLOADS, decode_inputs
+from parity import TOL, assert_close, assert_close_rounded, gpu_available, say, to_np
+from workloads import WORKLOADS, decode_inputs, decode_tokens_inputs
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
 DEV = "cuda"
@@ -86,3 +88,131 @@ def test_decode_steps_match_oracle_prefill():
     ref_o, ref_s = oracle.recurrence(cat("q"), cat("k"), cat("v"), cat("beta"), cat("log_alpha"), initial_state=s0)
     assert_close("out", torch.stack(outs, dim=1), ref_o, TOL[torch.bfloat16])
     assert_close("state", state, ref_s, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_decode_grouped_value_heads(gate):
+    """16 query-key heads shared by 48 value heads (groups of 3)."""
+    w = WORKLOADS["mtp_decode_256x48"]
+    inp = decode_inputs(w, DEV, gate=gate, num_seqs=16, seed=300)
+    assert inp["q"].shape[1] == 16 and inp["v"].shape[1] == 48
+    _run_and_check(inp, torch.bfloat16, f"N=16 H=48 Hk=16 {gate}")
+
+
+# --------------------------------------------------- multi-token decode ----
+def _tokens_gpu(inp, **kw):
+    pool = inp["state_pool"]
+    out = gdr.gdr_decode_tokens(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], pool,
+                                num_tokens=inp.get("num_tokens"), num_commit=inp.get("num_commit"),
+                                state_slots=inp.get("state_slots"), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _tokens_check(inp, pool0, out, label, tol):
+    """Written rows and every slot against the oracle; unwritten rows keep
+    their NaN poison; untouched slots are bit-identical."""
+    say(f"decode_tokens {label}")
+    ref_o, written, ref_pool = oracle.decode_tokens(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                                    pool0, num_tokens=inp.get("num_tokens"),
+                                                    num_commit=inp.get("num_commit"),
+                                                    state_slots=inp.get("state_slots"))
+    w = torch.from_numpy(written).to(out.device)
+    if written.any():
+        assert_close("out (written rows)", out[w], ref_o[written], tol)
+    assert torch.isnan(out[~w].float()).all(), "rows past num_tokens or of skipped sequences were written"
+    changed = np.any(ref_pool != to_np(pool0), axis=(1, 2, 3))
+    pool = inp["state_pool"]
+    if changed.any():
+        idx = torch.from_numpy(np.nonzero(changed)[0]).to(out.device)
+        assert_close("committed slots", pool[idx], ref_pool[changed], tol)
+    keep = torch.from_numpy(np.nonzero(~changed)[0]).to(out.device)
+    assert torch.equal(pool[keep], pool0.to(out.device)[keep]), "a slot without committed tokens changed"
+
+
+def _poisoned_out(inp, dtype=torch.float32):
+    N, K, H, dv = inp["v"].shape
+    return torch.full((N, K, H, dv), float("nan"), dtype=dtype, device=DEV)
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_decode_tokens_modes(gate):
+    """Slots out of order, padding entries (slot -1 and slot >= P), token
+    counts 0..K and above K (clamped), commits 0 (verify only), partial
+    (replay + verify) and full, commit above the token count (clamped)."""
+    w = WORKLOADS["mtp_decode_256x48"]
+    inp = decode_tokens_inputs(w, DEV, gate=gate, num_seqs=8, heads=6, qk_heads=2, tokens=5, slots=12, seed=310)
+    inp["state_slots"] = torch.tensor([3, 11, -1, 0, 7, 12, 5, 9], dtype=torch.int32, device=DEV)
+    inp["num_tokens"] = torch.tensor([5, 2, 5, 0, 9, 5, 1, 4], dtype=torch.int32, device=DEV)
+    inp["num_commit"] = torch.tensor([5, 0, 3, 0, 2, 1, 7, 3], dtype=torch.int32, device=DEV)
+    pool0 = inp["state_pool"].clone()
+    out = _tokens_gpu(inp, out=_poisoned_out(inp))
+    _tokens_check(inp, pool0, out, f"modes {gate}", TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("gate", ["head", "channel"])
+@pytest.mark.parametrize("dk,dv,K", [(16, 16, 3), (32, 20, 1), (64, 64, 6), (128, 4, 2), (128, 128, 8), (128, 200, 3),
+                                     (64, 256, 2)])
+def test_decode_tokens_shapes(dtype, gate, dk, dv, K):
+    w = WORKLOADS["mtp_decode_256x48"]
+    inp = decode_tokens_inputs(w, DEV, gate=gate, num_seqs=5, heads=3, qk_heads=3, tokens=K, slots=7, dk=dk, dv=dv,
+                               seed=320 + dk + dv + K, qkv_dtype=dtype)
+    pool0 = inp["state_pool"].clone()
+    out = _tokens_gpu(inp, out=_poisoned_out(inp))
+    _tokens_check(inp, pool0, out, f"dk={dk} dv={dv} K={K} {gate} {dtype}", TOL[dtype])
+
+
+def test_decode_tokens_defaults_equal_decode_steps():
+    """No slots, counts or commits: K tokens from state n, all committed --
+    the same as K one-token decode steps (both against the oracle)."""
+    w = WORKLOADS["decode_256x32"]
+    K = 4
+    steps = [decode_inputs(w, DEV, gate="channel", num_seqs=6, heads=4, seed=330 + i) for i in range(K)]
+    s0 = steps[0]["state"].clone()
+    stack = lambda key: torch.stack([st[key] for st in steps], dim=1).contiguous()
+    inp = {key: stack(key) for key in ("q", "k", "v", "beta", "log_alpha")}
+    inp["state_pool"] = s0.clone()
+    out = _tokens_gpu(inp)
+    _tokens_check(inp, s0, out, "defaults", TOL[torch.bfloat16])
+    state = s0.clone()
+    outs = [gdr.gdr_decode_step(st["q"], st["k"], st["v"], st["beta"], st["log_alpha"], state) for st in steps]
+    torch.cuda.synchronize()
+    assert_close("decode steps vs multi-token out", torch.stack(outs, dim=1), to_np(out), TOL[torch.bfloat16])
+    assert_close("decode steps vs multi-token state", state, to_np(inp["state_pool"]), TOL[torch.bfloat16])
+
+
+def test_decode_tokens_bf16_output_and_determinism():
+    w = WORKLOADS["mtp_decode_256x48"]
+    inp = decode_tokens_inputs(w, DEV, num_seqs=16, slots=16, seed=340)
+    pool0 = inp["state_pool"].clone()
+    o1 = _tokens_gpu(inp, out_dtype=torch.bfloat16)
+    p1 = inp["state_pool"].clone()
+    inp["state_pool"].copy_(pool0)
+    o2 = _tokens_gpu(inp, out_dtype=torch.bfloat16)
+    assert torch.equal(o1, o2) and torch.equal(p1, inp["state_pool"])
+    ref_o, written, _ = oracle.decode_tokens(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], pool0,
+                                             num_commit=inp["num_commit"], state_slots=inp["state_slots"])
+    assert written.all()
+    assert_close_rounded("out (bf16)", o1, ref_o, TOL[torch.bfloat16])
+
+
+@pytest.mark.slow
+def test_mtp_decode_256x48_workload():
+    """256 sequences x 48 value heads (16 q/k heads), d=128, 4 tokens each,
+    slots drawn from a pool of 512, commits uniform in [0, 3]: every output
+    and every slot checked (the oracle runs on the slots in use)."""
+    w = WORKLOADS["mtp_decode_256x48"]
+    inp = decode_tokens_inputs(w, DEV)
+    slots = inp["state_slots"].long()
+    pool0 = inp["state_pool"].clone()
+    out = _tokens_gpu(inp)
+    say("decode_tokens mtp_decode_256x48")
+    ref_o, written, ref_pool = oracle.decode_tokens(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                                    pool0[slots], num_commit=inp["num_commit"])
+    assert written.all()
+    assert_close("out", out, ref_o, TOL[torch.bfloat16])
+    assert_close("slots in use", inp["state_pool"][slots], ref_pool, TOL[torch.bfloat16])
+    unused = torch.ones(pool0.shape[0], dtype=torch.bool, device=DEV)
+    unused[slots] = False
+    assert torch.equal(inp["state_pool"][unused], pool0[unused])

@@ -36,9 +36,9 @@ def _check_all(inp, label, **kw):
     return out, fin
 
 
-def _small(dk, dv, H, T, gate, dtype, init, seed, B=1, lengths=None):
+def _small(dk, dv, H, T, gate, dtype, init, seed, B=1, lengths=None, Hk=0):
     w = Workload("small", "prefill", heads=H, dk=dk, dv=dv, qkv_dtype=dtype, gate=gate, batch=B, seqlen=T,
-                 init_state=init, seed=seed)
+                 init_state=init, seed=seed, qk_heads=Hk)
     return prefill_inputs(w, DEV, lengths=lengths)
 
 
@@ -62,15 +62,17 @@ def _check_sampled(inp, units, label, **kw):
     out, fin = _gpu(inp, **kw)
     cu = inp["cu_seqlens"]
     tol = TOL[inp["q"].dtype]
+    G = inp["v"].shape[2] // inp["q"].shape[2]            # value heads per q/k head
     for (n, h) in units:
         if cu is None:
-            sl = (slice(n, n + 1), slice(None), slice(h, h + 1))
-            lo, hi = None, None
+            rows = (slice(n, n + 1), slice(None))
         else:
             bounds = cu.cpu().numpy()
-            lo, hi = int(bounds[n]), int(bounds[n + 1])
-            sl = (slice(0, 1), slice(lo, hi), slice(h, h + 1))
-        sub = {key: inp[key][sl].contiguous() for key in ("q", "k", "v", "beta", "log_alpha")}
+            rows = (slice(0, 1), slice(int(bounds[n]), int(bounds[n + 1])))
+        sl = rows + (slice(h, h + 1),)
+        sub = {key: inp[key][sl].contiguous() for key in ("v", "beta", "log_alpha")}
+        for key in ("q", "k"):
+            sub[key] = inp[key][rows + (slice(h // G, h // G + 1),)].contiguous()
         s0 = inp["initial_state"]
         s0 = None if s0 is None else s0[n:n + 1, h:h + 1].contiguous()
         ref_o, ref_s = oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["beta"], sub["log_alpha"],
@@ -99,6 +101,17 @@ def test_packed_gdn_256k_workload():
     lens = np.diff(inp["cu_seqlens"].cpu().numpy())
     longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
     out, fin = _check_sampled(inp, [(longest, 0), (shortest, 15), (3, 7)], "packed_gdn_256k")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(fin).all()
+
+
+@pytest.mark.slow
+def test_gdn_gva_prefill_32k_workload():
+    """B=1, T=32768, 16 query-key heads shared by 48 value heads, d=128,
+    bf16, per-head decay, S0 ~ N(0, 0.02^2): units from different groups and
+    from one group (they share q/k) checked against the oracle."""
+    w = WORKLOADS["gdn_gva_prefill_32k"]
+    inp = prefill_inputs(w, DEV)
+    out, fin = _check_sampled(inp, [(0, 0), (0, 1), (0, 2), (0, 47)], "gdn_gva_prefill_32k")
     assert torch.isfinite(out.float()).all() and torch.isfinite(fin).all()
 
 
@@ -143,6 +156,31 @@ F32_CASES = [
 def test_prefill_f32_shapes(dk, dv, H, T, gate, init, chunk):
     inp = _small(dk, dv, H, T, gate, torch.float32, init, seed=7 * dk + T)
     _check_all(inp, f"fp32 dk={dk} dv={dv} H={H} T={T} {gate}", chunk_size=chunk)
+
+
+GROUPED_CASES = [
+    # dk, dv, H, Hk, T, gate, dtype
+    (128, 128, 6, 2, 197, "head", torch.bfloat16),
+    (128, 128, 6, 2, 130, "channel", torch.bfloat16),
+    (64, 64, 3, 1, 100, "head", torch.bfloat16),
+    (128, 64, 8, 4, 64, "channel", torch.bfloat16),
+    (32, 32, 4, 2, 70, "channel", torch.float32),
+    (64, 48, 6, 3, 45, "head", torch.float32),
+]
+
+
+@pytest.mark.parametrize("dk,dv,H,Hk,T,gate,dtype", GROUPED_CASES)
+def test_prefill_grouped_value_heads(dk, dv, H, Hk, T, gate, dtype):
+    """Hk query-key heads shared by groups of H / Hk consecutive value heads."""
+    inp = _small(dk, dv, H, T, gate, dtype, True, seed=dk + H + T, Hk=Hk)
+    assert inp["q"].shape[2] == Hk and inp["v"].shape[2] == H
+    _check_all(inp, f"grouped H={H} Hk={Hk} dk={dk} dv={dv} T={T} {gate} {dtype}")
+
+
+def test_prefill_grouped_packed():
+    lens = [33, 0, 100, 7]
+    inp = _small(128, 128, 4, 0, "channel", torch.bfloat16, True, seed=71, lengths=lens, Hk=2)
+    _check_all(inp, f"grouped packed {lens}")
 
 
 @pytest.mark.parametrize("gate", ["head", "channel"])

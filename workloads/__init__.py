@@ -17,6 +17,13 @@ Recipe (per workload, one seed):
   (one value per (token, head) for per-head decay, one per key channel for
   per-channel decay), initial state ~ N(0, 0.02^2) where asked for.
   Draw order: q, k, v, beta logits, alpha logits, initial state.
+  Grouped value heads: q and k are drawn with the query-key head count, v,
+  the gates and the states with the value head count.
+  Multi-token decode adds, after the states: the slot of each sequence (a
+  random choice of distinct slots of the pool), the accepted count of each
+  sequence's previous draft (uniform in [0, K - 1]: the tokens its call
+  replays and commits) -- so every call reads every state and writes those
+  with at least one accepted token.
   Draws are fp32 from torch's seeded generator on the target device; q/k/v are
   then rounded to the storage dtype (bf16 round-to-nearest-even), gates and
   states stay fp32.
@@ -44,6 +51,9 @@ class Workload:
     init_state: bool = False
     packed: dict = field(default_factory=dict)   # {"num_seqs", "min_len", "max_len"}
     seed: int = 0
+    qk_heads: int = 0         # query-key heads shared by the value heads (0: = heads)
+    tokens: int = 1           # decode: tokens per sequence per call
+    slots: int = 0            # multi-token decode: state pool slots (0: one per sequence)
 
 
 WORKLOADS = {
@@ -62,6 +72,15 @@ WORKLOADS = {
                                 qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=262144,
                                 chunk=64, init_state=True,
                                 packed={"num_seqs": 8, "min_len": 4096, "max_len": 61440}, seed=4),
+    # the Gated DeltaNet layer shape of the pages' Qwen model: 16 query-key
+    # heads shared by 48 value heads of dimension 128
+    "gdn_gva_prefill_32k": Workload("gdn_gva_prefill_32k", "prefill", heads=48, qk_heads=16, dk=128, dv=128,
+                                    qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=32768,
+                                    init_state=True, seed=5),
+    # speculative decode with that shape: 4 drafted tokens per sequence, the
+    # previous draft's accepted tokens replayed and committed in the same call
+    "mtp_decode_256x48": Workload("mtp_decode_256x48", "decode", heads=48, qk_heads=16, dk=128, dv=128,
+                                  qkv_dtype=torch.bfloat16, gate="head", batch=256, tokens=4, slots=512, seed=6),
 }
 
 
@@ -100,6 +119,7 @@ def prefill_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batc
     B = w.batch if batch is None else batch
     T = w.seqlen if seqlen is None else seqlen
     H = w.heads if heads is None else heads
+    Hk = (w.qk_heads or w.heads) if heads is None else H // (w.heads // (w.qk_heads or w.heads))
     gate = w.gate if gate is None else gate
     seed = w.seed if seed is None else seed
     init_state = w.init_state if init_state is None else init_state
@@ -118,8 +138,8 @@ def prefill_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batc
         N = B
     g = _gen(device, seed)
     f32 = torch.float32
-    q = _unit_norm(torch.randn(B, T, H, dk, generator=g, device=device, dtype=f32)).to(w.qkv_dtype)
-    k = _unit_norm(torch.randn(B, T, H, dk, generator=g, device=device, dtype=f32)).to(w.qkv_dtype)
+    q = _unit_norm(torch.randn(B, T, Hk, dk, generator=g, device=device, dtype=f32)).to(w.qkv_dtype)
+    k = _unit_norm(torch.randn(B, T, Hk, dk, generator=g, device=device, dtype=f32)).to(w.qkv_dtype)
     v = torch.randn(B, T, H, dv, generator=g, device=device, dtype=f32).to(w.qkv_dtype)
     beta = torch.sigmoid(torch.randn(B, T, H, generator=g, device=device, dtype=f32))
     ashape = (B, T, H) if gate == "head" else (B, T, H, dk)
@@ -133,21 +153,55 @@ def prefill_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batc
 
 def decode_inputs(w: Workload, device="cpu", *, gate: str = "head", num_seqs: int | None = None,
                   heads: int | None = None, dk: int | None = None, dv: int | None = None,
-                  seed: int | None = None, qkv_dtype=None):
-    """One token per sequence: q, k [N, H, dk], v [N, H, dv], beta [N, H],
+                  seed: int | None = None, qkv_dtype=None, qk_heads: int | None = None):
+    """One token per sequence: q, k [N, Hk, dk], v [N, H, dv], beta [N, H],
     log_alpha [N, H] or [N, H, dk], state [N, H, dv, dk] (fp32)."""
     N = w.batch if num_seqs is None else num_seqs
     H = w.heads if heads is None else heads
+    Hk = qk_heads or (w.qk_heads if heads is None and w.qk_heads else H)
     dk = w.dk if dk is None else dk
     dv = w.dv if dv is None else dv
     dt = w.qkv_dtype if qkv_dtype is None else qkv_dtype
     g = _gen(device, w.seed if seed is None else seed)
     f32 = torch.float32
-    q = _unit_norm(torch.randn(N, H, dk, generator=g, device=device, dtype=f32)).to(dt)
-    k = _unit_norm(torch.randn(N, H, dk, generator=g, device=device, dtype=f32)).to(dt)
+    q = _unit_norm(torch.randn(N, Hk, dk, generator=g, device=device, dtype=f32)).to(dt)
+    k = _unit_norm(torch.randn(N, Hk, dk, generator=g, device=device, dtype=f32)).to(dt)
     v = torch.randn(N, H, dv, generator=g, device=device, dtype=f32).to(dt)
     beta = torch.sigmoid(torch.randn(N, H, generator=g, device=device, dtype=f32))
     ashape = (N, H) if gate == "head" else (N, H, dk)
     log_alpha = -torch.nn.functional.softplus(torch.randn(*ashape, generator=g, device=device, dtype=f32))
     state = 0.02 * torch.randn(N, H, dv, dk, generator=g, device=device, dtype=f32)
     return {"q": q, "k": k, "v": v, "beta": beta, "log_alpha": log_alpha, "state": state}
+
+
+def decode_tokens_inputs(w: Workload, device="cpu", *, gate: str | None = None, num_seqs: int | None = None,
+                         heads: int | None = None, qk_heads: int | None = None, tokens: int | None = None,
+                         slots: int | None = None, dk: int | None = None, dv: int | None = None,
+                         seed: int | None = None, qkv_dtype=None):
+    """Several tokens per sequence from a pool of states: q, k [N, K, Hk, dk],
+    v [N, K, H, dv], beta [N, K, H], log_alpha [N, K, H] or [N, K, H, dk],
+    state_pool [P, H, dv, dk] (fp32), state_slots [N] (distinct slots, int32),
+    num_commit [N] (int32, uniform in [0, K - 1]); num_tokens is left to the
+    caller (None: all K)."""
+    N = w.batch if num_seqs is None else num_seqs
+    H = w.heads if heads is None else heads
+    Hk = qk_heads or (w.qk_heads if heads is None and w.qk_heads else H)
+    K = w.tokens if tokens is None else tokens
+    P = (w.slots or N) if slots is None else slots
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    gate = w.gate if gate is None else gate
+    dt = w.qkv_dtype if qkv_dtype is None else qkv_dtype
+    g = _gen(device, w.seed if seed is None else seed)
+    f32 = torch.float32
+    q = _unit_norm(torch.randn(N, K, Hk, dk, generator=g, device=device, dtype=f32)).to(dt)
+    k = _unit_norm(torch.randn(N, K, Hk, dk, generator=g, device=device, dtype=f32)).to(dt)
+    v = torch.randn(N, K, H, dv, generator=g, device=device, dtype=f32).to(dt)
+    beta = torch.sigmoid(torch.randn(N, K, H, generator=g, device=device, dtype=f32))
+    ashape = (N, K, H) if gate == "head" else (N, K, H, dk)
+    log_alpha = -torch.nn.functional.softplus(torch.randn(*ashape, generator=g, device=device, dtype=f32))
+    pool = 0.02 * torch.randn(P, H, dv, dk, generator=g, device=device, dtype=f32)
+    slots_ = torch.randperm(P, generator=g, device=device)[:N].to(torch.int32)
+    commit = torch.randint(0, K, (N,), generator=g, device=device, dtype=torch.int32)
+    return {"q": q, "k": k, "v": v, "beta": beta, "log_alpha": log_alpha, "state_pool": pool,
+            "state_slots": slots_, "num_commit": commit}
