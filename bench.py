@@ -5,6 +5,12 @@ One step = one chunked prefill of the Kimi-Delta-Attention workload
 decode step of 256 sequences x 32 heads (128x128 fp32 states, in place) with
 per-head decay and one with per-channel decay.  Prints one JSON line.
 
+Two further workloads are timed in their own loops and reported beside the
+step (not part of `value`): the grouped-head Gated DeltaNet prefill (16
+query-key heads shared by 48 value heads, T=32768) and the speculative
+multi-token decode over a pool of state slots (256 sequences x 48 value heads,
+4 tokens each, a per-sequence committed prefix).
+
 value = prefill throughput (B*T tokens, all heads) in Mtok/s.  Times come from
 HIP events on the stream the kernels are launched on, over the timed steps.
 One prefill call is two kernels (the per-chunk record kernel and the chain
@@ -40,9 +46,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def prefill_alg_bytes(B, T, H, dk, dv, kda, out_bytes, init_state=True, final_state=True):
+def prefill_alg_bytes(B, T, H, dk, dv, kda, out_bytes, init_state=True, final_state=True, Hk=None):
     tok = B * T * H
-    b = tok * (2 * dk + dv) * 2                  # q, k, v (bf16)
+    b = B * T * (H if Hk is None else Hk) * 2 * dk * 2   # q, k (bf16; shared by value-head groups)
+    b += tok * dv * 2                            # v (bf16)
     b += tok * 4                                 # beta
     b += tok * (dk if kda else 1) * 4            # log alpha (fp32)
     b += tok * dv * out_bytes                    # out
@@ -58,6 +65,31 @@ def prefill_alg_flops(B, T, H, dk, dv, C):
 def decode_alg_bytes(N, H, dk, dv, kda, out_bytes):
     u = N * H
     return u * (2 * dv * dk * 4 + (2 * dk + dv) * 2 + 4 + (dk if kda else 1) * 4 + dv * out_bytes)
+
+
+def decode_tokens_alg_bytes(N, K, H, Hk, dk, dv, kda, out_bytes, n_written):
+    """Every sequence's state read once, the states of the n_written
+    sequences that commit tokens written once, the K tokens' inputs read and
+    their outputs written once."""
+    st = H * dv * dk * 4
+    tok = N * K
+    return (N + n_written) * st + tok * (Hk * 2 * dk * 2 + H * dv * 2 + H * 4 + H * (dk if kda else 1) * 4
+                                         + H * dv * out_bytes)
+
+
+def time_per_launch(fn, steps):
+    """Mean seconds per call of fn over `steps` back-to-back calls, from HIP
+    events on the current stream (the stream the binding launches on)."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps / 1e3
 
 
 def cpu_baseline(inp, H, target_s):
@@ -95,6 +127,53 @@ def cpu_baseline(inp, H, target_s):
                       f"workload, fp64, {reps} run(s), {total:.1f} s wall"}
 
 
+def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tokens_inputs):
+    """The grouped-head prefill and the multi-token decode, each timed in its
+    own loop of args.steps calls after args.warmup untimed ones."""
+    res = {}
+    wg = WORKLOADS["gdn_gva_prefill_32k"]
+    print(f"[bench] {wg.name}", file=sys.stderr, flush=True)
+    g = prefill_inputs(wg, dev)
+    B, T, Hk, dk = g["q"].shape
+    H, dv = g["v"].shape[2:]
+    gout = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+    gfin = torch.empty_like(g["initial_state"])
+    f = lambda: gdr.gdr_prefill_chunked(g["q"], g["k"], g["v"], g["beta"], g["log_alpha"],
+                                        initial_state=g["initial_state"], out=gout, final_state=gfin)
+    for _ in range(args.warmup):
+        f()
+    t = time_per_launch(f, args.steps)
+    by = prefill_alg_bytes(B, T, H, dk, dv, False, 4, Hk=Hk)
+    res["grouped_prefill"] = {
+        "workload": f"{wg.name}: B={B}, T={T}, {Hk} q/k heads shared by {H} value heads, d={dk}, bf16 q/k/v, "
+                    "per-head decay, S0 given, fp32 out",
+        "us_per_launch": round(t * 1e6, 2), "Mtok_s": round(B * T / t / 1e6, 3), "alg_bytes": by,
+        "hbm_GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(prefill_alg_flops(B, T, H, dk, dv, 32) / t / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)}
+    del g, gout, gfin
+
+    wm = WORKLOADS["mtp_decode_256x48"]
+    print(f"[bench] {wm.name}", file=sys.stderr, flush=True)
+    m = decode_tokens_inputs(wm, dev)
+    N, K, Hk, dk = m["q"].shape
+    H, dv = m["v"].shape[2:]
+    mout = torch.empty(N, K, H, dv, dtype=torch.float32, device=dev)
+    f = lambda: gdr.gdr_decode_tokens(m["q"], m["k"], m["v"], m["beta"], m["log_alpha"], m["state_pool"],
+                                      num_commit=m["num_commit"], state_slots=m["state_slots"], out=mout)
+    for _ in range(args.warmup):
+        f()
+    t = time_per_launch(f, args.steps)
+    n_written = int((m["num_commit"] > 0).sum())
+    by = decode_tokens_alg_bytes(N, K, H, Hk, dk, dv, False, 4, n_written)
+    res["multi_token_decode"] = {
+        "workload": f"{wm.name}: {N} sequences x {H} value heads ({Hk} q/k heads), d={dk}, {K} tokens each, "
+                    f"states in a pool of {wm.slots} slots, committed prefix uniform in [0, {K - 1}] "
+                    f"({n_written} of {N} sequences write their state), per-head decay, fp32 out",
+        "us_per_call": round(t * 1e6, 2), "Mtok_s": round(N * K / t / 1e6, 4), "alg_bytes": by,
+        "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +195,7 @@ def main():
     import torch
 
     import gated_delta_rule_73_amd as gdr
-    from workloads import WORKLOADS, decode_inputs, prefill_inputs
+    from workloads import WORKLOADS, decode_inputs, decode_tokens_inputs, prefill_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -234,6 +313,7 @@ def main():
         },
         "cpu_baseline": None,
     }
+    result.update(extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tokens_inputs))
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, H, args.cpu_seconds)

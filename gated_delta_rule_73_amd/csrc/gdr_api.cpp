@@ -271,15 +271,12 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
         return fail(GDR_ERROR_INVALID_VALUE, "dv_slice %d not in {0, 16, 32, 64}", dv_slice);
     if (dv_slice != 0 && dv % dv_slice != 0)
         return fail(GDR_ERROR_INVALID_VALUE, "dv_slice %d does not divide head_dim_v %d", dv_slice, dv);
-    // automatic choices: 32-token chunks (16 where 32 is not compiled);
-    // value slices of 32 channels while that still gives >= 1 workgroup per CU
+    // automatic choices: 32-token chunks (16 where 32 is not compiled); the
+    // value-slice width that needs the fewest rounds of chain workgroups
     int C = chunk_size;
-    int DVS = dv_slice;
-    if (!DVS) {
-        const int64_t units = (int64_t)s.num_seqs * s.num_heads;
-        DVS = (!bf16 || dv % 32 != 0 || units * (dv / 32) < 256) ? 16 : 32;
-    }
     if (!C) C = auto_chunk(bf16, kda, dk);
+    int DVS = dv_slice;
+    if (!DVS) DVS = gdr::auto_dv_slice(bf16, kda, dk, dv, C, (long)s.num_seqs * s.num_heads);
     if (!gdr::prefill_supported(bf16, kda, dk, DVS, C))
         return fail(GDR_ERROR_NOT_SUPPORTED, "no prefill kernel for %s dk=%d dv_slice=%d chunk=%d",
                     bf16 ? "bf16" : "fp32", dk, DVS, C);
@@ -300,6 +297,8 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
                     kda ? 16 : 4);
 
     const PrefillWorkspace ws = fit_workspace(s, kda, bf16, C, packed, workspace_bytes);
+    if ((ws.record_chunks + 8) * s.num_heads >= INT32_MAX)
+        return fail(GDR_ERROR_NOT_SUPPORTED, "more than 2^31 (chunk, head) records in one pass");
     const size_t need_ws = ws.total;
     if (workspace_bytes < need_ws)
         return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need_ws);

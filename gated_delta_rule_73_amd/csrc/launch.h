@@ -57,6 +57,8 @@ hipError_t launch_decode_tokens(const DecodeArgs &p, hipStream_t st);
 
 // True when a prefill kernel is compiled for this combination.
 bool prefill_supported(bool bf16, bool kda, int dk, int dv_slice, int chunk);
+// Value-slice width when the caller passes 0: 16 or 32 (see prefill.hip).
+int auto_dv_slice(bool bf16, bool kda, int dk, int dv, int chunk, long units);
 hipError_t launch_prefill(const PrefillArgs &p, hipStream_t st);
 
 }  // namespace gdr

@@ -17,6 +17,10 @@ hipError_t launch_prefill_bf16_gdn(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_bf16_kda(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_f32_gdn(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_f32_kda(const PrefillArgs &a, hipStream_t st);
+int chain_blocks_per_cu_bf16_gdn(int dk, int dv_slice, int chunk);
+int chain_blocks_per_cu_bf16_kda(int dk, int dv_slice, int chunk);
+int chain_blocks_per_cu_f32_gdn(int dk, int dv_slice, int chunk);
+int chain_blocks_per_cu_f32_kda(int dk, int dv_slice, int chunk);
 
 __global__ __launch_bounds__(256) void schedule_kernel(const int32_t *__restrict__ cu, int n, int chunk,
                                                        int32_t *__restrict__ order, int32_t *__restrict__ choff) {
@@ -47,6 +51,27 @@ bool prefill_supported(bool bf16, bool kda, int dk, int dv_slice, int chunk) {
     }
 #undef GDR_CASE
     return false;
+}
+
+// Automatic value-slice width.  A chain workgroup walks all chunks of its
+// (sequence, head, slice) in order, so the call takes about one such walk per
+// round of workgroups the device holds at once.  The narrower slice gives
+// more, lighter workgroups; it is chosen only when it needs no more rounds
+// than the wider one (a d_k = 128 chain workgroup fills a CU's LDS, so one
+// round is one workgroup per CU).
+int auto_dv_slice(bool bf16, bool kda, int dk, int dv, int chunk, long units) {
+    if (!bf16 || dv % 32 != 0 || !prefill_supported(bf16, kda, dk, 32, chunk)) return 16;
+    if (!prefill_supported(bf16, kda, dk, 16, chunk)) return 32;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;                                   // no device to ask: MI355X
+    auto rounds = [&](int dvs) {
+        int per_cu = kda ? chain_blocks_per_cu_bf16_kda(dk, dvs, chunk) : chain_blocks_per_cu_bf16_gdn(dk, dvs, chunk);
+        const long cap = (long)cus * (per_cu > 0 ? per_cu : 1);
+        return (units * (dv / dvs) + cap - 1) / cap;
+    };
+    return rounds(32) < rounds(16) ? 32 : 16;
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {

@@ -362,7 +362,9 @@ struct PrepKArgs {
 // HBM traffic, not by the latency of its serial steps: a few persistent
 // workgroups (four waves each) per CU walk the records, each holding the next
 // record's inputs in flight while it computes the current one.
-template <int DK, int C, bool KDA, typename IT>
+// GRP: value heads share q/k heads (G > 1); compiled apart so that the
+// ungrouped kernel carries none of the grouped record order's registers.
+template <int DK, int C, bool KDA, typename IT, bool GRP>
 __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     using SM = PrepSmem<DK, C, KDA, IT>;
     using Rec = ChunkRec<DK, C, KDA, IT>;
@@ -395,14 +397,30 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     const IT *gk = static_cast<const IT *>(p.k);
     constexpr size_t RS = chunk_record_stride(DK, C, KDA, sizeof(ST));
 
-    // record r = (chunk slot x, head h), r = x * H + h: its first token and
-    // its token count (0: no such chunk)
-    auto locate = [&](long r, int &h, int &t0, int &nv) {
-        h = (int)(r % H);
-        const int x = (int)(r / H);
+    // Record L = (chunk slot x, head h), L = x * H + h; the G value heads
+    // h = G j .. G j + G - 1 share q/k head j, so their records form group
+    // L / G.  Workgroup b handles positions r = b, b + grid, ... (grid a
+    // multiple of 8, so all on XCD b % 8).  Groups go round-robin over the 8
+    // XCDs and a group's G records to positions r, r + 8, ..., so they run
+    // side by side on one XCD and read their q/k once from HBM, then from
+    // that XCD's L2 (with G = 1, position r holds record r).  locate gives the
+    // record's index, first token and token count (0: no such chunk).
+    // (Record counts stay below 2^31, which the host checks, so 32-bit
+    // arithmetic suffices.)
+    const int G = GRP ? p.G : 1;
+    const long NP = GRP ? (p.num_records / G + 7) / 8 * 8 * G : p.num_records;
+    auto record_at = [&](long r) -> long {       // num_records: no record
+        if constexpr (!GRP) return r;
+        if (r >= NP) return p.num_records;
+        const unsigned slot = (unsigned)r / 8u;
+        return (long)((slot / G * 8u + (unsigned)r % 8u) * G + slot % G);
+    };
+    auto locate = [&](long L, int &h, int &t0, int &nv) {
+        h = (int)(L % H);
+        const int x = (int)(L / H);
         nv = 0;
         t0 = 0;
-        if (r >= p.num_records) return;
+        if (L >= p.num_records) return;
         int n, j;
         if (p.cu) {
             if (x >= p.choff[p.num_seqs]) return;
@@ -430,7 +448,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     float br = 0.f, gs = 0.f;
     auto fetch = [&](long r) {
         int h, t0, nv;
-        locate(r, h, t0, nv);
+        locate(record_at(r), h, t0, nv);
 #pragma unroll
         for (int x = 0; x < KVPT; ++x) {
             const int e = tid + 256 * x;
@@ -462,14 +480,15 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     // record's inputs are requested as soon as this one's reach LDS
     long r = blockIdx.x;
     fetch(r);
-    for (; r < p.num_records; r += gridDim.x) {
+    for (; r < NP; r += gridDim.x) {
+    const long L = record_at(r);
     int h, t0, nv;
-    locate(r, h, t0, nv);
+    locate(L, h, t0, nv);
     if (nv == 0) {                           // uniform: a chunk slot past the last sequence's end
         fetch(r + gridDim.x);
         continue;
     }
-    Rec &rec = *reinterpret_cast<Rec *>(p.rec + (size_t)r * RS);
+    Rec &rec = *reinterpret_cast<Rec *>(p.rec + (size_t)L * RS);
 
     // ---- A: inputs to LDS
 #pragma unroll
@@ -1156,12 +1175,19 @@ hipError_t launch_prep(const PrefillArgs &a, int j0, int seg_chunks, char *rec, 
         int dev = 0, cus = 0, per_cu = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep_kernel<DK, C, KDA, IT>, 256, 0);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep_kernel<DK, C, KDA, IT, false>, 256, 0);
         if (e != hipSuccess) return e;
         resident = std::max(1, cus * per_cu);
     }
-    const long grid = std::min<long>(pk.num_records, resident);
-    hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT>), dim3((unsigned)grid), dim3(256), 0, st, pk);
+    // grouped: a multiple of 8 workgroups (8 XCDs) unless the device holds fewer
+    if (pk.G > 1) {
+        const long grid = std::min<long>((pk.num_records / pk.G + 7) / 8 * 8 * pk.G, resident);
+        hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT, true>), dim3((unsigned)grid), dim3(256), 0, st, pk);
+    } else {
+        const long grid = std::min<long>(pk.num_records, resident);
+        hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT, false>), dim3((unsigned)grid), dim3(256), 0, st, pk);
+    }
     return hipGetLastError();
 }
 
