@@ -5,11 +5,16 @@ One step = one chunked prefill of the Kimi-Delta-Attention workload
 decode step of 256 sequences x 32 heads (128x128 fp32 states, in place) with
 per-head decay and one with per-channel decay.  Prints one JSON line.
 
-Two further workloads are timed in their own loops and reported beside the
-step (not part of `value`): the grouped-head Gated DeltaNet prefill (16
-query-key heads shared by 48 value heads, T=32768) and the speculative
-multi-token decode over a pool of state slots (256 sequences x 48 value heads,
-4 tokens each, a per-sequence committed prefix).
+Further workloads are timed in their own loops and reported beside the step
+(not part of `value`): the per-head-decay prefill at T=8192 (cache-warm, and
+with a 512 MiB write between calls so its ~170 MB working set is not left in
+the 256 MB last-level cache), the packed batch of 8 sequences (262144 tokens),
+the grouped-head Gated DeltaNet prefill (16 query-key heads shared by 48 value
+heads, T=32768) and the speculative multi-token decode over a pool of state
+slots (256 sequences x 48 value heads, 4 tokens each, a per-sequence committed
+prefix).  Two measured ceilings of the same box are reported with them: a
+large bf16 GEMM (the library GEMM, for the MFMA side) and a 512 MiB
+read-modify-write (for the HBM side).
 
 value = prefill throughput (B*T tokens, all heads) in Mtok/s.  Times come from
 HIP events on the stream the kernels are launched on, over the timed steps.
@@ -46,12 +51,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def prefill_alg_bytes(B, T, H, dk, dv, kda, out_bytes, init_state=True, final_state=True, Hk=None):
+def prefill_alg_bytes(B, T, H, dk, dv, kda, out_bytes, init_state=True, final_state=True, Hk=None, gate_bytes=4):
     tok = B * T * H
     b = B * T * (H if Hk is None else Hk) * 2 * dk * 2   # q, k (bf16; shared by value-head groups)
     b += tok * dv * 2                            # v (bf16)
-    b += tok * 4                                 # beta
-    b += tok * (dk if kda else 1) * 4            # log alpha (fp32)
+    b += tok * gate_bytes                        # beta
+    b += tok * (dk if kda else 1) * gate_bytes   # log alpha
     b += tok * dv * out_bytes                    # out
     b += (int(init_state) + int(final_state)) * B * H * dv * dk * 4
     return b
@@ -77,19 +82,41 @@ def decode_tokens_alg_bytes(N, K, H, Hk, dk, dv, kda, out_bytes, n_written):
                                          + H * dv * out_bytes)
 
 
-def time_per_launch(fn, steps):
-    """Mean seconds per call of fn over `steps` back-to-back calls, from HIP
-    events on the current stream (the stream the binding launches on)."""
+def time_calls(fn, steps, between=None):
+    """Seconds per call of fn over `steps` calls, from HIP events on the
+    current stream (the stream the binding launches on) recorded around each
+    call: (mean, median, min).  `between`, if given, runs between calls,
+    outside the timed intervals."""
+    import statistics
+
     import torch
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
-    ev[0].record()
-    for i in range(steps):
+    for a, b in ev:
+        if between is not None:
+            between()
+        a.record()
         fn()
-        ev[i + 1].record()
+        b.record()
     torch.cuda.synchronize()
-    return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps / 1e3
+    t = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    return sum(t) / len(t), statistics.median(t), min(t)
+
+
+def time_per_launch(fn, steps):
+    """Mean seconds per call of fn over `steps` back-to-back calls."""
+    return time_calls(fn, steps)[0]
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, H, target_s):
@@ -123,6 +150,7 @@ def cpu_baseline(inp, H, target_s):
         reps += 1
     tokens = B * n * reps  # every head of these tokens
     return {"value": tokens / total / 1e6, "unit": "Mtok/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"first {n} of {T} tokens of all {B}x{H} (sequence, head) units of the prefill "
                       f"workload, fp64, {reps} run(s), {total:.1f} s wall"}
 
@@ -131,6 +159,75 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     """The grouped-head prefill and the multi-token decode, each timed in its
     own loop of args.steps calls after args.warmup untimed ones."""
     res = {}
+
+    def prefill_entry(w, inp, label, flush=None):
+        B, T, Hk, dk = inp["q"].shape
+        H, dv = inp["v"].shape[2:]
+        po = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+        N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+        pf = torch.empty(N, H, dv, dk, dtype=torch.float32, device=dev)
+        f = lambda: gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                            initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"],
+                                            out=po, final_state=pf)
+        for _ in range(args.warmup):
+            f()
+        mean, med, mn = time_calls(f, args.steps, between=flush)
+        kda = inp["log_alpha"].dim() == 4
+        by = prefill_alg_bytes(B, T, H, dk, dv, kda, 4, inp["initial_state"] is not None, True, Hk=Hk,
+                               gate_bytes=inp["beta"].element_size())
+        if inp["cu_seqlens"] is not None:   # one initial and one final state per sequence, not per row
+            by += (N - B) * 2 * H * dv * dk * 4
+        fl = prefill_alg_flops(B, T, H, dk, dv, 32)
+        return {"workload": label, "us_per_launch": round(mean * 1e6, 2), "us_median": round(med * 1e6, 2),
+                "us_min": round(mn * 1e6, 2), "Mtok_s": round(B * T / mean / 1e6, 3), "alg_bytes": by,
+                "hbm_GBps": round(by / mean / 1e9, 1), "frac_of_hbm_peak": round(by / mean / 1e9 / HBM_PEAK_GBS, 4),
+                "alg_flops": fl, "mfma_frac": round(fl / mean / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)}
+
+    w2 = WORKLOADS["kda_prefill_32k"]
+    print(f"[bench] {w2.name} with bf16 gates", file=sys.stderr, flush=True)
+    g2 = prefill_inputs(w2, dev, gate_dtype=torch.bfloat16)
+    res["kda_prefill_32k_bf16_gates"] = prefill_entry(
+        w2, g2, f"{w2.name} with beta and log alpha stored in bf16 (rounded from the same fp32 draws): B=2, "
+                "T=32768, H=32, d=128, bf16 q/k/v, per-channel decay, S0 given, fp32 out")
+    del g2
+
+    w1 = WORKLOADS["gdn_prefill_8k"]
+    print(f"[bench] {w1.name}", file=sys.stderr, flush=True)
+    g1 = prefill_inputs(w1, dev)
+    lbl = f"{w1.name}: B=1, T=8192, H=16, d=128, bf16 q/k/v, per-head decay, zero initial state, fp32 out"
+    flush_buf = torch.empty(1 << 27, dtype=torch.float32, device=dev)     # 512 MiB
+    res["gdn_prefill_8k"] = {"cache_warm": prefill_entry(w1, g1, lbl),
+                             "after_512MiB_write": prefill_entry(w1, g1, lbl, flush=lambda: flush_buf.fill_(1.0))}
+    del g1
+
+    w4 = WORKLOADS["packed_gdn_256k"]
+    print(f"[bench] {w4.name}", file=sys.stderr, flush=True)
+    g4 = prefill_inputs(w4, dev)
+    lens = (g4["cu_seqlens"][1:] - g4["cu_seqlens"][:-1]).tolist()
+    res["packed_gdn_256k"] = prefill_entry(w4, g4, f"{w4.name}: 8 packed sequences of {lens} tokens (262144), "
+                                                   "H=16, d=128, bf16 q/k/v, per-head decay, S0 given, fp32 out")
+    del g4
+
+    print("[bench] measured ceilings", file=sys.stderr, flush=True)
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    mean, med, mn = time_calls(lambda: torch.matmul(a, b, out=c), 10)
+    gemm_tflops = 2 * n ** 3 / med / 1e12
+    del a, b, c
+    for _ in range(3):
+        flush_buf.add_(1.0)
+    mean, med, mn = time_calls(lambda: flush_buf.add_(1.0), 10)
+    rmw_gbs = 2 * flush_buf.numel() * 4 / med / 1e9
+    del flush_buf
+    res["measured_ceilings"] = {
+        "bf16_gemm_8192_TFLOPs": round(gemm_tflops, 1), "bf16_gemm_frac_of_peak": round(gemm_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "rmw_512MiB_GBps": round(rmw_gbs, 1), "rmw_frac_of_peak": round(rmw_gbs / HBM_PEAK_GBS, 4),
+        "note": "library bf16 GEMM (torch.matmul, 8192^3) and an in-place add over 512 MiB of fp32, median of 10"}
+
     wg = WORKLOADS["gdn_gva_prefill_32k"]
     print(f"[bench] {wg.name}", file=sys.stderr, flush=True)
     g = prefill_inputs(wg, dev)
@@ -255,9 +352,13 @@ def main():
         ev_d[2 * s_ + 2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    t_pre = sum(ev_p[i].elapsed_time(ev_p[i + 1]) for i in range(K)) / K / 1e3   # s per launch
-    t_dg = sum(ev_d[2 * i].elapsed_time(ev_d[2 * i + 1]) for i in range(K)) / K / 1e3
-    t_dk = sum(ev_d[2 * i + 1].elapsed_time(ev_d[2 * i + 2]) for i in range(K)) / K / 1e3
+    import statistics
+
+    i_pre = [ev_p[i].elapsed_time(ev_p[i + 1]) / 1e3 for i in range(K)]       # s per launch
+    i_dg = [ev_d[2 * i].elapsed_time(ev_d[2 * i + 1]) / 1e3 for i in range(K)]
+    i_dk = [ev_d[2 * i + 1].elapsed_time(ev_d[2 * i + 2]) / 1e3 for i in range(K)]
+    t_pre, t_dg, t_dk = (sum(x) / K for x in (i_pre, i_dg, i_dk))
+    spread = lambda x: {"us_median": round(statistics.median(x) * 1e6, 2), "us_min": round(min(x) * 1e6, 2)}
 
     chunk = args.chunk or 32
     tokens = B * T
@@ -300,14 +401,14 @@ def main():
                      "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "prep_kernel<128,32,KDA,bf16> + chain_kernel<128,32,32,KDA,bf16> (one prefill call)",
                      "alg_bytes_per_launch": pre_bytes, "avg_launch_us": round(t_pre * 1e6, 2)},
-        "prefill": {"us_per_launch": round(t_pre * 1e6, 2), "Mtok_s": round(tokens / t_pre / 1e6, 3),
+        "prefill": {"us_per_launch": round(t_pre * 1e6, 2), **spread(i_pre), "Mtok_s": round(tokens / t_pre / 1e6, 3),
                     "mfma_frac": round(pre_flops / t_pre / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4),
                     "alg_flops": pre_flops, "hbm_GBps": round(pre_gbs, 1)},
         "decode": {
-            "per_head_decay": {"us_per_step": round(t_dg * 1e6, 2), "GBps": round(dg_bytes / t_dg / 1e9, 1),
+            "per_head_decay": {"us_per_step": round(t_dg * 1e6, 2), **spread(i_dg), "GBps": round(dg_bytes / t_dg / 1e9, 1),
                                "frac_of_hbm_peak": round(dg_bytes / t_dg / 1e9 / HBM_PEAK_GBS, 4),
                                "Mtok_s": round(wd.batch / t_dg / 1e6, 4), "alg_bytes": dg_bytes},
-            "per_channel_decay": {"us_per_step": round(t_dk * 1e6, 2), "GBps": round(dk_bytes / t_dk / 1e9, 1),
+            "per_channel_decay": {"us_per_step": round(t_dk * 1e6, 2), **spread(i_dk), "GBps": round(dk_bytes / t_dk / 1e9, 1),
                                   "frac_of_hbm_peak": round(dk_bytes / t_dk / 1e9 / HBM_PEAK_GBS, 4),
                                   "Mtok_s": round(wd.batch / t_dk / 1e6, 4), "alg_bytes": dk_bytes},
         },

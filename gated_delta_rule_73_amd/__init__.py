@@ -123,8 +123,8 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
                         dv_slice: int = 0, scale: float = 1.0, out=None, out_dtype=torch.float32,
                         final_state=None, output_final_state: bool = True, workspace=None):
     """Chunked prefill.  q, k [B, T, Hk, dk]; v [B, T, H, dv] (bf16 or fp32; Hk divides H);
-    beta [B, T, H] fp32; log_alpha [B, T, H] (per-head decay) or [B, T, H, dk]
-    (per-key-channel decay) fp32; initial_state [N, H, dv, dk] fp32 or None;
+    beta [B, T, H]; log_alpha [B, T, H] (per-head decay) or [B, T, H, dk]
+    (per-key-channel decay), both fp32 or both bf16; initial_state [N, H, dv, dk] fp32 or None;
     cu_seqlens int32 [N+1] (packed, B == 1) or None.
     out_dtype (fp32 or bf16) applies when ``out`` is not given.
     workspace: uint8 device tensor, or None to allocate the size
@@ -145,8 +145,8 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
         raise ValueError("log_alpha must be [B, T, H] or [B, T, H, dk]")
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, q.dtype, dev)
-    _need(beta, "beta", torch.float32, dev)
-    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(beta, "beta", None, dev)
+    _need(log_alpha, "log_alpha", beta.dtype, dev)
     _need(initial_state, "initial_state", torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
@@ -165,7 +165,7 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
         _need(workspace, "workspace", torch.uint8, dev)
         ws, ws_bytes = workspace, workspace.numel()
     _check(lib.gdr_prefill_chunked(
-        ctypes.byref(shape), gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+        ctypes.byref(shape), gate, _dtype_code(q), _dtype_code(beta), _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
         _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(dv_slice), float(scale), _ptr(out),
         _ptr(final_state), _ptr(ws), int(ws_bytes), _stream(dev)))
     return out, final_state
@@ -173,7 +173,7 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
 
 def gdr_decode_step(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, out=None, out_dtype=torch.float32):
     """Decode step, one token per sequence: q, k [N, Hk, dk]; v [N, H, dv];
-    beta [N, H]; log_alpha [N, H] or [N, H, dk]; state [N, H, dv, dk] fp32
+    beta [N, H]; log_alpha [N, H] or [N, H, dk] (gates fp32 or both bf16); state [N, H, dv, dk] fp32
     (updated in place).  Returns out [N, H, dv]."""
     lib = load_library()
     dev = q.device
@@ -184,13 +184,13 @@ def gdr_decode_step(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, out=
     gate = GDR_GATE_HEAD if log_alpha.dim() == 2 else GDR_GATE_CHANNEL
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, q.dtype, dev)
-    _need(beta, "beta", torch.float32, dev)
-    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(beta, "beta", None, dev)
+    _need(log_alpha, "log_alpha", beta.dtype, dev)
     _need(state, "state", torch.float32, dev)
     if out is None:
         out = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
     _need(out, "out", None, dev)
-    _check(lib.gdr_decode_step(N, H, Hk, dk, dv, gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+    _check(lib.gdr_decode_step(N, H, Hk, dk, dv, gate, _dtype_code(q), _dtype_code(beta), _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                _ptr(log_alpha), _ptr(state), float(scale), _ptr(out), _stream(dev)))
     return out
 
@@ -213,8 +213,8 @@ def gdr_decode_tokens(q, k, v, beta, log_alpha, state_pool, *, num_tokens=None, 
     gate = GDR_GATE_HEAD if log_alpha.dim() == 3 else GDR_GATE_CHANNEL
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, q.dtype, dev)
-    _need(beta, "beta", torch.float32, dev)
-    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(beta, "beta", None, dev)
+    _need(log_alpha, "log_alpha", beta.dtype, dev)
     _need(state_pool, "state_pool", torch.float32, dev)
     for t, nm in ((num_tokens, "num_tokens"), (num_commit, "num_commit"), (state_slots, "state_slots")):
         _need(t, nm, torch.int32, dev)
@@ -225,7 +225,7 @@ def gdr_decode_tokens(q, k, v, beta, log_alpha, state_pool, *, num_tokens=None, 
     if out is None:
         out = torch.empty(N, K, H, dv, dtype=out_dtype, device=dev)
     _need(out, "out", None, dev)
-    _check(lib.gdr_decode_tokens(N, K, H, Hk, dk, dv, gate, _dtype_code(q), GDR_F32, _dtype_code(out), _ptr(q),
+    _check(lib.gdr_decode_tokens(N, K, H, Hk, dk, dv, gate, _dtype_code(q), _dtype_code(beta), _dtype_code(out), _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(num_tokens), _ptr(num_commit),
                                  _ptr(state_slots), _ptr(state_pool), int(state_pool.shape[0]), float(scale),
                                  _ptr(out), _stream(dev)))

@@ -30,11 +30,12 @@ namespace gdr {
 
 // EXACT: d_v is a multiple of the rows one pass covers, so no row index
 // needs a bounds check (measured ~5% faster at d = 128); OUTB: bf16 outputs.
-// Value head h reads the q/k head h / G of HK (grouped value heads).
-template <int DK, bool KDA, typename QT, int RB, bool EXACT, bool OUTB>
+// Value head h reads the q/k head h / G of HK (grouped value heads).  GT:
+// storage type of beta and log alpha (float or __bf16).
+template <int DK, bool KDA, typename QT, typename GT, int RB, bool EXACT, bool OUTB>
 __global__ __launch_bounds__(256) void decode_kernel(
     int H, int HK, int G, int DV, const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ v,
-    const float *__restrict__ beta, const float *__restrict__ log_alpha, float *__restrict__ state,
+    const GT *__restrict__ beta, const GT *__restrict__ log_alpha, float *__restrict__ state,
     float scale, void *__restrict__ out) {
     constexpr int LPR = DK / 4;          // lanes per state row
     constexpr int RPP = 256 / LPR;       // rows covered by the workgroup per pass
@@ -48,13 +49,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const float4 qv = load4(q + (size_t)qku * DK + c0);
     float4 a;
     if constexpr (KDA) {
-        const float4 la = *reinterpret_cast<const float4 *>(log_alpha + (size_t)unit * DK + c0);
+        const float4 la = load4(log_alpha + (size_t)unit * DK + c0);
         a = make_float4(__expf(la.x), __expf(la.y), __expf(la.z), __expf(la.w));
     } else {
-        const float s = __expf(log_alpha[unit]);
+        const float s = __expf(to_f32(log_alpha[unit]));
         a = make_float4(s, s, s, s);
     }
-    const float b = beta[unit];
+    const float b = to_f32(beta[unit]);
     const float kq = group_sum<LPR>(kv.x * qv.x + kv.y * qv.y + kv.z * qv.z + kv.w * qv.w);
 
     float *S = state + (size_t)unit * DV * DK;
@@ -94,17 +95,17 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 }
 
-template <int DK, bool KDA, typename QT>
+template <int DK, bool KDA, typename QT, typename GT>
 static hipError_t launch_decode_t(const DecodeArgs &p, hipStream_t st) {
     constexpr int LPR = DK / 4;
     constexpr int RPP = 256 / LPR;
     constexpr int RB = (RPP >= 64) ? 2 : (RPP >= 32 ? 4 : 8);
     const unsigned grid = (unsigned)((size_t)p.num_seqs * p.num_heads);
     const bool exact = p.dv % (RPP * RB) == 0;
-#define GDR_DECODE_LAUNCH(E, O)                                                                        \
-    hipLaunchKernelGGL((decode_kernel<DK, KDA, QT, RB, E, O>), dim3(grid), dim3(256), 0, st, p.num_heads, \
-                       p.num_qk_heads, p.num_heads / p.num_qk_heads, p.dv, (const QT *)p.q, (const QT *)p.k, (const QT *)p.v, p.beta, p.log_alpha,     \
-                       p.state, p.scale, p.out)
+#define GDR_DECODE_LAUNCH(E, O)                                                                               \
+    hipLaunchKernelGGL((decode_kernel<DK, KDA, QT, GT, RB, E, O>), dim3(grid), dim3(256), 0, st, p.num_heads,  \
+                       p.num_qk_heads, p.num_heads / p.num_qk_heads, p.dv, (const QT *)p.q, (const QT *)p.k,    \
+                       (const QT *)p.v, (const GT *)p.beta, (const GT *)p.log_alpha, p.state, p.scale, p.out)
     if (exact) {
         if (p.out_bf16) GDR_DECODE_LAUNCH(true, true);
         else GDR_DECODE_LAUNCH(true, false);
@@ -116,21 +117,26 @@ static hipError_t launch_decode_t(const DecodeArgs &p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <bool KDA, typename QT>
+template <bool KDA, typename QT, typename GT>
 static hipError_t launch_decode_dk(const DecodeArgs &p, hipStream_t st) {
     switch (p.dk) {
-        case 16: return launch_decode_t<16, KDA, QT>(p, st);
-        case 32: return launch_decode_t<32, KDA, QT>(p, st);
-        case 64: return launch_decode_t<64, KDA, QT>(p, st);
-        case 128: return launch_decode_t<128, KDA, QT>(p, st);
+        case 16: return launch_decode_t<16, KDA, QT, GT>(p, st);
+        case 32: return launch_decode_t<32, KDA, QT, GT>(p, st);
+        case 64: return launch_decode_t<64, KDA, QT, GT>(p, st);
+        case 128: return launch_decode_t<128, KDA, QT, GT>(p, st);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <bool KDA, typename QT>
+static hipError_t launch_decode_gt(const DecodeArgs &p, hipStream_t st) {
+    return p.gate_bf16 ? launch_decode_dk<KDA, QT, __bf16>(p, st) : launch_decode_dk<KDA, QT, float>(p, st);
+}
+
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t st) {
     if (p.num_seqs == 0 || p.num_heads == 0) return hipSuccess;
-    if (p.kda) return p.bf16 ? launch_decode_dk<true, __bf16>(p, st) : launch_decode_dk<true, float>(p, st);
-    return p.bf16 ? launch_decode_dk<false, __bf16>(p, st) : launch_decode_dk<false, float>(p, st);
+    if (p.kda) return p.bf16 ? launch_decode_gt<true, __bf16>(p, st) : launch_decode_gt<true, float>(p, st);
+    return p.bf16 ? launch_decode_gt<false, __bf16>(p, st) : launch_decode_gt<false, float>(p, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -149,7 +155,7 @@ hipError_t launch_decode(const DecodeArgs &p, hipStream_t st) {
 struct DecodeTokensKArgs {
     int H, HK, G, DV, K, num_slots;
     const void *q, *k, *v;
-    const float *beta, *log_alpha;
+    const void *beta, *log_alpha;    // the kernel's GT
     const int32_t *num_tokens, *num_commit, *slots;
     float *pool;
     float scale;
@@ -173,7 +179,7 @@ __device__ __forceinline__ float dpp_group_sum(float x) {
     return x;
 }
 
-template <int DK, bool KDA, typename QT, int NR, bool OUTB>
+template <int DK, bool KDA, typename QT, typename GT, int NR, bool OUTB>
 __global__ __launch_bounds__(decode_tokens_threads<DK>()) void decode_tokens_kernel(DecodeTokensKArgs p) {
     constexpr int NTH = decode_tokens_threads<DK>();
     constexpr int LPR = decode_tokens_lpr<DK>();   // lanes per state row
@@ -196,6 +202,8 @@ __global__ __launch_bounds__(decode_tokens_threads<DK>()) void decode_tokens_ker
     const QT *q = static_cast<const QT *>(p.q);
     const QT *k = static_cast<const QT *>(p.k);
     const QT *v = static_cast<const QT *>(p.v);
+    const GT *gla = static_cast<const GT *>(p.log_alpha);
+    const GT *gbeta = static_cast<const GT *>(p.beta);
     using OT = typename std::conditional<OUTB, __bf16, float>::type;
     OT *out = static_cast<OT *>(p.out);
     float *S = p.pool + ((size_t)slot * H + h) * DV * DK;
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(decode_tokens_threads<DK>()) void decode_tokens_ker
             sk[tt][c / 4] = load4(k + qo);
             sq[tt][c / 4] = load4(q + qo);
             if constexpr (KDA) {
-                const float4 la = *reinterpret_cast<const float4 *>(p.log_alpha + (tr * H + h) * DK + c);
+                const float4 la = load4(gla + (tr * H + h) * DK + c);
                 sa[tt][c] = __expf(la.x); sa[tt][c + 1] = __expf(la.y);
                 sa[tt][c + 2] = __expf(la.z); sa[tt][c + 3] = __expf(la.w);
             }
@@ -237,8 +245,8 @@ __global__ __launch_bounds__(decode_tokens_threads<DK>()) void decode_tokens_ker
         }
         if (tid < nb) {
             const size_t tr = (size_t)n * K + t0 + tid;
-            sb[tid] = p.beta[tr * H + h];
-            if constexpr (!KDA) sa[tid][0] = __expf(p.log_alpha[tr * H + h]);
+            sb[tid] = to_f32(gbeta[tr * H + h]);
+            if constexpr (!KDA) sa[tid][0] = __expf(to_f32(gla[tr * H + h]));
         }
         __syncthreads();
         for (int tt = 0; tt < nb; ++tt) {
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(decode_tokens_threads<DK>()) void decode_tokens_ker
     }
 }
 
-template <int DK, bool KDA, typename QT>
+template <int DK, bool KDA, typename QT, typename GT>
 static hipError_t launch_decode_tokens_t(const DecodeArgs &a, hipStream_t st) {
     constexpr int NTH = decode_tokens_threads<DK>();
     constexpr int RPP = NTH / decode_tokens_lpr<DK>();
@@ -320,30 +328,35 @@ static hipError_t launch_decode_tokens_t(const DecodeArgs &a, hipStream_t st) {
     const unsigned grid = (unsigned)((size_t)a.num_seqs * a.num_heads);
     // rows per thread: enough for d_v <= 128, or for d_v <= 256
     if (a.dv <= 128) {
-        if (a.out_bf16) hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, div_up(128, RPP), true>), dim3(grid), dim3(NTH), 0, st, p);
-        else hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, div_up(128, RPP), false>), dim3(grid), dim3(NTH), 0, st, p);
+        if (a.out_bf16) hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, GT, div_up(128, RPP), true>), dim3(grid), dim3(NTH), 0, st, p);
+        else hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, GT, div_up(128, RPP), false>), dim3(grid), dim3(NTH), 0, st, p);
     } else {
-        if (a.out_bf16) hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, div_up(256, RPP), true>), dim3(grid), dim3(NTH), 0, st, p);
-        else hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, div_up(256, RPP), false>), dim3(grid), dim3(NTH), 0, st, p);
+        if (a.out_bf16) hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, GT, div_up(256, RPP), true>), dim3(grid), dim3(NTH), 0, st, p);
+        else hipLaunchKernelGGL((decode_tokens_kernel<DK, KDA, QT, GT, div_up(256, RPP), false>), dim3(grid), dim3(NTH), 0, st, p);
     }
     return hipGetLastError();
 }
 
-template <bool KDA, typename QT>
+template <bool KDA, typename QT, typename GT>
 static hipError_t launch_decode_tokens_dk(const DecodeArgs &p, hipStream_t st) {
     switch (p.dk) {
-        case 16: return launch_decode_tokens_t<16, KDA, QT>(p, st);
-        case 32: return launch_decode_tokens_t<32, KDA, QT>(p, st);
-        case 64: return launch_decode_tokens_t<64, KDA, QT>(p, st);
-        case 128: return launch_decode_tokens_t<128, KDA, QT>(p, st);
+        case 16: return launch_decode_tokens_t<16, KDA, QT, GT>(p, st);
+        case 32: return launch_decode_tokens_t<32, KDA, QT, GT>(p, st);
+        case 64: return launch_decode_tokens_t<64, KDA, QT, GT>(p, st);
+        case 128: return launch_decode_tokens_t<128, KDA, QT, GT>(p, st);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <bool KDA, typename QT>
+static hipError_t launch_decode_tokens_gt(const DecodeArgs &p, hipStream_t st) {
+    return p.gate_bf16 ? launch_decode_tokens_dk<KDA, QT, __bf16>(p, st) : launch_decode_tokens_dk<KDA, QT, float>(p, st);
+}
+
 hipError_t launch_decode_tokens(const DecodeArgs &p, hipStream_t st) {
     if (p.num_seqs == 0 || p.num_heads == 0) return hipSuccess;
-    if (p.kda) return p.bf16 ? launch_decode_tokens_dk<true, __bf16>(p, st) : launch_decode_tokens_dk<true, float>(p, st);
-    return p.bf16 ? launch_decode_tokens_dk<false, __bf16>(p, st) : launch_decode_tokens_dk<false, float>(p, st);
+    if (p.kda) return p.bf16 ? launch_decode_tokens_gt<true, __bf16>(p, st) : launch_decode_tokens_gt<true, float>(p, st);
+    return p.bf16 ? launch_decode_tokens_gt<false, __bf16>(p, st) : launch_decode_tokens_gt<false, float>(p, st);
 }
 
 }  // namespace gdr

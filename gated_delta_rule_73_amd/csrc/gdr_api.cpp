@@ -147,7 +147,6 @@ gdr_status check_decode(int32_t num_seqs, int32_t K, int32_t num_heads, int32_t 
     if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
         return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d out=%d)", (int)qkv_dtype,
                     (int)gate_dtype, (int)out_dtype);
-    if (gate_dtype != GDR_F32) return fail(GDR_ERROR_NOT_SUPPORTED, "gates must be fp32");
     if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128))
         return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_k %d not in {16, 32, 64, 128}", dk);
     if (dv % 4 != 0 || dv > 256) return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_v %d not a multiple of 4 <= 256", dv);
@@ -157,15 +156,16 @@ gdr_status check_decode(int32_t num_seqs, int32_t K, int32_t num_heads, int32_t 
     if (!q || !k || !v || !beta || !log_alpha || !state || !out)
         return fail(GDR_ERROR_INVALID_VALUE, "q, k, v, beta, log_alpha, state and out must be non-NULL");
     const bool kda = gate == GDR_GATE_CHANNEL;
-    const size_t es = dsize(qkv_dtype);
+    const size_t es = dsize(qkv_dtype), gs = dsize(gate_dtype);
     const size_t rows = (size_t)num_seqs * K;   // token rows
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(log_alpha, kda ? 16 : 4) ||
-        !aligned(v, es) || !aligned(out, dsize(out_dtype)) || !aligned(beta, 4) || !aligned(num_tokens, 4) ||
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(log_alpha, kda ? 4 * gs : gs) ||
+        !aligned(v, es) || !aligned(out, dsize(out_dtype)) || !aligned(beta, gs) || !aligned(num_tokens, 4) ||
         !aligned(num_commit, 4) || !aligned(slots, 4))
-        return fail(GDR_ERROR_INVALID_VALUE, "misaligned pointer (q/k/state need 16 bytes)");
+        return fail(GDR_ERROR_INVALID_VALUE, "misaligned pointer (q/k/state need 16 bytes, per-channel "
+                                             "log_alpha 4 elements)");
     const Range in[] = {range("q", q, rows * hk * dk * es), range("k", k, rows * hk * dk * es),
-                        range("v", v, rows * num_heads * dv * es), range("beta", beta, rows * num_heads * 4),
-                        range("log_alpha", log_alpha, rows * num_heads * (kda ? dk : 1) * 4),
+                        range("v", v, rows * num_heads * dv * es), range("beta", beta, rows * num_heads * gs),
+                        range("log_alpha", log_alpha, rows * num_heads * (kda ? dk : 1) * gs),
                         range("num_tokens", num_tokens, num_tokens ? 4 * (size_t)num_seqs : 0),
                         range("num_commit", num_commit, num_commit ? 4 * (size_t)num_seqs : 0),
                         range("state_slots", slots, slots ? 4 * (size_t)num_seqs : 0)};
@@ -185,8 +185,9 @@ gdr_status check_decode(int32_t num_seqs, int32_t K, int32_t num_heads, int32_t 
     a.bf16 = qkv_dtype == GDR_BF16;
     a.out_bf16 = out_dtype == GDR_BF16;
     a.q = q; a.k = k; a.v = v;
-    a.beta = static_cast<const float *>(beta);
-    a.log_alpha = static_cast<const float *>(log_alpha);
+    a.beta = beta;
+    a.log_alpha = log_alpha;
+    a.gate_bf16 = gate_dtype == GDR_BF16;
     a.state = state;
     a.scale = scale;
     a.out = out;
@@ -250,7 +251,6 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
         return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d out=%d)", (int)qkv_dtype,
                     (int)gate_dtype, (int)out_dtype);
-    if (gate_dtype != GDR_F32) return fail(GDR_ERROR_NOT_SUPPORTED, "gates must be fp32");
     const bool packed = cu_seqlens != nullptr;
     if (packed && s.batch != 1) return fail(GDR_ERROR_INVALID_VALUE, "cu_seqlens requires batch == 1");
     if (!packed && s.num_seqs != s.batch)
@@ -281,7 +281,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
         return fail(GDR_ERROR_NOT_SUPPORTED, "no prefill kernel for %s dk=%d dv_slice=%d chunk=%d",
                     bf16 ? "bf16" : "fp32", dk, DVS, C);
 
-    const size_t es = dsize(qkv_dtype);
+    const size_t es = dsize(qkv_dtype), gs = dsize(gate_dtype);
     const size_t nq = (size_t)tokens * hk * dk, nv = (size_t)tokens * s.num_heads * dv;
     const size_t ng = (size_t)tokens * s.num_heads;
     const size_t nla = kda ? ng * dk : ng;
@@ -292,9 +292,9 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     const char *names16[] = {"q", "k", "v", "out", "initial_state", "final_state"};
     for (int i = 0; i < 6; ++i)
         if (!aligned(aligned16[i], 16)) return fail(GDR_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", names16[i]);
-    if (!aligned(beta, 4) || !aligned(log_alpha, kda ? 16 : 4) || !aligned(cu_seqlens, 4))
-        return fail(GDR_ERROR_INVALID_VALUE, "beta and cu_seqlens must be 4-byte aligned, log_alpha %d-byte aligned",
-                    kda ? 16 : 4);
+    if (!aligned(beta, gs) || !aligned(log_alpha, kda ? 4 * gs : gs) || !aligned(cu_seqlens, 4))
+        return fail(GDR_ERROR_INVALID_VALUE, "beta must be %zu-byte aligned, cu_seqlens 4-byte, log_alpha %zu-byte",
+                    gs, kda ? 4 * gs : gs);
 
     const PrefillWorkspace ws = fit_workspace(s, kda, bf16, C, packed, workspace_bytes);
     if ((ws.record_chunks + 8) * s.num_heads >= INT32_MAX)
@@ -306,7 +306,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     if (need_ws && !aligned(workspace, 256)) return fail(GDR_ERROR_INVALID_VALUE, "workspace is not 256-byte aligned");
 
     const Range in[] = {range("q", q, nq * es), range("k", k, nq * es), range("v", v, nv * es),
-                        range("beta", beta, ng * 4), range("log_alpha", log_alpha, nla * 4),
+                        range("beta", beta, ng * gs), range("log_alpha", log_alpha, nla * gs),
                         range("initial_state", initial_state, nstate * 4),
                         range("cu_seqlens", cu_seqlens, packed ? 4 * ((size_t)s.num_seqs + 1) : 0)};
     const Range ro = range("out", out, nv * dsize(out_dtype));
@@ -336,8 +336,9 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     a.chunk = C;
     a.dv_slice = DVS;
     a.q = q; a.k = k; a.v = v;
-    a.beta = static_cast<const float *>(beta);
-    a.log_alpha = static_cast<const float *>(log_alpha);
+    a.beta = beta;
+    a.log_alpha = log_alpha;
+    a.gate_bf16 = gate_dtype == GDR_BF16;
     a.initial_state = initial_state;
     a.cu_seqlens = cu_seqlens;
     a.scale = scale;

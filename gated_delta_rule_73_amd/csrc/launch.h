@@ -13,7 +13,8 @@ struct DecodeArgs {
     int num_seqs, num_heads, num_qk_heads, dk, dv;
     bool kda, bf16, out_bf16;
     const void *q, *k, *v;
-    const float *beta, *log_alpha;
+    const void *beta, *log_alpha;   // fp32, or bf16 when gate_bf16
+    bool gate_bf16;
     float *state;                   // decode step: [num_seqs, H, dv, dk]; multi-token: the slot pool
     float scale;
     void *out;
@@ -27,7 +28,9 @@ struct PrefillArgs {
     bool kda, bf16, out_bf16;
     int chunk, dv_slice;            // resolved (non-zero) values
     const void *q, *k, *v;
-    const float *beta, *log_alpha, *initial_state;
+    const void *beta, *log_alpha;   // fp32, or bf16 when gate_bf16
+    bool gate_bf16;
+    const float *initial_state;
     const int32_t *cu_seqlens;
     float scale;
     void *out;

@@ -353,7 +353,7 @@ struct PrepKArgs {
     int j0, seg_chunks;          // dense: chunks [j0, j0 + seg_chunks) of every sequence
     float scale;                 // readout factor, folded into Q e^g and M
     const void *q, *k;
-    const float *beta, *log_alpha;
+    const void *beta, *log_alpha;    // fp32 or bf16 (the kernel's GDT)
     const int32_t *cu, *choff;
     char *rec;
 };
@@ -364,7 +364,9 @@ struct PrepKArgs {
 // record's inputs in flight while it computes the current one.
 // GRP: value heads share q/k heads (G > 1); compiled apart so that the
 // ungrouped kernel carries none of the grouped record order's registers.
-template <int DK, int C, bool KDA, typename IT, bool GRP>
+// GDT: storage type of beta and log alpha (float or __bf16; widened to fp32
+// when they reach LDS).
+template <int DK, int C, bool KDA, typename IT, bool GRP, typename GDT>
 __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     using SM = PrepSmem<DK, C, KDA, IT>;
     using Rec = ChunkRec<DK, C, KDA, IT>;
@@ -444,7 +446,10 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     // the raw inputs of one record, held in registers while the previous
     // record is processed (zeros past the sequence end)
     IV kr[KVPT], qr[KVPT];
-    f32x4 gr[GVPT];
+    using GV = typename std::conditional<std::is_same<GDT, float>::value, f32x4, bf16x4>::type;
+    const GDT *gla = static_cast<const GDT *>(p.log_alpha);
+    const GDT *gbeta = static_cast<const GDT *>(p.beta);
+    GV gr[GVPT];
     float br = 0.f, gs = 0.f;
     auto fetch = [&](long r) {
         int h, t0, nv;
@@ -466,14 +471,14 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
             for (int x = 0; x < GVPT; ++x) {
                 const int e = tid + 256 * x;
                 const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
-                gr[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                gr[x] = GV{};
                 if (e < C * DK / 4 && t < nv)
-                    gr[x] = *reinterpret_cast<const f32x4 *>(p.log_alpha + ((size_t)(t0 + t) * H + h) * DK + c);
+                    gr[x] = *reinterpret_cast<const GV *>(gla + ((size_t)(t0 + t) * H + h) * DK + c);
             }
         } else {
-            gs = tid < nv ? p.log_alpha[(size_t)(t0 + tid) * H + h] : 0.f;
+            gs = tid < nv ? to_f32(gla[(size_t)(t0 + tid) * H + h]) : 0.f;
         }
-        br = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        br = tid < nv ? to_f32(gbeta[(size_t)(t0 + tid) * H + h]) : 0.f;
     };
 
     // persistent workgroups: records blockIdx.x, + gridDim.x, ...; the next
@@ -506,7 +511,10 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
             const int e = tid + 256 * x;
             if (e < C * DK / 4) {
                 const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
-                *reinterpret_cast<f32x4 *>(&sm.u.in.G[t][c]) = gr[x];
+                f32x4 g4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) g4[i] = to_f32(gr[x][i]);
+                *reinterpret_cast<f32x4 *>(&sm.u.in.G[t][c]) = g4;
             }
         }
     } else if (wave == 0) {
@@ -1176,18 +1184,23 @@ hipError_t launch_prep(const PrefillArgs &a, int j0, int seg_chunks, char *rec, 
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep_kernel<DK, C, KDA, IT, false>, 256, 0);
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep_kernel<DK, C, KDA, IT, false, float>, 256, 0);
         if (e != hipSuccess) return e;
         resident = std::max(1, cus * per_cu);
     }
     // grouped: a multiple of 8 workgroups (8 XCDs) unless the device holds fewer
-    if (pk.G > 1) {
-        const long grid = std::min<long>((pk.num_records / pk.G + 7) / 8 * 8 * pk.G, resident);
-        hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT, true>), dim3((unsigned)grid), dim3(256), 0, st, pk);
+    const bool grp = pk.G > 1;
+    const long grid = grp ? std::min<long>((pk.num_records / pk.G + 7) / 8 * 8 * pk.G, resident)
+                          : std::min<long>(pk.num_records, resident);
+#define GDR_PREP(GRP_, GT_) hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT, GRP_, GT_>), dim3((unsigned)grid), dim3(256), 0, st, pk)
+    if (a.gate_bf16) {
+        if (grp) GDR_PREP(true, __bf16);
+        else GDR_PREP(false, __bf16);
     } else {
-        const long grid = std::min<long>(pk.num_records, resident);
-        hipLaunchKernelGGL((prep_kernel<DK, C, KDA, IT, false>), dim3((unsigned)grid), dim3(256), 0, st, pk);
+        if (grp) GDR_PREP(true, float);
+        else GDR_PREP(false, float);
     }
+#undef GDR_PREP
     return hipGetLastError();
 }
 

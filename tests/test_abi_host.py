@@ -95,7 +95,10 @@ def _decode_tokens(N=4, K=4, H=2, Hk=0, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=
     (dict(gate=7), 1, "gate"),
     (dict(qkv=5), 1, "dtype"),
     (dict(odt=9), 1, "dtype"),
-    (dict(gdt=1), 2, "fp32"),
+    (dict(gdt=1), 0, None),                                             # bf16 gates
+    (dict(gdt=1, gate=1, la=A + 25 * MB + 8), 0, None),                 # bf16 per-channel: 8-byte aligned
+    (dict(gdt=1, gate=1, la=A + 25 * MB + 4), 1, "log_alpha 8-byte"),
+    (dict(gdt=1, beta=A + 24 * MB + 1), 1, "beta must be 2-byte"),
     (dict(shape=(1, 64, 2, 48, 64, 1, 0)), 2, "head_dim_k"),
     (dict(shape=(1, 64, 2, 64, 40, 1, 0)), 2, "head_dim_v"),
     (dict(shape=(1, 64, 2, 16, 64, 1, 0)), 2, "no prefill kernel"),        # bf16 needs dk >= 32
@@ -157,7 +160,8 @@ def test_prefill_workspace_size():
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(N=-1), 1, "bad shape"),
     (dict(gate=3), 1, "gate"),
-    (dict(gdt=1), 2, "fp32"),
+    (dict(gdt=1, dk=96), 2, "head_dim_k"),                          # bf16 gates pass the dtype checks
+    (dict(gdt=1, gate=1, la=A + 4 * MB + 4), 1, "misaligned"),
     (dict(dk=96), 2, "head_dim_k"),
     (dict(dv=66), 2, "head_dim_v"),
     (dict(state=None), 1, "non-NULL"),

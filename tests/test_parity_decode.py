@@ -216,3 +216,19 @@ def test_mtp_decode_256x48_workload():
     unused = torch.ones(pool0.shape[0], dtype=torch.bool, device=DEV)
     unused[slots] = False
     assert torch.equal(inp["state_pool"][unused], pool0[unused])
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_decode_bf16_gates(gate):
+    """beta and log alpha stored in bf16: the one-token step and the
+    multi-token decode."""
+    w = WORKLOADS["decode_256x32"]
+    inp = decode_inputs(w, DEV, gate=gate, num_seqs=32, heads=8, qk_heads=4, seed=350, gate_dtype=torch.bfloat16)
+    assert inp["beta"].dtype == torch.bfloat16
+    _run_and_check(inp, torch.bfloat16, f"bf16 gates {gate}")
+    wm = WORKLOADS["mtp_decode_256x48"]
+    t = decode_tokens_inputs(wm, DEV, gate=gate, num_seqs=8, heads=6, qk_heads=2, tokens=3, slots=10, seed=351,
+                             gate_dtype=torch.bfloat16)
+    pool0 = t["state_pool"].clone()
+    out = _tokens_gpu(t, out=_poisoned_out(t))
+    _tokens_check(t, pool0, out, f"bf16 gates {gate}", TOL[torch.bfloat16])

@@ -177,6 +177,19 @@ def test_prefill_grouped_value_heads(dk, dv, H, Hk, T, gate, dtype):
     _check_all(inp, f"grouped H={H} Hk={Hk} dk={dk} dv={dv} T={T} {gate} {dtype}")
 
 
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_bf16_gates(gate):
+    """beta and log alpha stored in bf16 (the oracle reads the same bf16 values)."""
+    w = Workload("small", "prefill", heads=4, qk_heads=2, dk=128, dv=128, qkv_dtype=torch.bfloat16, gate=gate,
+                 batch=2, seqlen=197, init_state=True, seed=81)
+    inp = prefill_inputs(w, DEV, gate_dtype=torch.bfloat16)
+    assert inp["beta"].dtype == inp["log_alpha"].dtype == torch.bfloat16
+    _check_all(inp, f"bf16 gates {gate}")
+    w1 = Workload("small", "prefill", heads=2, dk=64, dv=64, qkv_dtype=torch.bfloat16, gate=gate, batch=2,
+                  seqlen=100, init_state=True, seed=82)
+    _check_all(prefill_inputs(w1, DEV, gate_dtype=torch.bfloat16), f"bf16 gates ungrouped {gate}")
+
+
 def test_prefill_grouped_packed():
     lens = [33, 0, 100, 7]
     inp = _small(128, 128, 4, 0, "channel", torch.bfloat16, True, seed=71, lengths=lens, Hk=2)

@@ -25,8 +25,9 @@ Recipe (per workload, one seed):
   replays and commits) -- so every call reads every state and writes those
   with at least one accepted token.
   Draws are fp32 from torch's seeded generator on the target device; q/k/v are
-  then rounded to the storage dtype (bf16 round-to-nearest-even), gates and
-  states stay fp32.
+  then rounded to the storage dtype (bf16 round-to-nearest-even), states stay
+  fp32, and gates stay fp32 unless a bf16 gate variant is asked for (then beta
+  and log alpha are rounded to bf16 after their fp32 draw).
 """
 from __future__ import annotations
 
@@ -109,7 +110,7 @@ def _gen(device, seed):
 
 def prefill_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batch: int | None = None,
                    heads: int | None = None, lengths=None, gate: str | None = None, seed: int | None = None,
-                   init_state: bool | None = None):
+                   init_state: bool | None = None, gate_dtype=torch.float32):
     """Inputs of a prefill workload (optionally resized for tests).
 
     Returns a dict with q, k, v [B, T, H, d], beta [B, T, H], log_alpha
@@ -147,13 +148,13 @@ def prefill_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batc
     s0 = None
     if init_state:
         s0 = 0.02 * torch.randn(N, H, dv, dk, generator=g, device=device, dtype=f32)
-    return {"q": q, "k": k, "v": v, "beta": beta, "log_alpha": log_alpha,
+    return {"q": q, "k": k, "v": v, "beta": beta.to(gate_dtype), "log_alpha": log_alpha.to(gate_dtype),
             "initial_state": s0, "cu_seqlens": cu}
 
 
 def decode_inputs(w: Workload, device="cpu", *, gate: str = "head", num_seqs: int | None = None,
                   heads: int | None = None, dk: int | None = None, dv: int | None = None,
-                  seed: int | None = None, qkv_dtype=None, qk_heads: int | None = None):
+                  seed: int | None = None, qkv_dtype=None, qk_heads: int | None = None, gate_dtype=torch.float32):
     """One token per sequence: q, k [N, Hk, dk], v [N, H, dv], beta [N, H],
     log_alpha [N, H] or [N, H, dk], state [N, H, dv, dk] (fp32)."""
     N = w.batch if num_seqs is None else num_seqs
@@ -171,13 +172,14 @@ def decode_inputs(w: Workload, device="cpu", *, gate: str = "head", num_seqs: in
     ashape = (N, H) if gate == "head" else (N, H, dk)
     log_alpha = -torch.nn.functional.softplus(torch.randn(*ashape, generator=g, device=device, dtype=f32))
     state = 0.02 * torch.randn(N, H, dv, dk, generator=g, device=device, dtype=f32)
-    return {"q": q, "k": k, "v": v, "beta": beta, "log_alpha": log_alpha, "state": state}
+    return {"q": q, "k": k, "v": v, "beta": beta.to(gate_dtype), "log_alpha": log_alpha.to(gate_dtype),
+            "state": state}
 
 
 def decode_tokens_inputs(w: Workload, device="cpu", *, gate: str | None = None, num_seqs: int | None = None,
                          heads: int | None = None, qk_heads: int | None = None, tokens: int | None = None,
                          slots: int | None = None, dk: int | None = None, dv: int | None = None,
-                         seed: int | None = None, qkv_dtype=None):
+                         seed: int | None = None, qkv_dtype=None, gate_dtype=torch.float32):
     """Several tokens per sequence from a pool of states: q, k [N, K, Hk, dk],
     v [N, K, H, dv], beta [N, K, H], log_alpha [N, K, H] or [N, K, H, dk],
     state_pool [P, H, dv, dk] (fp32), state_slots [N] (distinct slots, int32),
@@ -203,5 +205,5 @@ def decode_tokens_inputs(w: Workload, device="cpu", *, gate: str | None = None, 
     pool = 0.02 * torch.randn(P, H, dv, dk, generator=g, device=device, dtype=f32)
     slots_ = torch.randperm(P, generator=g, device=device)[:N].to(torch.int32)
     commit = torch.randint(0, K, (N,), generator=g, device=device, dtype=torch.int32)
-    return {"q": q, "k": k, "v": v, "beta": beta, "log_alpha": log_alpha, "state_pool": pool,
-            "state_slots": slots_, "num_commit": commit}
+    return {"q": q, "k": k, "v": v, "beta": beta.to(gate_dtype), "log_alpha": log_alpha.to(gate_dtype),
+            "state_pool": pool, "state_slots": slots_, "num_commit": commit}
