@@ -239,12 +239,13 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
                                         initial_state=g["initial_state"], out=gout, final_state=gfin)
     for _ in range(args.warmup):
         f()
-    t = time_per_launch(f, args.steps)
+    t, med, mn = time_calls(f, args.steps)
     by = prefill_alg_bytes(B, T, H, dk, dv, False, 4, Hk=Hk)
     res["grouped_prefill"] = {
         "workload": f"{wg.name}: B={B}, T={T}, {Hk} q/k heads shared by {H} value heads, d={dk}, bf16 q/k/v, "
                     "per-head decay, S0 given, fp32 out",
-        "us_per_launch": round(t * 1e6, 2), "Mtok_s": round(B * T / t / 1e6, 3), "alg_bytes": by,
+        "us_per_launch": round(t * 1e6, 2), "us_median": round(med * 1e6, 2), "us_min": round(mn * 1e6, 2),
+        "Mtok_s": round(B * T / t / 1e6, 3), "alg_bytes": by,
         "hbm_GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
         "mfma_frac": round(prefill_alg_flops(B, T, H, dk, dv, 32) / t / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)}
     del g, gout, gfin
@@ -259,14 +260,15 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
                                       num_commit=m["num_commit"], state_slots=m["state_slots"], out=mout)
     for _ in range(args.warmup):
         f()
-    t = time_per_launch(f, args.steps)
+    t, med, mn = time_calls(f, args.steps)
     n_written = int((m["num_commit"] > 0).sum())
     by = decode_tokens_alg_bytes(N, K, H, Hk, dk, dv, False, 4, n_written)
     res["multi_token_decode"] = {
         "workload": f"{wm.name}: {N} sequences x {H} value heads ({Hk} q/k heads), d={dk}, {K} tokens each, "
                     f"states in a pool of {wm.slots} slots, committed prefix uniform in [0, {K - 1}] "
                     f"({n_written} of {N} sequences write their state), per-head decay, fp32 out",
-        "us_per_call": round(t * 1e6, 2), "Mtok_s": round(N * K / t / 1e6, 4), "alg_bytes": by,
+        "us_per_call": round(t * 1e6, 2), "us_median": round(med * 1e6, 2), "us_min": round(mn * 1e6, 2),
+        "Mtok_s": round(N * K / t / 1e6, 4), "alg_bytes": by,
         "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
     return res
 
