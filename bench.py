@@ -6,15 +6,19 @@ decode step of 256 sequences x 32 heads (128x128 fp32 states, in place) with
 per-head decay and one with per-channel decay.  Prints one JSON line.
 
 Further workloads are timed in their own loops and reported beside the step
-(not part of `value`): the per-head-decay prefill at T=8192 (cache-warm, and
-with a 512 MiB write between calls so its ~170 MB working set is not left in
-the 256 MB last-level cache), the packed batch of 8 sequences (262144 tokens),
-the grouped-head Gated DeltaNet prefill (16 query-key heads shared by 48 value
-heads, T=32768) and the speculative multi-token decode over a pool of state
-slots (256 sequences x 48 value heads, 4 tokens each, a per-sequence committed
-prefix).  Two measured ceilings of the same box are reported with them: a
-large bf16 GEMM (the library GEMM, for the MFMA side) and a 512 MiB
-read-modify-write (for the HBM side).
+(not part of `value`):
+- the per-head-decay prefill at T=8192, cache-warm and with a 512 MiB write
+  between calls (its ~170 MB working set otherwise stays in the 256 MB
+  last-level cache);
+- the packed batch of 8 sequences (262144 tokens);
+- the grouped-head Gated DeltaNet prefill (16 query-key heads shared by 48
+  value heads, T=32768);
+- the speculative multi-token decode over a pool of state slots (256
+  sequences x 48 value heads, 4 tokens each, a per-sequence committed prefix);
+- the layer prologue on the grouped shape (T=32768, 10240 channels).
+Two measured ceilings of the same box are reported with them: a large bf16
+GEMM (the library GEMM, for the MFMA side) and a 512 MiB read-modify-write
+(for the HBM side).
 
 value = prefill throughput (B*T tokens, all heads) in Mtok/s.  Times come from
 HIP events on the stream the kernels are launched on, over the timed steps.
@@ -155,6 +159,13 @@ def cpu_baseline(inp, H, target_s):
                       f"workload, fp64, {reps} run(s), {total:.1f} s wall"}
 
 
+def prologue_alg_bytes(tokens, C, H, NA, N, x_bytes):
+    """x read and q/k/v written once, the taps, the gate logits read and the
+    gates written once, the convolution state read and written once."""
+    return (2 * tokens * C * x_bytes + C * 16 + 2 * tokens * H * 4 + 2 * tokens * H * NA * 4
+            + 2 * N * 3 * C * x_bytes)
+
+
 def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tokens_inputs):
     """The grouped-head prefill and the multi-token decode, each timed in its
     own loop of args.steps calls after args.warmup untimed ones."""
@@ -249,6 +260,28 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
         "hbm_GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
         "mfma_frac": round(prefill_alg_flops(B, T, H, dk, dv, 32) / t / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)}
     del g, gout, gfin
+
+    from workloads import prologue_inputs
+
+    wpl = WORKLOADS["prologue_gdn_32k"]
+    print(f"[bench] {wpl.name}", file=sys.stderr, flush=True)
+    pi = prologue_inputs(wpl, dev)
+    B, T, C = pi["x"].shape
+    H = pi["b_logit"].shape[-1]
+    f = lambda: gdr.gdr_layer_prologue(pi["x"], pi["conv_weight"], pi["a_logit"], pi["b_logit"],
+                                       num_qk_heads=pi["num_qk_heads"], head_dim_k=pi["head_dim_k"],
+                                       head_dim_v=pi["head_dim_v"], conv_state=pi["conv_state"])
+    for _ in range(args.warmup):
+        f()
+    t, med, mn = time_calls(f, args.steps)
+    by = prologue_alg_bytes(B * T, C, H, 1, B, 2)
+    res["layer_prologue"] = {
+        "workload": f"{wpl.name}: B={B}, T={T}, {C} projected channels ({pi['num_qk_heads']} q/k heads and {H} value "
+                    "heads of 128), bf16, width-4 convolution with its state, q/k L2 norm, per-head gates",
+        "us_per_call": round(t * 1e6, 2), "us_median": round(med * 1e6, 2), "us_min": round(mn * 1e6, 2),
+        "Mtok_s": round(B * T / t / 1e6, 3), "alg_bytes": by, "GBps": round(by / t / 1e9, 1),
+        "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del pi
 
     wm = WORKLOADS["mtp_decode_256x48"]
     print(f"[bench] {wm.name}", file=sys.stderr, flush=True)

@@ -21,8 +21,8 @@ import os
 
 import torch
 
-__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "gdr_decode_tokens", "prefill_chunked", "decode_step",
-           "decode_tokens",
+__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "gdr_decode_tokens", "gdr_layer_prologue", "prefill_chunked",
+           "decode_step", "decode_tokens", "layer_prologue",
            "gdr_state_bytes", "GdrError", "load_library", "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,7 @@ GDR_SUCCESS, GDR_ERROR_INVALID_VALUE, GDR_ERROR_NOT_SUPPORTED = 0, 1, 2
 GDR_ERROR_INSUFFICIENT_WORKSPACE, GDR_ERROR_LAUNCH_FAILED = 3, 4
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_HEAD, GDR_GATE_CHANNEL = 0, 1
+GDR_PROLOGUE_SILU, GDR_PROLOGUE_QK_NORM = 1, 2
 
 
 class GdrError(RuntimeError):
@@ -71,6 +72,9 @@ def load_library():
         lib.gdr_decode_tokens.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, p, p, p, p, p, p, p, p, p, i32, ctypes.c_float, p, p]
         lib.gdr_decode_tokens.restype = ctypes.c_int
+        lib.gdr_layer_prologue.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, p, p, p, p, p, i32,
+                                           p, p, p, p, p, p, p, p]
+        lib.gdr_layer_prologue.restype = ctypes.c_int
         lib.gdr_state_bytes.argtypes = [ctypes.c_int64] * 4
         lib.gdr_state_bytes.restype = ctypes.c_uint64
         lib.gdr_status_string.argtypes = [ctypes.c_int]
@@ -232,6 +236,49 @@ def gdr_decode_tokens(q, k, v, beta, log_alpha, state_pool, *, num_tokens=None, 
     return out
 
 
+def gdr_layer_prologue(x, conv_weight, a_logit, b_logit, *, num_qk_heads: int, head_dim_k: int, head_dim_v: int,
+                       conv_state=None, update_conv_state: bool = True, cu_seqlens=None, silu: bool = False,
+                       qk_norm: bool = True):
+    """Short causal convolution (width 4) of the projected channels, optional
+    SiLU, per-head L2 norm of q and k, and the gate activations, in one pass.
+    x [B, T, C] (bf16 or fp32) with C = 2 Hk dk + H dv channels (q, k, v);
+    conv_weight [C, 4] fp32 (tap j multiplies x_{t-3+j}); a_logit [B, T, H] or
+    [B, T, H, dk] and b_logit [B, T, H] fp32; conv_state [N, 3, C] (x's dtype)
+    or None (zeros), updated in place to each sequence's last three inputs
+    when update_conv_state.  Returns (q, k [B, T, Hk, dk], v [B, T, H, dv],
+    beta = sigmoid(b), log_alpha = -softplus(a))."""
+    lib = load_library()
+    dev = x.device
+    B, T, C = x.shape
+    H = b_logit.shape[-1]
+    Hk, dk, dv = num_qk_heads, head_dim_k, head_dim_v
+    if C != 2 * Hk * dk + H * dv or b_logit.shape != (B, T, H):
+        raise ValueError(f"x must be [B, T, 2*Hk*dk + H*dv] = [{B}, {T}, {2 * Hk * dk + H * dv}], b_logit [B, T, H]")
+    gate = GDR_GATE_HEAD if a_logit.dim() == 3 else GDR_GATE_CHANNEL
+    _need(x, "x", None, dev)
+    _need(conv_weight, "conv_weight", torch.float32, dev)
+    _need(a_logit, "a_logit", torch.float32, dev)
+    _need(b_logit, "b_logit", torch.float32, dev)
+    _need(conv_state, "conv_state", x.dtype, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    if conv_state is not None and conv_state.shape != (N, 3, C):
+        raise ValueError(f"conv_state must be [{N}, 3, {C}]")
+    q = torch.empty(B, T, Hk, dk, dtype=x.dtype, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty(B, T, H, dv, dtype=x.dtype, device=dev)
+    beta = torch.empty(B, T, H, dtype=torch.float32, device=dev)
+    log_alpha = torch.empty_like(a_logit)
+    shape = PrefillShape(B, T, H, dk, dv, N, Hk)
+    flags = (GDR_PROLOGUE_SILU if silu else 0) | (GDR_PROLOGUE_QK_NORM if qk_norm else 0)
+    _check(lib.gdr_layer_prologue(ctypes.byref(shape), gate, _dtype_code(x), _ptr(x), _ptr(conv_weight),
+                                  _ptr(conv_state), _ptr(conv_state) if update_conv_state else None, _ptr(cu_seqlens),
+                                  flags, _ptr(a_logit), _ptr(b_logit), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                  _ptr(log_alpha), _stream(dev)))
+    return q, k, v, beta, log_alpha
+
+
 prefill_chunked = gdr_prefill_chunked
 decode_step = gdr_decode_step
 decode_tokens = gdr_decode_tokens
+layer_prologue = gdr_layer_prologue

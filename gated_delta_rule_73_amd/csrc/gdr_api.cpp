@@ -255,6 +255,8 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     if (packed && s.batch != 1) return fail(GDR_ERROR_INVALID_VALUE, "cu_seqlens requires batch == 1");
     if (!packed && s.num_seqs != s.batch)
         return fail(GDR_ERROR_INVALID_VALUE, "dense batch needs num_seqs == batch (%d != %d)", s.num_seqs, s.batch);
+    if (packed && s.num_seqs == 0 && s.seqlen > 0)
+        return fail(GDR_ERROR_INVALID_VALUE, "packed tokens need at least one sequence");
     const int64_t tokens = (int64_t)s.batch * s.seqlen;
     if (tokens > INT32_MAX) return fail(GDR_ERROR_INVALID_VALUE, "more than 2^31-1 tokens");
     if ((int64_t)s.num_seqs * s.num_heads > INT32_MAX / 8)
@@ -385,6 +387,89 @@ gdr_status gdr_decode_tokens(int32_t num_seqs, int32_t max_tokens, int32_t num_h
                                        num_commit, state_slots, state_pool, num_slots, scale, out, a);
     if (st != GDR_SUCCESS || num_seqs == 0) return st;
     return launch_status(gdr::launch_decode_tokens(a, static_cast<hipStream_t>(hip_stream)), "gdr_decode_tokens");
+}
+
+gdr_status gdr_layer_prologue(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype x_dtype, const void *x,
+                              const float *conv_weight, const void *conv_state_in, void *conv_state_out,
+                              const int32_t *cu_seqlens, int32_t flags, const float *a_logit, const float *b_logit,
+                              void *q, void *k, void *v, float *beta, float *log_alpha, void *hip_stream) {
+    if (!shape) return fail(GDR_ERROR_INVALID_VALUE, "shape is NULL");
+    const gdr_prefill_shape s = *shape;
+    if (s.batch < 1 || s.seqlen < 0 || s.num_heads < 1 || s.head_dim_k < 1 || s.head_dim_v < 1 || s.num_seqs < 0)
+        return fail(GDR_ERROR_INVALID_VALUE, "bad shape (batch=%d seqlen=%d heads=%d dk=%d dv=%d num_seqs=%d)",
+                    s.batch, s.seqlen, s.num_heads, s.head_dim_k, s.head_dim_v, s.num_seqs);
+    int hk = 0;
+    if (resolve_qk_heads(s.num_heads, s.num_qk_heads, hk) != GDR_SUCCESS) return GDR_ERROR_INVALID_VALUE;
+    if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
+    if (!valid_dtype(x_dtype)) return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype %d", (int)x_dtype);
+    if (flags & ~(GDR_PROLOGUE_SILU | GDR_PROLOGUE_QK_NORM))
+        return fail(GDR_ERROR_INVALID_VALUE, "unknown flags 0x%x", (unsigned)flags);
+    const bool packed = cu_seqlens != nullptr;
+    if (packed && s.batch != 1) return fail(GDR_ERROR_INVALID_VALUE, "cu_seqlens requires batch == 1");
+    if (!packed && s.num_seqs != s.batch)
+        return fail(GDR_ERROR_INVALID_VALUE, "dense batch needs num_seqs == batch (%d != %d)", s.num_seqs, s.batch);
+    if (packed && s.num_seqs == 0 && s.seqlen > 0)
+        return fail(GDR_ERROR_INVALID_VALUE, "packed tokens need at least one sequence");
+    const int dk = s.head_dim_k, dv = s.head_dim_v;
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_k %d not in {16, 32, 64, 128}", dk);
+    if (dv % 8 != 0) return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_v %d not a multiple of 8", dv);
+    const int64_t tokens = (int64_t)s.batch * s.seqlen;
+    const int64_t C = 2 * (int64_t)hk * dk + (int64_t)s.num_heads * dv;
+    if (tokens > INT32_MAX || C > INT32_MAX / 8) return fail(GDR_ERROR_INVALID_VALUE, "problem too large");
+    const bool kda = gate == GDR_GATE_CHANNEL;
+    if (tokens > 0 && (!x || !conv_weight || !a_logit || !b_logit || !q || !k || !v || !beta || !log_alpha))
+        return fail(GDR_ERROR_INVALID_VALUE, "x, conv_weight, a_logit, b_logit, q, k, v, beta and log_alpha must be non-NULL");
+    const void *a16[] = {x, conv_weight, conv_state_in, conv_state_out, q, k, v};
+    const char *n16[] = {"x", "conv_weight", "conv_state_in", "conv_state_out", "q", "k", "v"};
+    for (int i = 0; i < 7; ++i)
+        if (!aligned(a16[i], 16)) return fail(GDR_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", n16[i]);
+    if (!aligned(a_logit, 4) || !aligned(b_logit, 4) || !aligned(beta, 4) || !aligned(log_alpha, 4) ||
+        !aligned(cu_seqlens, 4))
+        return fail(GDR_ERROR_INVALID_VALUE, "gates and cu_seqlens must be 4-byte aligned");
+    const size_t es = dsize(x_dtype), ng = (size_t)tokens * s.num_heads, na = kda ? ng * dk : ng;
+    const size_t st_bytes = (size_t)s.num_seqs * 3 * C * es;
+    const Range in[] = {range("x", x, (size_t)tokens * C * es), range("conv_weight", conv_weight, (size_t)C * 16),
+                        range("conv_state_in", conv_state_in, conv_state_in ? st_bytes : 0),
+                        range("a_logit", a_logit, na * 4), range("b_logit", b_logit, ng * 4),
+                        range("cu_seqlens", cu_seqlens, packed ? 4 * ((size_t)s.num_seqs + 1) : 0)};
+    const Range outs[] = {range("q", q, (size_t)tokens * hk * dk * es), range("k", k, (size_t)tokens * hk * dk * es),
+                          range("v", v, (size_t)tokens * s.num_heads * dv * es), range("beta", beta, ng * 4),
+                          range("log_alpha", log_alpha, na * 4),
+                          range("conv_state_out", conv_state_out, conv_state_out ? st_bytes : 0)};
+    for (const Range &o : outs) {
+        for (const Range &r : in) {
+            const bool same_state = o.lo == reinterpret_cast<uintptr_t>(conv_state_out) &&
+                                    r.lo == reinterpret_cast<uintptr_t>(conv_state_in) && conv_state_in == conv_state_out;
+            if (overlaps(o, r) && !same_state) return fail(GDR_ERROR_INVALID_VALUE, "%s overlaps %s", o.name, r.name);
+        }
+        for (const Range &o2 : outs)
+            if (&o2 != &o && overlaps(o, o2)) return fail(GDR_ERROR_INVALID_VALUE, "%s overlaps %s", o.name, o2.name);
+    }
+    if (tokens == 0 && !conv_state_out) return ok();
+    gdr::PrologueArgs a{};
+    a.batch = s.batch;
+    a.seqlen = s.seqlen;
+    a.num_seqs = s.num_seqs;
+    a.num_heads = s.num_heads;
+    a.num_qk_heads = hk;
+    a.dk = dk;
+    a.dv = dv;
+    a.kda = kda;
+    a.x_bf16 = x_dtype == GDR_BF16;
+    a.silu = (flags & GDR_PROLOGUE_SILU) != 0;
+    a.qk_norm = (flags & GDR_PROLOGUE_QK_NORM) != 0;
+    a.x = x;
+    a.conv_weight = conv_weight;
+    a.state_in = conv_state_in;
+    a.state_out = conv_state_out;
+    a.cu_seqlens = cu_seqlens;
+    a.a_logit = a_logit;
+    a.b_logit = b_logit;
+    a.q = q; a.k = k; a.v = v;
+    a.beta = beta;
+    a.log_alpha = log_alpha;
+    return launch_status(gdr::launch_prologue(a, static_cast<hipStream_t>(hip_stream)), "gdr_layer_prologue");
 }
 
 }  // extern "C"

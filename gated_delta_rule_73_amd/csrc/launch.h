@@ -55,6 +55,22 @@ constexpr size_t chunk_record_stride(int dk, int chunk, bool kda, int es) {
     return (chunk_record_bytes(dk, chunk, kda, es) + 255) & ~size_t(255);
 }
 
+// Layer prologue (prologue.hip): short convolution, optional SiLU and q/k
+// norm, gate activations, convolution state.
+struct PrologueArgs {
+    int batch, seqlen, num_seqs, num_heads, num_qk_heads, dk, dv;
+    bool kda, x_bf16, silu, qk_norm;
+    const void *x;                  // [batch, seqlen, C], C = 2 Hk dk + H dv
+    const float *conv_weight;       // [C, 4]
+    const void *state_in;           // [num_seqs, 3, C] or NULL
+    void *state_out;                // [num_seqs, 3, C] or NULL (may equal state_in)
+    const int32_t *cu_seqlens;
+    const float *a_logit, *b_logit;
+    void *q, *k, *v;
+    float *beta, *log_alpha;
+};
+
+hipError_t launch_prologue(const PrologueArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t st);
 hipError_t launch_decode_tokens(const DecodeArgs &p, hipStream_t st);
 

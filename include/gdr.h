@@ -250,6 +250,58 @@ gdr_status gdr_decode_tokens(int32_t num_seqs, int32_t max_tokens, int32_t num_h
                              const int32_t *state_slots, float *state_pool, int32_t num_slots,
                              float scale, void *out, void *hip_stream);
 
+/*
+ * Layer prologue: the steps between a linear-attention layer's input
+ * projections and the recurrence, in one pass (page "Qwen3.8-Flash-Next and
+ * GLM-5.3-Flash share a 3:1 long-context pattern", section "Kimi Delta
+ * Attention extends recurrent memory control": a short convolution of kernel
+ * four; page "How the New Flash Models Work...", section "Serving: prefill and
+ * decode are different problems": the convolution state travels with the
+ * recurrent state from prefill to decode).  The pages name no activation, no
+ * normalisation and no gate parameterisation; the flags make the two common
+ * choices available and the gates are the write strength and decay in their
+ * plainest form.
+ *
+ * x holds, per token, the C = 2 Hk dk + H dv projected channels: q (Hk heads
+ * of dk), then k (Hk x dk), then v (H x dv).  For every channel c and token t
+ * of a sequence:
+ *     y_t[c] = sum_{j<4} w[c][j] x_{t-3+j}[c]      (causal, per channel)
+ * where the three inputs before a sequence's first token are its convolution
+ * state (zeros when conv_state_in is NULL); then
+ *     y <- y * sigmoid(y)                  if flags & GDR_PROLOGUE_SILU
+ *     q, k <- y / |y| per head (over dk)   if flags & GDR_PROLOGUE_QK_NORM
+ *                                          (a zero vector stays zero)
+ * and q, k, v <- y in x's dtype (bf16: rounded to nearest even).  Gates:
+ *     beta = sigmoid(b_logit),  log_alpha = -softplus(a_logit)  (fp32),
+ * so alpha = exp(log_alpha) lies in (0, 1).  The new convolution state of each
+ * sequence is its last three inputs (older state rows when it has fewer than
+ * three tokens).  With seqlen = 1 and batch = num_seqs the call is the decode
+ * step's prologue.
+ *
+ *  shape          as for gdr_prefill_chunked (dense batch or packed by cu_seqlens)
+ *  x              [batch, seqlen, C]         bf16 or fp32 (x_dtype)
+ *  conv_weight    [C, 4] fp32: tap j multiplies x_{t-3+j}
+ *  conv_state_in  [num_seqs, 3, C] x_dtype, or NULL (zeros); row r holds the
+ *                 input 3 - r tokens before the sequence's first
+ *  conv_state_out [num_seqs, 3, C] x_dtype, or NULL (not written); may equal
+ *                 conv_state_in (updated in place)
+ *  cu_seqlens     NULL (dense) or int32 [num_seqs + 1]
+ *  a_logit        [batch, seqlen, H] (GDR_GATE_HEAD) or [batch, seqlen, H, dk]   fp32
+ *  b_logit        [batch, seqlen, H]                                               fp32
+ *  q, k           [batch, seqlen, Hk, dk]   out, x_dtype
+ *  v              [batch, seqlen, H, dv]    out, x_dtype
+ *  beta, log_alpha  out, fp32, shaped as b_logit and a_logit
+ * Limits: head_dim_k in {16, 32, 64, 128}; head_dim_v a multiple of 8;
+ * x, states, q, k, v and conv_weight 16-byte aligned.  Outputs must not
+ * overlap any input or each other.
+ */
+#define GDR_PROLOGUE_SILU 1
+#define GDR_PROLOGUE_QK_NORM 2
+gdr_status gdr_layer_prologue(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype x_dtype, const void *x,
+                              const float *conv_weight, const void *conv_state_in, void *conv_state_out,
+                              const int32_t *cu_seqlens, int32_t flags, const float *a_logit, const float *b_logit,
+                              void *q, void *k, void *v, float *beta, float *log_alpha, void *hip_stream);
+
 /* Bytes of fp32 recurrent state for num_seqs x num_heads heads of d_v x d_k
  * (the per-layer state the pages size in their state-size table). */
 uint64_t gdr_state_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim_k, int64_t head_dim_v);

@@ -217,3 +217,58 @@ def decode_tokens(q, k, v, beta, log_alpha, state_pool, *, num_tokens=None, num_
             out[n, c:t] = o2[0]
         written[n, :t] = True
     return out, written, new_pool
+
+
+def layer_prologue(x, conv_weight, a_logit, b_logit, *, num_qk_heads, head_dim_k, head_dim_v,
+                   conv_state=None, seq_bounds=None, silu=False, qk_norm=True):
+    """The layer prologue in fp64, written from its definition: for each
+    sequence, the three inputs before its first token (its convolution state,
+    or zeros) are put in front of its inputs and each channel is convolved
+    causally with its four taps (page "Qwen3.8-Flash-Next and GLM-5.3-Flash
+    share a 3:1 long-context pattern", section "Kimi Delta Attention extends
+    recurrent memory control": a short convolution of kernel four; page "How
+    the New Flash Models Work...", section "Serving: prefill and decode are
+    different problems": the convolution state goes with the recurrent state):
+
+        y_t[c] = sum_j w[c, j] x_{t-3+j}[c];  optionally y <- y * sigmoid(y);
+        q, k, v = the channel groups of y; optionally q, k <- q/|q|, k/|k| per head;
+        beta = sigmoid(b);  log alpha = -softplus(a) = -log(1 + e^a).
+
+    The new state of a sequence is the last three rows of its padded inputs.
+    x [B, T, C]; conv_weight [C, 4]; a_logit [B, T, H(, dk)]; b_logit [B, T, H];
+    conv_state [N, 3, C] or None; seq_bounds (packed, B == 1) or None.
+    Returns (q, k, v, beta, log_alpha, new_state) as fp64 arrays.
+    """
+    x, w, a, b = (_f64(t) for t in (x, conv_weight, a_logit, b_logit))
+    st = _f64(conv_state)
+    B, T, C = x.shape
+    Hk, dk, dv = num_qk_heads, head_dim_k, head_dim_v
+    H = b.shape[-1]
+    if C != 2 * Hk * dk + H * dv:
+        raise ValueError("channel count does not match the head sizes")
+    bounds = np.arange(B + 1) * T if seq_bounds is None else np.asarray(seq_bounds, dtype=np.int64)
+    N = len(bounds) - 1
+    rows = x.reshape(B * T, C)
+    y = np.zeros_like(rows)
+    new_state = np.zeros((N, 3, C))
+    for n in range(N):
+        lo, hi = int(bounds[n]), int(bounds[n + 1])
+        prev = st[n] if st is not None else np.zeros((3, C))
+        padded = np.concatenate([prev, rows[lo:hi]], axis=0)     # padded[i] = input at position lo - 3 + i
+        for t in range(hi - lo):
+            y[lo + t] = sum(w[:, j] * padded[t + j] for j in range(4))
+        new_state[n] = padded[-3:]
+    if silu:
+        y = y / (1.0 + np.exp(-y))
+    y = y.reshape(B, T, C)
+    q = y[..., :Hk * dk].reshape(B, T, Hk, dk)
+    k = y[..., Hk * dk:2 * Hk * dk].reshape(B, T, Hk, dk)
+    v = y[..., 2 * Hk * dk:].reshape(B, T, H, dv)
+    if qk_norm:
+        def unit(z):
+            nrm = np.sqrt((z * z).sum(-1, keepdims=True))
+            return np.where(nrm > 0, z / np.where(nrm > 0, nrm, 1.0), 0.0)
+        q, k = unit(q), unit(k)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    log_alpha = -np.logaddexp(0.0, a)
+    return q, k, v, beta, log_alpha, new_state

@@ -109,6 +109,7 @@ def _decode_tokens(N=4, K=4, H=2, Hk=0, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=
     (dict(shape=(1, 64, 2, 64, 48, 1, 0), dvs=32), 1, "does not divide"),
     (dict(shape=(2, 64, 2, 64, 64, 1, 0)), 1, "num_seqs == batch"),
     (dict(shape=(2, 64, 2, 64, 64, 2, 0), cu=A + 40 * MB), 1, "batch == 1"),
+    (dict(shape=(1, 64, 2, 64, 64, 0, 0), cu=A + 40 * MB), 1, "at least one sequence"),
     (dict(q=None), 1, "non-NULL"),
     (dict(q=A + 2), 1, "16-byte aligned"),
     (dict(out=A + 8 * MB + 64), 1, "out overlaps k"),
@@ -219,3 +220,50 @@ def test_binding_raises_without_gpu_tensors():
     with pytest.raises(Exception):
         gdr.gdr_prefill_chunked(q, q, q, torch.zeros(1, 4, 1, dtype=torch.float32),
                                 torch.zeros(1, 4, 1, 3, 3))
+
+
+def _prologue(shape=(1, 64, 2, 64, 64, 1, 1), gate=0, xdt=1, x=A, w=A + 4 * MB, si=None, so=None, cu=None, flags=2,
+              a=A + 5 * MB, b=A + 6 * MB, q=A + 8 * MB, k=A + 10 * MB, v=A + 12 * MB, beta=A + 14 * MB,
+              la=A + 15 * MB):
+    lib = gdr.load_library()
+    sh = gdr.PrefillShape(*shape)
+    v_ = lambda z: None if z is None else ctypes.c_void_p(z)
+    st = lib.gdr_layer_prologue(ctypes.byref(sh), gate, xdt, v_(x), v_(w), v_(si), v_(so), v_(cu), flags, v_(a), v_(b),
+                                v_(q), v_(k), v_(v), v_(beta), v_(la), None)
+    return st, lib.gdr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(shape=(0, 64, 2, 64, 64, 0, 1)), 1, "bad shape"),
+    (dict(shape=(1, 64, 3, 64, 64, 1, 2)), 1, "does not divide"),
+    (dict(gate=4), 1, "gate"),
+    (dict(xdt=3), 1, "dtype"),
+    (dict(flags=4), 1, "flags"),
+    (dict(shape=(1, 64, 2, 48, 64, 1, 1)), 2, "head_dim_k"),
+    (dict(shape=(1, 64, 2, 64, 60, 1, 1)), 2, "head_dim_v"),
+    (dict(shape=(2, 64, 2, 64, 64, 2, 1), cu=A + 20 * MB), 1, "batch == 1"),
+    (dict(shape=(2, 64, 2, 64, 64, 1, 1)), 1, "num_seqs == batch"),
+    (dict(shape=(1, 64, 2, 64, 64, 0, 1), cu=A + 20 * MB), 1, "at least one sequence"),
+    (dict(x=None), 1, "non-NULL"),
+    (dict(w=A + 4 * MB + 8), 1, "conv_weight is not 16-byte"),
+    (dict(si=A + 20 * MB + 4), 1, "conv_state_in is not 16-byte"),
+    (dict(a=A + 5 * MB + 2), 1, "4-byte"),
+    (dict(q=A + 112), 1, "q overlaps x"),
+    (dict(k=A + 8 * MB + 64), 1, "q overlaps k"),
+    (dict(so=A + 5 * MB), 1, "conv_state_out overlaps a_logit"),
+    (dict(beta=A + 6 * MB), 1, "beta overlaps b_logit"),
+])
+def test_prologue_rejects(kw, status, msg):
+    st, err = _prologue(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_prologue_accepts_in_place_state_and_empty_batch():
+    # in-place state passes validation (then fails at the launch: no GPU here)
+    st, err = _prologue(si=A + 20 * MB, so=A + 20 * MB)
+    assert st in (0, 4), err
+    assert "overlaps" not in err
+    st, err = _prologue(shape=(1, 0, 2, 64, 64, 1, 1), x=None, w=None, a=None, b=None, q=None, k=None, v=None,
+                        beta=None, la=None)
+    assert st == 0, err

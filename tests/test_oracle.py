@@ -344,3 +344,112 @@ def test_decode_tokens_verify_then_replay_equals_decoding_the_accepted_tokens():
         _, s_j = oracle.recurrence(q[n:n + 1, :j], k[n:n + 1, :j], v[n:n + 1, :j], beta[n:n + 1, :j],
                                    la[n:n + 1, :j], initial_state=pool[n:n + 1])
         np.testing.assert_allclose(p2[n], s_j[0], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------- layer prologue ----
+def _pro_case(T, Hk=1, H=2, dk=4, dv=2, seed=0, per_channel=False, state=True):
+    r = np.random.default_rng(seed)
+    C = 2 * Hk * dk + H * dv
+    x = r.standard_normal((1, T, C))
+    w = r.standard_normal((C, 4))
+    a = r.standard_normal((1, T, H, dk) if per_channel else (1, T, H))
+    b = r.standard_normal((1, T, H))
+    st = r.standard_normal((1, 3, C)) if state else None
+    return x, w, a, b, st, dict(num_qk_heads=Hk, head_dim_k=dk, head_dim_v=dv)
+
+
+def _split(y, Hk, dk, H, dv):
+    return (y[..., :Hk * dk].reshape(*y.shape[:-1], Hk, dk), y[..., Hk * dk:2 * Hk * dk].reshape(*y.shape[:-1], Hk, dk),
+            y[..., 2 * Hk * dk:].reshape(*y.shape[:-1], H, dv))
+
+
+def test_prologue_single_taps_are_shifts():
+    """Tap 3 alone passes x_t through; tap 0 alone gives x_{t-3}, whose first
+    three values are the state rows in order (row r: the input 3 - r tokens
+    before the first); the taps of a channel act on that channel only."""
+    x, w, a, b, st, kw = _pro_case(7, seed=50)
+    C = x.shape[-1]
+    for tap, expect in ((3, x[0]), (0, np.concatenate([st[0], x[0, :-3]])), (2, np.concatenate([st[0, 2:], x[0, :-1]]))):
+        wt = np.zeros((C, 4))
+        wt[:, tap] = 1.0
+        q, k, v, *_ = oracle.layer_prologue(x, wt, a, b, conv_state=st, qk_norm=False, **kw)
+        eq, ek, ev = _split(expect[None], 1, 4, 2, 2)
+        np.testing.assert_array_equal(q, eq)
+        np.testing.assert_array_equal(k, ek)
+        np.testing.assert_array_equal(v, ev)
+
+
+def test_prologue_constant_input_closed_form():
+    """x_t = c for all t with a zero state: y_t = c * (w_3 + ... + w_{3-t})
+    (the taps that reach a token inside the sequence)."""
+    T = 6
+    x, w, a, b, _, kw = _pro_case(T, seed=51, state=False)
+    c = np.linspace(-1.0, 2.0, x.shape[-1])
+    xc = np.broadcast_to(c, x.shape).copy()
+    q, k, v, *_ = oracle.layer_prologue(xc, w, a, b, qk_norm=False, **kw)
+    y = np.concatenate([q.reshape(1, T, -1), k.reshape(1, T, -1), v.reshape(1, T, -1)], axis=-1)
+    for t in range(T):
+        np.testing.assert_allclose(y[0, t], c * w[:, max(0, 3 - t):].sum(1), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("split_at", [1, 2, 3, 5])
+def test_prologue_continuation_through_the_state(split_at):
+    """Running the first tokens, then the rest from the returned state, gives
+    the single run's outputs and final state (also when the first part is
+    shorter than the convolution)."""
+    x, w, a, b, st, kw = _pro_case(9, seed=52, per_channel=True)
+    full = oracle.layer_prologue(x, w, a, b, conv_state=st, silu=True, **kw)
+    p1 = oracle.layer_prologue(x[:, :split_at], w, a[:, :split_at], b[:, :split_at], conv_state=st, silu=True, **kw)
+    p2 = oracle.layer_prologue(x[:, split_at:], w, a[:, split_at:], b[:, split_at:], conv_state=p1[5], silu=True, **kw)
+    for i in range(5):
+        np.testing.assert_allclose(np.concatenate([p1[i], p2[i]], axis=1), full[i], rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(p2[5], full[5])
+    np.testing.assert_array_equal(full[5][0], x[0, -3:])
+
+
+def test_prologue_short_sequence_state_keeps_older_rows():
+    x, w, a, b, st, kw = _pro_case(2, seed=53)
+    *_, new = oracle.layer_prologue(x, w, a, b, conv_state=st, **kw)
+    np.testing.assert_array_equal(new[0], np.concatenate([st[0, 2:], x[0]]))
+    *_, same = oracle.layer_prologue(x[:, :0], w, a[:, :0], b[:, :0], conv_state=st, **kw)
+    np.testing.assert_array_equal(same, st)
+
+
+def test_prologue_norm_silu_and_gates():
+    x, w, a, b, st, kw = _pro_case(5, Hk=2, H=3, dk=4, dv=2, seed=54, per_channel=True)
+    q0, k0, v0, *_ = oracle.layer_prologue(x, w, a, b, conv_state=st, qk_norm=False, **kw)
+    q, k, v, beta, la, _ = oracle.layer_prologue(x, w, a, b, conv_state=st, qk_norm=True, **kw)
+    np.testing.assert_allclose(np.linalg.norm(q, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(q * np.linalg.norm(q0, axis=-1, keepdims=True), q0, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(v, v0)
+    # a zero head stays zero
+    xz = x.copy()
+    xz[..., :4] = 0.0
+    stz = st.copy()
+    stz[..., :4] = 0.0
+    qz, *_ = oracle.layer_prologue(xz, w, a, b, conv_state=stz, **kw)
+    assert not qz[..., 0, :].any()
+    # silu(y) = y / (1 + e^-y), applied before the norm
+    qs, ks, vs, *_ = oracle.layer_prologue(x, w, a, b, conv_state=st, silu=True, qk_norm=False, **kw)
+    np.testing.assert_allclose(vs, v0 / (1 + np.exp(-v0)), rtol=1e-14)
+    # gates: closed forms and values at 0
+    np.testing.assert_allclose(beta, 1 / (1 + np.exp(-b)), rtol=1e-15)
+    np.testing.assert_allclose(la, np.log(1 / (1 + np.exp(a))), rtol=1e-13)
+    z = np.zeros((1, 1, 3))
+    *_, bz, lz, _ = oracle.layer_prologue(x[:, :1], w, z, z, conv_state=st, **kw)
+    assert np.all(bz == 0.5) and np.allclose(lz, -np.log(2.0), rtol=1e-15)
+
+
+def test_prologue_packed_equals_separate_runs():
+    lens = [4, 0, 1, 6]
+    T = sum(lens)
+    x, w, a, b, _, kw = _pro_case(T, seed=55)
+    st = np.random.default_rng(56).standard_normal((len(lens), 3, x.shape[-1]))
+    bounds = np.concatenate([[0], np.cumsum(lens)])
+    full = oracle.layer_prologue(x, w, a, b, conv_state=st, seq_bounds=bounds, **kw)
+    for n in range(len(lens)):
+        lo, hi = bounds[n], bounds[n + 1]
+        part = oracle.layer_prologue(x[:, lo:hi], w, a[:, lo:hi], b[:, lo:hi], conv_state=st[n:n + 1], **kw)
+        for i in range(5):
+            np.testing.assert_array_equal(full[i][:, lo:hi], part[i])
+        np.testing.assert_array_equal(full[5][n], part[5][0])

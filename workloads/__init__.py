@@ -82,6 +82,11 @@ WORKLOADS = {
     # previous draft's accepted tokens replayed and committed in the same call
     "mtp_decode_256x48": Workload("mtp_decode_256x48", "decode", heads=48, qk_heads=16, dk=128, dv=128,
                                   qkv_dtype=torch.bfloat16, gate="head", batch=256, tokens=4, slots=512, seed=6),
+    # the layer prologue on that shape: the 10240 projected q/k/v channels of
+    # 32768 tokens, with a convolution state
+    "prologue_gdn_32k": Workload("prologue_gdn_32k", "prologue", heads=48, qk_heads=16, dk=128, dv=128,
+                                 qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=32768, init_state=True,
+                                 seed=7),
 }
 
 
@@ -207,3 +212,43 @@ def decode_tokens_inputs(w: Workload, device="cpu", *, gate: str | None = None, 
     commit = torch.randint(0, K, (N,), generator=g, device=device, dtype=torch.int32)
     return {"q": q, "k": k, "v": v, "beta": beta.to(gate_dtype), "log_alpha": log_alpha.to(gate_dtype),
             "state_pool": pool, "state_slots": slots_, "num_commit": commit}
+
+
+def prologue_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batch: int | None = None,
+                    heads: int | None = None, qk_heads: int | None = None, dk: int | None = None,
+                    dv: int | None = None, lengths=None, gate: str | None = None, seed: int | None = None,
+                    init_state: bool | None = None, x_dtype=None):
+    """Inputs of the layer prologue: x [B, T, C] (C = 2 Hk dk + H dv) ~ N(0, 1)
+    in x_dtype, convolution taps [C, 4] ~ N(0, 0.5^2) (fp32), gate logits
+    a [B, T, H(, dk)] and b [B, T, H] ~ N(0, 1) (fp32), a convolution state
+    [N, 3, C] ~ N(0, 1) when asked for, cu_seqlens for packed lengths.
+    Draw order: x, taps, a, b, state."""
+    B = w.batch if batch is None else batch
+    T = w.seqlen if seqlen is None else seqlen
+    H = w.heads if heads is None else heads
+    if qk_heads:
+        Hk = qk_heads
+    else:
+        Hk = (w.qk_heads or w.heads) if heads is None else H
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    gate = w.gate if gate is None else gate
+    dt = w.qkv_dtype if x_dtype is None else x_dtype
+    init_state = w.init_state if init_state is None else init_state
+    cu = None
+    N = B
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        T, B, N = int(lengths.sum()), 1, len(lengths)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=device)
+    C = 2 * Hk * dk + H * dv
+    g = _gen(device, w.seed if seed is None else seed)
+    f32 = torch.float32
+    x = torch.randn(B, T, C, generator=g, device=device, dtype=f32).to(dt)
+    wt = 0.5 * torch.randn(C, 4, generator=g, device=device, dtype=f32)
+    ashape = (B, T, H) if gate == "head" else (B, T, H, dk)
+    a = torch.randn(*ashape, generator=g, device=device, dtype=f32)
+    b = torch.randn(B, T, H, generator=g, device=device, dtype=f32)
+    st = torch.randn(N, 3, C, generator=g, device=device, dtype=f32).to(dt) if init_state else None
+    return {"x": x, "conv_weight": wt, "a_logit": a, "b_logit": b, "conv_state": st, "cu_seqlens": cu,
+            "num_qk_heads": Hk, "head_dim_k": dk, "head_dim_v": dv}
