@@ -44,7 +44,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 PROFILE_PMC = os.path.join(ROOT, "profiles", "prefill_kda_32k_traffic.json")
-KERNEL_SOURCES = ["prefill_impl.h", "prefill_shapes.h", "prefill_bf16_kda.hip", "prefill.hip", "gdr_api.cpp", "launch.h"]
+# the sources that define the headline prefill's two kernels and their launch
+KERNEL_SOURCES = ["prefill_impl.h", "prefill_shapes.h", "prefill_bf16_kda.hip", "prefill.hip"]
 
 
 def kernel_source_hash() -> str:
