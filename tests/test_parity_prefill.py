@@ -310,3 +310,36 @@ def test_prefill_continuation_then_decode():
     torch.cuda.synchronize()
     assert_close("out", torch.cat(outs, dim=1), ref_o, TOL[torch.bfloat16])
     assert_close("final_state", state, ref_s, TOL[torch.bfloat16])
+
+
+# ------------------------------------------------------------ edge cases ----
+@pytest.mark.parametrize("dk,dv,gate,Hk", [(128, 256, "channel", 0), (128, 256, "head", 2), (32, 256, "head", 0),
+                                           (64, 208, "channel", 0)])
+def test_prefill_largest_value_dims(dk, dv, gate, Hk):
+    """head_dim_v up to its limit (256: eight 32-channel slices)."""
+    inp = _small(dk, dv, 4, 150, gate, torch.bfloat16, True, seed=90 + dv, Hk=Hk)
+    _check_all(inp, f"dk={dk} dv={dv} {gate} Hk={Hk}")
+
+
+def test_prefill_empty_dense_batch_keeps_the_state():
+    """T = 0: no outputs, and the final state is the initial state exactly."""
+    inp = _small(128, 128, 3, 0, "channel", torch.bfloat16, True, seed=95, B=2)
+    out, fin = _gpu(inp)
+    assert out.numel() == 0
+    assert torch.equal(fin, inp["initial_state"])
+
+
+def test_prefill_one_chunk_ragged():
+    for T in (5, 31, 32, 33):
+        inp = _small(128, 128, 2, T, "channel", torch.bfloat16, True, seed=96 + T)
+        _check_all(inp, f"T={T}")
+
+
+@pytest.mark.slow
+def test_prefill_long_single_sequence():
+    """One sequence of 65536 tokens (2048 chunks on one chain), 4 heads."""
+    w = Workload("long", "prefill", heads=4, dk=128, dv=128, qkv_dtype=torch.bfloat16, gate="channel", batch=1,
+                 seqlen=65536, init_state=True, seed=97)
+    inp = prefill_inputs(w, DEV)
+    out, fin = _check_sampled(inp, [(0, 0), (0, 3)], "long single sequence")
+    assert torch.isfinite(out.float()).all()
