@@ -601,11 +601,15 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     f32x4 accA[NT], accM[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) accA[t] = accM[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (16-bit operands: the two halves hh of a lane's eight channels are
+    // adjacent in the stored k-order, so they leave as one 16-byte store)
+    constexpr bool QT_MERGE = sizeof(ST) == 2 && DK >= 32;
     for (int s = wave; s < NSTEP; s += 4) {
         F8 fk[NB], fq[NB], fql[NB], fr[NB], frl[NB];
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             const int t = 16 * rb + lr;
+            ST qt8[8];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int ch = 32 * s + 16 * hh + 4 * lg;
@@ -646,8 +650,11 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
                         qt[i] = (ST)(qf[i] * e * p.scale);
                     }
                 }
-                if (valid) store_vec<ST, 4>(&rec.Qt[t][kpos<ST>(ch)], qt);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qt8[4 * hh + i] = qt[i];
+                if (!QT_MERGE && valid) store_vec<ST, 4>(&rec.Qt[t][kpos<ST>(ch)], qt);
             }
+            if constexpr (QT_MERGE) store_vec<ST, 8>(&rec.Qt[t][kpos<ST>(32 * s + 4 * lg)], qt8);
         }
 #pragma unroll
         for (int I = 0; I < NB; ++I)
@@ -677,34 +684,41 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
         }
     __syncthreads();
 
-    // ---- D: sum the partial tiles; masks, beta and (GDN) the decay factors
-    for (int e = tid; e < C * C / 4; e += 256) {
-        const int R = e / (C / 4), c0 = (e % (C / 4)) * 4;
-        const int I = R >> 4, J = c0 >> 4, r = R & 15, cc = c0 & 15;
-        f32x4 a{0.f, 0.f, 0.f, 0.f}, m{0.f, 0.f, 0.f, 0.f};
-        if (J <= I) {
-            const int tt = I * (I + 1) / 2 + J;
+    // ---- D: sum the partial tiles; masks, beta and (GDN) the decay factors.
+    // (16-bit operands, C = 32: a thread takes columns c0 and c0 + 16, which
+    // are adjacent in the stored k-order, and stores both at once.)
+    constexpr int MH = (sizeof(ST) == 2 && C == 32) ? 2 : 1;   // column halves per thread
+    for (int e = tid; e < C * C / (4 * MH); e += 256) {
+        const int R = e / (C / (4 * MH)), cb0 = (e % (C / (4 * MH))) * 4;
+        ST mv[4 * MH];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                a += *reinterpret_cast<const f32x4 *>(&sm.u.Pt[w][tt][r][cc]);
-                m += *reinterpret_cast<const f32x4 *>(&sm.u.Pt[w][NT + tt][r][cc]);
+        for (int hf = 0; hf < MH; ++hf) {
+            const int c0 = cb0 + 16 * hf;
+            const int I = R >> 4, J = c0 >> 4, r = R & 15, cc = c0 & 15;
+            f32x4 a{0.f, 0.f, 0.f, 0.f}, m{0.f, 0.f, 0.f, 0.f};
+            if (J <= I) {
+                const int tt = I * (I + 1) / 2 + J;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    a += *reinterpret_cast<const f32x4 *>(&sm.u.Pt[w][tt][r][cc]);
+                    m += *reinterpret_cast<const f32x4 *>(&sm.u.Pt[w][NT + tt][r][cc]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = c0 + i;
+                float fa = c < R ? a[i] * sm.beta[R] : 0.f;
+                float fm = c <= R ? m[i] : 0.f;
+                if constexpr (!KDA) {
+                    const float d = c <= R ? __expf(sm.g[R] - sm.g[c]) : 0.f;
+                    fa *= d;
+                    fm *= d;
+                }
+                if (J <= I) sm.a_tile(I * (I + 1) / 2 + J)[r * 20 + cc + i] = fa;
+                mv[4 * hf + i] = (ST)(fm * p.scale);
             }
         }
-        ST mv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = c0 + i;
-            float fa = c < R ? a[i] * sm.beta[R] : 0.f;
-            float fm = c <= R ? m[i] : 0.f;
-            if constexpr (!KDA) {
-                const float d = c <= R ? __expf(sm.g[R] - sm.g[c]) : 0.f;
-                fa *= d;
-                fm *= d;
-            }
-            if (J <= I) sm.a_tile(I * (I + 1) / 2 + J)[r * 20 + cc + i] = fa;
-            mv[i] = (ST)(fm * p.scale);
-        }
-        store_vec<ST, 4>(&rec.Mm[R][kpos<ST>(c0)], mv);
+        store_vec<ST, 4 * MH>(&rec.Mm[R][kpos<ST>(cb0)], mv);
     }
     __syncthreads();
     // T = (I + A)^-1 on wave 0.  Diagonal 16x16 blocks by forward
@@ -774,22 +788,30 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
             tbf[tb] = tbeta_fragment<ST, NB>(&Tf[row][0], sm.beta, row, lg);
             if (wave == tb) tbf[tb].store(&rec.Tm[row][0], lg);
         }
-        // key blocks kb = wave, wave + 4, ... of every token block
+        // Key blocks of every token block: 16-bit operands, the adjacent
+        // pairs (2p, 2p + 1) for p = wave, wave + 4, ..., whose results are
+        // adjacent in the stored k-order and leave as one 16-byte store;
+        // fp32 operands, blocks kb = wave, wave + 4, ...
+        constexpr int KP = sizeof(ST) == 2 ? 2 : 1;   // key blocks per store
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int j = 0; j < (DK / 16 + 3) / 4; ++j) {
-            const int kb = wave + 4 * j;
-            if (kb < DK / 16) {
-                RowA<ST, NB> a;
-                a.load(&sm.KtT[16 * kb + lr][0], lg);
-                f32x4 acc{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < (DK / (16 * KP) + 3) / 4; ++j) {
+            const int pb = wave + 4 * j;
+            if (pb < DK / (16 * KP)) {
+                ST w[4 * KP];
 #pragma unroll
-                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st) acc = rowa_mma(acc, a, tbf[tb], st);
-                ST w[4];
+                for (int x = 0; x < KP; ++x) {
+                    const int kb = KP * pb + x;
+                    RowA<ST, NB> a;
+                    a.load(&sm.KtT[16 * kb + lr][0], lg);
+                    f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = (ST)(-acc[i]);
-                store_vec<ST, 4>(&rec.Wn[16 * tb + lr][kpos<ST>(16 * kb + 4 * lg)], w);
+                    for (int st = 0; st < RegB<ST, NB>::STEPS; ++st) acc = rowa_mma(acc, a, tbf[tb], st);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[4 * x + i] = (ST)(-acc[i]);
+                }
+                store_vec<ST, 4 * KP>(&rec.Wn[16 * tb + lr][kpos<ST>(16 * KP * pb + 4 * lg)], w);
             }
         }
     }
