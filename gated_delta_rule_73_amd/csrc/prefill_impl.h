@@ -49,6 +49,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1200,7 +1201,10 @@ hipError_t launch_prep(const PrefillArgs &a, int j0, int seg_chunks, char *rec, 
     pk.choff = a.chunk_offset;
     pk.rec = rec;
     pk.num_records = record_chunks * a.num_heads;
-    static int resident = 0;   // workgroups of this kernel that fit on the device at once
+    // workgroups of this kernel that fit on the device at once (computed on
+    // the first call; concurrent first calls compute the same value)
+    static std::atomic<int> resident_cache{0};
+    int resident = resident_cache.load(std::memory_order_relaxed);
     if (!resident) {
         int dev = 0, cus = 0, per_cu = 0;
         hipError_t e = hipGetDevice(&dev);
@@ -1209,6 +1213,7 @@ hipError_t launch_prep(const PrefillArgs &a, int j0, int seg_chunks, char *rec, 
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep_kernel<DK, C, KDA, IT, false, float>, 256, 0);
         if (e != hipSuccess) return e;
         resident = std::max(1, cus * per_cu);
+        resident_cache.store(resident, std::memory_order_relaxed);
     }
     // grouped: a multiple of 8 workgroups (8 XCDs) unless the device holds fewer
     const bool grp = pk.G > 1;
