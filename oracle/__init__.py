@@ -58,6 +58,11 @@ def _load():
             i64, p, i64, i64, i64, ctypes.c_int, p, p, p, p, p, p, ctypes.c_double, p, p, ctypes.c_int,
         ]
         lib.gdr_oracle_recurrence.restype = ctypes.c_int
+        lib.gdr_oracle_recurrence_backward.argtypes = [
+            i64, p, i64, i64, i64, ctypes.c_int, p, p, p, p, p, p, ctypes.c_double, p, p,
+            p, p, p, p, p, p, ctypes.c_int,
+        ]
+        lib.gdr_oracle_recurrence_backward.restype = ctypes.c_int
         lib.gdr_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -112,6 +117,25 @@ def recurrence(q, k, v, beta, log_alpha, *, initial_state=None, seq_bounds=None,
     if k.shape != q.shape or q.ndim != 4 or v.ndim != 4:
         raise ValueError("q and k must be [B, T, Hk, dk], v [B, T, H, dv]")
     q, k = _expand_groups(q, k, v.shape[2])
+    bounds, per_channel = _check_prefill(q, k, v, beta, log_alpha, initial_state, seq_bounds)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = len(bounds) - 1
+    out = np.zeros((B, T, H, dv), dtype=np.float64)
+    final = np.zeros((N, H, dv, dk), dtype=np.float64)
+    rc = _load().gdr_oracle_recurrence(
+        N, _ptr(bounds), H, dk, dv, per_channel, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+        _ptr(log_alpha), _ptr(initial_state), float(scale), _ptr(out), _ptr(final),
+        int(num_threads),
+    )
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    return out, final
+
+
+def _check_prefill(q, k, v, beta, log_alpha, initial_state, seq_bounds):
+    """Shapes, gate form and sequence bounds shared by the forward and the
+    backward entry; returns (bounds, per_channel)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
@@ -133,16 +157,59 @@ def recurrence(q, k, v, beta, log_alpha, *, initial_state=None, seq_bounds=None,
     N = len(bounds) - 1
     if initial_state is not None and initial_state.shape != (N, H, dv, dk):
         raise ValueError(f"initial_state shape {initial_state.shape} != {(N, H, dv, dk)}")
-    out = np.zeros((B, T, H, dv), dtype=np.float64)
-    final = np.zeros((N, H, dv, dk), dtype=np.float64)
-    rc = _load().gdr_oracle_recurrence(
-        N, _ptr(bounds), H, dk, dv, per_channel, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-        _ptr(log_alpha), _ptr(initial_state), float(scale), _ptr(out), _ptr(final),
-        int(num_threads),
+    return bounds, per_channel
+
+
+def recurrence_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None,
+                        d_final_state=None, seq_bounds=None, scale: float = 1.0,
+                        num_threads: int = 0):
+    """Gradients of a scalar loss through :func:`recurrence`, given its
+    gradients with respect to the outputs (``d_out`` [B, T, H, dv]) and to the
+    final states (``d_final_state`` [N, H, dv, dk], None = zeros).
+
+    The pages train these layers but print no backward pass; this is the
+    chain rule applied to the recurrence's steps in reverse (the step list is
+    in ``gdr_oracle.c``).  Grouped q/k heads: each value head's gradient with
+    respect to its (repeated) q/k head is summed over the heads of the group,
+    the adjoint of the repetition.
+
+    Returns a dict of fp64 arrays: dq, dk (q's shape), dv (v's), dbeta
+    (beta's), dlog_alpha (log_alpha's) and d_initial_state [N, H, dv, dk]
+    (the gradient with respect to the initial state, whether or not one was
+    passed: a missing initial state is a zero one).
+    """
+    q, k, v, beta, log_alpha, d_out = (_f64(x) for x in (q, k, v, beta, log_alpha, d_out))
+    initial_state = _f64(initial_state)
+    d_final_state = _f64(d_final_state)
+    if k.shape != q.shape or q.ndim != 4 or v.ndim != 4:
+        raise ValueError("q and k must be [B, T, Hk, dk], v [B, T, H, dv]")
+    Hk = q.shape[2]
+    qe, ke = _expand_groups(q, k, v.shape[2])
+    bounds, per_channel = _check_prefill(qe, ke, v, beta, log_alpha, initial_state, seq_bounds)
+    B, T, H, dk = qe.shape
+    dv = v.shape[-1]
+    N = len(bounds) - 1
+    if d_out.shape != v.shape:
+        raise ValueError(f"d_out shape {d_out.shape} != {v.shape}")
+    if d_final_state is not None and d_final_state.shape != (N, H, dv, dk):
+        raise ValueError(f"d_final_state shape {d_final_state.shape} != {(N, H, dv, dk)}")
+    g = {
+        "dq": np.zeros(qe.shape), "dk": np.zeros(qe.shape), "dv": np.zeros(v.shape),
+        "dbeta": np.zeros(beta.shape), "dlog_alpha": np.zeros(log_alpha.shape),
+        "d_initial_state": np.zeros((N, H, dv, dk)),
+    }
+    rc = _load().gdr_oracle_recurrence_backward(
+        N, _ptr(bounds), H, dk, dv, per_channel, _ptr(qe), _ptr(ke), _ptr(v), _ptr(beta),
+        _ptr(log_alpha), _ptr(initial_state), float(scale), _ptr(d_out), _ptr(d_final_state),
+        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dbeta"]), _ptr(g["dlog_alpha"]),
+        _ptr(g["d_initial_state"]), int(num_threads),
     )
     if rc != 0:
         raise RuntimeError(f"oracle failed with code {rc}")
-    return out, final
+    if Hk != H:
+        for name in ("dq", "dk"):
+            g[name] = g[name].reshape(B, T, Hk, H // Hk, dk).sum(axis=3)
+    return g
 
 
 def decode(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, num_threads: int = 0):

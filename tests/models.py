@@ -19,6 +19,14 @@ route:
   S_C = S0 Diag(e^{g_C}) + U^T (K*e^{g_C - g}).  This is algebra derived from
   the KDA equation, not printed on the pages; it is pinned here against the
   oracle so the kernels' algorithm is checked before any kernel exists.
+* ``chunked_backward`` -- the gradients of that chunked form, in the
+  arrangement the backward kernels use: a forward pass over chunks keeping
+  each chunk's incoming state, a reverse pass over chunks carrying the state
+  gradient (its recurrence, dS_prev = dS_C Diag(e^{g_C}) + dO^T (Q*e^g) +
+  dU^T W with dU = M^T dO + K_end dS_C^T and W = -(I + A)^-1 diag(beta)(K*e^g),
+  needs no forward state), then every chunk's input gradients from its two
+  states alone, with the Gram-like products taken against operands shifted by
+  a per-channel reference exponent m.  Pinned against the oracle's backward.
 """
 from __future__ import annotations
 
@@ -96,3 +104,88 @@ def chunked(q, k, v, beta, log_alpha, S0=None, chunk=16):
         O[c0:c1] = Qt @ S.T + M @ U
         S = S * np.exp(g[-1])[None, :] + U.T @ Kend
     return O, S
+
+
+def chunked_backward(q, k, v, beta, log_alpha, d_out, S0=None, d_final=None, chunk=16, scale=1.0):
+    """Gradients of ``scale``-scaled :func:`chunked` for one sequence and head.
+
+    Returns dict dq, dk [T, dk]; dv [T, dv]; dbeta [T]; dlog_alpha like
+    log_alpha; d_initial_state [dv, dk].
+    """
+    T, dk = k.shape
+    dv = v.shape[1]
+    la_in = np.asarray(log_alpha, dtype=np.float64)
+    la = np.repeat(la_in[:, None], dk, axis=1) if la_in.ndim == 1 else la_in
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, dtype=np.float64)
+    bounds = [(c0, min(T, c0 + chunk)) for c0 in range(0, T, chunk)]
+
+    def operands(c0, c1):
+        K, Q, b = k[c0:c1], q[c0:c1], beta[c0:c1]
+        g = np.cumsum(la[c0:c1], axis=0)
+        n = c1 - c0
+        m = 0.5 * (g[0] + g[-1])                        # per-channel reference
+        Kts, Khs, Qts = K * np.exp(g - m), K * np.exp(m - g), Q * np.exp(g - m)
+        Tm = np.linalg.inv(np.eye(n) + np.tril(b[:, None] * (Kts @ Khs.T), -1))
+        M = np.tril(Qts @ Khs.T)
+        Kta, Qt, Kend = K * np.exp(g), Q * np.exp(g), K * np.exp(g[-1] - g)
+        W = -(Tm * b[None, :]) @ Kta                    # Wn = -T diag(beta) K e^g
+        return dict(K=K, Q=Q, b=b, g=g, m=m, Kts=Kts, Khs=Khs, Qts=Qts, T=Tm, M=M,
+                    Kta=Kta, Qt=Qt, Kend=Kend, Wn=W, D=np.exp(g[-1]))
+
+    # forward over chunks: each chunk's incoming state
+    starts = []
+    for c0, c1 in bounds:
+        op = operands(c0, c1)
+        starts.append(S.copy())
+        U = op["T"] @ (op["b"][:, None] * v[c0:c1]) + op["Wn"] @ S.T
+        S = S * op["D"][None, :] + U.T @ op["Kend"]
+
+    # reverse over chunks: state gradient at each chunk's end
+    dS = np.zeros((dv, dk)) if d_final is None else np.array(d_final, dtype=np.float64)
+    ends = [None] * len(bounds)
+    for ci in range(len(bounds) - 1, -1, -1):
+        c0, c1 = bounds[ci]
+        op = operands(c0, c1)
+        ends[ci] = dS.copy()
+        dO = scale * d_out[c0:c1]
+        dU = op["M"].T @ dO + op["Kend"] @ dS.T
+        dS = dS * op["D"][None, :] + dO.T @ op["Qt"] + dU.T @ op["Wn"]
+    d_initial = dS
+
+    # every chunk from its two states
+    g_out = dict(dq=np.zeros((T, dk)), dk=np.zeros((T, dk)), dv=np.zeros((T, dv)),
+                 dbeta=np.zeros(T), dla=np.zeros((T, dk)))
+    for ci, (c0, c1) in enumerate(bounds):
+        op = operands(c0, c1)
+        S0c, dSC = starts[ci], ends[ci]
+        b, g, m, Tm, M = op["b"], op["g"], op["m"], op["T"], op["M"]
+        dO = scale * d_out[c0:c1]
+        Y = v[c0:c1] - op["Kta"] @ S0c.T
+        U = Tm @ (b[:, None] * Y)
+        dU = M.T @ dO + op["Kend"] @ dSC.T
+        Z = Tm.T @ dU
+        dY = b[:, None] * Z
+        dbeta = (Z * Y).sum(axis=1)
+        dT = dU @ (b[:, None] * Y).T
+        dA = np.tril(-(Tm.T @ dT @ Tm.T), -1)
+        gram = op["Kts"] @ op["Khs"].T
+        dbeta = dbeta + (dA * gram).sum(axis=1)
+        dAb = b[:, None] * dA
+        dM = np.tril(dO @ U.T)
+        eg, egm, emg = np.exp(g), np.exp(g - m), np.exp(m - g)
+        dQ = (dO @ S0c) * eg + (dM @ op["Khs"]) * egm
+        gK1 = -(dY @ S0c) * eg + (dAb @ op["Khs"]) * egm
+        gK2 = (dM.T @ op["Qts"] + dAb.T @ op["Kts"]) * emg
+        gK3 = (U @ dSC) * np.exp(g[-1] - g)
+        K, Q = op["K"], op["Q"]
+        dg = K * (gK1 - gK2 - gK3) + Q * dQ
+        dg[-1] += (gK3 * K).sum(axis=0) + (dSC * S0c).sum(axis=0) * op["D"]
+        g_out["dq"][c0:c1] = dQ
+        g_out["dk"][c0:c1] = gK1 + gK2 + gK3
+        g_out["dv"][c0:c1] = dY
+        g_out["dbeta"][c0:c1] = dbeta
+        g_out["dla"][c0:c1] = np.cumsum(dg[::-1], axis=0)[::-1]   # reverse cumulative sum
+    dla = g_out.pop("dla")
+    g_out["dlog_alpha"] = dla.sum(axis=1) if la_in.ndim == 1 else dla
+    g_out["d_initial_state"] = d_initial
+    return g_out

@@ -453,3 +453,181 @@ def test_prologue_packed_equals_separate_runs():
         for i in range(5):
             np.testing.assert_array_equal(full[i][:, lo:hi], part[i])
         np.testing.assert_array_equal(full[5][n], part[5][0])
+
+
+# ------------------------------------------------------------ backward ----
+# The pages train these layers but print no backward pass.  The oracle's
+# gradients are pinned by (1) a closed form of the one-token scalar case,
+# (2) central finite differences of the (already pinned) forward oracle over
+# every input element, (3) exact identities that follow from the recurrence
+# being linear in q (readout) and jointly linear in (v, S0), and (4) a special
+# case (beta = 0 cuts k and v out of the recurrence).
+
+def _loss_weights(shape_out, shape_state, seed):
+    r = np.random.default_rng(seed)
+    return r.standard_normal(shape_out), r.standard_normal(shape_state)
+
+
+def test_backward_scalar_closed_form():
+    """d_k = d_v = 1, one token: s1 = a s0 (1 - b k^2) + b v k, o = c s1 q,
+    loss = w_o o + w_s s1; every derivative written out by hand."""
+    q, k, v, b, a, s0, c, w_o, w_s = 0.8, -1.3, 0.45, 0.6, 0.7, 1.7, 0.9, -0.35, 1.25
+    s1 = a * s0 * (1 - b * k * k) + b * v * k
+    G = w_s + c * w_o * q                      # d loss / d s1
+    want = {
+        "dq": c * w_o * s1,
+        "dv": G * b * k,
+        "dbeta": G * k * (v - a * s0 * k),
+        "dk": G * (b * v - 2 * a * s0 * b * k),
+        "dlog_alpha": G * a * s0 * (1 - b * k * k),
+        "d_initial_state": G * a * (1 - b * k * k),
+    }
+    arr = lambda x: np.full((1, 1, 1, 1), x)
+    for la in (np.full((1, 1, 1), np.log(a)), np.full((1, 1, 1, 1), np.log(a))):
+        g = oracle.recurrence_backward(arr(q), arr(k), arr(v), np.full((1, 1, 1), b), la,
+                                       arr(w_o), initial_state=arr(s0), d_final_state=arr(w_s),
+                                       scale=c)
+        for name, val in want.items():
+            assert abs(float(g[name].ravel()[0]) - val) < 1e-14, name
+
+
+def _fd_case(layout, per_channel, T=5, dk=3, dv=2, seed=0):
+    r = np.random.default_rng(seed)
+    B, H, Hk, bounds = 1, 1, 1, None
+    if layout == "dense":
+        B = 2
+    elif layout == "packed":
+        bounds = [0, 2, 2, T]                  # the middle sequence is empty
+    elif layout == "grouped":
+        H, Hk = 2, 1
+    N = B if bounds is None else len(bounds) - 1
+    q = r.standard_normal((B, T, Hk, dk))
+    k = r.standard_normal((B, T, Hk, dk)) / np.sqrt(dk)
+    v = r.standard_normal((B, T, H, dv))
+    beta = r.random((B, T, H))
+    la = -r.random((B, T, H, dk) if per_channel else (B, T, H))
+    S0 = r.standard_normal((N, H, dv, dk))
+    return [q, k, v, beta, la, S0], bounds
+
+
+def _finite_difference_check(args, bounds, scale, seed, eps=1e-6, backward=None):
+    q, k, v, beta, la, S0 = args
+    W_o, W_s = _loss_weights(v.shape, S0.shape, seed)
+
+    def loss(*a):
+        o, f = oracle.recurrence(*a[:5], initial_state=a[5], seq_bounds=bounds, scale=scale)
+        return float((o * W_o).sum() + (f * W_s).sum())
+
+    backward = backward or oracle.recurrence_backward
+    g = backward(q, k, v, beta, la, W_o, initial_state=S0, d_final_state=W_s,
+                 seq_bounds=bounds, scale=scale)
+    worst = 0.0
+    for ai, name in enumerate(["dq", "dk", "dv", "dbeta", "dlog_alpha", "d_initial_state"]):
+        x = args[ai]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a2 = list(args)
+            xp = x.copy(); xp[idx] += eps; a2[ai] = xp; lp = loss(*a2)
+            xm = x.copy(); xm[idx] -= eps; a2[ai] = xm; lm = loss(*a2)
+            num[idx] = (lp - lm) / (2 * eps)
+        worst = max(worst, np.abs(num - g[name]).max() / max(1.0, np.abs(num).max()))
+    return worst
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("layout", ["dense", "packed", "grouped"])
+def test_backward_matches_finite_differences(layout, per_channel):
+    args, bounds = _fd_case(layout, per_channel, seed=3)
+    assert _finite_difference_check(args, bounds, scale=0.7, seed=4) < 1e-8
+
+
+def test_backward_finite_differences_across_checkpoint_segments():
+    """150 tokens: three of the oracle's recomputation segments (64 tokens)."""
+    args, bounds = _fd_case("single", True, T=150, dk=2, dv=2, seed=5)
+    assert _finite_difference_check(args, bounds, scale=1.0, seed=6) < 1e-8
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_backward_homogeneity_identities(per_channel):
+    """o_t is linear in q_t and S_t does not depend on q, so
+    sum <dq, q> = <d_out, out>.  With k, beta and the gates fixed, (out, S_T)
+    is linear in (v, S0) jointly, so <dv, v> + <dS0, S0> = <d_out, out> +
+    <d_final, S_T> (Euler's identity for degree-one homogeneous maps)."""
+    r = np.random.default_rng(7)
+    T, H, dk, dv = 300, 2, 16, 12
+    bounds = [0, 37, 201, 300]
+    q = r.standard_normal((1, T, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((1, T, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((1, T, H, dv))
+    beta = 1 / (1 + np.exp(-r.standard_normal((1, T, H))))
+    la = -np.log1p(np.exp(r.standard_normal((1, T, H, dk) if per_channel else (1, T, H))))
+    S0 = r.standard_normal((3, H, dv, dk))
+    W_o, W_s = _loss_weights(v.shape, S0.shape, 8)
+    out, fin = oracle.recurrence(q, k, v, beta, la, initial_state=S0, seq_bounds=bounds, scale=0.5)
+    g = oracle.recurrence_backward(q, k, v, beta, la, W_o, initial_state=S0, d_final_state=W_s,
+                                   seq_bounds=bounds, scale=0.5)
+    lo, ls = float((W_o * out).sum()), float((W_s * fin).sum())
+    assert abs(float((g["dq"] * q).sum()) - lo) < 1e-10 * max(1.0, abs(lo))
+    rhs = float((g["dv"] * v).sum() + (g["d_initial_state"] * S0).sum())
+    assert abs(rhs - (lo + ls)) < 1e-10 * max(1.0, abs(lo + ls))
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_backward_zero_beta_cuts_keys_and_values(per_channel):
+    """beta = 0 leaves only decay and readout: k and v have no influence."""
+    q, k, v, beta, la, S0 = _rand_case(20, 8, 6, per_channel=per_channel, seed=9)
+    beta[:] = 0.0
+    W_o, W_s = _loss_weights(v.shape, S0.shape, 10)
+    g = oracle.recurrence_backward(q, k, v, beta, la, W_o, initial_state=S0, d_final_state=W_s)
+    assert np.all(g["dk"] == 0.0) and np.all(g["dv"] == 0.0)
+    assert np.abs(g["dbeta"]).max() > 1e-3 and np.abs(g["dq"]).max() > 1e-3
+
+
+def test_backward_planted_mistake_is_caught():
+    """Sanity check of the finite-difference pin: a token-by-token backward
+    with one term dropped (the key's path through what the state recalls,
+    S'^T dx) fails it by a wide margin."""
+    def wrong_backward(q, k, v, beta, la, d_out, *, initial_state, d_final_state, seq_bounds, scale):
+        right = oracle.recurrence_backward(q, k, v, beta, la, d_out, initial_state=initial_state,
+                                           d_final_state=d_final_state, seq_bounds=seq_bounds,
+                                           scale=scale)
+        T, dk = q.shape[1], q.shape[3]
+        S = initial_state[0, 0].copy()
+        wrong_dk = right["dk"].copy()
+        # recompute the dropped term and take it out of token 0's key gradient:
+        # only token 0's S' is the decayed initial state, so the term is exact there
+        a0 = np.exp(la[0, 0, 0]) * np.ones(dk)
+        Sp = S * a0[None, :]
+        dx = -beta[0, 0, 0] * (right["dv"][0, 0, 0] / beta[0, 0, 0])
+        wrong_dk[0, 0, 0] -= Sp.T @ dx
+        out = dict(right)
+        out["dk"] = wrong_dk
+        return out
+
+    args, bounds = _fd_case("single", True, seed=11)
+    assert _finite_difference_check(args, bounds, scale=1.0, seed=12) < 1e-8
+    assert _finite_difference_check(args, bounds, scale=1.0, seed=12, backward=wrong_backward) > 1e-3
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("chunk", [1, 2, 3, 5, 16, 32])
+def test_backward_chunked_algebra_matches_oracle(per_channel, chunk):
+    """The chunk-level gradient algebra (forward pass keeping chunk states,
+    reverse pass carrying the state gradient, per-chunk gradients from the
+    two states with shifted Gram operands) equals the oracle's token-by-token
+    chain rule; 37 tokens leave a ragged last chunk."""
+    r = np.random.default_rng(100 + chunk)
+    T, dk, dv = 37, 8, 6
+    q = r.standard_normal((T, dk))
+    k = r.standard_normal((T, dk)); k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = r.standard_normal((T, dv))
+    b = r.random(T)
+    la = -np.log1p(np.exp(r.standard_normal((T, dk) if per_channel else T)))
+    S0, dF = r.standard_normal((dv, dk)), r.standard_normal((dv, dk))
+    dO = r.standard_normal((T, dv))
+    got = models.chunked_backward(q, k, v, b, la, dO, S0, dF, chunk=chunk, scale=0.6)
+    e = lambda x: x[None, :, None]
+    want = oracle.recurrence_backward(e(q), e(k), e(v), e(b), e(la), e(dO), initial_state=S0[None, None],
+                                      d_final_state=dF[None, None], scale=0.6)
+    for name, val in got.items():
+        np.testing.assert_allclose(val, want[name].reshape(val.shape), rtol=0, atol=1e-12, err_msg=name)
