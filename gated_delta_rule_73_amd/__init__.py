@@ -9,6 +9,7 @@ missing, the calls raise.
     o, S = gdr_prefill_chunked(q, k, v, beta, log_alpha, initial_state=S0, cu_seqlens=cu)
     o    = gdr_decode_step(q, k, v, beta, log_alpha, state)   # state updated in place
     o    = gdr_decode_tokens(q, k, v, beta, log_alpha, pool, num_commit=c, state_slots=s)
+    g    = gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, initial_state=S0, d_final_state=dS)
 
 Value heads may share query-key heads: q and k carry Hk heads, v, the gates,
 the states and the outputs H (a multiple of Hk); value head h reads q/k head
@@ -21,8 +22,9 @@ import os
 
 import torch
 
-__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "gdr_decode_tokens", "gdr_layer_prologue", "prefill_chunked",
-           "decode_step", "decode_tokens", "layer_prologue",
+__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "gdr_decode_tokens", "gdr_layer_prologue",
+           "gdr_prefill_backward", "prefill_chunked", "decode_step", "decode_tokens", "layer_prologue",
+           "prefill_backward",
            "gdr_state_bytes", "GdrError", "load_library", "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -46,7 +48,7 @@ class PrefillShape(ctypes.Structure):
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("num_qk_heads", ctypes.c_int32)]
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 _lib = None
@@ -75,6 +77,11 @@ def load_library():
         lib.gdr_layer_prologue.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, p, p, p, p, p, i32,
                                            p, p, p, p, p, p, p, p]
         lib.gdr_layer_prologue.restype = ctypes.c_int
+        lib.gdr_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, i32]
+        lib.gdr_prefill_backward_workspace_bytes.restype = sz
+        lib.gdr_prefill_backward.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, p, p, p, p, p,
+                                             p, p, ctypes.c_float, p, p, p, p, p, p, p, p, p, sz, p]
+        lib.gdr_prefill_backward.restype = ctypes.c_int
         lib.gdr_state_bytes.argtypes = [ctypes.c_int64] * 4
         lib.gdr_state_bytes.restype = ctypes.c_uint64
         lib.gdr_status_string.argtypes = [ctypes.c_int]
@@ -173,6 +180,58 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
         _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(dv_slice), float(scale), _ptr(out),
         _ptr(final_state), _ptr(ws), int(ws_bytes), _stream(dev)))
     return out, final_state
+
+
+def gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None, d_final_state=None,
+                         cu_seqlens=None, scale: float = 1.0, output_d_initial_state: bool = True,
+                         workspace=None):
+    """Gradients through :func:`gdr_prefill_chunked` (same q, k, v, beta,
+    log_alpha, initial_state, cu_seqlens and scale; one q/k head per value
+    head; fp32 gates).  d_out [B, T, H, dv] fp32; d_final_state
+    [N, H, dv, dk] fp32 or None (zeros).
+    Returns a dict of fp32 tensors: dq, dk (q's shape), dv (v's), dbeta,
+    dlog_alpha (log_alpha's shape) and d_initial_state [N, H, dv, dk] (None
+    when not requested)."""
+    lib = load_library()
+    dev = q.device
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or beta.shape != (B, T, H):
+        raise ValueError("shapes: q, k [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+    if log_alpha.dim() == 3:
+        gate = GDR_GATE_HEAD
+    elif log_alpha.dim() == 4:
+        gate = GDR_GATE_CHANNEL
+    else:
+        raise ValueError("log_alpha must be [B, T, H] or [B, T, H, dk]")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, q.dtype, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(initial_state, "initial_state", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(d_out, "d_out", torch.float32, dev)
+    _need(d_final_state, "d_final_state", torch.float32, dev)
+    if d_out.shape != v.shape:
+        raise ValueError("d_out must have v's shape")
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(q.shape, **f32), "dv": torch.empty(v.shape, **f32),
+         "dbeta": torch.empty(beta.shape, **f32), "dlog_alpha": torch.empty(log_alpha.shape, **f32),
+         "d_initial_state": torch.empty(N, H, dv, dk, **f32) if output_d_initial_state else None}
+    shape = PrefillShape(B, T, H, dk, dv, N, Hk)
+    ws_bytes = lib.gdr_prefill_backward_workspace_bytes(ctypes.byref(shape), gate, int(cu_seqlens is not None))
+    if workspace is None:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+        ws, ws_bytes = workspace, workspace.numel()
+    _check(lib.gdr_prefill_backward(
+        ctypes.byref(shape), gate, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+        _ptr(initial_state), _ptr(cu_seqlens), float(scale), _ptr(d_out), _ptr(d_final_state), _ptr(g["dq"]),
+        _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dbeta"]), _ptr(g["dlog_alpha"]), _ptr(g["d_initial_state"]),
+        _ptr(ws), int(ws_bytes), _stream(dev)))
+    return g
 
 
 def gdr_decode_step(q, k, v, beta, log_alpha, state, *, scale: float = 1.0, out=None, out_dtype=torch.float32):
@@ -282,3 +341,4 @@ prefill_chunked = gdr_prefill_chunked
 decode_step = gdr_decode_step
 decode_tokens = gdr_decode_tokens
 layer_prologue = gdr_layer_prologue
+prefill_backward = gdr_prefill_backward

@@ -198,9 +198,157 @@ gdr_status check_decode(int32_t num_seqs, int32_t K, int32_t num_heads, int32_t 
     a.slots = slots;
     return ok();
 }
+// Workspace of one backward call: [order][chunk offsets] (packed batches),
+// the per-chunk records, the chunks' incoming states and their outgoing
+// state gradients.  Packed batches size the chunk slots by the bound
+// ceil(seqlen / C) + num_seqs, since the lengths live on the device.
+struct BackwardWorkspace {
+    size_t order_off = 0, choff_off = 0, rec_off = 0, st_off = 0, dst_off = 0, total = 0;
+    long record_chunks = 0;
+};
+
+BackwardWorkspace backward_workspace(const gdr_prefill_shape &s, bool packed) {
+    BackwardWorkspace w;
+    size_t off = 0;
+    if (packed) {
+        off = round256(sizeof(int32_t) * (size_t)s.num_seqs);
+        w.choff_off = off;
+        off += round256(sizeof(int32_t) * ((size_t)s.num_seqs + 1));
+    }
+    const long ncps = ((long)s.seqlen + gdr::kBackwardChunk - 1) / gdr::kBackwardChunk;
+    w.record_chunks = packed ? ncps + s.num_seqs : (long)s.batch * ncps;
+    const size_t slots = (size_t)w.record_chunks * (size_t)s.num_heads;
+    w.rec_off = off;
+    off += round256(slots * gdr::backward_record_bytes(s.head_dim_k));
+    w.st_off = off;
+    off += round256(slots * (size_t)s.head_dim_k * s.head_dim_v * sizeof(float));
+    w.dst_off = off;
+    off += round256(slots * (size_t)s.head_dim_k * s.head_dim_v * sizeof(float));
+    w.total = off;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t gdr_prefill_backward_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate, int32_t packed) {
+    if (!shape || !valid_gate(gate)) return 0;
+    const gdr_prefill_shape &s = *shape;
+    if (s.batch < 1 || s.seqlen < 0 || s.num_heads < 1 || s.head_dim_k < 1 || s.head_dim_v < 1 || s.num_seqs < 0)
+        return 0;
+    return backward_workspace(s, packed != 0).total;
+}
+
+gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
+                                const void *q, const void *k, const void *v, const float *beta,
+                                const float *log_alpha, const float *initial_state, const int32_t *cu_seqlens,
+                                float scale, const float *d_out, const float *d_final_state, float *dq,
+                                float *dk_out, float *dv_out, float *dbeta, float *dlog_alpha,
+                                float *d_initial_state, void *workspace, size_t workspace_bytes,
+                                void *hip_stream) {
+    if (!shape) return fail(GDR_ERROR_INVALID_VALUE, "shape is NULL");
+    const gdr_prefill_shape s = *shape;
+    if (s.batch < 1 || s.seqlen < 0 || s.num_heads < 1 || s.head_dim_k < 1 || s.head_dim_v < 1 || s.num_seqs < 0)
+        return fail(GDR_ERROR_INVALID_VALUE,
+                    "bad shape (batch=%d seqlen=%d heads=%d dk=%d dv=%d num_seqs=%d)", s.batch, s.seqlen,
+                    s.num_heads, s.head_dim_k, s.head_dim_v, s.num_seqs);
+    int hk = 0;
+    if (resolve_qk_heads(s.num_heads, s.num_qk_heads, hk) != GDR_SUCCESS) return GDR_ERROR_INVALID_VALUE;
+    if (hk != s.num_heads)
+        return fail(GDR_ERROR_NOT_SUPPORTED, "the backward takes one q/k head per value head (%d != %d)", hk,
+                    s.num_heads);
+    if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
+    if (!valid_dtype(qkv_dtype)) return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype %d", (int)qkv_dtype);
+    const bool packed = cu_seqlens != nullptr;
+    if (packed && s.batch != 1) return fail(GDR_ERROR_INVALID_VALUE, "cu_seqlens requires batch == 1");
+    if (!packed && s.num_seqs != s.batch)
+        return fail(GDR_ERROR_INVALID_VALUE, "dense batch needs num_seqs == batch (%d != %d)", s.num_seqs, s.batch);
+    if (packed && s.num_seqs == 0 && s.seqlen > 0)
+        return fail(GDR_ERROR_INVALID_VALUE, "packed tokens need at least one sequence");
+    const int64_t tokens = (int64_t)s.batch * s.seqlen;
+    if (tokens > INT32_MAX) return fail(GDR_ERROR_INVALID_VALUE, "more than 2^31-1 tokens");
+    if ((int64_t)s.num_seqs * s.num_heads * (s.head_dim_v / 16) > INT32_MAX)
+        return fail(GDR_ERROR_INVALID_VALUE, "too many (sequence, head) units");
+    if (s.num_heads > 65535) return fail(GDR_ERROR_NOT_SUPPORTED, "more than 65535 heads");
+    const int dk = s.head_dim_k, dv = s.head_dim_v;
+    const bool bf16 = qkv_dtype == GDR_BF16, kda = gate == GDR_GATE_CHANNEL;
+    if (!gdr::backward_supported(dk, dv))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "backward needs head_dim_k in {32, 64, 128} and head_dim_v a multiple "
+                    "of 16 <= 128 (got %d, %d)", dk, dv);
+
+    const size_t es = dsize(qkv_dtype);
+    const size_t nq = (size_t)tokens * s.num_heads * dk, nv = (size_t)tokens * s.num_heads * dv;
+    const size_t ng = (size_t)tokens * s.num_heads, nla = kda ? ng * dk : ng;
+    const size_t nstate = (size_t)s.num_seqs * s.num_heads * dv * dk;
+    if (tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !d_out || !dq || !dk_out || !dv_out || !dbeta ||
+                       !dlog_alpha))
+        return fail(GDR_ERROR_INVALID_VALUE, "q, k, v, beta, log_alpha, d_out and the five gradients must be non-NULL");
+    const void *aligned16[] = {q, k, v, d_out, initial_state, d_final_state, d_initial_state};
+    const char *names16[] = {"q", "k", "v", "d_out", "initial_state", "d_final_state", "d_initial_state"};
+    for (int i = 0; i < 7; ++i)
+        if (!aligned(aligned16[i], 16)) return fail(GDR_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", names16[i]);
+    const void *aligned4[] = {beta, dq, dk_out, dv_out, dbeta, dlog_alpha, cu_seqlens};
+    for (const void *p : aligned4)
+        if (!aligned(p, 4)) return fail(GDR_ERROR_INVALID_VALUE, "gradients, beta and cu_seqlens must be 4-byte aligned");
+    if (!aligned(log_alpha, kda ? 16 : 4))
+        return fail(GDR_ERROR_INVALID_VALUE, "log_alpha must be %d-byte aligned", kda ? 16 : 4);
+
+    const BackwardWorkspace ws = backward_workspace(s, packed);
+    if ((ws.record_chunks + 8) * s.num_heads >= INT32_MAX)
+        return fail(GDR_ERROR_NOT_SUPPORTED, "more than 2^31 (chunk, head) records");
+    if (workspace_bytes < ws.total)
+        return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, ws.total);
+    if (ws.total && !workspace) return fail(GDR_ERROR_INVALID_VALUE, "workspace is NULL");
+    if (ws.total && !aligned(workspace, 256)) return fail(GDR_ERROR_INVALID_VALUE, "workspace is not 256-byte aligned");
+
+    const Range in[] = {range("q", q, nq * es), range("k", k, nq * es), range("v", v, nv * es),
+                        range("beta", beta, ng * 4), range("log_alpha", log_alpha, nla * 4),
+                        range("initial_state", initial_state, nstate * 4),
+                        range("cu_seqlens", cu_seqlens, packed ? 4 * ((size_t)s.num_seqs + 1) : 0),
+                        range("d_out", d_out, nv * 4), range("d_final_state", d_final_state, nstate * 4)};
+    const Range outs[] = {range("dq", dq, nq * 4), range("dk", dk_out, nq * 4), range("dv", dv_out, nv * 4),
+                          range("dbeta", dbeta, ng * 4), range("dlog_alpha", dlog_alpha, nla * 4),
+                          range("d_initial_state", d_initial_state, nstate * 4),
+                          range("workspace", workspace, ws.total)};
+    for (const Range &o : outs) {
+        for (const Range &r : in)
+            if (overlaps(o, r)) return fail(GDR_ERROR_INVALID_VALUE, "%s overlaps %s", o.name, r.name);
+        for (const Range &o2 : outs)
+            if (&o2 != &o && overlaps(o, o2)) return fail(GDR_ERROR_INVALID_VALUE, "%s overlaps %s", o.name, o2.name);
+    }
+    if (tokens == 0 && !d_initial_state) return ok();
+
+    gdr::BackwardArgs a{};
+    a.batch = s.batch;
+    a.seqlen = s.seqlen;
+    a.num_heads = s.num_heads;
+    a.dk = dk;
+    a.dv = dv;
+    a.num_seqs = s.num_seqs;
+    a.kda = kda;
+    a.bf16 = bf16;
+    a.q = q; a.k = k; a.v = v;
+    a.beta = beta;
+    a.log_alpha = log_alpha;
+    a.initial_state = initial_state;
+    a.cu_seqlens = cu_seqlens;
+    a.scale = scale;
+    a.d_out = d_out;
+    a.d_final_state = d_final_state;
+    a.dq = dq; a.dk_out = dk_out; a.dv_out = dv_out;
+    a.dbeta = dbeta;
+    a.dlog_alpha = dlog_alpha;
+    a.d_initial_state = d_initial_state;
+    char *wsb = static_cast<char *>(workspace);
+    a.order = packed ? reinterpret_cast<int32_t *>(wsb + ws.order_off) : nullptr;
+    a.chunk_offset = packed ? reinterpret_cast<int32_t *>(wsb + ws.choff_off) : nullptr;
+    a.records = wsb ? reinterpret_cast<float *>(wsb + ws.rec_off) : nullptr;
+    a.states = wsb ? reinterpret_cast<float *>(wsb + ws.st_off) : nullptr;
+    a.dstates = wsb ? reinterpret_cast<float *>(wsb + ws.dst_off) : nullptr;
+    a.record_chunks = ws.record_chunks;
+    return launch_status(gdr::launch_backward(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_backward");
+}
 
 const char *gdr_status_string(gdr_status s) {
     switch (s) {

@@ -70,6 +70,39 @@ struct PrologueArgs {
     float *beta, *log_alpha;
 };
 
+// Gradients of the chunked prefill (backward.hip).  All gradients fp32.
+struct BackwardArgs {
+    int batch, seqlen, num_heads, dk, dv, num_seqs;
+    bool kda, bf16;
+    const void *q, *k, *v;
+    const float *beta, *log_alpha;
+    const float *initial_state;     // [num_seqs, H, dv, dk] or NULL
+    const int32_t *cu_seqlens;
+    float scale;
+    const float *d_out;             // [batch, seqlen, H, dv]
+    const float *d_final_state;     // [num_seqs, H, dv, dk] or NULL (zeros)
+    float *dq, *dk_out, *dv_out, *dbeta, *dlog_alpha;
+    float *d_initial_state;         // or NULL
+    // workspace (laid out by the C-ABI layer)
+    int32_t *order, *chunk_offset;  // packed only
+    float *records;                 // record_chunks * H records
+    float *states, *dstates;        // record_chunks * H states of dv x dk each
+    long record_chunks;             // chunk slots (packed: an upper bound)
+};
+
+constexpr int kBackwardChunk = 32;
+// One backward chunk record: e^{g_C} [dk], T and M [C][C], W, Q e^g and
+// K_end [C][dk], fp32, padded to 256 bytes.
+constexpr size_t backward_record_bytes(int dk) {
+    return (((size_t)dk + 2 * kBackwardChunk * kBackwardChunk + 3 * (size_t)kBackwardChunk * dk) * 4 + 255) &
+           ~size_t(255);
+}
+bool backward_supported(int dk, int dv);
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t st);
+// Packed batches: longest-first order and first record chunk per sequence.
+hipError_t launch_schedule(const int32_t *cu, int n, int chunk, int32_t *order, int32_t *chunk_offset,
+                           hipStream_t st);
+
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t st);
 hipError_t launch_decode_tokens(const DecodeArgs &p, hipStream_t st);

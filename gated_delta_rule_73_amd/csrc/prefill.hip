@@ -74,12 +74,17 @@ int auto_dv_slice(bool bf16, bool kda, int dk, int dv, int chunk, long units) {
     return rounds(32) < rounds(16) ? 32 : 16;
 }
 
+hipError_t launch_schedule(const int32_t *cu, int n, int chunk, int32_t *order, int32_t *chunk_offset,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cu, n, chunk, order,
+                       chunk_offset);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     if (a.num_seqs == 0 || a.num_heads == 0) return hipSuccess;
     if (a.cu_seqlens) {
-        hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)((a.num_seqs + 255) / 256)), dim3(256), 0, st,
-                           a.cu_seqlens, a.num_seqs, a.chunk, a.order, a.chunk_offset);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_schedule(a.cu_seqlens, a.num_seqs, a.chunk, a.order, a.chunk_offset, st);
         if (e != hipSuccess) return e;
     }
     if (a.bf16) return a.kda ? launch_prefill_bf16_kda(a, st) : launch_prefill_bf16_gdn(a, st);

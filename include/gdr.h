@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 typedef enum gdr_status {
     GDR_SUCCESS = 0,
@@ -308,6 +308,57 @@ uint64_t gdr_state_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim_k
 
 /* Static description of a status code. */
 const char *gdr_status_string(gdr_status status);
+
+/*
+ * Backward of gdr_prefill_chunked, for training.  The recurrence is the one
+ * of page "How the New Flash Models Work: Inside GLM-5.3-Flash and
+ * Qwen3.8-Flash-Next", section "Linear attention: a fixed-size memory in
+ * place of the cache" (Gated DeltaNet and Kimi Delta Attention equations);
+ * the pages train these layers but give no backward pass, so this is the
+ * chain rule of the forward computation.  Given the gradients of a scalar
+ * loss with respect to the forward's outputs (d_out) and final states
+ * (d_final_state), it returns the loss's gradients with respect to q, k, v,
+ * beta, log_alpha and the initial state.  The forward's outputs are not
+ * needed: the chunks' states are recomputed.
+ *
+ *  shape, gate, qkv_dtype, q, k, v, beta, log_alpha, initial_state,
+ *  cu_seqlens, scale
+ *                 exactly as passed to gdr_prefill_chunked; num_qk_heads
+ *                 must equal num_heads (0 also means that); beta and
+ *                 log_alpha fp32.
+ *  d_out          [batch, seqlen, num_heads, head_dim_v]              fp32
+ *  d_final_state  [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, or
+ *                 NULL for zeros
+ *  dq, dk         [batch, seqlen, num_heads, head_dim_k]              fp32
+ *  dv             [batch, seqlen, num_heads, head_dim_v]              fp32
+ *  dbeta          [batch, seqlen, num_heads]                          fp32
+ *  dlog_alpha     log_alpha's shape                                   fp32
+ *  d_initial_state [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, or
+ *                 NULL (not written).  With a NULL initial_state it is the
+ *                 gradient with respect to the zero state.
+ *  workspace      device buffer of gdr_prefill_backward_workspace_bytes(...)
+ *                 bytes, 256-byte aligned; the library writes it (chunk
+ *                 records, each chunk's state and state gradient: about
+ *                 (3.6 KB + 8 d_k d_v / 32 B) per token and head at d_k = 128)
+ *                 and keeps nothing in it after the stream has run the call.
+ *
+ * Supported: head_dim_k in {32, 64, 128}; head_dim_v a multiple of 16 up to
+ * 128 (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out and the states 16-byte
+ * aligned, log_alpha 16-byte aligned for GDR_GATE_CHANNEL, everything else
+ * 4-byte.  No output may overlap an input, another output or the
+ * workspace.  All arithmetic is fp32; every gradient element is written by
+ * exactly one thread (no atomics), so results are bitwise reproducible.
+ * Rows of padding and packed sequences of length zero are handled (an empty
+ * sequence's d_initial_state is its d_final_state).  Enqueued on hip_stream;
+ * returns GDR_SUCCESS or an error status (nothing enqueued on error).
+ */
+size_t gdr_prefill_backward_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate, int32_t packed);
+gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
+                                const void *q, const void *k, const void *v, const float *beta,
+                                const float *log_alpha, const float *initial_state, const int32_t *cu_seqlens,
+                                float scale, const float *d_out, const float *d_final_state, float *dq,
+                                float *dk, float *dv, float *dbeta, float *dlog_alpha, float *d_initial_state,
+                                void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Detail of the last failing call on the calling thread ("" if none). */
 const char *gdr_last_error(void);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = gdr.load_library()
-    assert lib.gdr_abi_version() == 3 == gdr.ABI_VERSION
+    assert lib.gdr_abi_version() == 4 == gdr.ABI_VERSION
     assert lib.gdr_status_string(0) == b"success"
     assert lib.gdr_status_string(2) == b"not supported"
 
@@ -267,3 +267,70 @@ def test_prologue_accepts_in_place_state_and_empty_batch():
     st, err = _prologue(shape=(1, 0, 2, 64, 64, 1, 1), x=None, w=None, a=None, b=None, q=None, k=None, v=None,
                         beta=None, la=None)
     assert st == 0, err
+
+
+# ---- backward ---------------------------------------------------------------
+def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, q=A, k=A + 8 * MB, v=A + 16 * MB, beta=A + 24 * MB,
+              la=A + 25 * MB, s0=None, cu=None, dout=A + 26 * MB, dfin=None, dq=A + 32 * MB, dk=A + 34 * MB,
+              dv=A + 36 * MB, db=A + 38 * MB, dla=A + 39 * MB, dinit=None, ws=A + 64 * MB, wsb=64 * MB):
+    lib = gdr.load_library()
+    sh = gdr.PrefillShape(*shape)
+    v_ = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.gdr_prefill_backward(ctypes.byref(sh), gate, qkv, v_(q), v_(k), v_(v), v_(beta), v_(la), v_(s0), v_(cu),
+                                  1.0, v_(dout), v_(dfin), v_(dq), v_(dk), v_(dv), v_(db), v_(dla), v_(dinit), v_(ws),
+                                  wsb, None)
+    return st, lib.gdr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(shape=(0, 64, 2, 64, 64, 0, 0)), 1, "bad shape"),
+    (dict(shape=(1, 64, 2, 64, 64, 1, 1)), 2, "one q/k head per value head"),
+    (dict(shape=(1, 64, 2, 64, 64, 1, 3)), 1, "does not divide"),
+    (dict(shape=(1, 64, 2, 16, 64, 1, 0)), 2, "head_dim_k"),
+    (dict(shape=(1, 64, 2, 64, 256, 1, 0)), 2, "head_dim_v"),
+    (dict(shape=(1, 64, 2, 64, 40, 1, 0)), 2, "head_dim_v"),
+    (dict(shape=(1, 64, 70000, 64, 64, 1, 0)), 2, "65535 heads"),
+    (dict(gate=4), 1, "gate"),
+    (dict(qkv=5), 1, "dtype"),
+    (dict(shape=(2, 64, 2, 64, 64, 2, 0), cu=A + 40 * MB), 1, "batch == 1"),
+    (dict(shape=(2, 64, 2, 64, 64, 1, 0)), 1, "num_seqs == batch"),
+    (dict(shape=(1, 64, 2, 64, 64, 0, 0), cu=A + 40 * MB), 1, "at least one sequence"),
+    (dict(dq=None), 1, "non-NULL"),
+    (dict(dout=None), 1, "non-NULL"),
+    (dict(q=A + 8), 1, "q is not 16-byte aligned"),
+    (dict(dout=A + 26 * MB + 4), 1, "d_out is not 16-byte aligned"),
+    (dict(dinit=A + 40 * MB + 4), 1, "d_initial_state is not 16-byte aligned"),
+    (dict(db=A + 38 * MB + 2), 1, "4-byte aligned"),
+    (dict(gate=1, la=A + 25 * MB + 4), 1, "log_alpha must be 16-byte"),
+    (dict(dq=A + 8), 1, "dq overlaps q"),
+    (dict(dv=A + 34 * MB + 64), 1, "dk overlaps dv"),
+    (dict(dla=A + 26 * MB), 1, "dlog_alpha overlaps d_out"),
+    (dict(s0=A + 40 * MB, dinit=A + 40 * MB), 1, "d_initial_state overlaps initial_state"),
+    (dict(ws=A + 24 * MB), 1, "workspace overlaps beta"),
+    (dict(wsb=1000), 3, "workspace"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(ws=A + 64 * MB + 16), 1, "256-byte"),
+])
+def test_backward_rejects(kw, status, msg):
+    st, err = _backward(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_backward_workspace_size():
+    """Per (chunk slot, head): a record of e^{g_C} (dk), T and M (C x C) and
+    three C x dk operands in fp32, 256-byte aligned, plus one state and one
+    state gradient (dv x dk fp32); packed batches add the schedule and one
+    spare chunk slot per sequence."""
+    lib = gdr.load_library()
+    f = lib.gdr_prefill_backward_workspace_bytes
+    r256 = lambda b: -(-b // 256) * 256
+    rec = lambda dk: r256((dk + 2 * 32 * 32 + 3 * 32 * dk) * 4)
+    sh = gdr.PrefillShape(1, 1000, 4, 64, 32, 9, 0)
+    slots = 32 * 4
+    assert f(ctypes.byref(sh), 0, 0) == r256(slots * rec(64)) + 2 * r256(slots * 64 * 32 * 4)
+    assert f(ctypes.byref(sh), 1, 0) == f(ctypes.byref(sh), 0, 0)
+    slots = (32 + 9) * 4
+    assert f(ctypes.byref(sh), 0, 1) == 256 + 256 + r256(slots * rec(64)) + 2 * r256(slots * 64 * 32 * 4)
+    assert f(None, 0, 0) == 0
+    assert f(ctypes.byref(sh), 3, 0) == 0

@@ -1,0 +1,152 @@
+"""Backward of the chunked prefill on the GPU vs the fp64 oracle's gradients.
+
+Every gradient (dq, dk, dv, dbeta, dlog_alpha, d_initial_state) is compared
+element by element with the oracle on the same seeded inputs and loss
+gradients.  The GPU computes in fp32 from the stored bf16/fp32 values the
+oracle also sees, so the bar is fp32 arithmetic: max |gpu - oracle| <=
+TOL_BWD * RMS(oracle) per tensor.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_73_amd as gdr
+import oracle
+from parity import assert_close, gpu_available, say, to_np
+from workloads import WORKLOADS, Workload, backward_cotangents, prefill_inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
+DEV = "cuda"
+TOL_BWD = 1e-3
+NAMES = ("dq", "dk", "dv", "dbeta", "dlog_alpha", "d_initial_state")
+
+
+def _gpu(inp, cot, *, scale=1.0, with_final=True, with_init=True):
+    g = gdr.gdr_prefill_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], cot["d_out"],
+                                 initial_state=inp["initial_state"],
+                                 d_final_state=cot["d_final_state"] if with_final else None,
+                                 cu_seqlens=inp["cu_seqlens"], scale=scale, output_d_initial_state=with_init)
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle(inp, cot, *, scale=1.0, with_final=True, sl=None):
+    cu = inp["cu_seqlens"]
+    return oracle.recurrence_backward(
+        inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], cot["d_out"],
+        initial_state=inp["initial_state"], d_final_state=cot["d_final_state"] if with_final else None,
+        seq_bounds=None if cu is None else cu.cpu().numpy(), scale=scale)
+
+
+def _check(inp, cot, label, tol=TOL_BWD, **kw):
+    say(f"backward {label} {kw}")
+    got = _gpu(inp, cot, **kw)
+    ref = _oracle(inp, cot, scale=kw.get("scale", 1.0), with_final=kw.get("with_final", True))
+    worst = 0.0
+    for name in NAMES:
+        if got[name] is None:
+            continue
+        worst = max(worst, assert_close(name, got[name], ref[name], tol))
+    return got, worst
+
+
+def _small(dk, dv, H, T, gate, dtype, init, seed, B=1, lengths=None):
+    w = Workload("small", "backward", heads=H, dk=dk, dv=dv, qkv_dtype=dtype, gate=gate, batch=B, seqlen=T,
+                 init_state=init, seed=seed)
+    inp = prefill_inputs(w, DEV, lengths=lengths)
+    return inp, backward_cotangents(inp, seed, DEV)
+
+
+CASES = [
+    # dk, dv, H, T, gate, init, B
+    (32, 32, 2, 100, "head", False, 1),
+    (32, 16, 2, 31, "channel", True, 1),      # one ragged chunk
+    (64, 64, 2, 97, "channel", True, 1),
+    (64, 128, 1, 32, "head", True, 2),        # exactly one chunk per sequence
+    (128, 64, 3, 77, "head", True, 1),
+    (128, 128, 2, 130, "channel", True, 2),
+    (128, 128, 2, 200, "head", False, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"dk{c[0]}-dv{c[1]}-H{c[2]}-T{c[3]}-{c[4]}-s0{int(c[5])}-B{c[6]}")
+def test_backward_shapes(case, dtype):
+    dk, dv, H, T, gate, init, B = case
+    inp, cot = _small(dk, dv, H, T, gate, dtype, init, seed=dk + dv + T, B=B)
+    _check(inp, cot, f"{case} {dtype}")
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_backward_packed_with_empty_and_one_token_sequences(gate):
+    """Packed sequences of 37, 0, 100, 1 and 64 tokens: ragged chunks, an empty
+    sequence (its initial-state gradient is its final-state gradient) and a
+    single token."""
+    inp, cot = _small(128, 128, 2, 0, gate, torch.bfloat16, True, seed=21, lengths=[37, 0, 100, 1, 64])
+    got, _ = _check(inp, cot, f"packed {gate}")
+    torch.testing.assert_close(got["d_initial_state"][1], cot["d_final_state"][1], rtol=0, atol=0)
+
+
+def test_backward_without_final_gradient_or_initial_state():
+    """No final-state gradient (zeros), no initial state (zeros), no
+    initial-state gradient requested, a query scale."""
+    inp, cot = _small(128, 128, 2, 150, "channel", torch.bfloat16, False, seed=22)
+    _check(inp, cot, "no dS_final", scale=0.125, with_final=False, with_init=False)
+
+
+def test_backward_strong_decay():
+    """Per-channel log decay three times the workload's (a 32-token chunk then
+    spans up to ~ 100 nats of decay per channel), exercising the shifted
+    Gram operands."""
+    inp, cot = _small(128, 128, 2, 96, "channel", torch.bfloat16, True, seed=23)
+    inp["log_alpha"] = (3.0 * inp["log_alpha"]).contiguous()
+    _check(inp, cot, "strong decay")
+
+
+def test_backward_is_deterministic():
+    inp, cot = _small(128, 128, 4, 300, "channel", torch.bfloat16, True, seed=24)
+    a = _gpu(inp, cot)
+    b = _gpu(inp, cot)
+    for name in NAMES:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_backward_grouped_heads_not_supported():
+    inp, cot = _small(64, 64, 2, 40, "head", torch.bfloat16, False, seed=25)
+    with pytest.raises(gdr.GdrError, match="one q/k head per value head"):
+        gdr.gdr_prefill_backward(inp["q"][:, :, :1].contiguous(), inp["k"][:, :, :1].contiguous(), inp["v"],
+                                 inp["beta"], inp["log_alpha"], cot["d_out"])
+
+
+def test_gdn_backward_8k_workload():
+    """B=1, T=8192, H=16, d=128, bf16, per-head decay, S0 ~ N(0, 0.02^2):
+    every gradient of every head against the oracle."""
+    w = WORKLOADS["gdn_backward_8k"]
+    inp = prefill_inputs(w, DEV)
+    cot = backward_cotangents(inp, w.seed, DEV)
+    _check(inp, cot, "gdn_backward_8k")
+
+
+@pytest.mark.slow
+def test_kda_backward_32k_workload():
+    """B=2, T=32768, H=32, d=128, bf16, per-channel decay, S0: the GPU computes
+    every gradient; two (sequence, head) units are checked against the oracle
+    and everything is checked for finiteness."""
+    w = WORKLOADS["kda_backward_32k"]
+    inp = prefill_inputs(w, DEV)
+    cot = backward_cotangents(inp, w.seed, DEV)
+    say("backward kda_backward_32k (sampled units)")
+    got = _gpu(inp, cot)
+    for name in NAMES:
+        assert torch.isfinite(got[name]).all(), name
+    for (n, h) in [(0, 3), (1, 31)]:
+        sl = (slice(n, n + 1), slice(None), slice(h, h + 1))
+        sub = {key: inp[key][sl].contiguous() for key in ("q", "k", "v", "beta", "log_alpha")}
+        sub["initial_state"] = inp["initial_state"][n:n + 1, h:h + 1].contiguous()
+        sub["cu_seqlens"] = None
+        subc = {"d_out": cot["d_out"][sl].contiguous(),
+                "d_final_state": cot["d_final_state"][n:n + 1, h:h + 1].contiguous()}
+        ref = _oracle(sub, subc)
+        for name in NAMES:
+            g = got[name][n:n + 1, h:h + 1] if name == "d_initial_state" else got[name][sl]
+            assert_close(f"{name}[{n},{h}]", g, ref[name], TOL_BWD)

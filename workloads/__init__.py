@@ -24,6 +24,10 @@ Recipe (per workload, one seed):
   sequence's previous draft (uniform in [0, K - 1]: the tokens its call
   replays and commits) -- so every call reads every state and writes those
   with at least one accepted token.
+  The backward adds the loss's gradients with respect to the outputs and the
+  final states, d_out ~ N(0, 1) and d_final_state ~ N(0, 1), from a generator
+  seeded with the workload's seed + 1000003, so the forward inputs are the
+  prefill workload's own.
   Draws are fp32 from torch's seeded generator on the target device; q/k/v are
   then rounded to the storage dtype (bf16 round-to-nearest-even), states stay
   fp32, and gates stay fp32 unless a bf16 gate variant is asked for (then beta
@@ -40,7 +44,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" or "decode"
+    kind: str                 # "prefill", "decode", "prologue" or "backward"
     heads: int
     dk: int
     dv: int
@@ -82,6 +86,14 @@ WORKLOADS = {
     # previous draft's accepted tokens replayed and committed in the same call
     "mtp_decode_256x48": Workload("mtp_decode_256x48", "decode", heads=48, qk_heads=16, dk=128, dv=128,
                                   qkv_dtype=torch.bfloat16, gate="head", batch=256, tokens=4, slots=512, seed=6),
+    # the backward (training) pass on the two prefill shapes, with an initial
+    # state so its gradient is exercised
+    "gdn_backward_8k": Workload("gdn_backward_8k", "backward", heads=16, dk=128, dv=128,
+                                qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=8192,
+                                init_state=True, seed=8),
+    "kda_backward_32k": Workload("kda_backward_32k", "backward", heads=32, dk=128, dv=128,
+                                 qkv_dtype=torch.bfloat16, gate="channel", batch=2, seqlen=32768,
+                                 init_state=True, seed=9),
     # the layer prologue on that shape: the 10240 projected q/k/v channels of
     # 32768 tokens, with a convolution state
     "prologue_gdn_32k": Workload("prologue_gdn_32k", "prologue", heads=48, qk_heads=16, dk=128, dv=128,
@@ -155,6 +167,20 @@ def prefill_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, batc
         s0 = 0.02 * torch.randn(N, H, dv, dk, generator=g, device=device, dtype=f32)
     return {"q": q, "k": k, "v": v, "beta": beta.to(gate_dtype), "log_alpha": log_alpha.to(gate_dtype),
             "initial_state": s0, "cu_seqlens": cu}
+
+
+def backward_cotangents(inp, seed: int, device="cpu"):
+    """Gradients of a synthetic loss with respect to the prefill's outputs
+    and final states: d_out ~ N(0, 1) with v's shape and d_final_state ~
+    N(0, 1) [N, H, dv, dk], fp32 (generator seed: seed + 1000003)."""
+    B, T, H, dv = inp["v"].shape
+    dk = inp["k"].shape[-1]
+    cu = inp["cu_seqlens"]
+    N = B if cu is None else cu.numel() - 1
+    g = _gen(device, seed + 1000003)
+    d_out = torch.randn(B, T, H, dv, generator=g, device=device, dtype=torch.float32)
+    d_final = torch.randn(N, H, dv, dk, generator=g, device=device, dtype=torch.float32)
+    return {"d_out": d_out, "d_final_state": d_final}
 
 
 def decode_inputs(w: Workload, device="cpu", *, gate: str = "head", num_seqs: int | None = None,
