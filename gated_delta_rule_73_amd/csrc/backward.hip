@@ -22,15 +22,15 @@
 // Three kernels, all in fp32 on the 16x16x4 fp32 MFMA:
 //   bwd_prep_kernel  one workgroup per (chunk, head): the chunk record
 //                    D = e^{g_C}, T, M, Wn, Q e^g, K_end (fp32, in HBM).
-//   bwd_scan_kernel  one wave per (sequence, head, 16 value rows), walking
-//                    the sequence's chunks: forward from the initial state,
-//                    writing each chunk's incoming state; then backward from
-//                    the final-state gradient, writing each chunk's outgoing
-//                    state gradient and, at the end, the initial-state
-//                    gradient.  The wave keeps its 16 x d_k slice of the
-//                    state transposed in MFMA accumulators, so the products
-//                    with the state take it as an operand straight from
-//                    registers.
+//   bwd_scan_kernel  one workgroup per (sequence, head, 32 or 64 value rows),
+//                    walking the sequence's chunks: forward from the initial
+//                    state, writing each chunk's incoming state; then
+//                    backward from the final-state gradient, writing each
+//                    chunk's outgoing state gradient and, at the end, the
+//                    initial-state gradient.  Each wave keeps its 16 x d_k
+//                    slice of the state transposed in MFMA accumulators, so
+//                    the products with the state take it as an operand
+//                    straight from registers.
 //   bwd_grad_kernel  one workgroup per (chunk, head): every input gradient of
 //                    the chunk from its two states (no cross-chunk sums, no
 //                    atomics: the result is deterministic).
@@ -46,6 +46,7 @@
 namespace gdr {
 
 constexpr int kBC = 32;                      // chunk length of the backward
+constexpr int kGradThreads = 512;            // 8 waves: two per SIMD (the LDS holds one workgroup)
 
 // Record of one (chunk, head), fp32: D[dk] | T[C][C] | M[C][C] | Wn[C][dk] |
 // Qg[C][dk] (Q e^g) | Ke[C][dk] (K e^{g_C - g}); stride from launch.h.
@@ -73,13 +74,78 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // One 16x16 output tile of a product: acc += sum_k A(m, k) B(k, n) for
-// k < K, where fa(mi, k) = A(m0 + mi, k) and fb(k, ni) = B(k, n0 + ni).
-// On return acc[i] holds the element (m0 + 4 (lane >> 4) + i, n0 + (lane & 15)).
-template <class FA, class FB>
+// k < K <= KMAX, K a multiple of 32 (d_v, d_k or the chunk length), where
+// fa(mi, k) = A(m0 + mi, k) and fb(k, ni) = B(k, n0 + ni).  On return acc[i]
+// holds the element (m0 + 4 (lane >> 4) + i, n0 + (lane & 15)).  Each block of
+// 32 k gathers its operands first (their loads in flight together), then runs
+// its eight MFMAs.
+template <int KMAX, class FA, class FB>
 __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, int K, FA fa, FB fb) {
+    static_assert(KMAX % 32 == 0, "k blocks of 32");
     const int l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
-    for (int k0 = 0; k0 < K; k0 += 4) acc = mfma4(fa(lr, k0 + lq), fb(k0 + lq, lr), acc);
+#pragma unroll
+    for (int kb = 0; kb < KMAX; kb += 32) {
+        if (kb < K) {
+            float a[8], b[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                a[s] = fa(lr, kb + 4 * s + lq);
+                b[s] = fb(kb + 4 * s + lq, lr);
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) acc = mfma4(a[s], b[s], acc);
+        }
+    }
+    // keep the next product's operand loads behind this one
+    __builtin_amdgcn_sched_barrier(0);
     return acc;
+}
+
+// NQ tiles at once: acc[q] += sum_k A_q(m, k) B_q(k, n), with
+// fa(q, mi, kb, lk) = A_q(m0 + mi, kb + lk) and fb(q, kb, lk, ni) =
+// B_q(kb + lk, n0 + ni): kb is the wave-uniform part of k (a constant once
+// unrolled, so a buffer load can carry it as its scalar offset), lk the
+// lane's part.  The operands of a block of 32 k (every product's;
+// identical loads are shared) are gathered one block ahead of its 8 NQ
+// MFMAs, so products that read the same slow operand wait for it once and
+// the wait overlaps the previous block's MFMAs.
+template <int KMAX, int NQ, class FA, class FB>
+__device__ __forceinline__ void tile_mma_n(f32x4 (&acc)[NQ], int K, FA fa, FB fb) {
+    static_assert(KMAX % 32 == 0, "k blocks of 32");
+    constexpr int NB = KMAX / 32;
+    const int l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+    float a[2][NQ][8], b[2][NQ][8];
+    auto gather = [&](int blk, int buf) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                a[buf][q][s] = fa(q, lr, 32 * blk + 4 * s, lq);
+                b[buf][q][s] = fb(q, 32 * blk + 4 * s, lq, lr);
+            }
+    };
+    gather(0, 0);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        if (32 * blk < K) {
+            if (blk + 1 < NB && 32 * (blk + 1) < K) gather(blk + 1, (blk + 1) & 1);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) acc[q] = mfma4(a[blk & 1][q][s], b[blk & 1][q][s], acc[q]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Raw buffer loads: the byte offset splits into a per-lane VGPR part and a
+// uniform scalar part, so a sweep over k needs no per-k address registers.
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const float *base, long floats) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, (int)(floats * 4), kRawBufferWord3);
+}
+__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int lane_bytes, int uniform_bytes) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, lane_bytes, uniform_bytes, 0));
 }
 
 template <typename IT> __device__ __forceinline__ float ld1(const IT *p) { return to_f32(*p); }
@@ -135,22 +201,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
 
     for (int e = tid; e < C * DK / 4; e += NT) {
         const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv, gv = kv;
-        if (r < L.len) {
-            const long o = ((L.tok0 + r) * H + h) * DK + j;
-            kv = load4(k + o);
-            qv = load4(q + o);
-            if (KDA) gv = *reinterpret_cast<const float4 *>(p.log_alpha + o);
-        }
+        const bool in = r < L.len;                 // padding rows: zeros (clamped loads, no branch)
+        const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j;
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 kv = in ? load4(k + o) : z4, qv = in ? load4(q + o) : z4;
+        const float4 gv = KDA && in ? *reinterpret_cast<const float4 *>(p.log_alpha + o) : z4;
         sK[r][j] = kv.x, sK[r][j + 1] = kv.y, sK[r][j + 2] = kv.z, sK[r][j + 3] = kv.w;
         sQ[r][j] = qv.x, sQ[r][j + 1] = qv.y, sQ[r][j + 2] = qv.z, sQ[r][j + 3] = qv.w;
         if (KDA) sX[r][j] = gv.x, sX[r][j + 1] = gv.y, sX[r][j + 2] = gv.z, sX[r][j + 3] = gv.w;
     }
     if (tid < C) {
         const bool in = tid < L.len;
-        const long o = (L.tok0 + tid) * H + h;
-        sb[tid] = in ? p.beta[o] : 0.f;
-        if (!KDA) sg[tid] = in ? p.log_alpha[o] : 0.f;
+        const long o = (L.tok0 + min(tid, L.len - 1)) * H + h;
+        const float bb = p.beta[o], gg = KDA ? 0.f : p.log_alpha[o];
+        sb[tid] = in ? bb : 0.f;
+        if (!KDA) sg[tid] = in ? gg : 0.f;
     }
     __syncthreads();
     // inclusive cumulative log-decay (padding rows add zero)
@@ -215,7 +280,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
     // Wn = -T (diag(b) K e^g)
     for (int t = w; t < 2 * (DK / 16); t += NT / 64) {
         const int rt = t & 1, jt = t >> 1;
-        const f32x4 acc = tile_mma(zero4(), C, [&](int mi, int kk) { return sT[16 * rt + mi][kk]; },
+        const f32x4 acc = tile_mma<C>(zero4(), C, [&](int mi, int kk) { return sT[16 * rt + mi][kk]; },
                                    [&](int kk, int ni) { return sX[kk][16 * jt + ni]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) rec[R::W + (16 * rt + 4 * lq + i) * DK + 16 * jt + lr] = -acc[i];
@@ -223,23 +288,34 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// State scan over a sequence's chunks, one wave per 16 value rows.
+// State scan over a sequence's chunks.  A workgroup of NW waves takes 16 NW
+// value rows of one (sequence, head); each wave keeps its 16 x d_k slice of X
+// transposed in MFMA accumulators.
 //   forward  (BWD = false): X = state;  P = T diag(b) V + Wn X^T,
 //            X <- X Diag(D) + P^T K_end; writes X before each chunk.
 //   backward (BWD = true):  X = state gradient; Z = scale dO;
 //            P = M^T Z + K_end X^T, X <- X Diag(D) + P^T Wn + Z^T (Q e^g);
 //            writes X before each chunk (the chunk's outgoing gradient) and
 //            the initial-state gradient at the end.
-template <int DK, bool BWD, typename IT>
-__global__ __launch_bounds__(64) void bwd_scan_kernel(BwdKArgs p) {
-    constexpr int C = kBC, PK = DK + 4;
+// The next chunk's record and inputs are fetched into registers while the
+// current chunk's products run, then written to the other half of a
+// double-buffered LDS stage: one barrier per chunk.  The workgroups of one
+// (sequence, head) sit on one XCD (block b runs on XCD b mod 8), so its
+// records come from HBM once and from that XCD's L2 for the other slices.
+template <int DK, int NW, bool BWD, typename IT>
+__global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p) {
+    constexpr int C = kBC, PK = DK + 4, NT = 64 * NW, ZW = 16 * NW, ZP = ZW + 1, NGR = BWD ? C : 1;
+    constexpr int NE = C * DK / 4 / NT, NL = C * C / NT, NZ = C * ZW / NT;
+    static_assert(NE >= 1 && NL >= 1 && NZ >= 1, "scan tiling");
     using R = BRec<DK>;
-    __shared__ float sE[C][PK], sB[C][PK], sG[BWD ? C : 1][PK];
-    __shared__ float sL[C][C + 1], sZ[C][17], sD[DK], sS[C];
-    const int H = p.H, DV = p.dv, slices = DV / 16;
-    const int slice = blockIdx.x % slices, unit = blockIdx.x / slices;
+    __shared__ float sE[2][C][PK], sB[2][C][PK], sG[2][NGR][PK];
+    __shared__ float sL[2][C][C + 1], sZ[2][C][ZP], sD[2][DK], sS[2][C];
+    const int H = p.H, DV = p.dv, S = DV / ZW;
+    const int xcd = blockIdx.x & 7, kb = blockIdx.x >> 3;
+    const int unit = xcd + 8 * (kb / S), slice = kb % S;
+    if (unit >= p.num_seqs * H) return;
     const int n = p.cu ? p.order[unit / H] : unit / H, h = unit % H;
-    const int l = threadIdx.x, lr = l & 15, lq = l >> 4;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
     long rc0, tok_base;
     int nc, len;
     if (p.cu) {
@@ -249,7 +325,70 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdKArgs p) {
         nc = div_up(p.seqlen, C), rc0 = (long)n * nc;
         tok_base = (long)n * p.seqlen, len = p.seqlen;
     }
-    const int row = 16 * slice + lr;          // this lane's value row (as MFMA column)
+    const int row = ZW * slice + 16 * w + lr;     // this lane's value row (as MFMA column)
+    const IT *v = static_cast<const IT *>(p.v);
+
+    f32x4 rE[NE], rB[NE], rG[BWD ? NE : 1];
+    float rL[NL], rZ[NZ], rD = 0.f, rS = 0.f;
+    auto fetch = [&](int s) {
+        const int c = BWD ? nc - 1 - s : s;
+        const long rc = rc0 + c, tok0 = tok_base + (long)c * C;
+        const int clen = min(C, len - c * C);
+        const float *rec = p.rec + (rc * H + h) * p.rec_stride;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = tid + NT * u, r = e / (DK / 4), j = (e % (DK / 4)) * 4;
+            const f32x4 we = *reinterpret_cast<const f32x4 *>(rec + R::W + r * DK + j);
+            const f32x4 ke = *reinterpret_cast<const f32x4 *>(rec + R::KE + r * DK + j);
+            rE[u] = BWD ? ke : we;
+            rB[u] = BWD ? we : ke;
+            if (BWD) rG[u] = *reinterpret_cast<const f32x4 *>(rec + R::Q + r * DK + j);
+        }
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int e = tid + NT * u, r = e / C, cc = e % C;
+            rL[u] = BWD ? rec[R::M + cc * C + r] : rec[R::T + e];
+        }
+        // loads from clamped, always-valid rows and a select for padding rows:
+        // a load under a lane-dependent branch would make the compiler wait for
+        // every load in flight, the record loads above included
+#pragma unroll
+        for (int u = 0; u < NZ; ++u) {
+            const int e = tid + NT * u, r = e / ZW, i = e % ZW;
+            const long o = ((tok0 + min(r, clen - 1)) * H + h) * DV + ZW * slice + i;
+            const float z = BWD ? p.scale * p.d_out[o] : ld1(v + o);
+            rZ[u] = r < clen ? z : 0.f;
+        }
+        rD = rec[R::D + (tid & (DK - 1))];
+        const int tr = tid & (C - 1);
+        const float bb = p.beta[(tok0 + min(tr, clen - 1)) * H + h];
+        rS = BWD ? 1.f : (tr < clen ? bb : 0.f);
+    };
+    auto put = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = tid + NT * u, r = e / (DK / 4), j = (e % (DK / 4)) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sE[b][r][j + i] = rE[u][i];
+                sB[b][r][j + i] = rB[u][i];
+                if (BWD) sG[b][r][j + i] = rG[u][i];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int e = tid + NT * u;
+            sL[b][e / C][e % C] = rL[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NZ; ++u) {
+            const int e = tid + NT * u;
+            sZ[b][e / ZW][e % ZW] = rZ[u];
+        }
+        if (tid < DK) sD[b][tid] = rD;
+        if (tid < C) sS[b][tid] = rS;
+    };
+
     f32x4 x[DK / 16];
     {
         const float *init = BWD ? p.d_final : p.initial_state;
@@ -258,73 +397,51 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdKArgs p) {
             x[jt] = init ? *reinterpret_cast<const f32x4 *>(init + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq)
                          : zero4();
     }
-    const IT *v = static_cast<const IT *>(p.v);
+    if (nc > 0) {
+        fetch(0);
+        put(0);
+    }
+    __syncthreads();
     for (int s = 0; s < nc; ++s) {
+        const int b = s & 1;
+        if (s + 1 < nc) fetch(s + 1);
         const int c = BWD ? nc - 1 - s : s;
-        const long rc = rc0 + c, tok0 = tok_base + (long)c * C;
-        const int clen = std::min(C, len - c * C);
-        const float *rec = p.rec + (rc * H + h) * p.rec_stride;
+        const long rc = rc0 + c;
         float *dump = (BWD ? p.dstates : p.states) + ((rc * H + h) * DV + row) * DK;
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt) *reinterpret_cast<f32x4 *>(dump + 16 * jt + 4 * lq) = x[jt];
-        __syncthreads();
-        for (int e = l; e < C * DK / 4; e += 64) {
-            const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-            const f32x4 we = *reinterpret_cast<const f32x4 *>(rec + R::W + r * DK + j);
-            const f32x4 ke = *reinterpret_cast<const f32x4 *>(rec + R::KE + r * DK + j);
-            const f32x4 a = BWD ? ke : we, b = BWD ? we : ke;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sE[r][j + i] = a[i], sB[r][j + i] = b[i];
-            if (BWD) {
-                const f32x4 qg = *reinterpret_cast<const f32x4 *>(rec + R::Q + r * DK + j);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sG[r][j + i] = qg[i];
-            }
-        }
-        for (int e = l; e < C * C; e += 64) {
-            const int r = e / C, cc = e % C;
-            sL[r][cc] = BWD ? rec[R::M + cc * C + r] : rec[R::T + e];
-        }
-        for (int e = l; e < C * 16; e += 64) {
-            const int r = e >> 4, i = e & 15;
-            float z = 0.f;
-            if (r < clen) {
-                const long o = ((tok0 + r) * H + h) * DV + 16 * slice + i;
-                z = BWD ? p.scale * p.d_out[o] : ld1(v + o);
-            }
-            sZ[r][i] = z;
-        }
-        if (l < C) sS[l] = BWD ? 1.f : (l < clen ? p.beta[(tok0 + l) * H + h] : 0.f);
-        for (int j = l; j < DK; j += 64) sD[j] = rec[R::D + j];
-        __syncthreads();
 
         f32x4 pc[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int k0 = 0; k0 < C; k0 += 4) acc = mfma4(sL[16 * rt + lr][k0 + lq], sS[k0 + lq] * sZ[k0 + lq][lr], acc);
+            for (int k0 = 0; k0 < C; k0 += 4)
+                acc = mfma4(sL[b][16 * rt + lr][k0 + lq], sS[b][k0 + lq] * sZ[b][k0 + lq][16 * w + lr], acc);
 #pragma unroll
             for (int jt = 0; jt < DK / 16; ++jt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma4(sE[16 * rt + lr][16 * jt + 4 * lq + i], x[jt][i], acc);
+                for (int i = 0; i < 4; ++i) acc = mfma4(sE[b][16 * rt + lr][16 * jt + 4 * lq + i], x[jt][i], acc);
             pc[rt] = acc;
         }
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt) {
             f32x4 acc = x[jt];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= sD[16 * jt + 4 * lq + i];
+            for (int i = 0; i < 4; ++i) acc[i] *= sD[b][16 * jt + 4 * lq + i];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma4(sB[16 * rt + 4 * lq + i][16 * jt + lr], pc[rt][i], acc);
+                for (int i = 0; i < 4; ++i) acc = mfma4(sB[b][16 * rt + 4 * lq + i][16 * jt + lr], pc[rt][i], acc);
             if (BWD) {
 #pragma unroll
-                for (int k0 = 0; k0 < C; k0 += 4) acc = mfma4(sG[k0 + lq][16 * jt + lr], sZ[k0 + lq][lr], acc);
+                for (int k0 = 0; k0 < C; k0 += 4)
+                    acc = mfma4(sG[b][k0 + lq][16 * jt + lr], sZ[b][k0 + lq][16 * w + lr], acc);
             }
             x[jt] = acc;
         }
+        if (s + 1 < nc) put(b ^ 1);
+        __syncthreads();
     }
     if (BWD && p.d_init) {
 #pragma unroll
@@ -338,8 +455,9 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdKArgs p) {
 // outgoing state gradient dS.  Eight waves; C x n outputs are 16x16 tiles
 // (row tile rt, column tile) dealt round-robin to the waves.
 template <int DK, bool KDA, typename IT>
-__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
-    constexpr int C = kBC, NT = 512, NW = 8, PK = DK + 4, PV = 128 + 4, PB = PK > PV ? PK : PV;
+__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
+    constexpr int C = kBC, NT = kGradThreads, NW = NT / 64, PK = DK + 4, PV = 128 + 4, PB = PK > PV ? PK : PV;
+    constexpr int UV = div_up(2 * 128 / 16, NW), UK = div_up(2 * DK / 16, NW);   // tiles per wave (max)
     using R = BRec<DK>;
     // K e^g, then K e^{g-m}       | raw K, then K e^{m-g}      | g, then dg (per channel)
     __shared__ float sX1[C][PK], sX2[C][PK], sGg[KDA ? C : 1][PK];
@@ -360,28 +478,27 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     const float *rec = p.rec + (rc * H + h) * p.rec_stride;
     const float *S0 = p.states + (rc * H + h) * (long)DV * DK;
     const float *dS = p.dstates + (rc * H + h) * (long)DV * DK;
+    const __amdgpu_buffer_rsrc_t rS0 = buffer_of(S0, (long)DV * DK), rdS = buffer_of(dS, (long)DV * DK);
+    const __amdgpu_buffer_rsrc_t rRec = buffer_of(rec, p.rec_stride);
     const int ntv = 2 * (DV / 16), ntk = 2 * (DK / 16);
 
     // ---- loads
     for (int e = tid; e < C * DK / 4; e += NT) {
         const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), gv = kv;
-        if (r < L.len) {
-            const long o = ((L.tok0 + r) * H + h) * DK + j;
-            kv = load4(k + o);
-            if (KDA) gv = *reinterpret_cast<const float4 *>(p.log_alpha + o);
-        }
+        const bool in = r < L.len;
+        const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j;
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 kv = in ? load4(k + o) : z4;
+        const float4 gv = KDA && in ? *reinterpret_cast<const float4 *>(p.log_alpha + o) : z4;
         sX2[r][j] = kv.x, sX2[r][j + 1] = kv.y, sX2[r][j + 2] = kv.z, sX2[r][j + 3] = kv.w;
         if (KDA) sGg[r][j] = gv.x, sGg[r][j + 1] = gv.y, sGg[r][j + 2] = gv.z, sGg[r][j + 3] = gv.w;
     }
     for (int e = tid; e < C * DV / 4; e += NT) {
         const int r = e / (DV / 4), i = (e % (DV / 4)) * 4;
-        float4 vv = make_float4(0.f, 0.f, 0.f, 0.f), dd = vv;
-        if (r < L.len) {
-            const long o = ((L.tok0 + r) * H + h) * DV + i;
-            vv = load4(v + o);
-            dd = *reinterpret_cast<const float4 *>(p.d_out + o);
-        }
+        const bool in = r < L.len;
+        const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DV + i;
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 vv = in ? load4(v + o) : z4, dd = in ? *reinterpret_cast<const float4 *>(p.d_out + o) : z4;
         sB1[r][i] = vv.x, sB1[r][i + 1] = vv.y, sB1[r][i + 2] = vv.z, sB1[r][i + 3] = vv.w;
         sB4[r][i] = p.scale * dd.x, sB4[r][i + 1] = p.scale * dd.y;
         sB4[r][i + 2] = p.scale * dd.z, sB4[r][i + 3] = p.scale * dd.w;
@@ -393,9 +510,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     }
     if (tid < C) {
         const bool in = tid < L.len;
-        const long o = (L.tok0 + tid) * H + h;
-        sb[tid] = in ? p.beta[o] : 0.f;
-        if (!KDA) sg[tid] = in ? p.log_alpha[o] : 0.f;
+        const long o = (L.tok0 + min(tid, L.len - 1)) * H + h;
+        const float bb = p.beta[o], gg = KDA ? 0.f : p.log_alpha[o];
+        sb[tid] = in ? bb : 0.f;
+        if (!KDA) sg[tid] = in ? gg : 0.f;
     }
     {   // column partials of dS o S0 (the decay's share of the outgoing gradient)
         const int j = tid % DK, ig = tid / DK;
@@ -432,47 +550,67 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     }
     __syncthreads();
 
+    // Phases over C x d_v tiles: wave w takes (rt, it0) and (rt, it0 + 4),
+    // rt = w & 1, it0 = w >> 1, together (the two share their A rows).
+    const int nvt = DV / 16, rt_v = w & 1, it0 = w >> 1, it1 = it0 + 4 < nvt ? it0 + 4 : it0;
+    const bool has_v = it0 < nvt, has_v1 = it0 + 4 < nvt;
     // ---- Y = V - (K e^g) S0^T
-    for (int t = w; t < ntv; t += NW) {
-        const int rt = t & 1, it = t >> 1;
-        const f32x4 acc = tile_mma(zero4(), DK, [&](int mi, int kk) { return sX1[16 * rt + mi][kk]; },
-                                   [&](int kk, int ni) { return S0[(long)(16 * it + ni) * DK + kk]; });
+    if (has_v) {
+        f32x4 acc[2] = {zero4(), zero4()};
+        tile_mma_n<DK, 2>(acc, DK, [&](int, int mi, int kb, int lk) { return sX1[16 * rt_v + mi][kb + lk]; },
+                          [&](int q, int kb, int lk, int ni) {
+                              return bload(rS0, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
+                          });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sB1[16 * rt + 4 * lq + i][16 * it + lr] -= acc[i];
+        for (int i = 0; i < 4; ++i) {
+            sB1[16 * rt_v + 4 * lq + i][16 * it0 + lr] -= acc[0][i];
+            if (has_v1) sB1[16 * rt_v + 4 * lq + i][16 * it1 + lr] -= acc[1][i];
+        }
     }
     __syncthreads();
     // ---- U = T diag(b) Y;  dU = M^T dO' + K_end dS^T
-    for (int t = w; t < ntv; t += NW) {
-        const int rt = t & 1, it = t >> 1;
-        const f32x4 u = tile_mma(zero4(), C, [&](int mi, int kk) { return sT[16 * rt + mi][kk]; },
-                                 [&](int kk, int ni) { return sb[kk] * sB1[kk][16 * it + ni]; });
-        f32x4 du = tile_mma(zero4(), C, [&](int mi, int kk) { return sM[kk][16 * rt + mi]; },
-                            [&](int kk, int ni) { return sB4[kk][16 * it + ni]; });
-        du = tile_mma(du, DK, [&](int mi, int kk) { return rec[R::KE + (16 * rt + mi) * DK + kk]; },
-                      [&](int kk, int ni) { return dS[(long)(16 * it + ni) * DK + kk]; });
+    if (has_v) {
+        f32x4 u[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
+        tile_mma_n<C, 2>(u, C, [&](int, int mi, int kb, int lk) { return sT[16 * rt_v + mi][kb + lk]; },
+                         [&](int q, int kb, int lk, int ni) {
+                             return sb[kb + lk] * sB1[kb + lk][16 * (q ? it1 : it0) + ni];
+                         });
+        tile_mma_n<C, 2>(du, C, [&](int, int mi, int kb, int lk) { return sM[kb + lk][16 * rt_v + mi]; },
+                         [&](int q, int kb, int lk, int ni) { return sB4[kb + lk][16 * (q ? it1 : it0) + ni]; });
+        tile_mma_n<DK, 2>(du, DK, [&](int, int mi, int kb, int lk) {
+                              return bload(rRec, (R::KE + (16 * rt_v + mi) * DK + lk) * 4, kb * 4);
+                          },
+                          [&](int q, int kb, int lk, int ni) {
+                              return bload(rdS, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
+                          });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sB2[16 * rt + 4 * lq + i][16 * it + lr] = u[i];
-            sB3[16 * rt + 4 * lq + i][16 * it + lr] = du[i];
+            const int r = 16 * rt_v + 4 * lq + i;
+            sB2[r][16 * it0 + lr] = u[0][i];
+            sB3[r][16 * it0 + lr] = du[0][i];
+            if (has_v1) {
+                sB2[r][16 * it1 + lr] = u[1][i];
+                sB3[r][16 * it1 + lr] = du[1][i];
+            }
         }
     }
     __syncthreads();
     // ---- dT = dU (diag(b) Y)^T;  Z = T^T dU (kept in registers);  d beta (value part)
     if (w < 4) {
         const int rt = w & 1, ct = w >> 1;
-        const f32x4 a = tile_mma(zero4(), DV, [&](int mi, int kk) { return sB3[16 * rt + mi][kk]; },
+        const f32x4 a = tile_mma<128>(zero4(), DV, [&](int mi, int kk) { return sB3[16 * rt + mi][kk]; },
                                  [&](int kk, int ni) { return sb[16 * ct + ni] * sB1[16 * ct + ni][kk]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) sdT[16 * rt + 4 * lq + i][16 * ct + lr] = a[i];
     }
-    f32x4 z[2];
+    f32x4 z[UV];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < UV; ++u) {
         const int t = w + NW * u;
         z[u] = zero4();
         if (t < ntv) {
             const int rt = t & 1, it = t >> 1;
-            z[u] = tile_mma(zero4(), C, [&](int mi, int kk) { return sT[kk][16 * rt + mi]; },
+            z[u] = tile_mma<C>(zero4(), C, [&](int mi, int kk) { return sT[kk][16 * rt + mi]; },
                             [&](int kk, int ni) { return sB3[kk][16 * it + ni]; });
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -486,7 +624,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     // ---- dV = dY = diag(b) Z (written out and kept in place of dU);
     //      E1 = dT T^T;  shifted operands;  Q e^{g-m} in place of Y
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < UV; ++u) {
         const int t = w + NW * u;
         if (t < ntv) {
             const int rt = t & 1, it = t >> 1;
@@ -501,7 +639,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     }
     if (w < 4) {
         const int rt = w & 1, ct = w >> 1;
-        const f32x4 a = tile_mma(zero4(), C, [&](int mi, int kk) { return sdT[16 * rt + mi][kk]; },
+        const f32x4 a = tile_mma<C>(zero4(), C, [&](int mi, int kk) { return sdT[16 * rt + mi][kk]; },
                                  [&](int kk, int ni) { return sT[16 * ct + ni][kk]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) sE1[16 * rt + 4 * lq + i][16 * ct + lr] = a[i];
@@ -514,8 +652,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     }
     for (int e = tid; e < C * DK / 4; e += NT) {
         const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < L.len) qv = load4(q + ((L.tok0 + r) * H + h) * DK + j);
+        const float4 qv = r < L.len ? load4(q + ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
         sB1[r][j] = qv.x * expf(gval(r, j) - mval(j));
         sB1[r][j + 1] = qv.y * expf(gval(r, j + 1) - mval(j + 1));
         sB1[r][j + 2] = qv.z * expf(gval(r, j + 2) - mval(j + 2));
@@ -530,9 +668,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     // ---- dA = strict_tril(-T^T E1), d beta (Gram part), diag(b) dA;  dM = tril(dO' U^T)
     if (w < 4) {
         const int rt = w & 1, ct = w >> 1;
-        const f32x4 a = tile_mma(zero4(), C, [&](int mi, int kk) { return sT[kk][16 * rt + mi]; },
+        const f32x4 a = tile_mma<C>(zero4(), C, [&](int mi, int kk) { return sT[kk][16 * rt + mi]; },
                                  [&](int kk, int ni) { return sE1[kk][16 * ct + ni]; });
-        const f32x4 gm = tile_mma(zero4(), DK, [&](int mi, int kk) { return sX1[16 * rt + mi][kk]; },
+        const f32x4 gm = tile_mma<DK>(zero4(), DK, [&](int mi, int kk) { return sX1[16 * rt + mi][kk]; },
                                   [&](int kk, int ni) { return sX2[16 * ct + ni][kk]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -546,7 +684,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
         }
     } else {
         const int rt = (w - 4) & 1, ct = (w - 4) >> 1;
-        const f32x4 a = tile_mma(zero4(), DV, [&](int mi, int kk) { return sB4[16 * rt + mi][kk]; },
+        const f32x4 a = tile_mma<128>(zero4(), DV, [&](int mi, int kk) { return sB4[16 * rt + mi][kk]; },
                                  [&](int kk, int ni) { return sB2[16 * ct + ni][kk]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -556,26 +694,37 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
     }
     __syncthreads();
     // ---- per (row, key channel): dq, dk and the log-decay gradient dg
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    //      (one output tile at a time: each holds seven products' operands)
+#pragma unroll 1
+    for (int u = 0; u < UK; ++u) {
         const int t = w + NW * u;
         if (t >= ntk) continue;
         const int rt = t & 1, jt = t >> 1;
         const int j = 16 * jt + lr;
-        const f32x4 dq0 = tile_mma(zero4(), DV, [&](int mi, int kk) { return sB4[16 * rt + mi][kk]; },
-                                   [&](int kk, int ni) { return S0[(long)kk * DK + 16 * jt + ni]; });
-        const f32x4 dy0 = tile_mma(zero4(), DV, [&](int mi, int kk) { return sB3[16 * rt + mi][kk]; },
-                                   [&](int kk, int ni) { return S0[(long)kk * DK + 16 * jt + ni]; });
-        const f32x4 uds = tile_mma(zero4(), DV, [&](int mi, int kk) { return sB2[16 * rt + mi][kk]; },
-                                   [&](int kk, int ni) { return dS[(long)kk * DK + 16 * jt + ni]; });
-        const f32x4 dmk = tile_mma(zero4(), C, [&](int mi, int kk) { return sdM[16 * rt + mi][kk]; },
-                                   [&](int kk, int ni) { return sX2[kk][16 * jt + ni]; });
-        const f32x4 dak = tile_mma(zero4(), C, [&](int mi, int kk) { return sdA[16 * rt + mi][kk]; },
-                                   [&](int kk, int ni) { return sX2[kk][16 * jt + ni]; });
-        f32x4 tq = tile_mma(zero4(), C, [&](int mi, int kk) { return sdM[kk][16 * rt + mi]; },
-                            [&](int kk, int ni) { return sB1[kk][16 * jt + ni]; });
-        tq = tile_mma(tq, C, [&](int mi, int kk) { return sdA[kk][16 * rt + mi]; },
-                      [&](int kk, int ni) { return sX1[kk][16 * jt + ni]; });
+        // the three products with the states (dO' S0, dY S0, U dS: S0 read once)
+        f32x4 st[3] = {zero4(), zero4(), zero4()};
+        tile_mma_n<128, 3>(st, DV, [&](int q, int mi, int kb, int lk) {
+                               const int kk = kb + lk;
+                               return q == 0 ? sB4[16 * rt + mi][kk] : q == 1 ? sB3[16 * rt + mi][kk] : sB2[16 * rt + mi][kk];
+                           },
+                           [&](int q, int kb, int lk, int ni) {
+                               return bload(q < 2 ? rS0 : rdS, (lk * DK + 16 * jt + ni) * 4, kb * DK * 4);
+                           });
+        // the chunk-local ones: dM Khs, dA Khs, dM^T Qts + dA^T Kts
+        f32x4 gm[4] = {zero4(), zero4(), zero4(), zero4()};
+        tile_mma_n<C, 4>(gm, C, [&](int q, int mi, int kb, int lk) {
+                             const int kk = kb + lk;
+                             return q == 0 ? sdM[16 * rt + mi][kk] : q == 1 ? sdA[16 * rt + mi][kk]
+                                  : q == 2 ? sdM[kk][16 * rt + mi] : sdA[kk][16 * rt + mi];
+                         },
+                         [&](int q, int kb, int lk, int ni) {
+                             const int kk = kb + lk;
+                             return q < 2 ? sX2[kk][16 * jt + ni] : q == 2 ? sB1[kk][16 * jt + ni] : sX1[kk][16 * jt + ni];
+                         });
+        const f32x4 dq0 = st[0], dy0 = st[1], uds = st[2], dmk = gm[0], dak = gm[1];
+        f32x4 tq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tq[i] = gm[2][i] + gm[3][i];
         float colk = 0.f;
         float rowg[4];
 #pragma unroll
@@ -587,11 +736,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdKArgs p) {
             const float gk1 = -dy0[i] * eg + dak[i] * egm;
             const float gk2 = tq[i] * emg;
             const float gk3 = uds[i] * egc;
-            float kk = 0.f, qq = 0.f;
+            const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j;
+            const float kk = r < L.len ? ld1(k + o) : 0.f, qq = r < L.len ? ld1(q + o) : 0.f;
             if (r < L.len) {
-                const long o = ((L.tok0 + r) * H + h) * DK + j;
-                kk = ld1(k + o);
-                qq = ld1(q + o);
                 p.dq[o] = dQ;
                 p.dk[o] = gk1 + gk2 + gk3;
             }
@@ -648,13 +795,24 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStr
         hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    const unsigned scan_blocks = (unsigned)((long)a.num_seqs * a.num_heads * (a.dv / 16));
-    hipLaunchKernelGGL((bwd_scan_kernel<DK, false, IT>), dim3(scan_blocks), dim3(64), 0, st, kp);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL((bwd_scan_kernel<DK, true, IT>), dim3(scan_blocks), dim3(64), 0, st, kp);
+    // four waves (64 value rows) per scan workgroup when that still gives a
+    // workgroup to at least half the CUs, else two
+    const long units = (long)a.num_seqs * a.num_heads;
+    const bool four = a.dv % 64 == 0 && units * (a.dv / 64) >= 128;
+    const long per_unit = a.dv / (four ? 64 : 32);
+    const unsigned scan_blocks = (unsigned)(8 * ((units + 7) / 8) * per_unit);
+    if (four) {
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, false, IT>), dim3(scan_blocks), dim3(256), 0, st, kp);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, true, IT>), dim3(scan_blocks), dim3(256), 0, st, kp);
+    } else {
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, false, IT>), dim3(scan_blocks), dim3(128), 0, st, kp);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, true, IT>), dim3(scan_blocks), dim3(128), 0, st, kp);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (nrc > 0) {
-        hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(512), 0, st, kp);
+        hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(kGradThreads), 0, st, kp);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     return hipSuccess;
@@ -667,7 +825,7 @@ static hipError_t dispatch_dk(const BackwardArgs &a, const BwdKArgs &kp, hipStre
 }
 
 bool backward_supported(int dk, int dv) {
-    return (dk == 32 || dk == 64 || dk == 128) && dv >= 16 && dv <= 128 && dv % 16 == 0;
+    return (dk == 32 || dk == 64 || dk == 128) && dv >= 32 && dv <= 128 && dv % 32 == 0;
 }
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {

@@ -274,8 +274,8 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     const int dk = s.head_dim_k, dv = s.head_dim_v;
     const bool bf16 = qkv_dtype == GDR_BF16, kda = gate == GDR_GATE_CHANNEL;
     if (!gdr::backward_supported(dk, dv))
-        return fail(GDR_ERROR_NOT_SUPPORTED, "backward needs head_dim_k in {32, 64, 128} and head_dim_v a multiple "
-                    "of 16 <= 128 (got %d, %d)", dk, dv);
+        return fail(GDR_ERROR_NOT_SUPPORTED, "backward needs head_dim_k in {32, 64, 128} and head_dim_v in {32, 64, "
+                    "96, 128} (got %d, %d)", dk, dv);
 
     const size_t es = dsize(qkv_dtype);
     const size_t nq = (size_t)tokens * s.num_heads * dk, nv = (size_t)tokens * s.num_heads * dv;

@@ -342,8 +342,8 @@ const char *gdr_status_string(gdr_status status);
  *                 (3.6 KB + 8 d_k d_v / 32 B) per token and head at d_k = 128)
  *                 and keeps nothing in it after the stream has run the call.
  *
- * Supported: head_dim_k in {32, 64, 128}; head_dim_v a multiple of 16 up to
- * 128 (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out and the states 16-byte
+ * Supported: head_dim_k in {32, 64, 128}; head_dim_v in {32, 64, 96, 128}
+ * (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out and the states 16-byte
  * aligned, log_alpha 16-byte aligned for GDR_GATE_CHANNEL, everything else
  * 4-byte.  No output may overlap an input, another output or the
  * workspace.  All arithmetic is fp32; every gradient element is written by

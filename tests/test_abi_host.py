@@ -289,6 +289,8 @@ def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, q=A, k=A + 8 * MB, 
     (dict(shape=(1, 64, 2, 16, 64, 1, 0)), 2, "head_dim_k"),
     (dict(shape=(1, 64, 2, 64, 256, 1, 0)), 2, "head_dim_v"),
     (dict(shape=(1, 64, 2, 64, 40, 1, 0)), 2, "head_dim_v"),
+    (dict(shape=(1, 64, 2, 64, 48, 1, 0)), 2, "head_dim_v"),
+    (dict(shape=(1, 64, 2, 64, 16, 1, 0)), 2, "head_dim_v"),
     (dict(shape=(1, 64, 70000, 64, 64, 1, 0)), 2, "65535 heads"),
     (dict(gate=4), 1, "gate"),
     (dict(qkv=5), 1, "dtype"),

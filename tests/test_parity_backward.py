@@ -60,7 +60,8 @@ def _small(dk, dv, H, T, gate, dtype, init, seed, B=1, lengths=None):
 CASES = [
     # dk, dv, H, T, gate, init, B
     (32, 32, 2, 100, "head", False, 1),
-    (32, 16, 2, 31, "channel", True, 1),      # one ragged chunk
+    (32, 32, 2, 31, "channel", True, 1),      # one ragged chunk
+    (64, 96, 2, 70, "channel", True, 1),      # value rows in two-wave slices
     (64, 64, 2, 97, "channel", True, 1),
     (64, 128, 1, 32, "head", True, 2),        # exactly one chunk per sequence
     (128, 64, 3, 77, "head", True, 1),
