@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 PROFILE_PMC = os.path.join(ROOT, "profiles", "prefill_kda_32k_traffic.json")
 # the sources that define the headline prefill's two kernels and their launch
 KERNEL_SOURCES = ["prefill_impl.h", "prefill_shapes.h", "prefill_bf16_kda.hip", "prefill.hip"]
@@ -70,6 +71,31 @@ def prefill_alg_bytes(B, T, H, dk, dv, kda, out_bytes, init_state=True, final_st
 def prefill_alg_flops(B, T, H, dk, dv, C):
     # dense chunk products of the chunked form, full C x C tiles
     return B * T * H * (4 * C * (dk + dv) + 6 * dk * dv)
+
+
+def backward_alg_bytes(B, T, H, dk, dv, kda, N, qkv_bytes=2, init_state=True):
+    """Bytes the backward must move once: q, k, v, beta, log alpha and d_out
+    in; dq, dk, dv, dbeta, dlog alpha out (fp32); the initial state and the
+    final-state gradient in, the initial-state gradient out."""
+    gate = 4 * dk if kda else 4
+    per = qkv_bytes * (2 * dk + dv) + 4 + gate + 4 * dv          # inputs and d_out
+    per += 4 * (2 * dk + dv) + 4 + gate                            # gradients
+    states = N * H * dv * dk * 4 * (3 if init_state else 2)
+    return B * T * H * per + states
+
+
+def backward_alg_flops(B, T, H, dk, dv, C=32):
+    """Flops of the chunked backward's dense products per token-head (full
+    C x C tiles): the chunk records (A, M, W), the forward state pass
+    (T diag(b) V, W S^T, U^T K_end), the backward state pass (M^T dO,
+    K_end dS^T, dU^T W, dO^T Q e^g) and the chunk gradients (five C dk dv,
+    five C^2 dv, five C^2 dk products and the two C^3 of the inverse's
+    adjoint), divided by C."""
+    per = 2 * 3 * C * dk
+    per += 2 * (C * dv + 2 * dk * dv)
+    per += 2 * (C * dv + 3 * dk * dv)
+    per += 2 * (5 * dk * dv + 5 * C * dv + 5 * C * dk + 2 * C * C)
+    return B * T * H * per
 
 
 def decode_alg_bytes(N, H, dk, dv, kda, out_bytes):
@@ -304,6 +330,38 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
         "us_per_call": round(t * 1e6, 2), "us_median": round(med * 1e6, 2), "us_min": round(mn * 1e6, 2),
         "Mtok_s": round(N * K / t / 1e6, 4), "alg_bytes": by,
         "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del m, mout
+
+    from workloads import backward_cotangents
+
+    res["prefill_backward"] = {}
+    for name in ("kda_backward_32k", "gdn_backward_8k"):
+        wb = WORKLOADS[name]
+        print(f"[bench] {wb.name}", file=sys.stderr, flush=True)
+        bi = prefill_inputs(wb, dev)
+        bc = backward_cotangents(bi, wb.seed, dev)
+        B, T, H, dk = bi["q"].shape
+        dv = bi["v"].shape[-1]
+        kda = bi["log_alpha"].dim() == 4
+        f = lambda: gdr.gdr_prefill_backward(bi["q"], bi["k"], bi["v"], bi["beta"], bi["log_alpha"], bc["d_out"],
+                                             initial_state=bi["initial_state"], d_final_state=bc["d_final_state"])
+        for _ in range(args.warmup):
+            f()
+        steps = max(1, min(args.steps, 5)) if kda else args.steps
+        t, med, mn = time_calls(f, steps)
+        by = backward_alg_bytes(B, T, H, dk, dv, kda, B)
+        fl = backward_alg_flops(B, T, H, dk, dv)
+        res["prefill_backward"][name] = {
+            "workload": f"{name}: gradients of q, k, v, beta, log alpha and the initial state through the chunked "
+                        f"prefill, B={B}, T={T}, H={H}, d={dk}, bf16 q/k/v, fp32 gates, d_out and d_final_state "
+                        f"~ N(0, 1), {'per-channel' if kda else 'per-head'} decay, S0 given; fp32 arithmetic",
+            "calls": steps, "us_per_call": round(t * 1e6, 1), "us_median": round(med * 1e6, 1),
+            "us_min": round(mn * 1e6, 1), "Mtok_s": round(B * T / t / 1e6, 3), "alg_bytes": by,
+            "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+            "alg_flops": fl, "TFLOPs": round(fl / t / 1e12, 2),
+            "frac_of_fp32_mfma_peak": round(fl / t / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
+        del bi, bc
+        torch.cuda.empty_cache()
     return res
 
 

@@ -458,6 +458,7 @@ template <int DK, bool KDA, typename IT>
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     constexpr int C = kBC, NT = kGradThreads, NW = NT / 64, PK = DK + 4, PV = 128 + 4, PB = PK > PV ? PK : PV;
     constexpr int UV = div_up(2 * 128 / 16, NW), UK = div_up(2 * DK / 16, NW);   // tiles per wave (max)
+    static_assert(NW >= 8 && NW % 2 == 0, "the C x C phases deal tiles to waves 0-7");
     using R = BRec<DK>;
     // K e^g, then K e^{g-m}       | raw K, then K e^{m-g}      | g, then dg (per channel)
     __shared__ float sX1[C][PK], sX2[C][PK], sGg[KDA ? C : 1][PK];
@@ -550,10 +551,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     }
     __syncthreads();
 
-    // Phases over C x d_v tiles: wave w takes (rt, it0) and (rt, it0 + 4),
-    // rt = w & 1, it0 = w >> 1, together (the two share their A rows).
-    const int nvt = DV / 16, rt_v = w & 1, it0 = w >> 1, it1 = it0 + 4 < nvt ? it0 + 4 : it0;
-    const bool has_v = it0 < nvt, has_v1 = it0 + 4 < nvt;
+    // Phases over C x d_v tiles: wave w takes (rt, it0) and, when it exists,
+    // (rt, it0 + NW / 2), rt = w & 1, it0 = w >> 1, together (the two share
+    // their A rows).
+    constexpr int HW = NW / 2;
+    const int nvt = DV / 16, rt_v = w & 1, it0 = w >> 1, it1 = it0 + HW < nvt ? it0 + HW : it0;
+    const bool has_v = it0 < nvt, has_v1 = it0 + HW < nvt;
     // ---- Y = V - (K e^g) S0^T
     if (has_v) {
         f32x4 acc[2] = {zero4(), zero4()};
@@ -682,7 +685,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
             if (lr == 0) sPb2[ct][r] = s;
             sdA[r][c] = sb[r] * d;
         }
-    } else {
+    } else if (w < 8) {
         const int rt = (w - 4) & 1, ct = (w - 4) >> 1;
         const f32x4 a = tile_mma<128>(zero4(), DV, [&](int mi, int kk) { return sB4[16 * rt + mi][kk]; },
                                  [&](int kk, int ni) { return sB2[16 * ct + ni][kk]; });
