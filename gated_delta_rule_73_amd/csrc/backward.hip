@@ -237,12 +237,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
         const int r = e / DK, j = e % DK;
         const float g = KDA ? sX[r][j] : sg[r], m = KDA ? sm[j] : sm[0], gl = KDA ? sgl[j] : sgl[0];
         const float kk = sK[r][j], qq = sQ[r][j];
-        rec[R::Q + e] = qq * expf(g);
+        // e^{g} and e^{g_C - g} are at most 1; e^{g - m} and its reciprocal stay
+        // within e^{+-(g_first - g_last)/2}
+        const float eg = expf(g), egm = expf(g - m), emg = 1.f / egm;
+        rec[R::Q + e] = qq * eg;
         rec[R::KE + e] = kk * expf(gl - g);
-        sK[r][j] = kk * expf(g - m);
-        sKh[r][j] = kk * expf(m - g);
-        sQ[r][j] = qq * expf(g - m);
-        sX[r][j] = sb[r] * kk * expf(g);
+        sK[r][j] = kk * egm;
+        sKh[r][j] = kk * emg;
+        sQ[r][j] = qq * egm;
+        sX[r][j] = sb[r] * kk * eg;
     }
     for (int j = tid; j < DK; j += NT) rec[R::D + j] = expf(KDA ? sgl[j] : sgl[0]);
     __syncthreads();
@@ -265,18 +268,49 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
         }
     }
     __syncthreads();
-    // T = (I + A)^-1 by forward substitution, lane j building column j
-    if (tid < C) {
-        const int j = tid;
-        for (int r = 0; r < C; ++r) {
+    // T = (I + A)^-1 by 16 x 16 blocks.  The diagonal blocks by forward
+    // substitution row by row: lane j of a half-wave keeps column j of its block
+    // in registers and reads A's entries as LDS broadcasts (fully unrolled);
+    // then T21 = -T22 (A21 T11) by two MFMA products; T12 = 0.
+    if (tid < 32) {
+        const int o = 16 * (tid >> 4), j = tid & 15;
+        float col[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
             float t = r == j ? 1.f : 0.f;
-            if (r > j)
-                for (int i = j; i < r; ++i) t -= sA[r][i] * sT[i][j];
-            sT[r][j] = t;
-            rec[R::T + r * C + j] = t;
+#pragma unroll
+            for (int i = 0; i < r; ++i) t -= sA[o + r][o + i] * col[i];
+            col[r] = t;                         // zero above the diagonal (col[i] = 0 for i < j)
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sT[o + r][o + j] = col[r];
+            sT[r][16 + j] = 0.f;                // T12 (both half-waves write the same zeros)
         }
     }
     __syncthreads();
+    if (w == 0) {   // X = A21 T11 into T12's place (zero again below)
+        f32x4 x = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) x = mfma4(sA[16 + lr][k0 + lq], sT[k0 + lq][lr], x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[4 * lq + i][16 + lr] = x[i];
+    }
+    __syncthreads();
+    if (w == 0) {   // T21 = -T22 X
+        f32x4 t21 = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) t21 = mfma4(sT[16 + lr][16 + k0 + lq], sT[k0 + lq][16 + lr], t21);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[16 + 4 * lq + i][lr] = -t21[i];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[4 * lq + i][16 + lr] = 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < C * C; e += NT) rec[R::T + e] = sT[e / C][e % C];
     // Wn = -T (diag(b) K e^g)
     for (int t = w; t < 2 * (DK / 16); t += NT / 64) {
         const int rt = t & 1, jt = t >> 1;
@@ -466,7 +500,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     __shared__ float sB1[C][PB], sB2[C][PV], sB3[C][PV], sB4[C][PV];
     __shared__ float sT[C][C + 1], sM[C][C + 1], sdT[C][C + 1], sdA[C][C + 1], sdM[C][C + 1], sE1[C][C + 1];
     __shared__ float sb[C], sg[C], sm[DK], sgl[DK], sdgc[DK], sdb[C];
-    __shared__ float sRed[NT / DK][DK];       // column partials of dS o S0
+    constexpr int Q4 = DK / 4, RS = NT / Q4;   // dS o S0 column sums: RS row groups of float4 columns
+    __shared__ float sRed[RS][DK];            // column partials of dS o S0
     __shared__ float sPb[8][C], sPb2[2][C];   // d beta partials (per value tile / column tile)
     __shared__ float sPc[2][DK];              // column partials of gK3 o K
     __shared__ float sPr[DK / 16][C];         // row partials of dg (per-head decay)
@@ -494,12 +529,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         sX2[r][j] = kv.x, sX2[r][j + 1] = kv.y, sX2[r][j + 2] = kv.z, sX2[r][j + 3] = kv.w;
         if (KDA) sGg[r][j] = gv.x, sGg[r][j + 1] = gv.y, sGg[r][j + 2] = gv.z, sGg[r][j + 3] = gv.w;
     }
-    for (int e = tid; e < C * DV / 4; e += NT) {
-        const int r = e / (DV / 4), i = (e % (DV / 4)) * 4;
+#pragma unroll
+    for (int u = 0; u < div_up(C * 128 / 4, NT); ++u) {     // fixed trip count, clamped index
+        const int e = tid + NT * u, ec = min(e, C * DV / 4 - 1);
+        const int r = ec / (DV / 4), i = (ec % (DV / 4)) * 4;
         const bool in = r < L.len;
         const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DV + i;
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
         const float4 vv = in ? load4(v + o) : z4, dd = in ? *reinterpret_cast<const float4 *>(p.d_out + o) : z4;
+        if (e >= C * DV / 4) continue;
         sB1[r][i] = vv.x, sB1[r][i + 1] = vv.y, sB1[r][i + 2] = vv.z, sB1[r][i + 3] = vv.w;
         sB4[r][i] = p.scale * dd.x, sB4[r][i + 1] = p.scale * dd.y;
         sB4[r][i + 2] = p.scale * dd.z, sB4[r][i + 3] = p.scale * dd.w;
@@ -516,11 +554,23 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         sb[tid] = in ? bb : 0.f;
         if (!KDA) sg[tid] = in ? gg : 0.f;
     }
-    {   // column partials of dS o S0 (the decay's share of the outgoing gradient)
-        const int j = tid % DK, ig = tid / DK;
-        float s = 0.f;
-        for (int i = ig; i < DV; i += NT / DK) s += dS[(long)i * DK + j] * S0[(long)i * DK + j];
-        sRed[ig][j] = s;
+    {   // column partials of dS o S0 (the decay's share of the outgoing gradient): thread tid
+        // sums the four columns 4 (tid % Q4).. over rows tid / Q4 + RS u.  The loop is
+        // unrolled to its compile-time bound with clamped rows, so all its loads (the first
+        // touch of this chunk's two states) are in flight together.
+        const int j4 = (tid % Q4) * 4, i0 = tid / Q4;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int u = 0; u < div_up(128, RS); ++u) {
+            const int i = i0 + RS * u, ic = min(i, DV - 1);
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(dS + (long)ic * DK + j4);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(S0 + (long)ic * DK + j4);
+            const float on = i < DV ? 1.f : 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] += on * a[c] * b[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sRed[i0][j4 + c] = acc[c];
     }
     __syncthreads();
     if (KDA) {
@@ -542,7 +592,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     auto glast = [&](int j) { return KDA ? sgl[j] : sgl[0]; };
     if (tid < DK) {
         float s = 0.f;
-        for (int ig = 0; ig < NT / DK; ++ig) s += sRed[ig][tid];
+        for (int ig = 0; ig < RS; ++ig) s += sRed[ig][tid];
         sdgc[tid] = s * rec[R::D + tid];
     }
     for (int e = tid; e < C * DK; e += NT) {
