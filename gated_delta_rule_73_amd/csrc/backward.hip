@@ -148,6 +148,49 @@ __device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int lane_bytes,
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, lane_bytes, uniform_bytes, 0));
 }
 
+__device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, int lane_bytes, int uniform_bytes) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, uniform_bytes, 0));
+}
+
+// NQ tiles of A_q B_q^T products whose operands are both contiguous along k
+// (rows of A_q and rows of B_q^T): a lane reads four consecutive k of each as
+// one 16-byte access and spends them on four MFMA steps, lane group lq taking
+// k = kb + 4 lq + s in step s (the same on both sides, so the sum is the
+// same).  fa4(q, mi, kb, lk) = A_q(m0 + mi, kb + lk .. kb + lk + 3) and
+// fb4(q, ni, kb, lk) = B_q^T(n0 + ni, kb + lk .. kb + lk + 3); kb is
+// wave-uniform.  Blocks of 32 k, gathered one block ahead of their MFMAs.
+template <int KMAX, int NQ, class FA, class FB>
+__device__ __forceinline__ void tile_mma_nt(f32x4 (&acc)[NQ], int K, FA fa4, FB fb4) {
+    static_assert(KMAX % 32 == 0, "k blocks of 32");
+    constexpr int NB = KMAX / 32;
+    const int l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+    f32x4 a[2][NQ][2], b[2][NQ][2];
+    auto gather = [&](int blk, int buf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                a[buf][q][h] = fa4(q, lr, 32 * blk + 16 * h, 4 * lq);
+                b[buf][q][h] = fb4(q, lr, 32 * blk + 16 * h, 4 * lq);
+            }
+    };
+    gather(0, 0);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        if (32 * blk < K) {                     // K (a multiple of 32) is wave-uniform
+            if (blk + 1 < NB && 32 * (blk + 1) < K) gather(blk + 1, (blk + 1) & 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) acc[q] = mfma4(a[blk & 1][q][h][s], b[blk & 1][q][h][s], acc[q]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <typename IT> __device__ __forceinline__ float ld1(const IT *p) { return to_f32(*p); }
 
 // Where record chunk rc lies: its sequence, first token (flat index over
@@ -495,9 +538,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     static_assert(NW >= 8 && NW % 2 == 0, "the C x C phases deal tiles to waves 0-7");
     using R = BRec<DK>;
     // K e^g, then K e^{g-m}       | raw K, then K e^{m-g}      | g, then dg (per channel)
-    __shared__ float sX1[C][PK], sX2[C][PK], sGg[KDA ? C : 1][PK];
+    // (16-byte aligned: the A B^T products read four floats at a time)
+    __shared__ __align__(16) float sX1[C][PK], sX2[C][PK], sGg[KDA ? C : 1][PK];
     // V -> Y, then Q e^{g-m}      | U                          | dU -> dY      | scale dO
-    __shared__ float sB1[C][PB], sB2[C][PV], sB3[C][PV], sB4[C][PV];
+    __shared__ __align__(16) float sB1[C][PB], sB2[C][PV], sB3[C][PV], sB4[C][PV];
     __shared__ float sT[C][C + 1], sM[C][C + 1], sdT[C][C + 1], sdA[C][C + 1], sdM[C][C + 1], sE1[C][C + 1];
     __shared__ float sb[C], sg[C], sm[DK], sgl[DK], sdgc[DK], sdb[C];
     constexpr int Q4 = DK / 4, RS = NT / Q4;   // dS o S0 column sums: RS row groups of float4 columns
@@ -610,10 +654,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     // ---- Y = V - (K e^g) S0^T
     if (has_v) {
         f32x4 acc[2] = {zero4(), zero4()};
-        tile_mma_n<DK, 2>(acc, DK, [&](int, int mi, int kb, int lk) { return sX1[16 * rt_v + mi][kb + lk]; },
-                          [&](int q, int kb, int lk, int ni) {
-                              return bload(rS0, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
-                          });
+        tile_mma_nt<DK, 2>(acc, DK, [&](int, int mi, int kb, int lk) { return lds4(&sX1[16 * rt_v + mi][kb + lk]); },
+                           [&](int q, int ni, int kb, int lk) {
+                               return bload4(rS0, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
+                           });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sB1[16 * rt_v + 4 * lq + i][16 * it0 + lr] -= acc[0][i];
@@ -630,12 +674,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
                          });
         tile_mma_n<C, 2>(du, C, [&](int, int mi, int kb, int lk) { return sM[kb + lk][16 * rt_v + mi]; },
                          [&](int q, int kb, int lk, int ni) { return sB4[kb + lk][16 * (q ? it1 : it0) + ni]; });
-        tile_mma_n<DK, 2>(du, DK, [&](int, int mi, int kb, int lk) {
-                              return bload(rRec, (R::KE + (16 * rt_v + mi) * DK + lk) * 4, kb * 4);
-                          },
-                          [&](int q, int kb, int lk, int ni) {
-                              return bload(rdS, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
-                          });
+        tile_mma_nt<DK, 2>(du, DK, [&](int, int mi, int kb, int lk) {
+                               return bload4(rRec, (R::KE + (16 * rt_v + mi) * DK + lk) * 4, kb * 4);
+                           },
+                           [&](int q, int ni, int kb, int lk) {
+                               return bload4(rdS, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
+                           });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt_v + 4 * lq + i;
@@ -651,8 +695,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     // ---- dT = dU (diag(b) Y)^T;  Z = T^T dU (kept in registers);  d beta (value part)
     if (w < 4) {
         const int rt = w & 1, ct = w >> 1;
-        const f32x4 a = tile_mma<128>(zero4(), DV, [&](int mi, int kk) { return sB3[16 * rt + mi][kk]; },
-                                 [&](int kk, int ni) { return sb[16 * ct + ni] * sB1[16 * ct + ni][kk]; });
+        f32x4 t1[1] = {zero4()};
+        tile_mma_nt<128, 1>(t1, DV, [&](int, int mi, int kb, int lk) { return lds4(&sB3[16 * rt + mi][kb + lk]); },
+                            [&](int, int ni, int kb, int lk) { return sb[16 * ct + ni] * lds4(&sB1[16 * ct + ni][kb + lk]); });
+        const f32x4 a = t1[0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sdT[16 * rt + 4 * lq + i][16 * ct + lr] = a[i];
     }
@@ -723,8 +769,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         const int rt = w & 1, ct = w >> 1;
         const f32x4 a = tile_mma<C>(zero4(), C, [&](int mi, int kk) { return sT[kk][16 * rt + mi]; },
                                  [&](int kk, int ni) { return sE1[kk][16 * ct + ni]; });
-        const f32x4 gm = tile_mma<DK>(zero4(), DK, [&](int mi, int kk) { return sX1[16 * rt + mi][kk]; },
-                                  [&](int kk, int ni) { return sX2[16 * ct + ni][kk]; });
+        f32x4 g1[1] = {zero4()};
+        tile_mma_nt<DK, 1>(g1, DK, [&](int, int mi, int kb, int lk) { return lds4(&sX1[16 * rt + mi][kb + lk]); },
+                           [&](int, int ni, int kb, int lk) { return lds4(&sX2[16 * ct + ni][kb + lk]); });
+        const f32x4 gm = g1[0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lq + i, c = 16 * ct + lr;
@@ -737,8 +785,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         }
     } else if (w < 8) {
         const int rt = (w - 4) & 1, ct = (w - 4) >> 1;
-        const f32x4 a = tile_mma<128>(zero4(), DV, [&](int mi, int kk) { return sB4[16 * rt + mi][kk]; },
-                                 [&](int kk, int ni) { return sB2[16 * ct + ni][kk]; });
+        f32x4 m1[1] = {zero4()};
+        tile_mma_nt<128, 1>(m1, DV, [&](int, int mi, int kb, int lk) { return lds4(&sB4[16 * rt + mi][kb + lk]); },
+                            [&](int, int ni, int kb, int lk) { return lds4(&sB2[16 * ct + ni][kb + lk]); });
+        const f32x4 a = m1[0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lq + i, c = 16 * ct + lr;
