@@ -379,16 +379,36 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
 // double-buffered LDS stage: one barrier per chunk.  The workgroups of one
 // (sequence, head) sit on one XCD (block b runs on XCD b mod 8), so its
 // records come from HBM once and from that XCD's L2 for the other slices.
+// LDS of one scan workgroup.  Every operand is read as four consecutive k
+// per lane (one 16-byte LDS read for four MFMA steps): E as stored ([r][j]),
+// the state-update operands B and G transposed ([j][r]), Z transposed
+// ([value row][r]); two stages.
+template <int DK, int NW> struct ScanLds {
+    static constexpr int C = kBC, PK = DK + 4, PC = C + 4, ZW = 16 * NW;
+    __align__(16) float E[2][C][PK];
+    __align__(16) float Bt[2][DK][PC];
+    __align__(16) float Gt[2][DK][PC];
+    __align__(16) float L[2][C][PC];
+    __align__(16) float Zt[2][ZW][PC];
+    __align__(16) float D[2][DK];
+    __align__(16) float S[2][C];
+};
+
 template <int DK, int NW, bool BWD, typename IT>
-__global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p) {
-    constexpr int C = kBC, PK = DK + 4, NT = 64 * NW, ZW = 16 * NW, ZP = ZW + 1, NGR = BWD ? C : 1;
-    constexpr int NE = C * DK / 4 / NT, NL = C * C / NT, NZ = C * ZW / NT;
+__device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<DK, NW> &lds) {
+    constexpr int C = kBC, NT = 64 * NW, ZW = 16 * NW;
+    constexpr int NE = C * DK / 4 / NT, NL = C * C / NT, NZ = C * ZW / 4 / NT;
     static_assert(NE >= 1 && NL >= 1 && NZ >= 1, "scan tiling");
     using R = BRec<DK>;
-    __shared__ float sE[2][C][PK], sB[2][C][PK], sG[2][NGR][PK];
-    __shared__ float sL[2][C][C + 1], sZ[2][C][ZP], sD[2][DK], sS[2][C];
+    auto &sE = lds.E;
+    auto &sBt = lds.Bt;
+    auto &sGt = lds.Gt;
+    auto &sL = lds.L;
+    auto &sZt = lds.Zt;
+    auto &sD = lds.D;
+    auto &sS = lds.S;
     const int H = p.H, DV = p.dv, S = DV / ZW;
-    const int xcd = blockIdx.x & 7, kb = blockIdx.x >> 3;
+    const int xcd = block & 7, kb = block >> 3;
     const int unit = xcd + 8 * (kb / S), slice = kb % S;
     if (unit >= p.num_seqs * H) return;
     const int n = p.cu ? p.order[unit / H] : unit / H, h = unit % H;
@@ -405,21 +425,28 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p) {
     const int row = ZW * slice + 16 * w + lr;     // this lane's value row (as MFMA column)
     const IT *v = static_cast<const IT *>(p.v);
 
-    f32x4 rE[NE], rB[NE], rG[BWD ? NE : 1];
-    float rL[NL], rZ[NZ], rD = 0.f, rS = 0.f;
+    f32x4 rE[NE], rB[NE], rG[BWD ? NE : 1], rZ[NZ];
+    float rL[NL], rD = 0.f, rS = 0.f;
+    // rE[u]: E[r][j .. j + 3] (row-major, as stored); rB[u], rG[u]: B[r .. r + 3][j]
+    // and G[r .. r + 3][j] (four rows of one column: written as one 16-byte
+    // row piece of the transposed copy); rZ[u]: Z[r .. r + 3][i] likewise.
     auto fetch = [&](int s) {
         const int c = BWD ? nc - 1 - s : s;
         const long rc = rc0 + c, tok0 = tok_base + (long)c * C;
         const int clen = min(C, len - c * C);
         const float *rec = p.rec + (rc * H + h) * p.rec_stride;
+        const float *eb = rec + (BWD ? R::KE : R::W), *bb = rec + (BWD ? R::W : R::KE);
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
-            const int e = tid + NT * u, r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-            const f32x4 we = *reinterpret_cast<const f32x4 *>(rec + R::W + r * DK + j);
-            const f32x4 ke = *reinterpret_cast<const f32x4 *>(rec + R::KE + r * DK + j);
-            rE[u] = BWD ? ke : we;
-            rB[u] = BWD ? we : ke;
-            if (BWD) rG[u] = *reinterpret_cast<const f32x4 *>(rec + R::Q + r * DK + j);
+            const int e = tid + NT * u;
+            const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;      // E: row r, columns j..j+3
+            rE[u] = *reinterpret_cast<const f32x4 *>(eb + r * DK + j);
+            const int jc = e % DK, r4 = (e / DK) * 4;                 // B, G: column jc, rows r4..r4+3
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                rB[u][t] = bb[(r4 + t) * DK + jc];
+                if (BWD) rG[u][t] = rec[R::Q + (r4 + t) * DK + jc];
+            }
         }
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
@@ -431,26 +458,29 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p) {
         // every load in flight, the record loads above included
 #pragma unroll
         for (int u = 0; u < NZ; ++u) {
-            const int e = tid + NT * u, r = e / ZW, i = e % ZW;
-            const long o = ((tok0 + min(r, clen - 1)) * H + h) * DV + ZW * slice + i;
-            const float z = BWD ? p.scale * p.d_out[o] : ld1(v + o);
-            rZ[u] = r < clen ? z : 0.f;
+            const int e = tid + NT * u, i = e % ZW, r4 = (e / ZW) * 4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = r4 + t;
+                const long o = ((tok0 + min(r, clen - 1)) * H + h) * DV + ZW * slice + i;
+                const float z = BWD ? p.scale * p.d_out[o] : ld1(v + o);
+                rZ[u][t] = r < clen ? z : 0.f;
+            }
         }
         rD = rec[R::D + (tid & (DK - 1))];
         const int tr = tid & (C - 1);
-        const float bb = p.beta[(tok0 + min(tr, clen - 1)) * H + h];
-        rS = BWD ? 1.f : (tr < clen ? bb : 0.f);
+        const float bb1 = p.beta[(tok0 + min(tr, clen - 1)) * H + h];
+        rS = BWD ? 1.f : (tr < clen ? bb1 : 0.f);
     };
     auto put = [&](int b) {
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
-            const int e = tid + NT * u, r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sE[b][r][j + i] = rE[u][i];
-                sB[b][r][j + i] = rB[u][i];
-                if (BWD) sG[b][r][j + i] = rG[u][i];
-            }
+            const int e = tid + NT * u;
+            const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
+            *reinterpret_cast<f32x4 *>(&sE[b][r][j]) = rE[u];
+            const int jc = e % DK, r4 = (e / DK) * 4;
+            *reinterpret_cast<f32x4 *>(&sBt[b][jc][r4]) = rB[u];
+            if (BWD) *reinterpret_cast<f32x4 *>(&sGt[b][jc][r4]) = rG[u];
         }
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
@@ -460,7 +490,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p) {
 #pragma unroll
         for (int u = 0; u < NZ; ++u) {
             const int e = tid + NT * u;
-            sZ[b][e / ZW][e % ZW] = rZ[u];
+            *reinterpret_cast<f32x4 *>(&sZt[b][e % ZW][(e / ZW) * 4]) = rZ[u];
         }
         if (tid < DK) sD[b][tid] = rD;
         if (tid < C) sS[b][tid] = rS;
@@ -488,32 +518,47 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p) {
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt) *reinterpret_cast<f32x4 *>(dump + 16 * jt + 4 * lq) = x[jt];
 
+        // lane group lq takes k = 16 h + 4 lq + i in MFMA step (h, i) of the
+        // 32-deep products, k = 16 jt + 4 lq + i in those over d_k
+        const f32x4 zt[2] = {lds4(&sZt[b][16 * w + lr][4 * lq]), lds4(&sZt[b][16 * w + lr][16 + 4 * lq])};
         f32x4 pc[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int k0 = 0; k0 < C; k0 += 4)
-                acc = mfma4(sL[b][16 * rt + lr][k0 + lq], sS[b][k0 + lq] * sZ[b][k0 + lq][16 * w + lr], acc);
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 lv = lds4(&sL[b][16 * rt + lr][16 * h + 4 * lq]);
+                const f32x4 sv = lds4(&sS[b][16 * h + 4 * lq]);
 #pragma unroll
-            for (int jt = 0; jt < DK / 16; ++jt)
+                for (int i = 0; i < 4; ++i) acc = mfma4(lv[i], sv[i] * zt[h][i], acc);
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma4(sE[b][16 * rt + lr][16 * jt + 4 * lq + i], x[jt][i], acc);
+            for (int jt = 0; jt < DK / 16; ++jt) {
+                const f32x4 ev = lds4(&sE[b][16 * rt + lr][16 * jt + 4 * lq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mfma4(ev[i], x[jt][i], acc);
+            }
             pc[rt] = acc;
         }
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt) {
             f32x4 acc = x[jt];
+            const f32x4 dv4 = lds4(&sD[b][16 * jt + 4 * lq]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= sD[b][16 * jt + 4 * lq + i];
+            for (int i = 0; i < 4; ++i) acc[i] *= dv4[i];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt) {
+                const f32x4 bv = lds4(&sBt[b][16 * jt + lr][16 * rt + 4 * lq]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma4(sB[b][16 * rt + 4 * lq + i][16 * jt + lr], pc[rt][i], acc);
+                for (int i = 0; i < 4; ++i) acc = mfma4(bv[i], pc[rt][i], acc);
+            }
             if (BWD) {
 #pragma unroll
-                for (int k0 = 0; k0 < C; k0 += 4)
-                    acc = mfma4(sG[b][k0 + lq][16 * jt + lr], sZ[b][k0 + lq][16 * w + lr], acc);
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4 gv = lds4(&sGt[b][16 * jt + lr][16 * h + 4 * lq]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = mfma4(gv[i], zt[h][i], acc);
+                }
             }
             x[jt] = acc;
         }
@@ -525,6 +570,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p) {
         for (int jt = 0; jt < DK / 16; ++jt)
             *reinterpret_cast<f32x4 *>(p.d_init + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq) = x[jt];
     }
+}
+
+// Both state passes in one launch: the first half of the grid walks the
+// states forward, the second half the state gradients backward.  The two
+// recurrences are independent, so each half fills the CUs the other leaves.
+template <int DK, int NW, typename IT>
+__global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half) {
+    __shared__ ScanLds<DK, NW> lds;
+    if ((int)blockIdx.x < half)
+        scan_body<DK, NW, false, IT>(p, blockIdx.x, lds);
+    else
+        scan_body<DK, NW, true, IT>(p, blockIdx.x - half, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -898,21 +955,16 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStr
         hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    // four waves (64 value rows) per scan workgroup when that still gives a
-    // workgroup to at least half the CUs, else two
+    // four waves (64 value rows) per scan workgroup when the two passes still
+    // give a workgroup to every CU, else two
     const long units = (long)a.num_seqs * a.num_heads;
     const bool four = a.dv % 64 == 0 && units * (a.dv / 64) >= 128;
     const long per_unit = a.dv / (four ? 64 : 32);
     const unsigned scan_blocks = (unsigned)(8 * ((units + 7) / 8) * per_unit);
-    if (four) {
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, false, IT>), dim3(scan_blocks), dim3(256), 0, st, kp);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, true, IT>), dim3(scan_blocks), dim3(256), 0, st, kp);
-    } else {
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, false, IT>), dim3(scan_blocks), dim3(128), 0, st, kp);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, true, IT>), dim3(scan_blocks), dim3(128), 0, st, kp);
-    }
+    if (four)
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, IT>), dim3(2 * scan_blocks), dim3(256), 0, st, kp, (int)scan_blocks);
+    else
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, IT>), dim3(2 * scan_blocks), dim3(128), 0, st, kp, (int)scan_blocks);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (nrc > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(kGradThreads), 0, st, kp);
