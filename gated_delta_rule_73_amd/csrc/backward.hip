@@ -232,7 +232,7 @@ template <int DK, bool KDA, typename IT>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
     constexpr int C = kBC, PK = DK + 4, NT = 256;
     using R = BRec<DK>;
-    __shared__ float sK[C][PK], sQ[C][PK], sX[C][PK], sKh[C][PK];
+    __shared__ __align__(16) float sK[C][PK], sQ[C][PK], sX[C][PK], sKh[C][PK];
     __shared__ float sA[C][C + 1], sT[C][C + 1];
     __shared__ float sg[C], sb[C], sm[DK], sgl[DK];
     const int H = p.H, h = blockIdx.y, tid = threadIdx.x;
@@ -296,13 +296,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
     const int w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
     {   // A = strict_tril(diag(b) Kts Khs^T), M = tril(Qts Khs^T): one tile each per wave
         const int rt = w & 1, ct = w >> 1;
-        f32x4 a = zero4(), mm = zero4();
-#pragma unroll 4
-        for (int k0 = 0; k0 < DK; k0 += 4) {
-            const float kh = sKh[16 * ct + lr][k0 + lq];
-            a = mfma4(sK[16 * rt + lr][k0 + lq], kh, a);
-            mm = mfma4(sQ[16 * rt + lr][k0 + lq], kh, mm);
-        }
+        f32x4 am[2] = {zero4(), zero4()};
+        tile_mma_nt<DK, 2>(am, DK, [&](int q, int mi, int kb, int lk) {
+                               return lds4(q ? &sQ[16 * rt + mi][kb + lk] : &sK[16 * rt + mi][kb + lk]);
+                           },
+                           [&](int, int ni, int kb, int lk) { return lds4(&sKh[16 * ct + ni][kb + lk]); });
+        const f32x4 a = am[0], mm = am[1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lq + i, c = 16 * ct + lr;
@@ -619,59 +618,83 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     const __amdgpu_buffer_rsrc_t rRec = buffer_of(rec, p.rec_stride);
     const int ntv = 2 * (DV / 16), ntk = 2 * (DK / 16);
 
-    // ---- loads
-    for (int e = tid; e < C * DK / 4; e += NT) {
-        const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        const bool in = r < L.len;
+    // ---- loads: every load of the chunk is issued first (all in flight
+    //      together, from clamped rows), then the LDS stores and the column
+    //      sums of dS o S0 (the decay's share of the outgoing gradient) consume them
+    constexpr int NKL = div_up(C * DK / 4, NT), NVL = div_up(C * 128 / 4, NT), NTL = C * C / NT, NCS = div_up(128, RS);
+    static_assert(NTL >= 1 && C * C % NT == 0, "load tiling");
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 kv[NKL], gv[NKL], vv[NVL], dd[NVL];
+    float tv[NTL], mv[NTL];
+    f32x4 ca[NCS], cb[NCS];
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+        const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
         const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j;
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 kv = in ? load4(k + o) : z4;
-        const float4 gv = KDA && in ? *reinterpret_cast<const float4 *>(p.log_alpha + o) : z4;
-        sX2[r][j] = kv.x, sX2[r][j + 1] = kv.y, sX2[r][j + 2] = kv.z, sX2[r][j + 3] = kv.w;
-        if (KDA) sGg[r][j] = gv.x, sGg[r][j + 1] = gv.y, sGg[r][j + 2] = gv.z, sGg[r][j + 3] = gv.w;
+        kv[u] = load4(k + o);
+        gv[u] = KDA ? *reinterpret_cast<const float4 *>(p.log_alpha + o) : z4;
     }
 #pragma unroll
-    for (int u = 0; u < div_up(C * 128 / 4, NT); ++u) {     // fixed trip count, clamped index
-        const int e = tid + NT * u, ec = min(e, C * DV / 4 - 1);
-        const int r = ec / (DV / 4), i = (ec % (DV / 4)) * 4;
-        const bool in = r < L.len;
+    for (int u = 0; u < NVL; ++u) {
+        const int e = min(tid + NT * u, C * DV / 4 - 1), r = e / (DV / 4), i = (e % (DV / 4)) * 4;
         const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DV + i;
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 vv = in ? load4(v + o) : z4, dd = in ? *reinterpret_cast<const float4 *>(p.d_out + o) : z4;
-        if (e >= C * DV / 4) continue;
-        sB1[r][i] = vv.x, sB1[r][i + 1] = vv.y, sB1[r][i + 2] = vv.z, sB1[r][i + 3] = vv.w;
-        sB4[r][i] = p.scale * dd.x, sB4[r][i + 1] = p.scale * dd.y;
-        sB4[r][i + 2] = p.scale * dd.z, sB4[r][i + 3] = p.scale * dd.w;
+        vv[u] = load4(v + o);
+        dd[u] = *reinterpret_cast<const float4 *>(p.d_out + o);
     }
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e / C, c = e % C;
-        sT[r][c] = rec[R::T + e];
-        sM[r][c] = rec[R::M + e];
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+        tv[u] = rec[R::T + tid + NT * u];
+        mv[u] = rec[R::M + tid + NT * u];
+    }
+    const int j4c = (tid % Q4) * 4, i0c = tid / Q4;
+#pragma unroll
+    for (int u = 0; u < NCS; ++u) {
+        const int ic = min(i0c + RS * u, DV - 1);
+        ca[u] = *reinterpret_cast<const f32x4 *>(dS + (long)ic * DK + j4c);
+        cb[u] = *reinterpret_cast<const f32x4 *>(S0 + (long)ic * DK + j4c);
+    }
+    const long obg = (L.tok0 + min(tid & (C - 1), L.len - 1)) * H + h;
+    const float bb = p.beta[obg], gg = KDA ? 0.f : p.log_alpha[obg];
+
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+        const int e = tid + NT * u;
+        if (e >= C * DK / 4) continue;
+        const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
+        const float4 kk4 = r < L.len ? kv[u] : z4, gg4 = r < L.len ? gv[u] : z4;
+        sX2[r][j] = kk4.x, sX2[r][j + 1] = kk4.y, sX2[r][j + 2] = kk4.z, sX2[r][j + 3] = kk4.w;
+        if (KDA) sGg[r][j] = gg4.x, sGg[r][j + 1] = gg4.y, sGg[r][j + 2] = gg4.z, sGg[r][j + 3] = gg4.w;
+    }
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+        const int e = tid + NT * u;
+        if (e >= C * DV / 4) continue;
+        const int r = e / (DV / 4), i = (e % (DV / 4)) * 4;
+        const float4 v4 = r < L.len ? vv[u] : z4, d4 = r < L.len ? dd[u] : z4;
+        sB1[r][i] = v4.x, sB1[r][i + 1] = v4.y, sB1[r][i + 2] = v4.z, sB1[r][i + 3] = v4.w;
+        sB4[r][i] = p.scale * d4.x, sB4[r][i + 1] = p.scale * d4.y;
+        sB4[r][i + 2] = p.scale * d4.z, sB4[r][i + 3] = p.scale * d4.w;
+    }
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+        const int e = tid + NT * u;
+        sT[e / C][e % C] = tv[u];
+        sM[e / C][e % C] = mv[u];
     }
     if (tid < C) {
-        const bool in = tid < L.len;
-        const long o = (L.tok0 + min(tid, L.len - 1)) * H + h;
-        const float bb = p.beta[o], gg = KDA ? 0.f : p.log_alpha[o];
-        sb[tid] = in ? bb : 0.f;
-        if (!KDA) sg[tid] = in ? gg : 0.f;
+        sb[tid] = tid < L.len ? bb : 0.f;
+        if (!KDA) sg[tid] = tid < L.len ? gg : 0.f;
     }
-    {   // column partials of dS o S0 (the decay's share of the outgoing gradient): thread tid
-        // sums the four columns 4 (tid % Q4).. over rows tid / Q4 + RS u.  The loop is
-        // unrolled to its compile-time bound with clamped rows, so all its loads (the first
-        // touch of this chunk's two states) are in flight together.
-        const int j4 = (tid % Q4) * 4, i0 = tid / Q4;
+    {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int u = 0; u < div_up(128, RS); ++u) {
-            const int i = i0 + RS * u, ic = min(i, DV - 1);
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(dS + (long)ic * DK + j4);
-            const f32x4 b = *reinterpret_cast<const f32x4 *>(S0 + (long)ic * DK + j4);
-            const float on = i < DV ? 1.f : 0.f;
+        for (int u = 0; u < NCS; ++u) {
+            const float on = i0c + RS * u < DV ? 1.f : 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] += on * a[c] * b[c];
+            for (int c = 0; c < 4; ++c) acc[c] += on * ca[u][c] * cb[u][c];
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) sRed[i0][j4 + c] = acc[c];
+        for (int c = 0; c < 4; ++c) sRed[i0c][j4c + c] = acc[c];
     }
     __syncthreads();
     if (KDA) {
