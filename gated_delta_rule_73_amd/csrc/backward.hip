@@ -885,14 +885,20 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         const int rt = t & 1, jt = t >> 1;
         const int j = 16 * jt + lr;
         // the three products with the states (dO' S0, dY S0, U dS: S0 read once)
+        // (A rows contiguous along k: one 16-byte LDS read per four steps; the
+        // states' rows run along j, so their four k come from four loads)
         f32x4 st[3] = {zero4(), zero4(), zero4()};
-        tile_mma_n<128, 3>(st, DV, [&](int q, int mi, int kb, int lk) {
-                               const int kk = kb + lk;
-                               return q == 0 ? sB4[16 * rt + mi][kk] : q == 1 ? sB3[16 * rt + mi][kk] : sB2[16 * rt + mi][kk];
-                           },
-                           [&](int q, int kb, int lk, int ni) {
-                               return bload(q < 2 ? rS0 : rdS, (lk * DK + 16 * jt + ni) * 4, kb * DK * 4);
-                           });
+        tile_mma_nt<128, 3>(st, DV, [&](int q, int mi, int kb, int lk) {
+                                return lds4(q == 0 ? &sB4[16 * rt + mi][kb + lk]
+                                          : q == 1 ? &sB3[16 * rt + mi][kb + lk] : &sB2[16 * rt + mi][kb + lk]);
+                            },
+                            [&](int q, int ni, int kb, int lk) {
+                                f32x4 v;
+#pragma unroll
+                                for (int t = 0; t < 4; ++t)
+                                    v[t] = bload(q < 2 ? rS0 : rdS, (lk * DK + 16 * jt + ni) * 4, (kb + t) * DK * 4);
+                                return v;
+                            });
         // the chunk-local ones: dM Khs, dA Khs, dM^T Qts + dA^T Kts
         f32x4 gm[4] = {zero4(), zero4(), zero4(), zero4()};
         tile_mma_n<C, 4>(gm, C, [&](int q, int mi, int kb, int lk) {
