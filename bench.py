@@ -73,15 +73,17 @@ def prefill_alg_flops(B, T, H, dk, dv, C):
     return B * T * H * (4 * C * (dk + dv) + 6 * dk * dv)
 
 
-def backward_alg_bytes(B, T, H, dk, dv, kda, N, qkv_bytes=2, init_state=True):
+def backward_alg_bytes(B, T, H, dk, dv, kda, N, qkv_bytes=2, init_state=True, Hk=None):
     """Bytes the backward must move once: q, k, v, beta, log alpha and d_out
     in; dq, dk, dv, dbeta, dlog alpha out (fp32); the initial state and the
-    final-state gradient in, the initial-state gradient out."""
+    final-state gradient in, the initial-state gradient out.  q, k and their
+    gradients come once per q/k head (Hk of them)."""
+    Hk = H if Hk is None else Hk
     gate = 4 * dk if kda else 4
-    per = qkv_bytes * (2 * dk + dv) + 4 + gate + 4 * dv          # inputs and d_out
-    per += 4 * (2 * dk + dv) + 4 + gate                            # gradients
+    per_v = qkv_bytes * dv + 4 + gate + 4 * dv + 4 * dv + 4 + gate   # v, gates, d_out; dv, dbeta, dlog alpha
+    per_qk = (qkv_bytes + 4) * 2 * dk                                 # q, k; dq, dk
     states = N * H * dv * dk * 4 * (3 if init_state else 2)
-    return B * T * H * per + states
+    return B * T * (H * per_v + Hk * per_qk) + states
 
 
 def backward_alg_flops(B, T, H, dk, dv, C=32):
@@ -335,26 +337,27 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     from workloads import backward_cotangents
 
     res["prefill_backward"] = {}
-    for name in ("kda_backward_32k", "gdn_backward_8k"):
+    for name in ("kda_backward_32k", "gdn_backward_8k", "gdn_gva_backward_32k"):
         wb = WORKLOADS[name]
         print(f"[bench] {wb.name}", file=sys.stderr, flush=True)
         bi = prefill_inputs(wb, dev)
         bc = backward_cotangents(bi, wb.seed, dev)
-        B, T, H, dk = bi["q"].shape
-        dv = bi["v"].shape[-1]
+        B, T, Hk, dk = bi["q"].shape
+        H, dv = bi["v"].shape[2:]
         kda = bi["log_alpha"].dim() == 4
         f = lambda: gdr.gdr_prefill_backward(bi["q"], bi["k"], bi["v"], bi["beta"], bi["log_alpha"], bc["d_out"],
                                              initial_state=bi["initial_state"], d_final_state=bc["d_final_state"])
         for _ in range(args.warmup):
             f()
-        steps = max(1, min(args.steps, 5)) if kda else args.steps
+        steps = max(1, min(args.steps, 5)) if T * B >= 32768 else args.steps
         t, med, mn = time_calls(f, steps)
-        by = backward_alg_bytes(B, T, H, dk, dv, kda, B)
+        by = backward_alg_bytes(B, T, H, dk, dv, kda, B, Hk=Hk)
         fl = backward_alg_flops(B, T, H, dk, dv)
         res["prefill_backward"][name] = {
             "workload": f"{name}: gradients of q, k, v, beta, log alpha and the initial state through the chunked "
-                        f"prefill, B={B}, T={T}, H={H}, d={dk}, bf16 q/k/v, fp32 gates, d_out and d_final_state "
-                        f"~ N(0, 1), {'per-channel' if kda else 'per-head'} decay, S0 given; fp32 arithmetic",
+                        f"prefill, B={B}, T={T}, H={H}" + (f" value heads sharing {Hk} q/k heads" if Hk != H else "")
+                        + f", d={dk}, bf16 q/k/v, fp32 gates, d_out and d_final_state ~ N(0, 1), "
+                        f"{'per-channel' if kda else 'per-head'} decay, S0 given; fp32 arithmetic",
             "calls": steps, "us_per_call": round(t * 1e6, 1), "us_median": round(med * 1e6, 1),
             "us_min": round(mn * 1e6, 1), "Mtok_s": round(B * T / t / 1e6, 3), "alg_bytes": by,
             "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),

@@ -186,8 +186,8 @@ def gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None,
                          cu_seqlens=None, scale: float = 1.0, output_d_initial_state: bool = True,
                          workspace=None):
     """Gradients through :func:`gdr_prefill_chunked` (same q, k, v, beta,
-    log_alpha, initial_state, cu_seqlens and scale; one q/k head per value
-    head; fp32 gates).  d_out [B, T, H, dv] fp32; d_final_state
+    log_alpha, initial_state, cu_seqlens and scale, grouped q/k heads
+    included; fp32 gates).  d_out [B, T, H, dv] fp32; d_final_state
     [N, H, dv, dk] fp32 or None (zeros).
     Returns a dict of fp32 tensors: dq, dk (q's shape), dv (v's), dbeta,
     dlog_alpha (log_alpha's shape) and d_initial_state [N, H, dv, dk] (None
@@ -197,7 +197,7 @@ def gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None,
     B, T, Hk, dk = q.shape
     H, dv = v.shape[2], v.shape[3]
     if k.shape != q.shape or v.shape[:2] != (B, T) or beta.shape != (B, T, H):
-        raise ValueError("shapes: q, k [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+        raise ValueError("shapes: q, k [B, T, Hk, dk], v [B, T, H, dv], beta [B, T, H]")
     if log_alpha.dim() == 3:
         gate = GDR_GATE_HEAD
     elif log_alpha.dim() == 4:

@@ -57,13 +57,14 @@ template <int DK> struct BRec {
 
 struct BwdKArgs {
     int batch, seqlen, H, dv, num_seqs;
+    int Hk, G;                                // q/k heads; value heads per q/k head (H = Hk G)
     const void *q, *k, *v;
     const float *beta, *log_alpha;
     const float *initial_state;
     const int32_t *cu, *order, *choff;
     float scale;
     const float *d_out, *d_final;
-    float *dq, *dk, *dv_out, *dbeta, *dla, *d_init;
+    float *dq, *dk, *dv_out, *dbeta, *dla, *d_init;   // dq, dk: per value head ([.., H, dk])
     float *rec, *states, *dstates;
     long rec_stride;                          // floats per record
 };
@@ -245,9 +246,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
     for (int e = tid; e < C * DK / 4; e += NT) {
         const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
         const bool in = r < L.len;                 // padding rows: zeros (clamped loads, no branch)
-        const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j;
+        const long t = L.tok0 + min(r, L.len - 1);
+        const long o = (t * H + h) * DK + j, oq = (t * p.Hk + h / p.G) * DK + j;
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 kv = in ? load4(k + o) : z4, qv = in ? load4(q + o) : z4;
+        const float4 kv = in ? load4(k + oq) : z4, qv = in ? load4(q + oq) : z4;
         const float4 gv = KDA && in ? *reinterpret_cast<const float4 *>(p.log_alpha + o) : z4;
         sK[r][j] = kv.x, sK[r][j + 1] = kv.y, sK[r][j + 2] = kv.z, sK[r][j + 3] = kv.w;
         sQ[r][j] = qv.x, sQ[r][j + 1] = qv.y, sQ[r][j + 2] = qv.z, sQ[r][j + 3] = qv.w;
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     const long rc = blockIdx.x;
     const ChunkLoc L = locate(p, rc);
     if (L.len <= 0) return;
-    const int w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
+    const int w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4, hq = h / p.G;
     const IT *q = static_cast<const IT *>(p.q), *k = static_cast<const IT *>(p.k), *v = static_cast<const IT *>(p.v);
     const float *rec = p.rec + (rc * H + h) * p.rec_stride;
     const float *S0 = p.states + (rc * H + h) * (long)DV * DK;
@@ -630,9 +632,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
         const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j;
-        kv[u] = load4(k + o);
-        gv[u] = KDA ? *reinterpret_cast<const float4 *>(p.log_alpha + o) : z4;
+        const long t = L.tok0 + min(r, L.len - 1);
+        kv[u] = load4(k + (t * p.Hk + hq) * DK + j);
+        gv[u] = KDA ? *reinterpret_cast<const float4 *>(p.log_alpha + (t * H + h) * DK + j) : z4;
     }
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
@@ -831,7 +833,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     }
     for (int e = tid; e < C * DK / 4; e += NT) {
         const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        const float4 qv = r < L.len ? load4(q + ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j)
+        const float4 qv = r < L.len ? load4(q + ((L.tok0 + min(r, L.len - 1)) * p.Hk + hq) * DK + j)
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
         sB1[r][j] = qv.x * expf(gval(r, j) - mval(j));
         sB1[r][j + 1] = qv.y * expf(gval(r, j + 1) - mval(j + 1));
@@ -925,8 +927,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
             const float gk1 = -dy0[i] * eg + dak[i] * egm;
             const float gk2 = tq[i] * emg;
             const float gk3 = uds[i] * egc;
-            const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DK + j;
-            const float kk = r < L.len ? ld1(k + o) : 0.f, qq = r < L.len ? ld1(q + o) : 0.f;
+            const long t = L.tok0 + min(r, L.len - 1), o = (t * H + h) * DK + j;
+            const long oq = (t * p.Hk + hq) * DK + j;
+            const float kk = r < L.len ? ld1(k + oq) : 0.f, qq = r < L.len ? ld1(q + oq) : 0.f;
             if (r < L.len) {
                 p.dq[o] = dQ;
                 p.dk[o] = gk1 + gk2 + gk3;
@@ -977,6 +980,25 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped q/k heads: the gradient of a q/k head is the sum of those of the G
+// value heads that read it (value head h reads q/k head h / G).
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *__restrict__ dqv,
+                                                            const float *__restrict__ dkv, float *__restrict__ dq,
+                                                            float *__restrict__ dk, long n4, int G, int dk4) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;   // one float4 of [tokens, Hk, dk]
+    if (e >= n4) return;
+    const long row = e / dk4, c = e % dk4;                  // row = token * Hk + hk
+    f32x4 sq = zero4(), sk = zero4();
+    for (int g = 0; g < G; ++g) {
+        const long src = (row * G + g) * dk4 + c;
+        const f32x4 a = reinterpret_cast<const f32x4 *>(dqv)[src], b = reinterpret_cast<const f32x4 *>(dkv)[src];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sq[i] += a[i], sk[i] += b[i];
+    }
+    reinterpret_cast<f32x4 *>(dq)[e] = sq;
+    reinterpret_cast<f32x4 *>(dk)[e] = sk;
+}
+
 template <int DK, bool KDA, typename IT>
 static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStream_t st) {
     const long nrc = a.record_chunks;
@@ -998,6 +1020,12 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStr
     if (nrc > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(kGradThreads), 0, st, kp);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        if (kp.G > 1) {
+            const long n4 = (long)a.batch * a.seqlen * kp.Hk * (DK / 4);
+            hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, kp.dq, kp.dk,
+                               a.dq, a.dk_out, n4, kp.G, DK / 4);
+            if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        }
     }
     return hipSuccess;
 }
@@ -1024,7 +1052,12 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     kp.initial_state = a.initial_state;
     kp.cu = a.cu_seqlens, kp.order = a.order, kp.choff = a.chunk_offset;
     kp.scale = a.scale, kp.d_out = a.d_out, kp.d_final = a.d_final_state;
-    kp.dq = a.dq, kp.dk = a.dk_out, kp.dv_out = a.dv_out, kp.dbeta = a.dbeta, kp.dla = a.dlog_alpha;
+    kp.Hk = a.num_qk_heads, kp.G = a.num_heads / a.num_qk_heads;
+    // per-value-head q/k gradients go straight to dq, dk, or (grouped heads)
+    // to the workspace, summed over each group afterwards
+    kp.dq = kp.G > 1 ? a.dq_heads : a.dq;
+    kp.dk = kp.G > 1 ? a.dk_heads : a.dk_out;
+    kp.dv_out = a.dv_out, kp.dbeta = a.dbeta, kp.dla = a.dlog_alpha;
     kp.d_init = a.d_initial_state;
     kp.rec = a.records, kp.states = a.states, kp.dstates = a.dstates;
     kp.rec_stride = (long)(backward_record_bytes(a.dk) / sizeof(float));

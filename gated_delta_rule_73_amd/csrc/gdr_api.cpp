@@ -203,7 +203,7 @@ gdr_status check_decode(int32_t num_seqs, int32_t K, int32_t num_heads, int32_t 
 // state gradients.  Packed batches size the chunk slots by the bound
 // ceil(seqlen / C) + num_seqs, since the lengths live on the device.
 struct BackwardWorkspace {
-    size_t order_off = 0, choff_off = 0, rec_off = 0, st_off = 0, dst_off = 0, total = 0;
+    size_t order_off = 0, choff_off = 0, rec_off = 0, st_off = 0, dst_off = 0, dqh_off = 0, dkh_off = 0, total = 0;
     long record_chunks = 0;
 };
 
@@ -224,6 +224,14 @@ BackwardWorkspace backward_workspace(const gdr_prefill_shape &s, bool packed) {
     off += round256(slots * (size_t)s.head_dim_k * s.head_dim_v * sizeof(float));
     w.dst_off = off;
     off += round256(slots * (size_t)s.head_dim_k * s.head_dim_v * sizeof(float));
+    // grouped q/k heads: per-value-head dq and dk before the sum over each group
+    const int hk = s.num_qk_heads > 0 ? s.num_qk_heads : s.num_heads;
+    if (hk != s.num_heads) {
+        const size_t per = round256((size_t)s.batch * s.seqlen * s.num_heads * s.head_dim_k * sizeof(float));
+        w.dqh_off = off;
+        w.dkh_off = off + per;
+        off += 2 * per;
+    }
     w.total = off;
     return w;
 }
@@ -255,9 +263,6 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
                     s.num_heads, s.head_dim_k, s.head_dim_v, s.num_seqs);
     int hk = 0;
     if (resolve_qk_heads(s.num_heads, s.num_qk_heads, hk) != GDR_SUCCESS) return GDR_ERROR_INVALID_VALUE;
-    if (hk != s.num_heads)
-        return fail(GDR_ERROR_NOT_SUPPORTED, "the backward takes one q/k head per value head (%d != %d)", hk,
-                    s.num_heads);
     if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
     if (!valid_dtype(qkv_dtype)) return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype %d", (int)qkv_dtype);
     const bool packed = cu_seqlens != nullptr;
@@ -278,17 +283,17 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
                     "96, 128} (got %d, %d)", dk, dv);
 
     const size_t es = dsize(qkv_dtype);
-    const size_t nq = (size_t)tokens * s.num_heads * dk, nv = (size_t)tokens * s.num_heads * dv;
+    const size_t nq = (size_t)tokens * hk * dk, nv = (size_t)tokens * s.num_heads * dv;
     const size_t ng = (size_t)tokens * s.num_heads, nla = kda ? ng * dk : ng;
     const size_t nstate = (size_t)s.num_seqs * s.num_heads * dv * dk;
     if (tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !d_out || !dq || !dk_out || !dv_out || !dbeta ||
                        !dlog_alpha))
         return fail(GDR_ERROR_INVALID_VALUE, "q, k, v, beta, log_alpha, d_out and the five gradients must be non-NULL");
-    const void *aligned16[] = {q, k, v, d_out, initial_state, d_final_state, d_initial_state};
-    const char *names16[] = {"q", "k", "v", "d_out", "initial_state", "d_final_state", "d_initial_state"};
-    for (int i = 0; i < 7; ++i)
+    const void *aligned16[] = {q, k, v, d_out, initial_state, d_final_state, d_initial_state, dq, dk_out};
+    const char *names16[] = {"q", "k", "v", "d_out", "initial_state", "d_final_state", "d_initial_state", "dq", "dk"};
+    for (int i = 0; i < 9; ++i)
         if (!aligned(aligned16[i], 16)) return fail(GDR_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", names16[i]);
-    const void *aligned4[] = {beta, dq, dk_out, dv_out, dbeta, dlog_alpha, cu_seqlens};
+    const void *aligned4[] = {beta, dv_out, dbeta, dlog_alpha, cu_seqlens};
     for (const void *p : aligned4)
         if (!aligned(p, 4)) return fail(GDR_ERROR_INVALID_VALUE, "gradients, beta and cu_seqlens must be 4-byte aligned");
     if (!aligned(log_alpha, kda ? 16 : 4))
@@ -323,6 +328,7 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     a.batch = s.batch;
     a.seqlen = s.seqlen;
     a.num_heads = s.num_heads;
+    a.num_qk_heads = hk;
     a.dk = dk;
     a.dv = dv;
     a.num_seqs = s.num_seqs;
@@ -346,6 +352,8 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     a.records = wsb ? reinterpret_cast<float *>(wsb + ws.rec_off) : nullptr;
     a.states = wsb ? reinterpret_cast<float *>(wsb + ws.st_off) : nullptr;
     a.dstates = wsb ? reinterpret_cast<float *>(wsb + ws.dst_off) : nullptr;
+    a.dq_heads = hk != s.num_heads ? reinterpret_cast<float *>(wsb + ws.dqh_off) : nullptr;
+    a.dk_heads = hk != s.num_heads ? reinterpret_cast<float *>(wsb + ws.dkh_off) : nullptr;
     a.record_chunks = ws.record_chunks;
     return launch_status(gdr::launch_backward(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_backward");
 }

@@ -72,7 +72,7 @@ struct PrologueArgs {
 
 // Gradients of the chunked prefill (backward.hip).  All gradients fp32.
 struct BackwardArgs {
-    int batch, seqlen, num_heads, dk, dv, num_seqs;
+    int batch, seqlen, num_heads, num_qk_heads, dk, dv, num_seqs;
     bool kda, bf16;
     const void *q, *k, *v;
     const float *beta, *log_alpha;
@@ -87,6 +87,7 @@ struct BackwardArgs {
     int32_t *order, *chunk_offset;  // packed only
     float *records;                 // record_chunks * H records
     float *states, *dstates;        // record_chunks * H states of dv x dk each
+    float *dq_heads, *dk_heads;     // grouped heads only: per-value-head dq, dk [batch, seqlen, H, dk]
     long record_chunks;             // chunk slots (packed: an upper bound)
 };
 

@@ -322,14 +322,14 @@ const char *gdr_status_string(gdr_status status);
  * needed: the chunks' states are recomputed.
  *
  *  shape, gate, qkv_dtype, q, k, v, beta, log_alpha, initial_state,
- *  cu_seqlens, scale
- *                 exactly as passed to gdr_prefill_chunked; num_qk_heads
- *                 must equal num_heads (0 also means that); beta and
- *                 log_alpha fp32.
+ *                 cu_seqlens, scale
+ *                 exactly as passed to gdr_prefill_chunked (grouped q/k
+ *                 heads included); beta and log_alpha fp32.
  *  d_out          [batch, seqlen, num_heads, head_dim_v]              fp32
  *  d_final_state  [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, or
  *                 NULL for zeros
- *  dq, dk         [batch, seqlen, num_heads, head_dim_k]              fp32
+ *  dq, dk         [batch, seqlen, num_qk_heads, head_dim_k]           fp32
+ *                 (a shared q/k head's gradient sums its value heads')
  *  dv             [batch, seqlen, num_heads, head_dim_v]              fp32
  *  dbeta          [batch, seqlen, num_heads]                          fp32
  *  dlog_alpha     log_alpha's shape                                   fp32
@@ -339,13 +339,15 @@ const char *gdr_status_string(gdr_status status);
  *  workspace      device buffer of gdr_prefill_backward_workspace_bytes(...)
  *                 bytes, 256-byte aligned; the library writes it (chunk
  *                 records, each chunk's state and state gradient: about
- *                 (3.6 KB + 8 d_k d_v / 32 B) per token and head at d_k = 128)
- *                 and keeps nothing in it after the stream has run the call.
+ *                 1.8 KB + 8 d_k d_v / 32 bytes, 5.9 KB at d = 128, per token
+ *                 and value head; with grouped q/k heads also the value
+ *                 heads' dq and dk) and keeps nothing in it after the stream
+ *                 has run the call.
  *
  * Supported: head_dim_k in {32, 64, 128}; head_dim_v in {32, 64, 96, 128}
- * (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out and the states 16-byte
- * aligned, log_alpha 16-byte aligned for GDR_GATE_CHANNEL, everything else
- * 4-byte.  No output may overlap an input, another output or the
+ * (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out, dq, dk and the states
+ * 16-byte aligned, log_alpha 16-byte aligned for GDR_GATE_CHANNEL,
+ * everything else 4-byte.  No output may overlap an input, another output or the
  * workspace.  All arithmetic is fp32; every gradient element is written by
  * exactly one thread (no atomics), so results are bitwise reproducible.
  * Rows of padding and packed sequences of length zero are handled (an empty

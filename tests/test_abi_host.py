@@ -284,7 +284,6 @@ def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, q=A, k=A + 8 * MB, 
 
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(shape=(0, 64, 2, 64, 64, 0, 0)), 1, "bad shape"),
-    (dict(shape=(1, 64, 2, 64, 64, 1, 1)), 2, "one q/k head per value head"),
     (dict(shape=(1, 64, 2, 64, 64, 1, 3)), 1, "does not divide"),
     (dict(shape=(1, 64, 2, 16, 64, 1, 0)), 2, "head_dim_k"),
     (dict(shape=(1, 64, 2, 64, 256, 1, 0)), 2, "head_dim_v"),
@@ -304,7 +303,9 @@ def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, q=A, k=A + 8 * MB, 
     (dict(dinit=A + 40 * MB + 4), 1, "d_initial_state is not 16-byte aligned"),
     (dict(db=A + 38 * MB + 2), 1, "4-byte aligned"),
     (dict(gate=1, la=A + 25 * MB + 4), 1, "log_alpha must be 16-byte"),
-    (dict(dq=A + 8), 1, "dq overlaps q"),
+    (dict(dq=A + 16), 1, "dq overlaps q"),
+    (dict(dq=A + 32 * MB + 4), 1, "dq is not 16-byte aligned"),
+    (dict(shape=(1, 64, 2, 64, 64, 1, 1), dq=A + 8 * MB + 16), 1, "dq overlaps k"),   # grouped: dq sized by q/k heads
     (dict(dv=A + 34 * MB + 64), 1, "dk overlaps dv"),
     (dict(dla=A + 26 * MB), 1, "dlog_alpha overlaps d_out"),
     (dict(s0=A + 40 * MB, dinit=A + 40 * MB), 1, "d_initial_state overlaps initial_state"),
@@ -336,3 +337,6 @@ def test_backward_workspace_size():
     assert f(ctypes.byref(sh), 0, 1) == 256 + 256 + r256(slots * rec(64)) + 2 * r256(slots * 64 * 32 * 4)
     assert f(None, 0, 0) == 0
     assert f(ctypes.byref(sh), 3, 0) == 0
+    # grouped q/k heads add the value heads' dq and dk (tokens x H x dk fp32 each)
+    shg = gdr.PrefillShape(1, 1000, 4, 64, 32, 1, 2)
+    assert f(ctypes.byref(shg), 0, 0) == f(ctypes.byref(sh), 0, 0) + 2 * r256(1000 * 4 * 64 * 4)

@@ -112,11 +112,26 @@ def test_backward_is_deterministic():
         assert torch.equal(a[name], b[name]), name
 
 
-def test_backward_grouped_heads_not_supported():
-    inp, cot = _small(64, 64, 2, 40, "head", torch.bfloat16, False, seed=25)
-    with pytest.raises(gdr.GdrError, match="one q/k head per value head"):
-        gdr.gdr_prefill_backward(inp["q"][:, :, :1].contiguous(), inp["k"][:, :, :1].contiguous(), inp["v"],
-                                 inp["beta"], inp["log_alpha"], cot["d_out"])
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_backward_grouped_heads(gate):
+    """2 q/k heads shared by 6 value heads: each q/k head's gradient is the sum
+    over its group (the oracle's adjoint of the repetition)."""
+    w = Workload("small", "backward", heads=6, qk_heads=2, dk=64, dv=64, qkv_dtype=torch.bfloat16, gate=gate,
+                 batch=1, seqlen=77, init_state=True, seed=25)
+    inp = prefill_inputs(w, DEV)
+    cot = backward_cotangents(inp, 25, DEV)
+    assert inp["q"].shape[2] == 2 and inp["v"].shape[2] == 6
+    _check(inp, cot, f"grouped {gate}")
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_backward_grouped_packed(gate):
+    """Grouped heads (4 q/k heads, 16 value heads, d = 128) over packed sequences."""
+    w = Workload("small", "backward", heads=16, qk_heads=4, dk=128, dv=128, qkv_dtype=torch.bfloat16, gate=gate,
+                 batch=1, seqlen=0, init_state=True, seed=26)
+    inp = prefill_inputs(w, DEV, lengths=[45, 130, 3])
+    cot = backward_cotangents(inp, 26, DEV)
+    _check(inp, cot, f"grouped packed {gate}")
 
 
 def test_gdn_backward_8k_workload():
@@ -151,3 +166,33 @@ def test_kda_backward_32k_workload():
         for name in NAMES:
             g = got[name][n:n + 1, h:h + 1] if name == "d_initial_state" else got[name][sl]
             assert_close(f"{name}[{n},{h}]", g, ref[name], TOL_BWD)
+
+
+@pytest.mark.slow
+def test_gdn_gva_backward_32k_workload():
+    """The pages' Gated DeltaNet shape: T=32768, 16 q/k heads shared by 48
+    value heads, d=128, bf16, S0.  Every gradient is computed on the GPU and
+    checked for finiteness; two q/k heads (with all three value heads of each
+    group, whose gradients their dq and dk sum) are checked against the oracle."""
+    w = WORKLOADS["gdn_gva_backward_32k"]
+    inp = prefill_inputs(w, DEV)
+    cot = backward_cotangents(inp, w.seed, DEV)
+    say("backward gdn_gva_backward_32k (sampled groups)")
+    got = _gpu(inp, cot)
+    for name in NAMES:
+        assert torch.isfinite(got[name]).all(), name
+    G = inp["v"].shape[2] // inp["q"].shape[2]
+    for hq in (0, 15):
+        hv = slice(hq * G, (hq + 1) * G)
+        sub = {"q": inp["q"][:, :, hq:hq + 1].contiguous(), "k": inp["k"][:, :, hq:hq + 1].contiguous(),
+               "v": inp["v"][:, :, hv].contiguous(), "beta": inp["beta"][:, :, hv].contiguous(),
+               "log_alpha": inp["log_alpha"][:, :, hv].contiguous(),
+               "initial_state": inp["initial_state"][:, hv].contiguous(), "cu_seqlens": None}
+        subc = {"d_out": cot["d_out"][:, :, hv].contiguous(), "d_final_state": cot["d_final_state"][:, hv].contiguous()}
+        ref = _oracle(sub, subc)
+        assert_close(f"dq[{hq}]", got["dq"][:, :, hq:hq + 1], ref["dq"], TOL_BWD)
+        assert_close(f"dk[{hq}]", got["dk"][:, :, hq:hq + 1], ref["dk"], TOL_BWD)
+        for name in ("dv", "dbeta", "dlog_alpha"):
+            assert_close(f"{name}[{hv.start}:{hv.stop}]", got[name][:, :, hv], ref[name], TOL_BWD)
+        assert_close(f"d_initial_state[{hv.start}:{hv.stop}]", got["d_initial_state"][:, hv], ref["d_initial_state"],
+                     TOL_BWD)

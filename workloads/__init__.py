@@ -94,6 +94,9 @@ WORKLOADS = {
     "kda_backward_32k": Workload("kda_backward_32k", "backward", heads=32, dk=128, dv=128,
                                  qkv_dtype=torch.bfloat16, gate="channel", batch=2, seqlen=32768,
                                  init_state=True, seed=9),
+    "gdn_gva_backward_32k": Workload("gdn_gva_backward_32k", "backward", heads=48, qk_heads=16, dk=128, dv=128,
+                                     qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=32768,
+                                     init_state=True, seed=10),
     # the layer prologue on that shape: the 10240 projected q/k/v channels of
     # 32768 tokens, with a convolution state
     "prologue_gdn_32k": Workload("prologue_gdn_32k", "prologue", heads=48, qk_heads=16, dk=128, dv=128,
