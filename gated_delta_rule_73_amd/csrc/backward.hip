@@ -1006,10 +1006,15 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStr
         hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    // four waves (64 value rows) per scan workgroup when the two passes still
-    // give a workgroup to every CU, else two
+    // A scan workgroup fills a CU's LDS, so the grid runs in rounds of one
+    // workgroup per CU, each round one full chain.  Two waves (32 value rows)
+    // per workgroup when both passes then fit in one round, else four.
     const long units = (long)a.num_seqs * a.num_heads;
-    const bool four = a.dv % 64 == 0 && units * (a.dv / 64) >= 128;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const bool four = a.dv % 64 == 0 && 2 * 8 * ((units + 7) / 8) * (a.dv / 32) > cus;
     const long per_unit = a.dv / (four ? 64 : 32);
     const unsigned scan_blocks = (unsigned)(8 * ((units + 7) / 8) * per_unit);
     if (four)
