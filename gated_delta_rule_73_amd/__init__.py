@@ -48,7 +48,7 @@ class PrefillShape(ctypes.Structure):
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("num_qk_heads", ctypes.c_int32)]
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 _lib = None
@@ -79,8 +79,8 @@ def load_library():
         lib.gdr_layer_prologue.restype = ctypes.c_int
         lib.gdr_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, i32]
         lib.gdr_prefill_backward_workspace_bytes.restype = sz
-        lib.gdr_prefill_backward.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, p, p, p, p, p,
-                                             p, p, ctypes.c_float, p, p, p, p, p, p, p, p, p, sz, p]
+        lib.gdr_prefill_backward.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             p, p, p, p, p, p, p, ctypes.c_float, p, p, p, p, p, p, p, p, p, sz, p]
         lib.gdr_prefill_backward.restype = ctypes.c_int
         lib.gdr_state_bytes.argtypes = [ctypes.c_int64] * 4
         lib.gdr_state_bytes.restype = ctypes.c_uint64
@@ -186,8 +186,8 @@ def gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None,
                          cu_seqlens=None, scale: float = 1.0, output_d_initial_state: bool = True,
                          workspace=None):
     """Gradients through :func:`gdr_prefill_chunked` (same q, k, v, beta,
-    log_alpha, initial_state, cu_seqlens and scale, grouped q/k heads
-    included; fp32 gates).  d_out [B, T, H, dv] fp32; d_final_state
+    log_alpha, initial_state, cu_seqlens and scale, grouped q/k heads and
+    bf16 gates included).  d_out [B, T, H, dv] fp32; d_final_state
     [N, H, dv, dk] fp32 or None (zeros).
     Returns a dict of fp32 tensors: dq, dk (q's shape), dv (v's), dbeta,
     dlog_alpha (log_alpha's shape) and d_initial_state [N, H, dv, dk] (None
@@ -206,8 +206,8 @@ def gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None,
         raise ValueError("log_alpha must be [B, T, H] or [B, T, H, dk]")
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, q.dtype, dev)
-    _need(beta, "beta", torch.float32, dev)
-    _need(log_alpha, "log_alpha", torch.float32, dev)
+    _need(beta, "beta", None, dev)
+    _need(log_alpha, "log_alpha", beta.dtype, dev)
     _need(initial_state, "initial_state", torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     _need(d_out, "d_out", torch.float32, dev)
@@ -227,7 +227,8 @@ def gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None,
         _need(workspace, "workspace", torch.uint8, dev)
         ws, ws_bytes = workspace, workspace.numel()
     _check(lib.gdr_prefill_backward(
-        ctypes.byref(shape), gate, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+        ctypes.byref(shape), gate, _dtype_code(q), _dtype_code(beta), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+        _ptr(log_alpha),
         _ptr(initial_state), _ptr(cu_seqlens), float(scale), _ptr(d_out), _ptr(d_final_state), _ptr(g["dq"]),
         _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dbeta"]), _ptr(g["dlog_alpha"]), _ptr(g["d_initial_state"]),
         _ptr(ws), int(ws_bytes), _stream(dev)))

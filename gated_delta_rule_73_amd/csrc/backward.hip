@@ -59,7 +59,7 @@ struct BwdKArgs {
     int batch, seqlen, H, dv, num_seqs;
     int Hk, G;                                // q/k heads; value heads per q/k head (H = Hk G)
     const void *q, *k, *v;
-    const float *beta, *log_alpha;
+    const void *beta, *log_alpha;             // fp32, or bf16 (the kernels' GT)
     const float *initial_state;
     const int32_t *cu, *order, *choff;
     float scale;
@@ -193,6 +193,13 @@ __device__ __forceinline__ void tile_mma_nt(f32x4 (&acc)[NQ], int K, FA fa4, FB 
 }
 
 template <typename IT> __device__ __forceinline__ float ld1(const IT *p) { return to_f32(*p); }
+// gates (beta, log alpha): fp32 or bf16 storage, fp32 arithmetic
+template <typename GT> __device__ __forceinline__ float gate1(const void *g, long o) {
+    return to_f32(static_cast<const GT *>(g)[o]);
+}
+template <typename GT> __device__ __forceinline__ float4 gate4(const void *g, long o) {
+    return load4(static_cast<const GT *>(g) + o);
+}
 
 // Where record chunk rc lies: its sequence, first token (flat index over
 // batch x seqlen) and length; len <= 0 past the last chunk of a packed batch.
@@ -229,7 +236,7 @@ __device__ __forceinline__ ChunkLoc locate(const BwdKArgs &p, long rc) {
 
 // ---------------------------------------------------------------------------
 // Chunk records.
-template <int DK, bool KDA, typename IT>
+template <int DK, bool KDA, typename IT, typename GT>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
     constexpr int C = kBC, PK = DK + 4, NT = 256;
     using R = BRec<DK>;
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
         const long o = (t * H + h) * DK + j, oq = (t * p.Hk + h / p.G) * DK + j;
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
         const float4 kv = in ? load4(k + oq) : z4, qv = in ? load4(q + oq) : z4;
-        const float4 gv = KDA && in ? *reinterpret_cast<const float4 *>(p.log_alpha + o) : z4;
+        const float4 gv = KDA && in ? gate4<GT>(p.log_alpha, o) : z4;
         sK[r][j] = kv.x, sK[r][j + 1] = kv.y, sK[r][j + 2] = kv.z, sK[r][j + 3] = kv.w;
         sQ[r][j] = qv.x, sQ[r][j + 1] = qv.y, sQ[r][j + 2] = qv.z, sQ[r][j + 3] = qv.w;
         if (KDA) sX[r][j] = gv.x, sX[r][j + 1] = gv.y, sX[r][j + 2] = gv.z, sX[r][j + 3] = gv.w;
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
     if (tid < C) {
         const bool in = tid < L.len;
         const long o = (L.tok0 + min(tid, L.len - 1)) * H + h;
-        const float bb = p.beta[o], gg = KDA ? 0.f : p.log_alpha[o];
+        const float bb = gate1<GT>(p.beta, o), gg = KDA ? 0.f : gate1<GT>(p.log_alpha, o);
         sb[tid] = in ? bb : 0.f;
         if (!KDA) sg[tid] = in ? gg : 0.f;
     }
@@ -395,7 +402,7 @@ template <int DK, int NW> struct ScanLds {
     __align__(16) float S[2][C];
 };
 
-template <int DK, int NW, bool BWD, typename IT>
+template <int DK, int NW, bool BWD, typename IT, typename GT>
 __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<DK, NW> &lds) {
     constexpr int C = kBC, NT = 64 * NW, ZW = 16 * NW;
     constexpr int NE = C * DK / 4 / NT, NL = C * C / NT, NZ = C * ZW / 4 / NT;
@@ -470,7 +477,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         }
         rD = rec[R::D + (tid & (DK - 1))];
         const int tr = tid & (C - 1);
-        const float bb1 = p.beta[(tok0 + min(tr, clen - 1)) * H + h];
+        const float bb1 = gate1<GT>(p.beta, (tok0 + min(tr, clen - 1)) * H + h);
         rS = BWD ? 1.f : (tr < clen ? bb1 : 0.f);
     };
     auto put = [&](int b) {
@@ -576,20 +583,20 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
 // Both state passes in one launch: the first half of the grid walks the
 // states forward, the second half the state gradients backward.  The two
 // recurrences are independent, so each half fills the CUs the other leaves.
-template <int DK, int NW, typename IT>
+template <int DK, int NW, typename IT, typename GT>
 __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half) {
     __shared__ ScanLds<DK, NW> lds;
     if ((int)blockIdx.x < half)
-        scan_body<DK, NW, false, IT>(p, blockIdx.x, lds);
+        scan_body<DK, NW, false, IT, GT>(p, blockIdx.x, lds);
     else
-        scan_body<DK, NW, true, IT>(p, blockIdx.x - half, lds);
+        scan_body<DK, NW, true, IT, GT>(p, blockIdx.x - half, lds);
 }
 
 // ---------------------------------------------------------------------------
 // Input gradients of one (chunk, head) from its incoming state S0 and its
 // outgoing state gradient dS.  Eight waves; C x n outputs are 16x16 tiles
 // (row tile rt, column tile) dealt round-robin to the waves.
-template <int DK, bool KDA, typename IT>
+template <int DK, bool KDA, typename IT, typename GT>
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     constexpr int C = kBC, NT = kGradThreads, NW = NT / 64, PK = DK + 4, PV = 128 + 4, PB = PK > PV ? PK : PV;
     constexpr int UV = div_up(2 * 128 / 16, NW), UK = div_up(2 * DK / 16, NW);   // tiles per wave (max)
@@ -634,7 +641,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
         const long t = L.tok0 + min(r, L.len - 1);
         kv[u] = load4(k + (t * p.Hk + hq) * DK + j);
-        gv[u] = KDA ? *reinterpret_cast<const float4 *>(p.log_alpha + (t * H + h) * DK + j) : z4;
+        gv[u] = KDA ? gate4<GT>(p.log_alpha, (t * H + h) * DK + j) : z4;
     }
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         cb[u] = *reinterpret_cast<const f32x4 *>(S0 + (long)ic * DK + j4c);
     }
     const long obg = (L.tok0 + min(tid & (C - 1), L.len - 1)) * H + h;
-    const float bb = p.beta[obg], gg = KDA ? 0.f : p.log_alpha[obg];
+    const float bb = gate1<GT>(p.beta, obg), gg = KDA ? 0.f : gate1<GT>(p.log_alpha, obg);
 
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
@@ -999,11 +1006,11 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *__restr
     reinterpret_cast<f32x4 *>(dk)[e] = sk;
 }
 
-template <int DK, bool KDA, typename IT>
+template <int DK, bool KDA, typename IT, typename GT>
 static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStream_t st) {
     const long nrc = a.record_chunks;
     if (nrc > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     // A scan workgroup fills a CU's LDS, so the grid runs in rounds of one
@@ -1018,12 +1025,12 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStr
     const long per_unit = a.dv / (four ? 64 : 32);
     const unsigned scan_blocks = (unsigned)(8 * ((units + 7) / 8) * per_unit);
     if (four)
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, IT>), dim3(2 * scan_blocks), dim3(256), 0, st, kp, (int)scan_blocks);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, IT, GT>), dim3(2 * scan_blocks), dim3(256), 0, st, kp, (int)scan_blocks);
     else
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, IT>), dim3(2 * scan_blocks), dim3(128), 0, st, kp, (int)scan_blocks);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, IT, GT>), dim3(2 * scan_blocks), dim3(128), 0, st, kp, (int)scan_blocks);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (nrc > 0) {
-        hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(kGradThreads), 0, st, kp);
+        hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(kGradThreads), 0, st, kp);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         if (kp.G > 1) {
             const long n4 = (long)a.batch * a.seqlen * kp.Hk * (DK / 4);
@@ -1037,8 +1044,14 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStr
 
 template <int DK>
 static hipError_t dispatch_dk(const BackwardArgs &a, const BwdKArgs &kp, hipStream_t st) {
-    if (a.bf16) return a.kda ? run_backward<DK, true, __bf16>(a, kp, st) : run_backward<DK, false, __bf16>(a, kp, st);
-    return a.kda ? run_backward<DK, true, float>(a, kp, st) : run_backward<DK, false, float>(a, kp, st);
+    if (a.gate_bf16) {
+        if (a.bf16)
+            return a.kda ? run_backward<DK, true, __bf16, __bf16>(a, kp, st) : run_backward<DK, false, __bf16, __bf16>(a, kp, st);
+        return a.kda ? run_backward<DK, true, float, __bf16>(a, kp, st) : run_backward<DK, false, float, __bf16>(a, kp, st);
+    }
+    if (a.bf16)
+        return a.kda ? run_backward<DK, true, __bf16, float>(a, kp, st) : run_backward<DK, false, __bf16, float>(a, kp, st);
+    return a.kda ? run_backward<DK, true, float, float>(a, kp, st) : run_backward<DK, false, float, float>(a, kp, st);
 }
 
 bool backward_supported(int dk, int dv) {

@@ -249,8 +249,8 @@ size_t gdr_prefill_backward_workspace_bytes(const gdr_prefill_shape *shape, gdr_
 }
 
 gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
-                                const void *q, const void *k, const void *v, const float *beta,
-                                const float *log_alpha, const float *initial_state, const int32_t *cu_seqlens,
+                                gdr_dtype gate_dtype, const void *q, const void *k, const void *v, const void *beta,
+                                const void *log_alpha, const float *initial_state, const int32_t *cu_seqlens,
                                 float scale, const float *d_out, const float *d_final_state, float *dq,
                                 float *dk_out, float *dv_out, float *dbeta, float *dlog_alpha,
                                 float *d_initial_state, void *workspace, size_t workspace_bytes,
@@ -264,7 +264,8 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     int hk = 0;
     if (resolve_qk_heads(s.num_heads, s.num_qk_heads, hk) != GDR_SUCCESS) return GDR_ERROR_INVALID_VALUE;
     if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
-    if (!valid_dtype(qkv_dtype)) return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype %d", (int)qkv_dtype);
+    if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype))
+        return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (qkv=%d gate=%d)", (int)qkv_dtype, (int)gate_dtype);
     const bool packed = cu_seqlens != nullptr;
     if (packed && s.batch != 1) return fail(GDR_ERROR_INVALID_VALUE, "cu_seqlens requires batch == 1");
     if (!packed && s.num_seqs != s.batch)
@@ -293,11 +294,13 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     const char *names16[] = {"q", "k", "v", "d_out", "initial_state", "d_final_state", "d_initial_state", "dq", "dk"};
     for (int i = 0; i < 9; ++i)
         if (!aligned(aligned16[i], 16)) return fail(GDR_ERROR_INVALID_VALUE, "%s is not 16-byte aligned", names16[i]);
-    const void *aligned4[] = {beta, dv_out, dbeta, dlog_alpha, cu_seqlens};
+    const size_t gs = dsize(gate_dtype);
+    const void *aligned4[] = {dv_out, dbeta, dlog_alpha, cu_seqlens};
     for (const void *p : aligned4)
-        if (!aligned(p, 4)) return fail(GDR_ERROR_INVALID_VALUE, "gradients, beta and cu_seqlens must be 4-byte aligned");
-    if (!aligned(log_alpha, kda ? 16 : 4))
-        return fail(GDR_ERROR_INVALID_VALUE, "log_alpha must be %d-byte aligned", kda ? 16 : 4);
+        if (!aligned(p, 4)) return fail(GDR_ERROR_INVALID_VALUE, "gradients and cu_seqlens must be 4-byte aligned");
+    if (!aligned(beta, gs)) return fail(GDR_ERROR_INVALID_VALUE, "beta must be %zu-byte aligned", gs);
+    if (!aligned(log_alpha, kda ? 4 * gs : gs))
+        return fail(GDR_ERROR_INVALID_VALUE, "log_alpha must be %zu-byte aligned", kda ? 4 * gs : gs);
 
     const BackwardWorkspace ws = backward_workspace(s, packed);
     if ((ws.record_chunks + 8) * s.num_heads >= INT32_MAX)
@@ -308,7 +311,7 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     if (ws.total && !aligned(workspace, 256)) return fail(GDR_ERROR_INVALID_VALUE, "workspace is not 256-byte aligned");
 
     const Range in[] = {range("q", q, nq * es), range("k", k, nq * es), range("v", v, nv * es),
-                        range("beta", beta, ng * 4), range("log_alpha", log_alpha, nla * 4),
+                        range("beta", beta, ng * gs), range("log_alpha", log_alpha, nla * gs),
                         range("initial_state", initial_state, nstate * 4),
                         range("cu_seqlens", cu_seqlens, packed ? 4 * ((size_t)s.num_seqs + 1) : 0),
                         range("d_out", d_out, nv * 4), range("d_final_state", d_final_state, nstate * 4)};
@@ -334,6 +337,7 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     a.num_seqs = s.num_seqs;
     a.kda = kda;
     a.bf16 = bf16;
+    a.gate_bf16 = gate_dtype == GDR_BF16;
     a.q = q; a.k = k; a.v = v;
     a.beta = beta;
     a.log_alpha = log_alpha;

@@ -73,9 +73,9 @@ struct PrologueArgs {
 // Gradients of the chunked prefill (backward.hip).  All gradients fp32.
 struct BackwardArgs {
     int batch, seqlen, num_heads, num_qk_heads, dk, dv, num_seqs;
-    bool kda, bf16;
+    bool kda, bf16, gate_bf16;
     const void *q, *k, *v;
-    const float *beta, *log_alpha;
+    const void *beta, *log_alpha;   // fp32, or bf16 when gate_bf16
     const float *initial_state;     // [num_seqs, H, dv, dk] or NULL
     const int32_t *cu_seqlens;
     float scale;

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 4
+#define GDR_ABI_VERSION 5
 
 typedef enum gdr_status {
     GDR_SUCCESS = 0,
@@ -321,10 +321,10 @@ const char *gdr_status_string(gdr_status status);
  * beta, log_alpha and the initial state.  The forward's outputs are not
  * needed: the chunks' states are recomputed.
  *
- *  shape, gate, qkv_dtype, q, k, v, beta, log_alpha, initial_state,
- *                 cu_seqlens, scale
+ *  shape, gate, qkv_dtype, gate_dtype, q, k, v, beta, log_alpha,
+ *                 initial_state, cu_seqlens, scale
  *                 exactly as passed to gdr_prefill_chunked (grouped q/k
- *                 heads included); beta and log_alpha fp32.
+ *                 heads and bf16 gates included).
  *  d_out          [batch, seqlen, num_heads, head_dim_v]              fp32
  *  d_final_state  [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, or
  *                 NULL for zeros
@@ -333,6 +333,7 @@ const char *gdr_status_string(gdr_status status);
  *  dv             [batch, seqlen, num_heads, head_dim_v]              fp32
  *  dbeta          [batch, seqlen, num_heads]                          fp32
  *  dlog_alpha     log_alpha's shape                                   fp32
+ *                 (fp32 also for bf16 gates)
  *  d_initial_state [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, or
  *                 NULL (not written).  With a NULL initial_state it is the
  *                 gradient with respect to the zero state.
@@ -346,8 +347,8 @@ const char *gdr_status_string(gdr_status status);
  *
  * Supported: head_dim_k in {32, 64, 128}; head_dim_v in {32, 64, 96, 128}
  * (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out, dq, dk and the states
- * 16-byte aligned, log_alpha 16-byte aligned for GDR_GATE_CHANNEL,
- * everything else 4-byte.  No output may overlap an input, another output or the
+ * 16-byte aligned; beta aligned to its element, log_alpha to four elements
+ * for GDR_GATE_CHANNEL; the other gradients 4-byte.  No output may overlap an input, another output or the
  * workspace.  All arithmetic is fp32; every gradient element is written by
  * exactly one thread (no atomics), so results are bitwise reproducible.
  * Rows of padding and packed sequences of length zero are handled (an empty
@@ -356,8 +357,8 @@ const char *gdr_status_string(gdr_status status);
  */
 size_t gdr_prefill_backward_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate, int32_t packed);
 gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
-                                const void *q, const void *k, const void *v, const float *beta,
-                                const float *log_alpha, const float *initial_state, const int32_t *cu_seqlens,
+                                gdr_dtype gate_dtype, const void *q, const void *k, const void *v, const void *beta,
+                                const void *log_alpha, const float *initial_state, const int32_t *cu_seqlens,
                                 float scale, const float *d_out, const float *d_final_state, float *dq,
                                 float *dk, float *dv, float *dbeta, float *dlog_alpha, float *d_initial_state,
                                 void *workspace, size_t workspace_bytes, void *hip_stream);

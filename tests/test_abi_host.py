@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = gdr.load_library()
-    assert lib.gdr_abi_version() == 4 == gdr.ABI_VERSION
+    assert lib.gdr_abi_version() == 5 == gdr.ABI_VERSION
     assert lib.gdr_status_string(0) == b"success"
     assert lib.gdr_status_string(2) == b"not supported"
 
@@ -270,13 +270,13 @@ def test_prologue_accepts_in_place_state_and_empty_batch():
 
 
 # ---- backward ---------------------------------------------------------------
-def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, q=A, k=A + 8 * MB, v=A + 16 * MB, beta=A + 24 * MB,
+def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, gdt=0, q=A, k=A + 8 * MB, v=A + 16 * MB, beta=A + 24 * MB,
               la=A + 25 * MB, s0=None, cu=None, dout=A + 26 * MB, dfin=None, dq=A + 32 * MB, dk=A + 34 * MB,
               dv=A + 36 * MB, db=A + 38 * MB, dla=A + 39 * MB, dinit=None, ws=A + 64 * MB, wsb=64 * MB):
     lib = gdr.load_library()
     sh = gdr.PrefillShape(*shape)
     v_ = lambda x: None if x is None else ctypes.c_void_p(x)
-    st = lib.gdr_prefill_backward(ctypes.byref(sh), gate, qkv, v_(q), v_(k), v_(v), v_(beta), v_(la), v_(s0), v_(cu),
+    st = lib.gdr_prefill_backward(ctypes.byref(sh), gate, qkv, gdt, v_(q), v_(k), v_(v), v_(beta), v_(la), v_(s0), v_(cu),
                                   1.0, v_(dout), v_(dfin), v_(dq), v_(dk), v_(dv), v_(db), v_(dla), v_(dinit), v_(ws),
                                   wsb, None)
     return st, lib.gdr_last_error().decode()
@@ -303,6 +303,9 @@ def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, q=A, k=A + 8 * MB, 
     (dict(dinit=A + 40 * MB + 4), 1, "d_initial_state is not 16-byte aligned"),
     (dict(db=A + 38 * MB + 2), 1, "4-byte aligned"),
     (dict(gate=1, la=A + 25 * MB + 4), 1, "log_alpha must be 16-byte"),
+    (dict(gdt=1, gate=1, la=A + 25 * MB + 4), 1, "log_alpha must be 8-byte"),
+    (dict(gdt=1, beta=A + 24 * MB + 1), 1, "beta must be 2-byte"),
+    (dict(gdt=3), 1, "dtype"),
     (dict(dq=A + 16), 1, "dq overlaps q"),
     (dict(dq=A + 32 * MB + 4), 1, "dq is not 16-byte aligned"),
     (dict(shape=(1, 64, 2, 64, 64, 1, 1), dq=A + 8 * MB + 16), 1, "dq overlaps k"),   # grouped: dq sized by q/k heads

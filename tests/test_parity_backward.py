@@ -196,3 +196,22 @@ def test_gdn_gva_backward_32k_workload():
             assert_close(f"{name}[{hv.start}:{hv.stop}]", got[name][:, :, hv], ref[name], TOL_BWD)
         assert_close(f"d_initial_state[{hv.start}:{hv.stop}]", got["d_initial_state"][:, hv], ref["d_initial_state"],
                      TOL_BWD)
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_backward_bf16_gates(gate):
+    """beta and log alpha stored in bf16 (the forward's bf16-gate variant); the
+    oracle reads the same bf16 values exactly; the gate gradients are fp32."""
+    w = Workload("small", "backward", heads=2, dk=128, dv=128, qkv_dtype=torch.bfloat16, gate=gate, batch=1,
+                 seqlen=100, init_state=True, seed=27)
+    inp = prefill_inputs(w, DEV, gate_dtype=torch.bfloat16)
+    cot = backward_cotangents(inp, 27, DEV)
+    got, _ = _check(inp, cot, f"bf16 gates {gate}")
+    assert got["dbeta"].dtype == torch.float32 and got["dlog_alpha"].dtype == torch.float32
+
+
+def test_backward_empty_dense_batch_passes_the_state_gradient_through():
+    """T = 0: no tokens, so the initial-state gradient is the final-state one."""
+    inp, cot = _small(64, 64, 2, 0, "channel", torch.bfloat16, True, seed=28, B=2)
+    g = _gpu(inp, cot)
+    assert torch.equal(g["d_initial_state"], cot["d_final_state"])
