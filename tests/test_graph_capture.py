@@ -7,7 +7,8 @@ import torch
 
 import gated_delta_rule_73_amd as gdr
 from parity import gpu_available, say
-from workloads import WORKLOADS, decode_inputs, decode_tokens_inputs, prologue_inputs
+from workloads import WORKLOADS, Workload, backward_cotangents, decode_inputs, decode_tokens_inputs, prefill_inputs, \
+    prologue_inputs
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
 DEV = "cuda"
@@ -64,3 +65,41 @@ def test_decode_calls_replay_in_a_graph():
                               got, ref[i]):
             assert torch.equal(a, b), f"replay {i}: {name} differs from the eager run"
         say(f"replay {i}: identical to the eager step")
+
+
+def test_training_step_forward_and_backward_replay_in_a_graph():
+    """A prefill and its backward captured together (their outputs and
+    workspaces come from the graph's own pool) replay identically to the
+    eager calls, with eager calls and synchronisations between the replays."""
+    w = Workload("small", "backward", heads=4, dk=128, dv=128, qkv_dtype=torch.bfloat16, gate="channel", batch=2,
+                 seqlen=100, init_state=True, seed=503)
+    inp = prefill_inputs(w, DEV)
+    cot = backward_cotangents(inp, 503, DEV)
+
+    def step():
+        out, fin = gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                                           initial_state=inp["initial_state"])
+        g = gdr.gdr_prefill_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], cot["d_out"],
+                                     initial_state=inp["initial_state"], d_final_state=cot["d_final_state"])
+        return [out, fin] + [g[n] for n in ("dq", "dk", "dv", "dbeta", "dlog_alpha", "d_initial_state")]
+
+    eager = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(gr, stream=s):
+            captured = step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in captured:
+            t.fill_(float("nan"))
+        gr.replay()
+        torch.cuda.synchronize()
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
+        for a, b in zip(captured, eager):
+            assert torch.equal(a, b), f"replay {i}"
+        say(f"  replay {i}: forward and backward identical to the eager calls")
