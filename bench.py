@@ -200,10 +200,10 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     own loop of args.steps calls after args.warmup untimed ones."""
     res = {}
 
-    def prefill_entry(w, inp, label, flush=None):
+    def prefill_entry(w, inp, label, flush=None, out_dtype=torch.float32):
         B, T, Hk, dk = inp["q"].shape
         H, dv = inp["v"].shape[2:]
-        po = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+        po = torch.empty(B, T, H, dv, dtype=out_dtype, device=dev)
         N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
         pf = torch.empty(N, H, dv, dk, dtype=torch.float32, device=dev)
         f = lambda: gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
@@ -213,8 +213,8 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
             f()
         mean, med, mn = time_calls(f, args.steps, between=flush)
         kda = inp["log_alpha"].dim() == 4
-        by = prefill_alg_bytes(B, T, H, dk, dv, kda, 4, inp["initial_state"] is not None, True, Hk=Hk,
-                               gate_bytes=inp["beta"].element_size())
+        by = prefill_alg_bytes(B, T, H, dk, dv, kda, po.element_size(), inp["initial_state"] is not None, True,
+                               Hk=Hk, gate_bytes=inp["beta"].element_size())
         if inp["cu_seqlens"] is not None:   # one initial and one final state per sequence, not per row
             by += (N - B) * 2 * H * dv * dk * 4
         fl = prefill_alg_flops(B, T, H, dk, dv, 32)
@@ -224,6 +224,12 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
                 "alg_flops": fl, "mfma_frac": round(fl / mean / (BF16_MFMA_PEAK_TFLOPS * 1e12), 4)}
 
     w2 = WORKLOADS["kda_prefill_32k"]
+    print(f"[bench] {w2.name} with bf16 outputs", file=sys.stderr, flush=True)
+    g2 = prefill_inputs(w2, dev)
+    res["kda_prefill_32k_bf16_out"] = prefill_entry(
+        w2, g2, f"{w2.name} writing its outputs in bf16 (rounded to nearest even) instead of fp32: B=2, T=32768, "
+                "H=32, d=128, bf16 q/k/v, per-channel decay, S0 given", out_dtype=torch.bfloat16)
+    del g2
     print(f"[bench] {w2.name} with bf16 gates", file=sys.stderr, flush=True)
     g2 = prefill_inputs(w2, dev, gate_dtype=torch.bfloat16)
     res["kda_prefill_32k_bf16_gates"] = prefill_entry(
