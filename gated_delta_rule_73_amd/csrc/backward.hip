@@ -139,6 +139,35 @@ __device__ __forceinline__ void tile_mma_n(f32x4 (&acc)[NQ], int K, FA fa, FB fb
     }
 }
 
+// Split bf16 operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
+// (x - hi is exact in fp32), 16 significant bits with fp32's exponent range.
+// A product takes hi*hi + hi*lo + lo*hi on the 16x16x32 bf16 MFMA with fp32
+// accumulation; the dropped lo*lo term and the rounding of lo are below
+// 2^-16 of each operand product.
+__device__ __forceinline__ void split4(const f32x4 v, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 h = (__bf16)v[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(v[i] - (float)h);
+    }
+}
+// the B operand of one 32-k step from two accumulator tiles (k = 4 lq + i of
+// tile a, then of tile b)
+__device__ __forceinline__ void split8(const f32x4 a, const f32x4 b, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 ha = (__bf16)a[i], hb = (__bf16)b[i];
+        hi[i] = ha, hi[4 + i] = hb;
+        lo[i] = (__bf16)(a[i] - (float)ha), lo[4 + i] = (__bf16)(b[i] - (float)hb);
+    }
+}
+__device__ __forceinline__ f32x4 mfma_split(const bf16x8 &ah, const bf16x8 &al, const bf16x8 &bh,
+                                            const bf16x8 &bl, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+}
 // Raw buffer loads: the byte offset splits into a per-lane VGPR part and a
 // uniform scalar part, so a sweep over k needs no per-k address registers.
 constexpr int kRawBufferWord3 = 0x00020000;
@@ -160,7 +189,10 @@ __device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, int lane_bytes
 // k = kb + 4 lq + s in step s (the same on both sides, so the sum is the
 // same).  fa4(q, mi, kb, lk) = A_q(m0 + mi, kb + lk .. kb + lk + 3) and
 // fb4(q, ni, kb, lk) = B_q^T(n0 + ni, kb + lk .. kb + lk + 3); kb is
-// wave-uniform.  Blocks of 32 k, gathered one block ahead of their MFMAs.
+// wave-uniform.  Blocks of 32 k, gathered one block ahead of their MFMAs;
+// each block is one split bf16 product (16x16x32, hi/lo operands, see
+// split8): a lane's k = kb + 4 lq + s and kb + 16 + 4 lq + s are the eight
+// k it supplies to that MFMA.
 template <int KMAX, int NQ, class FA, class FB>
 __device__ __forceinline__ void tile_mma_nt(f32x4 (&acc)[NQ], int K, FA fa4, FB fb4) {
     static_assert(KMAX % 32 == 0, "k blocks of 32");
@@ -182,11 +214,12 @@ __device__ __forceinline__ void tile_mma_nt(f32x4 (&acc)[NQ], int K, FA fa4, FB 
         if (32 * blk < K) {                     // K (a multiple of 32) is wave-uniform
             if (blk + 1 < NB && 32 * (blk + 1) < K) gather(blk + 1, (blk + 1) & 1);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) acc[q] = mfma4(a[blk & 1][q][h][s], b[blk & 1][q][h][s], acc[q]);
+            for (int q = 0; q < NQ; ++q) {
+                bf16x8 ah, al, bh, bl;
+                split8(a[blk & 1][q][0], a[blk & 1][q][1], ah, al);
+                split8(b[blk & 1][q][0], b[blk & 1][q][1], bh, bl);
+                acc[q] = mfma_split(ah, al, bh, bl, acc[q]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -392,26 +425,51 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
 // double-buffered LDS stage: one barrier per chunk.  The workgroups of one
 // (sequence, head) sit on one XCD (block b runs on XCD b mod 8), so its
 // records come from HBM once and from that XCD's L2 for the other slices.
-// LDS of one scan workgroup.  Every operand is read as four consecutive k
-// per lane (one 16-byte LDS read for four MFMA steps): E as stored ([r][j]),
-// the state-update operands B and G transposed ([j][r]), Z transposed
-// ([value row][r]); two stages.
+//
+// Products on the 16x16x32 bf16 MFMA with split operands (split8,
+// mfma_split; bf16 rather than fp16 because the state gradient has no
+// fp16-sized bound).  The state and P stay in fp32 accumulators and are split
+// afresh in registers for each chunk.
+//
+// Operand planes in LDS are blocks of 32 k (rows x 32, 64 bytes per row).
+// Inside a block the k order is permuted so that the eight k one lane
+// supplies to one MFMA -- k = 4 lq + i and 16 + 4 lq + i (i < 4): the layout
+// of two fp32 accumulator tiles -- sit at eight consecutive positions
+// 8 lq .. 8 lq + 7.  The 16 rows one wave reads are then 1 KB of contiguous
+// LDS, read as one 16-byte access per lane per plane.
+__device__ __forceinline__ int kperm32(int k) { return 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3); }
+
+__device__ __forceinline__ bf16x8 lds8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ void sts4(__bf16 *p, const bf16x4 v) { *reinterpret_cast<bf16x4 *>(p) = v; }
+
+// LDS of one scan workgroup, two stages; [.][0] hi, [.][1] lo planes.
+//   E:  the operand multiplying the state (forward Wn, backward K_end),
+//       [key block][chunk row][32 keys];
+//   Bt: the state update's left operand (forward K_end, backward Wn),
+//       transposed: [key][32 chunk rows];
+//   Gt: backward only, (Q e^g) transposed: [key][32 chunk rows];
+//   L:  forward T, backward M^T: [chunk row][32 chunk columns];
+//   Zt: forward diag(b) V, backward scale dO, transposed:
+//       [value row][32 chunk rows].
 template <int DK, int NW> struct ScanLds {
-    static constexpr int C = kBC, PK = DK + 4, PC = C + 4, ZW = 16 * NW;
-    __align__(16) float E[2][C][PK];
-    __align__(16) float Bt[2][DK][PC];
-    __align__(16) float Gt[2][DK][PC];
-    __align__(16) float L[2][C][PC];
-    __align__(16) float Zt[2][ZW][PC];
+    static constexpr int C = kBC, ZW = 16 * NW;
+    __align__(16) __bf16 E[2][2][DK / 32][C][32];
+    __align__(16) __bf16 Bt[2][2][DK][32];
+    __align__(16) __bf16 Gt[2][2][DK][32];
+    __align__(16) __bf16 L[2][2][C][32];
+    __align__(16) __bf16 Zt[2][2][ZW][32];
     __align__(16) float D[2][DK];
-    __align__(16) float S[2][C];
 };
 
 template <int DK, int NW, bool BWD, typename IT, typename GT>
 __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<DK, NW> &lds) {
-    constexpr int C = kBC, NT = 64 * NW, ZW = 16 * NW;
-    constexpr int NE = C * DK / 4 / NT, NL = C * C / NT, NZ = C * ZW / 4 / NT;
-    static_assert(NE >= 1 && NL >= 1 && NZ >= 1, "scan tiling");
+    constexpr int C = kBC, NT = 64 * NW, ZW = 16 * NW, NB = DK / 32;
+    // per thread: NE row pieces of E and NE column pieces of Bt (and Gt),
+    // NL pieces of L, NZ column pieces of Zt; four values each
+    // (the last round of a count below NT leaves threads idle: their loads
+    // are clamped to a valid piece, their LDS stores skipped)
+    constexpr int TE = C * DK / 4, TL = C * C / 4, NE = div_up(TE, NT), NL = div_up(TL, NT), NZ = C * ZW / 4 / NT;
+    static_assert(C * ZW % (4 * NT) == 0 && DK % 32 == 0, "scan tiling");
     using R = BRec<DK>;
     auto &sE = lds.E;
     auto &sBt = lds.Bt;
@@ -419,7 +477,6 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     auto &sL = lds.L;
     auto &sZt = lds.Zt;
     auto &sD = lds.D;
-    auto &sS = lds.S;
     const int H = p.H, DV = p.dv, S = DV / ZW;
     const int xcd = block & 7, kb = block >> 3;
     const int unit = xcd + 8 * (kb / S), slice = kb % S;
@@ -438,11 +495,25 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     const int row = ZW * slice + 16 * w + lr;     // this lane's value row (as MFMA column)
     const IT *v = static_cast<const IT *>(p.v);
 
-    f32x4 rE[NE], rB[NE], rG[BWD ? NE : 1], rZ[NZ];
-    float rL[NL], rD = 0.f, rS = 0.f;
-    // rE[u]: E[r][j .. j + 3] (row-major, as stored); rB[u], rG[u]: B[r .. r + 3][j]
-    // and G[r .. r + 3][j] (four rows of one column: written as one 16-byte
-    // row piece of the transposed copy); rZ[u]: Z[r .. r + 3][i] likewise.
+    // Thread-to-piece maps (element index e = tid + NT u):
+    //  row pieces (E; forward L): four consecutive k of one row; eight
+    //    threads cover one row's 32-k block, whose 64 bytes they write whole;
+    //  column pieces (Bt, Gt, Zt; backward L): four consecutive rows of one
+    //    column; 16 threads take 16 adjacent columns (64 contiguous bytes of
+    //    each source row), and a wave writes 16 whole 64-byte LDS rows.
+    auto row_piece = [](int e, int &r, int &k) {       // k: first of four, 32 k per row block
+        const int jj = e & 7;
+        r = (e >> 3) & (C - 1);
+        k = 32 * (e >> 8) + 4 * (jj >> 1) + 16 * (jj & 1);
+    };
+    auto col_piece = [](int e, int ncol, int &c, int &r4) {   // ncol: columns in all
+        const int rest = e >> 6, nch = ncol / 16;
+        c = 16 * (rest % nch) + (e & 15);
+        r4 = 16 * (rest / nch) + 4 * ((e >> 4) & 3);
+    };
+
+    f32x4 rE[NE], rB[NE], rG[BWD ? NE : 1], rL[NL], rZ[NZ];
+    float rD = 0.f;
     auto fetch = [&](int s) {
         const int c = BWD ? nc - 1 - s : s;
         const long rc = rc0 + c, tok0 = tok_base + (long)c * C;
@@ -451,10 +522,12 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         const float *eb = rec + (BWD ? R::KE : R::W), *bb = rec + (BWD ? R::W : R::KE);
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
-            const int e = tid + NT * u;
-            const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;      // E: row r, columns j..j+3
+            const int e = min(tid + NT * u, TE - 1);
+            int r, j;
+            row_piece(e, r, j);
             rE[u] = *reinterpret_cast<const f32x4 *>(eb + r * DK + j);
-            const int jc = e % DK, r4 = (e / DK) * 4;                 // B, G: column jc, rows r4..r4+3
+            int jc, r4;
+            col_piece(e, DK, jc, r4);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 rB[u][t] = bb[(r4 + t) * DK + jc];
@@ -463,50 +536,79 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         }
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int e = tid + NT * u, r = e / C, cc = e % C;
-            rL[u] = BWD ? rec[R::M + cc * C + r] : rec[R::T + e];
+            const int e = min(tid + NT * u, TL - 1);
+            if (BWD) {                        // L = M^T: column pieces of M^T are row pieces of M
+                int r, c4;
+                col_piece(e, C, r, c4);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) rL[u][t] = rec[R::M + (c4 + t) * C + r];
+            } else {
+                int r, c4;
+                row_piece(e, r, c4);
+                rL[u] = *reinterpret_cast<const f32x4 *>(rec + R::T + r * C + c4);
+            }
         }
         // loads from clamped, always-valid rows and a select for padding rows:
         // a load under a lane-dependent branch would make the compiler wait for
         // every load in flight, the record loads above included
 #pragma unroll
         for (int u = 0; u < NZ; ++u) {
-            const int e = tid + NT * u, i = e % ZW, r4 = (e / ZW) * 4;
+            int i, r4;
+            col_piece(tid + NT * u, ZW, i, r4);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int r = r4 + t;
-                const long o = ((tok0 + min(r, clen - 1)) * H + h) * DV + ZW * slice + i;
-                const float z = BWD ? p.scale * p.d_out[o] : ld1(v + o);
+                const long tr = (tok0 + min(r, clen - 1)) * H + h, o = tr * DV + ZW * slice + i;
+                const float z = BWD ? p.scale * p.d_out[o] : gate1<GT>(p.beta, tr) * ld1(v + o);
                 rZ[u][t] = r < clen ? z : 0.f;
             }
         }
         rD = rec[R::D + (tid & (DK - 1))];
-        const int tr = tid & (C - 1);
-        const float bb1 = gate1<GT>(p.beta, (tok0 + min(tr, clen - 1)) * H + h);
-        rS = BWD ? 1.f : (tr < clen ? bb1 : 0.f);
     };
     auto put = [&](int b) {
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
             const int e = tid + NT * u;
-            const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-            *reinterpret_cast<f32x4 *>(&sE[b][r][j]) = rE[u];
-            const int jc = e % DK, r4 = (e / DK) * 4;
-            *reinterpret_cast<f32x4 *>(&sBt[b][jc][r4]) = rB[u];
-            if (BWD) *reinterpret_cast<f32x4 *>(&sGt[b][jc][r4]) = rG[u];
+            if (TE % NT != 0 && e >= TE) continue;
+            bf16x4 hi, lo;
+            int r, j;
+            row_piece(e, r, j);
+            split4(rE[u], hi, lo);
+            sts4(&sE[b][0][j >> 5][r][kperm32(j)], hi);
+            sts4(&sE[b][1][j >> 5][r][kperm32(j)], lo);
+            int jc, r4;
+            col_piece(e, DK, jc, r4);
+            split4(rB[u], hi, lo);
+            sts4(&sBt[b][0][jc][kperm32(r4)], hi);
+            sts4(&sBt[b][1][jc][kperm32(r4)], lo);
+            if (BWD) {
+                split4(rG[u], hi, lo);
+                sts4(&sGt[b][0][jc][kperm32(r4)], hi);
+                sts4(&sGt[b][1][jc][kperm32(r4)], lo);
+            }
         }
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int e = tid + NT * u;
-            sL[b][e / C][e % C] = rL[u];
+            if (TL % NT != 0 && e >= TL) continue;
+            int r, c4;
+            if (BWD) col_piece(e, C, r, c4);
+            else row_piece(e, r, c4);
+            bf16x4 hi, lo;
+            split4(rL[u], hi, lo);
+            sts4(&sL[b][0][r][kperm32(c4)], hi);
+            sts4(&sL[b][1][r][kperm32(c4)], lo);
         }
 #pragma unroll
         for (int u = 0; u < NZ; ++u) {
-            const int e = tid + NT * u;
-            *reinterpret_cast<f32x4 *>(&sZt[b][e % ZW][(e / ZW) * 4]) = rZ[u];
+            int i, r4;
+            col_piece(tid + NT * u, ZW, i, r4);
+            bf16x4 hi, lo;
+            split4(rZ[u], hi, lo);
+            sts4(&sZt[b][0][i][kperm32(r4)], hi);
+            sts4(&sZt[b][1][i][kperm32(r4)], lo);
         }
         if (tid < DK) sD[b][tid] = rD;
-        if (tid < C) sS[b][tid] = rS;
     };
 
     f32x4 x[DK / 16];
@@ -531,48 +633,35 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt) *reinterpret_cast<f32x4 *>(dump + 16 * jt + 4 * lq) = x[jt];
 
-        // lane group lq takes k = 16 h + 4 lq + i in MFMA step (h, i) of the
-        // 32-deep products, k = 16 jt + 4 lq + i in those over d_k
-        const f32x4 zt[2] = {lds4(&sZt[b][16 * w + lr][4 * lq]), lds4(&sZt[b][16 * w + lr][16 + 4 * lq])};
+        // the state as B operand of the products over keys (k = key)
+        bf16x8 xh[NB], xl[NB];
+#pragma unroll
+        for (int kb2 = 0; kb2 < NB; ++kb2) split8(x[2 * kb2], x[2 * kb2 + 1], xh[kb2], xl[kb2]);
+        const bf16x8 zh = lds8(&sZt[b][0][16 * w + lr][8 * lq]), zl = lds8(&sZt[b][1][16 * w + lr][8 * lq]);
         f32x4 pc[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            f32x4 acc = zero4();
+            f32x4 acc = mfma_split(lds8(&sL[b][0][16 * rt + lr][8 * lq]), lds8(&sL[b][1][16 * rt + lr][8 * lq]), zh,
+                                   zl, zero4());
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const f32x4 lv = lds4(&sL[b][16 * rt + lr][16 * h + 4 * lq]);
-                const f32x4 sv = lds4(&sS[b][16 * h + 4 * lq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma4(lv[i], sv[i] * zt[h][i], acc);
-            }
-#pragma unroll
-            for (int jt = 0; jt < DK / 16; ++jt) {
-                const f32x4 ev = lds4(&sE[b][16 * rt + lr][16 * jt + 4 * lq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma4(ev[i], x[jt][i], acc);
-            }
+            for (int kb2 = 0; kb2 < NB; ++kb2)
+                acc = mfma_split(lds8(&sE[b][0][kb2][16 * rt + lr][8 * lq]), lds8(&sE[b][1][kb2][16 * rt + lr][8 * lq]),
+                                 xh[kb2], xl[kb2], acc);
             pc[rt] = acc;
         }
+        // P as B operand of the state update (k = chunk row)
+        bf16x8 ph, pl;
+        split8(pc[0], pc[1], ph, pl);
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt) {
             f32x4 acc = x[jt];
-            const f32x4 dv4 = lds4(&sD[b][16 * jt + 4 * lq]);
+            const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(&sD[b][16 * jt + 4 * lq]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] *= dv4[i];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const f32x4 bv = lds4(&sBt[b][16 * jt + lr][16 * rt + 4 * lq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma4(bv[i], pc[rt][i], acc);
-            }
-            if (BWD) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const f32x4 gv = lds4(&sGt[b][16 * jt + lr][16 * h + 4 * lq]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc = mfma4(gv[i], zt[h][i], acc);
-                }
-            }
+            acc = mfma_split(lds8(&sBt[b][0][16 * jt + lr][8 * lq]), lds8(&sBt[b][1][16 * jt + lr][8 * lq]), ph, pl, acc);
+            if (BWD)
+                acc = mfma_split(lds8(&sGt[b][0][16 * jt + lr][8 * lq]), lds8(&sGt[b][1][16 * jt + lr][8 * lq]), zh,
+                                 zl, acc);
             x[jt] = acc;
         }
         if (s + 1 < nc) put(b ^ 1);
@@ -604,7 +693,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half)
 template <int DK, bool KDA, typename IT, typename GT>
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     constexpr int C = kBC, NT = kGradThreads, NW = NT / 64, PK = DK + 4, PV = 128 + 4, PB = PK > PV ? PK : PV;
-    constexpr int UV = div_up(2 * 128 / 16, NW), UK = div_up(2 * DK / 16, NW);   // tiles per wave (max)
+    constexpr int UV = div_up(2 * 128 / 16, NW);   // C x d_v tiles per wave (max)
     static_assert(NW >= 8 && NW % 2 == 0, "the C x C phases deal tiles to waves 0-7");
     using R = BRec<DK>;
     // K e^g, then K e^{g-m}       | raw K, then K e^{m-g}      | g, then dg (per channel)
@@ -614,8 +703,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     __shared__ __align__(16) float sB1[C][PB], sB2[C][PV], sB3[C][PV], sB4[C][PV];
     __shared__ float sT[C][C + 1], sM[C][C + 1], sdT[C][C + 1], sdA[C][C + 1], sdM[C][C + 1], sE1[C][C + 1];
     __shared__ float sb[C], sg[C], sm[DK], sgl[DK], sdgc[DK], sdb[C];
-    constexpr int Q4 = DK / 4, RS = NT / Q4;   // dS o S0 column sums: RS row groups of float4 columns
-    __shared__ float sRed[RS][DK];            // column partials of dS o S0
     __shared__ float sPb[8][C], sPb2[2][C];   // d beta partials (per value tile / column tile)
     __shared__ float sPc[2][DK];              // column partials of gK3 o K
     __shared__ float sPr[DK / 16][C];         // row partials of dg (per-head decay)
@@ -629,18 +716,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     const float *S0 = p.states + (rc * H + h) * (long)DV * DK;
     const float *dS = p.dstates + (rc * H + h) * (long)DV * DK;
     const __amdgpu_buffer_rsrc_t rS0 = buffer_of(S0, (long)DV * DK), rdS = buffer_of(dS, (long)DV * DK);
-    const __amdgpu_buffer_rsrc_t rRec = buffer_of(rec, p.rec_stride);
-    const int ntv = 2 * (DV / 16), ntk = 2 * (DK / 16);
+    const int ntv = 2 * (DV / 16);
 
-    // ---- loads: every load of the chunk is issued first (all in flight
-    //      together, from clamped rows), then the LDS stores and the column
-    //      sums of dS o S0 (the decay's share of the outgoing gradient) consume them
-    constexpr int NKL = div_up(C * DK / 4, NT), NVL = div_up(C * 128 / 4, NT), NTL = C * C / NT, NCS = div_up(128, RS);
+    // ---- loads: every load of the chunk's inputs is issued first (all in
+    //      flight together, from clamped rows), then the LDS stores consume them
+    constexpr int NKL = div_up(C * DK / 4, NT), NVL = div_up(C * 128 / 4, NT), NTL = C * C / NT;
     static_assert(NTL >= 1 && C * C % NT == 0, "load tiling");
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 kv[NKL], gv[NKL], vv[NVL], dd[NVL];
     float tv[NTL], mv[NTL];
-    f32x4 ca[NCS], cb[NCS];
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
         const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
@@ -659,13 +743,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     for (int u = 0; u < NTL; ++u) {
         tv[u] = rec[R::T + tid + NT * u];
         mv[u] = rec[R::M + tid + NT * u];
-    }
-    const int j4c = (tid % Q4) * 4, i0c = tid / Q4;
-#pragma unroll
-    for (int u = 0; u < NCS; ++u) {
-        const int ic = min(i0c + RS * u, DV - 1);
-        ca[u] = *reinterpret_cast<const f32x4 *>(dS + (long)ic * DK + j4c);
-        cb[u] = *reinterpret_cast<const f32x4 *>(S0 + (long)ic * DK + j4c);
     }
     const long obg = (L.tok0 + min(tid & (C - 1), L.len - 1)) * H + h;
     const float bb = gate1<GT>(p.beta, obg), gg = KDA ? 0.f : gate1<GT>(p.log_alpha, obg);
@@ -699,17 +776,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         sb[tid] = tid < L.len ? bb : 0.f;
         if (!KDA) sg[tid] = tid < L.len ? gg : 0.f;
     }
-    {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int u = 0; u < NCS; ++u) {
-            const float on = i0c + RS * u < DV ? 1.f : 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] += on * ca[u][c] * cb[u][c];
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sRed[i0c][j4c + c] = acc[c];
-    }
     __syncthreads();
     if (KDA) {
         for (int j = tid; j < DK; j += NT) {
@@ -728,62 +794,56 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     auto gval = [&](int r, int j) { return KDA ? sGg[r][j] : sg[r]; };
     auto mval = [&](int j) { return KDA ? sm[j] : sm[0]; };
     auto glast = [&](int j) { return KDA ? sgl[j] : sgl[0]; };
-    if (tid < DK) {
-        float s = 0.f;
-        for (int ig = 0; ig < RS; ++ig) s += sRed[ig][tid];
-        sdgc[tid] = s * rec[R::D + tid];
-    }
     for (int e = tid; e < C * DK; e += NT) {
         const int r = e / DK, j = e % DK;
         sX1[r][j] = sX2[r][j] * fexp(gval(r, j));
     }
     __syncthreads();
 
-    // Phases over C x d_v tiles: wave w takes (rt, it0) and, when it exists,
-    // (rt, it0 + NW / 2), rt = w & 1, it0 = w >> 1, together (the two share
-    // their A rows).
-    constexpr int HW = NW / 2;
-    const int nvt = DV / 16, rt_v = w & 1, it0 = w >> 1, it1 = it0 + HW < nvt ? it0 + HW : it0;
-    const bool has_v = it0 < nvt, has_v1 = it0 + HW < nvt;
+    // Phases over C x d_v tiles: wave w takes value tile w (16 value rows)
+    // and both row tiles, so each state row is read from memory once.
+    const int nvt = DV / 16;
+    const bool has_v = w < nvt;
     // ---- Y = V - (K e^g) S0^T
     if (has_v) {
         f32x4 acc[2] = {zero4(), zero4()};
-        tile_mma_nt<DK, 2>(acc, DK, [&](int, int mi, int kb, int lk) { return lds4(&sX1[16 * rt_v + mi][kb + lk]); },
-                           [&](int q, int ni, int kb, int lk) {
-                               return bload4(rS0, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
+        tile_mma_nt<DK, 2>(acc, DK, [&](int q, int mi, int kb, int lk) { return lds4(&sX1[16 * q + mi][kb + lk]); },
+                           [&](int, int ni, int kb, int lk) {
+                               return bload4(rS0, ((16 * w + ni) * DK + lk) * 4, kb * 4);
                            });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sB1[16 * rt_v + 4 * lq + i][16 * it0 + lr] -= acc[0][i];
-            if (has_v1) sB1[16 * rt_v + 4 * lq + i][16 * it1 + lr] -= acc[1][i];
-        }
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sB1[16 * q + 4 * lq + i][16 * w + lr] -= acc[q][i];
     }
     __syncthreads();
-    // ---- U = T diag(b) Y;  dU = M^T dO' + K_end dS^T
+    // ---- U = T diag(b) Y;  dU = M^T dO' (then + K_end dS^T below);
+    //      K_end = K e^{g_C - g} built in place of K e^g (no longer read)
+    f32x4 u[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
     if (has_v) {
-        f32x4 u[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
-        tile_mma_n<C, 2>(u, C, [&](int, int mi, int kb, int lk) { return sT[16 * rt_v + mi][kb + lk]; },
-                         [&](int q, int kb, int lk, int ni) {
-                             return sb[kb + lk] * sB1[kb + lk][16 * (q ? it1 : it0) + ni];
-                         });
-        tile_mma_n<C, 2>(du, C, [&](int, int mi, int kb, int lk) { return sM[kb + lk][16 * rt_v + mi]; },
-                         [&](int q, int kb, int lk, int ni) { return sB4[kb + lk][16 * (q ? it1 : it0) + ni]; });
-        tile_mma_nt<DK, 2>(du, DK, [&](int, int mi, int kb, int lk) {
-                               return bload4(rRec, (R::KE + (16 * rt_v + mi) * DK + lk) * 4, kb * 4);
-                           },
-                           [&](int q, int ni, int kb, int lk) {
-                               return bload4(rdS, ((16 * (q ? it1 : it0) + ni) * DK + lk) * 4, kb * 4);
+        tile_mma_n<C, 2>(u, C, [&](int q, int mi, int kb, int lk) { return sT[16 * q + mi][kb + lk]; },
+                         [&](int, int kb, int lk, int ni) { return sb[kb + lk] * sB1[kb + lk][16 * w + ni]; });
+        tile_mma_n<C, 2>(du, C, [&](int q, int mi, int kb, int lk) { return sM[kb + lk][16 * q + mi]; },
+                         [&](int, int kb, int lk, int ni) { return sB4[kb + lk][16 * w + ni]; });
+    }
+    for (int e = tid; e < C * DK; e += NT) {
+        const int r = e / DK, j = e % DK;
+        sX1[r][j] = sX2[r][j] * fexp(glast(j) - gval(r, j));
+    }
+    __syncthreads();
+    if (has_v) {
+        tile_mma_nt<DK, 2>(du, DK, [&](int q, int mi, int kb, int lk) { return lds4(&sX1[16 * q + mi][kb + lk]); },
+                           [&](int, int ni, int kb, int lk) {
+                               return bload4(rdS, ((16 * w + ni) * DK + lk) * 4, kb * 4);
                            });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * rt_v + 4 * lq + i;
-            sB2[r][16 * it0 + lr] = u[0][i];
-            sB3[r][16 * it0 + lr] = du[0][i];
-            if (has_v1) {
-                sB2[r][16 * it1 + lr] = u[1][i];
-                sB3[r][16 * it1 + lr] = du[1][i];
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * q + 4 * lq + i;
+                sB2[r][16 * w + lr] = u[q][i];
+                sB3[r][16 * w + lr] = du[q][i];
             }
-        }
     }
     __syncthreads();
     // ---- dT = dU (diag(b) Y)^T;  Z = T^T dU (kept in registers);  d beta (value part)
@@ -890,75 +950,114 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         }
     }
     __syncthreads();
-    // ---- per (row, key channel): dq, dk and the log-decay gradient dg
-    //      (one output tile at a time: each holds seven products' operands)
-#pragma unroll 1
-    for (int u = 0; u < UK; ++u) {
-        const int t = w + NW * u;
-        if (t >= ntk) continue;
-        const int rt = t & 1, jt = t >> 1;
-        const int j = 16 * jt + lr;
-        // the three products with the states (dO' S0, dY S0, U dS: S0 read once)
-        // (A rows contiguous along k: one 16-byte LDS read per four steps; the
-        // states' rows run along j, so their four k come from four loads)
-        f32x4 st[3] = {zero4(), zero4(), zero4()};
-        tile_mma_nt<128, 3>(st, DV, [&](int q, int mi, int kb, int lk) {
-                                return lds4(q == 0 ? &sB4[16 * rt + mi][kb + lk]
-                                          : q == 1 ? &sB3[16 * rt + mi][kb + lk] : &sB2[16 * rt + mi][kb + lk]);
-                            },
-                            [&](int q, int ni, int kb, int lk) {
-                                f32x4 v;
+    // ---- per (row, key channel): dq, dk and the log-decay gradient dg.
+    //      Wave w takes key tile w and both row tiles, so each state column is
+    //      read once; the same values give the column sums of dS o S0 (the
+    //      decay's share of the outgoing gradient).
+    if (w < DK / 16) {
+        const int jt = w, j = 16 * jt + lr;
+        // the three products with the states, dO' S0, dY S0 and U dS, as
+        // split bf16 products over blocks of 32 value rows; lane group lq
+        // takes rows i = kb + 4 lq + t and kb + 16 + 4 lq + t (t < 4).  The
+        // states' rows run along j, so a lane's rows come from eight loads
+        // per state, fetched one block ahead.
+        f32x4 st[2][3];
 #pragma unroll
-                                for (int t = 0; t < 4; ++t)
-                                    v[t] = bload(q < 2 ? rS0 : rdS, (lk * DK + 16 * jt + ni) * 4, (kb + t) * DK * 4);
-                                return v;
-                            });
-        // the chunk-local ones: dM Khs, dA Khs, dM^T Qts + dA^T Kts
-        f32x4 gm[4] = {zero4(), zero4(), zero4(), zero4()};
-        tile_mma_n<C, 4>(gm, C, [&](int q, int mi, int kb, int lk) {
-                             const int kk = kb + lk;
-                             return q == 0 ? sdM[16 * rt + mi][kk] : q == 1 ? sdA[16 * rt + mi][kk]
-                                  : q == 2 ? sdM[kk][16 * rt + mi] : sdA[kk][16 * rt + mi];
-                         },
-                         [&](int q, int kb, int lk, int ni) {
-                             const int kk = kb + lk;
-                             return q < 2 ? sX2[kk][16 * jt + ni] : q == 2 ? sB1[kk][16 * jt + ni] : sX1[kk][16 * jt + ni];
-                         });
-        const f32x4 dq0 = st[0], dy0 = st[1], uds = st[2], dmk = gm[0], dak = gm[1];
-        f32x4 tq;
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tq[i] = gm[2][i] + gm[3][i];
-        float colk = 0.f;
-        float rowg[4];
+            for (int q = 0; q < 3; ++q) st[rt][q] = zero4();
+        float cs = 0.f;
+        f32x4 sa[2][2], sd[2][2];   // [buffer][half]: S0 and dS values of one block
+        auto gather = [&](int kb, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * rt + 4 * lq + i;
-            const float g = gval(r, j), m = mval(j);
-            const float eg = fexp(g), egm = fexp(g - m), emg = fexp(m - g), egc = fexp(glast(j) - g);
-            const float dQ = dq0[i] * eg + dmk[i] * egm;
-            const float gk1 = -dy0[i] * eg + dak[i] * egm;
-            const float gk2 = tq[i] * emg;
-            const float gk3 = uds[i] * egc;
-            const long t = L.tok0 + min(r, L.len - 1), o = (t * H + h) * DK + j;
-            const long oq = (t * p.Hk + hq) * DK + j;
-            const float kk = r < L.len ? ld1(k + oq) : 0.f, qq = r < L.len ? ld1(q + oq) : 0.f;
-            if (r < L.len) {
-                p.dq[o] = dQ;
-                p.dk[o] = gk1 + gk2 + gk3;
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int lane_bytes = ((4 * lq + t) * DK + j) * 4, ub = (kb + 16 * hf) * DK * 4;
+                    sa[buf][hf][t] = bload(rS0, lane_bytes, ub);
+                    sd[buf][hf][t] = bload(rdS, lane_bytes, ub);
+                }
+        };
+        gather(0, 0);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int kb = 32 * blk, buf = blk & 1;
+            if (kb < DV) {                      // DV (a multiple of 32) is wave-uniform
+                if (blk + 1 < 4 && kb + 32 < DV) gather(kb + 32, buf ^ 1);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) cs += sa[buf][hf][t] * sd[buf][hf][t];
+                bf16x8 s0h, s0l, dsh, dsl;
+                split8(sa[buf][0], sa[buf][1], s0h, s0l);
+                split8(sd[buf][0], sd[buf][1], dsh, dsl);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const int r = 16 * rt + lr, c0 = kb + 4 * lq, c1 = kb + 16 + 4 * lq;
+                    bf16x8 ah, al;
+                    split8(lds4(&sB4[r][c0]), lds4(&sB4[r][c1]), ah, al);
+                    st[rt][0] = mfma_split(ah, al, s0h, s0l, st[rt][0]);
+                    split8(lds4(&sB3[r][c0]), lds4(&sB3[r][c1]), ah, al);
+                    st[rt][1] = mfma_split(ah, al, s0h, s0l, st[rt][1]);
+                    split8(lds4(&sB2[r][c0]), lds4(&sB2[r][c1]), ah, al);
+                    st[rt][2] = mfma_split(ah, al, dsh, dsl, st[rt][2]);
+                }
             }
-            const float dg = kk * (gk1 - gk2 - gk3) + qq * dQ;
-            colk += gk3 * kk;
-            if (KDA) sGg[r][j] = dg;
-            rowg[i] = dg;
+            __builtin_amdgcn_sched_barrier(0);
         }
-        colk += __shfl_xor(colk, 16);
-        colk += __shfl_xor(colk, 32);
-        if (lq == 0) sPc[rt][j] = colk;
-        if (!KDA) {
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+        if (lq == 0) sdgc[j] = cs * rec[R::D + j];
+#pragma unroll 1
+        for (int rt = 0; rt < 2; ++rt) {
+            // the chunk-local products: dM Khs, dA Khs, dM^T Qts + dA^T Kts
+            f32x4 gm[4] = {zero4(), zero4(), zero4(), zero4()};
+            tile_mma_n<C, 4>(gm, C, [&](int q, int mi, int kb, int lk) {
+                                 const int kk = kb + lk;
+                                 return q == 0 ? sdM[16 * rt + mi][kk] : q == 1 ? sdA[16 * rt + mi][kk]
+                                      : q == 2 ? sdM[kk][16 * rt + mi] : sdA[kk][16 * rt + mi];
+                             },
+                             [&](int q, int kb, int lk, int ni) {
+                                 const int kk = kb + lk;
+                                 return q < 2 ? sX2[kk][16 * jt + ni] : q == 2 ? sB1[kk][16 * jt + ni] : sX1[kk][16 * jt + ni];
+                             });
+            const f32x4 dq0 = rt ? st[1][0] : st[0][0], dy0 = rt ? st[1][1] : st[0][1], uds = rt ? st[1][2] : st[0][2];
+            const f32x4 dmk = gm[0], dak = gm[1];
+            f32x4 tq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tq[i] = gm[2][i] + gm[3][i];
+            float colk = 0.f;
+            float rowg[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float s = group_sum<16>(rowg[i]);
-                if (lr == 0) sPr[jt][16 * rt + 4 * lq + i] = s;
+                const int r = 16 * rt + 4 * lq + i;
+                const float g = gval(r, j), m = mval(j);
+                const float eg = fexp(g), egm = fexp(g - m), emg = fexp(m - g), egc = fexp(glast(j) - g);
+                const float dQ = dq0[i] * eg + dmk[i] * egm;
+                const float gk1 = -dy0[i] * eg + dak[i] * egm;
+                const float gk2 = tq[i] * emg;
+                const float gk3 = uds[i] * egc;
+                const long t = L.tok0 + min(r, L.len - 1), o = (t * H + h) * DK + j;
+                const long oq = (t * p.Hk + hq) * DK + j;
+                const float kk = r < L.len ? ld1(k + oq) : 0.f, qq = r < L.len ? ld1(q + oq) : 0.f;
+                if (r < L.len) {
+                    p.dq[o] = dQ;
+                    p.dk[o] = gk1 + gk2 + gk3;
+                }
+                const float dg = kk * (gk1 - gk2 - gk3) + qq * dQ;
+                colk += gk3 * kk;
+                if (KDA) sGg[r][j] = dg;
+                rowg[i] = dg;
+            }
+            colk += __shfl_xor(colk, 16);
+            colk += __shfl_xor(colk, 32);
+            if (lq == 0) sPc[rt][j] = colk;
+            if (!KDA) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float s = group_sum<16>(rowg[i]);
+                    if (lr == 0) sPr[jt][16 * rt + 4 * lq + i] = s;
+                }
             }
         }
     }
