@@ -144,23 +144,35 @@ __device__ __forceinline__ void tile_mma_n(f32x4 (&acc)[NQ], int K, FA fa, FB fb
 // A product takes hi*hi + hi*lo + lo*hi on the 16x16x32 bf16 MFMA with fp32
 // accumulation; the dropped lo*lo term and the rounding of lo are below
 // 2^-16 of each operand product.
-__device__ __forceinline__ void split4(const f32x4 v, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 h = (__bf16)v[i];
-        hi[i] = h;
-        lo[i] = (__bf16)(v[i] - (float)h);
-    }
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+// two values at once (one packed conversion each for hi and lo): the
+// returned words hold x0 in their low and x1 in their high half
+__device__ __forceinline__ void split2(float x0, float x1, unsigned &hi, unsigned &lo) {
+    const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2v){x0, x1}, bf16x2v));
+    const float h0 = __builtin_bit_cast(float, h << 16), h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+    hi = h;
+    lo = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2v){x0 - h0, x1 - h1}, bf16x2v));
 }
-// the B operand of one 32-k step from two accumulator tiles (k = 4 lq + i of
-// tile a, then of tile b)
+__device__ __forceinline__ void split4(const f32x4 v, bf16x4 &hi, bf16x4 &lo) {
+    unsigned h0, h1, l0, l1;
+    split2(v[0], v[1], h0, l0);
+    split2(v[2], v[3], h1, l1);
+    hi = __builtin_bit_cast(bf16x4, (u32x2){h0, h1});
+    lo = __builtin_bit_cast(bf16x4, (u32x2){l0, l1});
+}
+// the operand of one 32-k MFMA step from two accumulator tiles (k = 4 lq + i
+// of tile a, then of tile b)
 __device__ __forceinline__ void split8(const f32x4 a, const f32x4 b, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 ha = (__bf16)a[i], hb = (__bf16)b[i];
-        hi[i] = ha, hi[4 + i] = hb;
-        lo[i] = (__bf16)(a[i] - (float)ha), lo[4 + i] = (__bf16)(b[i] - (float)hb);
-    }
+    unsigned h0, h1, h2, h3, l0, l1, l2, l3;
+    split2(a[0], a[1], h0, l0);
+    split2(a[2], a[3], h1, l1);
+    split2(b[0], b[1], h2, l2);
+    split2(b[2], b[3], h3, l3);
+    hi = __builtin_bit_cast(bf16x8, (u32x4){h0, h1, h2, h3});
+    lo = __builtin_bit_cast(bf16x8, (u32x4){l0, l1, l2, l3});
 }
 __device__ __forceinline__ f32x4 mfma_split(const bf16x8 &ah, const bf16x8 &al, const bf16x8 &bh,
                                             const bf16x8 &bl, f32x4 acc) {
@@ -686,6 +698,34 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half)
         scan_body<DK, NW, true, IT, GT>(p, blockIdx.x - half, lds);
 }
 
+// Scans over the 32 rows of one column, four adjacent lanes per column and
+// eight rows per lane.  seg_scan4: the lane's own running sums over its rows
+// of x[.][j] (prefix, or suffix when rev) into v; returns its rows' total.
+// scan4_offsets: what the other lanes of the column add (the totals of the
+// rows before the lane's, or after them when rev) and the column total.
+template <class X>
+__device__ __forceinline__ float seg_scan4(X &x, int qd, int j, float (&v)[kBC / 4], bool rev) {
+    constexpr int RQ = kBC / 4;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < RQ; ++i) {
+        const int rr = rev ? RQ - 1 - i : i;
+        s += x[qd * RQ + rr][j];
+        v[rr] = s;
+    }
+    return s;
+}
+__device__ __forceinline__ void scan4_offsets(float tot, int qd, bool rev, float &other, float &total) {
+    // inclusive scan of the four totals in the lane order (or reversed)
+    const float a1 = rev ? __shfl_down(tot, 1, 4) : __shfl_up(tot, 1, 4);
+    const float s1 = tot + ((rev ? qd < 3 : qd > 0) ? a1 : 0.f);
+    const float a2 = rev ? __shfl_down(s1, 2, 4) : __shfl_up(s1, 2, 4);
+    const float incl = s1 + ((rev ? qd < 2 : qd > 1) ? a2 : 0.f);
+    const float ex = rev ? __shfl_down(incl, 1, 4) : __shfl_up(incl, 1, 4);
+    other = (rev ? qd < 3 : qd > 0) ? ex : 0.f;
+    total = __shfl(incl, rev ? 0 : 3, 4);
+}
+
 // ---------------------------------------------------------------------------
 // Input gradients of one (chunk, head) from its incoming state S0 and its
 // outgoing state gradient dS.  Eight waves; C x n outputs are 16x16 tiles
@@ -723,13 +763,14 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     constexpr int NKL = div_up(C * DK / 4, NT), NVL = div_up(C * 128 / 4, NT), NTL = C * C / NT;
     static_assert(NTL >= 1 && C * C % NT == 0, "load tiling");
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 kv[NKL], gv[NKL], vv[NVL], dd[NVL];
+    float4 kv[NKL], qv[NKL], gv[NKL], vv[NVL], dd[NVL];
     float tv[NTL], mv[NTL];
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
         const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
         const long t = L.tok0 + min(r, L.len - 1);
         kv[u] = load4(k + (t * p.Hk + hq) * DK + j);
+        qv[u] = load4(q + (t * p.Hk + hq) * DK + j);
         gv[u] = KDA ? gate4<GT>(p.log_alpha, (t * H + h) * DK + j) : z4;
     }
 #pragma unroll
@@ -777,18 +818,35 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         if (!KDA) sg[tid] = tid < L.len ? gg : 0.f;
     }
     __syncthreads();
+    // inclusive cumulative sums of the log decay over the chunk's rows
     if (KDA) {
-        for (int j = tid; j < DK; j += NT) {
-            float s = 0.f;
-            for (int r = 0; r < C; ++r) sGg[r][j] = (s += sGg[r][j]);
-            sm[j] = 0.5f * (sGg[0][j] + s);
-            sgl[j] = s;
+        // four adjacent lanes per channel, eight rows each
+        for (int e = tid; e < 4 * DK; e += NT) {
+            const int j = e >> 2, qd = e & 3;
+            float v[C / 4];
+            const float tot = seg_scan4(sGg, qd, j, v, false);
+            float before, total;
+            scan4_offsets(tot, qd, false, before, total);
+#pragma unroll
+            for (int rr = 0; rr < C / 4; ++rr) sGg[qd * (C / 4) + rr][j] = before + v[rr];
+            if (qd == 0) {
+                sm[j] = 0.5f * (v[0] + total);
+                sgl[j] = total;
+            }
         }
-    } else if (tid == 0) {
-        float s = 0.f;
-        for (int r = 0; r < C; ++r) sg[r] = (s += sg[r]);
-        sm[0] = 0.5f * (sg[0] + s);
-        sgl[0] = s;
+    } else if (w == 0) {
+        float g = l < C ? sg[l] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            const float t = __shfl_up(g, o, 32);
+            if ((l & 31) >= o) g += t;
+        }
+        const float first = __shfl(g, 0), total = __shfl(g, C - 1);
+        if (l < C) sg[l] = g;
+        if (l == 0) {
+            sm[0] = 0.5f * (first + total);
+            sgl[0] = total;
+        }
     }
     __syncthreads();
     auto gval = [&](int r, int j) { return KDA ? sGg[r][j] : sg[r]; };
@@ -903,14 +961,16 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         sX1[r][j] = kk * fexp(g - m);
         sX2[r][j] = kk * fexp(m - g);
     }
-    for (int e = tid; e < C * DK / 4; e += NT) {
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {               // q as loaded at the start
+        const int e = tid + NT * u;
+        if (e >= C * DK / 4) continue;
         const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        const float4 qv = r < L.len ? load4(q + ((L.tok0 + min(r, L.len - 1)) * p.Hk + hq) * DK + j)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-        sB1[r][j] = qv.x * fexp(gval(r, j) - mval(j));
-        sB1[r][j + 1] = qv.y * fexp(gval(r, j + 1) - mval(j + 1));
-        sB1[r][j + 2] = qv.z * fexp(gval(r, j + 2) - mval(j + 2));
-        sB1[r][j + 3] = qv.w * fexp(gval(r, j + 3) - mval(j + 3));
+        const float4 q4 = r < L.len ? qv[u] : z4;
+        sB1[r][j] = q4.x * fexp(gval(r, j) - mval(j));
+        sB1[r][j + 1] = q4.y * fexp(gval(r, j + 1) - mval(j + 1));
+        sB1[r][j + 2] = q4.z * fexp(gval(r, j + 2) - mval(j + 2));
+        sB1[r][j + 3] = q4.w * fexp(gval(r, j + 3) - mval(j + 3));
     }
     if (tid < C) {
         float s = 0.f;
@@ -950,6 +1010,25 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         }
     }
     __syncthreads();
+    // ---- dO' (sB4), dY (sB3) and U (sB2) as split bf16 operands, in place:
+    //      each row's 528 bytes become [hi of its 128 values | lo | unused],
+    //      the value index permuted within blocks of 32 (kperm32).  One wave
+    //      converts a whole row (one read, then the writes), so no other wave
+    //      touches a row while it changes form.
+    static_assert(PV * 4 >= 2 * 128 * 2, "a row holds its split form");
+    for (int rr = w; rr < 3 * C; rr += NW) {
+        float *row = rr < C ? sB4[rr] : rr < 2 * C ? sB3[rr - C] : sB2[rr - 2 * C];
+        const float2 x = *reinterpret_cast<const float2 *>(row + 2 * l);
+        unsigned hu, lu;
+        split2(x.x, x.y, hu, lu);
+        const int pos = (2 * l & ~31) + kperm32(2 * l);
+        __bf16 *rb = reinterpret_cast<__bf16 *>(row);
+        *reinterpret_cast<unsigned *>(rb + pos) = hu;
+        *reinterpret_cast<unsigned *>(rb + 128 + pos) = lu;
+    }
+    __syncthreads();
+    auto plane = [&](float (*buf)[PV], int r) { return reinterpret_cast<const __bf16 *>(buf[r]); };
+
     // ---- per (row, key channel): dq, dk and the log-decay gradient dg.
     //      Wave w takes key tile w and both row tiles, so each state column is
     //      read once; the same values give the column sums of dS o S0 (the
@@ -993,14 +1072,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
                 split8(sd[buf][0], sd[buf][1], dsh, dsl);
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
-                    const int r = 16 * rt + lr, c0 = kb + 4 * lq, c1 = kb + 16 + 4 * lq;
-                    bf16x8 ah, al;
-                    split8(lds4(&sB4[r][c0]), lds4(&sB4[r][c1]), ah, al);
-                    st[rt][0] = mfma_split(ah, al, s0h, s0l, st[rt][0]);
-                    split8(lds4(&sB3[r][c0]), lds4(&sB3[r][c1]), ah, al);
-                    st[rt][1] = mfma_split(ah, al, s0h, s0l, st[rt][1]);
-                    split8(lds4(&sB2[r][c0]), lds4(&sB2[r][c1]), ah, al);
-                    st[rt][2] = mfma_split(ah, al, dsh, dsl, st[rt][2]);
+                    const int r = 16 * rt + lr, c = kb + 8 * lq;
+                    const __bf16 *a0 = plane(sB4, r), *a1 = plane(sB3, r), *a2 = plane(sB2, r);
+                    st[rt][0] = mfma_split(lds8(a0 + c), lds8(a0 + 128 + c), s0h, s0l, st[rt][0]);
+                    st[rt][1] = mfma_split(lds8(a1 + c), lds8(a1 + 128 + c), s0h, s0l, st[rt][1]);
+                    st[rt][2] = mfma_split(lds8(a2 + c), lds8(a2 + 128 + c), dsh, dsl, st[rt][2]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1038,8 +1114,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
                 const float gk2 = tq[i] * emg;
                 const float gk3 = uds[i] * egc;
                 const long t = L.tok0 + min(r, L.len - 1), o = (t * H + h) * DK + j;
-                const long oq = (t * p.Hk + hq) * DK + j;
-                const float kk = r < L.len ? ld1(k + oq) : 0.f, qq = r < L.len ? ld1(q + oq) : 0.f;
+                // raw k and q from their shifted copies in LDS (zero on padding rows)
+                const float kk = sX1[r][j] * emg, qq = sB1[r][j] * emg;
                 if (r < L.len) {
                     p.dq[o] = dQ;
                     p.dk[o] = gk1 + gk2 + gk3;
@@ -1065,27 +1141,35 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     // ---- log-decay gradient: reverse cumulative sum of dg, plus the
     //      chunk-end terms (through e^{g_C}) on every row; d beta
     if (KDA) {
-        for (int j = tid; j < DK; j += NT) {
-            float run = sdgc[j] + sPc[0][j] + sPc[1][j];
-            for (int r = C - 1; r >= 0; --r) {
-                run += sGg[r][j];
-                if (r < L.len) p.dla[((L.tok0 + r) * H + h) * DK + j] = run;
+        // four adjacent lanes per channel, eight rows each (suffix sums)
+        for (int e = tid; e < 4 * DK; e += NT) {
+            const int j = e >> 2, qd = e & 3;
+            float v[C / 4];
+            const float tot = seg_scan4(sGg, qd, j, v, true);
+            float after, total;
+            scan4_offsets(tot, qd, true, after, total);
+            const float base = sdgc[j] + sPc[0][j] + sPc[1][j] + after;
+#pragma unroll
+            for (int rr = 0; rr < C / 4; ++rr) {
+                const int r = qd * (C / 4) + rr;
+                if (r < L.len) p.dla[((L.tok0 + r) * H + h) * DK + j] = base + v[rr];
             }
         }
     } else if (w == 0) {
-        // one head-wide decay per row: sum the channel terms, then scan rows
+        // one head-wide decay per row: sum the channel terms, then a suffix
+        // scan over the rows (row r on lane r)
         float gc = 0.f;
         for (int j = l; j < DK; j += 64) gc += sdgc[j] + sPc[0][j] + sPc[1][j];
         for (int m = 32; m >= 1; m >>= 1) gc += __shfl_xor(gc, m);
-        if (l == 0) {
-            float run = gc;
-            for (int r = C - 1; r >= 0; --r) {
-                float d = 0.f;
-                for (int jt = 0; jt < DK / 16; ++jt) d += sPr[jt][r];
-                run += d;
-                if (r < L.len) p.dla[(L.tok0 + r) * H + h] = run;
-            }
+        float d = 0.f;
+        if (l < C)
+            for (int jt = 0; jt < DK / 16; ++jt) d += sPr[jt][l];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            const float t = __shfl_down(d, o, 32);
+            if ((l & 31) + o < 32) d += t;
         }
+        if (l < L.len) p.dla[(L.tok0 + l) * H + h] = gc + d;
     }
     if (tid < L.len) p.dbeta[(L.tok0 + tid) * H + h] = sdb[tid] + sPb2[0][tid] + sPb2[1][tid];
 }
