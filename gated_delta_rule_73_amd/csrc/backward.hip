@@ -284,6 +284,34 @@ __device__ __forceinline__ ChunkLoc locate(const BwdKArgs &p, long rc) {
     return L;
 }
 
+// Scans over the 32 rows of one column, four adjacent lanes per column and
+// eight rows per lane.  seg_scan4: the lane's own running sums over its rows
+// of x[.][j] (prefix, or suffix when rev) into v; returns its rows' total.
+// scan4_offsets: what the other lanes of the column add (the totals of the
+// rows before the lane's, or after them when rev) and the column total.
+template <class X>
+__device__ __forceinline__ float seg_scan4(X &x, int qd, int j, float (&v)[kBC / 4], bool rev) {
+    constexpr int RQ = kBC / 4;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < RQ; ++i) {
+        const int rr = rev ? RQ - 1 - i : i;
+        s += x[qd * RQ + rr][j];
+        v[rr] = s;
+    }
+    return s;
+}
+__device__ __forceinline__ void scan4_offsets(float tot, int qd, bool rev, float &other, float &total) {
+    // inclusive scan of the four totals in the lane order (or reversed)
+    const float a1 = rev ? __shfl_down(tot, 1, 4) : __shfl_up(tot, 1, 4);
+    const float s1 = tot + ((rev ? qd < 3 : qd > 0) ? a1 : 0.f);
+    const float a2 = rev ? __shfl_down(s1, 2, 4) : __shfl_up(s1, 2, 4);
+    const float incl = s1 + ((rev ? qd < 2 : qd > 1) ? a2 : 0.f);
+    const float ex = rev ? __shfl_down(incl, 1, 4) : __shfl_up(incl, 1, 4);
+    other = (rev ? qd < 3 : qd > 0) ? ex : 0.f;
+    total = __shfl(incl, rev ? 0 : 3, 4);
+}
+
 // ---------------------------------------------------------------------------
 // Chunk records.
 template <int DK, bool KDA, typename IT, typename GT>
@@ -300,39 +328,68 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
     const IT *q = static_cast<const IT *>(p.q), *k = static_cast<const IT *>(p.k);
     float *rec = p.rec + (rc * H + h) * p.rec_stride;
 
-    for (int e = tid; e < C * DK / 4; e += NT) {
-        const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        const bool in = r < L.len;                 // padding rows: zeros (clamped loads, no branch)
+    // every load first (clamped rows, all in flight together), then the LDS
+    // stores; padding rows are zeroed by a select, not a branch
+    constexpr int NL4 = div_up(C * DK / 4, NT);
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 kv[NL4], qv[NL4], gv[NL4];
+#pragma unroll
+    for (int u = 0; u < NL4; ++u) {
+        const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
         const long t = L.tok0 + min(r, L.len - 1);
         const long o = (t * H + h) * DK + j, oq = (t * p.Hk + h / p.G) * DK + j;
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 kv = in ? load4(k + oq) : z4, qv = in ? load4(q + oq) : z4;
-        const float4 gv = KDA && in ? gate4<GT>(p.log_alpha, o) : z4;
-        sK[r][j] = kv.x, sK[r][j + 1] = kv.y, sK[r][j + 2] = kv.z, sK[r][j + 3] = kv.w;
-        sQ[r][j] = qv.x, sQ[r][j + 1] = qv.y, sQ[r][j + 2] = qv.z, sQ[r][j + 3] = qv.w;
-        if (KDA) sX[r][j] = gv.x, sX[r][j + 1] = gv.y, sX[r][j + 2] = gv.z, sX[r][j + 3] = gv.w;
+        kv[u] = load4(k + oq);
+        qv[u] = load4(q + oq);
+        gv[u] = KDA ? gate4<GT>(p.log_alpha, o) : z4;
+    }
+    const long ob = (L.tok0 + min(tid & (C - 1), L.len - 1)) * H + h;
+    const float bb = gate1<GT>(p.beta, ob), gg = KDA ? 0.f : gate1<GT>(p.log_alpha, ob);
+#pragma unroll
+    for (int u = 0; u < NL4; ++u) {
+        const int e = tid + NT * u;
+        if (e >= C * DK / 4) continue;
+        const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
+        const bool in = r < L.len;
+        const float4 k4 = in ? kv[u] : z4, q4 = in ? qv[u] : z4, g4 = in ? gv[u] : z4;
+        sK[r][j] = k4.x, sK[r][j + 1] = k4.y, sK[r][j + 2] = k4.z, sK[r][j + 3] = k4.w;
+        sQ[r][j] = q4.x, sQ[r][j + 1] = q4.y, sQ[r][j + 2] = q4.z, sQ[r][j + 3] = q4.w;
+        if (KDA) sX[r][j] = g4.x, sX[r][j + 1] = g4.y, sX[r][j + 2] = g4.z, sX[r][j + 3] = g4.w;
     }
     if (tid < C) {
         const bool in = tid < L.len;
-        const long o = (L.tok0 + min(tid, L.len - 1)) * H + h;
-        const float bb = gate1<GT>(p.beta, o), gg = KDA ? 0.f : gate1<GT>(p.log_alpha, o);
         sb[tid] = in ? bb : 0.f;
         if (!KDA) sg[tid] = in ? gg : 0.f;
     }
     __syncthreads();
     // inclusive cumulative log-decay (padding rows add zero)
     if (KDA) {
-        for (int j = tid; j < DK; j += NT) {
-            float s = 0.f;
-            for (int r = 0; r < C; ++r) sX[r][j] = (s += sX[r][j]);
-            sm[j] = 0.5f * (sX[0][j] + s);
-            sgl[j] = s;
+        // four adjacent lanes per channel, eight rows each
+        for (int e = tid; e < 4 * DK; e += NT) {
+            const int j = e >> 2, qd = e & 3;
+            float v[C / 4];
+            const float tot = seg_scan4(sX, qd, j, v, false);
+            float before, total;
+            scan4_offsets(tot, qd, false, before, total);
+#pragma unroll
+            for (int rr = 0; rr < C / 4; ++rr) sX[qd * (C / 4) + rr][j] = before + v[rr];
+            if (qd == 0) {
+                sm[j] = 0.5f * (v[0] + total);
+                sgl[j] = total;
+            }
         }
-    } else if (tid == 0) {
-        float s = 0.f;
-        for (int r = 0; r < C; ++r) sg[r] = (s += sg[r]);
-        sm[0] = 0.5f * (sg[0] + s);
-        sgl[0] = s;
+    } else if (tid < 64) {
+        float g = tid < C ? sg[tid] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            const float t = __shfl_up(g, o, 32);
+            if ((tid & 31) >= o) g += t;
+        }
+        const float first = __shfl(g, 0), total = __shfl(g, C - 1);
+        if (tid < C) sg[tid] = g;
+        if (tid == 0) {
+            sm[0] = 0.5f * (first + total);
+            sgl[0] = total;
+        }
     }
     __syncthreads();
     for (int e = tid; e < C * DK; e += NT) {
@@ -696,34 +753,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half)
         scan_body<DK, NW, false, IT, GT>(p, blockIdx.x, lds);
     else
         scan_body<DK, NW, true, IT, GT>(p, blockIdx.x - half, lds);
-}
-
-// Scans over the 32 rows of one column, four adjacent lanes per column and
-// eight rows per lane.  seg_scan4: the lane's own running sums over its rows
-// of x[.][j] (prefix, or suffix when rev) into v; returns its rows' total.
-// scan4_offsets: what the other lanes of the column add (the totals of the
-// rows before the lane's, or after them when rev) and the column total.
-template <class X>
-__device__ __forceinline__ float seg_scan4(X &x, int qd, int j, float (&v)[kBC / 4], bool rev) {
-    constexpr int RQ = kBC / 4;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < RQ; ++i) {
-        const int rr = rev ? RQ - 1 - i : i;
-        s += x[qd * RQ + rr][j];
-        v[rr] = s;
-    }
-    return s;
-}
-__device__ __forceinline__ void scan4_offsets(float tot, int qd, bool rev, float &other, float &total) {
-    // inclusive scan of the four totals in the lane order (or reversed)
-    const float a1 = rev ? __shfl_down(tot, 1, 4) : __shfl_up(tot, 1, 4);
-    const float s1 = tot + ((rev ? qd < 3 : qd > 0) ? a1 : 0.f);
-    const float a2 = rev ? __shfl_down(s1, 2, 4) : __shfl_up(s1, 2, 4);
-    const float incl = s1 + ((rev ? qd < 2 : qd > 1) ? a2 : 0.f);
-    const float ex = rev ? __shfl_down(incl, 1, 4) : __shfl_up(incl, 1, 4);
-    other = (rev ? qd < 3 : qd > 0) ? ex : 0.f;
-    total = __shfl(incl, rev ? 0 : 3, 4);
 }
 
 // ---------------------------------------------------------------------------
