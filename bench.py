@@ -363,12 +363,15 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
             "workload": f"{name}: gradients of q, k, v, beta, log alpha and the initial state through the chunked "
                         f"prefill, B={B}, T={T}, H={H}" + (f" value heads sharing {Hk} q/k heads" if Hk != H else "")
                         + f", d={dk}, bf16 q/k/v, fp32 gates, d_out and d_final_state ~ N(0, 1), "
-                        f"{'per-channel' if kda else 'per-head'} decay, S0 given; fp32 arithmetic",
+                        f"{'per-channel' if kda else 'per-head'} decay, S0 given; fp32 accumulation, the large "
+                        f"products as split bf16 (hi/lo operands, three bf16 MFMAs each), the C x C ones in fp32",
             "calls": steps, "us_per_call": round(t * 1e6, 1), "us_median": round(med * 1e6, 1),
             "us_min": round(mn * 1e6, 1), "Mtok_s": round(B * T / t / 1e6, 3), "alg_bytes": by,
             "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
             "alg_flops": fl, "TFLOPs": round(fl / t / 1e12, 2),
-            "frac_of_fp32_mfma_peak": round(fl / t / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
+            "frac_of_fp32_mfma_peak": round(fl / t / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            # a split-bf16 product issues three bf16 MFMAs: its dense roof is a third of bf16's
+            "frac_of_split_bf16_peak": round(fl / t / 1e12 / (BF16_MFMA_PEAK_TFLOPS / 3), 4)}
         del bi, bc
         torch.cuda.empty_cache()
     return res

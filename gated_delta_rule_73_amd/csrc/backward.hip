@@ -19,7 +19,9 @@
 //     dS_prev = dS_C Diag(e^{g_C}) + dO'^T (Q e^g) + dU^T Wn
 // and each chunk's input gradients follow from its own S0 and dS_C.
 //
-// Three kernels, all in fp32 on the 16x16x4 fp32 MFMA:
+// Three kernels, fp32 data and accumulation; the products with a d_k or d_v
+// contraction run as split bf16 products (split8, mfma_split), the C x C ones
+// on the 16x16x4 fp32 MFMA:
 //   bwd_prep_kernel  one workgroup per (chunk, head): the chunk record
 //                    D = e^{g_C}, T, M, Wn, Q e^g, K_end (fp32, in HBM).
 //   bwd_scan_kernel  one workgroup per (sequence, head, 32 or 64 value rows),

@@ -349,8 +349,11 @@ const char *gdr_status_string(gdr_status status);
  * (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out, dq, dk and the states
  * 16-byte aligned; beta aligned to its element, log_alpha to four elements
  * for GDR_GATE_CHANNEL; the other gradients 4-byte.  No output may overlap an input, another output or the
- * workspace.  All arithmetic is fp32; every gradient element is written by
- * exactly one thread (no atomics), so results are bitwise reproducible.
+ * workspace.  Data and accumulation are fp32; the products with a head_dim
+ * contraction take their operands as bf16 hi + lo pairs (16 significant
+ * bits, relative error about 2^-16 per product).  Every gradient element is
+ * written by exactly one thread (no atomics), so results are bitwise
+ * reproducible.
  * Rows of padding and packed sequences of length zero are handled (an empty
  * sequence's d_initial_state is its d_final_state).  Enqueued on hip_stream;
  * returns GDR_SUCCESS or an error status (nothing enqueued on error).
