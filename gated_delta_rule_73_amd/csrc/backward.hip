@@ -760,7 +760,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half)
 // ---------------------------------------------------------------------------
 // Input gradients of one (chunk, head) from its incoming state S0 and its
 // outgoing state gradient dS.  Eight waves; C x n outputs are 16x16 tiles
-// (row tile rt, column tile) dealt round-robin to the waves.
+// (row tile rt, column tile).  The products with the states give a wave one
+// column tile and both row tiles (each state row or column is then read
+// once); the others deal the tiles round-robin to the waves.
 template <int DK, bool KDA, typename IT, typename GT>
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     constexpr int C = kBC, NT = kGradThreads, NW = NT / 64, PK = DK + 4, PV = 128 + 4, PB = PK > PV ? PK : PV;
