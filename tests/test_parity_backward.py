@@ -78,6 +78,24 @@ def test_backward_shapes(case, dtype):
     _check(inp, cot, f"{case} {dtype}")
 
 
+# Enough (sequence, head) units that the state scans take four waves (64 value
+# rows) per workgroup on a 256-CU device, at the small key widths the large
+# workloads do not reach.
+FOUR_WAVE_CASES = [
+    # dk, dv, H, T, gate, B
+    (32, 64, 72, 70, "channel", 1),
+    (64, 128, 40, 45, "head", 2),
+    (32, 128, 36, 33, "head", 2),
+]
+
+
+@pytest.mark.parametrize("case", FOUR_WAVE_CASES, ids=lambda c: f"dk{c[0]}-dv{c[1]}-H{c[2]}-T{c[3]}-{c[4]}-B{c[5]}")
+def test_backward_four_wave_scan_small_keys(case):
+    dk, dv, H, T, gate, B = case
+    inp, cot = _small(dk, dv, H, T, gate, torch.bfloat16, True, seed=3 * dk + T, B=B)
+    _check(inp, cot, f"four-wave scan {case}")
+
+
 @pytest.mark.parametrize("gate", ["head", "channel"])
 def test_backward_packed_with_empty_and_one_token_sequences(gate):
     """Packed sequences of 37, 0, 100, 1 and 64 tokens: ragged chunks, an empty
