@@ -51,10 +51,16 @@ constexpr int kBC = 32;                      // chunk length of the backward
 constexpr int kGradThreads = 512;            // 8 waves: two per SIMD (the LDS holds one workgroup)
 
 // Record of one (chunk, head), fp32: D[dk] | T[C][C] | M[C][C] | Wn[C][dk] |
-// Qg[C][dk] (Q e^g) | Ke[C][dk] (K e^{g_C - g}); stride from launch.h.
+// Qg[C][dk] (Q e^g) | Ke[C][dk] (K e^{g_C - g}) | G[C]; stride from launch.h.
+// With a per-head decay, Q e^g and K e^{g_C - g} are q and k scaled per row,
+// and G holds the rows' cumulative log decay.  When the four-wave state scan
+// runs (raw_qk), it stages q and k themselves, scaled as they reach LDS, and
+// Qg, Ke are not written: the scan's fetch, which bounds it, shrinks by a
+// third.  (With two-wave scans, whose chains are latency-bound, the scattered
+// q/k rows cost more than the bytes saved.)
 template <int DK> struct BRec {
     static constexpr int D = 0, T = DK, M = T + kBC * kBC, W = M + kBC * kBC, Q = W + kBC * DK,
-                         KE = Q + kBC * DK;
+                         KE = Q + kBC * DK, G = KE + kBC * DK;
 };
 
 struct BwdKArgs {
@@ -69,6 +75,7 @@ struct BwdKArgs {
     float *dq, *dk, *dv_out, *dbeta, *dla, *d_init;   // dq, dk: per value head ([.., H, dk])
     float *rec, *states, *dstates;
     long rec_stride;                          // floats per record
+    int raw_qk;                               // per-head decay, four-wave scans: see BRec
 };
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -401,14 +408,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
         // e^{g} and e^{g_C - g} are at most 1; e^{g - m} and its reciprocal stay
         // within e^{+-(g_first - g_last)/2}
         const float eg = fexp(g), egm = fexp(g - m), emg = 1.f / egm;
-        rec[R::Q + e] = qq * eg;
-        rec[R::KE + e] = kk * fexp(gl - g);
+        if (KDA || !p.raw_qk) {
+            rec[R::Q + e] = qq * eg;
+            rec[R::KE + e] = kk * fexp(gl - g);
+        }
         sK[r][j] = kk * egm;
         sKh[r][j] = kk * emg;
         sQ[r][j] = qq * egm;
         sX[r][j] = sb[r] * kk * eg;
     }
     for (int j = tid; j < DK; j += NT) rec[R::D + j] = fexp(KDA ? sgl[j] : sgl[0]);
+    if (!KDA && tid < C) rec[R::G + tid] = sg[tid];
     __syncthreads();
 
     const int w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -532,8 +542,9 @@ template <int DK, int NW> struct ScanLds {
     __align__(16) float D[2][DK];
 };
 
-template <int DK, int NW, bool BWD, typename IT, typename GT>
+template <int DK, int NW, bool BWD, bool KDA, typename IT, typename GT>
 __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<DK, NW> &lds) {
+    constexpr bool RAW = !KDA && NW == 4;     // q, k staged raw (BRec; the launch sets raw_qk to match)
     constexpr int C = kBC, NT = 64 * NW, ZW = 16 * NW, NB = DK / 32;
     // per thread: NE row pieces of E and NE column pieces of Bt (and Gt),
     // NL pieces of L, NZ column pieces of Zt; four values each
@@ -565,6 +576,8 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     }
     const int row = ZW * slice + 16 * w + lr;     // this lane's value row (as MFMA column)
     const IT *v = static_cast<const IT *>(p.v);
+    const IT *kin = static_cast<const IT *>(p.k), *qin = static_cast<const IT *>(p.q);
+    const int hq = h / p.G;
 
     // Thread-to-piece maps (element index e = tid + NT u):
     //  row pieces (E; forward L): four consecutive k of one row; eight
@@ -585,25 +598,41 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
 
     f32x4 rE[NE], rB[NE], rG[BWD ? NE : 1], rL[NL], rZ[NZ];
     float rD = 0.f;
+    // raw q, k: the fetched chunk's row log decays (lane l holds row l mod 32)
+    // and length, for scaling them in put
+    float rGv = 0.f;
+    int rClen = 0;
     auto fetch = [&](int s) {
         const int c = BWD ? nc - 1 - s : s;
         const long rc = rc0 + c, tok0 = tok_base + (long)c * C;
         const int clen = min(C, len - c * C);
         const float *rec = p.rec + (rc * H + h) * p.rec_stride;
         const float *eb = rec + (BWD ? R::KE : R::W), *bb = rec + (BWD ? R::W : R::KE);
+        // (raw q, k: K_end and Q e^g come as q and k rows, clamped to valid
+        // rows here and scaled or zeroed in put)
+        auto qk_off = [&](int r, int c) { return ((tok0 + min(r, clen - 1)) * p.Hk + hq) * DK + c; };
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
             const int e = min(tid + NT * u, TE - 1);
             int r, j;
             row_piece(e, r, j);
-            rE[u] = *reinterpret_cast<const f32x4 *>(eb + r * DK + j);
+            if (!RAW || !BWD) {
+                rE[u] = *reinterpret_cast<const f32x4 *>(eb + r * DK + j);
+            } else {
+                const float4 k4 = load4(kin + qk_off(r, j));
+                rE[u] = f32x4{k4.x, k4.y, k4.z, k4.w};
+            }
             int jc, r4;
             col_piece(e, DK, jc, r4);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                rB[u][t] = bb[(r4 + t) * DK + jc];
-                if (BWD) rG[u][t] = rec[R::Q + (r4 + t) * DK + jc];
+                rB[u][t] = !RAW || BWD ? bb[(r4 + t) * DK + jc] : ld1(kin + qk_off(r4 + t, jc));
+                if (BWD) rG[u][t] = !RAW ? rec[R::Q + (r4 + t) * DK + jc] : ld1(qin + qk_off(r4 + t, jc));
             }
+        }
+        if (RAW) {
+            rGv = rec[R::G + (l & (C - 1))];
+            rClen = clen;
         }
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
@@ -637,6 +666,31 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         rD = rec[R::D + (tid & (DK - 1))];
     };
     auto put = [&](int b) {
+        if (RAW) {
+            // K_end = k e^{g_C - g_r}, Q e^g = q e^{g_r}, zero past the chunk's
+            // end: lane r forms row r's two factors, the pieces read them across
+            // lanes (before any lane skips)
+            const int rr = l & (C - 1);
+            const float gC = __shfl(rGv, C - 1), in = rr < rClen ? 1.f : 0.f;
+            const float fk = in * fexp(gC - rGv), fq = in * fexp(rGv);
+#pragma unroll
+            for (int u = 0; u < NE; ++u) {
+                const int e = min(tid + NT * u, TE - 1);
+                int r, j, jc, r4;
+                row_piece(e, r, j);
+                col_piece(e, DK, jc, r4);
+                if (BWD) {
+                    const float f = __shfl(fk, r);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) rE[u][t] *= f;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (BWD) rG[u][t] *= __shfl(fq, r4 + t);
+                    else rB[u][t] *= __shfl(fk, r4 + t);
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
             const int e = tid + NT * u;
@@ -748,13 +802,13 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
 // Both state passes in one launch: the first half of the grid walks the
 // states forward, the second half the state gradients backward.  The two
 // recurrences are independent, so each half fills the CUs the other leaves.
-template <int DK, int NW, typename IT, typename GT>
+template <int DK, int NW, bool KDA, typename IT, typename GT>
 __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half) {
     __shared__ ScanLds<DK, NW> lds;
     if ((int)blockIdx.x < half)
-        scan_body<DK, NW, false, IT, GT>(p, blockIdx.x, lds);
+        scan_body<DK, NW, false, KDA, IT, GT>(p, blockIdx.x, lds);
     else
-        scan_body<DK, NW, true, IT, GT>(p, blockIdx.x - half, lds);
+        scan_body<DK, NW, true, KDA, IT, GT>(p, blockIdx.x - half, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1228,12 +1282,8 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *__restr
 }
 
 template <int DK, bool KDA, typename IT, typename GT>
-static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStream_t st) {
+static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp0, hipStream_t st) {
     const long nrc = a.record_chunks;
-    if (nrc > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    }
     // A scan workgroup fills a CU's LDS, so the grid runs in rounds of one
     // workgroup per CU, each round one full chain.  Two waves (32 value rows)
     // per workgroup when both passes then fit in one round, else four.
@@ -1243,12 +1293,18 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp, hipStr
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     const bool four = a.dv % 64 == 0 && 2 * 8 * ((units + 7) / 8) * (a.dv / 32) > cus;
+    BwdKArgs kp = kp0;
+    kp.raw_qk = !KDA && four;                 // the four-wave scan stages q, k raw with a per-head decay
+    if (nrc > 0) {
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
     const long per_unit = a.dv / (four ? 64 : 32);
     const unsigned scan_blocks = (unsigned)(8 * ((units + 7) / 8) * per_unit);
     if (four)
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, IT, GT>), dim3(2 * scan_blocks), dim3(256), 0, st, kp, (int)scan_blocks);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, KDA, IT, GT>), dim3(2 * scan_blocks), dim3(256), 0, st, kp, (int)scan_blocks);
     else
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, IT, GT>), dim3(2 * scan_blocks), dim3(128), 0, st, kp, (int)scan_blocks);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(2 * scan_blocks), dim3(128), 0, st, kp, (int)scan_blocks);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (nrc > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(kGradThreads), 0, st, kp);

@@ -95,7 +95,8 @@ constexpr int kBackwardChunk = 32;
 // One backward chunk record: e^{g_C} [dk], T and M [C][C], W, Q e^g and
 // K_end [C][dk], fp32, padded to 256 bytes.
 constexpr size_t backward_record_bytes(int dk) {
-    return (((size_t)dk + 2 * kBackwardChunk * kBackwardChunk + 3 * (size_t)kBackwardChunk * dk) * 4 + 255) &
+    return (((size_t)dk + 2 * kBackwardChunk * kBackwardChunk + 3 * (size_t)kBackwardChunk * dk + kBackwardChunk) * 4 +
+            255) &
            ~size_t(255);
 }
 bool backward_supported(int dk, int dv);

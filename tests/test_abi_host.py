@@ -324,14 +324,15 @@ def test_backward_rejects(kw, status, msg):
 
 
 def test_backward_workspace_size():
-    """Per (chunk slot, head): a record of e^{g_C} (dk), T and M (C x C) and
-    three C x dk operands in fp32, 256-byte aligned, plus one state and one
+    """Per (chunk slot, head): a record of e^{g_C} (dk), T and M (C x C),
+    three C x dk operands and the C row log decays in fp32, 256-byte aligned,
+    plus one state and one
     state gradient (dv x dk fp32); packed batches add the schedule and one
     spare chunk slot per sequence."""
     lib = gdr.load_library()
     f = lib.gdr_prefill_backward_workspace_bytes
     r256 = lambda b: -(-b // 256) * 256
-    rec = lambda dk: r256((dk + 2 * 32 * 32 + 3 * 32 * dk) * 4)
+    rec = lambda dk: r256((dk + 2 * 32 * 32 + 3 * 32 * dk + 32) * 4)
     sh = gdr.PrefillShape(1, 1000, 4, 64, 32, 9, 0)
     slots = 32 * 4
     assert f(ctypes.byref(sh), 0, 0) == r256(slots * rec(64)) + 2 * r256(slots * 64 * 32 * 4)
