@@ -81,18 +81,23 @@ def test_backward_shapes(case, dtype):
 # Enough (sequence, head) units that the state scans take four waves (64 value
 # rows) per workgroup on a 256-CU device, at the small key widths the large
 # workloads do not reach.
+# (With a per-head decay the four-wave scans stage raw q and k, scaled per row,
+# so those cases also run with fp32 q/k/v.)
 FOUR_WAVE_CASES = [
-    # dk, dv, H, T, gate, B
-    (32, 64, 72, 70, "channel", 1),
-    (64, 128, 40, 45, "head", 2),
-    (32, 128, 36, 33, "head", 2),
+    # dk, dv, H, T, gate, B, dtype
+    (32, 64, 72, 70, "channel", 1, torch.bfloat16),
+    (64, 128, 40, 45, "head", 2, torch.bfloat16),
+    (32, 128, 36, 33, "head", 2, torch.bfloat16),
+    (64, 128, 40, 45, "head", 2, torch.float32),
+    (128, 64, 80, 37, "head", 1, torch.float32),
 ]
 
 
-@pytest.mark.parametrize("case", FOUR_WAVE_CASES, ids=lambda c: f"dk{c[0]}-dv{c[1]}-H{c[2]}-T{c[3]}-{c[4]}-B{c[5]}")
+@pytest.mark.parametrize("case", FOUR_WAVE_CASES,
+                         ids=lambda c: f"dk{c[0]}-dv{c[1]}-H{c[2]}-T{c[3]}-{c[4]}-B{c[5]}-{str(c[6])[6:]}")
 def test_backward_four_wave_scan_small_keys(case):
-    dk, dv, H, T, gate, B = case
-    inp, cot = _small(dk, dv, H, T, gate, torch.bfloat16, True, seed=3 * dk + T, B=B)
+    dk, dv, H, T, gate, B, dtype = case
+    inp, cot = _small(dk, dv, H, T, gate, dtype, True, seed=3 * dk + T, B=B)
     _check(inp, cot, f"four-wave scan {case}")
 
 
