@@ -111,6 +111,15 @@ def test_backward_packed_with_empty_and_one_token_sequences(gate):
     torch.testing.assert_close(got["d_initial_state"][1], cot["d_final_state"][1], rtol=0, atol=0)
 
 
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_backward_packed_four_wave_scan(gate):
+    """The same kind of packed batch with enough heads for four-wave scans
+    (with a per-head decay, the raw q/k staging) at d_v = 64."""
+    inp, cot = _small(64, 64, 40, 0, gate, torch.bfloat16, True, seed=23, lengths=[37, 0, 70, 1, 33])
+    got, _ = _check(inp, cot, f"packed four-wave {gate}")
+    torch.testing.assert_close(got["d_initial_state"][1], cot["d_final_state"][1], rtol=0, atol=0)
+
+
 def test_backward_without_final_gradient_or_initial_state():
     """No final-state gradient (zeros), no initial state (zeros), no
     initial-state gradient requested, a query scale."""
