@@ -103,8 +103,10 @@ def _decode_tokens(N=4, K=4, H=2, Hk=0, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=
     (dict(shape=(1, 64, 2, 64, 40, 1, 0)), 2, "head_dim_v"),
     (dict(shape=(1, 64, 2, 16, 64, 1, 0)), 2, "no prefill kernel"),        # bf16 needs dk >= 32
     (dict(chunk=48), 1, "chunk_size"),
-    (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 runs 32-token chunks
-    (dict(chunk=64), 2, "no prefill kernel"),
+    (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 runs 32- and 64-token chunks
+    (dict(chunk=64, qkv=0), 2, "no prefill kernel"),                    # fp32 q/k/v: 16 or 32 only
+    (dict(chunk=64, shape=(1, 64, 2, 16, 64, 1, 0)), 2, "no fused prefill kernel"),   # fused: dk >= 32
+    (dict(chunk=64, dvs=64, shape=(1, 64, 2, 128, 128, 1, 0)), 2, "no fused prefill kernel"),
     (dict(dvs=48), 1, "dv_slice"),
     (dict(shape=(1, 64, 2, 64, 48, 1, 0), dvs=32), 1, "does not divide"),
     (dict(shape=(2, 64, 2, 64, 64, 1, 0)), 1, "num_seqs == batch"),
@@ -143,19 +145,57 @@ def test_prefill_workspace_size():
     lib = gdr.load_library()
     f = lib.gdr_prefill_workspace_bytes
     sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9, 0)
-    rec_gdn_bf16 = -(-(4 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
+    rec_gdn_f32 = -(-(4 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 4) // 256) * 256
     rec_kda_f32 = -(-(64 * 4 + (3 * 16 * 64 + 2 * 16 * 16) * 4) // 256) * 256
-    assert f(ctypes.byref(sh), 0, 1, 32, 0) == 32 * 4 * rec_gdn_bf16
-    assert f(ctypes.byref(sh), 0, 1, 0, 0) == 32 * 4 * rec_gdn_bf16          # automatic chunk = 32
-    assert f(ctypes.byref(sh), 0, 1, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_bf16
+    assert f(ctypes.byref(sh), 0, 0, 32, 0) == 32 * 4 * rec_gdn_f32
+    assert f(ctypes.byref(sh), 0, 0, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_f32
     assert f(ctypes.byref(sh), 1, 0, 16, 0) == 63 * 4 * rec_kda_f32
     # one pass over every chunk, whatever the length
     sh = gdr.PrefillShape(2, 32768, 4, 128, 64, 2, 0)
-    rec_kda_bf16 = -(-(128 * 4 + (3 * 32 * 128 + 2 * 32 * 32) * 2) // 256) * 256
-    assert f(ctypes.byref(sh), 1, 1, 32, 0) == 2 * 1024 * 4 * rec_kda_bf16
+    rec_kda_f32 = -(-(128 * 4 + (3 * 32 * 128 + 2 * 32 * 32) * 4) // 256) * 256
+    assert f(ctypes.byref(sh), 1, 0, 32, 0) == 2 * 1024 * 4 * rec_kda_f32
+    assert f(ctypes.byref(sh), 1, 0, 0, 0) == f(ctypes.byref(sh), 1, 0, 32, 0)   # fp32: automatic chunk = 32
     assert f(None, 0, 1, 0, 1) == 0
     assert f(ctypes.byref(sh), 5, 1, 0, 0) == 0
     assert f(ctypes.byref(sh), 0, 1, 48, 0) == 0
+
+
+def _fused_ws(num_seqs, H, Hk, dk, dv, kda, packed, C, cus=256):
+    """The fused prefill's workspace as documented: handshake words, a ring of
+    records per group of NS value slices (NS + 2 of them for 64-token chunks,
+    2 NS + 4 for 32-token chunks), and for 64-token chunks a scratch per
+    workgroup; the largest over the value-slice widths a call may pick."""
+    r256 = lambda b: -(-b // 256) * 256
+    rec = r256((dk if kda else 4) * 4 + (3 * C * dk + 2 * C * C) * 2)
+    scr = r256(((C // 16) * (2 if kda else 1) * 16 * dk + dk * C) * 2) if C == 64 else 0
+    G = H // Hk
+    per_xcd = -(-num_seqs * Hk // 8) * G
+    best = 0
+    for dvs in (16, 32):
+        if dv % dvs:
+            continue
+        ns = dv // dvs
+        gpx = max(1, min(per_xcd, cus // (8 * ns)))
+        ngroups, grid, d = 8 * gpx, 8 * gpx * ns, (ns + 2 if C == 64 else 2 * ns + 4)
+        off = (r256(4 * num_seqs) + r256(4 * (num_seqs + 1))) if packed else 0
+        off += r256(4 * (ngroups * (d + 2 * ns) + 1)) + ngroups * d * rec + grid * scr
+        best = max(best, off)
+    return best
+
+
+def test_fused_prefill_workspace_size():
+    """bf16 q/k/v (32- or 64-token chunks) size the fused kernel's ring:
+    independent of the sequence length."""
+    lib = gdr.load_library()
+    f = lib.gdr_prefill_workspace_bytes
+    for (B, T, H, dk, dv, N, Hk, gate, packed) in [(1, 1000, 4, 64, 64, 9, 0, 0, 0), (2, 32768, 32, 128, 128, 2, 0, 1, 0),
+                                                   (1, 262144, 16, 128, 128, 8, 0, 0, 1),
+                                                   (1, 32768, 48, 128, 128, 1, 16, 0, 0)]:
+        sh = gdr.PrefillShape(B, T, H, dk, dv, N, Hk)
+        for C in (32, 64):
+            assert f(ctypes.byref(sh), gate, 1, C, packed) == _fused_ws(N, H, Hk or H, dk, dv, gate == 1, packed, C)
+        assert f(ctypes.byref(sh), gate, 1, 0, packed) == f(ctypes.byref(sh), gate, 1, 64, packed)   # automatic chunk
+    assert _fused_ws(2, 32, 32, 128, 128, True, False, 64) < 64 << 20   # KDA 32K: tens of MB, not GB
 
 
 @pytest.mark.parametrize("kw,status,msg", [

@@ -50,10 +50,10 @@ def test_tiny_gdn_workload():
 
 
 def test_gdn_prefill_8k_workload():
-    """B=1, H=16, T=8192, d=128, bf16 q/k/v, per-head decay (the kernel's own
-    32-token chunking; the function does not depend on the chunk size)."""
+    """B=1, H=16, T=8192, d=128, bf16 q/k/v, per-head decay, chunk size 64 as
+    the workload states."""
     w = WORKLOADS["gdn_prefill_8k"]
-    _check_all(prefill_inputs(w, DEV), "gdn_prefill_8k")
+    _check_all(prefill_inputs(w, DEV), "gdn_prefill_8k", chunk_size=64)
 
 
 def _check_sampled(inp, units, label, **kw):
@@ -139,6 +139,55 @@ def test_prefill_bf16_shapes(dk, dv, H, T, gate, init, chunk, dvs):
     _check_all(inp, f"bf16 dk={dk} dv={dv} H={H} T={T} {gate} init={init}", chunk_size=chunk, dv_slice=dvs)
 
 
+# 64-token chunks: the single-kernel prefill (records shared through a ring)
+FUSED_CASES = [
+    # dk, dv, H, T, gate, init, dv_slice (0: automatic)
+    (128, 128, 2, 1, "head", False, 0),
+    (128, 128, 2, 63, "channel", True, 32),
+    (128, 128, 1, 64, "head", True, 16),
+    (128, 128, 3, 65, "channel", False, 16),
+    (128, 128, 2, 200, "head", True, 32),
+    (128, 128, 2, 513, "channel", True, 0),
+    (128, 64, 1, 300, "channel", True, 32),
+    (128, 16, 2, 129, "head", True, 16),
+    (64, 64, 3, 130, "head", True, 32),
+    (64, 32, 2, 129, "channel", True, 16),
+    (64, 48, 2, 191, "channel", True, 16),
+    (32, 32, 1, 95, "head", False, 32),
+    (32, 48, 2, 100, "channel", True, 16),
+    (32, 128, 2, 257, "head", True, 0),
+]
+
+
+@pytest.mark.parametrize("dk,dv,H,T,gate,init,dvs", FUSED_CASES)
+def test_prefill_fused_shapes(dk, dv, H, T, gate, init, dvs):
+    inp = _small(dk, dv, H, T, gate, torch.bfloat16, init, seed=3 * dk + dv + T + H)
+    _check_all(inp, f"fused dk={dk} dv={dv} H={H} T={T} {gate} init={init} dvs={dvs}", chunk_size=64, dv_slice=dvs)
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_fused_more_units_than_workgroups(gate):
+    """300 heads of 32 value channels: one slice per group and more (sequence,
+    head) units than workgroups, so groups take several units in turn (each
+    group builds, publishes and consumes every record of its units itself)."""
+    inp = _small(64, 32, 300, 70, gate, torch.bfloat16, True, seed=301)
+    _check_all(inp, f"fused 300 heads {gate}", chunk_size=64)
+
+
+def test_prefill_fused_workspace_reuse_and_scale():
+    """Two different calls through one workspace (the handshake words are
+    reset per call), then a readout scale: o(s) = s o(1)."""
+    a = _small(128, 128, 4, 333, "channel", torch.bfloat16, True, seed=311)
+    b = _small(128, 128, 4, 97, "head", torch.bfloat16, False, seed=312)
+    ws = torch.empty(32 << 20, dtype=torch.uint8, device=DEV)      # more than either call needs
+    for inp, label in ((a, "first"), (b, "second"), (a, "first again")):
+        _check_all(inp, f"workspace reuse: {label}", chunk_size=64, workspace=ws)
+    ref_o, ref_s = _oracle(a)
+    o, s = _gpu(a, chunk_size=64, scale=0.37)
+    assert_close("out (scale 0.37)", o, 0.37 * ref_o, TOL[torch.bfloat16])
+    assert_close("final_state (scale only reads out)", s, ref_s, TOL[torch.bfloat16])
+
+
 F32_CASES = [
     (16, 16, 2, 1, "head", False, 16),
     (16, 16, 2, 17, "channel", True, 16),
@@ -217,17 +266,18 @@ def test_prefill_segments(gate):
     between them; outputs and states match the one-pass run bit for bit."""
     T = 64 * 32 * 2 + 77                                   # 131 chunks -> segments 64, 64, 3
     inp = _small(64, 64, 2, T, gate, torch.bfloat16, True, seed=61, B=2)
-    out, fin = _check_all(inp, f"one pass {gate}")
+    out, fin = _check_all(inp, f"one pass {gate}", chunk_size=32)
     rec = -(-((64 * 4 if gate == "channel" else 16) + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
     ws_bytes = 2 * 64 * 2 * rec + 2 * 2 * 64 * 64 * 4   # records of one 64-chunk segment + carried state
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
     say("segments of 64 chunks; then in place; then without the final state")
-    o1, f1 = _gpu(inp, workspace=ws)
+    o1, f1 = _gpu(inp, workspace=ws, chunk_size=32)
     state = inp["initial_state"].clone()
     o2, _ = gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
-                                    initial_state=state, final_state=state, workspace=ws)
+                                    initial_state=state, final_state=state, workspace=ws, chunk_size=32)
     o3, f3 = gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
-                                     initial_state=inp["initial_state"], output_final_state=False, workspace=ws)
+                                     initial_state=inp["initial_state"], output_final_state=False, workspace=ws,
+                                     chunk_size=32)
     torch.cuda.synchronize()
     assert f3 is None
     for o in (o1, o2, o3):
@@ -235,7 +285,7 @@ def test_prefill_segments(gate):
     assert torch.equal(f1, fin) and torch.equal(state, fin)
     with pytest.raises(gdr.GdrError, match="workspace"):
         gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
-                                workspace=ws[: 2 * 15 * 2 * rec])
+                                workspace=ws[: 2 * 15 * 2 * rec], chunk_size=32)
 
 
 # ------------------------------------------------------- GPU properties ----
