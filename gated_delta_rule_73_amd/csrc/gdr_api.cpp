@@ -116,14 +116,11 @@ PrefillWorkspace fit_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, 
     return best;
 }
 
-// automatic chunk size: bf16 q/k/v take the fused 64-token kernel where it
-// is compiled; otherwise 32 tokens where compiled, else 16
-int auto_chunk(bool bf16, bool kda, int dk) {
-    if (bf16 && gdr::fused_supported(kda, dk, 16)) return gdr::kFusedChunkHost;
-    return gdr::prefill_supported(bf16, kda, dk, 16, 32) ? 32 : 16;
-}
-// the fused kernels serve bf16 q/k/v with 32- and 64-token chunks
-bool use_fused(bool bf16, int chunk) { return bf16 && (chunk == 32 || chunk == gdr::kFusedChunkHost); }
+// automatic chunk size: 32 tokens where compiled (the fastest schedule
+// measured on every workload), else 16
+int auto_chunk(bool bf16, bool kda, int dk) { return gdr::prefill_supported(bf16, kda, dk, 16, 32) ? 32 : 16; }
+// the fused single-kernel prefill serves bf16 q/k/v with 64-token chunks
+bool use_fused(bool bf16, int chunk) { return bf16 && chunk == gdr::kFusedChunkHost; }
 
 
 constexpr int kMaxDecodeTokens = 64;
@@ -403,7 +400,7 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
         size_t most = 0;
         for (int dvs : {0, 16, 32, 64})
             most = std::max(most, gdr::fused_plan(kda, s.head_dim_k, s.head_dim_v, s.num_seqs, s.num_heads, hk, dvs,
-                                                  packed != 0, C).total);
+                                                  packed != 0).total);
         return most;
     }
     return prefill_workspace(s, kda, bf16, C, packed != 0).total;
@@ -457,7 +454,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     gdr::FusedPlan plan;
     int DVS = dv_slice;
     if (fused) {
-        plan = gdr::fused_plan(kda, dk, dv, s.num_seqs, s.num_heads, hk, dv_slice, packed, C);
+        plan = gdr::fused_plan(kda, dk, dv, s.num_seqs, s.num_heads, hk, dv_slice, packed);
         if (!plan.dvs)
             return fail(GDR_ERROR_NOT_SUPPORTED, "no fused prefill kernel for dk=%d dv=%d dv_slice=%d chunk=%d", dk,
                         dv, dv_slice, C);

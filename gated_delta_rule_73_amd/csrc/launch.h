@@ -58,12 +58,6 @@ constexpr size_t fused_record_bytes(int dk, bool kda) {
     const size_t C = kFusedChunkHost;
     return (((size_t)(kda ? dk : 4) * 4 + (3 * C * dk + 2 * C * C) * 2) + 255) & ~size_t(255);
 }
-// one ring record of the 32-token fused kernel (fused32_impl.h Fused32Rec):
-// e^{g_C}, W_n, Q e^g, K_end^T, T diag(b), M; fp16 operands, padded to 256 bytes
-constexpr size_t fused32_record_bytes(int dk, bool kda) {
-    const size_t C = 32;
-    return (((size_t)(kda ? dk : 4) * 4 + (3 * C * dk + 2 * C * C) * 2) + 255) & ~size_t(255);
-}
 // the prep waves' per-workgroup scratch (FusedScratch): right Gram operands
 // of every 16-token row tile, (K e^g)^T
 constexpr size_t fused_scratch_bytes(int dk, bool kda) {
@@ -76,10 +70,10 @@ struct FusedPlan {
 };
 // True when the fused kernel is compiled for (gate kind, d_k, value slice).
 bool fused_supported(bool kda, int dk, int dvs);
-// Launch plan and workspace layout for chunk 32 or 64.  dvs_req = 0 picks the
-// slice width; the result has dvs = 0 when no fused kernel fits.
+// Launch plan and workspace layout.  dvs_req = 0 picks the slice width; the
+// result has dvs = 0 when no fused kernel fits.
 FusedPlan fused_plan(bool kda, int dk, int dv, int num_seqs, int num_heads, int num_qk_heads, int dvs_req,
-                     bool packed, int chunk);
+                     bool packed);
 hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t st);
 
 // Size of one per-chunk record of the prefill (see ChunkRec in

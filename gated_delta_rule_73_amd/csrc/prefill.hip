@@ -86,8 +86,6 @@ hipError_t launch_schedule(const int32_t *cu, int n, int chunk, int32_t *order, 
 
 hipError_t launch_fused_gdn(const FusedArgs &fa, int dk, int dvs, int grid, hipStream_t st);
 hipError_t launch_fused_kda(const FusedArgs &fa, int dk, int dvs, int grid, hipStream_t st);
-hipError_t launch_fused32_gdn(const FusedArgs &fa, int dk, int dvs, int grid, hipStream_t st);
-hipError_t launch_fused32_kda(const FusedArgs &fa, int dk, int dvs, int grid, hipStream_t st);
 
 // Fused prefill: d_k in {32, 64, 128}; value slices of 16 or 32 channels (a
 // 64-channel slice needs a fourth chain wave, which leaves too few registers
@@ -117,7 +115,7 @@ int device_cus() {
 // narrowest whose groups all fit at once (most workgroups, most record
 // producers per unit), else the widest compiled.
 FusedPlan fused_plan(bool kda, int dk, int dv, int num_seqs, int num_heads, int num_qk_heads, int dvs_req,
-                     bool packed, int chunk) {
+                     bool packed) {
     FusedPlan pl;
     const int cap = device_cus();
     const int G = num_heads / num_qk_heads;
@@ -136,9 +134,9 @@ FusedPlan fused_plan(bool kda, int dk, int dv, int num_seqs, int num_heads, int 
     if (8 * ns > cap) return pl;                           // one group per XCD must fit
     pl.dvs = dvs;
     pl.ns = ns;
-    // ring depth: the records being built (one per slice at chunk 64, two per
-    // slice at chunk 32) and the ones the loaders and chains still read
-    pl.d = chunk == 32 ? 2 * ns + 4 : ns + 2;
+    // ring depth: the records being built (one per slice) and the ones the
+    // loaders and chains still read
+    pl.d = ns + 2;
     pl.gpx = (int)std::max<long>(1, std::min<long>(per_xcd, cap / (8 * ns)));
     pl.ngroups = 8 * pl.gpx;
     pl.grid = pl.ngroups * ns;
@@ -152,9 +150,9 @@ FusedPlan fused_plan(bool kda, int dk, int dv, int num_seqs, int num_heads, int 
     pl.ctl_off = off;
     off += r256(4 * ((size_t)pl.ngroups * (pl.d + 2 * ns) + 1));
     pl.ring_off = off;
-    off += (size_t)pl.ngroups * pl.d * (chunk == 32 ? fused32_record_bytes(dk, kda) : fused_record_bytes(dk, kda));
+    off += (size_t)pl.ngroups * pl.d * fused_record_bytes(dk, kda);
     pl.scratch_off = off;
-    if (chunk != 32) off += (size_t)pl.grid * fused_scratch_bytes(dk, kda);
+    off += (size_t)pl.grid * fused_scratch_bytes(dk, kda);
     pl.total = off;
     return pl;
 }
@@ -190,9 +188,6 @@ hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t st) {
     fa.scratch = a.f_scratch;
     fa.ctl = a.f_ctl;
     fa.out = a.out;
-    if (a.chunk == 32)
-        return a.kda ? launch_fused32_kda(fa, a.dk, a.dv_slice, a.f_grid, st)
-                     : launch_fused32_gdn(fa, a.dk, a.dv_slice, a.f_grid, st);
     return a.kda ? launch_fused_kda(fa, a.dk, a.dv_slice, a.f_grid, st)
                  : launch_fused_gdn(fa, a.dk, a.dv_slice, a.f_grid, st);
 }

@@ -145,29 +145,32 @@ def test_prefill_workspace_size():
     lib = gdr.load_library()
     f = lib.gdr_prefill_workspace_bytes
     sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9, 0)
+    rec_gdn_bf16 = -(-(4 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 2) // 256) * 256
     rec_gdn_f32 = -(-(4 * 4 + (3 * 32 * 64 + 2 * 32 * 32) * 4) // 256) * 256
     rec_kda_f32 = -(-(64 * 4 + (3 * 16 * 64 + 2 * 16 * 16) * 4) // 256) * 256
+    assert f(ctypes.byref(sh), 0, 1, 32, 0) == 32 * 4 * rec_gdn_bf16
+    assert f(ctypes.byref(sh), 0, 1, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_bf16
     assert f(ctypes.byref(sh), 0, 0, 32, 0) == 32 * 4 * rec_gdn_f32
-    assert f(ctypes.byref(sh), 0, 0, 32, 1) == 256 + 256 + (32 + 9) * 4 * rec_gdn_f32
     assert f(ctypes.byref(sh), 1, 0, 16, 0) == 63 * 4 * rec_kda_f32
     # one pass over every chunk, whatever the length
     sh = gdr.PrefillShape(2, 32768, 4, 128, 64, 2, 0)
-    rec_kda_f32 = -(-(128 * 4 + (3 * 32 * 128 + 2 * 32 * 32) * 4) // 256) * 256
-    assert f(ctypes.byref(sh), 1, 0, 32, 0) == 2 * 1024 * 4 * rec_kda_f32
-    assert f(ctypes.byref(sh), 1, 0, 0, 0) == f(ctypes.byref(sh), 1, 0, 32, 0)   # fp32: automatic chunk = 32
+    rec_kda_bf16 = -(-(128 * 4 + (3 * 32 * 128 + 2 * 32 * 32) * 2) // 256) * 256
+    assert f(ctypes.byref(sh), 1, 1, 32, 0) == 2 * 1024 * 4 * rec_kda_bf16
+    assert f(ctypes.byref(sh), 1, 1, 0, 0) == f(ctypes.byref(sh), 1, 1, 32, 0)   # automatic chunk = 32
+    assert f(ctypes.byref(sh), 1, 0, 0, 0) == f(ctypes.byref(sh), 1, 0, 32, 0)
     assert f(None, 0, 1, 0, 1) == 0
     assert f(ctypes.byref(sh), 5, 1, 0, 0) == 0
     assert f(ctypes.byref(sh), 0, 1, 48, 0) == 0
 
 
-def _fused_ws(num_seqs, H, Hk, dk, dv, kda, packed, C, cus=256):
+def _fused_ws(num_seqs, H, Hk, dk, dv, kda, packed, cus=256):
     """The fused prefill's workspace as documented: handshake words, a ring of
-    records per group of NS value slices (NS + 2 of them for 64-token chunks,
-    2 NS + 4 for 32-token chunks), and for 64-token chunks a scratch per
-    workgroup; the largest over the value-slice widths a call may pick."""
+    NS + 2 records per group of NS value slices, a scratch per workgroup; the
+    largest over the value-slice widths a call may pick."""
     r256 = lambda b: -(-b // 256) * 256
+    C = 64
     rec = r256((dk if kda else 4) * 4 + (3 * C * dk + 2 * C * C) * 2)
-    scr = r256(((C // 16) * (2 if kda else 1) * 16 * dk + dk * C) * 2) if C == 64 else 0
+    scr = r256(((C // 16) * (2 if kda else 1) * 16 * dk + dk * C) * 2)
     G = H // Hk
     per_xcd = -(-num_seqs * Hk // 8) * G
     best = 0
@@ -176,7 +179,7 @@ def _fused_ws(num_seqs, H, Hk, dk, dv, kda, packed, C, cus=256):
             continue
         ns = dv // dvs
         gpx = max(1, min(per_xcd, cus // (8 * ns)))
-        ngroups, grid, d = 8 * gpx, 8 * gpx * ns, (ns + 2 if C == 64 else 2 * ns + 4)
+        ngroups, grid, d = 8 * gpx, 8 * gpx * ns, ns + 2
         off = (r256(4 * num_seqs) + r256(4 * (num_seqs + 1))) if packed else 0
         off += r256(4 * (ngroups * (d + 2 * ns) + 1)) + ngroups * d * rec + grid * scr
         best = max(best, off)
@@ -184,7 +187,7 @@ def _fused_ws(num_seqs, H, Hk, dk, dv, kda, packed, C, cus=256):
 
 
 def test_fused_prefill_workspace_size():
-    """bf16 q/k/v (32- or 64-token chunks) size the fused kernel's ring:
+    """bf16 q/k/v with 64-token chunks size the fused kernel's ring:
     independent of the sequence length."""
     lib = gdr.load_library()
     f = lib.gdr_prefill_workspace_bytes
@@ -192,10 +195,8 @@ def test_fused_prefill_workspace_size():
                                                    (1, 262144, 16, 128, 128, 8, 0, 0, 1),
                                                    (1, 32768, 48, 128, 128, 1, 16, 0, 0)]:
         sh = gdr.PrefillShape(B, T, H, dk, dv, N, Hk)
-        for C in (32, 64):
-            assert f(ctypes.byref(sh), gate, 1, C, packed) == _fused_ws(N, H, Hk or H, dk, dv, gate == 1, packed, C)
-        assert f(ctypes.byref(sh), gate, 1, 0, packed) == f(ctypes.byref(sh), gate, 1, 64, packed)   # automatic chunk
-    assert _fused_ws(2, 32, 32, 128, 128, True, False, 64) < 64 << 20   # KDA 32K: tens of MB, not GB
+        assert f(ctypes.byref(sh), gate, 1, 64, packed) == _fused_ws(N, H, Hk or H, dk, dv, gate == 1, packed)
+    assert _fused_ws(2, 32, 32, 128, 128, True, False) < 64 << 20       # KDA 32K: tens of MB, not GB
 
 
 @pytest.mark.parametrize("kw,status,msg", [
