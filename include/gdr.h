@@ -58,7 +58,17 @@ extern "C" {
 
 #define GDR_ABI_VERSION 5
 
-typedef enum gdr_status {
+/* The enumerations travel as 32-bit ints.  Compiled as C++ they name that
+ * type, so any int a C caller passes (an invalid one included, which the
+ * calls reject) is a value the library may read; C sees plain enums of the
+ * same size. */
+#ifdef __cplusplus
+#define GDR_ENUM_BASE : int32_t
+#else
+#define GDR_ENUM_BASE
+#endif
+
+typedef enum gdr_status GDR_ENUM_BASE {
     GDR_SUCCESS = 0,
     GDR_ERROR_INVALID_VALUE = 1,        /* null pointer, bad size, misalignment, overlap */
     GDR_ERROR_NOT_SUPPORTED = 2,        /* valid request outside the compiled kernel set */
@@ -66,12 +76,12 @@ typedef enum gdr_status {
     GDR_ERROR_LAUNCH_FAILED = 4         /* the HIP runtime refused a launch */
 } gdr_status;
 
-typedef enum gdr_dtype {
+typedef enum gdr_dtype GDR_ENUM_BASE {
     GDR_F32 = 0,
     GDR_BF16 = 1
 } gdr_dtype;
 
-typedef enum gdr_gate {
+typedef enum gdr_gate GDR_ENUM_BASE {
     GDR_GATE_HEAD = 0,      /* Gated DeltaNet: log_alpha has one value per (token, head)        */
     GDR_GATE_CHANNEL = 1    /* Kimi Delta Attention: one value per (token, head, key channel)   */
 } gdr_gate;

@@ -34,6 +34,19 @@ _LIB = os.path.join(_HERE, "libgdr_oracle.so")
 _lib = None
 
 
+def build_sanitized(out: str) -> str:
+    """The oracle with host AddressSanitizer + UndefinedBehaviorSanitizer
+    (ROCm's clang, whose ASan runtime also serves the HIP library's sanitized
+    build; serial: the OpenMP pragmas are left out).  For the sanitizer test."""
+    clang = "/opt/rocm/llvm/bin/clang"
+    tmp = out + ".tmp"
+    subprocess.run([clang, "-std=c99", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-Wno-unknown-pragmas", _SRC,
+                    "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
     """Compile the oracle with the host C compiler (gcc, OpenMP)."""
     if force or not os.path.exists(_LIB):
