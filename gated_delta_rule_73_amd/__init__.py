@@ -22,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["gdr_prefill_chunked", "gdr_decode_step", "gdr_decode_tokens", "gdr_layer_prologue",
+__all__ = ["gdr_prefill_chunked", "gdr_prefill_chunked_static", "gdr_decode_step", "gdr_decode_tokens", "gdr_layer_prologue",
            "gdr_prefill_backward", "prefill_chunked", "decode_step", "decode_tokens", "layer_prologue",
            "prefill_backward",
            "gdr_state_bytes", "GdrError", "load_library", "library_path"]
@@ -68,6 +68,10 @@ def load_library():
                                             ctypes.c_int, p, p, p, p, p, p, p, i32, i32, ctypes.c_float, p, p, p,
                                             sz, p]
         lib.gdr_prefill_chunked.restype = ctypes.c_int
+        lib.gdr_prefill_chunked_static.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int, p, p, p, p, p, p, p, i32, i32,
+                                                   ctypes.c_float, p, p, p]
+        lib.gdr_prefill_chunked_static.restype = ctypes.c_int
         lib.gdr_decode_step.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, p, p, p, p, p, p, ctypes.c_float, p, p]
         lib.gdr_decode_step.restype = ctypes.c_int
@@ -179,6 +183,43 @@ def gdr_prefill_chunked(q, k, v, beta, log_alpha, *, initial_state=None, cu_seql
         ctypes.byref(shape), gate, _dtype_code(q), _dtype_code(beta), _dtype_code(out), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
         _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(dv_slice), float(scale), _ptr(out),
         _ptr(final_state), _ptr(ws), int(ws_bytes), _stream(dev)))
+    return out, final_state
+
+
+def gdr_prefill_chunked_static(q, k, v, beta, log_alpha, *, initial_state=None, cu_seqlens=None,
+                               chunk_size: int = 0, dv_slice: int = 0, scale: float = 1.0, out=None,
+                               out_dtype=torch.float32, final_state=None, output_final_state: bool = True):
+    """:func:`gdr_prefill_chunked` on the library's fixed per-device scratch
+    (no workspace argument, no device allocation inside the call).  Calls that
+    overlap on one GPU share that scratch and race.  Raises GdrError
+    (insufficient workspace) when the problem does not fit the scratch."""
+    lib = load_library()
+    dev = q.device
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or beta.shape != (B, T, H):
+        raise ValueError("shapes: q, k [B, T, Hk, dk], v [B, T, H, dv], beta [B, T, H]")
+    if log_alpha.dim() not in (3, 4):
+        raise ValueError("log_alpha must be [B, T, H] or [B, T, H, dk]")
+    gate = GDR_GATE_HEAD if log_alpha.dim() == 3 else GDR_GATE_CHANNEL
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, q.dtype, dev)
+    _need(beta, "beta", None, dev)
+    _need(log_alpha, "log_alpha", beta.dtype, dev)
+    _need(initial_state, "initial_state", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    if out is None:
+        out = torch.empty(B, T, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", None, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty(N, H, dv, dk, dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev)
+    shape = PrefillShape(B, T, H, dk, dv, N, Hk)
+    _check(lib.gdr_prefill_chunked_static(
+        ctypes.byref(shape), gate, _dtype_code(q), _dtype_code(beta), _dtype_code(out), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(beta), _ptr(log_alpha), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(dv_slice),
+        float(scale), _ptr(out), _ptr(final_state), _stream(dev)))
     return out, final_state
 
 

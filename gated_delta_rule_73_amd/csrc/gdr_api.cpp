@@ -554,6 +554,28 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     return launch_status(gdr::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_chunked");
 }
 
+gdr_status gdr_prefill_chunked_static(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
+                                      gdr_dtype gate_dtype, gdr_dtype out_dtype, const void *q, const void *k,
+                                      const void *v, const void *beta, const void *log_alpha,
+                                      const float *initial_state, const int32_t *cu_seqlens, int32_t chunk_size,
+                                      int32_t dv_slice, float scale, void *out, float *final_state,
+                                      void *hip_stream) {
+    void *ws = nullptr;
+    const hipError_t e = gdr::static_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(GDR_ERROR_LAUNCH_FAILED, "gdr_prefill_chunked_static: static scratch address: %s", hipGetErrorString(e));
+    const gdr_status st = gdr_prefill_chunked(shape, gate, qkv_dtype, gate_dtype, out_dtype, q, k, v, beta, log_alpha,
+                                              initial_state, cu_seqlens, chunk_size, dv_slice, scale, out, final_state,
+                                              ws, gdr::kStaticScratchBytes, hip_stream);
+    if (st == GDR_ERROR_INSUFFICIENT_WORKSPACE) {
+        char why[sizeof(g_last_error)];
+        snprintf(why, sizeof why, "%s", g_last_error);
+        return fail(st, "gdr_prefill_chunked_static: the problem needs more than the %zu-byte static scratch (%s)",
+                    gdr::kStaticScratchBytes, why);
+    }
+    return st;
+}
+
 gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t num_qk_heads, int32_t head_dim_k,
                            int32_t head_dim_v, gdr_gate gate, gdr_dtype qkv_dtype, gdr_dtype gate_dtype,
                            gdr_dtype out_dtype, const void *q, const void *k, const void *v, const void *beta,

@@ -76,6 +76,12 @@ FusedPlan fused_plan(bool kda, int dk, int dv, int num_seqs, int num_heads, int 
                      bool packed);
 hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t st);
 
+// The prefill workspace of gdr_prefill_chunked_static (static_scratch.hip):
+// one array of this size per device; static_scratch returns its address on
+// the current device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void **ptr);
+
 // Size of one per-chunk record of the prefill (see ChunkRec in
 // prefill_impl.h): decay row, K e^g, Q e^g, K_end^T, T diag(b), M.
 // es = bytes per operand element (2 for fp16 operands, 4 for fp32).

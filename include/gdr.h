@@ -189,6 +189,31 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate,
                                void *hip_stream);
 
 /*
+ * gdr_prefill_chunked without a caller-provided workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The caller still passes every
+ * input and output; the workspace is instead a fixed 64 MiB array that the
+ * library holds on each GPU it runs on until the process ends.  No call
+ * allocates or frees device memory.
+ * Arguments, layouts, limits and results: as gdr_prefill_chunked.  A dense
+ * batch whose one-pass workspace exceeds 64 MiB runs in segments that fit; a
+ * problem whose smallest workspace (always the one-pass size for packed
+ * batches) exceeds 64 MiB returns GDR_ERROR_INSUFFICIENT_WORKSPACE, with the
+ * sizes in gdr_last_error(), and enqueues nothing.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the kernels need nothing of it cleared): calls that overlap on
+ * one GPU (on different streams, or from different threads without ordering)
+ * race and give undefined results.  Calls on one stream are ordered.
+ */
+gdr_status gdr_prefill_chunked_static(const gdr_prefill_shape *shape, gdr_gate gate,
+                                      gdr_dtype qkv_dtype, gdr_dtype gate_dtype, gdr_dtype out_dtype,
+                                      const void *q, const void *k, const void *v,
+                                      const void *beta, const void *log_alpha,
+                                      const float *initial_state, const int32_t *cu_seqlens,
+                                      int32_t chunk_size, int32_t dv_slice, float scale,
+                                      void *out, float *final_state, void *hip_stream);
+
+/*
  * Decode step: one new token for each of num_seqs sequences.  Reads each
  * (sequence, head) state once, applies the decay, the erase-then-write update
  * and the readout, and writes the state back in place.
