@@ -1,5 +1,4 @@
 """Chunked prefill on the GPU vs the fp64 oracle (sequential recurrence)."""
-import numpy as np
 import pytest
 import torch
 
@@ -56,63 +55,28 @@ def test_gdn_prefill_8k_workload():
     _check_all(prefill_inputs(w, DEV), "gdn_prefill_8k", chunk_size=64)
 
 
-def _check_sampled(inp, units, label, **kw):
-    """Full-size GPU run; oracle on sampled (sequence, head) units."""
-    say(f"prefill {label} (sampled units {units}) {kw}")
-    out, fin = _gpu(inp, **kw)
-    cu = inp["cu_seqlens"]
-    tol = TOL[inp["q"].dtype]
-    G = inp["v"].shape[2] // inp["q"].shape[2]            # value heads per q/k head
-    for (n, h) in units:
-        if cu is None:
-            rows = (slice(n, n + 1), slice(None))
-        else:
-            bounds = cu.cpu().numpy()
-            rows = (slice(0, 1), slice(int(bounds[n]), int(bounds[n + 1])))
-        sl = rows + (slice(h, h + 1),)
-        sub = {key: inp[key][sl].contiguous() for key in ("v", "beta", "log_alpha")}
-        for key in ("q", "k"):
-            sub[key] = inp[key][rows + (slice(h // G, h // G + 1),)].contiguous()
-        s0 = inp["initial_state"]
-        s0 = None if s0 is None else s0[n:n + 1, h:h + 1].contiguous()
-        ref_o, ref_s = oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["beta"], sub["log_alpha"],
-                                         initial_state=s0)
-        assert_close(f"out[{n},{h}]", out[sl], ref_o, tol)
-        assert_close(f"final_state[{n},{h}]", fin[n:n + 1, h:h + 1], ref_s, tol)
-    return out, fin
-
-
 @pytest.mark.slow
 def test_kda_prefill_32k_workload():
-    """B=2, H=32, T=32768, d=128, bf16, per-channel decay, S0 ~ N(0, 0.02^2);
-    every output is produced by the GPU, four (sequence, head) units are
-    checked against the oracle, and the whole output is checked for finiteness."""
+    """B=2, H=32, T=32768, d=128, bf16, per-channel decay, S0 ~ N(0, 0.02^2):
+    every element of out and final_state against the oracle (all host cores)."""
     w = WORKLOADS["kda_prefill_32k"]
-    inp = prefill_inputs(w, DEV)
-    out, fin = _check_sampled(inp, [(0, 0), (0, 17), (1, 5), (1, 31)], "kda_prefill_32k")
-    assert torch.isfinite(out.float()).all() and torch.isfinite(fin).all()
+    _check_all(prefill_inputs(w, DEV), "kda_prefill_32k (whole tensors)")
 
 
 @pytest.mark.slow
 def test_packed_gdn_256k_workload():
     """262144 tokens as 8 packed sequences (4096..61440 each), H=16, d=128."""
     w = WORKLOADS["packed_gdn_256k"]
-    inp = prefill_inputs(w, DEV)
-    lens = np.diff(inp["cu_seqlens"].cpu().numpy())
-    longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
-    out, fin = _check_sampled(inp, [(longest, 0), (shortest, 15), (3, 7)], "packed_gdn_256k")
-    assert torch.isfinite(out.float()).all() and torch.isfinite(fin).all()
+    _check_all(prefill_inputs(w, DEV), "packed_gdn_256k (whole tensors)")
 
 
 @pytest.mark.slow
 def test_gdn_gva_prefill_32k_workload():
     """B=1, T=32768, 16 query-key heads shared by 48 value heads, d=128,
-    bf16, per-head decay, S0 ~ N(0, 0.02^2): units from different groups and
-    from one group (they share q/k) checked against the oracle."""
+    bf16, per-head decay, S0 ~ N(0, 0.02^2): every element of out and
+    final_state against the oracle."""
     w = WORKLOADS["gdn_gva_prefill_32k"]
-    inp = prefill_inputs(w, DEV)
-    out, fin = _check_sampled(inp, [(0, 0), (0, 1), (0, 2), (0, 47)], "gdn_gva_prefill_32k")
-    assert torch.isfinite(out.float()).all() and torch.isfinite(fin).all()
+    _check_all(prefill_inputs(w, DEV), "gdn_gva_prefill_32k (whole tensors)")
 
 
 # -------------------------------------------------------- shape sweeps ----
@@ -390,6 +354,4 @@ def test_prefill_long_single_sequence():
     """One sequence of 65536 tokens (2048 chunks on one chain), 4 heads."""
     w = Workload("long", "prefill", heads=4, dk=128, dv=128, qkv_dtype=torch.bfloat16, gate="channel", batch=1,
                  seqlen=65536, init_state=True, seed=97)
-    inp = prefill_inputs(w, DEV)
-    out, fin = _check_sampled(inp, [(0, 0), (0, 3)], "long single sequence")
-    assert torch.isfinite(out.float()).all()
+    _check_all(prefill_inputs(w, DEV), "long single sequence (whole tensors)")
