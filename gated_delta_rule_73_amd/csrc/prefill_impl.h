@@ -11,22 +11,25 @@
 // inclusive in-chunk cumulative log-decay g_r (per key channel),
 //     A   = strict_tril(diag(b) (K e^g)(K e^-g)^T)           Gram with decay
 //     T   = (I + A)^-1                                        UT transform
-//     X   = (K e^g) S0^T,   U = T diag(b) (V - X)
+//     W_n = -T diag(b) (K e^g)                                WY factor (negated)
+//     U   = T diag(b) V + W_n S0^T
 //     O   = (Q e^g) S0^T + M U,   M = tril((Q e^g)(K e^-g)^T)
 //     S_C = S0 Diag(e^{g_C}) + U^T (K e^{g_C - g}).
+// (U = T diag(b) (V - (K e^g) S0^T) regrouped so that W_n, which does not
+// depend on the state, is formed once per chunk outside the serial chain.)
 //
 // Two kernels.  Everything that does not depend on the state (prefix sums of
 // the gates, decayed operands, the Gram matrices, T) is independent across
-// chunks, so prep_kernel computes it for every (chunk, head) at once and
-// writes one record per chunk to the workspace.  chain_kernel then walks the
+// chunks (W_n included), so prep_kernel computes it for every (chunk, head)
+// at once and writes one record per chunk to the workspace.  chain_kernel then walks the
 // chunks of each (sequence, head) in order: loader waves stream the records
 // (and the value slice) several chunks ahead into a double buffer in LDS, and
 // one chain wave per 16 value channels carries its part of the state
 // transposed (S^T: key rows x value columns) as fp32 MFMA accumulators.  In
-// that layout the state, W and U feed the next product straight from
+// that layout the state and U feed the next product straight from
 // registers (each lane's accumulator rows are exactly the k-indices its MFMA
-// operand fragment needs), so the serial chain X -> W -> U -> (O, S) reads LDS
-// only for the record's shared operands.
+// operand fragment needs), so the serial chain U -> (O, S) reads LDS only for
+// the record's shared operands.
 //
 // Precision (bf16 q/k/v).  Outputs reach ~15x their RMS, so an error bound of
 // 2e-2 x RMS on the largest element needs ~1e-3 relative accuracy on the

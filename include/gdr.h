@@ -141,7 +141,8 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  *  shape          host pointer, see gdr_prefill_shape.
  *  gate           GDR_GATE_HEAD or GDR_GATE_CHANNEL.
  *  qkv_dtype      dtype of q, k and v: GDR_BF16 or GDR_F32.
- *  gate_dtype     dtype of beta and log_alpha: GDR_F32.
+ *  gate_dtype     dtype of beta and log_alpha (both the same): GDR_F32 or
+ *                 GDR_BF16.
  *  out_dtype      dtype of out: GDR_F32 or GDR_BF16 (independent of q/k/v;
  *                 bf16 outputs are rounded to nearest even from fp32).
  *  q, k           [batch, seqlen, num_qk_heads, head_dim_k]
@@ -154,9 +155,16 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  *  cu_seqlens     NULL (dense) or int32 [num_seqs+1]: 0 = cu[0] <= cu[1] <=
  *                 ... <= cu[N] = seqlen (not checked: device memory).  Empty
  *                 sequences are allowed (their final state = initial state).
- *  chunk_size     tokens per chunk: 0 = automatic, else 16, 32 or 64.
- *  dv_slice       value channels one workgroup owns: 0 = automatic, else
- *                 16, 32 or 64 (a divisor of head_dim_v).
+ *  chunk_size     tokens per chunk: 0 = automatic (32 where compiled, else 16),
+ *                 else one of the compiled sizes below.
+ *  dv_slice       value channels one workgroup owns: 0 = automatic, else a
+ *                 compiled width below that divides head_dim_v.
+ *                 Compiled (q/k/v dtype: head_dim_k; chunk_size; dv_slice):
+ *                   bf16: {32, 64, 128}; 32; 16 or 32 (record and chain kernels)
+ *                   bf16: {32, 64, 128}; 64; 16 or 32 (single fused kernel,
+ *                         chosen by chunk_size 64)
+ *                   fp32: {16, 32, 64, 128}; 16 or 32; 16
+ *                 Any other request returns GDR_ERROR_NOT_SUPPORTED.
  *  scale          readout factor (1 for the printed equations).
  *  out            [batch, seqlen, num_heads, head_dim_v], dtype out_dtype.
  *                 Must not overlap any input.
@@ -170,9 +178,18 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  * a multiple of 16 up to 256; num_heads a multiple of num_qk_heads (when
  * that is not 0); the q/k/v/out/state base pointers 16-byte
  * aligned; beta 4-byte aligned; log_alpha 16-byte aligned for
- * GDR_GATE_CHANNEL, else 4-byte aligned.  Per-channel decay: the log-decay
- * summed over one chunk must stay above about -170 in every channel (the
- * chunk's operands are scaled around its midpoint in fp32 range).
+ * GDR_GATE_CHANNEL, else 4-byte aligned (halved for bf16 gates).  Per-channel
+ * decay: the log-decay summed over one chunk must stay above about -170 in
+ * every channel (the chunk's operands are scaled around its midpoint in fp32
+ * range).
+ * Operand range (bf16 q/k/v): v, the state and the intra-chunk update U enter
+ * the MFMA products as fp16.  Every |v| and every element of the state along
+ * the sequence must stay below 65504 (fp16's largest finite value; beyond it
+ * results become inf), and the RMS of v and of the state at or above about
+ * 1e-4 (fp16 numbers below 6.1e-5 are subnormal and lose relative precision:
+ * at RMS 1e-5 the error reaches several percent of RMS).  Measured within
+ * these bounds: out within about 1e-2 RMS of the exact recurrence.  fp32
+ * q/k/v carry everything in fp32 and have no such bound.
  * Work: one kernel computes every chunk's record into the workspace, a second
  * walks each sequence's chunks in order (per segment, when the workspace is
  * smaller than gdr_prefill_workspace_bytes reports); all on hip_stream.
@@ -223,15 +240,16 @@ gdr_status gdr_prefill_chunked_static(const gdr_prefill_shape *shape, gdr_gate g
  *                (0 = num_heads)
  *  q, k       [num_seqs, num_qk_heads, head_dim_k] dtype qkv_dtype
  *  v          [num_seqs, num_heads, head_dim_v]   dtype qkv_dtype
- *  beta       [num_seqs, num_heads]               fp32
+ *  beta       [num_seqs, num_heads]               dtype gate_dtype
  *  log_alpha  [num_seqs, num_heads] (GDR_GATE_HEAD) or
- *             [num_seqs, num_heads, head_dim_k] (GDR_GATE_CHANNEL), fp32
+ *             [num_seqs, num_heads, head_dim_k] (GDR_GATE_CHANNEL), dtype
+ *             gate_dtype (GDR_F32 or GDR_BF16, the same as beta)
  *  state      [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, read and
  *             written in place (must not overlap any other argument)
  *  out        [num_seqs, num_heads, head_dim_v]   dtype out_dtype (GDR_F32 or
  *             GDR_BF16, rounded to nearest even)
  * Limits: head_dim_k in {16, 32, 64, 128}; head_dim_v a multiple of 4 up to
- * 256; base pointers 16-byte aligned (gates 4-byte).
+ * 256; base pointers 16-byte aligned (gates aligned to their element size).
  */
 gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t num_qk_heads, int32_t head_dim_k,
                            int32_t head_dim_v, gdr_gate gate, gdr_dtype qkv_dtype,
@@ -267,9 +285,10 @@ gdr_status gdr_decode_step(int32_t num_seqs, int32_t num_heads, int32_t num_qk_h
  *
  *  q, k         [num_seqs, max_tokens, num_qk_heads, head_dim_k]  qkv_dtype
  *  v            [num_seqs, max_tokens, num_heads, head_dim_v]     qkv_dtype
- *  beta         [num_seqs, max_tokens, num_heads]                 fp32
+ *  beta         [num_seqs, max_tokens, num_heads]                 gate_dtype
  *  log_alpha    [num_seqs, max_tokens, num_heads] (GDR_GATE_HEAD) or
- *               [num_seqs, max_tokens, num_heads, head_dim_k]     fp32
+ *               [num_seqs, max_tokens, num_heads, head_dim_k]     gate_dtype
+ *               (gate_dtype GDR_F32 or GDR_BF16, the same for both)
  *  num_tokens, num_commit, state_slots   int32 [num_seqs] device arrays or NULL
  *  state_pool   [num_slots, num_heads, head_dim_v, head_dim_k] fp32, read and
  *               written in place (must not overlap any other argument)

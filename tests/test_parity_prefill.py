@@ -355,3 +355,23 @@ def test_prefill_long_single_sequence():
     w = Workload("long", "prefill", heads=4, dk=128, dv=128, qkv_dtype=torch.bfloat16, gate="channel", batch=1,
                  seqlen=65536, init_state=True, seed=97)
     _check_all(prefill_inputs(w, DEV), "long single sequence (whole tensors)")
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("gate", ["head", "channel"])
+@pytest.mark.parametrize("edge", ["low", "high"])
+def test_prefill_bf16_operand_range_edges(edge, gate, chunk):
+    """The bf16 prefill carries v and the state into its products as fp16.
+    At both documented edges of their range it still meets the bound: v and
+    S0 scaled down by 1e-4 (RMS of v 1e-4: fp16 subnormals begin at 6.1e-5),
+    and scaled up until the largest |v| is 60000 (fp16's largest finite value
+    is 65504; the state stays below it here)."""
+    inp = _small(128, 128, 2, 1024, gate, torch.bfloat16, True, seed=300 + chunk + (gate == "head"))
+    if edge == "low":
+        s = 1e-4
+    else:
+        s = 60000.0 / float(inp["v"].float().abs().max())
+    inp["v"] = (inp["v"].float() * s).to(torch.bfloat16)
+    inp["initial_state"] = inp["initial_state"] * s
+    say(f"  v scaled by {s:.4g}: max|v| = {float(inp['v'].float().abs().max()):.4g}")
+    _check_all(inp, f"operand range {edge} {gate}", chunk_size=chunk)
