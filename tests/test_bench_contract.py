@@ -30,3 +30,13 @@ def test_algorithmic_bytes():
     # multi-token decode: every state read, n_written written
     assert bench.decode_tokens_alg_bytes(2, 3, 4, 2, 16, 16, True, 4, 1) == \
         3 * 4 * 16 * 16 * 4 + 6 * (2 * 2 * 16 * 2 + 4 * (16 * 2 + 4 + 16 * 4 + 16 * 4))
+
+
+def test_prefill_roofline_accounting():
+    """The prefill's MFMA roof uses the chunked form's dense flops per
+    token-head at the stated chunk (4 C (dk + dv) + 6 dk dv); HBM beside it
+    counts bf16 outputs (2 bytes less per output element than fp32)."""
+    tok = 2 * 32768 * 32
+    assert bench.prefill_alg_flops(2, 32768, 32, 128, 128, 32) == tok * 131072
+    assert bench.prefill_alg_flops(2, 32768, 32, 128, 128, 64) == tok * 163840
+    assert bench.prefill_alg_bytes(2, 32768, 32, 128, 128, True, 2) == 3238002688
