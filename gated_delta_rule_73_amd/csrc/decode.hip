@@ -15,12 +15,13 @@
 // "Linear attention: a fixed-size memory in place of the cache" of that page,
 // applied row by row.
 //
-// Layout of the work: one 256-thread workgroup per (sequence, head); each row
-// is spread over DK/4 consecutive lanes that hold 4 consecutive columns each
-// (16-byte loads/stores, so a wave reads 1 KiB of contiguous state per
-// instruction).  The two row dot products are finished with cross-lane sums
-// inside the row's lane group.  Rows are independent, so a thread keeps RB
-// rows in flight at once to cover HBM latency.
+// Layout of the work: one workgroup per (sequence, head), 512 threads for
+// d_k >= 64.  A state row is spread over LPR = min(8, d_k / 4) lanes, lane l
+// holding the VPL four-column groups 4 l + 4 LPR j (j < VPL): a row group's
+// loads cover whole 128-byte lines, and each row's two dot products finish in
+// log2(LPR) DPP steps inside the lane group.  Every row of the state a thread
+// owns is requested before any is used, so the whole state is in flight at
+// once.
 #include <type_traits>
 
 #include "common.h"
@@ -28,90 +29,124 @@
 
 namespace gdr {
 
-// EXACT: d_v is a multiple of the rows one pass covers, so no row index
-// needs a bounds check (measured ~5% faster at d = 128); OUTB: bf16 outputs.
-// Value head h reads the q/k head h / G of HK (grouped value heads).  GT:
-// storage type of beta and log alpha (float or __bf16).
-template <int DK, bool KDA, typename QT, typename GT, int RB, bool EXACT, bool OUTB>
-__global__ __launch_bounds__(256) void decode_kernel(
+// Lane layout shared by both decode kernels (see the top of the file).
+template <int DK> constexpr int decode_threads() { return DK >= 64 ? 512 : 256; }
+template <int DK> constexpr int decode_lpr() { return DK / 4 < 8 ? DK / 4 : 8; }
+constexpr int kDecodeTokenBatch = 8;
+
+// Sum over aligned groups of W in {4, 8} lanes by DPP: swap neighbours, swap
+// pairs, then (W = 8) mirror each half-row of 8 lanes.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float x) {
+    static_assert(W == 4 || W == 8, "DPP lane groups of 4 or 8");
+#define GDR_DPP(y, ctrl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), ctrl, 0xF, 0xF, false))
+    x += GDR_DPP(x, 0xB1);                          // quad_perm [1, 0, 3, 2]
+    x += GDR_DPP(x, 0x4E);                          // quad_perm [2, 3, 0, 1]
+    if constexpr (W == 8) x += GDR_DPP(x, 0x141);   // row_half_mirror
+#undef GDR_DPP
+    return x;
+}
+
+// One token per (sequence, head), layout as described at the top of the file.
+// NR: rows per thread (the largest d_v the instance holds is NR x rows per
+// pass); OUTB: bf16 outputs.  Value head h reads the q/k head h / G of HK
+// (grouped value heads).  GT: storage type of beta and log alpha.
+template <int DK, bool KDA, typename QT, typename GT, int NR, bool OUTB>
+__global__ __launch_bounds__(decode_threads<DK>()) void decode_kernel(
     int H, int HK, int G, int DV, const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ v,
     const GT *__restrict__ beta, const GT *__restrict__ log_alpha, float *__restrict__ state,
     float scale, void *__restrict__ out) {
-    constexpr int LPR = DK / 4;          // lanes per state row
-    constexpr int RPP = 256 / LPR;       // rows covered by the workgroup per pass
-    const int unit = blockIdx.x;         // n * H + h
+    constexpr int NTH = decode_threads<DK>();
+    constexpr int LPR = decode_lpr<DK>();   // lanes per state row
+    constexpr int VPL = DK / (4 * LPR);            // four-column groups per lane and row
+    constexpr int RPP = NTH / LPR;                 // rows covered by the workgroup per pass
+    const int unit = blockIdx.x;                   // n * H + h
     const int qku = (unit / H) * HK + (unit % H) / G;
     const int lane = threadIdx.x % LPR;
     const int rsub = threadIdx.x / LPR;
-    const int c0 = lane * 4;
 
-    const float4 kv = load4(k + (size_t)qku * DK + c0);
-    const float4 qv = load4(q + (size_t)qku * DK + c0);
-    float4 a;
-    if constexpr (KDA) {
-        const float4 la = load4(log_alpha + (size_t)unit * DK + c0);
-        a = make_float4(__expf(la.x), __expf(la.y), __expf(la.z), __expf(la.w));
-    } else {
-        const float s = __expf(to_f32(log_alpha[unit]));
-        a = make_float4(s, s, s, s);
+    float4 kv[VPL], qv[VPL], a[VPL];
+    float kq = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int c = 4 * (lane + LPR * j);
+        kv[j] = load4(k + (size_t)qku * DK + c);
+        qv[j] = load4(q + (size_t)qku * DK + c);
+        if constexpr (KDA) {
+            const float4 la = load4(log_alpha + (size_t)unit * DK + c);
+            a[j] = make_float4(__expf(la.x), __expf(la.y), __expf(la.z), __expf(la.w));
+        }
+        kq += kv[j].x * qv[j].x + kv[j].y * qv[j].y + kv[j].z * qv[j].z + kv[j].w * qv[j].w;
+    }
+    if constexpr (!KDA) {
+        const float e = __expf(to_f32(log_alpha[unit]));
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) a[j] = make_float4(e, e, e, e);
     }
     const float b = to_f32(beta[unit]);
-    const float kq = group_sum<LPR>(kv.x * qv.x + kv.y * qv.y + kv.z * qv.z + kv.w * qv.w);
 
     float *S = state + (size_t)unit * DV * DK;
     const QT *vu = v + (size_t)unit * DV;
     using OT = typename std::conditional<OUTB, __bf16, float>::type;
     OT *ou = static_cast<OT *>(out) + (size_t)unit * DV;
-
-    for (int base = 0; base < DV; base += RPP * RB) {
-        f32x4 s[RB];
-        float vi[RB];
+    f32x4 s[NR][VPL];
+    float vi[NR];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int i = base + r * RPP + rsub;
-            if (EXACT || i < DV) {
-                s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)i * DK + c0));
-                vi[r] = to_f32(vu[i]);
-            }
+    for (int r = 0; r < NR; ++r) {
+        const int i = r * RPP + rsub;
+        if (i < DV) {
+#pragma unroll
+            for (int j = 0; j < VPL; ++j)
+                s[r][j] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4 *>(S + (size_t)i * DK + 4 * (lane + LPR * j)));
+            vi[r] = to_f32(vu[i]);
         }
+    }
+    kq = dpp_group_sum<LPR>(kq);
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int i = base + r * RPP + rsub;
-            // the group-sum below needs every lane of the row group; i < DV is
-            // uniform over the group (all its lanes share rsub), so skipping is safe
-            if (EXACT || i < DV) {
-                f32x4 t = s[r];
-                t[0] *= a.x; t[1] *= a.y; t[2] *= a.z; t[3] *= a.w;
-                float x = t[0] * kv.x + t[1] * kv.y + t[2] * kv.z + t[3] * kv.w;
-                float y = t[0] * qv.x + t[1] * qv.y + t[2] * qv.z + t[3] * qv.w;
-                x = group_sum<LPR>(x);
-                y = group_sum<LPR>(y);
-                const float u = b * (vi[r] - x);
-                t[0] += u * kv.x; t[1] += u * kv.y; t[2] += u * kv.z; t[3] += u * kv.w;
-                __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(S + (size_t)i * DK + c0));
-                if (lane == 0) ou[i] = (OT)(scale * (y + u * kq));
+    for (int r = 0; r < NR; ++r) {
+        const int i = r * RPP + rsub;
+        // i < DV is uniform over a row's lane group (they share rsub), so the
+        // DPP sums below see every lane of the group
+        if (i < DV) {
+            float x = 0.f, y = 0.f;
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                f32x4 &w = s[r][j];
+                w[0] *= a[j].x; w[1] *= a[j].y; w[2] *= a[j].z; w[3] *= a[j].w;
+                x += w[0] * kv[j].x + w[1] * kv[j].y + w[2] * kv[j].z + w[3] * kv[j].w;
+                y += w[0] * qv[j].x + w[1] * qv[j].y + w[2] * qv[j].z + w[3] * qv[j].w;
             }
+            x = dpp_group_sum<LPR>(x);
+            y = dpp_group_sum<LPR>(y);
+            const float u = b * (vi[r] - x);
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                f32x4 &w = s[r][j];
+                w[0] += u * kv[j].x; w[1] += u * kv[j].y; w[2] += u * kv[j].z; w[3] += u * kv[j].w;
+                __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(S + (size_t)i * DK + 4 * (lane + LPR * j)));
+            }
+            if (lane == 0) ou[i] = (OT)(scale * (y + u * kq));
         }
     }
 }
 
 template <int DK, bool KDA, typename QT, typename GT>
 static hipError_t launch_decode_t(const DecodeArgs &p, hipStream_t st) {
-    constexpr int LPR = DK / 4;
-    constexpr int RPP = 256 / LPR;
-    constexpr int RB = (RPP >= 64) ? 2 : (RPP >= 32 ? 4 : 8);
+    constexpr int NTH = decode_threads<DK>();
+    constexpr int RPP = NTH / decode_lpr<DK>();
     const unsigned grid = (unsigned)((size_t)p.num_seqs * p.num_heads);
-    const bool exact = p.dv % (RPP * RB) == 0;
-#define GDR_DECODE_LAUNCH(E, O)                                                                               \
-    hipLaunchKernelGGL((decode_kernel<DK, KDA, QT, GT, RB, E, O>), dim3(grid), dim3(256), 0, st, p.num_heads,  \
+#define GDR_DECODE_LAUNCH(NR, O)                                                                               \
+    hipLaunchKernelGGL((decode_kernel<DK, KDA, QT, GT, NR, O>), dim3(grid), dim3(NTH), 0, st, p.num_heads,      \
                        p.num_qk_heads, p.num_heads / p.num_qk_heads, p.dv, (const QT *)p.q, (const QT *)p.k,    \
                        (const QT *)p.v, (const GT *)p.beta, (const GT *)p.log_alpha, p.state, p.scale, p.out)
-    if (exact) {
-        if (p.out_bf16) GDR_DECODE_LAUNCH(true, true);
-        else GDR_DECODE_LAUNCH(true, false);
+    // rows per thread: enough for d_v <= 128, or for d_v <= 256
+    if (p.dv <= 128) {
+        if (p.out_bf16) GDR_DECODE_LAUNCH(div_up(128, RPP), true);
+        else GDR_DECODE_LAUNCH(div_up(128, RPP), false);
     } else {
-        if (p.out_bf16) GDR_DECODE_LAUNCH(false, true);
-        else GDR_DECODE_LAUNCH(false, false);
+        if (p.out_bf16) GDR_DECODE_LAUNCH(div_up(256, RPP), true);
+        else GDR_DECODE_LAUNCH(div_up(256, RPP), false);
     }
 #undef GDR_DECODE_LAUNCH
     return hipGetLastError();
@@ -162,27 +197,10 @@ struct DecodeTokensKArgs {
     void *out;
 };
 
-template <int DK> constexpr int decode_tokens_threads() { return DK >= 64 ? 512 : 256; }
-template <int DK> constexpr int decode_tokens_lpr() { return DK / 4 < 8 ? DK / 4 : 8; }
-constexpr int kDecodeTokenBatch = 8;
-
-// Sum over aligned groups of W in {4, 8} lanes by DPP: swap neighbours, swap
-// pairs, then (W = 8) mirror each half-row of 8 lanes.
-template <int W>
-__device__ __forceinline__ float dpp_group_sum(float x) {
-    static_assert(W == 4 || W == 8, "DPP lane groups of 4 or 8");
-#define GDR_DPP(y, ctrl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), ctrl, 0xF, 0xF, false))
-    x += GDR_DPP(x, 0xB1);                          // quad_perm [1, 0, 3, 2]
-    x += GDR_DPP(x, 0x4E);                          // quad_perm [2, 3, 0, 1]
-    if constexpr (W == 8) x += GDR_DPP(x, 0x141);   // row_half_mirror
-#undef GDR_DPP
-    return x;
-}
-
 template <int DK, bool KDA, typename QT, typename GT, int NR, bool OUTB>
-__global__ __launch_bounds__(decode_tokens_threads<DK>()) void decode_tokens_kernel(DecodeTokensKArgs p) {
-    constexpr int NTH = decode_tokens_threads<DK>();
-    constexpr int LPR = decode_tokens_lpr<DK>();   // lanes per state row
+__global__ __launch_bounds__(decode_threads<DK>()) void decode_tokens_kernel(DecodeTokensKArgs p) {
+    constexpr int NTH = decode_threads<DK>();
+    constexpr int LPR = decode_lpr<DK>();   // lanes per state row
     constexpr int VPL = DK / (4 * LPR);            // four-column groups per lane and row
     constexpr int RPP = NTH / LPR;                 // rows covered by the workgroup per pass
     constexpr int DVM = NR * RPP;                  // largest d_v this instance holds
@@ -307,8 +325,8 @@ __global__ __launch_bounds__(decode_tokens_threads<DK>()) void decode_tokens_ker
 
 template <int DK, bool KDA, typename QT, typename GT>
 static hipError_t launch_decode_tokens_t(const DecodeArgs &a, hipStream_t st) {
-    constexpr int NTH = decode_tokens_threads<DK>();
-    constexpr int RPP = NTH / decode_tokens_lpr<DK>();
+    constexpr int NTH = decode_threads<DK>();
+    constexpr int RPP = NTH / decode_lpr<DK>();
     DecodeTokensKArgs p;
     p.H = a.num_heads;
     p.HK = a.num_qk_heads;
