@@ -15,7 +15,10 @@ Further workloads are timed in their own loops and reported beside the step
   value heads, T=32768);
 - the speculative multi-token decode over a pool of state slots (256
   sequences x 48 value heads, 4 tokens each, a per-sequence committed prefix);
-- the layer prologue on the grouped shape (T=32768, 10240 channels).
+- the layer prologue on the grouped shape (T=32768, 10240 channels);
+- one decode step of that layer fed from its projected channels, the fused
+  call (prologue and state update in one kernel) beside the two calls it
+  replaces.
 Two measured ceilings of the same box are reported with them: a large bf16
 GEMM (the library GEMM, for the MFMA side) and a 512 MiB read-modify-write
 (for the HBM side).
@@ -375,6 +378,40 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
             "frac_of_split_bf16_peak": round(fl / t / 1e12 / (BF16_MFMA_PEAK_TFLOPS / 3), 4)}
         del bi, bc
         torch.cuda.empty_cache()
+
+    # one decode step fed from the layer's projected channels: the fused call
+    # against the two calls it replaces (layer prologue, then decode step)
+    from workloads import decode_prologue_inputs
+    wdp = WORKLOADS["decode_prologue_256x48"]
+    print(f"[bench] {wdp.name}", file=sys.stderr, flush=True)
+    dp = decode_prologue_inputs(wdp, dev)
+    N, H, Hk, dk, dv = wdp.batch, wdp.heads, wdp.qk_heads, wdp.dk, wdp.dv
+    x1, a1, b1 = dp["x"][:, 0].contiguous(), dp["a_logit"][:, 0].contiguous(), dp["b_logit"][:, 0].contiguous()
+    x3, a3, b3 = dp["x"], dp["a_logit"], dp["b_logit"]
+    dout = torch.empty(N, H, dv, dtype=torch.float32, device=dev)
+    kw = dict(num_qk_heads=Hk, head_dim_k=dk, head_dim_v=dv, conv_state=dp["conv_state"])
+    fused = lambda: gdr.gdr_decode_step_prologue(x1, dp["conv_weight"], a1, b1, dp["state"], out=dout, **kw)
+
+    def unfused():
+        q, k, v, beta, la = gdr.gdr_layer_prologue(x3, dp["conv_weight"], a3, b3, **kw)
+        gdr.gdr_decode_step(q[:, 0], k[:, 0], v[:, 0], beta[:, 0], la[:, 0], dp["state"], out=dout)
+
+    res["decode_with_prologue"] = {
+        "workload": f"{wdp.name}: one token for each of {N} sequences x {H} value heads ({Hk} q/k heads), d={dk}, "
+                    f"from bf16 projected channels ({2 * Hk * dk + H * dv} per token) with a convolution state: "
+                    f"width-4 convolution, q/k L2 norm, per-head gates, then the state update; fp32 out"}
+    C = 2 * Hk * dk + H * dv
+    common = N * H * dv * dk * 4 * 2 + N * C * 2 + N * 3 * C * 2 * 2 + C * 16 + N * H * 4 * 2 + N * H * dv * 4
+    qkv_rt = 2 * (N * (2 * Hk * dk + H * dv) * 2 + N * H * 4 * 2)   # q, k, v (bf16) and gates written, read back
+    for name, f, by in (("fused", fused, common), ("unfused", unfused, common + qkv_rt)):
+        for _ in range(args.warmup):
+            f()
+        t, med, mn = time_calls(f, args.steps)
+        res["decode_with_prologue"][name] = {
+            "us_per_call": round(t * 1e6, 2), "us_median": round(med * 1e6, 2), "us_min": round(mn * 1e6, 2),
+            "alg_bytes": by, "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    res["decode_with_prologue"]["bytes_saved_per_call"] = qkv_rt
+    del dp, dout
     return res
 
 

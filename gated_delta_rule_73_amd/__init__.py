@@ -22,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["gdr_prefill_chunked", "gdr_prefill_chunked_static", "gdr_decode_step", "gdr_decode_tokens", "gdr_layer_prologue",
+__all__ = ["gdr_prefill_chunked", "gdr_prefill_chunked_static", "gdr_decode_step", "gdr_decode_step_prologue", "gdr_decode_tokens", "gdr_layer_prologue",
            "gdr_prefill_backward", "prefill_chunked", "decode_step", "decode_tokens", "layer_prologue",
            "prefill_backward",
            "gdr_state_bytes", "GdrError", "load_library", "library_path"]
@@ -81,6 +81,9 @@ def load_library():
         lib.gdr_layer_prologue.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, p, p, p, p, p, i32,
                                            p, p, p, p, p, p, p, p]
         lib.gdr_layer_prologue.restype = ctypes.c_int
+        lib.gdr_decode_step_prologue.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 p, p, p, p, i32, p, p, p, ctypes.c_float, p, p]
+        lib.gdr_decode_step_prologue.restype = ctypes.c_int
         lib.gdr_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, i32]
         lib.gdr_prefill_backward_workspace_bytes.restype = sz
         lib.gdr_prefill_backward.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -377,6 +380,44 @@ def gdr_layer_prologue(x, conv_weight, a_logit, b_logit, *, num_qk_heads: int, h
                                   flags, _ptr(a_logit), _ptr(b_logit), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                   _ptr(log_alpha), _stream(dev)))
     return q, k, v, beta, log_alpha
+
+
+def gdr_decode_step_prologue(x, conv_weight, a_logit, b_logit, state, *, num_qk_heads: int, head_dim_k: int,
+                             head_dim_v: int, conv_state=None, update_conv_state: bool = True, silu: bool = False,
+                             qk_norm: bool = True, scale: float = 1.0, out=None, out_dtype=torch.float32):
+    """One decode step from the token's projected channels: the layer prologue
+    (as :func:`gdr_layer_prologue` with T = 1) fused with the state update (as
+    :func:`gdr_decode_step`).  x [N, C] (bf16 or fp32), C = 2 Hk dk + H dv;
+    conv_weight [C, 4] fp32; a_logit [N, H] or [N, H, dk] and b_logit [N, H]
+    fp32; state [N, H, dv, dk] fp32, updated in place; conv_state [N, 3, C]
+    (x's dtype) or None (zeros), advanced in place when update_conv_state.
+    Returns out [N, H, dv]."""
+    lib = load_library()
+    dev = x.device
+    N, C = x.shape
+    H = b_logit.shape[-1]
+    Hk, dk, dv = num_qk_heads, head_dim_k, head_dim_v
+    if C != 2 * Hk * dk + H * dv or b_logit.shape != (N, H) or state.shape != (N, H, dv, dk):
+        raise ValueError(f"x must be [N, 2*Hk*dk + H*dv] = [{N}, {2 * Hk * dk + H * dv}], b_logit [N, H], "
+                         f"state [N, H, dv, dk]")
+    gate = GDR_GATE_HEAD if a_logit.dim() == 2 else GDR_GATE_CHANNEL
+    _need(x, "x", None, dev)
+    _need(conv_weight, "conv_weight", torch.float32, dev)
+    _need(a_logit, "a_logit", torch.float32, dev)
+    _need(b_logit, "b_logit", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    _need(conv_state, "conv_state", x.dtype, dev)
+    if conv_state is not None and conv_state.shape != (N, 3, C):
+        raise ValueError(f"conv_state must be [{N}, 3, {C}]")
+    if out is None:
+        out = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", None, dev)
+    flags = (GDR_PROLOGUE_SILU if silu else 0) | (GDR_PROLOGUE_QK_NORM if qk_norm else 0)
+    _check(lib.gdr_decode_step_prologue(N, H, Hk, dk, dv, gate, _dtype_code(x), _dtype_code(out), _ptr(x),
+                                        _ptr(conv_weight), _ptr(conv_state),
+                                        _ptr(conv_state) if update_conv_state else None, flags, _ptr(a_logit),
+                                        _ptr(b_logit), _ptr(state), float(scale), _ptr(out), _stream(dev)))
+    return out
 
 
 prefill_chunked = gdr_prefill_chunked

@@ -175,6 +175,235 @@ hipError_t launch_decode(const DecodeArgs &p, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode step with the layer prologue fused in: for each (sequence, value
+// head) the workgroup forms its own q, k (of its q/k head) and v from the
+// token's projected channels x and the convolution state -- the width-4 causal
+// convolution, the optional SiLU and per-head q/k L2 norm, in the layer
+// prologue's order of operations -- and the gates beta = sigmoid(b),
+// log alpha = -softplus(a), then runs the decode update above.  q, k, v and
+// the gates never leave the chip and stay fp32 (the unfused calls store them
+// in x's dtype in between).  Value heads that share a
+// q/k head each recompute it (a few hundred flops).  The convolution state is
+// only read here; decode_conv_shift_kernel advances it afterwards on the same
+// stream, which keeps an in-place update safe.
+struct DecodePrologueKArgs {
+    int H, HK, G, DV, C;
+    const void *x, *cs_in;
+    const float *w, *a_logit, *b_logit;
+    float *state;
+    float scale;
+    void *out;
+};
+
+// one channel's convolution output for the token: taps on x_{t-3}, x_{t-2},
+// x_{t-1} (convolution state rows 0, 1, 2) and x_t, in the layer prologue's
+// order, then the optional SiLU
+template <typename XT, bool SILU>
+__device__ __forceinline__ float conv1(const DecodePrologueKArgs &p, int n, int ch) {
+    const XT *x = static_cast<const XT *>(p.x);
+    const XT *cs = static_cast<const XT *>(p.cs_in);
+    const float4 w = *reinterpret_cast<const float4 *>(p.w + (size_t)ch * 4);
+    float h3 = 0.f, h2 = 0.f, h1 = 0.f;
+    if (cs) {
+        h3 = to_f32(cs[((size_t)n * 3 + 0) * p.C + ch]);
+        h2 = to_f32(cs[((size_t)n * 3 + 1) * p.C + ch]);
+        h1 = to_f32(cs[((size_t)n * 3 + 2) * p.C + ch]);
+    }
+    float y = w.x * h3 + w.y * h2 + w.z * h1 + w.w * to_f32(x[(size_t)n * p.C + ch]);
+    if constexpr (SILU) y = y / (1.f + __expf(-y));
+    return y;
+}
+
+template <int DK, bool KDA, typename XT, int NR, bool SILU, bool NORM, bool OUTB>
+__global__ __launch_bounds__(decode_threads<DK>()) void decode_prologue_kernel(DecodePrologueKArgs p) {
+    constexpr int NTH = decode_threads<DK>();
+    constexpr int LPR = decode_lpr<DK>();
+    constexpr int VPL = DK / (4 * LPR);
+    constexpr int RPP = NTH / LPR;
+    constexpr int DVM = NR * RPP;                  // largest d_v this instance holds
+    const int unit = blockIdx.x;                   // n * H + h
+    const int n = unit / p.H, h = unit % p.H, hq = h / p.G;
+    const int tid = threadIdx.x;
+    const int lane = tid % LPR;
+    const int rsub = tid / LPR;
+    const int DV = p.DV;
+    const int qk = p.HK * DK;                      // channels of q (and of k)
+
+    // the state first: every row this thread owns in flight while the
+    // prologue runs
+    float *S = p.state + (size_t)unit * DV * DK;
+    f32x4 s[NR][VPL];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int i = r * RPP + rsub;
+        if (i < DV) {
+#pragma unroll
+            for (int j = 0; j < VPL; ++j)
+                s[r][j] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4 *>(S + (size_t)i * DK + 4 * (lane + LPR * j)));
+        }
+    }
+
+    // the prologue, one channel per thread: q, k of head hq, v of head h and,
+    // per channel, alpha = exp(-softplus(a))
+    __shared__ float sq[DK], sk[DK], sv[DVM], sa[KDA ? DK : 1], sn[2];
+    auto alpha_of = [](float al) { return __expf(-(fmaxf(al, 0.f) + log1pf(__expf(-fabsf(al))))); };
+    for (int c = tid; c < 2 * DK + DV; c += NTH) {
+        if (c < DK) sq[c] = conv1<XT, SILU>(p, n, hq * DK + c);
+        else if (c < 2 * DK) sk[c - DK] = conv1<XT, SILU>(p, n, qk + hq * DK + c - DK);
+        else sv[c - 2 * DK] = conv1<XT, SILU>(p, n, 2 * qk + h * DV + c - 2 * DK);
+    }
+    if constexpr (KDA)
+        for (int c = tid; c < DK; c += NTH) sa[c] = alpha_of(p.a_logit[(size_t)unit * DK + c]);
+    __syncthreads();
+    if constexpr (NORM) {
+        // per-head L2 norms of q and k: wave 0 sums q, wave 1 sums k
+        if (tid < 128) {
+            const float *src = tid < 64 ? sq : sk;
+            float ss = 0.f;
+            for (int c = tid % 64; c < DK; c += 64) ss += src[c] * src[c];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+            if (tid % 64 == 0) sn[tid / 64] = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+        }
+        __syncthreads();
+    }
+    const float scq = NORM ? sn[0] : 1.f, sck = NORM ? sn[1] : 1.f;
+
+    float4 kv[VPL], qv[VPL], a[VPL];
+    float kq = 0.f;
+    const float eh = KDA ? 0.f : alpha_of(p.a_logit[unit]);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int c = 4 * (lane + LPR * j);
+        qv[j] = make_float4(sq[c] * scq, sq[c + 1] * scq, sq[c + 2] * scq, sq[c + 3] * scq);
+        kv[j] = make_float4(sk[c] * sck, sk[c + 1] * sck, sk[c + 2] * sck, sk[c + 3] * sck);
+        if constexpr (KDA) a[j] = make_float4(sa[c], sa[c + 1], sa[c + 2], sa[c + 3]);
+        else a[j] = make_float4(eh, eh, eh, eh);
+        kq += kv[j].x * qv[j].x + kv[j].y * qv[j].y + kv[j].z * qv[j].z + kv[j].w * qv[j].w;
+    }
+    kq = dpp_group_sum<LPR>(kq);
+    const float b = 1.f / (1.f + __expf(-p.b_logit[unit]));   // sigmoid(b)
+
+    using OT = typename std::conditional<OUTB, __bf16, float>::type;
+    OT *ou = static_cast<OT *>(p.out) + (size_t)unit * DV;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int i = r * RPP + rsub;
+        // i < DV is uniform over a row's lane group (they share rsub)
+        if (i < DV) {
+            float xx = 0.f, yy = 0.f;
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                f32x4 &w = s[r][j];
+                w[0] *= a[j].x; w[1] *= a[j].y; w[2] *= a[j].z; w[3] *= a[j].w;
+                xx += w[0] * kv[j].x + w[1] * kv[j].y + w[2] * kv[j].z + w[3] * kv[j].w;
+                yy += w[0] * qv[j].x + w[1] * qv[j].y + w[2] * qv[j].z + w[3] * qv[j].w;
+            }
+            xx = dpp_group_sum<LPR>(xx);
+            yy = dpp_group_sum<LPR>(yy);
+            const float u = b * (sv[i] - xx);
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                f32x4 &w = s[r][j];
+                w[0] += u * kv[j].x; w[1] += u * kv[j].y; w[2] += u * kv[j].z; w[3] += u * kv[j].w;
+                __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(S + (size_t)i * DK + 4 * (lane + LPR * j)));
+            }
+            if (lane == 0) ou[i] = (OT)(p.scale * (yy + u * kq));
+        }
+    }
+}
+
+// The new convolution state of each sequence: rows (x_{t-2}, x_{t-1}, x_t),
+// i.e. the old rows 1 and 2 and the token's input.  Eight channels per thread,
+// both old rows read before any row is written (in place safe).
+template <typename XT>
+__global__ __launch_bounds__(256) void decode_conv_shift_kernel(int N, int C, const XT *__restrict__ x,
+                                                                const XT *cs_in, XT *cs_out) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int CV = C / 8;
+    if (i >= (long)N * CV) return;
+    const int n = (int)(i / CV), c = (int)(i % CV) * 8;
+    XT r[3][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[0][e] = r[1][e] = (XT)0.f;
+    if (cs_in) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            r[0][e] = cs_in[((size_t)n * 3 + 1) * C + c + e];
+            r[1][e] = cs_in[((size_t)n * 3 + 2) * C + c + e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[2][e] = x[(size_t)n * C + c + e];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs_out[((size_t)n * 3 + j) * C + c + e] = r[j][e];
+}
+
+template <int DK, bool KDA, typename XT>
+static hipError_t launch_decode_prologue_t(const DecodePrologueArgs &a, hipStream_t st) {
+    constexpr int NTH = decode_threads<DK>();
+    constexpr int RPP = NTH / decode_lpr<DK>();
+    DecodePrologueKArgs p;
+    p.H = a.num_heads;
+    p.HK = a.num_qk_heads;
+    p.G = a.num_heads / a.num_qk_heads;
+    p.DV = a.dv;
+    p.C = 2 * a.num_qk_heads * DK + a.num_heads * a.dv;
+    p.x = a.x;
+    p.cs_in = a.conv_state_in;
+    p.w = a.conv_weight;
+    p.a_logit = a.a_logit;
+    p.b_logit = a.b_logit;
+    p.state = a.state;
+    p.scale = a.scale;
+    p.out = a.out;
+    const unsigned grid = (unsigned)((size_t)a.num_seqs * a.num_heads);
+#define GDR_DP(NR, S, N, O) \
+    hipLaunchKernelGGL((decode_prologue_kernel<DK, KDA, XT, NR, S, N, O>), dim3(grid), dim3(NTH), 0, st, p)
+#define GDR_DP_NR(NR)                                                              \
+    do {                                                                           \
+        if (a.silu) {                                                              \
+            if (a.qk_norm) { if (a.out_bf16) GDR_DP(NR, true, true, true); else GDR_DP(NR, true, true, false); }     \
+            else { if (a.out_bf16) GDR_DP(NR, true, false, true); else GDR_DP(NR, true, false, false); }           \
+        } else {                                                                   \
+            if (a.qk_norm) { if (a.out_bf16) GDR_DP(NR, false, true, true); else GDR_DP(NR, false, true, false); }   \
+            else { if (a.out_bf16) GDR_DP(NR, false, false, true); else GDR_DP(NR, false, false, false); }         \
+        }                                                                          \
+    } while (0)
+    if (a.dv <= 128) GDR_DP_NR(div_up(128, RPP));
+    else GDR_DP_NR(div_up(256, RPP));
+#undef GDR_DP_NR
+#undef GDR_DP
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.conv_state_out) return e;
+    const long work = (long)a.num_seqs * (p.C / 8);
+    hipLaunchKernelGGL((decode_conv_shift_kernel<XT>), dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st,
+                       a.num_seqs, p.C, static_cast<const XT *>(a.x), static_cast<const XT *>(a.conv_state_in),
+                       static_cast<XT *>(a.conv_state_out));
+    return hipGetLastError();
+}
+
+template <bool KDA, typename XT>
+static hipError_t launch_decode_prologue_dk(const DecodePrologueArgs &a, hipStream_t st) {
+    switch (a.dk) {
+        case 16: return launch_decode_prologue_t<16, KDA, XT>(a, st);
+        case 32: return launch_decode_prologue_t<32, KDA, XT>(a, st);
+        case 64: return launch_decode_prologue_t<64, KDA, XT>(a, st);
+        case 128: return launch_decode_prologue_t<128, KDA, XT>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_prologue(const DecodePrologueArgs &a, hipStream_t st) {
+    if (a.num_seqs == 0 || a.num_heads == 0) return hipSuccess;
+    if (a.kda) return a.x_bf16 ? launch_decode_prologue_dk<true, __bf16>(a, st) : launch_decode_prologue_dk<true, float>(a, st);
+    return a.x_bf16 ? launch_decode_prologue_dk<false, __bf16>(a, st) : launch_decode_prologue_dk<false, float>(a, st);
+}
+
+// ---------------------------------------------------------------------------
 // Multi-token decode over a pool of state slots.  One workgroup of NTH threads
 // per (sequence, value head); the whole d_v x d_k state stays in registers
 // while the tokens of the sequence are applied one after another, each as in

@@ -691,4 +691,77 @@ gdr_status gdr_layer_prologue(const gdr_prefill_shape *shape, gdr_gate gate, gdr
     return launch_status(gdr::launch_prologue(a, static_cast<hipStream_t>(hip_stream)), "gdr_layer_prologue");
 }
 
+gdr_status gdr_decode_step_prologue(int32_t num_seqs, int32_t num_heads, int32_t num_qk_heads, int32_t head_dim_k,
+                                    int32_t head_dim_v, gdr_gate gate, gdr_dtype x_dtype, gdr_dtype out_dtype,
+                                    const void *x, const float *conv_weight, const void *conv_state_in,
+                                    void *conv_state_out, int32_t flags, const float *a_logit, const float *b_logit,
+                                    float *state, float scale, void *out, void *hip_stream) {
+    if (num_seqs < 0 || num_heads < 1 || head_dim_k < 1 || head_dim_v < 1)
+        return fail(GDR_ERROR_INVALID_VALUE, "bad shape (num_seqs=%d heads=%d dk=%d dv=%d)", num_seqs, num_heads,
+                    head_dim_k, head_dim_v);
+    int hk = 0;
+    if (resolve_qk_heads(num_heads, num_qk_heads, hk) != GDR_SUCCESS) return GDR_ERROR_INVALID_VALUE;
+    if (!valid_gate(gate)) return fail(GDR_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)gate);
+    if (!valid_dtype(x_dtype) || !valid_dtype(out_dtype))
+        return fail(GDR_ERROR_INVALID_VALUE, "unknown dtype (x=%d out=%d)", (int)x_dtype, (int)out_dtype);
+    if (flags & ~(GDR_PROLOGUE_SILU | GDR_PROLOGUE_QK_NORM))
+        return fail(GDR_ERROR_INVALID_VALUE, "unknown flags 0x%x", (unsigned)flags);
+    const int dk = head_dim_k, dv = head_dim_v;
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_k %d not in {16, 32, 64, 128}", dk);
+    if (dv % 8 != 0 || dv > 256) return fail(GDR_ERROR_NOT_SUPPORTED, "head_dim_v %d not a multiple of 8 <= 256", dv);
+    const int64_t C = 2 * (int64_t)hk * dk + (int64_t)num_heads * dv;
+    if ((int64_t)num_seqs * num_heads > INT32_MAX || (int64_t)num_seqs * C > INT32_MAX)
+        return fail(GDR_ERROR_INVALID_VALUE, "problem too large");
+    if (num_seqs == 0) return ok();
+    if (!x || !conv_weight || !a_logit || !b_logit || !state || !out)
+        return fail(GDR_ERROR_INVALID_VALUE, "x, conv_weight, a_logit, b_logit, state and out must be non-NULL");
+    const bool kda = gate == GDR_GATE_CHANNEL;
+    const void *a16[] = {x, conv_weight, conv_state_in, conv_state_out, state, a_logit};
+    const char *n16[] = {"x", "conv_weight", "conv_state_in", "conv_state_out", "state", "a_logit"};
+    for (int i = 0; i < 6; ++i)
+        if (!aligned(a16[i], i == 5 && !kda ? 4 : 16))
+            return fail(GDR_ERROR_INVALID_VALUE, "%s is not %d-byte aligned", n16[i], i == 5 && !kda ? 4 : 16);
+    if (!aligned(b_logit, 4) || !aligned(out, dsize(out_dtype)))
+        return fail(GDR_ERROR_INVALID_VALUE, "b_logit and out must be aligned to their element size");
+    const size_t es = dsize(x_dtype), ng = (size_t)num_seqs * num_heads;
+    const size_t st_bytes = (size_t)num_seqs * 3 * C * es;
+    const Range in[] = {range("x", x, (size_t)num_seqs * C * es), range("conv_weight", conv_weight, (size_t)C * 16),
+                        range("conv_state_in", conv_state_in, conv_state_in ? st_bytes : 0),
+                        range("a_logit", a_logit, (kda ? ng * dk : ng) * 4), range("b_logit", b_logit, ng * 4)};
+    const Range outs[] = {range("state", state, ng * dv * dk * 4), range("out", out, ng * dv * dsize(out_dtype)),
+                          range("conv_state_out", conv_state_out, conv_state_out ? st_bytes : 0)};
+    for (const Range &o : outs) {
+        for (const Range &r : in) {
+            const bool same_state = o.lo == reinterpret_cast<uintptr_t>(conv_state_out) &&
+                                    r.lo == reinterpret_cast<uintptr_t>(conv_state_in) && conv_state_in == conv_state_out;
+            if (overlaps(o, r) && !same_state) return fail(GDR_ERROR_INVALID_VALUE, "%s overlaps %s", o.name, r.name);
+        }
+        for (const Range &o2 : outs)
+            if (&o2 != &o && overlaps(o, o2)) return fail(GDR_ERROR_INVALID_VALUE, "%s overlaps %s", o.name, o2.name);
+    }
+    gdr::DecodePrologueArgs a{};
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_qk_heads = hk;
+    a.dk = dk;
+    a.dv = dv;
+    a.kda = kda;
+    a.x_bf16 = x_dtype == GDR_BF16;
+    a.out_bf16 = out_dtype == GDR_BF16;
+    a.silu = (flags & GDR_PROLOGUE_SILU) != 0;
+    a.qk_norm = (flags & GDR_PROLOGUE_QK_NORM) != 0;
+    a.x = x;
+    a.conv_weight = conv_weight;
+    a.conv_state_in = conv_state_in;
+    a.conv_state_out = conv_state_out;
+    a.a_logit = a_logit;
+    a.b_logit = b_logit;
+    a.state = state;
+    a.scale = scale;
+    a.out = out;
+    return launch_status(gdr::launch_decode_prologue(a, static_cast<hipStream_t>(hip_stream)),
+                         "gdr_decode_step_prologue");
+}
+
 }  // extern "C"

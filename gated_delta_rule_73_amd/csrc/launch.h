@@ -144,6 +144,24 @@ hipError_t launch_schedule(const int32_t *cu, int n, int chunk, int32_t *order, 
 
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t st);
+
+// Decode step with the layer prologue fused in (decode.hip): the token's
+// projected channels x and the convolution state give q, k, v and the gates
+// inside the decode kernel; a second small kernel then shifts the
+// convolution state (so it may be updated in place).
+struct DecodePrologueArgs {
+    int num_seqs, num_heads, num_qk_heads, dk, dv;
+    bool kda, x_bf16, out_bf16, silu, qk_norm;
+    const void *x;                  // [num_seqs, C], C = 2 Hk dk + H dv
+    const float *conv_weight;       // [C, 4]
+    const void *conv_state_in;      // [num_seqs, 3, C] or NULL (zeros)
+    void *conv_state_out;           // [num_seqs, 3, C] or NULL; may equal conv_state_in
+    const float *a_logit, *b_logit; // [num_seqs, H(, dk)], [num_seqs, H]
+    float *state;                   // [num_seqs, H, dv, dk]
+    float scale;
+    void *out;                      // [num_seqs, H, dv]
+};
+hipError_t launch_decode_prologue(const DecodePrologueArgs &p, hipStream_t st);
 hipError_t launch_decode_tokens(const DecodeArgs &p, hipStream_t st);
 
 // True when a prefill kernel is compiled for this combination.

@@ -356,6 +356,52 @@ gdr_status gdr_layer_prologue(const gdr_prefill_shape *shape, gdr_gate gate, gdr
                               const int32_t *cu_seqlens, int32_t flags, const float *a_logit, const float *b_logit,
                               void *q, void *k, void *v, float *beta, float *log_alpha, void *hip_stream);
 
+/*
+ * Decode step with the layer prologue fused in: one new token for each of
+ * num_seqs sequences, given as its projected channels x rather than as q, k,
+ * v and gates.  The result is that of gdr_layer_prologue with seqlen = 1
+ * (batch = num_seqs, dense) followed by gdr_decode_step on its outputs, except
+ * that q, k, v and the gates stay fp32 on the chip in between (the two calls
+ * store q, k, v in x_dtype): they never reach device memory (page
+ * "Qwen3.8-Flash-Next and GLM-5.3-Flash share a 3:1 long-context pattern",
+ * section "Kimi Delta Attention extends recurrent memory control": the short
+ * convolution in front of the recurrence; page "How the New Flash Models
+ * Work...", section "Serving: prefill and decode are different problems": the
+ * convolution state travels with the recurrent state).
+ *
+ *  num_heads, num_qk_heads, head_dim_k, head_dim_v, gate   as gdr_decode_step
+ *  x_dtype        dtype of x and of the convolution states: GDR_BF16 or GDR_F32
+ *  out_dtype      dtype of out: GDR_F32 or GDR_BF16
+ *  x              [num_seqs, C], C = 2 num_qk_heads head_dim_k + num_heads
+ *                 head_dim_v: q, k, v channels as for gdr_layer_prologue
+ *  conv_weight    [C, 4] fp32 (tap j multiplies x_{t-3+j})
+ *  conv_state_in  [num_seqs, 3, C] x_dtype, or NULL (zeros)
+ *  conv_state_out [num_seqs, 3, C] x_dtype, or NULL (not written); may equal
+ *                 conv_state_in (advanced in place)
+ *  flags          GDR_PROLOGUE_SILU | GDR_PROLOGUE_QK_NORM, as for
+ *                 gdr_layer_prologue
+ *  a_logit        [num_seqs, num_heads] (GDR_GATE_HEAD) or
+ *                 [num_seqs, num_heads, head_dim_k] fp32: log_alpha = -softplus(a)
+ *  b_logit        [num_seqs, num_heads] fp32: beta = sigmoid(b)
+ *  state          [num_seqs, num_heads, head_dim_v, head_dim_k] fp32, read and
+ *                 written in place
+ *  out            [num_seqs, num_heads, head_dim_v], dtype out_dtype
+ * Limits: head_dim_k in {16, 32, 64, 128}; head_dim_v a multiple of 8 up to
+ * 256; x, the convolution states, conv_weight and state 16-byte aligned (and
+ * a_logit for GDR_GATE_CHANNEL), other gates 4-byte aligned.  state, out and
+ * conv_state_out must not overlap the inputs or each other (except
+ * conv_state_out == conv_state_in).
+ * Work: one kernel for the prologue and the state update, a second small one
+ * that advances the convolution state (after the first on hip_stream, so the
+ * in-place update is safe).  Returns GDR_SUCCESS or an error status (nothing
+ * enqueued on error).
+ */
+gdr_status gdr_decode_step_prologue(int32_t num_seqs, int32_t num_heads, int32_t num_qk_heads, int32_t head_dim_k,
+                                    int32_t head_dim_v, gdr_gate gate, gdr_dtype x_dtype, gdr_dtype out_dtype,
+                                    const void *x, const float *conv_weight, const void *conv_state_in,
+                                    void *conv_state_out, int32_t flags, const float *a_logit, const float *b_logit,
+                                    float *state, float scale, void *out, void *hip_stream);
+
 /* Bytes of fp32 recurrent state for num_seqs x num_heads heads of d_v x d_k
  * (the per-layer state the pages size in their state-size table). */
 uint64_t gdr_state_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim_k, int64_t head_dim_v);

@@ -102,6 +102,11 @@ WORKLOADS = {
     "prologue_gdn_32k": Workload("prologue_gdn_32k", "prologue", heads=48, qk_heads=16, dk=128, dv=128,
                                  qkv_dtype=torch.bfloat16, gate="head", batch=1, seqlen=32768, init_state=True,
                                  seed=7),
+    # one decode step of that layer fed from its projected channels: the
+    # prologue (convolution with its state, q/k norm, gates) fused with the
+    # state update, 256 sequences
+    "decode_prologue_256x48": Workload("decode_prologue_256x48", "decode", heads=48, qk_heads=16, dk=128, dv=128,
+                                       qkv_dtype=torch.bfloat16, gate="head", batch=256, init_state=True, seed=11),
 }
 
 
@@ -281,3 +286,24 @@ def prologue_inputs(w: Workload, device="cpu", *, seqlen: int | None = None, bat
     st = torch.randn(N, 3, C, generator=g, device=device, dtype=f32).to(dt) if init_state else None
     return {"x": x, "conv_weight": wt, "a_logit": a, "b_logit": b, "conv_state": st, "cu_seqlens": cu,
             "num_qk_heads": Hk, "head_dim_k": dk, "head_dim_v": dv}
+
+
+def decode_prologue_inputs(w: Workload, device="cpu", *, num_seqs: int | None = None, steps: int = 1,
+                           heads: int | None = None, qk_heads: int | None = None, dk: int | None = None,
+                           dv: int | None = None, gate: str | None = None, seed: int | None = None,
+                           init_conv_state: bool = True, x_dtype=None):
+    """Decode steps fed from projected channels: the prologue inputs of
+    ``steps`` tokens per sequence (x [N, steps, C], taps, gate logits and a
+    convolution state, drawn as by prologue_inputs) and a recurrent state
+    [N, H, dv, dk] ~ N(0, 0.02^2) drawn after them."""
+    N = w.batch if num_seqs is None else num_seqs
+    H = w.heads if heads is None else heads
+    Hk = qk_heads or (w.qk_heads if heads is None and w.qk_heads else H)
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    s = w.seed if seed is None else seed
+    p = prologue_inputs(w, device, seqlen=steps, batch=N, heads=H, qk_heads=Hk, dk=dk, dv=dv, gate=gate, seed=s,
+                        init_state=init_conv_state, x_dtype=x_dtype)
+    g = _gen(device, s + 7919)
+    p["state"] = 0.02 * torch.randn(N, H, dv, dk, generator=g, device=device, dtype=torch.float32)
+    return p
