@@ -195,21 +195,31 @@ struct DecodePrologueKArgs {
     void *out;
 };
 
-// one channel's convolution output for the token: taps on x_{t-3}, x_{t-2},
-// x_{t-1} (convolution state rows 0, 1, 2) and x_t, in the layer prologue's
-// order, then the optional SiLU
-template <typename XT, bool SILU>
-__device__ __forceinline__ float conv1(const DecodePrologueKArgs &p, int n, int ch) {
+// one channel's convolution inputs for the token: its taps and x_{t-3},
+// x_{t-2}, x_{t-1} (convolution state rows 0, 1, 2), x_t
+struct ConvIn {
+    float4 w;
+    float h3, h2, h1, x0;
+};
+template <typename XT>
+__device__ __forceinline__ ConvIn conv_in(const DecodePrologueKArgs &p, int n, int ch) {
     const XT *x = static_cast<const XT *>(p.x);
     const XT *cs = static_cast<const XT *>(p.cs_in);
-    const float4 w = *reinterpret_cast<const float4 *>(p.w + (size_t)ch * 4);
-    float h3 = 0.f, h2 = 0.f, h1 = 0.f;
+    ConvIn c;
+    c.w = *reinterpret_cast<const float4 *>(p.w + (size_t)ch * 4);
+    c.h3 = c.h2 = c.h1 = 0.f;
     if (cs) {
-        h3 = to_f32(cs[((size_t)n * 3 + 0) * p.C + ch]);
-        h2 = to_f32(cs[((size_t)n * 3 + 1) * p.C + ch]);
-        h1 = to_f32(cs[((size_t)n * 3 + 2) * p.C + ch]);
+        c.h3 = to_f32(cs[((size_t)n * 3 + 0) * p.C + ch]);
+        c.h2 = to_f32(cs[((size_t)n * 3 + 1) * p.C + ch]);
+        c.h1 = to_f32(cs[((size_t)n * 3 + 2) * p.C + ch]);
     }
-    float y = w.x * h3 + w.y * h2 + w.z * h1 + w.w * to_f32(x[(size_t)n * p.C + ch]);
+    c.x0 = to_f32(x[(size_t)n * p.C + ch]);
+    return c;
+}
+// the convolution output in the layer prologue's order, then the optional SiLU
+template <bool SILU>
+__device__ __forceinline__ float conv_out(const ConvIn &c) {
+    float y = c.w.x * c.h3 + c.w.y * c.h2 + c.w.z * c.h1 + c.w.w * c.x0;
     if constexpr (SILU) y = y / (1.f + __expf(-y));
     return y;
 }
@@ -229,8 +239,23 @@ __global__ __launch_bounds__(decode_threads<DK>()) void decode_prologue_kernel(D
     const int DV = p.DV;
     const int qk = p.HK * DK;                      // channels of q (and of k)
 
-    // the state first: every row this thread owns in flight while the
-    // prologue runs
+    // the prologue, one channel per thread: q, k of head hq, v of head h and,
+    // per channel, alpha = exp(-softplus(a)).  The inputs of a thread's first
+    // channel are requested before the state (loads complete in order, so the
+    // prologue does not wait for the state), the state right after them.
+    __shared__ float sq[DK], sk[DK], sv[DVM], sa[KDA ? DK : 1], sn[2];
+    auto alpha_of = [](float al) { return __expf(-(fmaxf(al, 0.f) + log1pf(__expf(-fabsf(al))))); };
+    auto channel = [&](int c) { return c < DK ? hq * DK + c : c < 2 * DK ? qk + hq * DK + c - DK : 2 * qk + h * DV + c - 2 * DK; };
+    auto put = [&](int c, float y) {
+        if (c < DK) sq[c] = y;
+        else if (c < 2 * DK) sk[c - DK] = y;
+        else sv[c - 2 * DK] = y;
+    };
+    const int total = 2 * DK + DV;
+    ConvIn first{};
+    if (tid < total) first = conv_in<XT>(p, n, channel(tid));
+    const float al0 = (KDA && tid < DK) ? p.a_logit[(size_t)unit * DK + tid] : 0.f;
+
     float *S = p.state + (size_t)unit * DV * DK;
     f32x4 s[NR][VPL];
 #pragma unroll
@@ -244,17 +269,12 @@ __global__ __launch_bounds__(decode_threads<DK>()) void decode_prologue_kernel(D
         }
     }
 
-    // the prologue, one channel per thread: q, k of head hq, v of head h and,
-    // per channel, alpha = exp(-softplus(a))
-    __shared__ float sq[DK], sk[DK], sv[DVM], sa[KDA ? DK : 1], sn[2];
-    auto alpha_of = [](float al) { return __expf(-(fmaxf(al, 0.f) + log1pf(__expf(-fabsf(al))))); };
-    for (int c = tid; c < 2 * DK + DV; c += NTH) {
-        if (c < DK) sq[c] = conv1<XT, SILU>(p, n, hq * DK + c);
-        else if (c < 2 * DK) sk[c - DK] = conv1<XT, SILU>(p, n, qk + hq * DK + c - DK);
-        else sv[c - 2 * DK] = conv1<XT, SILU>(p, n, 2 * qk + h * DV + c - 2 * DK);
+    if (tid < total) put(tid, conv_out<SILU>(first));
+    for (int c = tid + NTH; c < total; c += NTH) put(c, conv_out<SILU>(conv_in<XT>(p, n, channel(c))));
+    if constexpr (KDA) {
+        if (tid < DK) sa[tid] = alpha_of(al0);
+        for (int c = tid + NTH; c < DK; c += NTH) sa[c] = alpha_of(p.a_logit[(size_t)unit * DK + c]);
     }
-    if constexpr (KDA)
-        for (int c = tid; c < DK; c += NTH) sa[c] = alpha_of(p.a_logit[(size_t)unit * DK + c]);
     __syncthreads();
     if constexpr (NORM) {
         // per-head L2 norms of q and k: wave 0 sums q, wave 1 sums k
