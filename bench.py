@@ -141,6 +141,22 @@ def time_calls(fn, steps, between=None):
     return sum(t) / len(t), statistics.median(t), min(t)
 
 
+def time_back_to_back(fn, steps):
+    """Mean seconds per call of fn over `steps` calls issued back to back
+    between one pair of HIP events on the current stream: no event sits
+    between two calls, so the figure carries no per-call event cost."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / steps
+
+
 def time_per_launch(fn, steps):
     """Mean seconds per call of fn over `steps` back-to-back calls."""
     return time_calls(fn, steps)[0]
@@ -333,6 +349,7 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     for _ in range(args.warmup):
         f()
     t, med, mn = time_calls(f, args.steps)
+    tb = time_back_to_back(f, args.steps)
     n_written = int((m["num_commit"] > 0).sum())
     by = decode_tokens_alg_bytes(N, K, H, Hk, dk, dv, False, 4, n_written)
     res["multi_token_decode"] = {
@@ -341,7 +358,11 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
                     f"({n_written} of {N} sequences write their state), per-head decay, fp32 out",
         "us_per_call": round(t * 1e6, 2), "us_median": round(med * 1e6, 2), "us_min": round(mn * 1e6, 2),
         "Mtok_s": round(N * K / t / 1e6, 4), "alg_bytes": by,
-        "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+        "GBps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+        # the per-call figures carry one event pair per call, which costs this
+        # call about 12 us of device time; calls issued back to back do not
+        "us_back_to_back": round(tb * 1e6, 2),
+        "frac_of_hbm_peak_back_to_back": round(by / tb / 1e9 / HBM_PEAK_GBS, 4)}
     del m, mout
 
     from workloads import backward_cotangents
