@@ -818,7 +818,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half)
 // column tile and both row tiles (each state row or column is then read
 // once); the others deal the tiles round-robin to the waves.
 template <int DK, bool KDA, typename IT, typename GT>
-__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
+__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p, long nitems) {
     constexpr int C = kBC, NT = kGradThreads, NW = NT / 64, PK = DK + 4, PV = 128 + 4, PB = PK > PV ? PK : PV;
     constexpr int UV = div_up(2 * 128 / 16, NW);   // C x d_v tiles per wave (max)
     static_assert(NW >= 8 && NW % 2 == 0, "the C x C phases deal tiles to waves 0-7");
@@ -833,48 +833,101 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
     __shared__ float sPb[8][C], sPb2[2][C];   // d beta partials (per value tile / column tile)
     __shared__ float sPc[2][DK];              // column partials of gK3 o K
     __shared__ float sPr[DK / 16][C];         // row partials of dg (per-head decay)
-    const int H = p.H, DV = p.dv, h = blockIdx.y, tid = threadIdx.x;
-    const long rc = blockIdx.x;
-    const ChunkLoc L = locate(p, rc);
-    if (L.len <= 0) return;
-    const int w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4, hq = h / p.G;
+    const int H = p.H, DV = p.dv;
     const IT *q = static_cast<const IT *>(p.q), *k = static_cast<const IT *>(p.k), *v = static_cast<const IT *>(p.v);
-    const float *rec = p.rec + (rc * H + h) * p.rec_stride;
-    const float *S0 = p.states + (rc * H + h) * (long)DV * DK;
-    const float *dS = p.dstates + (rc * H + h) * (long)DV * DK;
-    const __amdgpu_buffer_rsrc_t rS0 = buffer_of(S0, (long)DV * DK), rdS = buffer_of(dS, (long)DV * DK);
     const int ntv = 2 * (DV / 16);
 
-    // ---- loads: every load of the chunk's inputs is issued first (all in
-    //      flight together, from clamped rows), then the LDS stores consume them
+    // Persistent workgroups: items (chunk slot rc, head h), item = rc H + h,
+    // blockIdx.x, + gridDim.x, ...  While one item's phases run, the next
+    // item's inputs and its S0 rows for Y are already in flight into
+    // registers: the LDS holds one workgroup per CU, so without
+    // this a CU's loads and its products would take turns.  (Barriers wait
+    // only for LDS operations, so those loads stay in flight across them.)
     constexpr int NKL = div_up(C * DK / 4, NT), NVL = div_up(C * 128 / 4, NT), NTL = C * C / NT;
+    constexpr int NSB = DK / 32;                   // 32-wide k blocks of a state row
     static_assert(NTL >= 1 && C * C % NT == 0, "load tiling");
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 kv[NKL], qv[NKL], gv[NKL], vv[NVL], dd[NVL];
-    float tv[NTL], mv[NTL];
+    float tv[NTL], mv[NTL], bb = 0.f, gg = 0.f;
+    // wave w's rows 16 w + lr of S0, k = 32 blk + 16 hh + 4 lq .. + 3: the B
+    // operand of its Y product
+    f32x4 s0r[NSB][2];
+    auto item_loc = [&](long it) {
+        ChunkLoc L;
+        L.n = 0, L.tok0 = 0, L.len = 0;
+        if (it < nitems) L = locate(p, it / H);
+        return L;
+    };
+    auto fetch_inputs = [&](long it, const ChunkLoc &L) {
+        const int tid = threadIdx.x;
+        const long rc = it / H;
+        const int h = (int)(it % H), hq = h / p.G;
+        const float *rec = p.rec + (rc * H + h) * p.rec_stride;
 #pragma unroll
-    for (int u = 0; u < NKL; ++u) {
-        const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        const long t = L.tok0 + min(r, L.len - 1);
-        kv[u] = load4(k + (t * p.Hk + hq) * DK + j);
-        qv[u] = load4(q + (t * p.Hk + hq) * DK + j);
-        gv[u] = KDA ? gate4<GT>(p.log_alpha, (t * H + h) * DK + j) : z4;
-    }
+        for (int u = 0; u < NKL; ++u) {
+            const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
+            const long t = L.tok0 + min(r, L.len - 1);
+            kv[u] = load4(k + (t * p.Hk + hq) * DK + j);
+            qv[u] = load4(q + (t * p.Hk + hq) * DK + j);
+            gv[u] = KDA ? gate4<GT>(p.log_alpha, (t * H + h) * DK + j) : z4;
+        }
 #pragma unroll
-    for (int u = 0; u < NVL; ++u) {
-        const int e = min(tid + NT * u, C * DV / 4 - 1), r = e / (DV / 4), i = (e % (DV / 4)) * 4;
-        const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DV + i;
-        vv[u] = load4(v + o);
-        dd[u] = *reinterpret_cast<const float4 *>(p.d_out + o);
-    }
+        for (int u = 0; u < NVL; ++u) {
+            const int e = min(tid + NT * u, C * DV / 4 - 1), r = e / (DV / 4), i = (e % (DV / 4)) * 4;
+            const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DV + i;
+            vv[u] = load4(v + o);
+            dd[u] = *reinterpret_cast<const float4 *>(p.d_out + o);
+        }
 #pragma unroll
-    for (int u = 0; u < NTL; ++u) {
-        tv[u] = rec[R::T + tid + NT * u];
-        mv[u] = rec[R::M + tid + NT * u];
-    }
-    const long obg = (L.tok0 + min(tid & (C - 1), L.len - 1)) * H + h;
-    const float bb = gate1<GT>(p.beta, obg), gg = KDA ? 0.f : gate1<GT>(p.log_alpha, obg);
+        for (int u = 0; u < NTL; ++u) {
+            tv[u] = rec[R::T + tid + NT * u];
+            mv[u] = rec[R::M + tid + NT * u];
+        }
+        const long obg = (L.tok0 + min(tid & (C - 1), L.len - 1)) * H + h;
+        bb = gate1<GT>(p.beta, obg);
+        gg = KDA ? 0.f : gate1<GT>(p.log_alpha, obg);
+    };
+    auto fetch_rows = [&](const float *base, f32x4 (&r)[NSB][2]) {
+        const int w = threadIdx.x >> 6, lr = threadIdx.x & 15, lq = (threadIdx.x >> 4) & 3;
+        if (w >= DV / 16) return;
+        const __amdgpu_buffer_rsrc_t rs = buffer_of(base, (long)DV * DK);
+#pragma unroll
+        for (int blk = 0; blk < NSB; ++blk)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) r[blk][hh] = bload4(rs, ((16 * w + lr) * DK + 4 * lq) * 4, (32 * blk + 16 * hh) * 4);
+    };
+    auto states_of = [&](long it) { return p.states + it * (long)DV * DK; };    // item = rc H + h
+    auto dstates_of = [&](long it) { return p.dstates + it * (long)DV * DK; };
+    (void)dstates_of;
 
+    long item = blockIdx.x;
+    ChunkLoc L = item_loc(item);
+    if (L.len > 0) {
+        fetch_inputs(item, L);
+        fetch_rows(states_of(item), s0r);
+    }
+    // (an empty chunk slot ends the packed batch's slots, so every later item is empty too)
+    while (L.len > 0) {
+    // The lane index, opaque to the compiler once per item: the per-lane LDS
+    // addresses of the phases are then formed where they are used, as in a
+    // workgroup that runs one item, instead of being hoisted out of the loop
+    // and held in registers across it.
+    int opaque_zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
+    const int tid = ((int)threadIdx.x + opaque_zero) & (NT - 1);   // (the mask keeps tid's range known)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lr = l & 15, lq = l >> 4;
+    const bool has_v = w < DV / 16;
+    const long rc = item / H;
+    const int h = (int)(item % H);
+    const float *rec = p.rec + (rc * H + h) * p.rec_stride;
+    const float *S0 = states_of(item);
+    const float *dS = dstates_of(item);
+    const __amdgpu_buffer_rsrc_t rS0 = buffer_of(S0, (long)DV * DK), rdS = buffer_of(dS, (long)DV * DK);
+    const long nxt = item + gridDim.x;
+    const ChunkLoc Ln = item_loc(nxt);
+    const bool more = Ln.len > 0;
+
+    // ---- the item's inputs from registers into LDS
 #pragma unroll
     for (int u = 0; u < NKL; ++u) {
         const int e = tid + NT * u;
@@ -904,7 +957,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         sb[tid] = tid < L.len ? bb : 0.f;
         if (!KDA) sg[tid] = tid < L.len ? gg : 0.f;
     }
-    __syncthreads();
+    // q stays in registers for the last phases (raw q from its LDS copy there)
+    float4 qkeep[NKL];
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) qkeep[u] = qv[u];
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) fetch_inputs(nxt, Ln);
     // inclusive cumulative sums of the log decay over the chunk's rows
     if (KDA) {
         // four adjacent lanes per channel, eight rows each
@@ -935,7 +994,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
             sgl[0] = total;
         }
     }
-    __syncthreads();
+    lds_barrier();
     auto gval = [&](int r, int j) { return KDA ? sGg[r][j] : sg[r]; };
     auto mval = [&](int j) { return KDA ? sm[j] : sm[0]; };
     auto glast = [&](int j) { return KDA ? sgl[j] : sgl[0]; };
@@ -943,25 +1002,24 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         const int r = e / DK, j = e % DK;
         sX1[r][j] = sX2[r][j] * fexp(gval(r, j));
     }
-    __syncthreads();
+    lds_barrier();
 
     // Phases over C x d_v tiles: wave w takes value tile w (16 value rows)
     // and both row tiles, so each state row is read from memory once.
     const int nvt = DV / 16;
-    const bool has_v = w < nvt;
     // ---- Y = V - (K e^g) S0^T
     if (has_v) {
         f32x4 acc[2] = {zero4(), zero4()};
         tile_mma_nt<DK, 2>(acc, DK, [&](int q, int mi, int kb, int lk) { return lds4(&sX1[16 * q + mi][kb + lk]); },
-                           [&](int, int ni, int kb, int lk) {
-                               return bload4(rS0, ((16 * w + ni) * DK + lk) * 4, kb * 4);
-                           });
+                           [&](int, int, int kb, int) { return s0r[kb >> 5][(kb >> 4) & 1]; });
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sB1[16 * q + 4 * lq + i][16 * w + lr] -= acc[q][i];
     }
-    __syncthreads();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) fetch_rows(states_of(nxt), s0r);
     // ---- U = T diag(b) Y;  dU = M^T dO' (then + K_end dS^T below);
     //      K_end = K e^{g_C - g} built in place of K e^g (no longer read)
     f32x4 u[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
@@ -975,7 +1033,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         const int r = e / DK, j = e % DK;
         sX1[r][j] = sX2[r][j] * fexp(glast(j) - gval(r, j));
     }
-    __syncthreads();
+    lds_barrier();
     if (has_v) {
         tile_mma_nt<DK, 2>(du, DK, [&](int q, int mi, int kb, int lk) { return lds4(&sX1[16 * q + mi][kb + lk]); },
                            [&](int, int ni, int kb, int lk) {
@@ -990,7 +1048,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
                 sB3[r][16 * w + lr] = du[q][i];
             }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- dT = dU (diag(b) Y)^T;  Z = T^T dU (kept in registers);  d beta (value part)
     if (w < 4) {
         const int rt = w & 1, ct = w >> 1;
@@ -1018,7 +1076,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- dV = dY = diag(b) Z (written out and kept in place of dU);
     //      E1 = dT T^T;  shifted operands;  Q e^{g-m} in place of Y
 #pragma unroll
@@ -1053,7 +1111,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         const int e = tid + NT * u;
         if (e >= C * DK / 4) continue;
         const int r = e / (DK / 4), j = (e % (DK / 4)) * 4;
-        const float4 q4 = r < L.len ? qv[u] : z4;
+        const float4 q4 = r < L.len ? qkeep[u] : z4;
         sB1[r][j] = q4.x * fexp(gval(r, j) - mval(j));
         sB1[r][j + 1] = q4.y * fexp(gval(r, j + 1) - mval(j + 1));
         sB1[r][j + 2] = q4.z * fexp(gval(r, j + 2) - mval(j + 2));
@@ -1064,7 +1122,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         for (int it = 0; it < DV / 16; ++it) s += sPb[it][tid];
         sdb[tid] = s;
     }
-    __syncthreads();
+    lds_barrier();
     // ---- dA = strict_tril(-T^T E1), d beta (Gram part), diag(b) dA;  dM = tril(dO' U^T)
     if (w < 4) {
         const int rt = w & 1, ct = w >> 1;
@@ -1096,24 +1154,34 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
             sdM[r][c] = c <= r ? a[i] : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- dO' (sB4), dY (sB3) and U (sB2) as split bf16 operands, in place:
     //      each row's 528 bytes become [hi of its 128 values | lo | unused],
     //      the value index permuted within blocks of 32 (kperm32).  One wave
     //      converts a whole row (one read, then the writes), so no other wave
     //      touches a row while it changes form.
     static_assert(PV * 4 >= 2 * 128 * 2, "a row holds its split form");
-    for (int rr = w; rr < 3 * C; rr += NW) {
-        float *row = rr < C ? sB4[rr] : rr < 2 * C ? sB3[rr - C] : sB2[rr - 2 * C];
-        const float2 x = *reinterpret_cast<const float2 *>(row + 2 * l);
-        unsigned hu, lu;
-        split2(x.x, x.y, hu, lu);
+    {
+        // (all of the wave's row reads are issued before the first write, so
+        // their LDS latencies overlap; a row is written only by the wave
+        // that read it, after its read)
+        static_assert(3 * C % NW == 0, "rows per wave");
+        constexpr int NRR = 3 * C / NW;
+        auto row_of = [&](int rr) { return rr < C ? sB4[rr] : rr < 2 * C ? sB3[rr - C] : sB2[rr - 2 * C]; };
+        float2 xs[NRR];
+#pragma unroll
+        for (int i = 0; i < NRR; ++i) xs[i] = *reinterpret_cast<const float2 *>(row_of(w + NW * i) + 2 * l);
         const int pos = (2 * l & ~31) + kperm32(2 * l);
-        __bf16 *rb = reinterpret_cast<__bf16 *>(row);
-        *reinterpret_cast<unsigned *>(rb + pos) = hu;
-        *reinterpret_cast<unsigned *>(rb + 128 + pos) = lu;
+#pragma unroll
+        for (int i = 0; i < NRR; ++i) {
+            unsigned hu, lu;
+            split2(xs[i].x, xs[i].y, hu, lu);
+            __bf16 *rb = reinterpret_cast<__bf16 *>(row_of(w + NW * i));
+            *reinterpret_cast<unsigned *>(rb + pos) = hu;
+            *reinterpret_cast<unsigned *>(rb + 128 + pos) = lu;
+        }
     }
-    __syncthreads();
+    lds_barrier();
     auto plane = [&](float (*buf)[PV], int r) { return reinterpret_cast<const __bf16 *>(buf[r]); };
 
     // ---- per (row, key channel): dq, dk and the log-decay gradient dg.
@@ -1224,7 +1292,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- log-decay gradient: reverse cumulative sum of dg, plus the
     //      chunk-end terms (through e^{g_C}) on every row; d beta
     if (KDA) {
@@ -1259,6 +1327,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p) {
         if (l < L.len) p.dla[(L.tok0 + l) * H + h] = gc + d;
     }
     if (tid < L.len) p.dbeta[(L.tok0 + tid) * H + h] = sdb[tid] + sPb2[0][tid] + sPb2[1][tid];
+    lds_barrier();   // the next item's inputs overwrite this one's LDS
+    item = nxt;
+    L = Ln;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1307,7 +1379,10 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp0, hipSt
         hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(2 * scan_blocks), dim3(128), 0, st, kp, (int)scan_blocks);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (nrc > 0) {
-        hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(kGradThreads), 0, st, kp);
+        // one grad workgroup fills a CU's LDS: one persistent workgroup per CU
+        const long nitems = nrc * a.num_heads;
+        const unsigned ggrid = (unsigned)std::min<long>(nitems, cus);
+        hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT, GT>), dim3(ggrid), dim3(kGradThreads), 0, st, kp, nitems);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         if (kp.G > 1) {
             const long n4 = (long)a.batch * a.seqlen * kp.Hk * (DK / 4);

@@ -35,4 +35,10 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __host__ __device__ constexpr int div_up(int a, int b) { return (a + b - 1) / b; }
 
+// Workgroup barrier that waits only for this wave's LDS operations: loads
+// in flight to registers or to LDS keep going across it (the compiler's own
+// barrier would drain them).  It orders LDS accesses only; waves that fill
+// LDS with LDS-direct loads wait for them explicitly before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace gdr

@@ -886,11 +886,6 @@ __device__ __forceinline__ void lds_direct_load16(const void *src, void *lds) {
 #endif
 }
 
-// Workgroup barrier that waits only for this wave's LDS operations: loads
-// in flight to registers or to LDS keep going across it (the compiler's own
-// barrier would drain them).  Waves that fill LDS with LDS-direct loads wait
-// for them explicitly before it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct ChainKArgs {
     int T, H, DV, num_seqs;
