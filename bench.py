@@ -50,7 +50,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 PROFILE_PMC = os.path.join(ROOT, "profiles", "prefill_kda_32k_traffic.json")
 # the sources that define the headline prefill's two kernels and their launch
-KERNEL_SOURCES = ["prefill_impl.h", "prefill_shapes.h", "prefill_bf16_kda.hip", "prefill.hip"]
+KERNEL_SOURCES = ["prefill_impl.h", "prefill_shapes.h", "prefill_bf16_kda.hip", "prefill.hip", "common.h"]
 
 
 def kernel_source_hash() -> str:
