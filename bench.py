@@ -248,7 +248,9 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     g2 = prefill_inputs(w2, dev)
     res["kda_prefill_32k_bf16_out"] = prefill_entry(
         w2, g2, f"{w2.name} writing its outputs in bf16 (rounded to nearest even) instead of fp32: B=2, T=32768, "
-                "H=32, d=128, bf16 q/k/v, per-channel decay, S0 given", out_dtype=torch.bfloat16)
+                "H=32, d=128, bf16 q/k/v, per-channel decay, S0 given; not parity-equal to the fp32-output line: "
+                "its parity test allows the output rounding on top of the bound (tol x RMS + 2^-8 |ref|), since "
+                "rounding alone exceeds 2e-2 x RMS on the largest outputs", out_dtype=torch.bfloat16)
     del g2
     print(f"[bench] {w2.name} with bf16 gates", file=sys.stderr, flush=True)
     g2 = prefill_inputs(w2, dev, gate_dtype=torch.bfloat16)
