@@ -402,6 +402,36 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
         del bi, bc
         torch.cuda.empty_cache()
 
+    # the KDA 32K backward inside a 4 GB workspace: time segments (the library
+    # takes the longest segments that fit, as found here)
+    wb = WORKLOADS["kda_backward_32k"]
+    print(f"[bench] {wb.name} in a 4 GB workspace", file=sys.stderr, flush=True)
+    bi = prefill_inputs(wb, dev)
+    bc = backward_cotangents(bi, wb.seed, dev)
+    B, T, Hk, dk = bi["q"].shape
+    H, dv = bi["v"].shape[2:]
+    cap = 4_000_000_000
+    ws_of = lambda s: gdr.gdr_prefill_backward_workspace_bytes(bi["q"], bi["v"], bi["log_alpha"], segment_chunks=s)
+    nct = -(-T // 32)
+    S = max(s for s in range(16, nct) if 0 < ws_of(s) <= cap)
+    ws = torch.empty(ws_of(S), dtype=torch.uint8, device=dev)
+    f = lambda: gdr.gdr_prefill_backward(bi["q"], bi["k"], bi["v"], bi["beta"], bi["log_alpha"], bc["d_out"],
+                                         initial_state=bi["initial_state"], d_final_state=bc["d_final_state"],
+                                         workspace=ws)
+    for _ in range(max(1, min(args.warmup, 2))):
+        f()
+    steps = max(1, min(args.steps, 5))
+    t, med, mn = time_calls(f, steps)
+    res["prefill_backward"]["kda_backward_32k_in_4GB"] = {
+        "workload": f"kda_backward_32k with a workspace of at most {cap} bytes: segments of {S} chunks "
+                    f"({-(-nct // S)} segments; the one-pass workspace is "
+                    f"{gdr.gdr_prefill_backward_workspace_bytes(bi['q'], bi['v'], bi['log_alpha'])} bytes); "
+                    "gradients equal to the one-pass call's bit for bit",
+        "workspace_bytes": ws.numel(), "segment_chunks": S, "calls": steps, "us_per_call": round(t * 1e6, 1),
+        "us_median": round(med * 1e6, 1), "us_min": round(mn * 1e6, 1), "Mtok_s": round(B * T / t / 1e6, 3)}
+    del bi, bc, ws
+    torch.cuda.empty_cache()
+
     # one decode step fed from the layer's projected channels: the fused call
     # against the two calls it replaces (layer prologue, then decode step)
     from workloads import decode_prologue_inputs

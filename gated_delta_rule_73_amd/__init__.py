@@ -23,7 +23,7 @@ import os
 import torch
 
 __all__ = ["gdr_prefill_chunked", "gdr_prefill_chunked_static", "gdr_decode_step", "gdr_decode_step_prologue", "gdr_decode_tokens", "gdr_layer_prologue",
-           "gdr_prefill_backward", "prefill_chunked", "decode_step", "decode_tokens", "layer_prologue",
+           "gdr_prefill_backward", "gdr_prefill_backward_workspace_bytes", "prefill_chunked", "decode_step", "decode_tokens", "layer_prologue",
            "prefill_backward",
            "gdr_state_bytes", "GdrError", "load_library", "library_path"]
 
@@ -48,7 +48,7 @@ class PrefillShape(ctypes.Structure):
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("num_qk_heads", ctypes.c_int32)]
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 _lib = None
@@ -86,6 +86,8 @@ def load_library():
         lib.gdr_decode_step_prologue.restype = ctypes.c_int
         lib.gdr_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, i32]
         lib.gdr_prefill_backward_workspace_bytes.restype = sz
+        lib.gdr_prefill_backward_segment_workspace_bytes.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, i32]
+        lib.gdr_prefill_backward_segment_workspace_bytes.restype = sz
         lib.gdr_prefill_backward.argtypes = [ctypes.POINTER(PrefillShape), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              p, p, p, p, p, p, p, ctypes.c_float, p, p, p, p, p, p, p, p, p, sz, p]
         lib.gdr_prefill_backward.restype = ctypes.c_int
@@ -226,13 +228,32 @@ def gdr_prefill_chunked_static(q, k, v, beta, log_alpha, *, initial_state=None, 
     return out, final_state
 
 
+def gdr_prefill_backward_workspace_bytes(q, v, log_alpha, *, cu_seqlens=None, segment_chunks: int = 0) -> int:
+    """Workspace bytes :func:`gdr_prefill_backward` needs for these shapes: one
+    pass (segment_chunks 0), or a dense batch in time segments of
+    segment_chunks >= 16 chunks (0 if that is not possible)."""
+    lib = load_library()
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
+    gate = GDR_GATE_HEAD if log_alpha.dim() == 3 else GDR_GATE_CHANNEL
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    shape = PrefillShape(B, T, H, dk, dv, N, Hk)
+    if segment_chunks:
+        if cu_seqlens is not None:
+            return 0
+        return int(lib.gdr_prefill_backward_segment_workspace_bytes(ctypes.byref(shape), gate, int(segment_chunks)))
+    return int(lib.gdr_prefill_backward_workspace_bytes(ctypes.byref(shape), gate, int(cu_seqlens is not None)))
+
+
 def gdr_prefill_backward(q, k, v, beta, log_alpha, d_out, *, initial_state=None, d_final_state=None,
                          cu_seqlens=None, scale: float = 1.0, output_d_initial_state: bool = True,
                          workspace=None):
     """Gradients through :func:`gdr_prefill_chunked` (same q, k, v, beta,
     log_alpha, initial_state, cu_seqlens and scale, grouped q/k heads and
     bf16 gates included).  d_out [B, T, H, dv] fp32; d_final_state
-    [N, H, dv, dk] fp32 or None (zeros).
+    [N, H, dv, dk] fp32 or None (zeros).  workspace: uint8 device tensor, or
+    None to allocate the one-pass size; a dense batch also runs in a smaller
+    one, in time segments (see :func:`gdr_prefill_backward_workspace_bytes`).
     Returns a dict of fp32 tensors: dq, dk (q's shape), dv (v's), dbeta,
     dlog_alpha (log_alpha's shape) and d_initial_state [N, H, dv, dk] (None
     when not requested)."""

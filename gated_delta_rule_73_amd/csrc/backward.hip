@@ -76,6 +76,14 @@ struct BwdKArgs {
     float *rec, *states, *dstates;
     long rec_stride;                          // floats per record
     int raw_qk;                               // per-head decay, four-wave scans: see BRec
+    // Dense batches in time segments: this launch covers chunks [seg_c0,
+    // seg_c0 + seg_nc) of every sequence, its records and states indexed
+    // from the segment's first chunk (seg_nc = 0: every chunk).  fwd_final:
+    // the forward pass also writes the state after its last chunk; no_dump:
+    // it writes no per-chunk states.
+    int seg_c0, seg_nc;
+    float *fwd_final;
+    int no_dump;
 };
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -270,9 +278,9 @@ struct ChunkLoc {
 __device__ __forceinline__ ChunkLoc locate(const BwdKArgs &p, long rc) {
     ChunkLoc L;
     if (!p.cu) {
-        const int nct = div_up(p.seqlen, kBC);
+        const int nct = p.seg_nc ? p.seg_nc : div_up(p.seqlen, kBC);
         L.n = (int)(rc / nct);
-        const int c = (int)(rc % nct);
+        const int c = p.seg_c0 + (int)(rc % nct);
         L.tok0 = (long)L.n * p.seqlen + (long)c * kBC;
         L.len = std::min(kBC, p.seqlen - c * kBC);
         return L;
@@ -571,8 +579,8 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         rc0 = p.choff[n], nc = p.choff[n + 1] - p.choff[n];
         tok_base = p.cu[n], len = p.cu[n + 1] - p.cu[n];
     } else {
-        nc = div_up(p.seqlen, C), rc0 = (long)n * nc;
-        tok_base = (long)n * p.seqlen, len = p.seqlen;
+        nc = p.seg_nc ? p.seg_nc : div_up(p.seqlen, C), rc0 = (long)n * nc;
+        tok_base = (long)n * p.seqlen + (long)p.seg_c0 * C, len = p.seqlen - p.seg_c0 * C;
     }
     const int row = ZW * slice + 16 * w + lr;     // this lane's value row (as MFMA column)
     const IT *v = static_cast<const IT *>(p.v);
@@ -754,9 +762,11 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         if (s + 1 < nc) fetch(s + 1);
         const int c = BWD ? nc - 1 - s : s;
         const long rc = rc0 + c;
-        float *dump = (BWD ? p.dstates : p.states) + ((rc * H + h) * DV + row) * DK;
+        if (!p.no_dump) {
+            float *dump = (BWD ? p.dstates : p.states) + ((rc * H + h) * DV + row) * DK;
 #pragma unroll
-        for (int jt = 0; jt < DK / 16; ++jt) *reinterpret_cast<f32x4 *>(dump + 16 * jt + 4 * lq) = x[jt];
+            for (int jt = 0; jt < DK / 16; ++jt) *reinterpret_cast<f32x4 *>(dump + 16 * jt + 4 * lq) = x[jt];
+        }
 
         // the state as B operand of the products over keys (k = key)
         bf16x8 xh[NB], xl[NB];
@@ -792,10 +802,11 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         if (s + 1 < nc) put(b ^ 1);
         __syncthreads();
     }
-    if (BWD && p.d_init) {
+    float *fin = BWD ? p.d_init : p.fwd_final;
+    if (fin) {
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt)
-            *reinterpret_cast<f32x4 *>(p.d_init + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq) = x[jt];
+            *reinterpret_cast<f32x4 *>(fin + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq) = x[jt];
     }
 }
 
@@ -1365,31 +1376,79 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp0, hipSt
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     const bool four = a.dv % 64 == 0 && 2 * 8 * ((units + 7) / 8) * (a.dv / 32) > cus;
-    BwdKArgs kp = kp0;
-    kp.raw_qk = !KDA && four;                 // the four-wave scan stages q, k raw with a per-head decay
-    if (nrc > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc, (unsigned)a.num_heads), dim3(256), 0, st, kp);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    }
+    BwdKArgs base = kp0;
+    base.raw_qk = !KDA && four;                 // the four-wave scan stages q, k raw with a per-head decay
     const long per_unit = a.dv / (four ? 64 : 32);
     const unsigned scan_blocks = (unsigned)(8 * ((units + 7) / 8) * per_unit);
-    if (four)
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, KDA, IT, GT>), dim3(2 * scan_blocks), dim3(256), 0, st, kp, (int)scan_blocks);
-    else
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(2 * scan_blocks), dim3(128), 0, st, kp, (int)scan_blocks);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    if (nrc > 0) {
+    // records of chunk slots [0, nrc): prep; then the two state passes
+    // (forward: grid [0, half); backward: [half, 2 half)); then the gradients
+    auto prep = [&](const BwdKArgs &kp, long nrc_) -> hipError_t {
+        if (nrc_ <= 0) return hipSuccess;
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, KDA, IT, GT>), dim3((unsigned)nrc_, (unsigned)a.num_heads), dim3(256), 0, st, kp);
+        return hipGetLastError();
+    };
+    auto scan = [&](const BwdKArgs &kp, bool fwd, bool bwd) -> hipError_t {
+        const unsigned grid = (fwd ? scan_blocks : 0) + (bwd ? scan_blocks : 0);
+        const int half = fwd ? (int)scan_blocks : 0;
+        if (four)
+            hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, KDA, IT, GT>), dim3(grid), dim3(256), 0, st, kp, half);
+        else
+            hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(grid), dim3(128), 0, st, kp, half);
+        return hipGetLastError();
+    };
+    auto grad = [&](const BwdKArgs &kp, long nrc_) -> hipError_t {
+        if (nrc_ <= 0) return hipSuccess;
         // one grad workgroup fills a CU's LDS: one persistent workgroup per CU
-        const long nitems = nrc * a.num_heads;
+        const long nitems = nrc_ * a.num_heads;
         const unsigned ggrid = (unsigned)std::min<long>(nitems, cus);
         hipLaunchKernelGGL((bwd_grad_kernel<DK, KDA, IT, GT>), dim3(ggrid), dim3(kGradThreads), 0, st, kp, nitems);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-        if (kp.G > 1) {
-            const long n4 = (long)a.batch * a.seqlen * kp.Hk * (DK / 4);
-            hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, kp.dq, kp.dk,
-                               a.dq, a.dk_out, n4, kp.G, DK / 4);
-            if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        return hipGetLastError();
+    };
+    hipError_t e = hipSuccess;
+    if (a.num_segments <= 1) {
+        if ((e = prep(base, nrc)) != hipSuccess || (e = scan(base, true, true)) != hipSuccess ||
+            (e = grad(base, nrc)) != hipSuccess)
+            return hipErrorLaunchFailure;
+    } else {
+        // Dense batch in time segments of S chunks: a forward pass over the
+        // segments keeps only the state entering each segment; then, last
+        // segment first, each segment's records and per-chunk states are
+        // rebuilt from that state, its state gradients run backward from the
+        // one carried out of the segment after it, and its gradients follow.
+        // The chunks see the same arithmetic as in one pass, so the results
+        // are the same bit for bit.
+        const long nct = div_up(a.seqlen, kBC), S = a.segment_chunks;
+        const int NS = a.num_segments;
+        const size_t SZ = (size_t)a.num_seqs * a.num_heads * a.dv * DK;   // floats of one set of states
+        auto seg = [&](int sgi) {
+            BwdKArgs kp = base;
+            kp.seg_c0 = (int)(sgi * S);
+            kp.seg_nc = (int)std::min<long>(S, nct - sgi * S);
+            kp.initial_state = sgi == 0 ? a.initial_state : a.boundary_states + (size_t)(sgi - 1) * SZ;
+            return kp;
+        };
+        for (int sgi = 0; sgi + 1 < NS; ++sgi) {
+            BwdKArgs kp = seg(sgi);
+            kp.fwd_final = a.boundary_states + (size_t)sgi * SZ;
+            kp.no_dump = 1;
+            if ((e = prep(kp, (long)a.batch * kp.seg_nc)) != hipSuccess || (e = scan(kp, true, false)) != hipSuccess)
+                return hipErrorLaunchFailure;
         }
+        for (int sgi = NS - 1; sgi >= 0; --sgi) {
+            BwdKArgs kp = seg(sgi);
+            kp.d_final = sgi == NS - 1 ? a.d_final_state : a.carry + (size_t)((sgi + 1) & 1) * SZ;
+            kp.d_init = sgi == 0 ? a.d_initial_state : a.carry + (size_t)(sgi & 1) * SZ;
+            const long nrc_s = (long)a.batch * kp.seg_nc;
+            if ((e = prep(kp, nrc_s)) != hipSuccess || (e = scan(kp, true, true)) != hipSuccess ||
+                (e = grad(kp, nrc_s)) != hipSuccess)
+                return hipErrorLaunchFailure;
+        }
+    }
+    if (nrc > 0 && base.G > 1) {
+        const long n4 = (long)a.batch * a.seqlen * base.Hk * (DK / 4);
+        hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, base.dq, base.dk,
+                           a.dq, a.dk_out, n4, base.G, DK / 4);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     return hipSuccess;
 }
@@ -1431,6 +1490,8 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     kp.d_init = a.d_initial_state;
     kp.rec = a.records, kp.states = a.states, kp.dstates = a.dstates;
     kp.rec_stride = (long)(backward_record_bytes(a.dk) / sizeof(float));
+    kp.raw_qk = 0;
+    kp.seg_c0 = 0, kp.seg_nc = 0, kp.fwd_final = nullptr, kp.no_dump = 0;
     switch (a.dk) {
         case 32: return dispatch_dk<32>(a, kp, st);
         case 64: return dispatch_dk<64>(a, kp, st);

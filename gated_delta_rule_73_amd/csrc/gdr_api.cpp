@@ -206,11 +206,21 @@ gdr_status check_decode(int32_t num_seqs, int32_t K, int32_t num_heads, int32_t 
 // state gradients.  Packed batches size the chunk slots by the bound
 // ceil(seqlen / C) + num_seqs, since the lengths live on the device.
 struct BackwardWorkspace {
-    size_t order_off = 0, choff_off = 0, rec_off = 0, st_off = 0, dst_off = 0, dqh_off = 0, dkh_off = 0, total = 0;
+    size_t order_off = 0, choff_off = 0, rec_off = 0, st_off = 0, dst_off = 0, dqh_off = 0, dkh_off = 0;
+    size_t bnd_off = 0, carry_off = 0, total = 0;
     long record_chunks = 0;
+    int num_segments = 1;
+    long segment_chunks = 0;
+    bool fits = true;            // backward_workspace_within: false when nothing fits
 };
 
-BackwardWorkspace backward_workspace(const gdr_prefill_shape &s, bool packed) {
+// Dense batches may run the backward in time segments of at least this many
+// chunks when the workspace holds less than one pass needs.
+constexpr long kMinBackwardSegment = 16;
+
+// Workspace of one pass (segment_chunks = 0 or >= the chunks per sequence),
+// or of segments of segment_chunks chunks (dense batches only).
+BackwardWorkspace backward_workspace(const gdr_prefill_shape &s, bool packed, long segment_chunks = 0) {
     BackwardWorkspace w;
     size_t off = 0;
     if (packed) {
@@ -219,14 +229,29 @@ BackwardWorkspace backward_workspace(const gdr_prefill_shape &s, bool packed) {
         off += round256(sizeof(int32_t) * ((size_t)s.num_seqs + 1));
     }
     const long ncps = ((long)s.seqlen + gdr::kBackwardChunk - 1) / gdr::kBackwardChunk;
-    w.record_chunks = packed ? ncps + s.num_seqs : (long)s.batch * ncps;
+    long per_seq = ncps;
+    if (!packed && segment_chunks > 0 && segment_chunks < ncps) {
+        w.segment_chunks = segment_chunks;
+        w.num_segments = (int)((ncps + segment_chunks - 1) / segment_chunks);
+        per_seq = segment_chunks;
+    }
+    w.record_chunks = packed ? ncps + s.num_seqs : (long)s.batch * per_seq;
     const size_t slots = (size_t)w.record_chunks * (size_t)s.num_heads;
+    const size_t state_bytes = (size_t)s.head_dim_k * s.head_dim_v * sizeof(float);
     w.rec_off = off;
     off += round256(slots * gdr::backward_record_bytes(s.head_dim_k));
     w.st_off = off;
-    off += round256(slots * (size_t)s.head_dim_k * s.head_dim_v * sizeof(float));
+    off += round256(slots * state_bytes);
     w.dst_off = off;
-    off += round256(slots * (size_t)s.head_dim_k * s.head_dim_v * sizeof(float));
+    off += round256(slots * state_bytes);
+    if (w.num_segments > 1) {
+        // the states entering segments 1 .. NS - 1, and two carried gradient sets
+        const size_t set = (size_t)s.num_seqs * s.num_heads * state_bytes;
+        w.bnd_off = off;
+        off += round256((size_t)(w.num_segments - 1) * set);
+        w.carry_off = off;
+        off += round256(2 * set);
+    }
     // grouped q/k heads: per-value-head dq and dk before the sum over each group
     const int hk = s.num_qk_heads > 0 ? s.num_qk_heads : s.num_heads;
     if (hk != s.num_heads) {
@@ -239,6 +264,21 @@ BackwardWorkspace backward_workspace(const gdr_prefill_shape &s, bool packed) {
     return w;
 }
 
+// The one-pass workspace when it fits, else (dense batches) the longest
+// segments that fit; fits = false when nothing does.
+BackwardWorkspace backward_workspace_within(const gdr_prefill_shape &s, bool packed, size_t bytes) {
+    BackwardWorkspace one = backward_workspace(s, packed);
+    one.fits = one.total <= bytes;
+    if (one.fits || packed) return one;
+    const long ncps = ((long)s.seqlen + gdr::kBackwardChunk - 1) / gdr::kBackwardChunk;
+    for (long S = ncps - 1; S >= kMinBackwardSegment; --S) {
+        const BackwardWorkspace w = backward_workspace(s, packed, S);
+        if (w.total <= bytes) return w;
+    }
+    one.fits = false;
+    return one;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +289,16 @@ size_t gdr_prefill_backward_workspace_bytes(const gdr_prefill_shape *shape, gdr_
     if (s.batch < 1 || s.seqlen < 0 || s.num_heads < 1 || s.head_dim_k < 1 || s.head_dim_v < 1 || s.num_seqs < 0)
         return 0;
     return backward_workspace(s, packed != 0).total;
+}
+
+size_t gdr_prefill_backward_segment_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate,
+                                                    int32_t segment_chunks) {
+    if (!shape || !valid_gate(gate)) return 0;
+    const gdr_prefill_shape &s = *shape;
+    if (s.batch < 1 || s.seqlen < 0 || s.num_heads < 1 || s.head_dim_k < 1 || s.head_dim_v < 1 || s.num_seqs < 0)
+        return 0;
+    if (segment_chunks < kMinBackwardSegment) return 0;
+    return backward_workspace(s, false, segment_chunks).total;
 }
 
 gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
@@ -305,11 +355,20 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     if (!aligned(log_alpha, kda ? 4 * gs : gs))
         return fail(GDR_ERROR_INVALID_VALUE, "log_alpha must be %zu-byte aligned", kda ? 4 * gs : gs);
 
-    const BackwardWorkspace ws = backward_workspace(s, packed);
-    if ((ws.record_chunks + 8) * s.num_heads >= INT32_MAX)
+    const BackwardWorkspace full = backward_workspace(s, packed);
+    const BackwardWorkspace ws = backward_workspace_within(s, packed, workspace_bytes);
+    if ((full.record_chunks + 8) * s.num_heads >= INT32_MAX)
         return fail(GDR_ERROR_NOT_SUPPORTED, "more than 2^31 (chunk, head) records");
-    if (workspace_bytes < ws.total)
-        return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, ws.total);
+    if (!ws.fits) {
+        const long ncps = ((long)s.seqlen + gdr::kBackwardChunk - 1) / gdr::kBackwardChunk;
+        if (packed || ncps <= kMinBackwardSegment)
+            return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes,
+                        full.total);
+        return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE,
+                    "workspace %zu bytes < %zu needed (one pass), or %zu for segments of %ld chunks",
+                    workspace_bytes, full.total, backward_workspace(s, packed, kMinBackwardSegment).total,
+                    kMinBackwardSegment);
+    }
     if (ws.total && !workspace) return fail(GDR_ERROR_INVALID_VALUE, "workspace is NULL");
     if (ws.total && !aligned(workspace, 256)) return fail(GDR_ERROR_INVALID_VALUE, "workspace is not 256-byte aligned");
 
@@ -362,6 +421,10 @@ gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, g
     a.dq_heads = hk != s.num_heads ? reinterpret_cast<float *>(wsb + ws.dqh_off) : nullptr;
     a.dk_heads = hk != s.num_heads ? reinterpret_cast<float *>(wsb + ws.dkh_off) : nullptr;
     a.record_chunks = ws.record_chunks;
+    a.num_segments = ws.num_segments;
+    a.segment_chunks = ws.segment_chunks;
+    a.boundary_states = ws.num_segments > 1 ? reinterpret_cast<float *>(wsb + ws.bnd_off) : nullptr;
+    a.carry = ws.num_segments > 1 ? reinterpret_cast<float *>(wsb + ws.carry_off) : nullptr;
     return launch_status(gdr::launch_backward(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_backward");
 }
 

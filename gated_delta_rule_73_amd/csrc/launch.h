@@ -125,7 +125,13 @@ struct BackwardArgs {
     float *records;                 // record_chunks * H records
     float *states, *dstates;        // record_chunks * H states of dv x dk each
     float *dq_heads, *dk_heads;     // grouped heads only: per-value-head dq, dk [batch, seqlen, H, dk]
-    long record_chunks;             // chunk slots (packed: an upper bound)
+    long record_chunks;             // chunk slots (packed: an upper bound; segments: one segment's)
+    // dense batches in time segments (num_segments > 1): segment_chunks
+    // chunks per segment; the states entering segments 1 .. num_segments - 1
+    // and two state-gradient sets carried between segments
+    int num_segments;
+    long segment_chunks;
+    float *boundary_states, *carry;
 };
 
 constexpr int kBackwardChunk = 32;

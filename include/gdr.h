@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 5
+#define GDR_ABI_VERSION 6
 
 /* The enumerations travel as 32-bit ints.  Compiled as C++ they name that
  * type, so any int a C caller passes (an invalid one included, which the
@@ -443,7 +443,18 @@ const char *gdr_status_string(gdr_status status);
  *                 1.8 KB + 8 d_k d_v / 32 bytes, 5.9 KB at d = 128, per token
  *                 and value head; with grouped q/k heads also the value
  *                 heads' dq and dk) and keeps nothing in it after the stream
- *                 has run the call.
+ *                 has run the call.  That is one pass over all chunks, the
+ *                 fastest schedule.  A dense batch also accepts a smaller
+ *                 workspace, down to
+ *                 gdr_prefill_backward_segment_workspace_bytes(shape, gate, 16):
+ *                 the call then runs in time segments of S >= 16 chunks (the
+ *                 largest S that fits), keeping records and per-chunk states
+ *                 for one segment only, plus the state entering each later
+ *                 segment and two state gradients carried between segments.
+ *                 A first forward pass over the segments finds those states;
+ *                 each segment's records and forward states are then built
+ *                 again, so the call takes longer.  The results are the same
+ *                 bit for bit.  Packed batches need the one-pass size.
  *
  * Supported: head_dim_k in {32, 64, 128}; head_dim_v in {32, 64, 96, 128}
  * (else GDR_ERROR_NOT_SUPPORTED).  q, k, v, d_out, dq, dk and the states
@@ -459,6 +470,17 @@ const char *gdr_status_string(gdr_status status);
  * returns GDR_SUCCESS or an error status (nothing enqueued on error).
  */
 size_t gdr_prefill_backward_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate, int32_t packed);
+/* Workspace of gdr_prefill_backward for a dense batch (cu_seqlens NULL) run in
+ * time segments of segment_chunks chunks of 32 tokens: for
+ * NS = ceil(ceil(seqlen / 32) / segment_chunks) segments, batch x
+ * segment_chunks x num_heads records and state pairs, plus (NS - 1 + 2) x
+ * num_seqs x num_heads x head_dim_v x head_dim_k x 4 bytes of states carried
+ * between segments, each part rounded up to 256 bytes (and the grouped
+ * heads' dq, dk as in one pass).  With segment_chunks at or above the chunks
+ * per sequence it is the one-pass size.  Returns 0 for a NULL shape, an
+ * invalid gate or segment_chunks below 16. */
+size_t gdr_prefill_backward_segment_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate,
+                                                    int32_t segment_chunks);
 gdr_status gdr_prefill_backward(const gdr_prefill_shape *shape, gdr_gate gate, gdr_dtype qkv_dtype,
                                 gdr_dtype gate_dtype, const void *q, const void *k, const void *v, const void *beta,
                                 const void *log_alpha, const float *initial_state, const int32_t *cu_seqlens,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = gdr.load_library()
-    assert lib.gdr_abi_version() == 5 == gdr.ABI_VERSION
+    assert lib.gdr_abi_version() == 6 == gdr.ABI_VERSION
     assert lib.gdr_status_string(0) == b"success"
     assert lib.gdr_status_string(2) == b"not supported"
 
@@ -355,6 +355,9 @@ def _backward(shape=(1, 64, 2, 64, 64, 1, 0), gate=0, qkv=1, gdt=0, q=A, k=A + 8
     (dict(s0=A + 40 * MB, dinit=A + 40 * MB), 1, "d_initial_state overlaps initial_state"),
     (dict(ws=A + 24 * MB), 1, "workspace overlaps beta"),
     (dict(wsb=1000), 3, "workspace"),
+    # 40 chunks per sequence: a dense batch could also run in segments
+    (dict(shape=(1, 32 * 40, 2, 64, 64, 1, 0), wsb=1000), 3, "needed (one pass)"),
+    (dict(shape=(1, 32 * 40, 2, 64, 64, 1, 0), wsb=1000), 3, "for segments of 16 chunks"),
     (dict(ws=None), 1, "workspace is NULL"),
     (dict(ws=A + 64 * MB + 16), 1, "256-byte"),
 ])
@@ -385,3 +388,37 @@ def test_backward_workspace_size():
     # grouped q/k heads add the value heads' dq and dk (tokens x H x dk fp32 each)
     shg = gdr.PrefillShape(1, 1000, 4, 64, 32, 1, 2)
     assert f(ctypes.byref(shg), 0, 0) == f(ctypes.byref(sh), 0, 0) + 2 * r256(1000 * 4 * 64 * 4)
+
+
+def test_backward_segment_workspace_size():
+    """Dense batch in time segments of S chunks: S chunks' records, states
+    and state gradients per (sequence, head), plus the states entering the
+    later segments and two carried gradient sets; at or above the chunks per
+    sequence, the one-pass size; below 16 chunks, 0."""
+    lib = gdr.load_library()
+    f = lib.gdr_prefill_backward_segment_workspace_bytes
+    one = lib.gdr_prefill_backward_workspace_bytes
+    r256 = lambda b: -(-b // 256) * 256
+    rec = lambda dk: r256((dk + 2 * 32 * 32 + 3 * 32 * dk + 32) * 4)
+    B, T, H, dk, dv = 2, 1000, 4, 64, 32          # 32 chunks per sequence
+    sh = gdr.PrefillShape(B, T, H, dk, dv, B, 0)
+    state_set = B * H * dv * dk * 4
+    for S, NS in ((16, 2), (20, 2), (17, 2)):
+        slots = B * S * H
+        want = (r256(slots * rec(dk)) + 2 * r256(slots * dv * dk * 4) + r256((NS - 1) * state_set)
+                + r256(2 * state_set))
+        assert f(ctypes.byref(sh), 0, S) == want, S
+        assert f(ctypes.byref(sh), 0, S) < one(ctypes.byref(sh), 0, 0)
+    sh3 = gdr.PrefillShape(1, 32 * 40 + 5, H, dk, dv, 1, 0)   # 41 chunks: 16, 16, 9
+    slots = 16 * H
+    set1 = H * dv * dk * 4
+    assert f(ctypes.byref(sh3), 1, 16) == (r256(slots * rec(dk)) + 2 * r256(slots * dv * dk * 4) + r256(2 * set1)
+                                          + r256(2 * set1))
+    assert f(ctypes.byref(sh), 0, 32) == one(ctypes.byref(sh), 0, 0)
+    assert f(ctypes.byref(sh), 0, 100) == one(ctypes.byref(sh), 0, 0)
+    assert f(ctypes.byref(sh), 0, 15) == 0
+    assert f(None, 0, 16) == 0
+    assert f(ctypes.byref(sh), 3, 16) == 0
+    # grouped q/k heads keep the value heads' dq and dk at full size
+    shg = gdr.PrefillShape(B, T, H, dk, dv, B, 2)
+    assert f(ctypes.byref(shg), 0, 16) == f(ctypes.byref(sh), 0, 16) + 2 * r256(B * T * H * dk * 4)

@@ -213,3 +213,55 @@ def test_backward_empty_dense_batch_passes_the_state_gradient_through():
     inp, cot = _small(64, 64, 2, 0, "channel", torch.bfloat16, True, seed=28, B=2)
     g = _gpu(inp, cot)
     assert torch.equal(g["d_initial_state"], cot["d_final_state"])
+
+
+SEGMENT_CASES = [
+    # dk, dv, H, T, gate, B, segment chunks
+    (128, 128, 2, 32 * 40 + 5, "channel", 2, 16),   # 41 chunks: segments of 16, 16, 9 (ragged last chunk)
+    (64, 64, 3, 32 * 33, "head", 1, 16),            # 33 chunks: 16, 16, 1
+    (128, 64, 2, 32 * 20 - 7, "head", 2, 16),       # 20 chunks: 16, 4
+    (32, 32, 2, 32 * 50, "channel", 1, 24),         # 50 chunks: 24, 24, 2
+]
+
+
+@pytest.mark.parametrize("case", SEGMENT_CASES,
+                         ids=lambda c: f"dk{c[0]}-dv{c[1]}-H{c[2]}-T{c[3]}-{c[4]}-B{c[5]}-S{c[6]}")
+def test_backward_in_time_segments(case):
+    """A workspace holding one segment's records and states (dense batch):
+    the call runs in time segments, rebuilding each segment's records and
+    forward states from the state entering it and carrying the state
+    gradient from segment to segment.  Every gradient equals the one-pass
+    call's bit for bit, and stays within the bound against the oracle."""
+    dk, dv, H, T, gate, B, S = case
+    inp, cot = _small(dk, dv, H, T, gate, torch.bfloat16, True, seed=dk + T + S, B=B)
+    one = _gpu(inp, cot)
+    nbytes = gdr.gdr_prefill_backward_workspace_bytes(inp["q"], inp["v"], inp["log_alpha"], segment_chunks=S)
+    full = gdr.gdr_prefill_backward_workspace_bytes(inp["q"], inp["v"], inp["log_alpha"])
+    assert 0 < nbytes < full
+    say(f"backward in segments {case}: workspace {nbytes} of {full} bytes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    seg = gdr.gdr_prefill_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], cot["d_out"],
+                                   initial_state=inp["initial_state"], d_final_state=cot["d_final_state"],
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        assert torch.equal(seg[name], one[name]), name
+    ref = _oracle(inp, cot)
+    for name in NAMES:
+        assert_close(name, seg[name], ref[name], TOL_BWD)
+
+
+def test_backward_in_time_segments_without_state_gradients():
+    """Segments with no final-state gradient and no initial-state gradient
+    requested: the carried gradient starts from zeros, and nothing is written
+    for the first segment's incoming state."""
+    inp, cot = _small(64, 64, 2, 32 * 36, "channel", torch.bfloat16, False, seed=31)
+    one = _gpu(inp, cot, with_final=False, with_init=False)
+    nbytes = gdr.gdr_prefill_backward_workspace_bytes(inp["q"], inp["v"], inp["log_alpha"], segment_chunks=16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    seg = gdr.gdr_prefill_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], cot["d_out"],
+                                   initial_state=None, d_final_state=None, output_d_initial_state=False, workspace=ws)
+    torch.cuda.synchronize()
+    for name in NAMES[:-1]:
+        assert torch.equal(seg[name], one[name]), name
+    assert seg["d_initial_state"] is None
