@@ -220,7 +220,7 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     own loop of args.steps calls after args.warmup untimed ones."""
     res = {}
 
-    def prefill_entry(w, inp, label, flush=None, out_dtype=torch.float32):
+    def prefill_entry(w, inp, label, flush=None, out_dtype=torch.float32, chunk=0):
         B, T, Hk, dk = inp["q"].shape
         H, dv = inp["v"].shape[2:]
         po = torch.empty(B, T, H, dv, dtype=out_dtype, device=dev)
@@ -228,7 +228,7 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
         pf = torch.empty(N, H, dv, dk, dtype=torch.float32, device=dev)
         f = lambda: gdr.gdr_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
                                             initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"],
-                                            out=po, final_state=pf)
+                                            out=po, final_state=pf, chunk_size=chunk)
         for _ in range(args.warmup):
             f()
         mean, med, mn = time_calls(f, args.steps, between=flush)
@@ -237,7 +237,7 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
                                Hk=Hk, gate_bytes=inp["beta"].element_size())
         if inp["cu_seqlens"] is not None:   # one initial and one final state per sequence, not per row
             by += (N - B) * 2 * H * dv * dk * 4
-        fl = prefill_alg_flops(B, T, H, dk, dv, 32)
+        fl = prefill_alg_flops(B, T, H, dk, dv, chunk or 32)
         return {"workload": label, "us_per_launch": round(mean * 1e6, 2), "us_median": round(med * 1e6, 2),
                 "us_min": round(mn * 1e6, 2), "Mtok_s": round(B * T / mean / 1e6, 3), "alg_bytes": by,
                 "hbm_GBps": round(by / mean / 1e9, 1), "frac_of_hbm_peak": round(by / mean / 1e9 / HBM_PEAK_GBS, 4),
@@ -265,7 +265,10 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     lbl = f"{w1.name}: B=1, T=8192, H=16, d=128, bf16 q/k/v, per-head decay, zero initial state, fp32 out"
     flush_buf = torch.empty(1 << 27, dtype=torch.float32, device=dev)     # 512 MiB
     res["gdn_prefill_8k"] = {"cache_warm": prefill_entry(w1, g1, lbl),
-                             "after_512MiB_write": prefill_entry(w1, g1, lbl, flush=lambda: flush_buf.fill_(1.0))}
+                             "after_512MiB_write": prefill_entry(w1, g1, lbl, flush=lambda: flush_buf.fill_(1.0)),
+                             # its stated chunk size: the single-kernel path, records kept in L2
+                             "chunk_64": prefill_entry(w1, g1, lbl + "; chunk size 64 (single-kernel path, "
+                                                       "records held in L2, not HBM)", chunk=64)}
     del g1
 
     w4 = WORKLOADS["packed_gdn_256k"]
