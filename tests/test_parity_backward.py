@@ -265,3 +265,27 @@ def test_backward_in_time_segments_without_state_gradients():
     for name in NAMES[:-1]:
         assert torch.equal(seg[name], one[name]), name
     assert seg["d_initial_state"] is None
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_backward_in_time_segments_grouped_heads_bf16_gates(gate):
+    """Time segments with 2 q/k heads shared by 6 value heads and bf16 gates:
+    each value head's dq and dk stay whole-length in the workspace and are
+    summed over each group once, after the last segment."""
+    w = Workload("small", "backward", heads=6, qk_heads=2, dk=64, dv=64, qkv_dtype=torch.bfloat16, gate=gate,
+                 batch=2, seqlen=32 * 35 + 9, init_state=True, seed=33)
+    inp = prefill_inputs(w, DEV, gate_dtype=torch.bfloat16)
+    cot = backward_cotangents(inp, 33, DEV)
+    one = _gpu(inp, cot)
+    nbytes = gdr.gdr_prefill_backward_workspace_bytes(inp["q"], inp["v"], inp["log_alpha"], segment_chunks=16)
+    assert 0 < nbytes < gdr.gdr_prefill_backward_workspace_bytes(inp["q"], inp["v"], inp["log_alpha"])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    seg = gdr.gdr_prefill_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], cot["d_out"],
+                                   initial_state=inp["initial_state"], d_final_state=cot["d_final_state"],
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        assert torch.equal(seg[name], one[name]), name
+    ref = _oracle(inp, cot)
+    for name in NAMES:
+        assert_close(name, seg[name], ref[name], TOL_BWD)
