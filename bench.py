@@ -406,7 +406,7 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
         torch.cuda.empty_cache()
 
     # the KDA 32K backward inside a 4 GB workspace: time segments (the library
-    # takes the longest segments that fit, as found here)
+    # takes the fewest equal segments that fit, as found here)
     wb = WORKLOADS["kda_backward_32k"]
     print(f"[bench] {wb.name} in a 4 GB workspace", file=sys.stderr, flush=True)
     bi = prefill_inputs(wb, dev)
@@ -416,7 +416,7 @@ def extra_workloads(args, gdr, torch, dev, WORKLOADS, prefill_inputs, decode_tok
     cap = 4_000_000_000
     ws_of = lambda s: gdr.gdr_prefill_backward_workspace_bytes(bi["q"], bi["v"], bi["log_alpha"], segment_chunks=s)
     nct = -(-T // 32)
-    S = max(s for s in range(16, nct) if 0 < ws_of(s) <= cap)
+    S = next(max(16, -(-nct // ns)) for ns in range(2, nct + 1) if 0 < ws_of(max(16, -(-nct // ns))) <= cap)
     ws = torch.empty(ws_of(S), dtype=torch.uint8, device=dev)
     f = lambda: gdr.gdr_prefill_backward(bi["q"], bi["k"], bi["v"], bi["beta"], bi["log_alpha"], bc["d_out"],
                                          initial_state=bi["initial_state"], d_final_state=bc["d_final_state"],

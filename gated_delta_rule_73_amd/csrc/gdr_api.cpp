@@ -264,16 +264,27 @@ BackwardWorkspace backward_workspace(const gdr_prefill_shape &s, bool packed, lo
     return w;
 }
 
-// The one-pass workspace when it fits, else (dense batches) the longest
-// segments that fit; fits = false when nothing does.
+// Segment length for NS segments of (nearly) equal length, at least the
+// minimum: ceil(ncps / NS) chunks, the last segment taking what remains.
+long backward_segment_length(long ncps, long NS) {
+    return std::max(kMinBackwardSegment, (ncps + NS - 1) / NS);
+}
+
+// The one-pass workspace when it fits, else (dense batches) the fewest time
+// segments that fit, of equal length: every segment but the last is built
+// twice, so fewer and shorter segments cost less; fits = false when none do.
 BackwardWorkspace backward_workspace_within(const gdr_prefill_shape &s, bool packed, size_t bytes) {
     BackwardWorkspace one = backward_workspace(s, packed);
     one.fits = one.total <= bytes;
     if (one.fits || packed) return one;
     const long ncps = ((long)s.seqlen + gdr::kBackwardChunk - 1) / gdr::kBackwardChunk;
-    for (long S = ncps - 1; S >= kMinBackwardSegment; --S) {
-        const BackwardWorkspace w = backward_workspace(s, packed, S);
-        if (w.total <= bytes) return w;
+    for (long NS = 2; ncps > kMinBackwardSegment; ++NS) {
+        const long S = backward_segment_length(ncps, NS);
+        if ((ncps + S - 1) / S == NS) {          // (else a longer NS repeats a shorter one's S)
+            const BackwardWorkspace w = backward_workspace(s, packed, S);
+            if (w.total <= bytes) return w;
+        }
+        if (S == kMinBackwardSegment) break;     // more segments would not be shorter
     }
     one.fits = false;
     return one;

@@ -447,8 +447,9 @@ const char *gdr_status_string(gdr_status status);
  *                 fastest schedule.  A dense batch also accepts a smaller
  *                 workspace, down to
  *                 gdr_prefill_backward_segment_workspace_bytes(shape, gate, 16):
- *                 the call then runs in time segments of S >= 16 chunks (the
- *                 largest S that fits), keeping records and per-chunk states
+ *                 the call then runs in the fewest time segments that fit,
+ *                 NS of them with S = max(16, ceil(chunks per sequence / NS))
+ *                 chunks each (the last one shorter), keeping records and per-chunk states
  *                 for one segment only, plus the state entering each later
  *                 segment and two state gradients carried between segments.
  *                 A first forward pass over the segments finds those states;
