@@ -509,9 +509,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
 //            P = M^T Z + K_end X^T, X <- X Diag(D) + P^T Wn + Z^T (Q e^g);
 //            writes X before each chunk (the chunk's outgoing gradient) and
 //            the initial-state gradient at the end.
-// The next chunk's record and inputs are fetched into registers while the
-// current chunk's products run, then written to the other half of a
-// double-buffered LDS stage: one barrier per chunk.  The workgroups of one
+// The workgroup has NW more waves that only load: they fetch chunk s + 2's
+// record and inputs into registers and write chunk s + 1's, split, to the
+// other half of a double-buffered LDS stage while the NW state waves run
+// chunk s: one barrier per chunk, which waits for LDS operations only, so
+// the loads stay in flight across it.  (A wave whose loads queue at the CU's
+// memory pipeline issues nothing else; with the loads in the state waves,
+// the fetch and the products of a chunk took turns.)  The workgroups of one
 // (sequence, head) sit on one XCD (block b runs on XCD b mod 8), so its
 // records come from HBM once and from that XCD's L2 for the other slices.
 //
@@ -529,6 +533,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKArgs p) {
 __device__ __forceinline__ int kperm32(int k) { return 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3); }
 
 __device__ __forceinline__ bf16x8 lds8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// 4 x 4 transpose inside each quad of lanes: lane t holds row t of a 4 x 4
+// block on entry and column t on return.  Two exchange stages over the DPP
+// quad permutations: lanes t and t ^ 2 swap the off-diagonal 2 x 2 blocks,
+// then lanes t and t ^ 1 swap the off-diagonal entries of each.
+template <int CTRL> __device__ __forceinline__ float quad_perm(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(f32x4 &v) {
+    const int t = threadIdx.x & 3;
+    const bool b1 = t & 2, b0 = t & 1;
+    float r0 = quad_perm<0x4E>(b1 ? v[0] : v[2]), r1 = quad_perm<0x4E>(b1 ? v[1] : v[3]);   // lanes t ^ 2
+    v = f32x4{b1 ? r0 : v[0], b1 ? r1 : v[1], b1 ? v[2] : r0, b1 ? v[3] : r1};
+    r0 = quad_perm<0xB1>(b0 ? v[0] : v[1]), r1 = quad_perm<0xB1>(b0 ? v[2] : v[3]);         // lanes t ^ 1
+    v = f32x4{b0 ? r0 : v[0], b0 ? v[1] : r0, b0 ? r1 : v[2], b0 ? v[3] : r1};
+}
 __device__ __forceinline__ void sts4(__bf16 *p, const bf16x4 v) { *reinterpret_cast<bf16x4 *>(p) = v; }
 
 // LDS of one scan workgroup, two stages; [.][0] hi, [.][1] lo planes.
@@ -540,6 +560,9 @@ __device__ __forceinline__ void sts4(__bf16 *p, const bf16x4 v) { *reinterpret_c
 //   L:  forward T, backward M^T: [chunk row][32 chunk columns];
 //   Zt: forward diag(b) V, backward scale dO, transposed:
 //       [value row][32 chunk rows].
+// loader waves beside the NW state waves (one per SIMD)
+constexpr int scan_loader_waves(int) { return 4; }
+
 template <int DK, int NW> struct ScanLds {
     static constexpr int C = kBC, ZW = 16 * NW;
     __align__(16) __bf16 E[2][2][DK / 32][C][32];
@@ -553,13 +576,18 @@ template <int DK, int NW> struct ScanLds {
 template <int DK, int NW, bool BWD, bool KDA, typename IT, typename GT>
 __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<DK, NW> &lds) {
     constexpr bool RAW = !KDA && NW == 4;     // q, k staged raw (BRec; the launch sets raw_qk to match)
-    constexpr int C = kBC, NT = 64 * NW, ZW = 16 * NW, NB = DK / 32;
-    // per thread: NE row pieces of E and NE column pieces of Bt (and Gt),
-    // NL pieces of L, NZ column pieces of Zt; four values each
+    // column pieces loaded as rows and transposed in quads (see below), for
+    // the record fields; the raw q, k rows measured faster with their
+    // two-byte column loads
+    constexpr bool COLT = !RAW;
+    constexpr int C = kBC, SNT = 64 * NW, NT = 64 * scan_loader_waves(NW), ZW = 16 * NW, NB = DK / 32;
+    // per loader thread (NT of them): NE row pieces of E and NE column
+    // pieces of Bt (and Gt), NL pieces of L, NZ column pieces of Zt; four
+    // values each
     // (the last round of a count below NT leaves threads idle: their loads
     // are clamped to a valid piece, their LDS stores skipped)
     constexpr int TE = C * DK / 4, TL = C * C / 4, NE = div_up(TE, NT), NL = div_up(TL, NT), NZ = C * ZW / 4 / NT;
-    static_assert(C * ZW % (4 * NT) == 0 && DK % 32 == 0, "scan tiling");
+    static_assert(C * ZW % (4 * NT) == 0 && TE % NT == 0 && TL % NT == 0 && DK % 32 == 0, "scan tiling");
     using R = BRec<DK>;
     auto &sE = lds.E;
     auto &sBt = lds.Bt;
@@ -572,7 +600,9 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     const int unit = xcd + 8 * (kb / S), slice = kb % S;
     if (unit >= p.num_seqs * H) return;
     const int n = p.cu ? p.order[unit / H] : unit / H, h = unit % H;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lr = l & 15, lq = l >> 4;
+    const bool loader = w >= NW;                  // waves 0 .. NW - 1 hold the state, the others load
+    int lt = tid - SNT;                           // loader thread index (made opaque per chunk below)
     long rc0, tok_base;
     int nc, len;
     if (p.cu) {
@@ -582,7 +612,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         nc = p.seg_nc ? p.seg_nc : div_up(p.seqlen, C), rc0 = (long)n * nc;
         tok_base = (long)n * p.seqlen + (long)p.seg_c0 * C, len = p.seqlen - p.seg_c0 * C;
     }
-    const int row = ZW * slice + 16 * w + lr;     // this lane's value row (as MFMA column)
+    const int row = ZW * slice + 16 * (w & (NW - 1)) + lr;   // a state lane's value row (as MFMA column)
     const IT *v = static_cast<const IT *>(p.v);
     const IT *kin = static_cast<const IT *>(p.k), *qin = static_cast<const IT *>(p.q);
     const int hq = h / p.G;
@@ -592,7 +622,11 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     //    threads cover one row's 32-k block, whose 64 bytes they write whole;
     //  column pieces (Bt, Gt, Zt; backward L): four consecutive rows of one
     //    column; 16 threads take 16 adjacent columns (64 contiguous bytes of
-    //    each source row), and a wave writes 16 whole 64-byte LDS rows.
+    //    each source row), and a wave writes 16 whole 64-byte LDS rows.  With
+    //    COLT they are loaded as rows: each lane of a quad loads four columns
+    //    of one of the piece's rows (col_load; a wave reads 64 contiguous
+    //    bytes of 16 source rows), and quad_transpose turns the quad's 4 x 4
+    //    block into its four column pieces.
     auto row_piece = [](int e, int &r, int &k) {       // k: first of four, 32 k per row block
         const int jj = e & 7;
         r = (e >> 3) & (C - 1);
@@ -603,11 +637,16 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         c = 16 * (rest % nch) + (e & 15);
         r4 = 16 * (rest / nch) + 4 * ((e >> 4) & 3);
     };
+    auto col_load = [](int e, int ncol, int &r, int &c4) {   // row r, columns c4 .. c4 + 3
+        const int rest = e >> 6, nch = ncol / 16;
+        c4 = 16 * (rest % nch) + 4 * ((e >> 2) & 3);
+        r = 16 * (rest / nch) + 4 * ((e >> 4) & 3) + (e & 3);
+    };
 
     f32x4 rE[NE], rB[NE], rG[BWD ? NE : 1], rL[NL], rZ[NZ];
-    float rD = 0.f;
-    // raw q, k: the fetched chunk's row log decays (lane l holds row l mod 32)
-    // and length, for scaling them in put
+    float rD = 0.f, rZb[NZ] = {};
+    // the fetched chunk's length; raw q, k: its row log decays (lane l holds
+    // row l mod 32), for scaling them in put
     float rGv = 0.f;
     int rClen = 0;
     auto fetch = [&](int s) {
@@ -621,7 +660,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         auto qk_off = [&](int r, int c) { return ((tok0 + min(r, clen - 1)) * p.Hk + hq) * DK + c; };
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
-            const int e = min(tid + NT * u, TE - 1);
+            const int e = min(lt + NT * u, TE - 1);
             int r, j;
             row_piece(e, r, j);
             if (!RAW || !BWD) {
@@ -630,22 +669,31 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
                 const float4 k4 = load4(kin + qk_off(r, j));
                 rE[u] = f32x4{k4.x, k4.y, k4.z, k4.w};
             }
-            int jc, r4;
-            col_piece(e, DK, jc, r4);
+            if (COLT) {
+                int rr, c4;
+                col_load(e, DK, rr, c4);
+                rB[u] = *reinterpret_cast<const f32x4 *>(bb + rr * DK + c4);
+                if (BWD) rG[u] = *reinterpret_cast<const f32x4 *>(rec + R::Q + rr * DK + c4);
+            } else {
+                int jc, r4;
+                col_piece(e, DK, jc, r4);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                rB[u][t] = !RAW || BWD ? bb[(r4 + t) * DK + jc] : ld1(kin + qk_off(r4 + t, jc));
-                if (BWD) rG[u][t] = !RAW ? rec[R::Q + (r4 + t) * DK + jc] : ld1(qin + qk_off(r4 + t, jc));
+                for (int t = 0; t < 4; ++t) {
+                    rB[u][t] = !RAW || BWD ? bb[(r4 + t) * DK + jc] : ld1(kin + qk_off(r4 + t, jc));
+                    if (BWD) rG[u][t] = !RAW ? rec[R::Q + (r4 + t) * DK + jc] : ld1(qin + qk_off(r4 + t, jc));
+                }
             }
         }
-        if (RAW) {
-            rGv = rec[R::G + (l & (C - 1))];
-            rClen = clen;
-        }
+        if (RAW) rGv = rec[R::G + (l & (C - 1))];
+        rClen = clen;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int e = min(tid + NT * u, TL - 1);
-            if (BWD) {                        // L = M^T: column pieces of M^T are row pieces of M
+            const int e = min(lt + NT * u, TL - 1);
+            if (BWD && COLT) {                // L = M^T: column pieces of M^T are row pieces of M
+                int mr, mc4;
+                col_load(e, C, mr, mc4);
+                rL[u] = *reinterpret_cast<const f32x4 *>(rec + R::M + mr * C + mc4);
+            } else if (BWD) {
                 int r, c4;
                 col_piece(e, C, r, c4);
 #pragma unroll
@@ -659,21 +707,57 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         // loads from clamped, always-valid rows and a select for padding rows:
         // a load under a lane-dependent branch would make the compiler wait for
         // every load in flight, the record loads above included
+        // (COLT: scaled and masked in put, after the loads have landed)
 #pragma unroll
         for (int u = 0; u < NZ; ++u) {
-            int i, r4;
-            col_piece(tid + NT * u, ZW, i, r4);
+            if (COLT) {
+                int zr, zc4;
+                col_load(lt + NT * u, ZW, zr, zc4);
+                const long tr = (tok0 + min(zr, clen - 1)) * H + h, o = tr * DV + ZW * slice + zc4;
+                if (BWD) {
+                    rZ[u] = *reinterpret_cast<const f32x4 *>(p.d_out + o);
+                } else {
+                    const float4 v4 = load4(v + o);
+                    rZ[u] = f32x4{v4.x, v4.y, v4.z, v4.w};
+                    rZb[u] = gate1<GT>(p.beta, tr);
+                }
+            } else {
+                int i, r4;
+                col_piece(lt + NT * u, ZW, i, r4);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = r4 + t;
-                const long tr = (tok0 + min(r, clen - 1)) * H + h, o = tr * DV + ZW * slice + i;
-                const float z = BWD ? p.scale * p.d_out[o] : gate1<GT>(p.beta, tr) * ld1(v + o);
-                rZ[u][t] = r < clen ? z : 0.f;
+                for (int t = 0; t < 4; ++t) {
+                    const int r = r4 + t;
+                    const long tr = (tok0 + min(r, clen - 1)) * H + h, o = tr * DV + ZW * slice + i;
+                    const float z = BWD ? p.scale * p.d_out[o] : gate1<GT>(p.beta, tr) * ld1(v + o);
+                    rZ[u][t] = r < clen ? z : 0.f;
+                }
             }
         }
-        rD = rec[R::D + (tid & (DK - 1))];
+        rD = rec[R::D + (lt & (DK - 1))];
     };
     auto put = [&](int b) {
+        if (COLT) {
+            // the column pieces: Z scaled by its row's factor (zero past the
+            // chunk's end), then every quad's rows turned into columns
+#pragma unroll
+            for (int u = 0; u < NZ; ++u) {
+                int zr, zc4;
+                col_load(lt + NT * u, ZW, zr, zc4);
+                const float f = BWD ? p.scale : rZb[u];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) rZ[u][t] = zr < rClen ? f * rZ[u][t] : 0.f;
+                quad_transpose(rZ[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < NE; ++u) {
+                quad_transpose(rB[u]);
+                if (BWD) quad_transpose(rG[u]);
+            }
+            if (BWD) {
+#pragma unroll
+                for (int u = 0; u < NL; ++u) quad_transpose(rL[u]);
+            }
+        }
         if (RAW) {
             // K_end = k e^{g_C - g_r}, Q e^g = q e^{g_r}, zero past the chunk's
             // end: lane r forms row r's two factors, the pieces read them across
@@ -683,7 +767,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
             const float fk = in * fexp(gC - rGv), fq = in * fexp(rGv);
 #pragma unroll
             for (int u = 0; u < NE; ++u) {
-                const int e = min(tid + NT * u, TE - 1);
+                const int e = min(lt + NT * u, TE - 1);
                 int r, j, jc, r4;
                 row_piece(e, r, j);
                 col_piece(e, DK, jc, r4);
@@ -701,7 +785,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         }
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
-            const int e = tid + NT * u;
+            const int e = lt + NT * u;
             if (TE % NT != 0 && e >= TE) continue;
             bf16x4 hi, lo;
             int r, j;
@@ -722,7 +806,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         }
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int e = tid + NT * u;
+            const int e = lt + NT * u;
             if (TL % NT != 0 && e >= TL) continue;
             int r, c4;
             if (BWD) col_piece(e, C, r, c4);
@@ -735,31 +819,47 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
 #pragma unroll
         for (int u = 0; u < NZ; ++u) {
             int i, r4;
-            col_piece(tid + NT * u, ZW, i, r4);
+            col_piece(lt + NT * u, ZW, i, r4);
             bf16x4 hi, lo;
             split4(rZ[u], hi, lo);
             sts4(&sZt[b][0][i][kperm32(r4)], hi);
             sts4(&sZt[b][1][i][kperm32(r4)], lo);
         }
-        if (tid < DK) sD[b][tid] = rD;
+        if (lt < DK) sD[b][lt] = rD;
     };
 
     f32x4 x[DK / 16];
-    {
+    if (!loader) {
         const float *init = BWD ? p.d_final : p.initial_state;
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt)
             x[jt] = init ? *reinterpret_cast<const f32x4 *>(init + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq)
                          : zero4();
+    } else {
+        if (nc > 0) {
+            fetch(0);
+            put(0);
+        }
+        if (nc > 1) fetch(1);
     }
-    if (nc > 0) {
-        fetch(0);
-        put(0);
-    }
-    __syncthreads();
+    lds_barrier();
     for (int s = 0; s < nc; ++s) {
         const int b = s & 1;
-        if (s + 1 < nc) fetch(s + 1);
+        if (loader) {
+            // chunk s + 1 into the stage chunk s - 1 used, then chunk s + 2's
+            // loads.  The thread index is made opaque each chunk, so the
+            // pieces' addresses are formed where they are used rather than
+            // kept in registers across the loop.
+            int opaque_zero;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
+            lt = ((int)threadIdx.x - SNT + opaque_zero) & (NT - 1);
+            if (s + 1 < nc) {
+                put(b ^ 1);
+                if (s + 2 < nc) fetch(s + 2);
+            }
+            lds_barrier();
+            continue;
+        }
         const int c = BWD ? nc - 1 - s : s;
         const long rc = rc0 + c;
         if (!p.no_dump) {
@@ -799,11 +899,10 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
                                  zl, acc);
             x[jt] = acc;
         }
-        if (s + 1 < nc) put(b ^ 1);
-        __syncthreads();
+        lds_barrier();
     }
     float *fin = BWD ? p.d_init : p.fwd_final;
-    if (fin) {
+    if (!loader && fin) {
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt)
             *reinterpret_cast<f32x4 *>(fin + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq) = x[jt];
@@ -814,7 +913,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
 // states forward, the second half the state gradients backward.  The two
 // recurrences are independent, so each half fills the CUs the other leaves.
 template <int DK, int NW, bool KDA, typename IT, typename GT>
-__global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(BwdKArgs p, int half) {
+__global__ __launch_bounds__(64 * (NW + scan_loader_waves(NW))) void bwd_scan_kernel(BwdKArgs p, int half) {
     __shared__ ScanLds<DK, NW> lds;
     if ((int)blockIdx.x < half)
         scan_body<DK, NW, false, KDA, IT, GT>(p, blockIdx.x, lds);
@@ -1391,9 +1490,11 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp0, hipSt
         const unsigned grid = (fwd ? scan_blocks : 0) + (bwd ? scan_blocks : 0);
         const int half = fwd ? (int)scan_blocks : 0;
         if (four)
-            hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, KDA, IT, GT>), dim3(grid), dim3(256), 0, st, kp, half);
+            hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, KDA, IT, GT>), dim3(grid), dim3(64 * (4 + scan_loader_waves(4))), 0, st,
+                               kp, half);
         else
-            hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(grid), dim3(128), 0, st, kp, half);
+            hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(grid), dim3(64 * (2 + scan_loader_waves(2))), 0, st,
+                               kp, half);
         return hipGetLastError();
     };
     auto grad = [&](const BwdKArgs &kp, long nrc_) -> hipError_t {
