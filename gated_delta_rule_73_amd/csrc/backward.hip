@@ -950,7 +950,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p, long
     // Persistent workgroups: items (chunk slot rc, head h), item = rc H + h,
     // blockIdx.x, + gridDim.x, ...  While one item's phases run, the next
     // item's inputs and its S0 rows for Y are already in flight into
-    // registers: the LDS holds one workgroup per CU, so without
+    // registers (and, once Y has used those registers, the item's own dS
+    // rows for K_end dS^T): the LDS holds one workgroup per CU, so without
     // this a CU's loads and its products would take turns.  (Barriers wait
     // only for LDS operations, so those loads stay in flight across them.)
     constexpr int NKL = div_up(C * DK / 4, NT), NVL = div_up(C * 128 / 4, NT), NTL = C * C / NT;
@@ -1129,7 +1130,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p, long
     }
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (more) fetch_rows(states_of(nxt), s0r);
+    // the same registers now take this item's dS rows, for K_end dS^T below
+    fetch_rows(dS, s0r);
     // ---- U = T diag(b) Y;  dU = M^T dO' (then + K_end dS^T below);
     //      K_end = K e^{g_C - g} built in place of K e^g (no longer read)
     f32x4 u[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
@@ -1146,9 +1148,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p, long
     lds_barrier();
     if (has_v) {
         tile_mma_nt<DK, 2>(du, DK, [&](int q, int mi, int kb, int lk) { return lds4(&sX1[16 * q + mi][kb + lk]); },
-                           [&](int, int ni, int kb, int lk) {
-                               return bload4(rdS, ((16 * w + ni) * DK + lk) * 4, kb * 4);
-                           });
+                           [&](int, int, int kb, int) { return s0r[kb >> 5][(kb >> 4) & 1]; });
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -1159,6 +1159,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p, long
             }
     }
     lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) fetch_rows(states_of(nxt), s0r);
     // ---- dT = dU (diag(b) Y)^T;  Z = T^T dU (kept in registers);  d beta (value part)
     if (w < 4) {
         const int rt = w & 1, ct = w >> 1;
