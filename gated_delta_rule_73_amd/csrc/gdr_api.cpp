@@ -119,8 +119,12 @@ PrefillWorkspace fit_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, 
 // automatic chunk size: 32 tokens where compiled (the fastest schedule
 // measured on every workload), else 16
 int auto_chunk(bool bf16, bool kda, int dk) { return gdr::prefill_supported(bf16, kda, dk, 16, 32) ? 32 : 16; }
-// the fused single-kernel prefill serves bf16 q/k/v with 64-token chunks
-bool use_fused(bool bf16, int chunk) { return bf16 && chunk == gdr::kFusedChunkHost; }
+// bf16 q/k/v with 64-token chunks: the two-kernel path where it is compiled
+// (d_k = 128), else the fused single-kernel prefill
+bool use_fused(bool bf16, bool kda, int dk, int chunk) {
+    return bf16 && chunk == gdr::kFusedChunkHost && !gdr::prefill_supported(bf16, kda, dk, 16, chunk) &&
+           !gdr::prefill_supported(bf16, kda, dk, 32, chunk);
+}
 
 
 constexpr int kMaxDecodeTokens = 64;
@@ -467,7 +471,7 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
     if (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
     const bool bf16 = qkv_dtype == GDR_BF16, kda = gate == GDR_GATE_CHANNEL;
     const int C = chunk_size ? chunk_size : auto_chunk(bf16, kda, s.head_dim_k);
-    if (use_fused(bf16, C)) {
+    if (use_fused(bf16, kda, s.head_dim_k, C)) {
         // enough for every value-slice width a call may pick
         int hk = 0;
         if (resolve_qk_heads(s.num_heads, s.num_qk_heads, hk) != GDR_SUCCESS) return 0;
@@ -524,7 +528,7 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     // value-slice width that needs the fewest rounds of chain workgroups
     int C = chunk_size;
     if (!C) C = auto_chunk(bf16, kda, dk);
-    const bool fused = use_fused(bf16, C);
+    const bool fused = use_fused(bf16, kda, dk, C);
     gdr::FusedPlan plan;
     int DVS = dv_slice;
     if (fused) {

@@ -200,17 +200,27 @@ template <int NBLK> struct RowA<float, NBLK> {
 // row and b: T_row,s b_s for s <= row, else 0, rounded to ST.
 template <typename ST, int NBLK>
 __device__ __forceinline__ RowA<ST, NBLK> tbeta_fragment(const float *trow, const float *beta, int row, int lg);
+template <int NBLK>
+__device__ __forceinline__ RowA<_Float16, NBLK> tbeta_fragment_f16(const float *trow, const float *beta, int row, int lg) {
+    RowA<_Float16, NBLK> r;
+#pragma unroll
+    for (int s = 0; s < NBLK / 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int s0 = 32 * s + 16 * h + 4 * lg;
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(trow + s0), b = *reinterpret_cast<const f32x4 *>(beta + s0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r.f[s][4 * h + i] = (_Float16)(s0 + i <= row ? t[i] * b[i] : 0.f);
+        }
+    return r;
+}
 template <>
 __device__ __forceinline__ RowA<_Float16, 2> tbeta_fragment<_Float16, 2>(const float *trow, const float *beta, int row, int lg) {
-    RowA<_Float16, 2> r;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int s0 = 16 * h + 4 * lg;
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(trow + s0), b = *reinterpret_cast<const f32x4 *>(beta + s0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.f[0][4 * h + i] = (_Float16)(s0 + i <= row ? t[i] * b[i] : 0.f);
-    }
-    return r;
+    return tbeta_fragment_f16<2>(trow, beta, row, lg);
+}
+template <>
+__device__ __forceinline__ RowA<_Float16, 4> tbeta_fragment<_Float16, 4>(const float *trow, const float *beta, int row, int lg) {
+    return tbeta_fragment_f16<4>(trow, beta, row, lg);
 }
 template <int NBLK>
 __device__ __forceinline__ RowA<float, NBLK> tbeta_fragment_f32(const float *trow, const float *beta, int row, int lg) {
@@ -326,28 +336,51 @@ struct PrepSmem {
     static constexpr int LDG = DK + 4;                 // fp32 rows
     static constexpr int LDI = DK + 16 / sizeof(IT);   // input rows
     static constexpr int LDA = C + 4;
+    // 64-token chunks (WIDE): the four waves' partial Gram tiles are summed
+    // in pairs into two copies, and (K e^g)^T lives in the union past those
+    // copies (written once the staged inputs are no longer read), so that
+    // two workgroups still share a CU.
+    static constexpr bool WIDE = NB == 4;
+    static constexpr int NCOPY = WIDE ? 2 : 4;
+    using ST = typename Prec<IT>::ST;
+    static constexpr int LDT = lds_pitch(C * (int)sizeof(ST)) / (int)sizeof(ST);
+    static constexpr int TILEB = 16 * 20 * 4;                    // one fp32 tile, rows of 20
+    static constexpr int OFF_TF = NT * TILEB;                    // WIDE: T after the A tiles
+    static constexpr int OFF_TFT = OFF_TF + C * LDA * 4;         //   then T^T
+    static constexpr int OFF_KT = NCOPY * 2 * NT * TILEB;        //   (K e^g)^T past the partial tiles
+    static constexpr int RAWB = WIDE ? OFF_KT + DK * LDT * (int)sizeof(ST) : 16;
+    static_assert(!WIDE || OFF_TFT + C * LDA * 4 <= OFF_KT, "T and T^T end before (K e^g)^T");
     union alignas(16) {
         struct {
             float G[KDA ? C : 1][LDG];   // KDA: log-decay, then g - m
             IT Ks[C][LDI];
             IT Qs[C][LDI];
         } in;
-        float Pt[4][2 * NT][16][20];     // per-wave partial Gram tiles: A tiles, then M tiles
+        float Pt[NCOPY][2 * NT][16][20];  // partial Gram tiles: A tiles, then M tiles
+        char raw[RAWB];
     } u;
     alignas(16) float em[KDA ? DK : 4];  // KDA: e^m
     float g[C], egc[C], egt[C];          // GDN: g, e^{g_C - g}, e^g
     alignas(16) float beta[C];
     // Once the partial tiles are summed, their space holds the lower tiles
-    // of A (in place of wave 0's partials: each thread overwrites only what
+    // of A (in place of copy 0's partials: each thread overwrites only what
     // it has read), T = (I + A)^-1 and T's diagonal blocks transposed.
     __device__ float *a_tile(int tt) { return &u.Pt[0][tt][0][0]; }   // rows of 20
-    __device__ float (*tf())[LDA] { return reinterpret_cast<float (*)[LDA]>(&u.Pt[1][0][0][0]); }
-    __device__ float (*tft())[LDA] { return reinterpret_cast<float (*)[LDA]>(&u.Pt[2][0][0][0]); }
-    static_assert(C * LDA <= 2 * NT * 16 * 20, "T fits in one wave's partial tiles");
+    __device__ float (*tf())[LDA] {
+        if constexpr (WIDE) return reinterpret_cast<float (*)[LDA]>(u.raw + OFF_TF);
+        else return reinterpret_cast<float (*)[LDA]>(&u.Pt[1][0][0][0]);
+    }
+    __device__ float (*tft())[LDA] {
+        if constexpr (WIDE) return reinterpret_cast<float (*)[LDA]>(u.raw + OFF_TFT);
+        else return reinterpret_cast<float (*)[LDA]>(&u.Pt[2][0][0][0]);
+    }
+    static_assert(WIDE || C * LDA <= 2 * NT * 16 * 20, "T fits in one wave's partial tiles");
     // operands of W = T diag(b) (K e^g), token index in kpos order
-    using ST = typename Prec<IT>::ST;
-    static constexpr int LDT = lds_pitch(C * (int)sizeof(ST)) / (int)sizeof(ST);
-    alignas(16) ST KtT[DK][LDT];         // (K e^g)^T
+    alignas(16) ST kt_own[WIDE ? 1 : DK][LDT];
+    __device__ ST (*ktT())[LDT] {
+        if constexpr (WIDE) return reinterpret_cast<ST (*)[LDT]>(u.raw + OFF_KT);
+        else return kt_own;
+    }
 };
 
 struct PrepKArgs {
@@ -371,7 +404,7 @@ struct PrepKArgs {
 // GDT: storage type of beta and log alpha (float or __bf16; widened to fp32
 // when they reach LDS).
 template <int DK, int C, bool KDA, typename IT, bool GRP, typename GDT>
-__global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
+__global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p) {
     using SM = PrepSmem<DK, C, KDA, IT>;
     using Rec = ChunkRec<DK, C, KDA, IT>;
     using ST = typename Prec<IT>::ST;
@@ -385,10 +418,11 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     constexpr int NSEG = 256 / DK;           // prefix-sum lanes per key channel
     constexpr int SEGL = C / NSEG;           //   tokens per lane
     constexpr int NSTEP = (DK + 31) / 32;    // 32-wide k-steps of the Gram
-    static_assert(NB <= 2, "the inverse below handles at most two 16-token blocks");
+    constexpr bool WIDE = SM::WIDE;
+    static_assert(NB <= 2 || (WIDE && sizeof(ST) == 2), "the inverse below handles two or four 16-token blocks (four: 16-bit operands)");
     static_assert(SEGL >= 1 && C <= 64, "prefix-sum thread mapping");
     static_assert(sizeof(Rec) == chunk_record_bytes(DK, C, KDA, sizeof(ST)), "record layout");
-    static_assert(sizeof(SM) <= (sizeof(ST) == 2 ? 64 : 160) * 1024, "LDS budget (fp16: two workgroups per CU)");
+    static_assert(sizeof(SM) <= (sizeof(ST) == 2 ? (WIDE ? 80 : 64) : 160) * 1024, "LDS budget (fp16: two workgroups per CU)");
     static_assert(sizeof(ST) == 4 || (C % 32 == 0 && DK % 32 == 0), "fp16 operands are stored in 32-wide k-blocks");
 
     constexpr int KVPT = (C * DK / EPV + 255) / 256;        // 16-byte k (and q) vectors per thread
@@ -537,13 +571,18 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
         if (lane < 4) rec.dec[lane] = lane == 0 ? __expf(gC) : 0.f;
     }
     if (tid < C) sm.beta[tid] = br;
-    fetch(r + gridDim.x);
+    // (WIDE: the next record's inputs are requested once the Gram tiles
+    // have left registers, which then have room for them)
+    if constexpr (!WIDE) fetch(r + gridDim.x);
     __syncthreads();
 
     // ---- B: per-channel prefix sums (KDA), K_end^T to the record and
     // (K e^g)^T to LDS, one key channel per NSEG lanes, SEGL tokens each
+    // (WIDE: (K e^g)^T stays in registers until the staged inputs are read)
+    const int gc = tid / NSEG, gseg = tid % NSEG;
+    typedef typename VecT<ST, 2>::type ST2;
+    ST2 ktw[WIDE ? SEGL / 2 : 1];
     {
-        const int gc = tid / NSEG, gseg = tid % NSEG;
         float ke[SEGL], kt[SEGL];
         if constexpr (KDA) {
             float gv[SEGL];
@@ -588,14 +627,20 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
             for (int s = 0; s < SEGL; s += 4) {
                 const ST v4[4] = {(ST)ke[s], (ST)ke[s + 1], (ST)ke[s + 2], (ST)ke[s + 3]};
                 store_vec<ST, 4>(&rec.KeT[gc][kpos<ST>(gseg * SEGL + s)], v4);
-                const ST w4[4] = {(ST)kt[s], (ST)kt[s + 1], (ST)kt[s + 2], (ST)kt[s + 3]};
-                store_vec<ST, 4>(&sm.KtT[gc][kpos<ST>(gseg * SEGL + s)], w4);
+                if constexpr (WIDE) {
+                    ktw[s / 2] = ST2{(ST)kt[s], (ST)kt[s + 1]};
+                    ktw[s / 2 + 1] = ST2{(ST)kt[s + 2], (ST)kt[s + 3]};
+                } else {
+                    const ST w4[4] = {(ST)kt[s], (ST)kt[s + 1], (ST)kt[s + 2], (ST)kt[s + 3]};
+                    store_vec<ST, 4>(&sm.ktT()[gc][kpos<ST>(gseg * SEGL + s)], w4);
+                }
             }
         } else {
+            static_assert(!WIDE, "64-token chunks take the vector path");
 #pragma unroll
             for (int s = 0; s < SEGL; ++s) {
                 rec.KeT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)ke[s];
-                sm.KtT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)kt[s];
+                sm.ktT()[gc][kpos<ST>(gseg * SEGL + s)] = (ST)kt[s];
             }
         }
     }
@@ -610,6 +655,21 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
     constexpr bool QT_MERGE = sizeof(ST) == 2 && DK >= 32;
     for (int s = wave; s < NSTEP; s += 4) {
         F8 fk[NB], fq[NB], fql[NB], fr[NB], frl[NB];
+        // the Gram tile (I, J) of this k-step
+        auto tile_mma = [&](int I, int J) {
+            const int tt = I * (I + 1) / 2 + J;
+            if constexpr (KDA) {
+                accA[tt] = gram_mma(accA[tt], fk[I], fr[J]);
+                accM[tt] = gram_mma(accM[tt], fq[I], fr[J]);
+                if constexpr (SPLIT) {
+                    accM[tt] = gram_mma(accM[tt], fq[I], frl[J]);
+                    accM[tt] = gram_mma(accM[tt], fql[I], fr[J]);
+                }
+            } else {
+                accA[tt] = gram_mma(accA[tt], fk[I], fk[J]);
+                accM[tt] = gram_mma(accM[tt], fq[I], fk[J]);
+            }
+        };
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             const int t = 16 * rb + lr;
@@ -659,33 +719,58 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
                 if (!QT_MERGE && valid) store_vec<ST, 4>(&rec.Qt[t][kpos<ST>(ch)], qt);
             }
             if constexpr (QT_MERGE) store_vec<ST, 8>(&rec.Qt[t][kpos<ST>(32 * s + 4 * lg)], qt8);
-        }
+            // WIDE: the tiles of row block rb as soon as its operands exist,
+            // so only the column operands stay live across row blocks
+            if constexpr (WIDE) {
 #pragma unroll
-        for (int I = 0; I < NB; ++I)
-#pragma unroll
-            for (int J = 0; J <= I; ++J) {
-                const int tt = I * (I + 1) / 2 + J;
-                if constexpr (KDA) {
-                    accA[tt] = gram_mma(accA[tt], fk[I], fr[J]);
-                    accM[tt] = gram_mma(accM[tt], fq[I], fr[J]);
-                    if constexpr (SPLIT) {
-                        accM[tt] = gram_mma(accM[tt], fq[I], frl[J]);
-                        accM[tt] = gram_mma(accM[tt], fql[I], fr[J]);
-                    }
-                } else {
-                    accA[tt] = gram_mma(accA[tt], fk[I], fk[J]);
-                    accM[tt] = gram_mma(accM[tt], fq[I], fk[J]);
-                }
+                for (int J = 0; J <= rb; ++J) tile_mma(rb, J);
             }
+        }
+        if constexpr (!WIDE) {
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+#pragma unroll
+                for (int J = 0; J <= I; ++J) tile_mma(I, J);
+        }
     }
     __syncthreads();   // the partial tiles overwrite the staged inputs
+    if constexpr (WIDE) {
+        // waves 2, 3 store their partial tiles as copies 0, 1 and every
+        // thread its (K e^g)^T entries; then waves 0, 1 add theirs in place
+        if (wave >= 2) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sm.u.Pt[wave][t][4 * lg + i][lr] = accA[t][i];
-            sm.u.Pt[wave][NT + t][4 * lg + i][lr] = accM[t][i];
+                for (int i = 0; i < 4; ++i) {
+                    sm.u.Pt[wave - 2][t][4 * lg + i][lr] = accA[t][i];
+                    sm.u.Pt[wave - 2][NT + t][4 * lg + i][lr] = accM[t][i];
+                }
         }
+#pragma unroll
+        for (int x = 0; x < SEGL; x += 4) {
+            const ST w4[4] = {ktw[x / 2][0], ktw[x / 2][1], ktw[x / 2 + 1][0], ktw[x / 2 + 1][1]};
+            store_vec<ST, 4>(&sm.ktT()[gc][kpos<ST>(gseg * SEGL + x)], w4);
+        }
+        __syncthreads();
+        if (wave < 2) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sm.u.Pt[wave][t][4 * lg + i][lr] += accA[t][i];
+                    sm.u.Pt[wave][NT + t][4 * lg + i][lr] += accM[t][i];
+                }
+        }
+        fetch(r + gridDim.x);
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sm.u.Pt[wave][t][4 * lg + i][lr] = accA[t][i];
+                sm.u.Pt[wave][NT + t][4 * lg + i][lr] = accM[t][i];
+            }
+    }
     __syncthreads();
 
     // ---- D: sum the partial tiles; masks, beta and (GDN) the decay factors.
@@ -703,7 +788,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
             if (J <= I) {
                 const int tt = I * (I + 1) / 2 + J;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
+                for (int w = 0; w < SM::NCOPY; ++w) {
                     a += *reinterpret_cast<const f32x4 *>(&sm.u.Pt[w][tt][r][cc]);
                     m += *reinterpret_cast<const f32x4 *>(&sm.u.Pt[w][NT + tt][r][cc]);
                 }
@@ -725,34 +810,59 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
         store_vec<ST, 4 * MH>(&rec.Mm[R][kpos<ST>(cb0)], mv);
     }
     __syncthreads();
-    // T = (I + A)^-1 on wave 0.  Diagonal 16x16 blocks by forward
-    // substitution, one column per lane (lanes 0-15 block 0, 16-31 block 1,
-    // the upper half wave repeating them): t_i = delta_ij - sum_{m<i} A_im t_m,
-    // with the block's strictly lower triangle read into registers first
-    // (all lanes of a block read the same rows).  Then, for two blocks,
-    // T_10 = -T_11 (A_10 T_00) as two fp32 MFMA products on the same wave:
-    // A_10 T_00 lands in the accumulator layout that the second product
-    // takes as its B operand.
+    // T = (I + A)^-1.  On wave 0: the diagonal 16x16 blocks by forward
+    // substitution, one column per lane (lanes 16 I .. 16 I + 15 block I; for
+    // two blocks the upper half wave repeats the lower): t_i = delta_ij -
+    // sum_{m<i} A_im t_m, with the block's strictly lower triangle read into
+    // registers first (all lanes of a block read the same rows).  Then the
+    // first subdiagonal block of each 32-token half, T_{I+1,I} =
+    // -T_{I+1,I+1} (A_{I+1,I} T_II), as two fp32 MFMA products on the same
+    // wave: A_{I+1,I} T_II lands in the accumulator layout that the second
+    // product takes as its B operand.  Four blocks (64-token chunks) add the
+    // lower-left 32x32 block, -T_hi (A_lo,hi T_lo) in 32-token blocks, one
+    // 16x16 tile per wave.
     float (*const Tf)[SM::LDA] = sm.tf();
     float (*const TfT)[SM::LDA] = sm.tft();
     if (wave == 0) {
-        const int I = NB == 2 ? (lane >> 4) & 1 : 0, jc = lane & 15;
-        f32x4 arow[16][4];
+        const int I = (lane >> 4) % NB, jc = lane & 15;
         const float *adiag = sm.a_tile(I * (I + 1) / 2 + I);
-#pragma unroll
-        for (int i = 1; i < 16; ++i)
-#pragma unroll
-            for (int m4 = 0; m4 < i; m4 += 4) arow[i][m4 / 4] = *reinterpret_cast<const f32x4 *>(&adiag[i * 20 + m4]);
         float tcol[16];
+        if constexpr (WIDE) {
+            // (rows read as they are needed: the next record's inputs are
+            // in flight in registers here)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc0 = (i == jc) ? 1.f : 0.f, acc1 = 0.f;
+            for (int i = 0; i < 16; ++i) {
+                float acc0 = (i == jc) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) {
-                if (m & 1) acc1 -= arow[i][m / 4][m % 4] * tcol[m];
-                else acc0 -= arow[i][m / 4][m % 4] * tcol[m];
+                for (int m4 = 0; m4 < i; m4 += 4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&adiag[i * 20 + m4]);
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) {
+                        const int m = m4 + mm;
+                        if (m < i) {
+                            if (m & 1) acc1 -= a4[mm] * tcol[m];
+                            else acc0 -= a4[mm] * tcol[m];
+                        }
+                    }
+                }
+                tcol[i] = acc0 + acc1;
             }
-            tcol[i] = acc0 + acc1;
+        } else {
+            f32x4 arow[16][4];
+#pragma unroll
+            for (int i = 1; i < 16; ++i)
+#pragma unroll
+                for (int m4 = 0; m4 < i; m4 += 4) arow[i][m4 / 4] = *reinterpret_cast<const f32x4 *>(&adiag[i * 20 + m4]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc0 = (i == jc) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) {
+                    if (m & 1) acc1 -= arow[i][m / 4][m % 4] * tcol[m];
+                    else acc0 -= arow[i][m / 4][m % 4] * tcol[m];
+                }
+                tcol[i] = acc0 + acc1;
+            }
         }
         if (lane < 16 * NB) {
 #pragma unroll
@@ -762,20 +872,53 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
                 *reinterpret_cast<f32x4 *>(&TfT[16 * I + jc][16 * I + i4]) =
                     f32x4{tcol[i4], tcol[i4 + 1], tcol[i4 + 2], tcol[i4 + 3]};
         }
-        if constexpr (NB == 2) {
-            // (this wave's LDS writes above are visible to its reads below:
-            // one wave's LDS operations execute in order)
+        // (this wave's LDS writes above are visible to its reads below:
+        // one wave's LDS operations execute in order)
+#pragma unroll
+        for (int I0 = 0; I0 + 1 < NB; I0 += 2) {
+            const int I1 = I0 + 1;
             RowA<float, 1> a10, t00c, t11;
-            a10.load(sm.a_tile(1) + lr * 20, lg);  // A_10 rows
-            t00c.load(&TfT[lr][0], lg);            // T_00 columns
+            a10.load(sm.a_tile(I1 * (I1 + 1) / 2 + I0) + lr * 20, lg);   // A_{I1,I0} rows
+            t00c.load(&TfT[16 * I0 + lr][16 * I0], lg);                   // T_{I0,I0} columns
             const f32x4 P = rowa_mma(f32x4{0.f, 0.f, 0.f, 0.f}, a10, t00c, 0);
             RegB<float, 1> pb;
             pb.set(&P);
-            t11.load(&Tf[16 + lr][16], lg);        // T_11 rows
+            t11.load(&Tf[16 * I1 + lr][16 * I1], lg);                     // T_{I1,I1} rows
             const f32x4 t10 = pb.mma(f32x4{0.f, 0.f, 0.f, 0.f}, t11);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Tf[16 + 4 * lg + i][lr] = -t10[i];
+            for (int i = 0; i < 4; ++i) Tf[16 * I1 + 4 * lg + i][16 * I0 + lr] = -t10[i];
         }
+    }
+    if constexpr (WIDE) {
+        __syncthreads();
+        // tile (i, j), i in {2, 3}, j in {0, 1}:  X_kj = sum_{m=j..1} A_km T_mj
+        // for k = 2 .. i, then T_ij = -sum_{k=2..i} T_ik X_kj.  The
+        // accumulator of X is the B operand of the second product (its rows
+        // are that product's k-index).  The tiles read only T's diagonal
+        // 32x32 blocks, which no wave writes here.
+        const int i = 2 + (wave >> 1), j = wave & 1;
+        auto mm_lds = [&](f32x4 acc, const float *A, int lda, const float *B, int ldb) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(A + lr * lda + 4 * lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], B[(4 * lg + r) * ldb + lr], acc, 0, 0, 0);
+            return acc;
+        };
+        auto mm_reg = [&](f32x4 acc, const float *A, int lda, const f32x4 &X) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(A + lr * lda + 4 * lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], X[r], acc, 0, 0, 0);
+            return acc;
+        };
+        auto xblk = [&](int k) {
+            f32x4 x{0.f, 0.f, 0.f, 0.f};
+            for (int m = j; m < 2; ++m) x = mm_lds(x, sm.a_tile(k * (k + 1) / 2 + m), 20, &Tf[16 * m][16 * j], SM::LDA);
+            return x;
+        };
+        f32x4 t = mm_reg(f32x4{0.f, 0.f, 0.f, 0.f}, &Tf[16 * i][32], SM::LDA, xblk(2));
+        if (i == 3) t = mm_reg(t, &Tf[48][48], SM::LDA, xblk(3));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tf[16 * i + 4 * lg + r][16 * j + lr] = -t[r];
     }
     __syncthreads();
     // ---- E: T diag(b) and W = T diag(b) (K e^g), both to the record.  The
@@ -808,10 +951,12 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrepKArgs p) {
                 for (int x = 0; x < KP; ++x) {
                     const int kb = KP * pb + x;
                     RowA<ST, NB> a;
-                    a.load(&sm.KtT[16 * kb + lr][0], lg);
+                    a.load(&sm.ktT()[16 * kb + lr][0], lg);
                     f32x4 acc{0.f, 0.f, 0.f, 0.f};
+                    // (k-steps past the diagonal of T's row block tb are zero)
 #pragma unroll
-                    for (int st = 0; st < RegB<ST, NB>::STEPS; ++st) acc = rowa_mma(acc, a, tbf[tb], st);
+                    for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+                        if (32 * st < 16 * tb + 16) acc = rowa_mma(acc, a, tbf[tb], st);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) w[4 * x + i] = (ST)(-acc[i]);
                 }
@@ -920,7 +1065,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     static_assert(GK <= 32 && GC <= 32, "row swizzle covers rows of up to 32 groups");
     static_assert(VV % 64 == 0, "whole value vectors per lane of the value wave");
     static_assert(NSLOT >= 2, "LDS budget");
-    static_assert(NB <= 2, "T and M rows span at most one 32-wide k-step");
+    static_assert(NB <= 2 || (NB == 4 && sizeof(ST) == 2), "16 or 32 tokens per chunk; 64 with 16-bit operands");
     // 32-wide k-steps of the lower-triangular T and M rows of row block rb
     auto tri_steps = [](int rb) { return (16 * rb + 16 + 31) / 32; };
 
@@ -993,6 +1138,68 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             OT *ob = static_cast<OT *>(p.out) + ((size_t)t0 * H + h) * DV + v0 + 16 * cb;
             const __amdgpu_buffer_rsrc_t orsrc =
                 __builtin_amdgcn_make_buffer_rsrc(ob, 0, ((nv - 1) * HDV + 16) * (int)sizeof(OT), kBufferWord3);
+            f32x4 U[NB], Y[NB];
+            if constexpr (NB == 4) {
+            // 64-token chunks: too many operands to hold at once, so each
+            // product's record rows are read just before it
+            {
+                RowA<ST, NB> vb;
+                vb.load(&bs.Vt[16 * cb + lr][0], lg);
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    RowA<ST, NB> ta;
+                    ta.load(&bc.Tm[16 * rb + lr][0], lg, tri_steps(rb), swC);
+                    U[rb] = Y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+                        if (st < tri_steps(rb)) U[rb] = rowa_mma(U[rb], ta, vb, st);
+                }
+            }
+            RegB<ST, NKB> sop;
+            sop.set(St);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                f32x4 d;
+                if constexpr (KDA) d = *reinterpret_cast<const f32x4 *>(&bc.dec[16 * kb + 4 * lg]);
+                else d = f32x4{bc.dec[0], bc.dec[0], bc.dec[0], bc.dec[0]};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) St[kb][i] *= d[i];
+            }
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                RowA<ST, NKB> wa;
+                wa.load(&bc.Wn[16 * rb + lr][0], lg, 1 << 20, swK);
+                U[rb] = sop.mma(U[rb], wa);
+            }
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                RowA<ST, NKB> qa;
+                qa.load(&bc.Qt[16 * rb + lr][0], lg, 1 << 20, swK);
+                Y[rb] = sop.mma(Y[rb], qa);
+            }
+            RegB<ST, NB> uh, ul;
+            uh.set_split(U, ul);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                RowA<ST, NB> kea;
+                kea.load(&bc.KeT[16 * kb + lr][0], lg, 1 << 20, swC);
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st) St[kb] = uh.step(St[kb], kea, st);
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st) St[kb] = ul.step(St[kb], kea, st);
+            }
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                RowA<ST, NB> ma;
+                ma.load(&bc.Mm[16 * rb + lr][0], lg, tri_steps(rb), swC);
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+                    if (st < tri_steps(rb)) Y[rb] = uh.step(Y[rb], ma, st);
+#pragma unroll
+                for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
+                    if (st < tri_steps(rb)) Y[rb] = ul.step(Y[rb], ma, st);
+            }
+            } else {
             // every LDS operand of the chunk, issued up front in the order of use
             RowA<ST, NKB> wa[NB], qa[NB];
             RowA<ST, NB> ta[NB], vb;
@@ -1019,7 +1226,6 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             for (int kb = 0; kb < NKB; ++kb) kea[kb].load(&bc.KeT[16 * kb + lr][0], lg, 1 << 20, swC);
 
             // U = T diag(b) V + W_neg S0^T: the state-independent part first
-            f32x4 U[NB], Y[NB];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
                 U[rb] = Y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1070,6 +1276,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
 #pragma unroll
                     for (int rb = 0; rb < NB; ++rb)
                         if (st < tri_steps(rb)) Y[rb] = ul.step(Y[rb], ma[rb], st);
+            }
             }
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb)
@@ -1131,10 +1338,16 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     } else if (nchunks > 0) {
         // ---- value wave: the value slice through registers, written
         // transposed (value rows, tokens in kpos order) as the fp16 operand
+        // VQ chunks in registers: the loads of chunk c + VQ - 1 are issued
+        // while chunk c + 1 is written to its slot (with two slots, still
+        // two chunks of lead)
         constexpr int VPL = VV / 64;
+        constexpr int VQ = NSLOT < 3 ? 3 : NSLOT;
+        constexpr int UNR = NSLOT % VQ == 0 ? NSLOT : VQ * NSLOT;   // a multiple of both
+        static_assert(UNR % VQ == 0 && UNR % NSLOT == 0, "value ring unroll");
         const IT *gv = static_cast<const IT *>(p.v);
-        IV vr[NSLOT][VPL];
-        bool vok[NSLOT][VPL];
+        IV vr[VQ][VPL];
+        bool vok[VQ][VPL];
         auto issue = [&](int c, int sl) {
             const int cc = min(c, nchunks - 1);
 #pragma unroll
@@ -1146,32 +1359,32 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             }
         };
         using UT = typename std::conditional<sizeof(IT) == 2, unsigned short, unsigned>::type;
-        auto commit = [&](int sl) {
+        auto commit = [&](int rq, int sl) {
 #pragma unroll
             for (int y = 0; y < VPL; ++y) {
                 const int e = lane + 64 * y, vt = e / (DVS / EPV), vc = (e % (DVS / EPV)) * EPV;
-                const UT keep = vok[sl][y] ? UT(~UT(0)) : UT(0);   // rows past the sequence become +0
+                const UT keep = vok[rq][y] ? UT(~UT(0)) : UT(0);   // rows past the sequence become +0
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) {
                     // (element copied out first: a bit cast of a vector element
                     // in place reads element 0 with this compiler)
-                    const IT el = vr[sl][y][i];
+                    const IT el = vr[rq][y][i];
                     const IT x = __builtin_bit_cast(IT, UT(__builtin_bit_cast(UT, el) & keep));
                     slot(sl).Vt[vc + i][kpos<ST>(vt)] = (ST)(float)x;
                 }
             }
         };
 #pragma unroll
-        for (int c = 0; c < NSLOT - 1; ++c) issue(c, c);
-        commit(0);
+        for (int c = 0; c < VQ - 1; ++c) issue(c, c);
+        commit(0, 0);
         lds_barrier();
-        for (int jb = 0; jb < nchunks; jb += NSLOT) {
+        for (int jb = 0; jb < nchunks; jb += UNR) {
 #pragma unroll
-            for (int u = 0; u < NSLOT; ++u) {
+            for (int u = 0; u < UNR; ++u) {
                 const int jc = jb + u;
                 if (jc < nchunks) {
-                    issue(jc + NSLOT - 1, (u + NSLOT - 1) % NSLOT);
-                    if (jc + 1 < nchunks) commit((u + 1) % NSLOT);
+                    issue(jc + VQ - 1, (u + VQ - 1) % VQ);
+                    if (jc + 1 < nchunks) commit((u + 1) % VQ, (u + 1) % NSLOT);
                     lds_barrier();
                 }
             }

@@ -106,7 +106,7 @@ def _decode_tokens(N=4, K=4, H=2, Hk=0, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=
     (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 runs 32- and 64-token chunks
     (dict(chunk=64, qkv=0), 2, "no prefill kernel"),                    # fp32 q/k/v: 16 or 32 only
     (dict(chunk=64, shape=(1, 64, 2, 16, 64, 1, 0)), 2, "no fused prefill kernel"),   # fused: dk >= 32
-    (dict(chunk=64, dvs=64, shape=(1, 64, 2, 128, 128, 1, 0)), 2, "no fused prefill kernel"),
+    (dict(chunk=64, dvs=64, shape=(1, 64, 2, 128, 128, 1, 0)), 2, "no prefill kernel"),   # 64-token chunks: slices of 16 or 32
     (dict(dvs=48), 1, "dv_slice"),
     (dict(shape=(1, 64, 2, 64, 48, 1, 0), dvs=32), 1, "does not divide"),
     (dict(shape=(2, 64, 2, 64, 64, 1, 0)), 1, "num_seqs == batch"),
@@ -187,16 +187,21 @@ def _fused_ws(num_seqs, H, Hk, dk, dv, kda, packed, cus=256):
 
 
 def test_fused_prefill_workspace_size():
-    """bf16 q/k/v with 64-token chunks size the fused kernel's ring:
-    independent of the sequence length."""
+    """bf16 q/k/v with 64-token chunks: d_k = 128 runs the two-kernel path
+    (one record per chunk and head, as for 32-token chunks); other key widths
+    run the fused kernel, whose ring does not depend on the sequence length."""
     lib = gdr.load_library()
     f = lib.gdr_prefill_workspace_bytes
-    for (B, T, H, dk, dv, N, Hk, gate, packed) in [(1, 1000, 4, 64, 64, 9, 0, 0, 0), (2, 32768, 32, 128, 128, 2, 0, 1, 0),
-                                                   (1, 262144, 16, 128, 128, 8, 0, 0, 1),
-                                                   (1, 32768, 48, 128, 128, 1, 16, 0, 0)]:
+    r256 = lambda b: -(-b // 256) * 256
+    for (B, T, H, dk, dv, N, Hk, gate, packed) in [(1, 1000, 4, 64, 64, 9, 0, 0, 0), (1, 777, 6, 32, 48, 3, 2, 1, 1)]:
         sh = gdr.PrefillShape(B, T, H, dk, dv, N, Hk)
         assert f(ctypes.byref(sh), gate, 1, 64, packed) == _fused_ws(N, H, Hk or H, dk, dv, gate == 1, packed)
     assert _fused_ws(2, 32, 32, 128, 128, True, False) < 64 << 20       # KDA 32K: tens of MB, not GB
+    rec64 = lambda kda: r256((128 if kda else 4) * 4 + (3 * 64 * 128 + 2 * 64 * 64) * 2)
+    sh = gdr.PrefillShape(2, 32768, 32, 128, 128, 2, 0)
+    assert f(ctypes.byref(sh), 1, 1, 64, 0) == 2 * 512 * 32 * rec64(True)
+    sh = gdr.PrefillShape(1, 262144, 16, 128, 128, 8, 0)
+    assert f(ctypes.byref(sh), 0, 1, 64, 1) == 256 + 256 + (4096 + 8) * 16 * rec64(False)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
