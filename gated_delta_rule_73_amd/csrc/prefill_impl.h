@@ -337,9 +337,9 @@ struct PrepSmem {
     static constexpr int LDI = DK + 16 / sizeof(IT);   // input rows
     static constexpr int LDA = C + 4;
     // 64-token chunks (WIDE): the four waves' partial Gram tiles are summed
-    // in pairs into two copies, and (K e^g)^T lives in the union past those
-    // copies (written once the staged inputs are no longer read), so that
-    // two workgroups still share a CU.
+    // in pairs into two copies, and (K e^g)^T is parked in the record's W_n
+    // rows in global memory until the W product reads it back, so that two
+    // workgroups still share a CU.
     static constexpr bool WIDE = NB == 4;
     static constexpr int NCOPY = WIDE ? 2 : 4;
     using ST = typename Prec<IT>::ST;
@@ -347,9 +347,7 @@ struct PrepSmem {
     static constexpr int TILEB = 16 * 20 * 4;                    // one fp32 tile, rows of 20
     static constexpr int OFF_TF = NT * TILEB;                    // WIDE: T after the A tiles
     static constexpr int OFF_TFT = OFF_TF + C * LDA * 4;         //   then T^T
-    static constexpr int OFF_KT = NCOPY * 2 * NT * TILEB;        //   (K e^g)^T past the partial tiles
-    static constexpr int RAWB = WIDE ? OFF_KT + DK * LDT * (int)sizeof(ST) : 16;
-    static_assert(!WIDE || OFF_TFT + C * LDA * 4 <= OFF_KT, "T and T^T end before (K e^g)^T");
+    static constexpr int RAWB = WIDE ? OFF_TFT + C * LDA * 4 : 16;
     union alignas(16) {
         struct {
             float G[KDA ? C : 1][LDG];   // KDA: log-decay, then g - m
@@ -376,11 +374,7 @@ struct PrepSmem {
     }
     static_assert(WIDE || C * LDA <= 2 * NT * 16 * 20, "T fits in one wave's partial tiles");
     // operands of W = T diag(b) (K e^g), token index in kpos order
-    alignas(16) ST kt_own[WIDE ? 1 : DK][LDT];
-    __device__ ST (*ktT())[LDT] {
-        if constexpr (WIDE) return reinterpret_cast<ST (*)[LDT]>(u.raw + OFF_KT);
-        else return kt_own;
-    }
+    alignas(16) ST ktT[WIDE ? 1 : DK][LDT];
 };
 
 struct PrepKArgs {
@@ -571,17 +565,17 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
         if (lane < 4) rec.dec[lane] = lane == 0 ? __expf(gC) : 0.f;
     }
     if (tid < C) sm.beta[tid] = br;
-    // (WIDE: the next record's inputs are requested once the Gram tiles
-    // have left registers, which then have room for them)
-    if constexpr (!WIDE) fetch(r + gridDim.x);
+    // (KDA with 64-token chunks: the next record's inputs are requested once
+    // the Gram tiles have left registers, which then have room for them)
+    constexpr bool LATE_FETCH = WIDE && KDA;
+    if constexpr (!LATE_FETCH) fetch(r + gridDim.x);
     __syncthreads();
 
     // ---- B: per-channel prefix sums (KDA), K_end^T to the record and
     // (K e^g)^T to LDS, one key channel per NSEG lanes, SEGL tokens each
-    // (WIDE: (K e^g)^T stays in registers until the staged inputs are read)
+    // (WIDE: (K e^g)^T goes to the record's W_n rows, viewed as [DK][C])
     const int gc = tid / NSEG, gseg = tid % NSEG;
-    typedef typename VecT<ST, 2>::type ST2;
-    ST2 ktw[WIDE ? SEGL / 2 : 1];
+    ST *const ktg = &rec.Wn[0][0];
     {
         float ke[SEGL], kt[SEGL];
         if constexpr (KDA) {
@@ -627,20 +621,16 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
             for (int s = 0; s < SEGL; s += 4) {
                 const ST v4[4] = {(ST)ke[s], (ST)ke[s + 1], (ST)ke[s + 2], (ST)ke[s + 3]};
                 store_vec<ST, 4>(&rec.KeT[gc][kpos<ST>(gseg * SEGL + s)], v4);
-                if constexpr (WIDE) {
-                    ktw[s / 2] = ST2{(ST)kt[s], (ST)kt[s + 1]};
-                    ktw[s / 2 + 1] = ST2{(ST)kt[s + 2], (ST)kt[s + 3]};
-                } else {
-                    const ST w4[4] = {(ST)kt[s], (ST)kt[s + 1], (ST)kt[s + 2], (ST)kt[s + 3]};
-                    store_vec<ST, 4>(&sm.ktT()[gc][kpos<ST>(gseg * SEGL + s)], w4);
-                }
+                const ST w4[4] = {(ST)kt[s], (ST)kt[s + 1], (ST)kt[s + 2], (ST)kt[s + 3]};
+                if constexpr (WIDE) store_vec<ST, 4>(ktg + gc * C + kpos<ST>(gseg * SEGL + s), w4);
+                else store_vec<ST, 4>(&sm.ktT[gc][kpos<ST>(gseg * SEGL + s)], w4);
             }
         } else {
             static_assert(!WIDE, "64-token chunks take the vector path");
 #pragma unroll
             for (int s = 0; s < SEGL; ++s) {
                 rec.KeT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)ke[s];
-                sm.ktT()[gc][kpos<ST>(gseg * SEGL + s)] = (ST)kt[s];
+                sm.ktT[gc][kpos<ST>(gseg * SEGL + s)] = (ST)kt[s];
             }
         }
     }
@@ -735,8 +725,8 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
     }
     __syncthreads();   // the partial tiles overwrite the staged inputs
     if constexpr (WIDE) {
-        // waves 2, 3 store their partial tiles as copies 0, 1 and every
-        // thread its (K e^g)^T entries; then waves 0, 1 add theirs in place
+        // waves 2, 3 store their partial tiles as copies 0, 1; then waves
+        // 0, 1 add theirs in place
         if (wave >= 2) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -745,11 +735,6 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                     sm.u.Pt[wave - 2][t][4 * lg + i][lr] = accA[t][i];
                     sm.u.Pt[wave - 2][NT + t][4 * lg + i][lr] = accM[t][i];
                 }
-        }
-#pragma unroll
-        for (int x = 0; x < SEGL; x += 4) {
-            const ST w4[4] = {ktw[x / 2][0], ktw[x / 2][1], ktw[x / 2 + 1][0], ktw[x / 2 + 1][1]};
-            store_vec<ST, 4>(&sm.ktT()[gc][kpos<ST>(gseg * SEGL + x)], w4);
         }
         __syncthreads();
         if (wave < 2) {
@@ -761,7 +746,7 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                     sm.u.Pt[wave][NT + t][4 * lg + i][lr] += accM[t][i];
                 }
         }
-        fetch(r + gridDim.x);
+        if constexpr (LATE_FETCH) fetch(r + gridDim.x);
     } else {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -940,6 +925,15 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
         // adjacent in the stored k-order and leave as one 16-byte store;
         // fp32 operands, blocks kb = wave, wave + 4, ...
         constexpr int KP = sizeof(ST) == 2 ? 2 : 1;   // key blocks per store
+        // WIDE: this wave's (K e^g)^T rows (one key-block pair) are read back
+        // from the W_n rows before any wave overwrites them with W
+        RowA<ST, NB> ktr[WIDE ? KP : 1];
+        if constexpr (WIDE) {
+            static_assert(DK / (16 * KP) == 4, "one key-block pair per wave");
+#pragma unroll
+            for (int x = 0; x < KP; ++x) ktr[x].load(ktg + (16 * (KP * wave + x) + lr) * C, lg);
+            __syncthreads();
+        }
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
@@ -951,7 +945,8 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                 for (int x = 0; x < KP; ++x) {
                     const int kb = KP * pb + x;
                     RowA<ST, NB> a;
-                    a.load(&sm.ktT()[16 * kb + lr][0], lg);
+                    if constexpr (WIDE) a = ktr[x];
+                    else a.load(&sm.ktT[16 * kb + lr][0], lg);
                     f32x4 acc{0.f, 0.f, 0.f, 0.f};
                     // (k-steps past the diagonal of T's row block tb are zero)
 #pragma unroll
