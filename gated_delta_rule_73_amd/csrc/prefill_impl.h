@@ -566,7 +566,8 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
     }
     if (tid < C) sm.beta[tid] = br;
     // (KDA with 64-token chunks: the next record's inputs are requested once
-    // the Gram tiles have left registers, which then have room for them)
+    // the Gram tiles have left registers, which then have room for them;
+    // requesting its q and k here already spills and was measured slower)
     constexpr bool LATE_FETCH = WIDE && KDA;
     if constexpr (!LATE_FETCH) fetch(r + gridDim.x);
     __syncthreads();
@@ -992,6 +993,69 @@ struct alignas(16) ChainSlot {
     ST Vt[DVS][LDVT];                   // value slice as an MFMA operand: value rows, tokens in kpos order
 };
 
+// 64-token chunks: a whole record per slot leaves room for only two slots,
+// i.e. one chunk of lead for its fetch.  So a slot is split into the fields a
+// chain wave reads before the chunk's mid-point barrier (part A: the decay row,
+// T diag(b), W_n, Q e^g) and after it (part B: K_end^T, M), and each part is
+// refilled as soon as the chain is done with it.  Rows are swizzled as in
+// ChainSlot; each part is padded to whole rounds of the record waves' loads.
+template <int DK, int DVS, int C, bool KDA, typename IT>
+struct alignas(16) ChainSlot64 {
+    using ST = typename Prec<IT>::ST;
+    struct PartA {
+        float dec[KDA ? DK : 4];
+        ST Tm[C][C];
+        ST Wn[C][DK];
+        ST Qt[C][DK];
+    };
+    struct PartB {
+        ST KeT[DK][C];
+        ST Mm[C][C];
+    };
+    static constexpr int ROUND = 64 * kRecordWaves;
+    static constexpr int APIECES = ((int)sizeof(PartA) / 16 + ROUND - 1) / ROUND * ROUND;
+    static constexpr int BPIECES = ((int)sizeof(PartB) / 16 + ROUND - 1) / ROUND * ROUND;
+    static constexpr int RPIECES = APIECES + BPIECES;
+    static constexpr int LDVT = lds_pitch(C * (int)sizeof(ST)) / (int)sizeof(ST);
+    union {
+        PartA r;
+        char raw[16 * APIECES];
+    } a;
+    union {
+        PartB r;
+        char raw[16 * BPIECES];
+    } b;
+    ST Vt[DVS][LDVT];
+};
+
+// Global record piece (plain ChunkRec layout) held by 16-byte position q of
+// part A (PB = false) or part B of a ChainSlot64 (past the part: piece 0).
+template <int DK, int C, bool KDA, typename IT>
+__device__ __forceinline__ int rec64_piece_at(bool PB, int q) {
+    using ST = typename Prec<IT>::ST;
+    constexpr int PD = (KDA ? DK : 4) * 4 / 16;
+    constexpr int GK = DK * (int)sizeof(ST) / 16, GC = C * (int)sizeof(ST) / 16;
+    constexpr int WN = PD, QT = WN + C * GK, KE = QT + C * GK, TM = KE + DK * GC, MM = TM + C * GC;
+    auto row = [](int base, int G, int x) {
+        const int r = x / G, g = x % G;
+        return base + r * G + (g ^ row_swizzle(G, r));
+    };
+    if (!PB) {
+        if (q < PD) return q;
+        q -= PD;
+        if (q < C * GC) return row(TM, GC, q);
+        q -= C * GC;
+        if (q < C * GK) return row(WN, GK, q);
+        q -= C * GK;
+        if (q < C * GK) return row(QT, GK, q);
+        return 0;
+    }
+    if (q < DK * GC) return row(KE, GC, q);
+    q -= DK * GC;
+    if (q < C * GC) return row(MM, GC, q);
+    return 0;
+}
+
 // The record piece held by 16-byte position q of a slot's record area (past
 // the record: any valid piece).  The decay row is stored plainly; the rows of
 // Wn, Qt (G = DK groups) and KeT, Tm, Mm (G = C groups) are swizzled.
@@ -1040,12 +1104,12 @@ struct ChainKArgs {
 
 template <int DK, int DVS, int C, bool KDA, typename IT, bool OUTB>
 __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(ChainKArgs p) {
-    using Slot = ChainSlot<DK, DVS, C, KDA, IT>;
+    constexpr int NB = C / 16;                     // 16-token blocks per chunk
+    using Slot = typename std::conditional<NB == 4, ChainSlot64<DK, DVS, C, KDA, IT>, ChainSlot<DK, DVS, C, KDA, IT>>::type;
     using Rec = ChunkRec<DK, C, KDA, IT>;
     using ST = typename Prec<IT>::ST;
     constexpr bool SPLIT = Prec<IT>::SPLIT;
     constexpr int NLW = kLoaderWaves;
-    constexpr int NB = C / 16;                     // 16-token blocks per chunk
     constexpr int NKB = DK / 16;                   // 16-channel key blocks
     constexpr int EPV = 16 / sizeof(IT);
     using IV = typename VecT<IT, EPV>::type;
@@ -1127,7 +1191,6 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
         lds_barrier();
         for (int jc = 0; jc < nchunks; ++jc) {
             const Slot &bs = slot(jc % NSLOT);
-            const Rec &bc = bs.rec.r;
             const int t0 = bos + jc * C;
             const int nv = min(C, eos - t0);
             OT *ob = static_cast<OT *>(p.out) + ((size_t)t0 * H + h) * DV + v0 + 16 * cb;
@@ -1136,7 +1199,11 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             f32x4 U[NB], Y[NB];
             if constexpr (NB == 4) {
             // 64-token chunks: too many operands to hold at once, so each
-            // product's record rows are read just before it
+            // product's record rows are read just before it.  Part A of the
+            // slot feeds U and Y, part B the state update and O; the barrier
+            // between them lets the loaders refill part A.
+            const auto &bc = bs.a.r;
+            const auto &bcb = bs.b.r;
             {
                 RowA<ST, NB> vb;
                 vb.load(&bs.Vt[16 * cb + lr][0], lg);
@@ -1174,10 +1241,11 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             }
             RegB<ST, NB> uh, ul;
             uh.set_split(U, ul);
+            lds_barrier();   // mid-chunk: part A is free
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 RowA<ST, NB> kea;
-                kea.load(&bc.KeT[16 * kb + lr][0], lg, 1 << 20, swC);
+                kea.load(&bcb.KeT[16 * kb + lr][0], lg, 1 << 20, swC);
 #pragma unroll
                 for (int st = 0; st < RegB<ST, NB>::STEPS; ++st) St[kb] = uh.step(St[kb], kea, st);
 #pragma unroll
@@ -1186,7 +1254,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
                 RowA<ST, NB> ma;
-                ma.load(&bc.Mm[16 * rb + lr][0], lg, tri_steps(rb), swC);
+                ma.load(&bcb.Mm[16 * rb + lr][0], lg, tri_steps(rb), swC);
 #pragma unroll
                 for (int st = 0; st < RegB<ST, NB>::STEPS; ++st)
                     if (st < tri_steps(rb)) Y[rb] = uh.step(Y[rb], ma, st);
@@ -1195,6 +1263,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
                     if (st < tri_steps(rb)) Y[rb] = ul.step(Y[rb], ma, st);
             }
             } else {
+            const Rec &bc = bs.rec.r;
             // every LDS operand of the chunk, issued up front in the order of use
             RowA<ST, NKB> wa[NB], qa[NB];
             RowA<ST, NB> ta[NB], vb;
@@ -1295,7 +1364,55 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     // flight is fixed.  The two kinds of loader run on separate waves: a wave
     // whose code both writes LDS and has LDS-direct loads in flight would be
     // made to wait for all of them before each write.
-    if (nchunks > 0 && wave < NRW) {
+    if (nchunks > 0 && wave < NRW && NB == 4) {
+        if constexpr (NB == 4) {
+        // ---- record waves, 64-token chunks: the slot's two parts are loaded
+        // separately, in the order A(0) B(0) A(1) B(1) A(2) ...: part B of
+        // chunk c + 1 once chunk c - 1 is done with that slot (its end
+        // barrier), part A of chunk c + 2 once chunk c is done with part A
+        // (its mid-point barrier).  Each barrier waits for the part the
+        // chain reads next, with the two parts issued after it in flight.
+        constexpr int XA = Slot::APIECES / (64 * NRW), XB = Slot::BPIECES / (64 * NRW);
+        constexpr int PEND = XA + XB;
+        static_assert(PEND < 64, "vmcnt range");
+        int goa[XA], gob[XB];
+#pragma unroll
+        for (int x = 0; x < XA; ++x) goa[x] = 16 * rec64_piece_at<DK, C, KDA, IT>(false, 64 * (x * NRW + wave) + lane);
+#pragma unroll
+        for (int x = 0; x < XB; ++x) gob[x] = 16 * rec64_piece_at<DK, C, KDA, IT>(true, 64 * (x * NRW + wave) + lane);
+        auto issue_a = [&](int c, int sl) {
+            const char *src = rec0 + (size_t)min(c, nchunks - 1) * H * RS;
+            char *dst = slot(sl).a.raw + 1024 * wave;
+#pragma unroll
+            for (int x = 0; x < XA; ++x) lds_direct_load16(src + goa[x], dst + 1024 * NRW * x);
+        };
+        auto issue_b = [&](int c, int sl) {
+            const char *src = rec0 + (size_t)min(c, nchunks - 1) * H * RS;
+            char *dst = slot(sl).b.raw + 1024 * wave;
+#pragma unroll
+            for (int x = 0; x < XB; ++x) lds_direct_load16(src + gob[x], dst + 1024 * NRW * x);
+        };
+        // every part but the two issued last has landed
+        auto wait_pend = [&]() { __builtin_amdgcn_s_waitcnt((PEND & 15) | ((PEND >> 4) << 14) | (7 << 4) | (15 << 8)); };
+        issue_a(0, 0);
+        issue_b(0, 0);
+        issue_a(1, 1);
+        wait_pend();       // A(0)
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            const int sl = c & 1;
+            issue_b(c + 1, sl ^ 1);
+            wait_pend();   // B(c)
+            lds_barrier();                 // chunk c: mid-point
+            issue_a(c + 2, sl);
+            wait_pend();   // A(c + 1)
+            lds_barrier();                 // chunk c: end
+        }
+        // no LDS-direct write may land after the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(0);
+        }
+    } else if (nchunks > 0 && wave < NRW) {
+        if constexpr (NB != 4) {
         // ---- record waves: global -> LDS directly, no registers.  Load x of
         // wave w fills the slot's record bytes [1 KB (x NRW + w), +1 KB), lane
         // l the 16-byte position q = 64 (x NRW + w) + l, which holds the
@@ -1330,6 +1447,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
         }
         // no LDS-direct write may land after the workgroup's LDS is released
         __builtin_amdgcn_s_waitcnt(0);
+        }
     } else if (nchunks > 0) {
         // ---- value wave: the value slice through registers, written
         // transposed (value rows, tokens in kpos order) as the fp16 operand
@@ -1379,6 +1497,7 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
                 const int jc = jb + u;
                 if (jc < nchunks) {
                     issue(jc + VQ - 1, (u + VQ - 1) % VQ);
+                    if constexpr (NB == 4) lds_barrier();   // chunk jc: mid-point
                     if (jc + 1 < nchunks) commit((u + 1) % VQ, (u + 1) % NSLOT);
                     lds_barrier();
                 }
