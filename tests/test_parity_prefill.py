@@ -64,6 +64,22 @@ def test_kda_prefill_32k_workload():
 
 
 @pytest.mark.slow
+def test_kda_prefill_32k_workload_chunk64():
+    """The same workload with 64-token chunks (the two-kernel path's
+    four-block inverse and split chain slots over 512 chunks per sequence):
+    whole tensors against the oracle."""
+    w = WORKLOADS["kda_prefill_32k"]
+    _check_all(prefill_inputs(w, DEV), "kda_prefill_32k, chunk 64 (whole tensors)", chunk_size=64)
+
+
+@pytest.mark.slow
+def test_packed_gdn_256k_workload_chunk64():
+    """Packed sequences of ragged lengths with 64-token chunks."""
+    w = WORKLOADS["packed_gdn_256k"]
+    _check_all(prefill_inputs(w, DEV), "packed_gdn_256k, chunk 64 (whole tensors)", chunk_size=64)
+
+
+@pytest.mark.slow
 def test_packed_gdn_256k_workload():
     """262144 tokens as 8 packed sequences (4096..61440 each), H=16, d=128."""
     w = WORKLOADS["packed_gdn_256k"]
@@ -103,7 +119,9 @@ def test_prefill_bf16_shapes(dk, dv, H, T, gate, init, chunk, dvs):
     _check_all(inp, f"bf16 dk={dk} dv={dv} H={H} T={T} {gate} init={init}", chunk_size=chunk, dv_slice=dvs)
 
 
-# 64-token chunks: the single-kernel prefill (records shared through a ring)
+# 64-token chunks: d_k = 128 runs the two kernels (four-block inverse, split
+# chain slots), d_k = 32 and 64 the single-kernel prefill (records shared
+# through a ring)
 FUSED_CASES = [
     # dk, dv, H, T, gate, init, dv_slice (0: automatic)
     (128, 128, 2, 1, "head", False, 0),
