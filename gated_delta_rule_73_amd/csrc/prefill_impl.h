@@ -348,9 +348,15 @@ struct PrepSmem {
     static constexpr int OFF_TF = NT * TILEB;                    // WIDE: T after the A tiles
     static constexpr int OFF_TFT = OFF_TF + C * LDA * 4;         //   then T^T
     static constexpr int RAWB = WIDE ? OFF_TFT + C * LDA * 4 : 16;
+    // WIDE: the staged q block is also where C parks (K e^g)^T for E, so it
+    // must lie past everything written in between
+    static_assert(!WIDE || (C * LDG * 4 + C * LDI * (int)sizeof(IT) >= NCOPY * 2 * NT * TILEB &&
+                            C * LDG * 4 + C * LDI * (int)sizeof(IT) >= RAWB), "staged q past the tiles");
     union alignas(16) {
         struct {
-            float G[KDA ? C : 1][LDG];   // KDA: log-decay, then g - m
+            // KDA: log-decay, then g - m (WIDE GDN: unused rows that keep Qs
+            // past the partial tiles, T and T^T, as for KDA)
+            float G[KDA || WIDE ? C : 1][LDG];
             IT Ks[C][LDI];
             IT Qs[C][LDI];
         } in;
@@ -565,18 +571,17 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
         if (lane < 4) rec.dec[lane] = lane == 0 ? __expf(gC) : 0.f;
     }
     if (tid < C) sm.beta[tid] = br;
-    // (KDA with 64-token chunks: the next record's inputs are requested once
+    // (64-token chunks: the next record's inputs are requested once
     // the Gram tiles have left registers, which then have room for them;
     // requesting its q and k here already spills and was measured slower)
-    constexpr bool LATE_FETCH = WIDE && KDA;
+    constexpr bool LATE_FETCH = WIDE;
     if constexpr (!LATE_FETCH) fetch(r + gridDim.x);
     __syncthreads();
 
     // ---- B: per-channel prefix sums (KDA), K_end^T to the record and
     // (K e^g)^T to LDS, one key channel per NSEG lanes, SEGL tokens each
-    // (WIDE: (K e^g)^T goes to the record's W_n rows, viewed as [DK][C])
+    // (WIDE: (K e^g)^T is formed in C below instead)
     const int gc = tid / NSEG, gseg = tid % NSEG;
-    ST *const ktg = &rec.Wn[0][0];
     {
         float ke[SEGL], kt[SEGL];
         if constexpr (KDA) {
@@ -602,7 +607,7 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                 sm.u.in.G[t][gc] = g - m;
                 const float kv = (float)sm.u.in.Ks[t][gc];
                 ke[s] = kv * __expf(gC - g);
-                kt[s] = kv * __expf(g);
+                if constexpr (!WIDE) kt[s] = kv * __expf(g);
             }
             if (gseg == 0) {
                 sm.em[gc] = __expf(m);
@@ -614,7 +619,7 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                 const int t = gseg * SEGL + s;
                 const float kv = (float)sm.u.in.Ks[t][gc];
                 ke[s] = kv * sm.egc[t];
-                kt[s] = kv * sm.egt[t];
+                if constexpr (!WIDE) kt[s] = kv * sm.egt[t];
             }
         }
         if constexpr (SEGL % 4 == 0) {
@@ -622,9 +627,10 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
             for (int s = 0; s < SEGL; s += 4) {
                 const ST v4[4] = {(ST)ke[s], (ST)ke[s + 1], (ST)ke[s + 2], (ST)ke[s + 3]};
                 store_vec<ST, 4>(&rec.KeT[gc][kpos<ST>(gseg * SEGL + s)], v4);
-                const ST w4[4] = {(ST)kt[s], (ST)kt[s + 1], (ST)kt[s + 2], (ST)kt[s + 3]};
-                if constexpr (WIDE) store_vec<ST, 4>(ktg + gc * C + kpos<ST>(gseg * SEGL + s), w4);
-                else store_vec<ST, 4>(&sm.ktT[gc][kpos<ST>(gseg * SEGL + s)], w4);
+                if constexpr (!WIDE) {
+                    const ST w4[4] = {(ST)kt[s], (ST)kt[s + 1], (ST)kt[s + 2], (ST)kt[s + 3]};
+                    store_vec<ST, 4>(&sm.ktT[gc][kpos<ST>(gseg * SEGL + s)], w4);
+                }
             }
         } else {
             static_assert(!WIDE, "64-token chunks take the vector path");
@@ -661,6 +667,13 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                 accM[tt] = gram_mma(accM[tt], fq[I], fk[J]);
             }
         };
+        // WIDE: (K e^g)^T of this k-step's 32 channels, for the W product.
+        // Only this wave reads these channels' columns of the staged q, so
+        // once a pair of row blocks is done their q columns take the values:
+        // piece (channel j, kpos group 4 s' + g) of (K e^g)^T goes to q row
+        // 32 s' + j, columns 32 s + 8 g .. + 7 (the W product reads it back).
+        ST ktp[2][8];
+        ST *const qcols = reinterpret_cast<ST *>(&sm.u.in.Qs[0][0]) + 32 * s;
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             const int t = 16 * rb + lr;
@@ -693,6 +706,7 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                         fql[rb][4 * hh + i] = (FT)(lq - (float)qh);
                         frl[rb][4 * hh + i] = (FT)(rk - (float)rh);
                         qt[i] = (ST)(lq * emv[i] * p.scale);
+                        if constexpr (WIDE) ktp[rb & 1][4 * hh + i] = (ST)(lk * emv[i]);
                     }
                 } else {
                     // raw k, q for the Gram (the decay scales its fp32 result);
@@ -703,6 +717,7 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                         fk[rb][4 * hh + i] = (ST)kf[i];
                         fq[rb][4 * hh + i] = (ST)qf[i];
                         qt[i] = (ST)(qf[i] * e * p.scale);
+                        if constexpr (WIDE) ktp[rb & 1][4 * hh + i] = (ST)(kf[i] * e);
                     }
                 }
 #pragma unroll
@@ -715,6 +730,16 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
             if constexpr (WIDE) {
 #pragma unroll
                 for (int J = 0; J <= rb; ++J) tile_mma(rb, J);
+                if (rb & 1) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                qcols[(32 * (rb >> 1) + 16 * hh + 4 * lg + i) * SM::LDI + 8 * (lr >> 2) + 4 * h + (lr & 3)] =
+                                    ktp[h][4 * hh + i];
+                }
             }
         }
         if constexpr (!WIDE) {
@@ -926,15 +951,9 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
         // adjacent in the stored k-order and leave as one 16-byte store;
         // fp32 operands, blocks kb = wave, wave + 4, ...
         constexpr int KP = sizeof(ST) == 2 ? 2 : 1;   // key blocks per store
-        // WIDE: this wave's (K e^g)^T rows (one key-block pair) are read back
-        // from the W_n rows before any wave overwrites them with W
-        RowA<ST, NB> ktr[WIDE ? KP : 1];
-        if constexpr (WIDE) {
-            static_assert(DK / (16 * KP) == 4, "one key-block pair per wave");
-#pragma unroll
-            for (int x = 0; x < KP; ++x) ktr[x].load(ktg + (16 * (KP * wave + x) + lr) * C, lg);
-            __syncthreads();
-        }
+        // WIDE: this wave's key-block pair is the k-step it took in C, whose
+        // (K e^g)^T pieces sit in its columns of the staged q
+        static_assert(!WIDE || DK / (16 * KP) == 4, "one key-block pair per wave");
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
@@ -946,8 +965,14 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
                 for (int x = 0; x < KP; ++x) {
                     const int kb = KP * pb + x;
                     RowA<ST, NB> a;
-                    if constexpr (WIDE) a = ktr[x];
-                    else a.load(&sm.ktT[16 * kb + lr][0], lg);
+                    if constexpr (WIDE) {
+                        const ST *qc = reinterpret_cast<const ST *>(&sm.u.in.Qs[0][0]) + 32 * wave + 8 * lg;
+#pragma unroll
+                        for (int st = 0; st < NB / 2; ++st)
+                            a.f[st] = *reinterpret_cast<const f16x8 *>(qc + (32 * st + 16 * x + lr) * SM::LDI);
+                    } else {
+                        a.load(&sm.ktT[16 * kb + lr][0], lg);
+                    }
                     f32x4 acc{0.f, 0.f, 0.f, 0.f};
                     // (k-steps past the diagonal of T's row block tb are zero)
 #pragma unroll
