@@ -270,6 +270,20 @@ def test_prefill_segments(gate):
                                 workspace=ws[: 2 * 15 * 2 * rec], chunk_size=32)
 
 
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_segments_chunk64(gate):
+    """The same at 64-token chunks (d_k = 128, the two-kernel path): 130
+    chunks in segments of 64, 64 and 2 match the one-pass run bit for bit."""
+    T = 64 * 64 * 2 + 77
+    inp = _small(128, 128, 2, T, gate, torch.bfloat16, True, seed=67, B=2)
+    out, fin = _check_all(inp, f"one pass, chunk 64, {gate}", chunk_size=64)
+    rec = -(-((128 * 4 if gate == "channel" else 16) + (3 * 64 * 128 + 2 * 64 * 64) * 2) // 256) * 256
+    ws = torch.empty(2 * 64 * 2 * rec + 2 * 2 * 128 * 128 * 4, dtype=torch.uint8, device=DEV)
+    say("segments of 64 chunks of 64 tokens")
+    o1, f1 = _gpu(inp, workspace=ws, chunk_size=64)
+    assert torch.equal(o1, out) and torch.equal(f1, fin)
+
+
 # ------------------------------------------------------- GPU properties ----
 def test_prefill_deterministic():
     inp = _small(128, 128, 2, 333, "channel", torch.bfloat16, True, seed=51)

@@ -80,6 +80,10 @@ def test_static_scratch_consecutive_calls():
     # 3: smaller still, the fused 64-token kernel
     tiny = _inputs("gdn_fused", 64, 64, 2, 200, "head", seed=13)
     _compare("GDN T=200 H=2 d=64, chunk 64 (fused)", tiny, chunk=64)
+    # 4: 64-token chunks at d_k = 128 (the two kernels), records past the
+    # scratch, so in segments
+    wide = _inputs("kda_wide", 128, 128, 8, 8192, "channel", B=2, seed=14)
+    _compare("KDA B=2 T=8192 H=8 d=128, chunk 64 (segmented)", wide, chunk=64)
 
 
 def test_static_scratch_rejects_larger_problem():
