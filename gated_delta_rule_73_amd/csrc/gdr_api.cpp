@@ -119,12 +119,6 @@ PrefillWorkspace fit_workspace(const gdr_prefill_shape &s, bool kda, bool bf16, 
 // automatic chunk size: 32 tokens where compiled (the fastest schedule
 // measured on every workload), else 16
 int auto_chunk(bool bf16, bool kda, int dk) { return gdr::prefill_supported(bf16, kda, dk, 16, 32) ? 32 : 16; }
-// bf16 q/k/v with 64-token chunks: the two-kernel path where it is compiled
-// (d_k = 128), else the fused single-kernel prefill
-bool use_fused(bool bf16, bool kda, int dk, int chunk) {
-    return bf16 && chunk == gdr::kFusedChunkHost && !gdr::prefill_supported(bf16, kda, dk, 16, chunk) &&
-           !gdr::prefill_supported(bf16, kda, dk, 32, chunk);
-}
 
 
 constexpr int kMaxDecodeTokens = 64;
@@ -471,16 +465,6 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
     if (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
     const bool bf16 = qkv_dtype == GDR_BF16, kda = gate == GDR_GATE_CHANNEL;
     const int C = chunk_size ? chunk_size : auto_chunk(bf16, kda, s.head_dim_k);
-    if (use_fused(bf16, kda, s.head_dim_k, C)) {
-        // enough for every value-slice width a call may pick
-        int hk = 0;
-        if (resolve_qk_heads(s.num_heads, s.num_qk_heads, hk) != GDR_SUCCESS) return 0;
-        size_t most = 0;
-        for (int dvs : {0, 16, 32, 64})
-            most = std::max(most, gdr::fused_plan(kda, s.head_dim_k, s.head_dim_v, s.num_seqs, s.num_heads, hk, dvs,
-                                                  packed != 0).total);
-        return most;
-    }
     return prefill_workspace(s, kda, bf16, C, packed != 0).total;
 }
 
@@ -528,21 +512,11 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     // value-slice width that needs the fewest rounds of chain workgroups
     int C = chunk_size;
     if (!C) C = auto_chunk(bf16, kda, dk);
-    const bool fused = use_fused(bf16, kda, dk, C);
-    gdr::FusedPlan plan;
     int DVS = dv_slice;
-    if (fused) {
-        plan = gdr::fused_plan(kda, dk, dv, s.num_seqs, s.num_heads, hk, dv_slice, packed);
-        if (!plan.dvs)
-            return fail(GDR_ERROR_NOT_SUPPORTED, "no fused prefill kernel for dk=%d dv=%d dv_slice=%d chunk=%d", dk,
-                        dv, dv_slice, C);
-        DVS = plan.dvs;
-    } else {
-        if (!DVS) DVS = gdr::auto_dv_slice(bf16, kda, dk, dv, C, (long)s.num_seqs * s.num_heads);
-        if (!gdr::prefill_supported(bf16, kda, dk, DVS, C))
-            return fail(GDR_ERROR_NOT_SUPPORTED, "no prefill kernel for %s dk=%d dv_slice=%d chunk=%d",
-                        bf16 ? "bf16" : "fp32", dk, DVS, C);
-    }
+    if (!DVS) DVS = gdr::auto_dv_slice(bf16, kda, dk, dv, C, (long)s.num_seqs * s.num_heads);
+    if (!gdr::prefill_supported(bf16, kda, dk, DVS, C))
+        return fail(GDR_ERROR_NOT_SUPPORTED, "no prefill kernel for %s dk=%d dv_slice=%d chunk=%d",
+                    bf16 ? "bf16" : "fp32", dk, DVS, C);
 
     const size_t es = dsize(qkv_dtype), gs = dsize(gate_dtype);
     const size_t nq = (size_t)tokens * hk * dk, nv = (size_t)tokens * s.num_heads * dv;
@@ -559,10 +533,10 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
         return fail(GDR_ERROR_INVALID_VALUE, "beta must be %zu-byte aligned, cu_seqlens 4-byte, log_alpha %zu-byte",
                     gs, kda ? 4 * gs : gs);
 
-    const PrefillWorkspace ws = fused ? PrefillWorkspace{} : fit_workspace(s, kda, bf16, C, packed, workspace_bytes);
-    if (!fused && (ws.record_chunks + 8) * s.num_heads >= INT32_MAX)
+    const PrefillWorkspace ws = fit_workspace(s, kda, bf16, C, packed, workspace_bytes);
+    if ((ws.record_chunks + 8) * s.num_heads >= INT32_MAX)
         return fail(GDR_ERROR_NOT_SUPPORTED, "more than 2^31 (chunk, head) records in one pass");
-    const size_t need_ws = fused ? plan.total : ws.total;
+    const size_t need_ws = ws.total;
     if (workspace_bytes < need_ws)
         return fail(GDR_ERROR_INSUFFICIENT_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need_ws);
     if (need_ws && !workspace) return fail(GDR_ERROR_INVALID_VALUE, "workspace is NULL");
@@ -608,20 +582,6 @@ gdr_status gdr_prefill_chunked(const gdr_prefill_shape *shape, gdr_gate gate, gd
     a.out = out;
     a.final_state = final_state;
     char *wsb = static_cast<char *>(workspace);
-    if (fused) {
-        a.fused = true;
-        a.f_ns = plan.ns;
-        a.f_d = plan.d;
-        a.f_ngroups = plan.ngroups;
-        a.f_gpx = plan.gpx;
-        a.f_grid = plan.grid;
-        a.f_ctl = reinterpret_cast<int *>(wsb + plan.ctl_off);
-        a.f_ring = wsb + plan.ring_off;
-        a.f_scratch = wsb + plan.scratch_off;
-        a.order = packed ? reinterpret_cast<int32_t *>(wsb + plan.order_off) : nullptr;
-        a.chunk_offset = packed ? reinterpret_cast<int32_t *>(wsb + plan.choff_off) : nullptr;
-        return launch_status(gdr::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "gdr_prefill_chunked");
-    }
     a.order = packed ? reinterpret_cast<int32_t *>(wsb + ws.order_off) : nullptr;
     a.chunk_offset = packed ? reinterpret_cast<int32_t *>(wsb + ws.choff_off) : nullptr;
     a.records = wsb ? wsb + ws.rec_off : nullptr;

@@ -43,38 +43,7 @@ struct PrefillArgs {
     int num_segments;               // dense batches in a bounded workspace: chunk segments
     int segment_chunks;             //   chunks per segment (records of one segment resident)
     float *carry;                   //   state between segments [num_seqs, H, dv, dk]
-    // fused single-kernel path (bf16 q/k/v, 64-token chunks; fused_impl.h)
-    bool fused;
-    int f_ns, f_d, f_ngroups, f_gpx, f_grid;   // slices per group, ring depth, groups, groups per XCD, workgroups
-    int *f_ctl;                     // handshake words
-    char *f_ring, *f_scratch;       // record rings, per-workgroup scratch
 };
-
-// ---- fused prefill: workspace and launch plan --------------------------------
-constexpr int kFusedChunkHost = 64;
-// one ring record (fused_impl.h FusedRec): e^{g_C}, W_n, K_end^T, T diag(b),
-// M, Q e^g; fp16 operands, padded to 256 bytes
-constexpr size_t fused_record_bytes(int dk, bool kda) {
-    const size_t C = kFusedChunkHost;
-    return (((size_t)(kda ? dk : 4) * 4 + (3 * C * dk + 2 * C * C) * 2) + 255) & ~size_t(255);
-}
-// the prep waves' per-workgroup scratch (FusedScratch): right Gram operands
-// of every 16-token row tile, (K e^g)^T
-constexpr size_t fused_scratch_bytes(int dk, bool kda) {
-    const size_t C = kFusedChunkHost;
-    return (((C / 16) * (kda ? 2 : 1) * 16 * dk + (size_t)dk * C) * 2 + 255) & ~size_t(255);
-}
-struct FusedPlan {
-    int dvs = 0, ns = 0, d = 0, ngroups = 0, gpx = 0, grid = 0;
-    size_t order_off = 0, choff_off = 0, ctl_off = 0, ring_off = 0, scratch_off = 0, total = 0;
-};
-// True when the fused kernel is compiled for (gate kind, d_k, value slice).
-bool fused_supported(bool kda, int dk, int dvs);
-// Launch plan and workspace layout.  dvs_req = 0 picks the slice width; the
-// result has dvs = 0 when no fused kernel fits.
-FusedPlan fused_plan(bool kda, int dk, int dv, int num_seqs, int num_heads, int num_qk_heads, int dvs_req,
-                     bool packed);
-hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t st);
 
 // The prefill workspace of gdr_prefill_chunked_static (static_scratch.hip):
 // one array of this size per device; static_scratch returns its address on

@@ -10,7 +10,6 @@
 // counts; quadratic in the number of sequences, which is small).
 #include <algorithm>
 
-#include "fused_impl.h"
 #include "launch.h"
 #include "prefill_shapes.h"
 
@@ -84,116 +83,7 @@ hipError_t launch_schedule(const int32_t *cu, int n, int chunk, int32_t *order, 
     return hipGetLastError();
 }
 
-hipError_t launch_fused_gdn(const FusedArgs &fa, int dk, int dvs, int grid, hipStream_t st);
-hipError_t launch_fused_kda(const FusedArgs &fa, int dk, int dvs, int grid, hipStream_t st);
-
-// Fused prefill: d_k in {32, 64, 128}; value slices of 16 or 32 channels (a
-// 64-channel slice needs a fourth chain wave, which leaves too few registers
-// per wave).
-bool fused_supported(bool kda, int dk, int dvs) {
-    (void)kda;
-    if (!(dk == 32 || dk == 64 || dk == 128)) return false;
-    return dvs == 16 || dvs == 32;
-}
-
-namespace {
-size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;   // no device to ask: MI355X
-    return cus;
-}
-}  // namespace
-
-// One fused workgroup fills a CU's LDS, so the device holds one per CU; all
-// workgroups of a call must be resident together (the slices of a group wait
-// on one another), so the grid never exceeds the CU count.  A group of NS
-// slices serves units in turn; the groups per XCD cover the largest number of
-// units any XCD receives, up to what the CUs hold.  The slice width is the
-// narrowest whose groups all fit at once (most workgroups, most record
-// producers per unit), else the widest compiled.
-FusedPlan fused_plan(bool kda, int dk, int dv, int num_seqs, int num_heads, int num_qk_heads, int dvs_req,
-                     bool packed) {
-    FusedPlan pl;
-    const int cap = device_cus();
-    const int G = num_heads / num_qk_heads;
-    const long NP = (long)num_seqs * num_qk_heads;
-    const long per_xcd = (NP + 7) / 8 * G;              // units on the busiest XCD
-    int dvs = dvs_req;
-    if (!dvs) {
-        for (int cand : {16, 32}) {
-            if (dv % cand || !fused_supported(kda, dk, cand)) continue;
-            dvs = cand;                                     // widest so far
-            if ((long)8 * per_xcd * (dv / cand) <= cap) break;
-        }
-    }
-    if (!dvs || dv % dvs || !fused_supported(kda, dk, dvs)) return pl;
-    const int ns = dv / dvs;
-    if (8 * ns > cap) return pl;                           // one group per XCD must fit
-    pl.dvs = dvs;
-    pl.ns = ns;
-    // ring depth: the records being built (one per slice) and the ones the
-    // loaders and chains still read
-    pl.d = ns + 2;
-    pl.gpx = (int)std::max<long>(1, std::min<long>(per_xcd, cap / (8 * ns)));
-    pl.ngroups = 8 * pl.gpx;
-    pl.grid = pl.ngroups * ns;
-    size_t off = 0;
-    if (packed) {
-        pl.order_off = off;
-        off += r256(4 * (size_t)num_seqs);
-        pl.choff_off = off;
-        off += r256(4 * ((size_t)num_seqs + 1));
-    }
-    pl.ctl_off = off;
-    off += r256(4 * ((size_t)pl.ngroups * (pl.d + 2 * ns) + 1));
-    pl.ring_off = off;
-    off += (size_t)pl.ngroups * pl.d * fused_record_bytes(dk, kda);
-    pl.scratch_off = off;
-    off += (size_t)pl.grid * fused_scratch_bytes(dk, kda);
-    pl.total = off;
-    return pl;
-}
-
-hipError_t launch_prefill_fused(const PrefillArgs &a, hipStream_t st) {
-    if (a.num_seqs == 0 || a.num_heads == 0) return hipSuccess;
-    if (a.cu_seqlens) {
-        const hipError_t e = launch_schedule(a.cu_seqlens, a.num_seqs, a.chunk, a.order, a.chunk_offset, st);
-        if (e != hipSuccess) return e;
-    }
-    FusedArgs fa;
-    fa.T = a.seqlen;
-    fa.H = a.num_heads;
-    fa.HK = a.num_qk_heads;
-    fa.G = a.num_heads / a.num_qk_heads;
-    fa.DV = a.dv;
-    fa.num_seqs = a.num_seqs;
-    fa.NS = a.f_ns;
-    fa.D = a.f_d;
-    fa.ngroups = a.f_ngroups;
-    fa.gpx = a.f_gpx;
-    fa.scale = a.scale;
-    fa.gate_bf16 = a.gate_bf16;
-    fa.out_bf16 = a.out_bf16;
-    fa.q = a.q; fa.k = a.k; fa.v = a.v;
-    fa.beta = a.beta;
-    fa.log_alpha = a.log_alpha;
-    fa.state_in = a.initial_state;
-    fa.state_out = a.final_state;
-    fa.cu = a.cu_seqlens;
-    fa.order = a.cu_seqlens ? a.order : nullptr;
-    fa.ring = a.f_ring;
-    fa.scratch = a.f_scratch;
-    fa.ctl = a.f_ctl;
-    fa.out = a.out;
-    return a.kda ? launch_fused_kda(fa, a.dk, a.dv_slice, a.f_grid, st)
-                 : launch_fused_gdn(fa, a.dk, a.dv_slice, a.f_grid, st);
-}
-
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
-    if (a.fused) return launch_prefill_fused(a, st);
     if (a.num_seqs == 0 || a.num_heads == 0) return hipSuccess;
     if (a.cu_seqlens) {
         const hipError_t e = launch_schedule(a.cu_seqlens, a.num_seqs, a.chunk, a.order, a.chunk_offset, st);

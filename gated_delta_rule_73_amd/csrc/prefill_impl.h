@@ -337,8 +337,8 @@ struct PrepSmem {
     static constexpr int LDI = DK + 16 / sizeof(IT);   // input rows
     static constexpr int LDA = C + 4;
     // 64-token chunks (WIDE): the four waves' partial Gram tiles are summed
-    // in pairs into two copies, and (K e^g)^T is parked in the record's W_n
-    // rows in global memory until the W product reads it back, so that two
+    // in pairs into two copies, and (K e^g)^T is parked in the staged q's
+    // columns once the Gram phase has read them (see the kernel), so that two
     // workgroups still share a CU.
     static constexpr bool WIDE = NB == 4;
     static constexpr int NCOPY = WIDE ? 2 : 4;
@@ -348,18 +348,29 @@ struct PrepSmem {
     static constexpr int OFF_TF = NT * TILEB;                    // WIDE: T after the A tiles
     static constexpr int OFF_TFT = OFF_TF + C * LDA * 4;         //   then T^T
     static constexpr int RAWB = WIDE ? OFF_TFT + C * LDA * 4 : 16;
-    // WIDE: the staged q block is also where C parks (K e^g)^T for E, so it
-    // must lie past everything written in between
-    static_assert(!WIDE || (C * LDG * 4 + C * LDI * (int)sizeof(IT) >= NCOPY * 2 * NT * TILEB &&
-                            C * LDG * 4 + C * LDI * (int)sizeof(IT) >= RAWB), "staged q past the tiles");
+    // WIDE: the staged q block is also where the Gram phase parks (K e^g)^T
+    // for the W product, so it must lie past everything written in between
+    // (the partial tiles, then A, T and T^T): padding before Ks where needed.
+    static constexpr int GR = KDA ? C : 1;            // rows of G
+    static constexpr int TILES_END = NCOPY * 2 * NT * TILEB > RAWB ? NCOPY * 2 * NT * TILEB : RAWB;
+    static constexpr int QB = C * LDI * (int)sizeof(IT);
+    static constexpr int PADB0 = TILES_END - GR * LDG * 4 - QB;
+    static constexpr int PADB = WIDE && PADB0 > 0 ? (PADB0 + 15) / 16 * 16 : 0;
+    struct InPlain {
+        float G[GR][LDG];   // KDA: log-decay, then g - m
+        IT Ks[C][LDI];
+        IT Qs[C][LDI];
+    };
+    struct InPadded {
+        float G[GR][LDG];
+        char pad[PADB > 0 ? PADB : 16];
+        IT Ks[C][LDI];
+        IT Qs[C][LDI];
+    };
+    using In = typename std::conditional<(PADB > 0), InPadded, InPlain>::type;
+    static_assert(!WIDE || GR * LDG * 4 + PADB + QB >= TILES_END, "staged q past the tiles");
     union alignas(16) {
-        struct {
-            // KDA: log-decay, then g - m (WIDE GDN: unused rows that keep Qs
-            // past the partial tiles, T and T^T, as for KDA)
-            float G[KDA || WIDE ? C : 1][LDG];
-            IT Ks[C][LDI];
-            IT Qs[C][LDI];
-        } in;
+        In in;
         float Pt[NCOPY][2 * NT][16][20];  // partial Gram tiles: A tiles, then M tiles
         char raw[RAWB];
     } u;
@@ -953,7 +964,7 @@ __global__ __launch_bounds__(256, C == 64 ? 2 : 3) void prep_kernel(PrepKArgs p)
         constexpr int KP = sizeof(ST) == 2 ? 2 : 1;   // key blocks per store
         // WIDE: this wave's key-block pair is the k-step it took in C, whose
         // (K e^g)^T pieces sit in its columns of the staged q
-        static_assert(!WIDE || DK / (16 * KP) == 4, "one key-block pair per wave");
+        static_assert(!WIDE || DK / (16 * KP) <= 4, "at most one key-block pair per wave");
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
@@ -1142,7 +1153,8 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
     constexpr int RX = Slot::RPIECES / (64 * NRW);  // LDS-direct loads per record-wave lane per chunk
     constexpr int VV = C * (DVS / EPV);            // 16-byte value vectors per chunk
     // LDS slots: the chain reads one while the loaders fill the next NSLOT - 1
-    constexpr int NSLOT = std::min<int>(4, (int)((160 * 1024) / sizeof(Slot)));
+    // (64-token chunks: two split slots, whatever fits; see ChainSlot64)
+    constexpr int NSLOT = NB == 4 ? 2 : std::min<int>(4, (int)((160 * 1024) / sizeof(Slot)));
     constexpr int GK = DK * (int)sizeof(ST) / 16, GC = C * (int)sizeof(ST) / 16;
     constexpr size_t RS = chunk_record_stride(DK, C, KDA, sizeof(ST));
     static_assert(sizeof(Rec) % 16 == 0, "record pieces");

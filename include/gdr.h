@@ -160,9 +160,7 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  *  dv_slice       value channels one workgroup owns: 0 = automatic, else a
  *                 compiled width below that divides head_dim_v.
  *                 Compiled (q/k/v dtype: head_dim_k; chunk_size; dv_slice):
- *                   bf16: {32, 64, 128}; 32; 16 or 32 (record and chain kernels)
- *                   bf16: 128; 64; 16 or 32 (record and chain kernels)
- *                   bf16: {32, 64}; 64; 16 or 32 (single fused kernel)
+ *                   bf16: {32, 64, 128}; 32 or 64; 16 or 32
  *                   fp32: {16, 32, 64, 128}; 16 or 32; 16
  *                 Any other request returns GDR_ERROR_NOT_SUPPORTED.
  *  scale          readout factor (1 for the printed equations).

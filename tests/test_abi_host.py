@@ -105,7 +105,7 @@ def _decode_tokens(N=4, K=4, H=2, Hk=0, dk=64, dv=64, gate=0, qkv=1, gdt=0, odt=
     (dict(chunk=48), 1, "chunk_size"),
     (dict(chunk=16), 2, "no prefill kernel"),                           # bf16 runs 32- and 64-token chunks
     (dict(chunk=64, qkv=0), 2, "no prefill kernel"),                    # fp32 q/k/v: 16 or 32 only
-    (dict(chunk=64, shape=(1, 64, 2, 16, 64, 1, 0)), 2, "no fused prefill kernel"),   # fused: dk >= 32
+    (dict(chunk=64, shape=(1, 64, 2, 16, 64, 1, 0)), 2, "no prefill kernel"),   # bf16, 64-token chunks: dk >= 32
     (dict(chunk=64, dvs=64, shape=(1, 64, 2, 128, 128, 1, 0)), 2, "no prefill kernel"),   # 64-token chunks: slices of 16 or 32
     (dict(dvs=48), 1, "dv_slice"),
     (dict(shape=(1, 64, 2, 64, 48, 1, 0), dvs=32), 1, "does not divide"),
@@ -163,45 +163,21 @@ def test_prefill_workspace_size():
     assert f(ctypes.byref(sh), 0, 1, 48, 0) == 0
 
 
-def _fused_ws(num_seqs, H, Hk, dk, dv, kda, packed, cus=256):
-    """The fused prefill's workspace as documented: handshake words, a ring of
-    NS + 2 records per group of NS value slices, a scratch per workgroup; the
-    largest over the value-slice widths a call may pick."""
-    r256 = lambda b: -(-b // 256) * 256
-    C = 64
-    rec = r256((dk if kda else 4) * 4 + (3 * C * dk + 2 * C * C) * 2)
-    scr = r256(((C // 16) * (2 if kda else 1) * 16 * dk + dk * C) * 2)
-    G = H // Hk
-    per_xcd = -(-num_seqs * Hk // 8) * G
-    best = 0
-    for dvs in (16, 32):
-        if dv % dvs:
-            continue
-        ns = dv // dvs
-        gpx = max(1, min(per_xcd, cus // (8 * ns)))
-        ngroups, grid, d = 8 * gpx, 8 * gpx * ns, ns + 2
-        off = (r256(4 * num_seqs) + r256(4 * (num_seqs + 1))) if packed else 0
-        off += r256(4 * (ngroups * (d + 2 * ns) + 1)) + ngroups * d * rec + grid * scr
-        best = max(best, off)
-    return best
-
-
-def test_fused_prefill_workspace_size():
-    """bf16 q/k/v with 64-token chunks: d_k = 128 runs the two-kernel path
-    (one record per chunk and head, as for 32-token chunks); other key widths
-    run the fused kernel, whose ring does not depend on the sequence length."""
+def test_prefill_workspace_size_chunk64():
+    """bf16 q/k/v with 64-token chunks: one record per (chunk slot, head), as
+    for 32-token chunks, at every compiled key width."""
     lib = gdr.load_library()
     f = lib.gdr_prefill_workspace_bytes
     r256 = lambda b: -(-b // 256) * 256
-    for (B, T, H, dk, dv, N, Hk, gate, packed) in [(1, 1000, 4, 64, 64, 9, 0, 0, 0), (1, 777, 6, 32, 48, 3, 2, 1, 1)]:
-        sh = gdr.PrefillShape(B, T, H, dk, dv, N, Hk)
-        assert f(ctypes.byref(sh), gate, 1, 64, packed) == _fused_ws(N, H, Hk or H, dk, dv, gate == 1, packed)
-    assert _fused_ws(2, 32, 32, 128, 128, True, False) < 64 << 20       # KDA 32K: tens of MB, not GB
-    rec64 = lambda kda: r256((128 if kda else 4) * 4 + (3 * 64 * 128 + 2 * 64 * 64) * 2)
+    rec64 = lambda dk, kda: r256((dk if kda else 4) * 4 + (3 * 64 * dk + 2 * 64 * 64) * 2)
+    sh = gdr.PrefillShape(1, 1000, 4, 64, 64, 9, 0)
+    assert f(ctypes.byref(sh), 0, 1, 64, 0) == 16 * 4 * rec64(64, False)
+    sh = gdr.PrefillShape(1, 777, 6, 32, 48, 3, 2)
+    assert f(ctypes.byref(sh), 1, 1, 64, 1) == 256 + 256 + (13 + 3) * 6 * rec64(32, True)
     sh = gdr.PrefillShape(2, 32768, 32, 128, 128, 2, 0)
-    assert f(ctypes.byref(sh), 1, 1, 64, 0) == 2 * 512 * 32 * rec64(True)
+    assert f(ctypes.byref(sh), 1, 1, 64, 0) == 2 * 512 * 32 * rec64(128, True)
     sh = gdr.PrefillShape(1, 262144, 16, 128, 128, 8, 0)
-    assert f(ctypes.byref(sh), 0, 1, 64, 1) == 256 + 256 + (4096 + 8) * 16 * rec64(False)
+    assert f(ctypes.byref(sh), 0, 1, 64, 1) == 256 + 256 + (4096 + 8) * 16 * rec64(128, False)
 
 
 @pytest.mark.parametrize("kw,status,msg", [

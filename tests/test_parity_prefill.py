@@ -119,10 +119,9 @@ def test_prefill_bf16_shapes(dk, dv, H, T, gate, init, chunk, dvs):
     _check_all(inp, f"bf16 dk={dk} dv={dv} H={H} T={T} {gate} init={init}", chunk_size=chunk, dv_slice=dvs)
 
 
-# 64-token chunks: d_k = 128 runs the two kernels (four-block inverse, split
-# chain slots), d_k = 32 and 64 the single-kernel prefill (records shared
-# through a ring)
-FUSED_CASES = [
+# 64-token chunks: the same two kernels with the UT inverse over four 16-token
+# blocks and the chain's split record slots
+CHUNK64_CASES = [
     # dk, dv, H, T, gate, init, dv_slice (0: automatic)
     (128, 128, 2, 1, "head", False, 0),
     (128, 128, 2, 63, "channel", True, 32),
@@ -141,24 +140,23 @@ FUSED_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dk,dv,H,T,gate,init,dvs", FUSED_CASES)
-def test_prefill_fused_shapes(dk, dv, H, T, gate, init, dvs):
+@pytest.mark.parametrize("dk,dv,H,T,gate,init,dvs", CHUNK64_CASES)
+def test_prefill_chunk64_shapes(dk, dv, H, T, gate, init, dvs):
     inp = _small(dk, dv, H, T, gate, torch.bfloat16, init, seed=3 * dk + dv + T + H)
-    _check_all(inp, f"fused dk={dk} dv={dv} H={H} T={T} {gate} init={init} dvs={dvs}", chunk_size=64, dv_slice=dvs)
+    _check_all(inp, f"chunk 64 dk={dk} dv={dv} H={H} T={T} {gate} init={init} dvs={dvs}", chunk_size=64, dv_slice=dvs)
 
 
 @pytest.mark.parametrize("gate", ["head", "channel"])
-def test_prefill_fused_more_units_than_workgroups(gate):
-    """300 heads of 32 value channels: one slice per group and more (sequence,
-    head) units than workgroups, so groups take several units in turn (each
-    group builds, publishes and consumes every record of its units itself)."""
+def test_prefill_chunk64_more_units_than_workgroups(gate):
+    """300 heads of 32 value channels at 64-token chunks: more chain
+    workgroups than the device holds at once, so they run in several rounds."""
     inp = _small(64, 32, 300, 70, gate, torch.bfloat16, True, seed=301)
-    _check_all(inp, f"fused 300 heads {gate}", chunk_size=64)
+    _check_all(inp, f"chunk 64, 300 heads {gate}", chunk_size=64)
 
 
-def test_prefill_fused_workspace_reuse_and_scale():
-    """Two different calls through one workspace (the handshake words are
-    reset per call), then a readout scale: o(s) = s o(1)."""
+def test_prefill_chunk64_workspace_reuse_and_scale():
+    """Two different calls through one caller workspace, then a readout scale:
+    o(s) = s o(1)."""
     a = _small(128, 128, 4, 333, "channel", torch.bfloat16, True, seed=311)
     b = _small(128, 128, 4, 97, "head", torch.bfloat16, False, seed=312)
     ws = torch.empty(32 << 20, dtype=torch.uint8, device=DEV)      # more than either call needs

@@ -77,9 +77,9 @@ def test_static_scratch_consecutive_calls():
     # 2: smaller, packed GDN (one pass over every chunk fits)
     small = _inputs("gdn_packed", 64, 64, 4, 700, "head", lengths=[300, 17, 383], seed=12)
     _compare("packed GDN 3 sequences, 700 tokens, H=4 d=64", small)
-    # 3: smaller still, the fused 64-token kernel
-    tiny = _inputs("gdn_fused", 64, 64, 2, 200, "head", seed=13)
-    _compare("GDN T=200 H=2 d=64, chunk 64 (fused)", tiny, chunk=64)
+    # 3: smaller still, 64-token chunks at d_k = 64
+    tiny = _inputs("gdn_c64", 64, 64, 2, 200, "head", seed=13)
+    _compare("GDN T=200 H=2 d=64, chunk 64", tiny, chunk=64)
     # 4: 64-token chunks at d_k = 128 (the two kernels), records past the
     # scratch, so in segments
     wide = _inputs("kda_wide", 128, 128, 8, 8192, "channel", B=2, seed=14)
