@@ -219,10 +219,23 @@ def test_prefill_bf16_gates(gate):
     _check_all(prefill_inputs(w1, DEV, gate_dtype=torch.bfloat16), f"bf16 gates ungrouped {gate}")
 
 
-def test_prefill_grouped_packed():
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_prefill_grouped_packed(chunk):
     lens = [33, 0, 100, 7]
     inp = _small(128, 128, 4, 0, "channel", torch.bfloat16, True, seed=71, lengths=lens, Hk=2)
-    _check_all(inp, f"grouped packed {lens}")
+    _check_all(inp, f"grouped packed {lens}", chunk_size=chunk)
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_chunk64_grouped_bf16_gates_packed(gate):
+    """64-token chunks with value heads sharing q/k heads, bf16 gates, and a
+    packed batch holding empty, one-token and ragged sequences."""
+    w = Workload("small", "prefill", heads=6, qk_heads=2, dk=64, dv=64, qkv_dtype=torch.bfloat16, gate=gate,
+                 batch=1, seqlen=0, init_state=True, seed=83)
+    lens = [130, 0, 1, 64, 65, 0, 257]
+    inp = prefill_inputs(w, DEV, gate_dtype=torch.bfloat16, lengths=lens)
+    _, fin = _check_all(inp, f"chunk 64, grouped, bf16 gates, packed {lens} {gate}", chunk_size=64)
+    assert torch.equal(fin[1], inp["initial_state"][1]) and torch.equal(fin[5], inp["initial_state"][5])
 
 
 @pytest.mark.parametrize("gate", ["head", "channel"])
@@ -325,10 +338,11 @@ def test_prefill_in_place_state_and_poisoned_output():
 
 
 @pytest.mark.parametrize("gate", ["head", "channel"])
-def test_prefill_bf16_output(gate):
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_prefill_bf16_output(gate, chunk):
     inp = _small(128, 128, 2, 190, gate, torch.bfloat16, True, seed=55)
     ref_o, ref_s = _oracle(inp)
-    out, fin = _gpu(inp, out_dtype=torch.bfloat16)
+    out, fin = _gpu(inp, out_dtype=torch.bfloat16, chunk_size=chunk)
     assert out.dtype == torch.bfloat16
     assert_close_rounded("out (bf16)", out, ref_o, TOL[torch.bfloat16])
     assert_close("final_state", fin, ref_s, TOL[torch.bfloat16])
