@@ -325,6 +325,21 @@ def test_prefill_chunk_invariance_fp32(gate):
         assert_close("final_state", s, ref_s, TOL[torch.float32])
 
 
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prefill_chunk_invariance_bf16(gate):
+    """32- and 64-token chunks compute the same function: each within the bf16
+    bound of the oracle, and within that bound of each other."""
+    inp = _small(128, 128, 3, 333, gate, torch.bfloat16, True, seed=57)
+    ref_o, ref_s = _oracle(inp)
+    got = {}
+    for chunk in (32, 64):
+        say(f"chunk {chunk}")
+        got[chunk] = _gpu(inp, chunk_size=chunk)
+        assert_close("out", got[chunk][0], ref_o, TOL[torch.bfloat16])
+        assert_close("final_state", got[chunk][1], ref_s, TOL[torch.bfloat16])
+    assert_close("out, chunk 64 vs 32", got[64][0], to_np(got[32][0]), TOL[torch.bfloat16])
+
+
 def test_prefill_in_place_state_and_poisoned_output():
     inp = _small(128, 128, 2, 100, "head", torch.bfloat16, True, seed=53)
     ref_o, ref_s = _oracle(inp)
