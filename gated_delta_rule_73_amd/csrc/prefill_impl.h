@@ -1504,7 +1504,12 @@ __global__ __launch_bounds__(64 * (kLoaderWaves + DVS / 16)) void chain_kernel(C
             for (int y = 0; y < VPL; ++y) {
                 const int e = lane + 64 * y, vt = e / (DVS / EPV), vc = (e % (DVS / EPV)) * EPV;
                 const int t = bos + cc * C + vt;
-                vr[sl][y] = *reinterpret_cast<const IV *>(gv + ((size_t)min(t, eos - 1) * H + h) * DV + v0 + vc);
+                // (non-temporal: each slice reads its values once, and leaving
+                // them out of L2 keeps the records the slices share there
+                // longer: the chain's HBM fetch fell from 2.9-3.4 to 2.5 GB
+                // per KDA 32K call)
+                vr[sl][y] = __builtin_nontemporal_load(
+                    reinterpret_cast<const IV *>(gv + ((size_t)min(t, eos - 1) * H + h) * DV + v0 + vc));
                 vok[sl][y] = t < eos;
             }
         };
