@@ -37,6 +37,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -53,11 +54,19 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "prefill_kda_32k_traffic.json")
 KERNEL_SOURCES = ["prefill_impl.h", "prefill_shapes.h", "prefill_bf16_kda.hip", "prefill.hip", "common.h"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (a comment edit does not
+    change the kernels the counters describe)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gated_delta_rule_73_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_73_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

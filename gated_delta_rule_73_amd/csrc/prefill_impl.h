@@ -23,7 +23,9 @@
 // chunks (W_n included), so prep_kernel computes it for every (chunk, head)
 // at once and writes one record per chunk to the workspace.  chain_kernel then walks the
 // chunks of each (sequence, head) in order: loader waves stream the records
-// (and the value slice) several chunks ahead into a double buffer in LDS, and
+// (and the value slice) ahead into LDS slots (four at 16/32-token chunks; at
+// 64-token chunks two slots, each split into the halves read before and after
+// a mid-chunk barrier and refilled separately), and
 // one chain wave per 16 value channels carries its part of the state
 // transposed (S^T: key rows x value columns) as fp32 MFMA accumulators.  In
 // that layout the state and U feed the next product straight from
