@@ -73,7 +73,16 @@ int auto_dv_slice(bool bf16, bool kda, int dk, int dv, int chunk, long units) {
         const long cap = (long)cus * (per_cu > 0 ? per_cu : 1);
         return (units * (dv / dvs) + cap - 1) / cap;
     };
-    return rounds(32) < rounds(16) ? 32 : 16;
+    // the narrowest width among those that need the fewest rounds (a slice
+    // fetches its chunk's whole record whatever its width, so wider slices
+    // only pay when they save a round)
+    int best = 32;
+    long best_r = rounds(32);
+    if (dv % 64 == 0 && prefill_supported(bf16, kda, dk, 64, chunk)) {
+        const long r64 = rounds(64);
+        if (r64 < best_r) best = 64, best_r = r64;
+    }
+    return rounds(16) <= best_r ? 16 : best;
 }
 
 hipError_t launch_schedule(const int32_t *cu, int n, int chunk, int32_t *order, int32_t *chunk_offset,

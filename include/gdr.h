@@ -161,6 +161,7 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_shape *shape, gdr_gate gate
  *                 compiled width below that divides head_dim_v.
  *                 Compiled (q/k/v dtype: head_dim_k; chunk_size; dv_slice):
  *                   bf16: {32, 64, 128}; 32 or 64; 16 or 32
+ *                   bf16: 128; 32; 64
  *                   fp32: {16, 32, 64, 128}; 16 or 32; 16
  *                 Any other request returns GDR_ERROR_NOT_SUPPORTED.
  *  scale          readout factor (1 for the printed equations).

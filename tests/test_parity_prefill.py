@@ -110,6 +110,9 @@ BF16_CASES = [
     (32, 32, 1, 95, "head", False, 32, 32),
     (32, 48, 2, 100, "channel", True, 32, 16),
     (32, 48, 2, 100, "head", True, 32, 16),
+    (128, 128, 2, 197, "channel", True, 32, 64),
+    (128, 128, 3, 95, "head", False, 32, 64),
+    (128, 64, 2, 130, "channel", True, 32, 64),
 ]
 
 
