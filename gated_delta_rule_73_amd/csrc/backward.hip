@@ -207,6 +207,25 @@ __device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int lane_bytes,
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, lane_bytes, uniform_bytes, 0));
 }
 
+// Loads with the non-temporal cache hint, for data a workgroup reads once or
+// for the last time: the L2 evicts such lines first, so they do not push out
+// lines that are read again (the grad kernel's states, read row-wise for Y and
+// K_end dS^T, then column-wise for dq and dk).  Fetch measured with and without
+// (KDA 32K): 19.9 against 21.5 GB per call.
+constexpr int kNonTemporal = 2;   // the cache-policy operand's nt bit on this chip
+__device__ __forceinline__ float bload_last(__amdgpu_buffer_rsrc_t r, int lane_bytes, int uniform_bytes) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, lane_bytes, uniform_bytes, kNonTemporal));
+}
+__device__ __forceinline__ float4 load4_once(const float *p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float4 load4_once(const __bf16 *p) {
+    const bf16x4 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x4 *>(p));
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+template <typename T> __device__ __forceinline__ float ld1_once(const T *p) { return to_f32(__builtin_nontemporal_load(p)); }
+
 __device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, int lane_bytes, int uniform_bytes) {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, uniform_bytes, 0));
@@ -978,21 +997,21 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p, long
         for (int u = 0; u < NKL; ++u) {
             const int e = min(tid + NT * u, C * DK / 4 - 1), r = e / (DK / 4), j = (e % (DK / 4)) * 4;
             const long t = L.tok0 + min(r, L.len - 1);
-            kv[u] = load4(k + (t * p.Hk + hq) * DK + j);
-            qv[u] = load4(q + (t * p.Hk + hq) * DK + j);
-            gv[u] = KDA ? gate4<GT>(p.log_alpha, (t * H + h) * DK + j) : z4;
+            kv[u] = load4_once(k + (t * p.Hk + hq) * DK + j);
+            qv[u] = load4_once(q + (t * p.Hk + hq) * DK + j);
+            gv[u] = KDA ? load4_once(static_cast<const GT *>(p.log_alpha) + (t * H + h) * DK + j) : z4;
         }
 #pragma unroll
         for (int u = 0; u < NVL; ++u) {
             const int e = min(tid + NT * u, C * DV / 4 - 1), r = e / (DV / 4), i = (e % (DV / 4)) * 4;
             const long o = ((L.tok0 + min(r, L.len - 1)) * H + h) * DV + i;
-            vv[u] = load4(v + o);
-            dd[u] = *reinterpret_cast<const float4 *>(p.d_out + o);
+            vv[u] = load4_once(v + o);
+            dd[u] = load4_once(p.d_out + o);
         }
 #pragma unroll
         for (int u = 0; u < NTL; ++u) {
-            tv[u] = rec[R::T + tid + NT * u];
-            mv[u] = rec[R::M + tid + NT * u];
+            tv[u] = ld1_once(rec + R::T + tid + NT * u);
+            mv[u] = ld1_once(rec + R::M + tid + NT * u);
         }
         const long obg = (L.tok0 + min(tid & (C - 1), L.len - 1)) * H + h;
         bb = gate1<GT>(p.beta, obg);
@@ -1320,8 +1339,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdKArgs p, long
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int lane_bytes = ((4 * lq + t) * DK + j) * 4, ub = (kb + 16 * hf) * DK * 4;
-                    sa[buf][hf][t] = bload(rS0, lane_bytes, ub);
-                    sd[buf][hf][t] = bload(rdS, lane_bytes, ub);
+                    sa[buf][hf][t] = bload_last(rS0, lane_bytes, ub);
+                    sd[buf][hf][t] = bload_last(rdS, lane_bytes, ub);
                 }
         };
         gather(0, 0);
