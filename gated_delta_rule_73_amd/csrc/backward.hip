@@ -579,8 +579,21 @@ __device__ __forceinline__ void sts4(__bf16 *p, const bf16x4 v) { *reinterpret_c
 //   L:  forward T, backward M^T: [chunk row][32 chunk columns];
 //   Zt: forward diag(b) V, backward scale dO, transposed:
 //       [value row][32 chunk rows].
-// loader waves beside the NW state waves (one per SIMD)
+// Four loader waves beside the NW state waves, eight waves in all (wave w
+// runs on SIMD w mod 4).  With four state waves, each SIMD holds one state
+// and one loader wave.  With two, the loaders are waves 2, 3, 6 and 7, on the
+// two SIMDs without a state wave, and waves 4 and 5 only keep the barrier
+// count.  (Loaders sharing a SIMD with a state wave had taken ~35% longer per
+// chunk than the others, GDN 8K clock stamps; apart, the GDN 8K backward went
+// from 1.17 to 1.16 ms and the grouped GDN 32K one from 10.48 to 10.36 ms.)
 constexpr int scan_loader_waves(int) { return 4; }
+constexpr int scan_block_waves(int) { return 8; }
+template <int NW> __device__ __forceinline__ bool scan_is_loader(int w) { return NW == 4 ? w >= 4 : (w & 3) >= 2; }
+// a loader thread's index, 0 .. 255
+template <int NW> __device__ __forceinline__ int scan_loader_thread(int tid) {
+    const int w = tid >> 6;
+    return NW == 4 ? tid - 256 : 64 * (2 * (w >> 2) + (w & 1)) + (tid & 63);
+}
 
 template <int DK, int NW> struct ScanLds {
     static constexpr int C = kBC, ZW = 16 * NW;
@@ -599,7 +612,8 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     // the record fields; the raw q, k rows measured faster with their
     // two-byte column loads
     constexpr bool COLT = !RAW;
-    constexpr int C = kBC, SNT = 64 * NW, NT = 64 * scan_loader_waves(NW), ZW = 16 * NW, NB = DK / 32;
+    constexpr int C = kBC, NT = 64 * scan_loader_waves(NW), ZW = 16 * NW, NB = DK / 32;
+    static_assert(NW == 2 || NW == 4, "scan wave layout");
     // per loader thread (NT of them): NE row pieces of E and NE column
     // pieces of Bt (and Gt), NL pieces of L, NZ column pieces of Zt; four
     // values each
@@ -620,8 +634,9 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     if (unit >= p.num_seqs * H) return;
     const int n = p.cu ? p.order[unit / H] : unit / H, h = unit % H;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lr = l & 15, lq = l >> 4;
-    const bool loader = w >= NW;                  // waves 0 .. NW - 1 hold the state, the others load
-    int lt = tid - SNT;                           // loader thread index (made opaque per chunk below)
+    const bool state = w < NW;                    // waves 0 .. NW - 1 hold the state
+    const bool loader = scan_is_loader<NW>(w);    // (neither: only the barriers)
+    int lt = scan_loader_thread<NW>(tid);         // loader thread index (made opaque per chunk below)
     long rc0, tok_base;
     int nc, len;
     if (p.cu) {
@@ -848,13 +863,13 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
     };
 
     f32x4 x[DK / 16];
-    if (!loader) {
+    if (state) {
         const float *init = BWD ? p.d_final : p.initial_state;
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt)
             x[jt] = init ? *reinterpret_cast<const f32x4 *>(init + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq)
                          : zero4();
-    } else {
+    } else if (loader) {
         if (nc > 0) {
             fetch(0);
             put(0);
@@ -875,13 +890,15 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
             // kept in registers across the loop.
             int opaque_zero;
             asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
-            lt = ((int)threadIdx.x - SNT + opaque_zero) & (NT - 1);
+            lt = scan_loader_thread<NW>((int)threadIdx.x + opaque_zero) & (NT - 1);   // (the mask keeps lt's range known)
             if (s + 1 < nc) {
                 put((s & 1) ^ 1);
                 if (s + 2 < nc) fetch(s + 2);
             }
             lds_barrier();
         }
+    } else if (!state) {
+        for (int s = 0; s < nc; ++s) lds_barrier();
     } else for (int s = 0; s < nc; ++s) {
         const int b = s & 1;
         const int c = BWD ? nc - 1 - s : s;
@@ -926,7 +943,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
         lds_barrier();
     }
     float *fin = BWD ? p.d_init : p.fwd_final;
-    if (!loader && fin) {
+    if (state && fin) {
 #pragma unroll
         for (int jt = 0; jt < DK / 16; ++jt)
             *reinterpret_cast<f32x4 *>(fin + (((long)n * H + h) * DV + row) * DK + 16 * jt + 4 * lq) = x[jt];
@@ -937,7 +954,7 @@ __device__ __forceinline__ void scan_body(const BwdKArgs &p, int block, ScanLds<
 // states forward, the second half the state gradients backward.  The two
 // recurrences are independent, so each half fills the CUs the other leaves.
 template <int DK, int NW, bool KDA, typename IT, typename GT>
-__global__ __launch_bounds__(64 * (NW + scan_loader_waves(NW))) void bwd_scan_kernel(BwdKArgs p, int half) {
+__global__ __launch_bounds__(64 * scan_block_waves(NW)) void bwd_scan_kernel(BwdKArgs p, int half) {
     __shared__ ScanLds<DK, NW> lds;
     if ((int)blockIdx.x < half)
         scan_body<DK, NW, false, KDA, IT, GT>(p, blockIdx.x, lds);
@@ -1516,10 +1533,10 @@ static hipError_t run_backward(const BackwardArgs &a, const BwdKArgs &kp0, hipSt
         const unsigned grid = (fwd ? scan_blocks : 0) + (bwd ? scan_blocks : 0);
         const int half = fwd ? (int)scan_blocks : 0;
         if (four)
-            hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, KDA, IT, GT>), dim3(grid), dim3(64 * (4 + scan_loader_waves(4))), 0, st,
+            hipLaunchKernelGGL((bwd_scan_kernel<DK, 4, KDA, IT, GT>), dim3(grid), dim3(64 * scan_block_waves(4)), 0, st,
                                kp, half);
         else
-            hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(grid), dim3(64 * (2 + scan_loader_waves(2))), 0, st,
+            hipLaunchKernelGGL((bwd_scan_kernel<DK, 2, KDA, IT, GT>), dim3(grid), dim3(64 * scan_block_waves(2)), 0, st,
                                kp, half);
         return hipGetLastError();
     };
