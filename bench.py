@@ -19,7 +19,7 @@ Further workloads are timed in their own loops and reported beside the step
 - one decode step of that layer fed from its projected channels, the fused
   call (prologue and state update in one kernel) beside the two calls it
   replaces.
-Two measured ceilings of the same box are reported with them: a large bf16
+Two measured ceilings of the same GPU are reported with them: a large bf16
 GEMM (the library GEMM, for the MFMA side) and a 512 MiB read-modify-write
 (for the HBM side).
 
